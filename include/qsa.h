@@ -1,0 +1,226 @@
+/*
+ * qsa.h — C ABI of libqsa: indexer-selected ("QSA-style") sparse attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (per query): an indexer scores keys mean-pooled into blocks of
+ * `ratio` tokens; a top-k keeps budget/ratio blocks; attention runs over the
+ * tokens of those blocks plus the incomplete tail block.  While the visible
+ * prefix L satisfies L <= budget + ratio - 1 (the inert bound) every complete
+ * block is kept, which is exactly dense causal attention.
+ *   Sources: "Agentic shootout — Atlas x Flash-Next research" page:
+ *   gap analysis #1, plan item P1 (indexer, block top-k, gather attention);
+ *   report "Flash-Next support: vLLM vs Atlas", section (a)6 (compressed keys
+ *   per complete group, block top-k, group->token expansion of width
+ *   budget + ratio - 1, -1 padded); "PR 16 review", section (a) (4Q+1K
+ *   indexer, 4-token mean-pooled blocks, relu score, top-512 + tail, inert
+ *   <= 2051 visible tokens); "llama.cpp vs Atlas", section (a)3 (the
+ *   incomplete tail block is always visible).  "Atlas Flash-Next defect
+ *   investigations" page, Defect 2 (inert_bound = budget + ratio - 1).
+ *
+ * Conventions shared by every call:
+ *  - Memory: every tensor pointer is a DEVICE pointer owned by the caller.
+ *    The library never allocates, frees or keeps a pointer after returning.
+ *    Struct arguments are HOST structs read during the call only.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream).  Work is enqueued asynchronously; inputs must stay valid and
+ *    unmodified until the stream has passed it.  No call synchronises, copies
+ *    device->host or allocates, so a sequence of calls can be captured in a
+ *    HIP graph.
+ *  - Errors: arguments are validated on the host BEFORE anything is
+ *    enqueued; on any error nothing is enqueued and outputs are untouched.
+ *    qsa_last_error() returns a thread-local message naming the argument and
+ *    the limit.  A failed kernel launch returns QSA_ERR_HIP with the HIP
+ *    error text.  Device-side contents (offset arrays) are not read by the
+ *    host; they must satisfy the layout rules below (out-of-contract
+ *    contents are undefined behaviour).  NaN/Inf inputs are out of contract.
+ *  - The library never substitutes dense attention for sparse attention past
+ *    the inert bound: the regime is decided per query from its own L.
+ *
+ * Layouts (row-major, varlen-packed, int64 offsets [B+1] with offsets[0]=0):
+ *  k_idx [sum N_s, d_idx]; K, V [sum N_s, hkv, d];
+ *  kc [sum floor(N_s/ratio), d_idx] (+ kc_scale [same rows] f32 for e4m3);
+ *  q [total_q, hq, d]; q_idx [total_q, h_idx, d_idx]; w [total_q, h_idx] f32;
+ *  scores [total_q, ld_scores] f32; idx [total_q, budget/ratio] int32;
+ *  out [total_q, hq, d] (dtype of q).
+ *  Sequence s holds N_s tokens (the queries' own keys already appended); its
+ *  n_s queries are its LAST n_s tokens, so query j (0-based) of s sees
+ *  L = N_s - n_s + j + 1 tokens.  Query head h uses KV head h / (hq/hkv).
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, inconsistent sizes */
+    QSA_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels implement */
+    QSA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    QSA_ERR_HIP = 4               /* a HIP call or kernel launch failed */
+} qsa_status;
+
+typedef enum qsa_dtype {
+    QSA_F32 = 0,
+    QSA_BF16 = 1,
+    QSA_FP8_E4M3 = 2 /* OCP E4M3FN: bias 7, max finite 448, no infinities */
+} qsa_dtype;
+
+/* A varlen batch.  Offsets are DEVICE int64 arrays of num_seqs+1 entries. */
+typedef struct qsa_batch {
+    int32_t num_seqs;            /* B >= 1 */
+    int32_t max_q_per_seq;       /* host upper bound on n_s (1 for decode) */
+    int64_t total_q;             /* host copy of q_offsets[B] (B when q_offsets is NULL) */
+    int64_t max_kv_len;          /* host upper bound on N_s (grid sizing only) */
+    const int64_t *kv_offsets;   /* rows of sequence s in K, V, k_idx */
+    const int64_t *blk_offsets;  /* rows of sequence s in kc: prefix sums of floor(N_s/ratio) */
+    const int64_t *q_offsets;    /* rows of sequence s in q, q_idx, w, scores, idx, out;
+                                    NULL => exactly one query per sequence (decode) */
+} qsa_batch;
+
+/* Indexer operands.  One key head (MQA), h_idx query heads. */
+typedef struct qsa_indexer {
+    const void *q_idx;           /* [total_q, h_idx, d_idx], dtype q_dtype */
+    const float *w;              /* [total_q, h_idx] per-query head weights */
+    const void *kc;              /* [sum nb, d_idx] compressed keys, dtype kc_dtype */
+    const float *kc_scale;       /* [sum nb] iff kc_dtype == QSA_FP8_E4M3, else NULL */
+    int32_t q_dtype;             /* QSA_F32 | QSA_BF16 */
+    int32_t kc_dtype;            /* QSA_F32 | QSA_BF16 | QSA_FP8_E4M3 */
+    int32_t h_idx;               /* 1, 2, 4, 8 or 16 */
+    int32_t d_idx;               /* 64 | 128 */
+} qsa_indexer;
+
+/* Attention operands; the output has the dtype of q. */
+typedef struct qsa_attn {
+    const void *q;               /* [total_q, hq, d] */
+    const void *k;               /* [sum N_s, hkv, d] */
+    const void *v;               /* [sum N_s, hkv, d] */
+    int32_t dtype;               /* QSA_F32 | QSA_BF16 (q, k, v and out) */
+    int32_t hq, hkv, d;          /* hq % hkv == 0, hq/hkv in {1,2,4,8,16}, d == 128 */
+    float softmax_scale;         /* e.g. 1/sqrt(d) rounded to fp32 */
+} qsa_attn;
+
+/* budget + ratio - 1: the largest visible prefix L that is still served by
+ * dense attention ("PR 16 review" (a): inert <= 2051 visible tokens for
+ * budget 2048, ratio 4; defect investigations page, Defect 2).  Returns -1
+ * for ratio <= 0 or budget <= 0. */
+int32_t qsa_inert_bound(int32_t budget, int32_t ratio);
+
+/* Thread-local text of the last error ("" if none). Never NULL. */
+const char *qsa_last_error(void);
+/* Library version string, e.g. "qsa 0.1.0 (abi 1, gfx950)". */
+const char *qsa_version(void);
+/* QSA_ABI_VERSION the library was built with. */
+int32_t qsa_abi_version(void);
+
+/* Key compression: kc[b] = mean of k_idx rows b*ratio .. b*ratio+ratio-1 for
+ * every COMPLETE block b < floor(N_s/ratio) of every sequence (vLLM report
+ * (a)6: one compressed key per complete group, mean-pooled; "PR 16 review"
+ * (a): 4-token mean-pooled blocks).
+ * Arithmetic: fp32 sum in row order, times 1/ratio (exact: ratio is a power
+ * of two), then stored as fp32, bf16 (round to nearest even) or e4m3: with
+ * amax = max_d |mean_d|, scale = amax/448 (fp32, correctly rounded) is written
+ * to kc_scale[b] and code_d = e4m3_rne(clamp(mean_d/scale, +-448)); scale 0
+ * gives all-zero codes.  (The e4m3 index plane with a per-block fp32 scale of
+ * max|x|/448 is the long-context decode workload's definition.)
+ *  k_idx:  device [sum N_s, d_idx], k_dtype QSA_F32 | QSA_BF16.
+ *  ratio:  power of two in [1, 64]; d_idx in {64, 128}.
+ *  first_block: device int64 [B] or NULL; blocks b < first_block[s] are not
+ *          rewritten (incremental ingest after appending tokens).
+ *  kc:     device [sum nb, d_idx] of kc_dtype (any of the three).
+ *  kc_scale: device f32 [sum nb], required iff kc_dtype == QSA_FP8_E4M3.
+ * Errors: INVALID_ARGUMENT (null pointers, num_seqs < 1), UNSUPPORTED (ratio,
+ * d_idx, dtype), HIP. */
+qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                             const qsa_batch *b, const int64_t *first_block, void *kc,
+                             int32_t kc_dtype, float *kc_scale, void *stream);
+
+/* Indexer scores.  For every query i and visible block b < floor(L_i/ratio)
+ * of its sequence:  s_b = sum_h w_h * ReLU(q_idx[i,h,:] . kc_b)  ("PR 16
+ * review" (a): relu score of a 4Q+1K indexer; one key head, vLLM report
+ * (a)1 validator).  For e4m3 keys the dot is taken over the code values and
+ * then multiplied by kc_scale[b].
+ *  QSA_SCORE_CANONICAL: the fp32 result of one fixed evaluation order —
+ *    dot = +0; for d ascending: dot = fl(dot + fl(q*k)); [dot = fl(dot*scale)];
+ *    r = dot > 0 ? dot : +0; s = +0; for h ascending: s = fl(s + fl(w_h*r)).
+ *    Bit-identical on every call and on any host that follows the same order.
+ *  QSA_SCORE_MFMA: matrix-core scores for prefill (q_idx and kc bf16 only);
+ *    within a certified bound of the canonical value but not bit-identical.
+ *    They must be passed to qsa_topk_blocks together with `recheck`.
+ *  scores: device [total_q, ld_scores]; entries b >= floor(L_i/ratio) of a row
+ *    are left untouched.  ld_scores >= ceil(max_kv_len/ratio).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype pair, h_idx, d_idx, ratio,
+ * MFMA with non-bf16 operands), HIP. */
+#define QSA_SCORE_CANONICAL 0u
+#define QSA_SCORE_MFMA 1u
+qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b,
+                           float *scores, int64_t ld_scores, uint32_t flags, void *stream);
+
+/* Workspace bytes qsa_topk_blocks needs (0 when recheck is NULL). */
+size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio,
+                               const qsa_indexer *recheck);
+
+/* Block top-k per query (vLLM report (a)6: block top-k of budget/ratio groups;
+ * "PR 16 review" (a): top-512 + tail).  With K = budget/ratio and
+ * nb = floor(L_i/ratio):
+ *   nb <= K (L_i <= inert bound, the dense regime): idx = 0,1,...,nb-1, -1...
+ *   otherwise: the K blocks with the largest score, ties to the LOWER block
+ *   index, written in ASCENDING block order.
+ * scores: as written by qsa_index_score.  recheck: NULL when the scores are
+ * canonical; when they are QSA_SCORE_MFMA scores, the same indexer operands,
+ * which the kernel uses to bound every score's error and recompute the
+ * undecided blocks canonically, so idx equals the canonical selection bit for
+ * bit.  idx: device int32 [total_q, K].  ws: device workspace of at least
+ * qsa_topk_workspace_size() bytes (may be NULL when that is 0).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (ratio not a power of two in [1,64],
+ * budget % ratio != 0, K outside [1, 2048]), WORKSPACE, HIP. */
+qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
+                           int32_t budget, int32_t ratio, const qsa_batch *b, int32_t *idx,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes qsa_sparse_attn_decode needs for this batch and shape
+ * (qsa_sparse_attn_prefill needs none and ignores ws). */
+size_t qsa_attn_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t budget,
+                               int32_t ratio);
+
+/* Sparse attention over T(L) = tokens of the selected blocks (idx >= 0) plus
+ * the tail ratio*floor(L/ratio) .. L-1 (vLLM report (a)6: gather attention
+ * over the expanded selection; "llama.cpp vs Atlas" (a)3: the tail block is
+ * always visible).  For each query head h with KV head g = h/(hq/hkv):
+ *   out_h = sum_{t in T} softmax_t(softmax_scale * q_h . K[t,g]) V[t,g]
+ * with fp32 softmax and accumulation.  Because idx lists every complete block
+ * in the dense regime, a query at or below the inert bound gets exactly dense
+ * causal attention.  Queries with an empty T get zeros.
+ *  idx: device int32 [total_q, budget/ratio] as written by qsa_topk_blocks.
+ *  out: device [total_q, hq, d], dtype of q.
+ *  ws:  decode: device workspace of at least qsa_attn_workspace_size()
+ *       bytes; prefill: unused (may be NULL).
+ * A query's result does not depend on the other queries of the launch: the
+ * decode split count depends only on budget/ratio and prefill does not split,
+ * so outputs are bit-identical across batch compositions (chunked prefill
+ * equals single-shot prefill bit for bit).
+ * Decode requires one query per sequence (q_offsets NULL or
+ * max_q_per_seq == 1), so L = N_s.  Prefill takes any n_s (chunked prefill or
+ * speculative verify): each query uses its own causal L and its own regime
+ * (defect investigations page, fix plan PR-G: two-chunk prefill must equal
+ * single-chunk prefill, which per-query selection guarantees).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype, d, group size), WORKSPACE,
+ * HIP. */
+qsa_status qsa_sparse_attn_decode(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                  int32_t ratio, const qsa_batch *b, void *out, void *ws,
+                                  size_t ws_bytes, void *stream);
+qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                   int32_t ratio, const qsa_batch *b, void *out, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

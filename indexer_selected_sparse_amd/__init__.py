@@ -1,0 +1,264 @@
+"""Python binding of libqsa (indexer-selected sparse attention on MI355X).
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+`libqsa.so` behind the C ABI declared in `include/qsa.h`.  PyTorch provides
+device memory and streams.  There is no CPU fallback: if the library is not
+built or fails to load, every call raises.
+
+Entry points mirror the C names:
+    inert_bound, version,
+    compress_keys, index_score, topk_workspace_size, topk_blocks,
+    attn_workspace_size, sparse_attn_decode, sparse_attn_prefill.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_HIP = range(5)
+QSA_F32, QSA_BF16, QSA_FP8_E4M3 = 0, 1, 2
+QSA_SCORE_CANONICAL, QSA_SCORE_MFMA = 0, 1
+
+EXPORTS = (
+    "qsa_inert_bound", "qsa_last_error", "qsa_version", "qsa_abi_version",
+    "qsa_compress_keys", "qsa_index_score", "qsa_topk_workspace_size", "qsa_topk_blocks",
+    "qsa_attn_workspace_size", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
+)
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"qsa status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("max_q_per_seq", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("max_kv_len", ctypes.c_int64),
+                ("kv_offsets", ctypes.c_void_p), ("blk_offsets", ctypes.c_void_p),
+                ("q_offsets", ctypes.c_void_p)]
+
+
+class _Indexer(ctypes.Structure):
+    _fields_ = [("q_idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("kc", ctypes.c_void_p),
+                ("kc_scale", ctypes.c_void_p), ("q_dtype", ctypes.c_int32),
+                ("kc_dtype", ctypes.c_int32), ("h_idx", ctypes.c_int32), ("d_idx", ctypes.c_int32)]
+
+
+class _Attn(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("dtype", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqsa.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libqsa.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.qsa_inert_bound.restype = i32
+        L.qsa_inert_bound.argtypes = [i32, i32]
+        L.qsa_last_error.restype = ctypes.c_char_p
+        L.qsa_version.restype = ctypes.c_char_p
+        L.qsa_abi_version.restype = i32
+        L.qsa_compress_keys.restype = i32
+        L.qsa_compress_keys.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P]
+        L.qsa_index_score.restype = i32
+        L.qsa_index_score.argtypes = [P, i32, P, P, i64, ctypes.c_uint32, P]
+        L.qsa_topk_workspace_size.restype = sz
+        L.qsa_topk_workspace_size.argtypes = [P, i32, i32, P]
+        L.qsa_topk_blocks.restype = i32
+        L.qsa_topk_blocks.argtypes = [P, i64, P, i32, i32, P, P, P, sz, P]
+        L.qsa_attn_workspace_size.restype = sz
+        L.qsa_attn_workspace_size.argtypes = [P, P, i32, i32]
+        for f in (L.qsa_sparse_attn_decode, L.qsa_sparse_attn_prefill):
+            f.restype = i32
+            f.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != QSA_OK:
+        raise QsaError(status, lib().qsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return QSA_F32
+    if t.dtype == torch.bfloat16:
+        return QSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return QSA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ batch
+@dataclass
+class Batch:
+    """A varlen batch: device int64 offsets plus host bounds (C qsa_batch)."""
+    kv_offsets: torch.Tensor            # device int64 [B+1]
+    blk_offsets: torch.Tensor           # device int64 [B+1]
+    q_offsets: Optional[torch.Tensor]   # device int64 [B+1] or None (decode)
+    total_q: int
+    max_kv_len: int
+    max_q_per_seq: int
+
+    @property
+    def num_seqs(self) -> int:
+        return self.kv_offsets.numel() - 1
+
+    @staticmethod
+    def from_lengths(kv_lens, q_lens=None, ratio: int = 4, device="cuda") -> "Batch":
+        kv_lens = [int(x) for x in kv_lens]
+        kv = [0]
+        bl = [0]
+        for n in kv_lens:
+            kv.append(kv[-1] + n)
+            bl.append(bl[-1] + n // ratio)
+        qo = None
+        total_q, max_q = len(kv_lens), 1
+        if q_lens is not None:
+            q_lens = [int(x) for x in q_lens]
+            acc = [0]
+            for n in q_lens:
+                acc.append(acc[-1] + n)
+            qo = torch.tensor(acc, dtype=torch.int64, device=device)
+            total_q, max_q = acc[-1], max(q_lens) if q_lens else 1
+        return Batch(torch.tensor(kv, dtype=torch.int64, device=device),
+                     torch.tensor(bl, dtype=torch.int64, device=device), qo, total_q,
+                     max(kv_lens) if kv_lens else 0, max(max_q, 1))
+
+    def _c(self) -> _Batch:
+        return _Batch(self.num_seqs, self.max_q_per_seq, self.total_q, self.max_kv_len,
+                      self.kv_offsets.data_ptr(), self.blk_offsets.data_ptr(),
+                      None if self.q_offsets is None else self.q_offsets.data_ptr())
+
+
+# -------------------------------------------------------------- functions
+def inert_bound(budget: int, ratio: int) -> int:
+    return int(lib().qsa_inert_bound(budget, ratio))
+
+
+def version() -> str:
+    return lib().qsa_version().decode()
+
+
+def compress_keys(k_idx: torch.Tensor, ratio: int, batch: Batch, kc: torch.Tensor,
+                  kc_scale: Optional[torch.Tensor] = None, first_block: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    """qsa_compress_keys: writes kc (f32, bf16, or uint8 e4m3 codes) [+ kc_scale]."""
+    _dev(k_idx, "k_idx")
+    _dev(kc, "kc")
+    kcd = QSA_FP8_E4M3 if kc.dtype == torch.uint8 else _dtype_code(kc)
+    b = batch._c()
+    _check(lib().qsa_compress_keys(_ptr(k_idx), _dtype_code(k_idx), k_idx.shape[-1], ratio,
+                                   ctypes.byref(b), _ptr(first_block), _ptr(kc), kcd,
+                                   _ptr(kc_scale), _stream(stream)))
+
+
+def _indexer(q_idx, w, kc, kc_scale) -> _Indexer:
+    for t, n in ((q_idx, "q_idx"), (w, "w"), (kc, "kc")):
+        _dev(t, n)
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    kcd = QSA_FP8_E4M3 if kc.dtype == torch.uint8 else _dtype_code(kc)
+    return _Indexer(q_idx.data_ptr(), w.data_ptr(), kc.data_ptr(),
+                    None if kc_scale is None else kc_scale.data_ptr(), _dtype_code(q_idx), kcd,
+                    q_idx.shape[1], q_idx.shape[2])
+
+
+def index_score(q_idx, w, kc, kc_scale, ratio: int, batch: Batch, scores: torch.Tensor,
+                mode: int = QSA_SCORE_CANONICAL, stream=None) -> None:
+    """qsa_index_score into scores [total_q, ld]."""
+    _dev(scores, "scores")
+    ix = _indexer(q_idx, w, kc, kc_scale)
+    b = batch._c()
+    _check(lib().qsa_index_score(ctypes.byref(ix), ratio, ctypes.byref(b), _ptr(scores),
+                                 scores.shape[1], mode, _stream(stream)))
+
+
+def topk_workspace_size(batch: Batch, budget: int, ratio: int, recheck=None) -> int:
+    b = batch._c()
+    ix = None if recheck is None else _indexer(*recheck)
+    return int(lib().qsa_topk_workspace_size(ctypes.byref(b), budget, ratio,
+                                             None if ix is None else ctypes.byref(ix)))
+
+
+def topk_blocks(scores, budget: int, ratio: int, batch: Batch, idx: torch.Tensor,
+                recheck=None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """qsa_topk_blocks into idx [total_q, budget/ratio] int32.  `recheck` is the
+    tuple (q_idx, w, kc, kc_scale) when scores came from QSA_SCORE_MFMA."""
+    _dev(scores, "scores")
+    _dev(idx, "idx")
+    b = batch._c()
+    ix = None if recheck is None else _indexer(*recheck)
+    _check(lib().qsa_topk_blocks(_ptr(scores), scores.shape[1],
+                                 None if ix is None else ctypes.byref(ix), budget, ratio,
+                                 ctypes.byref(b), _ptr(idx), _ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(stream)))
+
+
+def _attn(q, k, v, softmax_scale) -> _Attn:
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    return _Attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), q.shape[1], k.shape[1],
+                 q.shape[2], float(softmax_scale))
+
+
+def attn_workspace_size(q, k, v, softmax_scale, budget: int, ratio: int, batch: Batch) -> int:
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    return int(lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), budget, ratio))
+
+
+def _attn_call(fn, q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws, stream):
+    _dev(idx, "idx")
+    _dev(out, "out")
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    _check(fn(ctypes.byref(a), _ptr(idx), budget, ratio, ctypes.byref(b), _ptr(out), _ptr(ws),
+              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sparse_attn_decode(q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws=None,
+                       stream=None) -> None:
+    _attn_call(lib().qsa_sparse_attn_decode, q, k, v, softmax_scale, idx, budget, ratio, batch,
+               out, ws, stream)
+
+
+def sparse_attn_prefill(q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws=None,
+                        stream=None) -> None:
+    _attn_call(lib().qsa_sparse_attn_prefill, q, k, v, softmax_scale, idx, budget, ratio, batch,
+               out, ws, stream)

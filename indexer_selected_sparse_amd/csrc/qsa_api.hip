@@ -1,0 +1,269 @@
+// C ABI of libqsa: argument validation, error reporting and dispatch.
+// Every entry point validates on the host before anything is enqueued; on
+// error nothing is enqueued, outputs are untouched and qsa_last_error()
+// names the offending argument and the limit.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "qsa_internal.hpp"
+
+namespace qsa {
+
+static thread_local char g_err[512] = "";
+
+static qsa_status fail(qsa_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    if (trace_enabled()) fprintf(stderr, "[qsa] error %d: %s\n", (int)s, g_err);
+    return s;
+}
+
+static qsa_status ok() {
+    g_err[0] = '\0';
+    return QSA_OK;
+}
+
+static qsa_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(QSA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool trace_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char *s = getenv("QSA_TRACE");
+        v = (s && s[0] && s[0] != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+void trace(const char *fmt, ...) {
+    if (!trace_enabled()) return;
+    va_list ap;
+    va_start(ap, fmt);
+    fprintf(stderr, "[qsa] ");
+    vfprintf(stderr, fmt, ap);
+    fprintf(stderr, "\n");
+    va_end(ap);
+}
+
+static bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Largest number of complete blocks one row may hold (top-k keeps at most
+// 128 per thread of a 1024-thread workgroup).
+static constexpr int64_t kMaxBlocksPerRow = 131072;
+
+static qsa_status check_batch(const qsa_batch *b, bool need_blk) {
+    if (!b) return fail(QSA_ERR_INVALID_ARGUMENT, "batch is NULL");
+    if (b->num_seqs < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "batch.num_seqs=%d must be >= 1", b->num_seqs);
+    if (b->num_seqs > 65535)
+        return fail(QSA_ERR_UNSUPPORTED, "batch.num_seqs=%d exceeds 65535", b->num_seqs);
+    if (!b->kv_offsets) return fail(QSA_ERR_INVALID_ARGUMENT, "batch.kv_offsets is NULL");
+    if (need_blk && !b->blk_offsets) return fail(QSA_ERR_INVALID_ARGUMENT, "batch.blk_offsets is NULL");
+    if (b->max_kv_len < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "batch.max_kv_len=%lld < 0", (long long)b->max_kv_len);
+    if (b->total_q < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "batch.total_q=%lld < 0", (long long)b->total_q);
+    if (b->q_offsets == nullptr && b->total_q != b->num_seqs)
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "batch.q_offsets is NULL (one query per sequence) but total_q=%lld != num_seqs=%d",
+                    (long long)b->total_q, b->num_seqs);
+    if (b->q_offsets != nullptr && b->max_q_per_seq < 1 && b->total_q > 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "batch.max_q_per_seq=%d must be >= 1", b->max_q_per_seq);
+    if (b->total_q > 0x7fffffffLL)
+        return fail(QSA_ERR_UNSUPPORTED, "batch.total_q=%lld exceeds 2^31-1", (long long)b->total_q);
+    return ok();
+}
+
+static qsa_status check_ratio(int32_t ratio) {
+    if (!is_pow2(ratio) || ratio > 64)
+        return fail(QSA_ERR_UNSUPPORTED, "ratio=%d must be a power of two in [1, 64]", ratio);
+    return ok();
+}
+
+static qsa_status check_budget(int32_t budget, int32_t ratio) {
+    qsa_status s = check_ratio(ratio);
+    if (s != QSA_OK) return s;
+    if (budget <= 0 || budget % ratio != 0)
+        return fail(QSA_ERR_UNSUPPORTED, "budget=%d must be a positive multiple of ratio=%d", budget, ratio);
+    const int32_t K = budget / ratio;
+    if (K < 1 || K > 2048)
+        return fail(QSA_ERR_UNSUPPORTED, "budget/ratio=%d must be in [1, 2048]", K);
+    return ok();
+}
+
+static qsa_status check_rows(const qsa_batch *b, int32_t ratio) {
+    const int64_t max_nb = b->max_kv_len / ratio;
+    if (max_nb > kMaxBlocksPerRow)
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "max_kv_len/ratio=%lld exceeds %lld complete blocks per sequence",
+                    (long long)max_nb, (long long)kMaxBlocksPerRow);
+    return ok();
+}
+
+static qsa_status check_indexer(const qsa_indexer *ix, bool mfma) {
+    if (!ix) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer is NULL");
+    if (!ix->q_idx) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.q_idx is NULL");
+    if (!ix->w) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.w is NULL");
+    if (!ix->kc) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc is NULL");
+    if (ix->q_dtype != QSA_F32 && ix->q_dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "indexer.q_dtype=%d must be QSA_F32 or QSA_BF16", ix->q_dtype);
+    if (ix->kc_dtype != QSA_F32 && ix->kc_dtype != QSA_BF16 && ix->kc_dtype != QSA_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "indexer.kc_dtype=%d is not a qsa_dtype", ix->kc_dtype);
+    if (ix->kc_dtype == QSA_FP8_E4M3 && !ix->kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc_scale is NULL but kc_dtype is QSA_FP8_E4M3");
+    if (ix->kc_dtype != QSA_FP8_E4M3 && ix->kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc_scale must be NULL unless kc_dtype is QSA_FP8_E4M3");
+    if (ix->h_idx != 1 && ix->h_idx != 2 && ix->h_idx != 4 && ix->h_idx != 8 && ix->h_idx != 16)
+        return fail(QSA_ERR_UNSUPPORTED, "indexer.h_idx=%d must be 1, 2, 4, 8 or 16", ix->h_idx);
+    if (ix->d_idx != 64 && ix->d_idx != 128)
+        return fail(QSA_ERR_UNSUPPORTED, "indexer.d_idx=%d must be 64 or 128", ix->d_idx);
+    if (mfma && (ix->q_dtype != QSA_BF16 || ix->kc_dtype != QSA_BF16))
+        return fail(QSA_ERR_UNSUPPORTED, "QSA_SCORE_MFMA needs bf16 q_idx and bf16 kc");
+    return ok();
+}
+
+static qsa_status check_attn(const qsa_attn *a) {
+    if (!a) return fail(QSA_ERR_INVALID_ARGUMENT, "attn is NULL");
+    if (!a->q || !a->k || !a->v) return fail(QSA_ERR_INVALID_ARGUMENT, "attn.q/k/v must not be NULL");
+    if (a->dtype != QSA_F32 && a->dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "attn.dtype=%d must be QSA_F32 or QSA_BF16", a->dtype);
+    if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv != 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "attn.hq=%d must be a positive multiple of attn.hkv=%d", a->hq, a->hkv);
+    const int G = a->hq / a->hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(QSA_ERR_UNSUPPORTED, "attn.hq/attn.hkv=%d must be 1, 2, 4, 8 or 16", G);
+    if (a->d != 128) return fail(QSA_ERR_UNSUPPORTED, "attn.d=%d must be 128", a->d);
+    if (!(a->softmax_scale > 0.0f) || a->softmax_scale > 1e30f)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "attn.softmax_scale must be finite and > 0");
+    return ok();
+}
+
+static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                              const qsa_batch *b, void *out, void *ws, size_t ws_bytes, bool decode,
+                              hipStream_t st) {
+    qsa_status s = check_attn(a);
+    if (s == QSA_OK) s = check_batch(b, false);
+    if (s == QSA_OK) s = check_budget(budget, ratio);
+    if (s != QSA_OK) return s;
+    if (!idx) return fail(QSA_ERR_INVALID_ARGUMENT, "idx is NULL");
+    if (!out) return fail(QSA_ERR_INVALID_ARGUMENT, "out is NULL");
+    if (decode && b->q_offsets != nullptr && b->max_q_per_seq != 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "decode takes one query per sequence (q_offsets NULL or max_q_per_seq == 1); "
+                    "use qsa_sparse_attn_prefill for max_q_per_seq=%d", b->max_q_per_seq);
+    const size_t need = decode ? attn_workspace_bytes(*b, *a, budget, ratio) : 0;
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
+                    "(qsa_attn_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return hip_status(launch_attn(*a, idx, budget, ratio, *b, out, ws, decode, st),
+                      "sparse attention launch");
+}
+
+}  // namespace qsa
+
+using namespace qsa;
+
+extern "C" {
+
+int32_t qsa_inert_bound(int32_t budget, int32_t ratio) {
+    if (budget <= 0 || ratio <= 0) return -1;
+    return budget + ratio - 1;
+}
+
+const char *qsa_last_error(void) { return g_err; }
+
+const char *qsa_version(void) { return "qsa 0.1.0 (abi 1, gfx950)"; }
+
+int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                             const qsa_batch *b, const int64_t *first_block, void *kc,
+                             int32_t kc_dtype, float *kc_scale, void *stream) {
+    qsa_status s = check_batch(b, true);
+    if (s != QSA_OK) return s;
+    if (!k_idx) return fail(QSA_ERR_INVALID_ARGUMENT, "k_idx is NULL");
+    if (!kc) return fail(QSA_ERR_INVALID_ARGUMENT, "kc is NULL");
+    s = check_ratio(ratio);
+    if (s != QSA_OK) return s;
+    if (k_dtype != QSA_F32 && k_dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "k_dtype=%d must be QSA_F32 or QSA_BF16", k_dtype);
+    if (kc_dtype != QSA_F32 && kc_dtype != QSA_BF16 && kc_dtype != QSA_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "kc_dtype=%d is not a qsa_dtype", kc_dtype);
+    if (kc_dtype == QSA_FP8_E4M3 && !kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "kc_scale is NULL but kc_dtype is QSA_FP8_E4M3");
+    if (d_idx != 64 && d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d must be 64 or 128", d_idx);
+    if ((b->max_kv_len / ratio) > 0xffffffffLL * 16)
+        return fail(QSA_ERR_UNSUPPORTED, "max_kv_len=%lld is too large", (long long)b->max_kv_len);
+    return hip_status(launch_compress(k_idx, k_dtype, d_idx, ratio, *b, first_block, kc, kc_dtype,
+                                      kc_scale, (hipStream_t)stream),
+                      "qsa_compress_keys launch");
+}
+
+qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b, float *scores,
+                           int64_t ld_scores, uint32_t flags, void *stream) {
+    if (flags != QSA_SCORE_CANONICAL && flags != QSA_SCORE_MFMA)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "flags=%u must be QSA_SCORE_CANONICAL or QSA_SCORE_MFMA", flags);
+    const bool mfma = flags == QSA_SCORE_MFMA;
+    qsa_status s = check_indexer(ix, mfma);
+    if (s == QSA_OK) s = check_batch(b, true);
+    if (s == QSA_OK) s = check_ratio(ratio);
+    if (s == QSA_OK) s = check_rows(b, ratio);
+    if (s != QSA_OK) return s;
+    if (!scores) return fail(QSA_ERR_INVALID_ARGUMENT, "scores is NULL");
+    const int64_t need_ld = (b->max_kv_len + ratio - 1) / ratio;
+    if (ld_scores < need_ld || ld_scores < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
+                    (long long)ld_scores, (long long)need_ld);
+    hipError_t e = mfma ? launch_score_mfma(*ix, ratio, *b, scores, ld_scores, (hipStream_t)stream)
+                        : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, (hipStream_t)stream);
+    return hip_status(e, "qsa_index_score launch");
+}
+
+size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio,
+                               const qsa_indexer *recheck) {
+    if (!b || check_budget(budget, ratio) != QSA_OK) return 0;
+    return topk_workspace_bytes(*b, budget, ratio, recheck);
+}
+
+qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
+                           int32_t budget, int32_t ratio, const qsa_batch *b, int32_t *idx,
+                           void *ws, size_t ws_bytes, void *stream) {
+    qsa_status s = check_batch(b, recheck != nullptr);
+    if (s == QSA_OK) s = check_budget(budget, ratio);
+    if (s == QSA_OK) s = check_rows(b, ratio);
+    if (s == QSA_OK && recheck) s = check_indexer(recheck, false);
+    if (s != QSA_OK) return s;
+    if (!scores) return fail(QSA_ERR_INVALID_ARGUMENT, "scores is NULL");
+    if (!idx) return fail(QSA_ERR_INVALID_ARGUMENT, "idx is NULL");
+    const int64_t need_ld = (b->max_kv_len + ratio - 1) / ratio;
+    if (ld_scores < need_ld || ld_scores < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
+                    (long long)ld_scores, (long long)need_ld);
+    const size_t need = topk_workspace_bytes(*b, budget, ratio, recheck);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(QSA_ERR_WORKSPACE, "top-k workspace of %zu bytes is smaller than the %zu required "
+                    "(qsa_topk_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return hip_status(launch_topk(scores, ld_scores, recheck, budget, ratio, *b, idx, ws,
+                                  (hipStream_t)stream),
+                      "qsa_topk_blocks launch");
+}
+
+size_t qsa_attn_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t budget, int32_t ratio) {
+    if (!b || !a || check_budget(budget, ratio) != QSA_OK || a->hkv < 1) return 0;
+    return attn_workspace_bytes(*b, *a, budget, ratio);
+}
+
+qsa_status qsa_sparse_attn_decode(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                                  const qsa_batch *b, void *out, void *ws, size_t ws_bytes, void *stream) {
+    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, true, (hipStream_t)stream);
+}
+
+qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                                   const qsa_batch *b, void *out, void *ws, size_t ws_bytes, void *stream) {
+    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, false, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// Key compression: one mean-pooled indexer key per complete block of `ratio`
+// tokens ("Agentic shootout" page, report "Flash-Next support: vLLM vs Atlas",
+// section (a)6: one compressed key per complete group; "PR 16 review",
+// section (a): 4-token mean-pooled blocks), stored as fp32, bf16 or OCP e4m3
+// with one fp32 scale max|x|/448 per block (the e4m3 index plane of the
+// long-context decode workload).
+//
+// A streaming HBM pass: each wave owns whole blocks; a lane owns DPL
+// consecutive dims of the d_idx-wide row, so every row load of the wave is one
+// contiguous, coalesced 128..512-byte segment.  Sum in row order in fp32, then
+// times 1/ratio (exact for a power-of-two ratio, identical to dividing).
+#include "qsa_device.hpp"
+#include "qsa_internal.hpp"
+
+namespace qsa {
+namespace {
+
+constexpr int kCompressWaves = 4;        // waves per workgroup
+constexpr int kBlocksPerWave = 4;        // blocks a wave handles (loads issued together)
+
+template <typename TIn, int DPL>
+__device__ __forceinline__ void load_row(const TIn *__restrict__ p, float (&x)[DPL]);
+
+template <>
+__device__ __forceinline__ void load_row<uint16_t, 1>(const uint16_t *__restrict__ p, float (&x)[1]) {
+    x[0] = bf16_to_f32(p[0]);
+}
+template <>
+__device__ __forceinline__ void load_row<uint16_t, 2>(const uint16_t *__restrict__ p, float (&x)[2]) {
+    uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+    x[0] = bf16lo(u);
+    x[1] = bf16hi(u);
+}
+template <>
+__device__ __forceinline__ void load_row<float, 1>(const float *__restrict__ p, float (&x)[1]) {
+    x[0] = p[0];
+}
+template <>
+__device__ __forceinline__ void load_row<float, 2>(const float *__restrict__ p, float (&x)[2]) {
+    float2 v = *reinterpret_cast<const float2 *>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+}
+
+// KC: 0 = fp32, 1 = bf16, 2 = e4m3 (+ scale)
+template <typename TIn, int DPL, int KC>
+__global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
+    const TIn *__restrict__ k_idx, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ blk_off, const int64_t *__restrict__ first_block, int log2_ratio,
+    float inv_ratio, void *__restrict__ kc, float *__restrict__ kc_scale) {
+    constexpr int D = DPL * kWave;
+    const int s = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int ratio = 1 << log2_ratio;
+    const int64_t row0 = kv_off[s];
+    const int64_t nb = (kv_off[s + 1] - row0) >> log2_ratio;
+    const int64_t fb = first_block ? first_block[s] : 0;
+    const int64_t out0 = blk_off[s];
+    const int64_t b_base =
+        ((int64_t)blockIdx.x * kCompressWaves + wave) * kBlocksPerWave;
+
+    for (int u = 0; u < kBlocksPerWave; ++u) {
+        const int64_t b = b_base + u;
+        if (b >= nb || b < fb) continue;
+        const TIn *src = k_idx + (row0 + (b << log2_ratio)) * D + lane * DPL;
+        float acc[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+        for (int j = 0; j < ratio; ++j) {
+            float x[DPL];
+            load_row<TIn, DPL>(src + (int64_t)j * D, x);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[e];
+        }
+        float m[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) m[e] = acc[e] * inv_ratio;
+        const int64_t o = (out0 + b) * D + lane * DPL;
+        if constexpr (KC == 0) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) static_cast<float *>(kc)[o + e] = m[e];
+        } else if constexpr (KC == 1) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                static_cast<uint16_t *>(kc)[o + e] = (uint16_t)f32_to_bf16_bits(m[e]);
+        } else {
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(m[e]));
+            amax = wave_max(amax);
+            const float scale = amax / 448.0f;    // correctly rounded division
+            if (lane == 0) kc_scale[out0 + b] = scale;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                uint32_t c = 0;
+                if (scale != 0.0f) {
+                    float y = m[e] / scale;
+                    y = fminf(fmaxf(y, -448.0f), 448.0f);
+                    c = f32_to_e4m3(y);
+                }
+                static_cast<uint8_t *>(kc)[o + e] = (uint8_t)c;
+            }
+        }
+    }
+}
+
+template <typename TIn, int DPL>
+hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb, int log2r,
+                       void *kc, int kc_dtype, float *kc_scale, dim3 grid, hipStream_t st) {
+    const float inv = 1.0f / (float)(1 << log2r);
+    const TIn *x = static_cast<const TIn *>(k_idx);
+    dim3 block(kCompressWaves * kWave);
+    switch (kc_dtype) {
+    case QSA_F32:
+        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 0>), grid, block, 0, st, x, b.kv_offsets,
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale);
+        break;
+    case QSA_BF16:
+        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 1>), grid, block, 0, st, x, b.kv_offsets,
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale);
+        break;
+    default:
+        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 2>), grid, block, 0, st, x, b.kv_offsets,
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
+                           const int64_t *first_block, void *kc, int kc_dtype, float *kc_scale,
+                           hipStream_t st) {
+    const int log2r = __builtin_ctz((unsigned)ratio);
+    const int64_t max_nb = b.max_kv_len >> log2r;
+    const int64_t per_wg = (int64_t)kCompressWaves * kBlocksPerWave;
+    if (max_nb <= 0) return hipSuccess;
+    dim3 grid((unsigned)((max_nb + per_wg - 1) / per_wg), (unsigned)b.num_seqs);
+    trace("compress grid=(%u,%u) d_idx=%d ratio=%d k_dtype=%d kc_dtype=%d", grid.x, grid.y, d_idx,
+          ratio, k_dtype, kc_dtype);
+    const bool bf = (k_dtype == QSA_BF16);
+    if (d_idx == 64)
+        return bf ? dispatch_kc<uint16_t, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st)
+                  : dispatch_kc<float, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st);
+    return bf ? dispatch_kc<uint16_t, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st)
+              : dispatch_kc<float, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st);
+}
+
+}  // namespace qsa

@@ -1,0 +1,43 @@
+// Internal launcher declarations of libqsa (host side).  Every launcher is
+// called only after the C-ABI layer has validated its arguments; launchers
+// enqueue work on `st` and return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+// Key compression (mean-pool of complete blocks).
+hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
+                           const int64_t *first_block, void *kc, int kc_dtype, float *kc_scale,
+                           hipStream_t st);
+
+// Canonical (bit-defined) indexer scores, decode and prefill.
+hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
+                                  float *scores, int64_t ld, hipStream_t st);
+
+// Matrix-core indexer scores (bf16 only), prefill.
+hipError_t launch_score_mfma(const qsa_indexer &ix, int ratio, const qsa_batch &b, float *scores,
+                             int64_t ld, hipStream_t st);
+
+// Block top-k.  recheck == nullptr: scores are canonical.
+size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa_indexer *recheck);
+hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *recheck, int budget,
+                       int ratio, const qsa_batch &b, int32_t *idx, void *ws, hipStream_t st);
+
+// Sparse gather attention (decode and prefill share the kernel).
+int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio, bool decode);
+// Workspace of the decode entry point (prefill needs none).
+size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio);
+hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ratio,
+                       const qsa_batch &b, void *out, void *ws, bool decode, hipStream_t st);
+
+// Host tracing (QSA_TRACE=1): one line per launch on stderr.
+bool trace_enabled();
+void trace(const char *fmt, ...);
+
+}  // namespace qsa

@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/qsa.h declares, and rejects bad arguments on the host with the
+documented status codes before touching a device (all pointers below are
+never dereferenced)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import indexer_selected_sparse_amd as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a non-null address that validation never dereferences
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    L = Q.lib()
+    names = header_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
+    assert set(names) == set(Q.EXPORTS)
+    out = os.popen(f"nm -D --defined-only {Q.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_versions_and_inert_bound():
+    assert Q.lib().qsa_abi_version() == 1
+    assert "gfx950" in Q.version()
+    with open(os.path.join(ROOT, "tests", "golden", "page_constants.json")) as f:
+        page = json.load(f)
+    ib = page["inert_bound"]
+    assert Q.inert_bound(ib["budget"], ib["ratio"]) == ib["value"] == 2051
+    assert Q.inert_bound(8192, 4) == 8195
+    assert Q.inert_bound(0, 4) == -1 and Q.inert_bound(2048, 0) == -1
+
+
+def _batch(**kw):
+    d = dict(num_seqs=2, max_q_per_seq=1, total_q=2, max_kv_len=4096, kv_offsets=FAKE,
+             blk_offsets=FAKE, q_offsets=None)
+    d.update(kw)
+    return Q._Batch(**d)
+
+
+def _ix(**kw):
+    d = dict(q_idx=FAKE, w=FAKE, kc=FAKE, kc_scale=None, q_dtype=Q.QSA_BF16,
+             kc_dtype=Q.QSA_BF16, h_idx=8, d_idx=128)
+    d.update(kw)
+    return Q._Indexer(**d)
+
+
+def _attn(**kw):
+    d = dict(q=FAKE, k=FAKE, v=FAKE, dtype=Q.QSA_BF16, hq=32, hkv=4, d=128,
+             softmax_scale=0.0883883)
+    d.update(kw)
+    return Q._Attn(**d)
+
+
+def _err():
+    return Q.lib().qsa_last_error().decode()
+
+
+P = ctypes.c_void_p
+
+
+def score(ix=None, ratio=4, b=None, scores=FAKE, ld=1024, flags=0):
+    ix = ix or _ix()
+    b = b or _batch()
+    return Q.lib().qsa_index_score(ctypes.byref(ix), ratio, ctypes.byref(b), P(scores), ld, flags, None)
+
+
+def topk(scores=FAKE, ld=1024, recheck=None, budget=2048, ratio=4, b=None, idx=FAKE, ws=None, nws=0):
+    b = b or _batch()
+    return Q.lib().qsa_topk_blocks(P(scores), ld, None if recheck is None else ctypes.byref(recheck),
+                                   budget, ratio, ctypes.byref(b), P(idx), P(ws), nws, None)
+
+
+def decode(a=None, idx=FAKE, budget=2048, ratio=4, b=None, out=FAKE, ws=FAKE, nws=1 << 30):
+    a = a or _attn()
+    b = b or _batch()
+    return Q.lib().qsa_sparse_attn_decode(ctypes.byref(a), P(idx), budget, ratio, ctypes.byref(b),
+                                          P(out), P(ws), nws, None)
+
+
+def prefill(a=None, idx=FAKE, budget=2048, ratio=4, b=None, out=FAKE, ws=None, nws=0):
+    a = a or _attn()
+    b = b or _batch()
+    return Q.lib().qsa_sparse_attn_prefill(ctypes.byref(a), P(idx), budget, ratio,
+                                           ctypes.byref(b), P(out), P(ws), nws, None)
+
+
+def compress(k=FAKE, kdt=Q.QSA_BF16, d=128, ratio=4, b=None, kc=FAKE, kcdt=Q.QSA_BF16, scale=None):
+    b = b or _batch()
+    return Q.lib().qsa_compress_keys(P(k), kdt, d, ratio, ctypes.byref(b), None, P(kc), kcdt,
+                                     P(scale), None)
+
+
+INV, UNS, WS = Q.QSA_ERR_INVALID_ARGUMENT, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
+
+CASES = [
+    # (name, thunk, expected status, fragment of the message)
+    ("compress null k_idx", lambda: compress(k=None), INV, "k_idx"),
+    ("compress ratio 3", lambda: compress(ratio=3), UNS, "ratio=3"),
+    ("compress ratio 128", lambda: compress(ratio=128), UNS, "ratio=128"),
+    ("compress d_idx 96", lambda: compress(d=96), UNS, "d_idx=96"),
+    ("compress e4m3 without scale", lambda: compress(kcdt=Q.QSA_FP8_E4M3), INV, "kc_scale"),
+    ("compress num_seqs 0", lambda: compress(b=_batch(num_seqs=0)), INV, "num_seqs"),
+    ("compress missing blk_offsets", lambda: compress(b=_batch(blk_offsets=None)), INV, "blk_offsets"),
+    ("score bad flags", lambda: score(flags=7), INV, "flags"),
+    ("score h_idx 3", lambda: score(ix=_ix(h_idx=3)), UNS, "h_idx=3"),
+    ("score d_idx 32", lambda: score(ix=_ix(d_idx=32)), UNS, "d_idx=32"),
+    ("score scale without e4m3", lambda: score(ix=_ix(kc_scale=FAKE)), INV, "kc_scale"),
+    ("score q fp8", lambda: score(ix=_ix(q_dtype=Q.QSA_FP8_E4M3)), UNS, "q_dtype"),
+    ("score ld too small", lambda: score(ld=1023), INV, "ld_scores"),
+    ("score mfma f32", lambda: score(ix=_ix(q_dtype=Q.QSA_F32), flags=1), UNS, "MFMA"),
+    ("score total_q mismatch", lambda: score(b=_batch(total_q=3)), INV, "total_q"),
+    ("score too many blocks", lambda: score(b=_batch(max_kv_len=4 * 131073), ld=131073), UNS, "131072"),
+    ("topk budget not multiple", lambda: topk(budget=2047), UNS, "budget=2047"),
+    ("topk K too large", lambda: topk(budget=4 * 4096), UNS, "budget/ratio=4096"),
+    ("topk null idx", lambda: topk(idx=None), INV, "idx"),
+    ("topk null scores", lambda: topk(scores=None), INV, "scores"),
+    ("decode hq not multiple", lambda: decode(a=_attn(hq=30)), INV, "attn.hq=30"),
+    ("decode group 32", lambda: decode(a=_attn(hq=64, hkv=2)), UNS, "hq/attn.hkv=32"),
+    ("decode d 64", lambda: decode(a=_attn(d=64)), UNS, "attn.d=64"),
+    ("decode fp8", lambda: decode(a=_attn(dtype=Q.QSA_FP8_E4M3)), UNS, "attn.dtype"),
+    ("decode bad scale", lambda: decode(a=_attn(softmax_scale=0.0)), INV, "softmax_scale"),
+    ("decode null out", lambda: decode(out=None), INV, "out"),
+    ("decode workspace missing", lambda: decode(ws=None, nws=0), WS, "workspace"),
+    ("decode workspace small", lambda: decode(nws=16), WS, "workspace"),
+    ("decode multi-query batch", lambda: decode(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)),
+     INV, "prefill"),
+    ("prefill null idx", lambda: prefill(idx=None), INV, "idx"),
+]
+
+
+@pytest.mark.parametrize("name,thunk,status,frag", CASES, ids=[c[0] for c in CASES])
+def test_validation_rejects_before_launch(name, thunk, status, frag):
+    assert thunk() == status
+    assert frag in _err(), _err()
+
+
+def test_workspace_sizes():
+    b = _batch(total_q=32, num_seqs=32)
+    a = _attn()
+    n = Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2048, 4)
+    # 16 splits of 32 blocks: (m, l) + 128 partial outputs per split and head
+    assert n >= 32 * 32 * 16 * 130 * 4
+    assert Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, None) == 0
+    assert Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2047, 4) == 0

@@ -1,0 +1,160 @@
+"""GPU parity: every entry point through the C ABI vs the CPU oracle.
+
+Compressed keys, canonical scores and selected block indices must match bit
+for bit; attention outputs must be within the stated tolerance of the fp64
+oracle.  Small cases span several workgroup tiles and ragged tails; the
+full-size cases use the benchmark's launch configuration and compare sampled
+queries.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import qsa_workloads as W
+from tests.parity import full_check, gpu_available, run_gpu
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------ small cases
+SMALL = [
+    # (spec, lens, n_q or None, overrides)
+    ("c1", W.C1, [4096], None, {}),
+    ("c1_ragged", W.C1, [1027, 4099, 333, 2], None, {"budget": 256}),
+    ("c2_small", W.C2, [3001, 1234, 777, 5002, 2049, 2052], None, {}),
+    ("c2_budget64", W.C2, [1500, 903, 64, 65, 3], None, {"budget": 64}),
+    ("c3_small_e4m3", W.C3, [6001, 3003, 1000], None, {"budget": 512}),
+    ("c4_small_prefill", W.C4, [1500], [300], {"budget": 256}),
+    ("c5_small_verify", W.C5, [2044, 2050, 2051, 2052, 2055, 2064], None, {}),
+    ("c5_full_shape", W.C5, None, None, {}),
+]
+
+
+@pytest.mark.parametrize("name,spec,lens,nq,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_configs(name, spec, lens, nq, over):
+    sp = dataclasses.replace(spec, **over) if over else spec
+    wl = W.make(sp, lens=lens, n_q=nq, seed=sp.seed + 100)
+    _print(f"[parity] {name}: lens={wl.lens[:6]} n_q={wl.n_q[:6]} budget={sp.budget}")
+    _, _, worst = full_check(wl)
+    _print(f"[parity] {name}: ok, worst err/limit = {worst:.3f}")
+
+
+DTYPES = [
+    ("q_f32_kc_f32", "f32", "f32", "f32"),
+    ("q_bf16_kc_bf16", "bf16", "bf16", "bf16"),
+    ("q_bf16_kc_e4m3", "bf16", "bf16", "e4m3"),
+    ("q_f32_kc_e4m3", "f32", "f32", "e4m3"),
+    ("q_bf16_kc_f32", "bf16", "bf16", "f32"),
+    ("q_f32_kc_bf16", "f32", "f32", "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,kv,idx_dt,kc_dt", DTYPES, ids=[d[0] for d in DTYPES])
+@pytest.mark.parametrize("h_idx,d_idx", [(1, 64), (2, 128), (4, 64), (8, 128), (16, 64), (16, 128)])
+def test_indexer_dtype_and_shape_matrix(name, kv, idx_dt, kc_dt, h_idx, d_idx):
+    sp = dataclasses.replace(W.C2, kv_dtype=kv, idx_dtype=idx_dt, kc_dtype=kc_dt, h_idx=h_idx,
+                             d_idx=d_idx, hq=8, hkv=2, budget=128)
+    wl = W.make(sp, lens=[900, 517, 131], seed=7)
+    full_check(wl)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (32, 2)])
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_gqa_group_sizes(hq, hkv, kv):
+    sp = dataclasses.replace(W.C2, hq=hq, hkv=hkv, kv_dtype=kv, budget=256)
+    wl = W.make(sp, lens=[1400, 77, 2100], seed=11)
+    full_check(wl)
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 8, 16, 64])
+def test_other_ratios(ratio):
+    sp = dataclasses.replace(W.C2, ratio=ratio, budget=64 * ratio, hq=8, hkv=1)
+    wl = W.make(sp, lens=[64 * ratio * 3 + ratio - 1, 100, ratio * 70 + 1], seed=13)
+    full_check(wl)
+
+
+def test_prefill_ragged_chunks_and_empty_sequence():
+    sp = dataclasses.replace(W.C4, budget=128)
+    wl = W.make(sp, lens=[700, 300, 90, 1025], n_q=[33, 0, 90, 1], seed=17)
+    full_check(wl)
+
+
+def test_equal_scores_pick_lowest_blocks():
+    sp = dataclasses.replace(W.C2, budget=256)
+    wl = W.make(sp, lens=[4000, 2000], seed=19)
+    wl.q_idx.zero_()                       # every score is +0: ties everywhere
+    res, ref, _ = full_check(wl)
+    assert np.array_equal(res["idx"][0], np.arange(64))
+    assert np.array_equal(res["idx"][1], np.arange(64))
+
+
+def test_nonpositive_scores_with_some_ties():
+    sp = dataclasses.replace(W.C2, budget=512)
+    wl = W.make(sp, lens=[6000, 3001], seed=23)
+    # half of the indexer heads get no weight, making many scores exactly 0
+    wl.w[:, ::2] = 0.0
+    full_check(wl)
+
+
+def test_decode_equals_prefill_row_and_two_chunks_equal_one():
+    sp = dataclasses.replace(W.C4, budget=256)
+    wl = W.make(sp, lens=[2500], n_q=[40], seed=29)
+    res_all, _ = run_gpu(wl)
+    # the same sequence as two chunks: the first 17 queries, then the rest
+    a = dataclasses.replace(wl)
+    cut = 17
+    first = W.Workload(sp, [wl.lens[0] - (40 - cut)], [cut], np.array([0, wl.lens[0] - 23]),
+                       np.array([0, cut]), wl.K[: wl.lens[0] - 23], wl.V[: wl.lens[0] - 23],
+                       wl.k_idx[: wl.lens[0] - 23], wl.q[:cut], wl.q_idx[:cut], wl.w[:cut])
+    second = W.Workload(sp, wl.lens, [40 - cut], wl.kv_offsets, np.array([0, 40 - cut]),
+                        wl.K, wl.V, wl.k_idx, wl.q[cut:], wl.q_idx[cut:], wl.w[cut:])
+    r1, _ = run_gpu(first)
+    r2, _ = run_gpu(second)
+    assert np.array_equal(np.concatenate([r1["idx"], r2["idx"]]), res_all["idx"])
+    assert np.array_equal(np.concatenate([r1["out"], r2["out"]]), res_all["out"])
+    # the last query alone, as a decode batch: same selection bits; the
+    # decode entry point splits the blocks, so the output agrees to fp32
+    # rounding rather than bit for bit
+    last = W.Workload(sp, wl.lens, [1], wl.kv_offsets, np.array([0, 1]), wl.K, wl.V, wl.k_idx,
+                      wl.q[39:], wl.q_idx[39:], wl.w[39:])
+    r3, _ = run_gpu(last, decode=True)
+    assert np.array_equal(r3["idx"][0], res_all["idx"][39])
+    assert np.allclose(r3["out"][0], res_all["out"][39], rtol=2e-2, atol=2e-3)
+    del a
+
+
+# ------------------------------------------------------------ full sizes
+def _sample(total, k, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set([0, total - 1]) | set(rng.choice(total, min(k, total), replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c5"])
+def test_full_size_all_queries(cfg):
+    wl = W.make(W.CONFIGS[cfg])
+    _print(f"[parity] full {cfg}: B={wl.num_seqs} total_q={wl.total_q} max_len={max(wl.lens)}")
+    _, _, worst = full_check(wl)
+    _print(f"[parity] full {cfg}: ok, worst err/limit = {worst:.3f}")
+
+
+def test_full_size_c3_long_context_e4m3():
+    wl = W.make(W.C3)
+    _print(f"[parity] full c3: B={wl.num_seqs} len={wl.lens[0]}")
+    _, _, worst = full_check(wl)
+    _print(f"[parity] full c3: ok, worst err/limit = {worst:.3f}")
+
+
+def test_full_size_c4_prefill_sampled():
+    wl = W.make(W.C4)
+    q = _sample(wl.total_q, 24, seed=4)
+    _print(f"[parity] full c4: total_q={wl.total_q}, sampled {len(q)} queries")
+    _, _, worst = full_check(wl, query_ids=q)
+    _print(f"[parity] full c4: ok, worst err/limit = {worst:.3f}")
