@@ -20,11 +20,10 @@
 //    each lane with full dots of G/8 heads (or a shared head for G < 8).
 //  * online softmax in fp32 (exp2 domain), one running max per head.
 //  * PV: lane p owns dims 2p, 2p+1 of every head; V rows are read as one
-//    coalesced 256-byte row per token; probabilities come through a small
-//    per-wave LDS slot.  bf16: probabilities of tokens t and t+8 are packed as
-//    a bf16 pair and paired V elements are formed with v_perm, so every
-//    v_dot2 consumes two tokens (the denominator sums the same rounded
-//    probabilities, so the weights stay an exact convex combination).
+//    coalesced row per token; fp32 probabilities come through a small
+//    per-wave LDS slot and meet fp32-widened V in plain FMAs.  (Rounding the
+//    probabilities to bf16 for a packed dot would cost up to 2^-8 relative per
+//    weight, which is visible when only a few tokens carry the softmax.)
 // With more than one split, unnormalised (m, l, o) partials go to the
 // workspace and a combine kernel merges them.
 #include "qsa_device.hpp"
@@ -143,9 +142,8 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     using T = typename KVTypes<BF16>::elem;
     constexpr int NH = G >= 8 ? G / 8 : 1;
     constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
-    // per-wave LDS: probabilities [G][8] (bf16 pairs) or [G][16] (fp32), alpha[G], l[G]
-    constexpr int PW = BF16 ? 8 : 16;
-    __shared__ uint32_t sh_p[kAttnWaves][G * PW];
+    // per-wave LDS: probabilities [G][16] (fp32), alpha[G], l[G]
+    __shared__ float sh_p[kAttnWaves][G * kStep];
     __shared__ float sh_alpha[kAttnWaves][G];
     __shared__ float sh_l[kAttnWaves][G];
 
@@ -275,15 +273,8 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
             alpha[h] = exp2f(m_run[h] - m_safe);
             float ea = exp2f(xa - m_safe), eb = exp2f(xb - m_safe);
             m_run[h] = m_new;
-            if constexpr (BF16) {
-                const uint32_t pk = pack_bf16x2(ea, eb);
-                ea = bf16lo(pk);
-                eb = bf16hi(pk);
-                sh_p[wave][(hb + h) * 8 + tk] = pk;
-            } else {
-                sh_p[wave][(hb + h) * 16 + tk] = __float_as_uint(ea);
-                sh_p[wave][(hb + h) * 16 + 8 + tk] = __float_as_uint(eb);
-            }
+            sh_p[wave][(hb + h) * kStep + tk] = ea;
+            sh_p[wave][(hb + h) * kStep + 8 + tk] = eb;
             l_run[h] = l_run[h] * alpha[h] + (ea + eb);
             if (tk == 0) sh_alpha[wave][hb + h] = alpha[h];
         }
@@ -296,30 +287,21 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
             o[h][0] *= al;
             o[h][1] *= al;
         }
-        if constexpr (BF16) {
-            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8) {
-                const uint32_t va = vt[t8][0], vb = vt[t8 + 8][0];
-                const uint32_t vlo = __builtin_amdgcn_perm(vb, va, 0x05040100u);
-                const uint32_t vhi = __builtin_amdgcn_perm(vb, va, 0x07060302u);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const bf2 pp = __builtin_bit_cast(bf2, sh_p[wave][h * 8 + t8]);
-                    o[h][0] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf2, vlo), o[h][0], false);
-                    o[h][1] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf2, vhi), o[h][1], false);
-                }
+        for (int tt = 0; tt < kStep; ++tt) {
+            float v0, v1;
+            if constexpr (BF16) {
+                v0 = bf16lo(vt[tt][0]);
+                v1 = bf16hi(vt[tt][0]);
+            } else {
+                v0 = __uint_as_float(vt[tt][0]);
+                v1 = __uint_as_float(vt[tt][1]);
             }
-        } else {
 #pragma unroll
-            for (int tt = 0; tt < kStep; ++tt) {
-                const float v0 = __uint_as_float(vt[tt][0]), v1 = __uint_as_float(vt[tt][1]);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float pp = __uint_as_float(sh_p[wave][h * 16 + tt]);
-                    o[h][0] = __builtin_fmaf(pp, v0, o[h][0]);
-                    o[h][1] = __builtin_fmaf(pp, v1, o[h][1]);
-                }
+            for (int h = 0; h < G; ++h) {
+                const float pp = sh_p[wave][h * kStep + tt];
+                o[h][0] = __builtin_fmaf(pp, v0, o[h][0]);
+                o[h][1] = __builtin_fmaf(pp, v1, o[h][1]);
             }
         }
         wave_lds_sync();

@@ -129,37 +129,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_canonical_kernel(
     float s = 0.0f;
 
     if constexpr (kExact) {
-        // bf16 query x (bf16 | e4m3) key.  Each product is exact in fp32, so
-        // the canonical step acc = fl(acc + q*k) is one correctly rounded
-        // operation.  It is issued as v_dot2_f32_bf16 with the packed query
-        // pair (q_d, q_d+1) straight from SGPRs and a key operand that holds
-        // k_d in one half and zero in the other: the second product is an
-        // exact zero, so the instruction yields fl(acc + q*k) for one d.
-        // Key operands: lo[j] = (k_2j, 0), hi[j] = (0, k_2j+1) as bf16 pairs.
-        uint32_t klo[D / 2], khi[D / 2];
+        // bf16 query x (bf16 | e4m3) key: every product is exact in fp32, so
+        // the canonical step acc = fl(acc + q*k) is one IEEE fused
+        // multiply-add.  The query pair (q_d, q_d+1) arrives as one dword in
+        // an SGPR and is widened by two scalar ops (shift / mask); the
+        // scheduling groups below interleave each scalar widening with its
+        // FMA so that only a few widened values are live at a time (scalar
+        // and vector ops of different waves issue in the same cycle).
+        float kf[D];
         {
             KRow<KT, D> k;
             k.load(kc + row * D);
             if constexpr (kE4M3) {
-                // e4m3 values have 4 significant bits: exact in bf16.
 #pragma unroll
                 for (int c = 0; c < D / 4; ++c) {
                     const float2 a = e4m3x2_to_f32<false>(k.u[c]);
                     const float2 bb = e4m3x2_to_f32<true>(k.u[c]);
-                    klo[2 * c] = __float_as_uint(a.x) >> 16;
-                    khi[2 * c] = __float_as_uint(a.y) & 0xffff0000u;
-                    klo[2 * c + 1] = __float_as_uint(bb.x) >> 16;
-                    khi[2 * c + 1] = __float_as_uint(bb.y) & 0xffff0000u;
+                    kf[4 * c] = a.x; kf[4 * c + 1] = a.y; kf[4 * c + 2] = bb.x; kf[4 * c + 3] = bb.y;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < D / 2; ++j) {
-                    klo[j] = k.u[j] & 0xffffu;
-                    khi[j] = k.u[j] & 0xffff0000u;
-                }
+                for (int d = 0; d < D; ++d) kf[d] = k.get(d);
             }
         }
-        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
         const uint32_t *__restrict__ q32 =
             reinterpret_cast<const uint32_t *>(q_idx) + i * (int64_t)(H * D / 2);
 #pragma unroll 1
@@ -167,9 +159,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_canonical_kernel(
             float dot = 0.0f;
 #pragma unroll
             for (int j = 0; j < D / 2; ++j) {
-                const bf2 qq = __builtin_bit_cast(bf2, q32[h * (D / 2) + j]);
-                dot = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf2, klo[j]), dot, false);
-                dot = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf2, khi[j]), dot, false);
+                const uint32_t u = q32[h * (D / 2) + j];
+                dot = __builtin_fmaf(bf16lo(u), kf[2 * j], dot);
+                dot = __builtin_fmaf(bf16hi(u), kf[2 * j + 1], dot);
+            }
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);   // one SALU op
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU op
             }
             if constexpr (kE4M3) dot = dot * sc;
             const float r = dot > 0.0f ? dot : 0.0f;

@@ -7,9 +7,19 @@ import torch
 
 import oracle
 
-# Output tolerances against the unrounded fp64 oracle (see DESIGN.md):
-#   bf16 output: |gpu - o| <= 1e-3 + 2e-3 |o|     fp32 output: <= 1e-5 + 1e-5 |o|
+# Output tolerances against the unrounded fp64 oracle:
+#   bf16 output: |gpu - o| <= 1e-3 + 2e-3 |o| + half_ulp_bf16(o)
+#   fp32 output: |gpu - o| <= 1e-5 + 1e-5 |o|
+# The absolute/relative terms bound the computed value; the stored bf16 output
+# is then rounded to nearest, which alone can move it by half a bf16 ulp (up
+# to 2^-8 |o|, more than the 2e-3 relative term for |o| just above a power of
+# two), so that quantisation is added explicitly.
 TOL = {"bf16": (1e-3, 2e-3), "f32": (1e-5, 1e-5)}
+
+
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, (np.floor(np.log2(ax)) - 8).astype(np.int64))
 
 
 def gpu_available() -> bool:
@@ -81,6 +91,8 @@ def check_out(wl, res, ref, query_ids):
     exp = ref["out"]
     err = np.abs(got - exp)
     lim = atol + rtol * np.abs(exp)
+    if wl.spec.kv_dtype == "bf16":
+        lim = lim + half_ulp_bf16(exp)
     worst = np.unravel_index(np.argmax(err - lim), err.shape)
     assert np.all(err <= lim), (f"output outside tolerance: worst at {worst}: gpu {got[worst]} "
                                 f"oracle {exp[worst]} err {err[worst]:.3g} lim {lim[worst]:.3g}")
