@@ -104,51 +104,215 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Token position of flat token t of this split (-1 if t is past the end).
-// A selected block outside [0, nb) (malformed idx) yields no token, so the
-// kernel never reads outside the query's visible rows.
-struct SplitTokens {
-    const int32_t *__restrict__ sel;  // idx row + first slot of the split
-    int64_t nblk_tok;                 // tokens coming from selected blocks
-    int64_t ntok;                     // + tail tokens
-    int64_t tail0;                    // first tail position (ratio * nb)
-    int64_t nb;                       // complete blocks visible to the query
-    int log2r;
-    __device__ __forceinline__ int64_t pos(int64_t t) const {
-        if (t >= ntok) return -1;
-        if (t < nblk_tok) {
-            const int64_t b = sel[t >> log2r];
-            if (b < 0 || b >= nb) return -1;
-            return (b << log2r) + (t & ((1 << log2r) - 1));
-        }
-        return tail0 + (t - nblk_tok);
-    }
-};
-
 template <bool BF16>
 struct KVTypes;
 template <>
 struct KVTypes<true> {
     using elem = uint16_t;
     static constexpr int kDwordsPerLaneK = 8;   // 16 bf16 dims
+    static constexpr int kDwordsPerLaneV = 1;   // 2 bf16 dims
 };
 template <>
 struct KVTypes<false> {
     using elem = float;
     static constexpr int kDwordsPerLaneK = 16;  // 16 fp32 dims
+    static constexpr int kDwordsPerLaneV = 2;   // 2 fp32 dims
 };
+
+// Registers of one 16-token step: the K slices of this lane's two QK tokens,
+// the V dims of every token, and which tokens exist.
+template <bool BF16>
+struct StepBuf {
+    static constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
+    static constexpr int VW = KVTypes<BF16>::kDwordsPerLaneV;
+    uint32_t kA[KW], kB[KW];
+    uint32_t v[kStep][VW];
+    uint32_t valid;          // wave-uniform bit mask over the 16 tokens
+};
+
+// Wave-uniform description of the tokens one wave processes.
+struct WaveWork {
+    const int32_t *__restrict__ sel;  // idx row + first slot of this split
+    int nslot;                        // selected slots of the split
+    int nblk_tok;                     // tokens from selected blocks
+    int ntok;                         // + tail tokens
+    int64_t tail0;                    // first tail position (ratio * nb)
+    int64_t nb;                       // complete blocks visible to the query
+    int log2r;
+};
+
+// Issue the loads of step `st`.  Lane t < 16 resolves token t0+t to a row of
+// the sequence (a selected block id from the slot table held one slot per
+// lane, or a tail position; malformed ids and positions past the end give
+// "no token" and read row 0).  K rows reach the QK lanes by a cross-lane
+// permute; V rows become wave-uniform addresses, so each V row is one
+// coalesced scalar-based load.
+template <bool BF16>
+__device__ __forceinline__ void issue_step(const WaveWork &W, int st, int lane, int tk, int ds,
+                                           uint32_t slot_tab, int tab_base,
+                                           const typename KVTypes<BF16>::elem *__restrict__ kbase,
+                                           const typename KVTypes<BF16>::elem *__restrict__ vbase,
+                                           int64_t row_stride, StepBuf<BF16> &B) {
+    using T = typename KVTypes<BF16>::elem;
+    constexpr int KW = StepBuf<BF16>::KW;
+    const int t = st * kStep + (lane & (kStep - 1));
+    // The permute runs with every lane active: a lane that is switched off
+    // does not supply its value to the others.
+    int rel = (t >> W.log2r) - tab_base;             // slot within the table
+    rel = rel < 0 ? 0 : (rel > kWave - 1 ? kWave - 1 : rel);
+    const int b = __builtin_amdgcn_ds_bpermute(rel << 2, (int)slot_tab);
+    int row = 0;
+    bool ok = false;
+    if (t < W.nblk_tok) {
+        ok = b >= 0 && (int64_t)b < W.nb;
+        row = ok ? (b << W.log2r) + (t & ((1 << W.log2r) - 1)) : 0;
+    } else if (t < W.ntok) {
+        row = (int)(W.tail0 + (t - W.nblk_tok));
+        ok = true;
+    }
+    const uint64_t okm = __ballot(ok && lane < kStep);
+    B.valid = (uint32_t)okm & 0xffffu;
+    // K: lane (tk, ds) takes tokens tk and tk+8
+    const int rA = __builtin_amdgcn_ds_bpermute(tk << 2, row);
+    const int rB = __builtin_amdgcn_ds_bpermute((tk + 8) << 2, row);
+    {
+        const uint4 *sa = reinterpret_cast<const uint4 *>(kbase + (int64_t)rA * row_stride + ds * 16);
+        const uint4 *sb = reinterpret_cast<const uint4 *>(kbase + (int64_t)rB * row_stride + ds * 16);
+#pragma unroll
+        for (int c4 = 0; c4 < KW / 4; ++c4) {
+            const uint4 x = sa[c4], y = sb[c4];
+            B.kA[4 * c4 + 0] = x.x; B.kA[4 * c4 + 1] = x.y; B.kA[4 * c4 + 2] = x.z; B.kA[4 * c4 + 3] = x.w;
+            B.kB[4 * c4 + 0] = y.x; B.kB[4 * c4 + 1] = y.y; B.kB[4 * c4 + 2] = y.z; B.kB[4 * c4 + 3] = y.w;
+        }
+    }
+    // V: one coalesced row per token, wave-uniform base address
+#pragma unroll
+    for (int tt = 0; tt < kStep; ++tt) {
+        const int r = __builtin_amdgcn_readlane(row, tt);
+        const T *src = vbase + (int64_t)r * row_stride;
+        if constexpr (BF16) {
+            B.v[tt][0] = reinterpret_cast<const uint32_t *>(src)[lane];
+        } else {
+            const uint2 x = reinterpret_cast<const uint2 *>(src)[lane];
+            B.v[tt][0] = x.x;
+            B.v[tt][1] = x.y;
+        }
+    }
+}
+
+template <bool BF16, int G>
+struct AttnState {
+    static constexpr int NH = G >= 8 ? G / 8 : 1;
+    float m_run[NH], l_run[NH];
+    float o[G][2];
+};
+
+// Consume one step: QK, online softmax, PV.
+template <bool BF16, int G>
+__device__ __forceinline__ void compute_step(const StepBuf<BF16> &B,
+                                             const uint32_t (&qr)[G][KVTypes<BF16>::kDwordsPerLaneK],
+                                             float c, int tk, int ds, int hb,
+                                             float (*sh_p)[G], float *sh_alpha,
+                                             AttnState<BF16, G> &S) {
+    constexpr int NH = AttnState<BF16, G>::NH;
+    constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
+    // ---- QK partial dots over this lane's 16 dims
+    float dA[G], dB[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float a = 0.0f, b = 0.0f;
+        if constexpr (BF16) {
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int e = 0; e < KW; ++e) {
+                const bf2 qv = __builtin_bit_cast(bf2, qr[h][e]);
+                a = __builtin_amdgcn_fdot2_f32_bf16(qv, __builtin_bit_cast(bf2, B.kA[e]), a, false);
+                b = __builtin_amdgcn_fdot2_f32_bf16(qv, __builtin_bit_cast(bf2, B.kB[e]), b, false);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KW; ++e) {
+                const float qv = __uint_as_float(qr[h][e]);
+                a = __builtin_fmaf(qv, __uint_as_float(B.kA[e]), a);
+                b = __builtin_fmaf(qv, __uint_as_float(B.kB[e]), b);
+            }
+        }
+        dA[h] = a;
+        dB[h] = b;
+    }
+    float sA[NH], sB[NH];
+    transpose_reduce<G>(dA, sA, ds);
+    transpose_reduce<G>(dB, sB, ds);
+
+    // ---- online softmax (exp2 domain), one running max per head
+    const bool okA = (B.valid >> tk) & 1u, okB = (B.valid >> (tk + 8)) & 1u;
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const float xa = okA ? sA[h] * c : -INFINITY;
+        const float xb = okB ? sB[h] * c : -INFINITY;
+        float mx = fmaxf(xa, xb);
+        mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float m_new = fmaxf(S.m_run[h], mx);
+        const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = exp2f(S.m_run[h] - m_safe);
+        rescale |= m_new != S.m_run[h];
+        const float ea = exp2f(xa - m_safe), eb = exp2f(xb - m_safe);
+        S.m_run[h] = m_new;
+        sh_p[tk][hb + h] = ea;
+        sh_p[tk + 8][hb + h] = eb;
+        S.l_run[h] = S.l_run[h] * alpha + (ea + eb);
+        if (tk == 0) sh_alpha[hb + h] = alpha;
+    }
+    const bool any_rescale = __ballot(rescale) != 0;
+    wave_lds_sync();
+
+    // ---- PV: lane owns dims 2*lane, 2*lane+1 of every head
+    if (any_rescale) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float al = sh_alpha[h];
+            S.o[h][0] *= al;
+            S.o[h][1] *= al;
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kStep; ++tt) {
+        float v0, v1;
+        if constexpr (BF16) {
+            v0 = bf16lo(B.v[tt][0]);
+            v1 = bf16hi(B.v[tt][0]);
+        } else {
+            v0 = __uint_as_float(B.v[tt][0]);
+            v1 = __uint_as_float(B.v[tt][1]);
+        }
+        float pv[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pv[h] = sh_p[tt][h];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            S.o[h][0] = __builtin_fmaf(pv[h], v0, S.o[h][0]);
+            S.o[h][1] = __builtin_fmaf(pv[h], v1, S.o[h][1]);
+        }
+    }
+    wave_lds_sync();
+}
 
 template <bool BF16, int G>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     using T = typename KVTypes<BF16>::elem;
-    constexpr int NH = G >= 8 ? G / 8 : 1;
+    constexpr int NH = AttnState<BF16, G>::NH;
     constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
-    // per-wave LDS: probabilities [G][16] (fp32), alpha[G], l[G]
-    __shared__ float sh_p[kAttnWaves][G * kStep];
+    __shared__ float sh_p[kAttnWaves][kStep][G];   // probabilities [token][head]
     __shared__ float sh_alpha[kAttnWaves][G];
     __shared__ float sh_l[kAttnWaves][G];
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // The wave index is uniform across the wave; saying so keeps everything
+    // derived from it (query, split, positions) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t wid = (int64_t)blockIdx.x * kAttnWaves + wave;
     const int g = (int)(wid % A.hkv);
     const int64_t t2 = wid / A.hkv;
@@ -162,13 +326,14 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     const int64_t per = (nsel + A.n_split - 1) / A.n_split;
     const int64_t s_beg = imin64((int64_t)c * per, nsel);
     const int64_t s_end = imin64(s_beg + per, nsel);
-    SplitTokens tok;
-    tok.sel = A.idx + i * (int64_t)A.K + s_beg;
-    tok.log2r = A.log2r;
-    tok.nblk_tok = (s_end - s_beg) << A.log2r;
-    tok.tail0 = nb << A.log2r;
-    tok.nb = nb;
-    tok.ntok = tok.nblk_tok + ((c == A.n_split - 1) ? (qp.L - tok.tail0) : 0);
+    WaveWork W;
+    W.sel = A.idx + i * (int64_t)A.K + s_beg;
+    W.nslot = (int)(s_end - s_beg);
+    W.log2r = A.log2r;
+    W.nblk_tok = W.nslot << A.log2r;
+    W.tail0 = nb << A.log2r;
+    W.nb = nb;
+    W.ntok = W.nblk_tok + ((c == A.n_split - 1) ? (int)(qp.L - W.tail0) : 0);
 
     const int tk = lane >> 3, ds = lane & 7;
     const int hb = head_base<G>(ds);
@@ -193,130 +358,55 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
         }
     }
 
-    float m_run[NH], l_run[NH];
+    AttnState<BF16, G> S;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.0f; }
-    float o[G][2];
+    for (int h = 0; h < NH; ++h) { S.m_run[h] = -INFINITY; S.l_run[h] = 0.0f; }
 #pragma unroll
-    for (int h = 0; h < G; ++h) { o[h][0] = 0.0f; o[h][1] = 0.0f; }
+    for (int h = 0; h < G; ++h) { S.o[h][0] = 0.0f; S.o[h][1] = 0.0f; }
 
-    const int64_t nsteps = (tok.ntok + kStep - 1) / kStep;
-    for (int64_t st = 0; st < nsteps; ++st) {
-        const int64_t t0 = st * kStep;
-        // ---- positions: lane's own QK tokens, and all 16 for PV
-        const int64_t pA = tok.pos(t0 + tk), pB = tok.pos(t0 + 8 + tk);
-        uint32_t kA[KW], kB[KW];
-        {
-            const uint4 *sa = reinterpret_cast<const uint4 *>(kbase + (pA < 0 ? 0 : pA) * row_stride + ds * 16);
-            const uint4 *sb = reinterpret_cast<const uint4 *>(kbase + (pB < 0 ? 0 : pB) * row_stride + ds * 16);
-#pragma unroll
-            for (int c4 = 0; c4 < KW / 4; ++c4) {
-                const uint4 x = sa[c4], y = sb[c4];
-                kA[4 * c4 + 0] = x.x; kA[4 * c4 + 1] = x.y; kA[4 * c4 + 2] = x.z; kA[4 * c4 + 3] = x.w;
-                kB[4 * c4 + 0] = y.x; kB[4 * c4 + 1] = y.y; kB[4 * c4 + 2] = y.z; kB[4 * c4 + 3] = y.w;
-            }
+    // Slot table: lane j holds selected block id of slot tab_base + j.
+    int tab_base = 0;
+    uint32_t slot_tab = (uint32_t)(lane < W.nslot ? W.sel[lane] : -1);
+    const int nsteps = (W.ntok + kStep - 1) / kStep;
+    // slots a step touches: [ (16*st) >> log2r, (16*st + 15) >> log2r ]
+    auto ensure_table = [&](int st) {
+        const int first = (st * kStep) >> W.log2r;
+        const int last = (st * kStep + kStep - 1) >> W.log2r;
+        if (st * kStep < W.nblk_tok && (first < tab_base || last >= tab_base + kWave)) {
+            tab_base = first;
+            slot_tab = (uint32_t)(tab_base + lane < W.nslot ? W.sel[tab_base + lane] : -1);
         }
-        // V: one row dword (bf16 pair) or two floats per token for PV lane p
-        uint32_t vt[kStep][BF16 ? 1 : 2];
-#pragma unroll
-        for (int tt = 0; tt < kStep; ++tt) {
-            const int64_t p = tok.pos(t0 + tt);
-            const T *src = vbase + (p < 0 ? 0 : p) * row_stride;
-            if constexpr (BF16) {
-                vt[tt][0] = reinterpret_cast<const uint32_t *>(src)[lane];
-            } else {
-                const uint2 x = reinterpret_cast<const uint2 *>(src)[lane];
-                vt[tt][0] = x.x; vt[tt][1] = x.y;
-            }
-        }
+    };
 
-        // ---- QK partial dots over this lane's 16 dims
-        float dA[G], dB[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float a = 0.0f, b = 0.0f;
-            if constexpr (BF16) {
-                typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-                for (int e = 0; e < KW; ++e) {
-                    const bf2 qv = __builtin_bit_cast(bf2, qr[h][e]);
-                    a = __builtin_amdgcn_fdot2_f32_bf16(qv, __builtin_bit_cast(bf2, kA[e]), a, false);
-                    b = __builtin_amdgcn_fdot2_f32_bf16(qv, __builtin_bit_cast(bf2, kB[e]), b, false);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < KW; ++e) {
-                    const float qv = __uint_as_float(qr[h][e]);
-                    a = __builtin_fmaf(qv, __uint_as_float(kA[e]), a);
-                    b = __builtin_fmaf(qv, __uint_as_float(kB[e]), b);
-                }
-            }
-            dA[h] = a;
-            dB[h] = b;
+    StepBuf<BF16> b0, b1;
+    if (nsteps > 0) {
+        ensure_table(0);
+        issue_step<BF16>(W, 0, lane, tk, ds, slot_tab, tab_base, kbase, vbase, row_stride, b0);
+    }
+    for (int st = 0; st < nsteps; st += 2) {
+        if (st + 1 < nsteps) {
+            ensure_table(st + 1);
+            issue_step<BF16>(W, st + 1, lane, tk, ds, slot_tab, tab_base, kbase, vbase, row_stride, b1);
         }
-        float sA[NH], sB[NH];
-        transpose_reduce<G>(dA, sA, ds);
-        transpose_reduce<G>(dB, sB, ds);
-
-        // ---- online softmax (exp2 domain), per head
-        float alpha[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const float xa = pA >= 0 ? sA[h] * A.c : -INFINITY;
-            const float xb = pB >= 0 ? sB[h] * A.c : -INFINITY;
-            float mx = fmaxf(xa, xb);
-            mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = fmaxf(m_run[h], mx);
-            const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
-            alpha[h] = exp2f(m_run[h] - m_safe);
-            float ea = exp2f(xa - m_safe), eb = exp2f(xb - m_safe);
-            m_run[h] = m_new;
-            sh_p[wave][(hb + h) * kStep + tk] = ea;
-            sh_p[wave][(hb + h) * kStep + 8 + tk] = eb;
-            l_run[h] = l_run[h] * alpha[h] + (ea + eb);
-            if (tk == 0) sh_alpha[wave][hb + h] = alpha[h];
+        compute_step<BF16, G>(b0, qr, A.c, tk, ds, hb, sh_p[wave], sh_alpha[wave], S);
+        if (st + 1 >= nsteps) break;
+        if (st + 2 < nsteps) {
+            ensure_table(st + 2);
+            issue_step<BF16>(W, st + 2, lane, tk, ds, slot_tab, tab_base, kbase, vbase, row_stride, b0);
         }
-        wave_lds_sync();
-
-        // ---- PV: lane owns dims 2*lane, 2*lane+1 of every head
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float al = sh_alpha[wave][h];
-            o[h][0] *= al;
-            o[h][1] *= al;
-        }
-#pragma unroll
-        for (int tt = 0; tt < kStep; ++tt) {
-            float v0, v1;
-            if constexpr (BF16) {
-                v0 = bf16lo(vt[tt][0]);
-                v1 = bf16hi(vt[tt][0]);
-            } else {
-                v0 = __uint_as_float(vt[tt][0]);
-                v1 = __uint_as_float(vt[tt][1]);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float pp = sh_p[wave][h * kStep + tt];
-                o[h][0] = __builtin_fmaf(pp, v0, o[h][0]);
-                o[h][1] = __builtin_fmaf(pp, v1, o[h][1]);
-            }
-        }
-        wave_lds_sync();
+        compute_step<BF16, G>(b1, qr, A.c, tk, ds, hb, sh_p[wave], sh_alpha[wave], S);
     }
 
     // ---- denominators: sum the per-lane partials over the 8 token lanes
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-        float l = l_run[h];
+        float l = S.l_run[h];
         l = l + __shfl_xor(l, 8, kWave);
         l = l + __shfl_xor(l, 16, kWave);
         l = l + __shfl_xor(l, 32, kWave);
         if (tk == 0) {
             sh_l[wave][hb + h] = l;
-            sh_alpha[wave][hb + h] = m_run[h];     // reuse slot for the running max
+            sh_alpha[wave][hb + h] = S.m_run[h];    // reuse slot for the running max
         }
     }
     wave_lds_sync();
@@ -326,7 +416,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
         for (int h = 0; h < G; ++h) {
             const float l = sh_l[wave][h];
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const float r0 = o[h][0] * inv, r1 = o[h][1] * inv;
+            const float r0 = S.o[h][0] * inv, r1 = S.o[h][1] * inv;
             const int64_t off = (i * A.hq + qh0 + h) * kD + 2 * lane;
             if constexpr (BF16) {
                 reinterpret_cast<uint32_t *>(A.out)[off >> 1] = pack_bf16x2(r0, r1);
@@ -338,7 +428,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const int64_t slot = (i * A.hq + qh0 + h) * A.n_split + c;
-            reinterpret_cast<float2 *>(A.ws_o + slot * kD)[lane] = make_float2(o[h][0], o[h][1]);
+            reinterpret_cast<float2 *>(A.ws_o + slot * kD)[lane] = make_float2(S.o[h][0], S.o[h][1]);
             if (lane == 0) {
                 A.ws_ml[slot * 2 + 0] = sh_alpha[wave][h];
                 A.ws_ml[slot * 2 + 1] = sh_l[wave][h];
@@ -347,27 +437,38 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     }
 }
 
-// Merge split partials: one wave per (query, head), lane owns dims 2p, 2p+1.
+// Merge split partials: one wave per (query, head); lane s < n_split reads
+// split s's (m, l), the wave forms the weights, then every lane accumulates
+// dims 2p, 2p+1 over the splits (all partial loads issued together).
+constexpr int kMaxSplits = 16;
+
 template <bool BF16>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_combine_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int n_split, int64_t rows,
     void *__restrict__ out) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t r = (int64_t)blockIdx.x * kAttnWaves + threadIdx.x / kWave;   // query*hq + head
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t r = (int64_t)blockIdx.x * kAttnWaves + wave;   // query*hq + head
     if (r >= rows) return;
     const float *ml = ws_ml + r * n_split * 2;
-    float mmax = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+    float2 os[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < n_split) os[s] = reinterpret_cast<const float2 *>(ws_o + (r * n_split + s) * kD)[lane];
+    const float m_s = lane < n_split ? ml[2 * lane] : -INFINITY;
+    const float l_s = lane < n_split ? ml[2 * lane + 1] : 0.0f;
+    const float mmax = wave_max(m_s);
     const float msafe = mmax == -INFINITY ? 0.0f : mmax;
-    float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-        const float ls = ml[2 * s + 1];
-        if (ls == 0.0f) continue;
-        const float wgt = exp2f(ml[2 * s] - msafe);
-        const float2 os = reinterpret_cast<const float2 *>(ws_o + (r * n_split + s) * kD)[lane];
-        l = l + wgt * ls;
-        o0 = o0 + wgt * os.x;
-        o1 = o1 + wgt * os.y;
+    const float w_s = l_s > 0.0f ? exp2f(m_s - msafe) : 0.0f;
+    const float l = wave_sum(w_s * l_s);
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < n_split) {
+            const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_s), s));
+            o0 = __builtin_fmaf(wgt, os[s].x, o0);
+            o1 = __builtin_fmaf(wgt, os[s].y, o1);
+        }
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if constexpr (BF16) {
