@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="input copies to rotate over (0=auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy-mb", type=int, default=0,
+                   help="only run a plain device-to-device copy of this many MiB (5 times) "
+                        "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
     return p.parse_args()
 
 
@@ -109,6 +112,15 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 5}))
+        return
     import qsa_workloads as W
     from indexer_selected_sparse_amd import pipeline
 

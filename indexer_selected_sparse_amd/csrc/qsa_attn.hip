@@ -10,22 +10,31 @@
 // the tail ratio*nb .. L-1.  In the dense regime (nb <= K) idx lists every
 // complete block, so T = 0..L-1 and the result is dense causal attention.
 //
-// Work decomposition: one wave per (query, KV head, split); a split owns a
-// contiguous range of selected slots (the last split also owns the tail).
+// Work decomposition: a query's selected slots are cut into n_part parts (the
+// last part also owns the tail); one wave per (query, part, KV head), and the
+// waves of a workgroup are consecutive KV heads of the same (query, part), so
+// a workgroup reads whole token rows (all heads) contiguously.  With more than
+// one part (decode) each wave writes an unnormalised (m, l, o) partial and a
+// small combine kernel finishes.  The part count depends only on budget/ratio
+// (decode) or is 1 (prefill), so a query's arithmetic never depends on the
+// rest of the batch.
+//
 // The G = hq/hkv query heads of the KV head share every K/V load.  Tokens are
-// processed 16 at a time:
+// processed 16 per step, the next step's K/V loads in flight meanwhile:
 //  * QK: lane (tk = lane/8, ds = lane%8) loads dims ds*16..+16 of tokens tk
-//    and tk+8 straight from HBM and forms partial dots for all G heads
-//    (bf16: v_dot2_f32_bf16); a transpose-reduce across the 8 ds lanes leaves
-//    each lane with full dots of G/8 heads (or a shared head for G < 8).
-//  * online softmax in fp32 (exp2 domain), one running max per head.
+//    and tk+8 straight from HBM and forms partial dots for all G heads with
+//    v_dot2_f32_bf16 (query slices come from LDS).  The heads are laid out in
+//    a per-lane order chosen so that a 3-step transpose-reduce over the 8 ds
+//    lanes is three DPP adds per kept value (each lane keeps its first half
+//    and adds the partner's second half); every lane ends with the full dots
+//    of G/8 heads.
+//  * online softmax in fp32 (exp2 domain), one running max per head; the max
+//    over the 8 token lanes uses DPP and the gfx950 permlane swaps.
 //  * PV: lane p owns dims 2p, 2p+1 of every head; V rows are read as one
-//    coalesced row per token; fp32 probabilities come through a small
-//    per-wave LDS slot and meet fp32-widened V in plain FMAs.  (Rounding the
-//    probabilities to bf16 for a packed dot would cost up to 2^-8 relative per
-//    weight, which is visible when only a few tokens carry the softmax.)
-// With more than one split, unnormalised (m, l, o) partials go to the
-// workspace and a combine kernel merges them.
+//    coalesced row per token from a scalar base address; fp32 probabilities
+//    come through LDS and meet fp32-widened V in plain FMAs.  (bf16
+//    probabilities would cost up to 2^-8 relative per weight, visible when a
+//    few tokens carry the softmax.)
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -33,7 +42,7 @@ namespace qsa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kAttnWaves = 4;
+constexpr int kWgWaves = 4;             // waves (parts) per workgroup
 constexpr int kStep = 16;               // tokens per step
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -41,53 +50,91 @@ struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *idx;
     const int64_t *kv_off, *q_off;
-    int num_seqs, hq, hkv, log2r, K, n_split;
+    int num_seqs, hq, hkv, log2r, K;
+    int n_part;              // parts per query
     float c;                 // softmax_scale * log2(e)
     int64_t total_q;
     void *out;
-    float *ws_o;             // [total_q, hq, n_split, D]
-    float *ws_ml;            // [total_q, hq, n_split, 2]
+    float *ws_o;             // [total_q, hq, n_part, D]
+    float *ws_ml;            // [total_q, hq, n_part, 2]
 };
 
-// log2 of a power of two known at compile time
 template <int G>
 constexpr int ilog2() { return G <= 1 ? 0 : 1 + ilog2<G / 2>(); }
 
-// One step of the transpose-reduce: keep half of the array (upper half when
-// `upper`), add the partner's copy of that half.
-template <int N>
-__device__ __forceinline__ void tr_step(const float (&a)[N], float (&o)[N / 2], bool upper, int xm) {
-#pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-        const float mine = upper ? a[N / 2 + j] : a[j];
-        const float send = upper ? a[j] : a[N / 2 + j];
-        o[j] = mine + __shfl_xor(send, xm, kWave);
-    }
+// ---------------------------------------------------------- cross-lane ops
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppHalfMirror = 0x141;   // lane ^ 7 within 8
+constexpr int kDppXor2 = 0x4e;          // quad_perm [2,3,0,1]
+constexpr int kDppXor1 = 0xb1;          // quad_perm [1,0,3,2]
+constexpr int kDppRor8 = 0x128;         // lane ^ 8 within 16
+
+// max / sum over the 8 lanes {l ^ 8k}: same ds, all token slots
+__device__ __forceinline__ float tok_max(float x) {
+    x = fmaxf(x, dpp<kDppRor8>(x));
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float tok_sum(float x) {
+    x = x + dpp<kDppRor8>(x);
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Reduce G partial sums over the 8 ds-lanes; returns NH = max(1, G/8) sums.
+// Head held in partial-sum slot j of lane ds (G >= 8, unit U = G/8): the
+// order makes each transpose step "keep my first half, add my partner's
+// second half" — partners are ds^7, ds^2, ds^1 in turn, and the unit map
+// {0,1,2,3,7,6,5,4} satisfies gp(u+4) = gp(u)^7, gp(u+2) = gp(u)^2 (u < 2),
+// gp(1) = gp(0)^1.  Lane ds ends with heads U*ds .. U*ds+U-1.
+__device__ __forceinline__ int slot_head(int j, int ds, int U) {
+    constexpr int gp[8] = {0, 1, 2, 3, 7, 6, 5, 4};
+    return U * (ds ^ gp[j / U]) + (j % U);
+}
+
 template <int G>
 __device__ __forceinline__ void transpose_reduce(const float (&p)[G], float (&r)[(G >= 8 ? G / 8 : 1)],
                                                  int ds) {
     if constexpr (G >= 8) {
         float a4[G / 2], a2[G / 4];
-        tr_step<G>(p, a4, ds & 4, 4);
-        tr_step<G / 2>(a4, a2, ds & 2, 2);
-        tr_step<G / 4>(a2, r, ds & 1, 1);
-    } else if constexpr (G == 4) {
-        float a4[2], a2[1];
-        tr_step<4>(p, a4, ds & 4, 4);
-        tr_step<2>(a4, a2, ds & 2, 2);
-        r[0] = a2[0] + __shfl_xor(a2[0], 1, kWave);
-    } else if constexpr (G == 2) {
-        float a4[1];
-        tr_step<2>(p, a4, ds & 4, 4);
-        float x = a4[0] + __shfl_xor(a4[0], 2, kWave);
-        r[0] = x + __shfl_xor(x, 1, kWave);
+#pragma unroll
+        for (int j = 0; j < G / 2; ++j) a4[j] = p[j] + dpp<kDppHalfMirror>(p[G / 2 + j]);
+#pragma unroll
+        for (int j = 0; j < G / 4; ++j) a2[j] = a4[j] + dpp<kDppXor2>(a4[G / 4 + j]);
+#pragma unroll
+        for (int j = 0; j < G / 8; ++j) r[j] = a2[j] + dpp<kDppXor1>(a2[G / 8 + j]);
     } else {
-        float x = p[0] + __shfl_xor(p[0], 4, kWave);
-        x = x + __shfl_xor(x, 2, kWave);
-        r[0] = x + __shfl_xor(x, 1, kWave);
+        // G < 8: natural head order; keep the half selected by the lane's bit
+        float a[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) a[h] = p[h];
+        int n = G;
+        const int masks[3] = {4, 2, 1};
+#pragma unroll
+        for (int st = 0; st < 3; ++st) {
+            const int m = masks[st];
+            const bool upper = ds & m;
+            if (n > 1) {
+#pragma unroll
+                for (int j = 0; j < G / 2; ++j) {
+                    if (j < n / 2) {
+                        const float mine = upper ? a[n / 2 + j] : a[j];
+                        const float send = upper ? a[j] : a[n / 2 + j];
+                        a[j] = mine + __shfl_xor(send, m, kWave);
+                    }
+                }
+                n /= 2;
+            } else {
+                a[0] = a[0] + __shfl_xor(a[0], m, kWave);
+            }
+        }
+        r[0] = a[0];
     }
 }
 
@@ -97,13 +144,19 @@ __device__ __forceinline__ int head_base(int ds) {
     else return ds >> (3 - ilog2<G>());
 }
 
+// Head of partial-sum slot j for lane ds.
+template <int G>
+__device__ __forceinline__ int qk_head(int j, int ds) {
+    if constexpr (G >= 8) return slot_head(j, ds, G / 8);
+    else return j;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Token position of flat token t of this split (-1 if t is past the end).
 template <bool BF16>
 struct KVTypes;
 template <>
@@ -132,8 +185,8 @@ struct StepBuf {
 
 // Wave-uniform description of the tokens one wave processes.
 struct WaveWork {
-    const int32_t *__restrict__ sel;  // idx row + first slot of this split
-    int nslot;                        // selected slots of the split
+    const int32_t *__restrict__ sel;  // idx row + first slot of this part
+    int nslot;                        // selected slots of the part
     int nblk_tok;                     // tokens from selected blocks
     int ntok;                         // + tail tokens
     int64_t tail0;                    // first tail position (ratio * nb)
@@ -141,12 +194,12 @@ struct WaveWork {
     int log2r;
 };
 
-// Issue the loads of step `st`.  Lane t < 16 resolves token t0+t to a row of
-// the sequence (a selected block id from the slot table held one slot per
-// lane, or a tail position; malformed ids and positions past the end give
-// "no token" and read row 0).  K rows reach the QK lanes by a cross-lane
-// permute; V rows become wave-uniform addresses, so each V row is one
-// coalesced scalar-based load.
+// Issue the loads of step `st`.  Lane t < 16 resolves token 16*st+t to a row
+// of the sequence (a selected block id from the slot table, one slot per
+// lane, or a tail position; malformed ids and positions past the end give "no
+// token" and read row 0).  K rows reach the QK lanes by a cross-lane permute
+// (with every lane active); V rows become wave-uniform addresses, so each V
+// row is one coalesced load from a scalar base.
 template <bool BF16>
 __device__ __forceinline__ void issue_step(const WaveWork &W, int st, int lane, int tk, int ds,
                                            uint32_t slot_tab, int tab_base,
@@ -156,8 +209,6 @@ __device__ __forceinline__ void issue_step(const WaveWork &W, int st, int lane, 
     using T = typename KVTypes<BF16>::elem;
     constexpr int KW = StepBuf<BF16>::KW;
     const int t = st * kStep + (lane & (kStep - 1));
-    // The permute runs with every lane active: a lane that is switched off
-    // does not supply its value to the others.
     int rel = (t >> W.log2r) - tab_base;             // slot within the table
     rel = rel < 0 ? 0 : (rel > kWave - 1 ? kWave - 1 : rel);
     const int b = __builtin_amdgcn_ds_bpermute(rel << 2, (int)slot_tab);
@@ -172,7 +223,6 @@ __device__ __forceinline__ void issue_step(const WaveWork &W, int st, int lane, 
     }
     const uint64_t okm = __ballot(ok && lane < kStep);
     B.valid = (uint32_t)okm & 0xffffu;
-    // K: lane (tk, ds) takes tokens tk and tk+8
     const int rA = __builtin_amdgcn_ds_bpermute(tk << 2, row);
     const int rB = __builtin_amdgcn_ds_bpermute((tk + 8) << 2, row);
     {
@@ -185,7 +235,6 @@ __device__ __forceinline__ void issue_step(const WaveWork &W, int st, int lane, 
             B.kB[4 * c4 + 0] = y.x; B.kB[4 * c4 + 1] = y.y; B.kB[4 * c4 + 2] = y.z; B.kB[4 * c4 + 3] = y.w;
         }
     }
-    // V: one coalesced row per token, wave-uniform base address
 #pragma unroll
     for (int tt = 0; tt < kStep; ++tt) {
         const int r = __builtin_amdgcn_readlane(row, tt);
@@ -200,45 +249,51 @@ __device__ __forceinline__ void issue_step(const WaveWork &W, int st, int lane, 
     }
 }
 
-template <bool BF16, int G>
+template <int G>
 struct AttnState {
     static constexpr int NH = G >= 8 ? G / 8 : 1;
     float m_run[NH], l_run[NH];
     float o[G][2];
 };
 
+// This lane's query slices for the QK mapping: slot j holds dims ds*16..+16
+// of head qk_head(j, ds), as dwords (bf16 pairs or fp32).
+template <bool BF16, int G>
+struct QSlices {
+    uint32_t v[G][KVTypes<BF16>::kDwordsPerLaneK];
+};
+
 // Consume one step: QK, online softmax, PV.
 template <bool BF16, int G>
-__device__ __forceinline__ void compute_step(const StepBuf<BF16> &B,
-                                             const uint32_t (&qr)[G][KVTypes<BF16>::kDwordsPerLaneK],
+__device__ __forceinline__ void compute_step(const StepBuf<BF16> &B, const QSlices<BF16, G> &Q,
                                              float c, int tk, int ds, int hb,
-                                             float (*sh_p)[G], float *sh_alpha,
-                                             AttnState<BF16, G> &S) {
-    constexpr int NH = AttnState<BF16, G>::NH;
+                                             float (*sh_p)[G], float *sh_alpha, AttnState<G> &S) {
+    constexpr int NH = AttnState<G>::NH;
     constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
-    // ---- QK partial dots over this lane's 16 dims
+    // ---- QK partial dots over this lane's 16 dims, heads in slot order
     float dA[G], dB[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int j = 0; j < G; ++j) {
+        const uint32_t (&qv)[KW] = Q.v[j];
         float a = 0.0f, b = 0.0f;
         if constexpr (BF16) {
             typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int e = 0; e < KW; ++e) {
-                const bf2 qv = __builtin_bit_cast(bf2, qr[h][e]);
-                a = __builtin_amdgcn_fdot2_f32_bf16(qv, __builtin_bit_cast(bf2, B.kA[e]), a, false);
-                b = __builtin_amdgcn_fdot2_f32_bf16(qv, __builtin_bit_cast(bf2, B.kB[e]), b, false);
+                const bf2 qq = __builtin_bit_cast(bf2, qv[e]);
+                a = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf2, B.kA[e]), a, false);
+                b = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf2, B.kB[e]), b, false);
             }
         } else {
 #pragma unroll
             for (int e = 0; e < KW; ++e) {
-                const float qv = __uint_as_float(qr[h][e]);
-                a = __builtin_fmaf(qv, __uint_as_float(B.kA[e]), a);
-                b = __builtin_fmaf(qv, __uint_as_float(B.kB[e]), b);
+                const float qq = __uint_as_float(qv[e]);
+                a = __builtin_fmaf(qq, __uint_as_float(B.kA[e]), a);
+                b = __builtin_fmaf(qq, __uint_as_float(B.kB[e]), b);
             }
         }
-        dA[h] = a;
-        dB[h] = b;
+        dA[j] = a;
+        dB[j] = b;
     }
     float sA[NH], sB[NH];
     transpose_reduce<G>(dA, sA, ds);
@@ -251,10 +306,7 @@ __device__ __forceinline__ void compute_step(const StepBuf<BF16> &B,
     for (int h = 0; h < NH; ++h) {
         const float xa = okA ? sA[h] * c : -INFINITY;
         const float xb = okB ? sB[h] * c : -INFINITY;
-        float mx = fmaxf(xa, xb);
-        mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float mx = tok_max(fmaxf(xa, xb));
         const float m_new = fmaxf(S.m_run[h], mx);
         const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
         const float alpha = exp2f(S.m_run[h] - m_safe);
@@ -297,33 +349,46 @@ __device__ __forceinline__ void compute_step(const StepBuf<BF16> &B,
             S.o[h][1] = __builtin_fmaf(pv[h], v1, S.o[h][1]);
         }
     }
+    // Likewise keep each token's probability reads next to its FMAs (reading
+    // all 16 x G probabilities up front would hold 16*G registers).
+#pragma unroll
+    for (int tt = 0; tt < kStep; ++tt) {
+        __builtin_amdgcn_sched_group_barrier(0x100, G >= 4 ? G / 4 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * G + (BF16 ? 2 : 0), 0);
+    }
     wave_lds_sync();
 }
 
+template <int G>
+struct AttnLds {
+    // 16-byte aligned rows so a token's probabilities load as ds_read_b128
+    alignas(16) float p[kWgWaves][kStep][G];   // probabilities [token][head], per wave
+    alignas(16) float alpha[kWgWaves][G];
+    alignas(16) float l[kWgWaves][G];
+    alignas(16) float m[kWgWaves][G];
+};
+
 template <bool BF16, int G>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
+__device__ __forceinline__ void attn_body(const AttnArgs &A) {
     using T = typename KVTypes<BF16>::elem;
-    constexpr int NH = AttnState<BF16, G>::NH;
-    constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
-    __shared__ float sh_p[kAttnWaves][kStep][G];   // probabilities [token][head]
-    __shared__ float sh_alpha[kAttnWaves][G];
-    __shared__ float sh_l[kAttnWaves][G];
+    constexpr int NH = AttnState<G>::NH;
+    __shared__ __align__(16) AttnLds<G> L;
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is uniform across the wave; saying so keeps everything
-    // derived from it (query, split, positions) in scalar registers.
+    // derived from it (part, positions) in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t wid = (int64_t)blockIdx.x * kAttnWaves + wave;
+    const int64_t wid = (int64_t)blockIdx.x * kWgWaves + wave;
     const int g = (int)(wid % A.hkv);
     const int64_t t2 = wid / A.hkv;
-    const int c = (int)(t2 % A.n_split);
-    const int64_t i = t2 / A.n_split;
-    if (i >= A.total_q) return;
+    const int c = (int)(t2 % A.n_part);              // part of this wave
+    const int64_t i = t2 / A.n_part;
+    if (i >= A.total_q) return;                      // uniform over the wave
 
     const QueryPos qp = query_pos(A.kv_off, nullptr, A.q_off, A.num_seqs, i);
     const int64_t nb = qp.L >> A.log2r;
     const int64_t nsel = nb < A.K ? nb : (int64_t)A.K;
-    const int64_t per = (nsel + A.n_split - 1) / A.n_split;
+    const int64_t per = (nsel + A.n_part - 1) / A.n_part;
     const int64_t s_beg = imin64((int64_t)c * per, nsel);
     const int64_t s_end = imin64(s_beg + per, nsel);
     WaveWork W;
@@ -333,7 +398,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     W.nblk_tok = W.nslot << A.log2r;
     W.tail0 = nb << A.log2r;
     W.nb = nb;
-    W.ntok = W.nblk_tok + ((c == A.n_split - 1) ? (int)(qp.L - W.tail0) : 0);
+    W.ntok = W.nblk_tok + ((c == A.n_part - 1) ? (int)(qp.L - W.tail0) : 0);
 
     const int tk = lane >> 3, ds = lane & 7;
     const int hb = head_base<G>(ds);
@@ -342,23 +407,24 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     const T *__restrict__ kbase = static_cast<const T *>(A.k) + (qp.kv_row0 * A.hkv + g) * kD;
     const T *__restrict__ vbase = static_cast<const T *>(A.v) + (qp.kv_row0 * A.hkv + g) * kD;
 
-    // q slice for the QK lane mapping: heads qh0..qh0+G-1, dims ds*16..+16
-    uint32_t qr[G][KW];
+    // query slices for the QK mapping (kept in registers for the whole part)
+    QSlices<BF16, G> Q;
     {
-        const T *qp_ = static_cast<const T *>(A.q) + (i * A.hq + qh0) * kD + ds * 16;
+        constexpr int KW = KVTypes<BF16>::kDwordsPerLaneK;
+        const T *qrow = static_cast<const T *>(A.q) + (i * A.hq + qh0) * kD + ds * 16;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(qp_ + h * kD);
+        for (int j = 0; j < G; ++j) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(qrow + qk_head<G>(j, ds) * kD);
 #pragma unroll
             for (int c4 = 0; c4 < KW / 4; ++c4) {
                 const uint4 x = src[c4];
-                qr[h][4 * c4 + 0] = x.x; qr[h][4 * c4 + 1] = x.y;
-                qr[h][4 * c4 + 2] = x.z; qr[h][4 * c4 + 3] = x.w;
+                Q.v[j][4 * c4] = x.x; Q.v[j][4 * c4 + 1] = x.y;
+                Q.v[j][4 * c4 + 2] = x.z; Q.v[j][4 * c4 + 3] = x.w;
             }
         }
     }
 
-    AttnState<BF16, G> S;
+    AttnState<G> S;
 #pragma unroll
     for (int h = 0; h < NH; ++h) { S.m_run[h] = -INFINITY; S.l_run[h] = 0.0f; }
 #pragma unroll
@@ -368,7 +434,6 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
     int tab_base = 0;
     uint32_t slot_tab = (uint32_t)(lane < W.nslot ? W.sel[lane] : -1);
     const int nsteps = (W.ntok + kStep - 1) / kStep;
-    // slots a step touches: [ (16*st) >> log2r, (16*st + 15) >> log2r ]
     auto ensure_table = [&](int st) {
         const int first = (st * kStep) >> W.log2r;
         const int last = (st * kStep + kStep - 1) >> W.log2r;
@@ -388,83 +453,87 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs A) {
             ensure_table(st + 1);
             issue_step<BF16>(W, st + 1, lane, tk, ds, slot_tab, tab_base, kbase, vbase, row_stride, b1);
         }
-        compute_step<BF16, G>(b0, qr, A.c, tk, ds, hb, sh_p[wave], sh_alpha[wave], S);
+        compute_step<BF16, G>(b0, Q, A.c, tk, ds, hb, L.p[wave], L.alpha[wave], S);
         if (st + 1 >= nsteps) break;
         if (st + 2 < nsteps) {
             ensure_table(st + 2);
             issue_step<BF16>(W, st + 2, lane, tk, ds, slot_tab, tab_base, kbase, vbase, row_stride, b0);
         }
-        compute_step<BF16, G>(b1, qr, A.c, tk, ds, hb, sh_p[wave], sh_alpha[wave], S);
+        compute_step<BF16, G>(b1, Q, A.c, tk, ds, hb, L.p[wave], L.alpha[wave], S);
     }
 
-    // ---- denominators: sum the per-lane partials over the 8 token lanes
+    // ---- denominators over the 8 token lanes; running max per head
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-        float l = S.l_run[h];
-        l = l + __shfl_xor(l, 8, kWave);
-        l = l + __shfl_xor(l, 16, kWave);
-        l = l + __shfl_xor(l, 32, kWave);
+        const float l = tok_sum(S.l_run[h]);
         if (tk == 0) {
-            sh_l[wave][hb + h] = l;
-            sh_alpha[wave][hb + h] = S.m_run[h];    // reuse slot for the running max
+            L.l[wave][hb + h] = l;
+            L.m[wave][hb + h] = S.m_run[h];
         }
     }
     wave_lds_sync();
-
-    if (A.n_split == 1) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float l = sh_l[wave][h];
+    for (int h = 0; h < G; ++h) {
+        if (A.n_part == 1) {
+            const float l = L.l[wave][h];
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const float r0 = S.o[h][0] * inv, r1 = S.o[h][1] * inv;
             const int64_t off = (i * A.hq + qh0 + h) * kD + 2 * lane;
             if constexpr (BF16) {
-                reinterpret_cast<uint32_t *>(A.out)[off >> 1] = pack_bf16x2(r0, r1);
+                reinterpret_cast<uint32_t *>(A.out)[off >> 1] = pack_bf16x2(S.o[h][0] * inv, S.o[h][1] * inv);
             } else {
-                reinterpret_cast<float2 *>(A.out)[off >> 1] = make_float2(r0, r1);
+                reinterpret_cast<float2 *>(A.out)[off >> 1] = make_float2(S.o[h][0] * inv, S.o[h][1] * inv);
             }
-        }
-    } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const int64_t slot = (i * A.hq + qh0 + h) * A.n_split + c;
+        } else {
+            const int64_t slot = (i * A.hq + qh0 + h) * A.n_part + c;
             reinterpret_cast<float2 *>(A.ws_o + slot * kD)[lane] = make_float2(S.o[h][0], S.o[h][1]);
             if (lane == 0) {
-                A.ws_ml[slot * 2 + 0] = sh_alpha[wave][h];
-                A.ws_ml[slot * 2 + 1] = sh_l[wave][h];
+                A.ws_ml[slot * 2 + 0] = L.m[wave][h];
+                A.ws_ml[slot * 2 + 1] = L.l[wave][h];
             }
         }
     }
 }
 
-// Merge split partials: one wave per (query, head); lane s < n_split reads
-// split s's (m, l), the wave forms the weights, then every lane accumulates
-// dims 2p, 2p+1 over the splits (all partial loads issued together).
-constexpr int kMaxSplits = 16;
+// bf16 with G <= 4 fits three waves per SIMD (<= 168 VGPRs) without spills;
+// the wider variants keep the compiler's default budget.
+template <bool BF16, int G>
+__global__ __launch_bounds__(kWgWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(3))) void attn_kernel_w3(AttnArgs A) {
+    attn_body<BF16, G>(A);
+}
+template <bool BF16, int G>
+__global__ __launch_bounds__(kWgWaves * kWave) void attn_kernel(AttnArgs A) {
+    attn_body<BF16, G>(A);
+}
+
+// Merge part partials: one wave per (query, head); lane s < n_part reads
+// partial s's (m, l), the wave forms the weights, then every lane accumulates
+// dims 2p, 2p+1 over the partials (all partial loads issued together).
+constexpr int kMaxGroups = 32;
 
 template <bool BF16>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_combine_kernel(
-    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int n_split, int64_t rows,
+__global__ __launch_bounds__(kWgWaves * kWave) void attn_combine_kernel(
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int n_part, int64_t rows,
     void *__restrict__ out) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t r = (int64_t)blockIdx.x * kAttnWaves + wave;   // query*hq + head
+    const int64_t r = (int64_t)blockIdx.x * kWgWaves + wave;   // query*hq + head
     if (r >= rows) return;
-    const float *ml = ws_ml + r * n_split * 2;
-    float2 os[kMaxSplits];
+    const float *ml = ws_ml + r * n_part * 2;
+    float2 os[kMaxGroups];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-        if (s < n_split) os[s] = reinterpret_cast<const float2 *>(ws_o + (r * n_split + s) * kD)[lane];
-    const float m_s = lane < n_split ? ml[2 * lane] : -INFINITY;
-    const float l_s = lane < n_split ? ml[2 * lane + 1] : 0.0f;
+    for (int s = 0; s < kMaxGroups; ++s)
+        if (s < n_part) os[s] = reinterpret_cast<const float2 *>(ws_o + (r * n_part + s) * kD)[lane];
+    const float m_s = lane < n_part ? ml[2 * lane] : -INFINITY;
+    const float l_s = lane < n_part ? ml[2 * lane + 1] : 0.0f;
     const float mmax = wave_max(m_s);
     const float msafe = mmax == -INFINITY ? 0.0f : mmax;
     const float w_s = l_s > 0.0f ? exp2f(m_s - msafe) : 0.0f;
     const float l = wave_sum(w_s * l_s);
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < n_split) {
+    for (int s = 0; s < kMaxGroups; ++s) {
+        if (s < n_part) {
             const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_s), s));
             o0 = __builtin_fmaf(wgt, os[s].x, o0);
             o1 = __builtin_fmaf(wgt, os[s].y, o1);
@@ -480,22 +549,32 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_combine_kernel(
 
 template <bool BF16>
 hipError_t launch_attn_t(const AttnArgs &A, int G, hipStream_t st) {
-    const int64_t waves = A.total_q * A.n_split * A.hkv;
-    dim3 grid((unsigned)((waves + kAttnWaves - 1) / kAttnWaves));
-    dim3 block(kAttnWaves * kWave);
-    switch (G) {
-    case 1: hipLaunchKernelGGL((attn_kernel<BF16, 1>), grid, block, 0, st, A); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<BF16, 2>), grid, block, 0, st, A); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<BF16, 4>), grid, block, 0, st, A); break;
-    case 8: hipLaunchKernelGGL((attn_kernel<BF16, 8>), grid, block, 0, st, A); break;
-    default: hipLaunchKernelGGL((attn_kernel<BF16, 16>), grid, block, 0, st, A); break;
+    const int64_t waves = A.total_q * A.n_part * A.hkv;
+    dim3 grid((unsigned)((waves + kWgWaves - 1) / kWgWaves));
+    dim3 block(kWgWaves * kWave);
+    if constexpr (BF16) {
+        switch (G) {
+        case 1: hipLaunchKernelGGL((attn_kernel_w3<BF16, 1>), grid, block, 0, st, A); break;
+        case 2: hipLaunchKernelGGL((attn_kernel_w3<BF16, 2>), grid, block, 0, st, A); break;
+        case 4: hipLaunchKernelGGL((attn_kernel_w3<BF16, 4>), grid, block, 0, st, A); break;
+        case 8: hipLaunchKernelGGL((attn_kernel<BF16, 8>), grid, block, 0, st, A); break;
+        default: hipLaunchKernelGGL((attn_kernel<BF16, 16>), grid, block, 0, st, A); break;
+        }
+    } else {
+        switch (G) {
+        case 1: hipLaunchKernelGGL((attn_kernel<BF16, 1>), grid, block, 0, st, A); break;
+        case 2: hipLaunchKernelGGL((attn_kernel<BF16, 2>), grid, block, 0, st, A); break;
+        case 4: hipLaunchKernelGGL((attn_kernel<BF16, 4>), grid, block, 0, st, A); break;
+        case 8: hipLaunchKernelGGL((attn_kernel<BF16, 8>), grid, block, 0, st, A); break;
+        default: hipLaunchKernelGGL((attn_kernel<BF16, 16>), grid, block, 0, st, A); break;
+        }
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || A.n_split == 1) return e;
+    if (e != hipSuccess || A.n_part == 1) return e;
     const int64_t rows = A.total_q * A.hq;
-    dim3 cgrid((unsigned)((rows + kAttnWaves - 1) / kAttnWaves));
-    hipLaunchKernelGGL((attn_combine_kernel<BF16>), cgrid, block, 0, st, A.ws_o, A.ws_ml,
-                       A.n_split, rows, A.out);
+    dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves));
+    hipLaunchKernelGGL((attn_combine_kernel<BF16>), cgrid, block, 0, st, A.ws_o, A.ws_ml, A.n_part,
+                       rows, A.out);
     return hipGetLastError();
 }
 
@@ -503,11 +582,9 @@ hipError_t launch_attn_t(const AttnArgs &A, int G, hipStream_t st) {
 
 int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio, bool decode) {
     (void)b; (void)a;
-    // The split count depends on K alone (decode) or is 1 (prefill), never on
-    // how many queries share the launch: a query's fp32 accumulation order is
-    // then the same in any batch, so chunked prefill equals single-shot
-    // prefill bit for bit.  Decode splits the K selected blocks into runs of
-    // 32 (at most 16 runs); prefill has enough queries to fill the chip.
+    // Parts per query.  Decode cuts the K selected blocks into runs of 32 (at
+    // most 16 runs); prefill keeps one part per (query, KV head).  Never a
+    // function of the batch.
     if (!decode) return 1;
     const int K = budget / ratio;
     int s = K / 32;
@@ -517,9 +594,9 @@ int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio
 }
 
 size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
-    const int s = attn_num_splits(b, a, budget, ratio, true);
-    if (s <= 1) return 0;
-    const size_t rows = (size_t)b.total_q * (size_t)a.hq * (size_t)s;
+    const int parts = attn_num_splits(b, a, budget, ratio, true);
+    if (parts <= 1) return 0;
+    const size_t rows = (size_t)b.total_q * (size_t)a.hq * (size_t)parts;
     return rows * (kD + 2) * sizeof(float) + 256;
 }
 
@@ -532,16 +609,16 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     A.num_seqs = b.num_seqs; A.hq = a.hq; A.hkv = a.hkv;
     A.log2r = __builtin_ctz((unsigned)ratio);
     A.K = budget / ratio;
-    A.n_split = attn_num_splits(b, a, budget, ratio, decode);
+    A.n_part = attn_num_splits(b, a, budget, ratio, decode);
     A.c = a.softmax_scale * kLog2e;
     A.total_q = b.total_q;
     A.out = out;
-    const size_t rows = (size_t)b.total_q * (size_t)a.hq * (size_t)A.n_split;
+    const size_t rows = (size_t)b.total_q * (size_t)a.hq * (size_t)A.n_part;
     A.ws_o = static_cast<float *>(ws);
-    A.ws_ml = A.n_split > 1 ? static_cast<float *>(ws) + rows * kD : nullptr;
+    A.ws_ml = A.n_part > 1 ? static_cast<float *>(ws) + rows * kD : nullptr;
     const int G = a.hq / a.hkv;
-    trace("attn total_q=%lld hkv=%d G=%d splits=%d dtype=%d", (long long)b.total_q, a.hkv, G,
-          A.n_split, a.dtype);
+    trace("attn total_q=%lld hkv=%d G=%d parts=%d dtype=%d", (long long)b.total_q, a.hkv, G,
+          A.n_part, a.dtype);
     return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, st) : launch_attn_t<false>(A, G, st);
 }
 

@@ -8,18 +8,26 @@
 //   nb >  K:  the K blocks with the largest score, ties to the lower index,
 //             written in ascending block order.
 //
-// Algorithm: one workgroup (1024 threads) per query row.  Scores are mapped
-// to order-preserving uint32 keys.  The exact K-th largest key T is found by
-// an MSB-first radix select that starts below the bits shared by the row's
-// smallest and largest key (so the first 11-bit digit already spreads over
-// the populated range and the LDS histogram atomics rarely collide), then
-// 11-bit digits until all bits are fixed.  A final pass in index order takes
-// every key > T and the first `need` keys == T (lowest indices), using two
-// workgroup prefix scans so the output comes out ascending without a sort.
-//
-// With `recheck` (matrix-core scores that are only within a certified bound
-// of the canonical ones) a bounded-interval variant decides most blocks from
-// the bounds and recomputes only the undecided band in canonical order.
+// Algorithm: one 1024-thread workgroup per query row.  Scores become
+// order-preserving uint32 keys, cached in LDS (rows up to 32K blocks; longer
+// rows are re-read from memory on each pass).
+//  1. min/max of the row.
+//  2. A histogram of 2048 bins LINEAR in the score between min and max.  The
+//     bin map x -> floor((x - min) * 2048/(max - min)) is monotone, so every
+//     block of a higher bin scores strictly higher than every block of a lower
+//     bin, and the K-th largest score T lies in the bin tb where the count
+//     from the top first reaches K.  (Linear bins spread the bulk of the row
+//     over many bins, so the LDS atomics rarely collide.)
+//  3. The blocks of bin tb (typically a few dozen) are copied out and an exact
+//     MSB-first radix select on their keys yields T, how many keys equal T
+//     exist and how many of them the selection still needs.  A degenerate
+//     row (too many blocks in one bin, e.g. all scores equal) runs the same
+//     exact radix select over the whole row instead.
+//  4. An ordered pass emits every key > T and the first `need` keys == T by
+//     index: elements are visited round-major (index order), and per
+//     (round, wave) counts, scanned once, give each output position.
+#include <mutex>
+
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -28,138 +36,131 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kDigitBits = 11;
-constexpr int kBins = 1 << kDigitBits;
-constexpr int kMaxPerThread = 128;   // => nb <= 131072 per row
-constexpr int kMaskWords = kMaxPerThread / 32;
+constexpr int kBins = 2048;                  // linear bins of step 2
+constexpr int kDigitBits = 11;               // radix digits of step 3
+constexpr int kMaxRounds = 128;              // => nb <= 131072 per row
+constexpr int kMaskWords = kMaxRounds / 32;
+constexpr int kCandMax = 2048;               // blocks of the threshold bin kept in LDS
+constexpr int kLdsKeys = 32 * 1024;          // rows cached in LDS (128 KB)
+
+static_assert(kMaxRounds * kTopkWaves <= kBins, "emit counts reuse the histogram");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
+    const uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
-// Workgroup-wide exclusive prefix sum of one uint per thread; also returns
-// the total.  `tmp` holds kTopkWaves + 1 entries of LDS.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t &total) {
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+struct TopkShared {
+    uint32_t hist[kBins];        // bin / digit counts; later per-(round, wave) counts
+    uint32_t cand[kCandMax];     // keys of the threshold bin
+    uint32_t wsum[kTopkWaves];   // per-wave partials of workgroup scans/reductions
+    uint32_t wmin[kTopkWaves], wmax[kTopkWaves];
+    uint32_t s0, s1, s2, s3;     // broadcast slots
+};
+
+// Workgroup exclusive prefix sum (thread order); returns (excl, total).
+__device__ __forceinline__ uint32_t wg_scan(uint32_t v, TopkShared &S, uint32_t &total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     uint32_t incl = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t y = __shfl_up(incl, o, kWave);
+        const uint32_t y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
     }
-    if (lane == kWave - 1) tmp[wave] = incl;
+    if (lane == kWave - 1) S.wsum[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t run = 0;
-        for (int w = 0; w < kTopkWaves; ++w) {
-            uint32_t t = tmp[w];
-            tmp[w] = run;
-            run += t;
-        }
-        tmp[kTopkWaves] = run;
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+        const uint32_t x = S.wsum[w];
+        before += (w < wave) ? x : 0u;
+        tot += x;
     }
     __syncthreads();
-    const uint32_t excl = tmp[wave] + incl - v;
-    total = tmp[kTopkWaves];
-    __syncthreads();
-    return excl;
+    total = tot;
+    return before + incl - v;
 }
 
-__device__ __forceinline__ uint32_t block_reduce_min_u(uint32_t v, uint32_t *tmp) {
+// Workgroup min and max of uint keys.
+__device__ __forceinline__ void wg_minmax(uint32_t &mn, uint32_t &mx, TopkShared &S) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    if ((threadIdx.x & 63) == 0) tmp[threadIdx.x / kWave] = v;
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) { S.wmin[wave] = mn; S.wmax[wave] = mx; }
     __syncthreads();
-    uint32_t r = tmp[0];
-    for (int w = 1; w < kTopkWaves; ++w) r = min(r, tmp[w]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ uint32_t block_reduce_max_u(uint32_t v, uint32_t *tmp) {
+    mn = S.wmin[0];
+    mx = S.wmax[0];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    if ((threadIdx.x & 63) == 0) tmp[threadIdx.x / kWave] = v;
+    for (int w = 1; w < kTopkWaves; ++w) { mn = min(mn, S.wmin[w]); mx = max(mx, S.wmax[w]); }
     __syncthreads();
-    uint32_t r = tmp[0];
-    for (int w = 1; w < kTopkWaves; ++w) r = max(r, tmp[w]);
-    __syncthreads();
-    return r;
 }
 
-// Find the exact `need`-th largest key among keys(b), b < nb, whose bits above
-// `shift` equal prefix's.  Returns T and updates need to the number of keys
-// equal to T that must be taken.  Keys come from a functor so that the same
-// routine serves plain and interval-bounded rows.
-struct SelectState {
-    uint32_t hist[kBins];
-    uint32_t tmp[kTopkWaves + 1];
-    uint32_t sh_digit;
-    uint32_t sh_need;
-};
+// Find the bin where the count from the top first reaches `need` among
+// nbins (<= 2048) bins of S.hist: each thread owns two adjacent bins
+// (descending); a workgroup scan gives the count above them.  Returns the
+// bin; `above` = count in higher bins.
+__device__ __forceinline__ int find_bin(int nbins, uint32_t need, TopkShared &S, uint32_t &above) {
+    const int hi = nbins - 1 - 2 * (int)threadIdx.x;
+    const uint32_t h0 = hi >= 0 ? S.hist[hi] : 0u;
+    const uint32_t h1 = hi >= 1 ? S.hist[hi - 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = wg_scan(h0 + h1, S, tot);
+    if (ex < need && need <= ex + h0 + h1) {
+        if (ex + h0 >= need) { S.s0 = (uint32_t)hi; S.s1 = ex; }
+        else { S.s0 = (uint32_t)(hi - 1); S.s1 = ex + h0; }
+    }
+    __syncthreads();
+    above = S.s1;
+    const int bin = (int)S.s0;
+    __syncthreads();
+    return bin;
+}
 
+// Exact `need`-th largest key among keys(b), b < n (MSB-first radix, digits
+// of 11 bits starting below the bits shared by kmin and kmax).  Returns T;
+// need_eq = keys equal to T still to take; total_eq = keys equal to T.
 template <typename KeyF>
-__device__ uint32_t radix_select(const KeyF &key, int64_t nb, uint32_t need, uint32_t kmin,
-                                 uint32_t kmax, SelectState &S, uint32_t &need_eq) {
-    // Bits shared by every key of the row are already fixed.
+__device__ uint32_t radix_select(const KeyF &key, int64_t n, uint32_t need, uint32_t kmin,
+                                 uint32_t kmax, TopkShared &S, uint32_t &need_eq,
+                                 uint32_t &total_eq) {
     const uint32_t diff = kmin ^ kmax;
     if (diff == 0) {
         need_eq = need;
+        total_eq = (uint32_t)n;
         return kmin;
     }
-    int hi_bit = 31 - __builtin_clz(diff);       // highest differing bit
-    uint32_t prefix = kmax & ~((2u << hi_bit) - 1u) ;  // shared bits above hi_bit
-    if (hi_bit == 31) prefix = 0;
-    int lo_bit = hi_bit + 1;                     // bits >= lo_bit are fixed in `prefix`
+    const int hi_bit = 31 - __builtin_clz(diff);
+    uint32_t prefix = hi_bit == 31 ? 0u : (kmax & ~((2u << hi_bit) - 1u));
+    int lo_bit = hi_bit + 1;                     // bits >= lo_bit are fixed
+    total_eq = 0;
     while (lo_bit > 0) {
         const int width = lo_bit >= kDigitBits ? kDigitBits : lo_bit;
         const int shift = lo_bit - width;
-        const uint32_t mask_hi = (lo_bit >= 32) ? 0u : ~((1u << lo_bit) - 1u);
+        const uint32_t mask_hi = lo_bit >= 32 ? 0u : ~((1u << lo_bit) - 1u);
         for (int t = threadIdx.x; t < kBins; t += kTopkThreads) S.hist[t] = 0;
         __syncthreads();
-        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+#pragma unroll 4
+        for (int64_t b = threadIdx.x; b < n; b += kTopkThreads) {
             const uint32_t k = key(b);
-            if ((k & mask_hi) == prefix)
-                atomicAdd(&S.hist[(k >> shift) & ((1u << width) - 1u)], 1u);
+            if ((k & mask_hi) == prefix) atomicAdd(&S.hist[(k >> shift) & ((1u << width) - 1u)], 1u);
         }
         __syncthreads();
-        // Scan bins from the top: find digit d with above(d) < need <= above(d) + hist[d].
-        if (threadIdx.x < kWave) {
-            const int lane = threadIdx.x;
-            constexpr int kPer = kBins / kWave;
-            const int nbins = 1 << width;
-            // lane j owns bins [top - (j+1)*per, top - j*per) counted from the top
-            uint32_t sum = 0;
-            for (int e = 0; e < kPer; ++e) {
-                const int bin = nbins - 1 - (lane * kPer + e);
-                if (bin >= 0) sum += S.hist[bin];
-            }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                uint32_t y = __shfl_up(incl, o, kWave);
-                if (lane >= o) incl += y;
-            }
-            const uint32_t excl = incl - sum;
-            if (excl < need && need <= incl) {
-                uint32_t run = excl;
-                for (int e = 0; e < kPer; ++e) {
-                    const int bin = nbins - 1 - (lane * kPer + e);
-                    const uint32_t h = S.hist[bin];
-                    if (run + h >= need) {
-                        S.sh_digit = (uint32_t)bin;
-                        S.sh_need = need - run;
-                        break;
-                    }
-                    run += h;
-                }
-            }
-        }
-        __syncthreads();
-        prefix |= S.sh_digit << shift;
-        need = S.sh_need;
+        uint32_t above;
+        const int d = find_bin(1 << width, need, S, above);
+        total_eq = S.hist[d];
+        prefix |= (uint32_t)d << shift;
+        need -= above;
         lo_bit = shift;
         __syncthreads();
     }
@@ -167,62 +168,165 @@ __device__ uint32_t radix_select(const KeyF &key, int64_t nb, uint32_t need, uin
     return prefix;
 }
 
-// Ordered output: every b with key > T, plus the first need_eq with key == T.
+// Replace per-(round, wave) counts cnt[0..n) by their exclusive prefix sums.
+__device__ __forceinline__ void scan_counts(uint32_t *cnt, int n, TopkShared &S) {
+    uint32_t tot;
+    const int t0 = 2 * (int)threadIdx.x;
+    const uint32_t c0 = t0 < n ? cnt[t0] : 0u, c1 = t0 + 1 < n ? cnt[t0 + 1] : 0u;
+    const uint32_t ex = wg_scan(c0 + c1, S, tot);
+    if (t0 < n) cnt[t0] = ex;
+    if (t0 + 1 < n) cnt[t0 + 1] = ex + c0;
+    __syncthreads();
+}
+
+// Ordered output: every key > T, then the first need_eq keys == T by index.
 template <typename KeyF>
 __device__ void emit_selection(const KeyF &key, int64_t nb, uint32_t T, uint32_t need_eq,
-                               int32_t *__restrict__ out, int K, SelectState &S) {
-    const int64_t per = (nb + kTopkThreads - 1) / kTopkThreads;
-    const int64_t beg = imin64((int64_t)threadIdx.x * per, nb);
-    const int64_t end = imin64(beg + per, nb);
-    uint32_t gt[kMaskWords], eq[kMaskWords];
+                               uint32_t total_eq, int32_t *__restrict__ out, int K, TopkShared &S) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int rounds = (int)((nb + kTopkThreads - 1) / kTopkThreads);
+    const int ncnt = rounds * kTopkWaves;
+    const bool all_eq = need_eq >= total_eq;
+    uint32_t *cnt = S.hist;
+    // selected-element masks, one bit per round
+    uint32_t selm[kMaskWords];
 #pragma unroll
-    for (int w = 0; w < kMaskWords; ++w) { gt[w] = 0; eq[w] = 0; }
-    uint32_t n_eq = 0;
-    for (int64_t b = beg; b < end; ++b) {
-        const uint32_t k = key(b);
-        const int e = (int)(b - beg);
-        if (k > T) gt[e >> 5] |= 1u << (e & 31);
-        if (k == T) { eq[e >> 5] |= 1u << (e & 31); ++n_eq; }
-    }
-    uint32_t tot;
-    const uint32_t eq_before = block_exclusive_scan(n_eq, S.tmp, tot);
-    // keep only the first need_eq equal keys (index order)
-    uint32_t run = eq_before;
-    uint32_t n_sel = 0;
+    for (int g = 0; g < kMaskWords; ++g) {
+        selm[g] = 0;
+        if (g * 32 >= rounds) continue;
 #pragma unroll
-    for (int w = 0; w < kMaskWords; ++w) {
-        uint32_t m = eq[w], keep = 0;
-        while (m) {
-            const uint32_t bit = m & (~m + 1u);
-            if (run < need_eq) keep |= bit;
-            ++run;
-            m ^= bit;
+        for (int u = 0; u < 32; ++u) {
+            const int j = g * 32 + u;
+            const int64_t b = (int64_t)j * kTopkThreads + threadIdx.x;
+            if (j < rounds && b < nb && key(b) >= T) selm[g] |= 1u << u;
         }
-        gt[w] |= keep;
-        n_sel += __builtin_popcount(gt[w]);
     }
-    uint32_t pos = block_exclusive_scan(n_sel, S.tmp, tot);
+    if (!all_eq) {
+        // Ties at T: rank them in index order and keep the first need_eq.
 #pragma unroll
-    for (int w = 0; w < kMaskWords; ++w) {
-        uint32_t m = gt[w];
-        while (m) {
-            const int bit = __builtin_ctz(m);
-            if (pos < (uint32_t)K) out[pos] = (int32_t)(beg + w * 32 + bit);
-            ++pos;
-            m &= m - 1u;
+        for (int g = 0; g < kMaskWords; ++g) {
+            if (g * 32 >= rounds) continue;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int j = g * 32 + u;
+                const int64_t b = (int64_t)j * kTopkThreads + threadIdx.x;
+                const bool eq = j < rounds && b < nb && key(b) == T;
+                const uint64_t m = __ballot(eq);
+                if (lane == 0 && j < rounds) cnt[j * kTopkWaves + wave] = (uint32_t)__builtin_popcountll(m);
+            }
+        }
+        __syncthreads();
+        scan_counts(cnt, ncnt, S);
+#pragma unroll
+        for (int g = 0; g < kMaskWords; ++g) {
+            if (g * 32 >= rounds) continue;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int j = g * 32 + u;
+                const int64_t b = (int64_t)j * kTopkThreads + threadIdx.x;
+                const bool eq = j < rounds && b < nb && key(b) == T;
+                const uint64_t m = __ballot(eq);
+                if (eq) {
+                    const uint32_t rank = cnt[j * kTopkWaves + wave] + lanes_below(m);
+                    if (rank >= need_eq) selm[g] &= ~(1u << u);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // per-(round, wave) counts of selected elements -> output offsets
+#pragma unroll
+    for (int g = 0; g < kMaskWords; ++g) {
+        if (g * 32 >= rounds) continue;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            const int j = g * 32 + u;
+            const uint64_t m = __ballot((selm[g] >> u) & 1u);
+            if (lane == 0 && j < rounds) cnt[j * kTopkWaves + wave] = (uint32_t)__builtin_popcountll(m);
+        }
+    }
+    __syncthreads();
+    scan_counts(cnt, ncnt, S);
+#pragma unroll
+    for (int g = 0; g < kMaskWords; ++g) {
+        if (g * 32 >= rounds) continue;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            const int j = g * 32 + u;
+            const bool sel = (selm[g] >> u) & 1u;
+            const uint64_t m = __ballot(sel);
+            if (sel) {
+                const uint32_t pos = cnt[j * kTopkWaves + wave] + lanes_below(m);
+                if (pos < (uint32_t)K) out[pos] = (int32_t)((int64_t)j * kTopkThreads + threadIdx.x);
+            }
         }
     }
 }
 
-struct PlainKey {
+struct GlobalKey {
     const float *__restrict__ row;
     __device__ __forceinline__ uint32_t operator()(int64_t b) const { return order_key(row[b]); }
 };
 
+struct LdsKey {
+    const uint32_t *keys;
+    __device__ __forceinline__ uint32_t operator()(int64_t b) const { return keys[b]; }
+};
+
+template <typename KeyF>
+__device__ void select_row(const KeyF &key, int64_t nb, int K, uint32_t kmin, uint32_t kmax,
+                           int32_t *__restrict__ out, TopkShared &S) {
+    uint32_t need_eq, total_eq, T;
+    const float vmin = key_value(kmin), vmax = key_value(kmax);
+    const float scale = (float)kBins / (vmax - vmin);
+    if (kmin == kmax || !(scale < 3.0e38f)) {
+        // flat (or numerically flat) row: exact radix over the row
+        T = radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
+    } else {
+        for (int t = threadIdx.x; t < kBins; t += kTopkThreads) S.hist[t] = 0;
+        if (threadIdx.x == 0) S.s2 = 0;
+        __syncthreads();
+#pragma unroll 4
+        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+            const float x = key_value(key(b));
+            const int bin = min(kBins - 1, (int)((x - vmin) * scale));
+            atomicAdd(&S.hist[bin], 1u);
+        }
+        __syncthreads();
+        uint32_t above;
+        const int tb = find_bin(kBins, (uint32_t)K, S, above);
+        const uint32_t m = S.hist[tb];
+        const uint32_t need = (uint32_t)K - above;
+        __syncthreads();
+        if (m <= (uint32_t)kCandMax) {
+            // copy the threshold bin's keys, tracking their range
+            uint32_t cmin = 0xffffffffu, cmax = 0u;
+#pragma unroll 4
+            for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+                const uint32_t k = key(b);
+                const int bin = min(kBins - 1, (int)((key_value(k) - vmin) * scale));
+                if (bin == tb) {
+                    S.cand[atomicAdd(&S.s2, 1u)] = k;
+                    cmin = min(cmin, k);
+                    cmax = max(cmax, k);
+                }
+            }
+            wg_minmax(cmin, cmax, S);      // its barriers publish S.cand
+            T = radix_select(LdsKey{S.cand}, (int64_t)m, need, cmin, cmax, S, need_eq, total_eq);
+        } else {
+            T = radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
+        }
+    }
+    emit_selection(key, nb, T, need_eq, total_eq, out, K, S);
+}
+
+template <bool CACHED>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx) {
-    __shared__ SelectState S;
+    __shared__ TopkShared S;
+    extern __shared__ uint32_t lds_keys[];
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
@@ -231,18 +335,40 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         for (int t = threadIdx.x; t < K; t += kTopkThreads) out[t] = (t < nb) ? t : -1;
         return;
     }
-    PlainKey key{scores + i * ld};
+    const float *__restrict__ row = scores + i * ld;
     uint32_t kmin = 0xffffffffu, kmax = 0u;
-    for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
-        const uint32_t k = key(b);
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
+    if constexpr (CACHED) {
+        // One streaming pass: every load of the thread (at most 32) is issued
+        // before the first is consumed, so the row costs one memory latency.
+        constexpr int kR = kLdsKeys / kTopkThreads;
+        uint32_t kk[kR];
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
+            kk[u] = b < nb ? order_key(row[b]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
+            if (b < nb) {
+                lds_keys[b] = kk[u];
+                kmin = min(kmin, kk[u]);
+                kmax = max(kmax, kk[u]);
+            }
+        }
+        wg_minmax(kmin, kmax, S);     // its barrier also publishes lds_keys
+        select_row(LdsKey{lds_keys}, nb, K, kmin, kmax, out, S);
+    } else {
+        const GlobalKey key{row};
+#pragma unroll 4
+        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+            const uint32_t k = key(b);
+            kmin = min(kmin, k);
+            kmax = max(kmax, k);
+        }
+        wg_minmax(kmin, kmax, S);
+        select_row(key, nb, K, kmin, kmax, out, S);
     }
-    kmin = block_reduce_min_u(kmin, S.tmp);
-    kmax = block_reduce_max_u(kmax, S.tmp);
-    uint32_t need_eq;
-    const uint32_t T = radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq);
-    emit_selection(key, nb, T, need_eq, out, K, S);
 }
 
 }  // namespace
@@ -259,10 +385,27 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
     if (b.total_q == 0) return hipSuccess;
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int K = budget / ratio;
+    const int64_t max_nb = b.max_kv_len >> log2r;
     dim3 grid((unsigned)b.total_q);
-    trace("topk grid=%u K=%d ratio=%d", grid.x, K, ratio);
-    hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, st, scores, ld, b.kv_offsets,
-                       b.q_offsets, b.num_seqs, log2r, K, idx);
+    if (max_nb <= kLdsKeys) {
+        // Dynamic LDS above the 64 KB default must be enabled for the kernel.
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(once, [] {
+            attr_err = hipFuncSetAttribute((const void *)topk_kernel<true>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(kLdsKeys * sizeof(uint32_t)));
+        });
+        if (attr_err != hipSuccess) return attr_err;
+        const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * sizeof(uint32_t);
+        trace("topk grid=%u K=%d ratio=%d lds_keys=%lld", grid.x, K, ratio, (long long)max_nb);
+        hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTopkThreads), lds, st, scores, ld,
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx);
+    } else {
+        trace("topk grid=%u K=%d ratio=%d streaming", grid.x, K, ratio);
+        hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(kTopkThreads), 0, st, scores, ld,
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx);
+    }
     return hipGetLastError();
 }
 

@@ -152,7 +152,8 @@ def test_workspace_sizes():
     b = _batch(total_q=32, num_seqs=32)
     a = _attn()
     n = Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2048, 4)
-    # 16 splits of 32 blocks: (m, l) + 128 partial outputs per split and head
+    # decode cuts K=512 into 16 parts: 16 partials of (m, l) + 128 outputs
+    # per query head
     assert n >= 32 * 32 * 16 * 130 * 4
     assert Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, None) == 0
     assert Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2047, 4) == 0
