@@ -236,6 +236,10 @@ qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_ind
     if (s == QSA_OK) s = check_rows(b, ratio);
     if (s == QSA_OK && recheck) s = check_indexer(recheck, false);
     if (s != QSA_OK) return s;
+    if (recheck && b->max_kv_len / ratio > kTopkRecheckMaxBlocks)
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "re-checked top-k supports at most %lld blocks per row (max_kv_len/ratio=%lld)",
+                    (long long)kTopkRecheckMaxBlocks, (long long)(b->max_kv_len / ratio));
     if (!scores) return fail(QSA_ERR_INVALID_ARGUMENT, "scores is NULL");
     if (!idx) return fail(QSA_ERR_INVALID_ARGUMENT, "idx is NULL");
     const int64_t need_ld = (b->max_kv_len + ratio - 1) / ratio;

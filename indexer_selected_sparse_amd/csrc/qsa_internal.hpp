@@ -24,7 +24,9 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
 hipError_t launch_score_mfma(const qsa_indexer &ix, int ratio, const qsa_batch &b, float *scores,
                              int64_t ld, hipStream_t st);
 
-// Block top-k.  recheck == nullptr: scores are canonical.
+// Block top-k.  recheck == nullptr: scores are canonical.  With recheck the
+// rows are cached whole in LDS, which bounds the blocks per row.
+constexpr int64_t kTopkRecheckMaxBlocks = 32768;
 size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa_indexer *recheck);
 hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *recheck, int budget,
                        int ratio, const qsa_batch &b, int32_t *idx, void *ws, hipStream_t st);

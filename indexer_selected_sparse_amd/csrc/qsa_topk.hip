@@ -274,51 +274,82 @@ struct LdsKey {
     __device__ __forceinline__ uint32_t operator()(int64_t b) const { return keys[b]; }
 };
 
+// The K-th largest key T of the row, how many keys equal T the selection
+// still needs (need_eq) and how many there are (total_eq).
 template <typename KeyF>
-__device__ void select_row(const KeyF &key, int64_t nb, int K, uint32_t kmin, uint32_t kmax,
-                           int32_t *__restrict__ out, TopkShared &S) {
-    uint32_t need_eq, total_eq, T;
+__device__ uint32_t find_threshold(const KeyF &key, int64_t nb, int K, uint32_t kmin, uint32_t kmax,
+                                   TopkShared &S, uint32_t &need_eq, uint32_t &total_eq) {
     const float vmin = key_value(kmin), vmax = key_value(kmax);
     const float scale = (float)kBins / (vmax - vmin);
     if (kmin == kmax || !(scale < 3.0e38f)) {
         // flat (or numerically flat) row: exact radix over the row
-        T = radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
-    } else {
-        for (int t = threadIdx.x; t < kBins; t += kTopkThreads) S.hist[t] = 0;
-        if (threadIdx.x == 0) S.s2 = 0;
-        __syncthreads();
+        return radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
+    }
+    for (int t = threadIdx.x; t < kBins; t += kTopkThreads) S.hist[t] = 0;
+    if (threadIdx.x == 0) S.s2 = 0;
+    __syncthreads();
 #pragma unroll 4
-        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
-            const float x = key_value(key(b));
-            const int bin = min(kBins - 1, (int)((x - vmin) * scale));
-            atomicAdd(&S.hist[bin], 1u);
-        }
-        __syncthreads();
-        uint32_t above;
-        const int tb = find_bin(kBins, (uint32_t)K, S, above);
-        const uint32_t m = S.hist[tb];
-        const uint32_t need = (uint32_t)K - above;
-        __syncthreads();
-        if (m <= (uint32_t)kCandMax) {
-            // copy the threshold bin's keys, tracking their range
-            uint32_t cmin = 0xffffffffu, cmax = 0u;
+    for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+        const float x = key_value(key(b));
+        const int bin = min(kBins - 1, (int)((x - vmin) * scale));
+        atomicAdd(&S.hist[bin], 1u);
+    }
+    __syncthreads();
+    uint32_t above;
+    const int tb = find_bin(kBins, (uint32_t)K, S, above);
+    const uint32_t m = S.hist[tb];
+    const uint32_t need = (uint32_t)K - above;
+    __syncthreads();
+    if (m > (uint32_t)kCandMax) return radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
+    // copy the threshold bin's keys, tracking their range
+    uint32_t cmin = 0xffffffffu, cmax = 0u;
 #pragma unroll 4
-            for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
-                const uint32_t k = key(b);
-                const int bin = min(kBins - 1, (int)((key_value(k) - vmin) * scale));
-                if (bin == tb) {
-                    S.cand[atomicAdd(&S.s2, 1u)] = k;
-                    cmin = min(cmin, k);
-                    cmax = max(cmax, k);
-                }
-            }
-            wg_minmax(cmin, cmax, S);      // its barriers publish S.cand
-            T = radix_select(LdsKey{S.cand}, (int64_t)m, need, cmin, cmax, S, need_eq, total_eq);
-        } else {
-            T = radix_select(key, nb, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
+    for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+        const uint32_t k = key(b);
+        const int bin = min(kBins - 1, (int)((key_value(k) - vmin) * scale));
+        if (bin == tb) {
+            S.cand[atomicAdd(&S.s2, 1u)] = k;
+            cmin = min(cmin, k);
+            cmax = max(cmax, k);
         }
     }
+    wg_minmax(cmin, cmax, S);      // its barriers publish S.cand
+    return radix_select(LdsKey{S.cand}, (int64_t)m, need, cmin, cmax, S, need_eq, total_eq);
+}
+
+template <typename KeyF>
+__device__ void select_row(const KeyF &key, int64_t nb, int K, uint32_t kmin, uint32_t kmax,
+                           int32_t *__restrict__ out, TopkShared &S) {
+    uint32_t need_eq, total_eq;
+    const uint32_t T = find_threshold(key, nb, K, kmin, kmax, S, need_eq, total_eq);
     emit_selection(key, nb, T, need_eq, total_eq, out, K, S);
+}
+
+// Row -> order keys in LDS (rows of at most kLdsKeys blocks) and their range.
+// One streaming pass: every load of the thread (at most 32) is issued before
+// the first is consumed, so the row costs one memory latency.
+__device__ __forceinline__ void cache_row(const float *__restrict__ row, int64_t nb,
+                                          uint32_t *lds_keys, uint32_t &kmin, uint32_t &kmax,
+                                          TopkShared &S) {
+    constexpr int kR = kLdsKeys / kTopkThreads;
+    uint32_t kk[kR];
+#pragma unroll
+    for (int u = 0; u < kR; ++u) {
+        const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
+        kk[u] = b < nb ? order_key(row[b]) : 0u;
+    }
+    kmin = 0xffffffffu;
+    kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < kR; ++u) {
+        const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
+        if (b < nb) {
+            lds_keys[b] = kk[u];
+            kmin = min(kmin, kk[u]);
+            kmax = max(kmax, kk[u]);
+        }
+    }
+    wg_minmax(kmin, kmax, S);     // its barrier also publishes lds_keys
 }
 
 template <bool CACHED>
@@ -338,25 +369,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ row = scores + i * ld;
     uint32_t kmin = 0xffffffffu, kmax = 0u;
     if constexpr (CACHED) {
-        // One streaming pass: every load of the thread (at most 32) is issued
-        // before the first is consumed, so the row costs one memory latency.
-        constexpr int kR = kLdsKeys / kTopkThreads;
-        uint32_t kk[kR];
-#pragma unroll
-        for (int u = 0; u < kR; ++u) {
-            const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
-            kk[u] = b < nb ? order_key(row[b]) : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < kR; ++u) {
-            const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
-            if (b < nb) {
-                lds_keys[b] = kk[u];
-                kmin = min(kmin, kk[u]);
-                kmax = max(kmax, kk[u]);
-            }
-        }
-        wg_minmax(kmin, kmax, S);     // its barrier also publishes lds_keys
+        cache_row(row, nb, lds_keys, kmin, kmax, S);
         select_row(LdsKey{lds_keys}, nb, K, kmin, kmax, out, S);
     } else {
         const GlobalKey key{row};
@@ -371,33 +384,362 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
 }
 
+// ------------------------------------------------------------------------
+// Certified selection from approximate (matrix-core) scores.
+//
+// The scores a_b come from a summation order other than the canonical one.
+// Both a_b and the canonical c_b are fp32 evaluations of
+//   S_b = sum_h w_h ReLU(q_h . k_b)
+// whose D-term dots have bf16*bf16 (or exactly widened) products.  With unit
+// roundoff u = 2^-23 (valid for round-to-nearest and for truncation) and
+// gamma_n = n u / (1 - n u), the classic summation bound (Higham, Accuracy and
+// Stability of Numerical Algorithms, section 4.2) gives, for any order,
+// |dot - q.k| <= gamma_(D+1) sum_d |q_d k_d| <= gamma_(D+1) |q| |k| (Cauchy-
+// Schwarz; the +1 covers an e4m3 scale multiply).  ReLU is 1-Lipschitz, and
+// the head sum of H rounded products adds gamma_(H+1) sum_h |w_h| r_h.  Hence
+//   |a_b - S_b|, |c_b - S_b| <= (gamma_(D+1) + gamma_(H+1)(1 + gamma_(D+1))) P_b
+//   with P_b = sum_h |w_h| |q_h| |k_b|,
+// and |a_b - c_b| <= 2 (D + H + 2) u P_b (1 + O(nu)).  The kernel uses
+//   E = 4 (D + H + 2) u * F * n_max * (1 + 2^-10) + (1 + sum_h |w_h|) 2^-100,
+//   F = sum_h |w_h| |q_h|,  n_max = max_b |k_b| over the sequence,
+// i.e. twice the bound, so that the fp32 evaluation of F, n_max and t +- 2E
+// below stays on the safe side (their relative errors are O((D+H)u), far
+// below the slack), and the absolute term covers products or head terms
+// that underflow (flushed or subnormal).
+//
+// With t the K-th largest a, a block with a_b > t + 2E is certainly among
+// the canonical top K (at most K-1 blocks have a > t, and every block that
+// could beat it has c > t + E), and a block with a_b < t - 2E is certainly
+// out (at least K blocks have c >= t - E > c_b).  The remaining band blocks
+// (typically tens) are recomputed in the canonical order; the free slots go
+// to the band's best by (c desc, index asc).  The result is the canonical
+// selection, bit for bit.  A band larger than the candidate buffer (flat or
+// adversarial rows) recomputes the whole row canonically instead.
+
+constexpr int kNormThreads = 256;
+constexpr int kMaxHD = 16 * 128;
+
+// Max over chunks of kNormThreads blocks of |kc_b| (fp32; e4m3 codes times
+// the block scale): part[s * n_chunks + chunk].  Every slot is written.
+__global__ __launch_bounds__(kNormThreads) void block_norm_kernel(
+    const void *__restrict__ kc, int kc_dtype, const float *__restrict__ kc_scale, int D,
+    const int64_t *__restrict__ blk_off, int n_chunks, float *__restrict__ part) {
+    __shared__ float wmax[kNormThreads / kWave];
+    const int s = blockIdx.y;
+    const int64_t kb0 = blk_off[s];
+    const int64_t nblk = blk_off[s + 1] - kb0;
+    const int64_t b = (int64_t)blockIdx.x * kNormThreads + threadIdx.x;
+    float n = 0.0f;
+    if (b < nblk) {
+        float ss = 0.0f;
+        const int64_t row = kb0 + b;
+        if (kc_dtype == QSA_F32) {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(kc) + row * D);
+            for (int c = 0; c < D / 4; ++c) {
+                const float4 x = p[c];
+                ss = ss + x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+            }
+        } else if (kc_dtype == QSA_BF16) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(kc) + row * D);
+            for (int c = 0; c < D / 8; ++c) {
+                const uint4 x = p[c];
+                const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float lo = bf16lo(u[j]), hi = bf16hi(u[j]);
+                    ss = ss + lo * lo + hi * hi;
+                }
+            }
+        } else {
+            const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(kc) + row * D);
+            for (int c = 0; c < D / 16; ++c) {
+                const uint4 x = p[c];
+                const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float2 lo = e4m3x2_to_f32<false>(u[j]), hi = e4m3x2_to_f32<true>(u[j]);
+                    ss = ss + lo.x * lo.x + lo.y * lo.y + hi.x * hi.x + hi.y * hi.y;
+                }
+            }
+        }
+        n = __builtin_sqrtf(ss);
+        if (kc_dtype == QSA_FP8_E4M3) n = n * kc_scale[row];
+    }
+    n = wave_max(n);
+    if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = n;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = wmax[0];
+        for (int w = 1; w < kNormThreads / kWave; ++w) m = fmaxf(m, wmax[w]);
+        part[(int64_t)s * n_chunks + blockIdx.x] = m;
+    }
+}
+
+struct CertIndexer {
+    const void *q_idx;
+    const float *w;
+    const void *kc;
+    const float *kc_scale;
+    int q_dtype, kc_dtype, H, D;
+};
+
+// Canonical dot of query head row qh (fp32, LDS) with key row `row`:
+// +0, then d ascending, rounded product then rounded sum; e4m3 keys are
+// code values times the block scale afterwards.
+__device__ float canonical_dot(const CertIndexer &ix, const float *qh, int64_t row) {
+    const int D = ix.D;
+    float dot = 0.0f;
+    if (ix.kc_dtype == QSA_F32) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(ix.kc) + row * D);
+        for (int c = 0; c < D / 4; ++c) {
+            const float4 x = p[c];
+            dot = dot + qh[4 * c + 0] * x.x;
+            dot = dot + qh[4 * c + 1] * x.y;
+            dot = dot + qh[4 * c + 2] * x.z;
+            dot = dot + qh[4 * c + 3] * x.w;
+        }
+    } else if (ix.kc_dtype == QSA_BF16) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(ix.kc) + row * D);
+        for (int c = 0; c < D / 8; ++c) {
+            const uint4 x = p[c];
+            const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dot = dot + qh[8 * c + 2 * j] * bf16lo(u[j]);
+                dot = dot + qh[8 * c + 2 * j + 1] * bf16hi(u[j]);
+            }
+        }
+    } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(ix.kc) + row * D);
+        for (int c = 0; c < D / 16; ++c) {
+            const uint4 x = p[c];
+            const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float2 lo = e4m3x2_to_f32<false>(u[j]), hi = e4m3x2_to_f32<true>(u[j]);
+                dot = dot + qh[16 * c + 4 * j + 0] * lo.x;
+                dot = dot + qh[16 * c + 4 * j + 1] * lo.y;
+                dot = dot + qh[16 * c + 4 * j + 2] * hi.x;
+                dot = dot + qh[16 * c + 4 * j + 3] * hi.y;
+            }
+        }
+        dot = dot * ix.kc_scale[row];
+    }
+    return dot;
+}
+
+struct CertShared {
+    float q[kMaxHD + 16];        // query rows, head stride D+1
+    float w[16];
+    float part[kMaxHD / kWave];
+    float F, wabs, nmax;
+};
+
+struct BandKey {
+    const uint32_t *cand;
+    const uint32_t *keys;
+    __device__ __forceinline__ uint32_t operator()(int64_t j) const { return keys[cand[j]]; }
+};
+
+__global__ __launch_bounds__(kTopkThreads) void topk_cert_kernel(
+    const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
+    int log2r, int K, int32_t *__restrict__ idx, CertIndexer ix,
+    const float *__restrict__ norm_part, int n_norm_chunks) {
+    __shared__ TopkShared S;
+    __shared__ CertShared C;
+    extern __shared__ uint32_t lds_keys[];
+    const int64_t i = blockIdx.x;
+    const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    int32_t *out = idx + i * (int64_t)K;
+    if (nb <= K) {
+        for (int t = threadIdx.x; t < K; t += kTopkThreads) out[t] = (t < nb) ? t : -1;
+        return;
+    }
+    const int H = ix.H, D = ix.D, HD = H * D;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+
+    // query rows to LDS (fp32, exact widening) and |q|^2 partials per group
+    // of 64 consecutive elements (a group never straddles heads: D is a
+    // multiple of 64)
+    for (int e0 = 0; e0 < HD; e0 += kTopkThreads) {
+        const int e = e0 + (int)threadIdx.x;
+        float x = 0.0f;
+        if (e < HD) {
+            x = ix.q_dtype == QSA_F32 ? static_cast<const float *>(ix.q_idx)[i * HD + e]
+                                      : bf16_to_f32(static_cast<const uint16_t *>(ix.q_idx)[i * HD + e]);
+            const int h = e / D, d = e - h * D;
+            C.q[h * (D + 1) + d] = x;
+        }
+        const float sq = wave_sum(x * x);
+        if (lane == 0) C.part[e / kWave] = sq;
+    }
+    if ((int)threadIdx.x < H) C.w[threadIdx.x] = ix.w[i * H + threadIdx.x];
+    // n_max over the sequence's chunks (every block of the sequence bounds
+    // the visible ones)
+    float nm = 0.0f;
+    for (int c = threadIdx.x; c < n_norm_chunks; c += kTopkThreads)
+        nm = fmaxf(nm, norm_part[(int64_t)qp.seq * n_norm_chunks + c]);
+    nm = wave_max(nm);
+    const float *__restrict__ row = scores + i * ld;
+    uint32_t kmin, kmax;
+    cache_row(row, nb, lds_keys, kmin, kmax, S);     // barriers publish C.part too
+    if (lane == 0) S.wmax[wave] = __float_as_uint(nm);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float F = 0.0f, wabs = 0.0f;
+        const int wpd = D / kWave;
+        for (int h = 0; h < H; ++h) {
+            float ss = 0.0f;
+            for (int j = 0; j < wpd; ++j) ss = ss + C.part[h * wpd + j];
+            F = F + fabsf(C.w[h]) * __builtin_sqrtf(ss);
+            wabs = wabs + fabsf(C.w[h]);
+        }
+        float n = 0.0f;
+        for (int w = 0; w < kTopkWaves; ++w) n = fmaxf(n, __uint_as_float(S.wmax[w]));
+        C.F = F;
+        C.wabs = wabs;
+        C.nmax = n;
+        S.s2 = 0;
+        S.s3 = 0;
+    }
+    __syncthreads();
+    const float c_rel = 4.0f * (float)(D + H + 2) * 0x1p-23f * (1.0f + 0x1p-10f);
+    const float E = c_rel * C.F * C.nmax + (1.0f + C.wabs) * 0x1p-100f;
+
+    uint32_t need_eq, total_eq;
+    bool overflow = !(E <= 1.0e30f);
+    if (!overflow) {
+        // t = K-th largest approximate score; classify against t -+ 2E
+        const uint32_t T = find_threshold(LdsKey{lds_keys}, nb, K, kmin, kmax, S, need_eq, total_eq);
+        const float t = key_value(T);
+        const uint32_t k_in = order_key(t + 2.0f * E), k_out = order_key(t - 2.0f * E);
+        if (threadIdx.x == 0) { S.s2 = 0; S.s3 = 0; }
+        __syncthreads();
+        uint32_t n_in = 0;
+        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+            const uint32_t k = lds_keys[b];
+            if (k > k_in) {
+                lds_keys[b] = 0xffffffffu;          // certainly selected
+                ++n_in;
+            } else if (k < k_out) {
+                lds_keys[b] = 0u;                   // certainly not
+            } else {
+                const uint32_t pos = atomicAdd(&S.s2, 1u);
+                if (pos < (uint32_t)kCandMax) S.cand[pos] = (uint32_t)b;
+            }
+        }
+        atomicAdd(&S.s3, n_in);
+        __syncthreads();
+        overflow = S.s2 > (uint32_t)kCandMax;
+    }
+    const uint32_t n_band = S.s2, n_in = S.s3;
+    const int64_t items = overflow ? nb : (int64_t)n_band;
+    // canonical recompute: item j, head h on thread (j % per) * H + h
+    const int per = kTopkThreads / H;
+    float *dots = reinterpret_cast<float *>(S.hist);
+    for (int64_t j0 = 0; j0 < items; j0 += per) {
+        __syncthreads();
+        const int64_t j = j0 + threadIdx.x / H;
+        const int h = threadIdx.x % H;
+        if ((int)threadIdx.x < per * H && j < items) {
+            const int64_t b = overflow ? j : (int64_t)S.cand[j];
+            dots[threadIdx.x] = canonical_dot(ix, C.q + h * (D + 1), qp.blk_row0 + b);
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < per && j0 + threadIdx.x < items) {
+            const int64_t jj = j0 + threadIdx.x;
+            const int64_t b = overflow ? jj : (int64_t)S.cand[jj];
+            float sc = 0.0f;
+            for (int hh = 0; hh < H; ++hh) {
+                const float dt = dots[threadIdx.x * H + hh];
+                const float r = dt > 0.0f ? dt : 0.0f;
+                sc = sc + C.w[hh] * r;
+            }
+            lds_keys[b] = order_key(sc);
+        }
+    }
+    __syncthreads();
+    if (overflow) {
+        // every key is canonical now: the plain selection
+        kmin = 0xffffffffu;
+        kmax = 0u;
+        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+            kmin = min(kmin, lds_keys[b]);
+            kmax = max(kmax, lds_keys[b]);
+        }
+        wg_minmax(kmin, kmax, S);
+        select_row(LdsKey{lds_keys}, nb, K, kmin, kmax, out, S);
+        return;
+    }
+    // free slots K - n_in go to the band's best by (canonical key, index)
+    const BandKey bk{S.cand, lds_keys};
+    uint32_t bmin = 0xffffffffu, bmax = 0u;
+    for (int64_t j = threadIdx.x; j < (int64_t)n_band; j += kTopkThreads) {
+        bmin = min(bmin, bk(j));
+        bmax = max(bmax, bk(j));
+    }
+    wg_minmax(bmin, bmax, S);
+    const uint32_t T = radix_select(bk, (int64_t)n_band, (uint32_t)K - n_in, bmin, bmax, S, need_eq,
+                                    total_eq);
+    // certainly-in keys are all-ones (> any finite key), certainly-out keys
+    // are 0 (< any finite key): only band keys can equal T
+    emit_selection(LdsKey{lds_keys}, nb, T, need_eq, total_eq, out, K, S);
+}
+
 }  // namespace
 
+static int64_t norm_chunks(const qsa_batch &b, int ratio) {
+    const int64_t max_nb = b.max_kv_len / ratio;
+    return max_nb > 0 ? (max_nb + kNormThreads - 1) / kNormThreads : 1;
+}
+
 size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa_indexer *recheck) {
-    (void)b; (void)budget; (void)ratio; (void)recheck;
-    return 0;
+    (void)budget;
+    if (recheck == nullptr) return 0;
+    return (size_t)b.num_seqs * (size_t)norm_chunks(b, ratio) * sizeof(float) + 256;
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *recheck, int budget,
                        int ratio, const qsa_batch &b, int32_t *idx, void *ws, hipStream_t st) {
-    (void)ws;
-    if (recheck != nullptr) return hipErrorNotSupported;
     if (b.total_q == 0) return hipSuccess;
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int K = budget / ratio;
     const int64_t max_nb = b.max_kv_len >> log2r;
+    const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * sizeof(uint32_t);
     dim3 grid((unsigned)b.total_q);
-    if (max_nb <= kLdsKeys) {
-        // Dynamic LDS above the 64 KB default must be enabled for the kernel.
-        static std::once_flag once;
-        static hipError_t attr_err = hipSuccess;
-        std::call_once(once, [] {
-            attr_err = hipFuncSetAttribute((const void *)topk_kernel<true>,
+    // Dynamic LDS above the 64 KB default must be enabled per kernel.
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+        attr_err = hipFuncSetAttribute((const void *)topk_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kLdsKeys * sizeof(uint32_t)));
+        if (attr_err == hipSuccess)
+            attr_err = hipFuncSetAttribute((const void *)topk_cert_kernel,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kLdsKeys * sizeof(uint32_t)));
-        });
-        if (attr_err != hipSuccess) return attr_err;
-        const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * sizeof(uint32_t);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    if (recheck != nullptr) {
+        if (max_nb > kTopkRecheckMaxBlocks) return hipErrorNotSupported;
+        const int nch = (int)norm_chunks(b, ratio);
+        float *part = static_cast<float *>(ws);
+        trace("topk_cert norms grid=%dx%d", nch, b.num_seqs);
+        hipLaunchKernelGGL(block_norm_kernel, dim3((unsigned)nch, (unsigned)b.num_seqs),
+                           dim3(kNormThreads), 0, st, recheck->kc, recheck->kc_dtype,
+                           recheck->kc_scale, recheck->d_idx, b.blk_offsets, nch, part);
+        const CertIndexer cix{recheck->q_idx, recheck->w, recheck->kc, recheck->kc_scale,
+                              recheck->q_dtype, recheck->kc_dtype, recheck->h_idx, recheck->d_idx};
+        trace("topk_cert grid=%u K=%d ratio=%d lds_keys=%lld", grid.x, K, ratio, (long long)max_nb);
+        hipLaunchKernelGGL(topk_cert_kernel, grid, dim3(kTopkThreads), lds, st, scores, ld,
+                           b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, cix,
+                           part, nch);
+        return hipGetLastError();
+    }
+    if (max_nb <= kLdsKeys) {
         trace("topk grid=%u K=%d ratio=%d lds_keys=%lld", grid.x, K, ratio, (long long)max_nb);
         hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTopkThreads), lds, st, scores, ld,
                            b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx);

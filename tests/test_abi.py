@@ -128,6 +128,9 @@ CASES = [
     ("topk K too large", lambda: topk(budget=4 * 4096), UNS, "budget/ratio=4096"),
     ("topk null idx", lambda: topk(idx=None), INV, "idx"),
     ("topk null scores", lambda: topk(scores=None), INV, "scores"),
+    ("topk recheck row too long", lambda: topk(recheck=_ix(), b=_batch(max_kv_len=4 * 40000), ld=40000),
+     UNS, "re-checked"),
+    ("topk recheck workspace missing", lambda: topk(recheck=_ix()), WS, "workspace"),
     ("decode hq not multiple", lambda: decode(a=_attn(hq=30)), INV, "attn.hq=30"),
     ("decode group 32", lambda: decode(a=_attn(hq=64, hkv=2)), UNS, "hq/attn.hkv=32"),
     ("decode d 64", lambda: decode(a=_attn(d=64)), UNS, "attn.d=64"),
@@ -156,4 +159,8 @@ def test_workspace_sizes():
     # per query head
     assert n >= 32 * 32 * 16 * 130 * 4
     assert Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, None) == 0
+    # re-checked top-k: one fp32 key-norm maximum per 256 blocks per sequence
+    ix = _ix()
+    n = Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, ctypes.byref(ix))
+    assert n >= 32 * (1024 // 256) * 4
     assert Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2047, 4) == 0
