@@ -1,25 +1,36 @@
-"""Benchmark of the decode hot path (score -> top-k -> sparse attention) on one
-MI355X.  Prints ONE JSON line.
+"""Benchmark of the hot path (indexer score -> block top-k -> sparse attention)
+on one MI355X.  Prints ONE JSON line.
 
-Workload (default): the batched-decode configuration — 32 sequences with
-context lengths uniform in [8192, 32768] (seed 1), one query each, 32 query
-heads / 4 KV heads, head_dim 128, bf16; indexer 8 heads x 128 bf16, ratio 4,
-budget 2048 (512 blocks).  `--config c3` selects the 8 x 131072 long-context
-decode with the e4m3 index plane instead.
+Workloads (synthetic, seeded; see qsa_workloads):
+  batched_decode (default)  32 sequences, context U[8192, 32768] (seed 1),
+                one query each, 32 query heads / 4 KV heads x 128, bf16;
+                indexer 8 x 128 bf16, ratio 4, budget 2048 (512 blocks).
+  long_decode   8 x 131072 tokens, 64/8 heads, e4m3 compressed index keys
+                with per-block fp32 scales.
+  chunked_prefill  an 8193-query causal chunk on a 32768-token prefix;
+                indexer scores on the matrix cores, certified top-k, causal
+                sparse prefill attention.
 
-A step is one pass of the whole hot path over one batch: canonical indexer
-scores, block top-k and sparse gather attention, all resident in HBM.  Key
-compression is an ingest-time pass and is timed separately (`compress_ms`).
-Steps rotate over several device copies of the inputs (more distinct bytes
-than the 256 MB last-level cache holds), so a step cannot be served from a
-cache warmed by the previous one.
+A step is one pass of the whole hot path over one batch with every input
+resident in HBM.  Key compression is an ingest-time pass, timed on its own
+(`compress_ms`).  Decode steps rotate over several device copies of the
+inputs (more distinct bytes than the 256 MB last-level cache holds), so a
+step is not served from a cache warmed by the previous one.
+
+`roofline` describes the dominant kernel: for decode, the sparse attention
+call (gather kernel + split combine), timed with HIP events on the stream it
+runs on; achieved = algorithmic bytes / its mean duration.  `traffic` comes
+from the FETCH_SIZE / WRITE_SIZE counter summary under profiles/, used only
+while the attention source is unchanged since the counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -28,7 +39,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
+VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector peak (dot2 / dual-issue forms)
+ATTN_SRC = os.path.join(ROOT, "indexer_selected_sparse_amd", "csrc", "qsa_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_hbm_traffic.md")
 
 
 def parse():
@@ -36,7 +51,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="c2", choices=["c2", "c3"])
+    p.add_argument("--workload", default="batched_decode",
+                   choices=["batched_decode", "long_decode", "chunked_prefill"])
     p.add_argument("--replicas", type=int, default=0, help="input copies to rotate over (0=auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -46,10 +62,22 @@ def parse():
     return p.parse_args()
 
 
+def token_counts(wl):
+    """Per query: (L, nb, |T|) with |T| = min(L, K*ratio + tail)."""
+    sp = wl.spec
+    K = sp.budget // sp.ratio
+    out = []
+    for L in wl.visible_lengths():
+        L = int(L)
+        nb = L // sp.ratio
+        out.append((L, nb, min(L, K * sp.ratio + (L - nb * sp.ratio))))
+    return out
+
+
 def algorithmic_bytes(wl):
-    """Per-step bytes the method must move: index scan over
-    visible compressed keys, K/V rows of the selected token set, q and out,
-    indexer query/weights and the idx row.  Scores are an intermediate and are
+    """Per-step bytes the decode method must move: index scan over the visible
+    compressed keys, K/V rows of the selected token set, q and out, indexer
+    query/weights and the idx row.  Scores are an intermediate and are
     excluded.  Returns (step_bytes, attention_bytes, score_bytes)."""
     sp = wl.spec
     s_kv = 2 if sp.kv_dtype == "bf16" else 4
@@ -58,58 +86,92 @@ def algorithmic_bytes(wl):
     s_qi = 2 if sp.idx_dtype == "bf16" else 4
     K = sp.budget // sp.ratio
     attn = score = 0
-    for L in wl.visible_lengths():
-        L = int(L)
-        nb = L // sp.ratio
-        tail = L - nb * sp.ratio
-        T = min(L, K * sp.ratio + tail)
+    for L, nb, T in token_counts(wl):
         score += nb * (sp.d_idx * s_kc + s_scale) + sp.h_idx * sp.d_idx * s_qi + 4 * sp.h_idx
         attn += T * 2 * sp.hkv * sp.d * s_kv + sp.hq * sp.d * 2 * s_kv + 4 * K
     return score + attn, attn, score
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle, as it stands, on a bounded sample: all queries of the
-    workload, repeated until about `seconds` of wall time."""
+def prefill_flops(wl):
+    """(indexer flops over visible (query, block) pairs, attention flops:
+    QK and PV over each query's token set)."""
+    sp = wl.spec
+    idx = attn = 0
+    for L, nb, T in token_counts(wl):
+        idx += 2 * nb * sp.h_idx * sp.d_idx
+        attn += 4 * T * sp.hq * sp.d
+    return idx, attn
+
+
+def recorded_traffic(workload):
+    """Bytes per launch from the counter summary, if it was taken on the
+    current attention source; else None."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    ent = rec.get("workloads", {}).get(workload)
+    if rec.get("attn_source_sha256") != src_hash or ent is None:
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(wl, seconds, prefill):
+    """The oracle, as it stands, on a bounded sample of the workload's queries
+    (all of them for decode; a fixed 64-query subset for prefill), repeated
+    until about `seconds` of wall time."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     sp = wl.spec
     kc, kc_scale = oracle.compress(wl.k_idx.float().numpy(), wl.kv_offsets, sp.ratio, sp.kc_dtype)
     kcv = oracle.kc_values(kc, sp.kc_dtype)
     blk = wl.blk_offsets()
     Ls = wl.visible_lengths()
-    seqs = []
+    qseq = wl.query_seq()
+    if prefill:
+        rng = np.random.default_rng(12345)
+        qids = np.sort(rng.choice(wl.total_q, min(64, wl.total_q), replace=False))
+    else:
+        qids = np.arange(wl.total_q)
+    jobs = []
     for s in range(wl.num_seqs):
         a, b = int(wl.kv_offsets[s]), int(wl.kv_offsets[s + 1])
-        seqs.append((wl.K[a:b].float().numpy(), wl.V[a:b].float().numpy(),
-                     kcv[blk[s]:blk[s + 1]], None if kc_scale is None else kc_scale[blk[s]:blk[s + 1]],
-                     wl.q[s:s + 1].float().numpy(), wl.q_idx[s:s + 1].float().numpy(),
-                     wl.w[s:s + 1].numpy(), Ls[s:s + 1]))
+        Kf, Vf = wl.K[a:b].float().numpy(), wl.V[a:b].float().numpy()
+        kcs = kcv[blk[s]:blk[s + 1]]
+        scs = None if kc_scale is None else kc_scale[blk[s]:blk[s + 1]]
+        for i in qids[qseq[qids] == s]:
+            jobs.append((Kf, Vf, kcs, scs, wl.q[i:i + 1].float().numpy(),
+                         wl.q_idx[i:i + 1].float().numpy(), wl.w[i:i + 1].numpy(), Ls[i:i + 1]))
     threads = oracle.max_threads()
     t0 = time.perf_counter()
-    done = 0
-    reps = 0
-    while True:
-        # parallel over queries: one call per sequence uses 1 query, so batch
-        # the sequences through a thread pool of oracle calls
-        from concurrent.futures import ThreadPoolExecutor
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            list(ex.map(lambda a: oracle.run_queries(*a, sp.ratio, sp.budget, sp.softmax_scale,
-                                                     n_threads=1), seqs))
-        done += len(seqs)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+    done = reps = 0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(lambda j: oracle.run_queries(*j, sp.ratio, sp.budget, sp.softmax_scale,
+                                                     n_threads=1), jobs))
+            done += len(jobs)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
     dt = time.perf_counter() - t0
+    what = "decode queries" if not prefill else "prefill queries (seeded subset)"
     return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x all {len(seqs)} decode queries of the workload "
-                      f"(score+sort+fp64 attention per query; compression excluded), "
-                      f"{dt:.1f} s on {threads} threads of {os.cpu_count()} host cpus"}
+            "sample": f"{reps} x {len(jobs)} {what} of the workload (score + full sort + fp64 "
+                      f"attention per query; compression excluded), {dt:.1f} s on {threads} "
+                      f"threads of {os.cpu_count()} host cpus"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "one GPU only: the method runs on a single MI355X here; "
+                                   "--gpus must be 1"}))
         sys.exit(2)
     import torch
     if args.calibrate_copy_mb:
@@ -122,14 +184,15 @@ def main():
         print(json.dumps({"calibration_copy_bytes": n, "copies": 5}))
         return
     import qsa_workloads as W
-    from indexer_selected_sparse_amd import pipeline
+    from indexer_selected_sparse_amd import QSA_SCORE_MFMA, pipeline
 
-    spec = W.CONFIGS[args.config]
+    spec = W.CONFIGS[args.workload]
+    prefill = args.workload == "chunked_prefill"
     wl = W.make(spec)
     step_bytes, attn_bytes, score_bytes = algorithmic_bytes(wl)
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    base = pipeline.upload(wl, dev, decode=True)
+    base = pipeline.upload(wl, dev, decode=not prefill, mfma_ws=prefill)
 
     # compression (ingest pass), timed on its own
     base.compress()
@@ -142,7 +205,10 @@ def main():
     torch.cuda.synchronize()
     compress_ms = ev0.elapsed_time(ev1) / 5
 
-    R = args.replicas or max(2, math.ceil(2 * 256e6 / step_bytes) + 1)
+    if prefill:
+        R = args.replicas or 1      # the score matrix alone (336 MB) exceeds the LLC
+    else:
+        R = args.replicas or max(2, math.ceil(2 * 256e6 / step_bytes) + 1)
     reps = [base]
     for _ in range(R - 1):
         c = pipeline.DeviceProblem(**{**base.__dict__})
@@ -153,55 +219,79 @@ def main():
         reps.append(c)
     torch.cuda.synchronize()
 
+    def score(p):
+        p.score(QSA_SCORE_MFMA) if prefill else p.score()
+
+    def topk(p):
+        p.topk(certified=prefill)
+
     for s in range(args.warmup):
-        reps[s % R].step()
+        p = reps[s % R]
+        score(p)
+        topk(p)
+        p.attend()
     torch.cuda.synchronize()
 
+    # events are recorded on torch's current stream, which is the stream
+    # every library call below is enqueued on
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         p = reps[s % R]
         e = evs[s]
         e[0].record()
-        p.score()
+        score(p)
         e[1].record()
-        p.topk()
+        topk(p)
         e[2].record()
         p.attend()
         e[3].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / args.steps
-    t_score = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    t_topk = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    t_attn = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    t_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
     qps = wl.total_q / (ms_step / 1e3)
-    attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
     rec = {
         "metric": "sparse-attn decode queries/s + achieved HBM GB/s (% roofline) at 32K-128K ctx",
         "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": spec.name, "num_seqs": wl.num_seqs, "queries_per_step": wl.total_q,
+        "config": {"workload": f"{spec.name}", "num_seqs": wl.num_seqs, "queries_per_step": wl.total_q,
                    "context": (f"U[{spec.len_range[0]},{spec.len_range[1]}]" if spec.len_range
                                else str(wl.lens[0])),
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R},
-        "roofline": {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",
-                     "bytes_per_launch": attn_bytes, "avg_ms": float(t_attn)},
-        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
-        "step_bytes": step_bytes,
-        "kernel_ms": {"index_score": float(t_score), "topk": float(t_topk),
-                      "sparse_attn": float(t_attn)},
-        "index_score_gbps": score_bytes / (t_score * 1e-3) / 1e9,
+        "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn},
         "compress_ms": compress_ms,
     }
+    if prefill:
+        f_idx, f_attn = prefill_flops(wl)
+        ach = f_attn / (t_attn * 1e-3) / 1e12
+        rec["roofline"] = {"bound": "alu", "achieved": ach, "peak": VALU_FP32_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / VALU_FP32_PEAK_TFLOPS, "traffic": None,
+                           "kernel": "qsa_sparse_attn_prefill (causal gather attention)",
+                           "flops_per_launch": f_attn, "avg_ms": t_attn}
+        mf = f_idx / (t_score * 1e-3) / 1e12
+        rec["mfma_indexer"] = {"tflops": mf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                               "util": mf / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": f_idx,
+                               "avg_ms": t_score}
+    else:
+        attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
+        traffic = recorded_traffic(spec.name)
+        rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                           "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",
+                           "bytes_per_launch": attn_bytes, "avg_ms": t_attn}
+        rec["step_hbm_gbps"] = step_bytes / (ms_step * 1e-3) / 1e9
+        rec["step_bytes"] = step_bytes
+        rec["index_score_gbps"] = score_bytes / (t_score * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, prefill)
     print(json.dumps(rec), flush=True)
 
 

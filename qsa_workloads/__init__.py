@@ -64,16 +64,17 @@ class Spec:
 
 # The five configurations.  Sizes, head counts and dtypes are those the
 # method's evaluation names; seeds are 0..4 in order.
-C1 = Spec("c1_tiny_decode", 0, [4096], 1, 8, 1, 128, "f32", 4, 64, "f32", "f32")
-C2 = Spec("c2_batched_decode", 1, None, 1, 32, 4, 128, "bf16", 8, 128, "bf16", "bf16",
+TINY_DECODE = Spec("tiny_decode_4096_f32", 0, [4096], 1, 8, 1, 128, "f32", 4, 64, "f32", "f32")
+BATCHED_DECODE = Spec("batched_decode_32seq_8k-32k", 1, None, 1, 32, 4, 128, "bf16", 8, 128, "bf16", "bf16",
           len_range=(8192, 32768), num_seqs=32)
-C3 = Spec("c3_long_decode_e4m3", 2, [131072] * 8, 1, 64, 8, 128, "bf16", 8, 128, "bf16", "e4m3",
+LONG_DECODE = Spec("long_decode_8x131072_e4m3", 2, [131072] * 8, 1, 64, 8, 128, "bf16", 8, 128, "bf16", "e4m3",
           num_seqs=8)
-C4 = Spec("c4_chunked_prefill", 3, [40961], 8193, 32, 4, 128, "bf16", 8, 128, "bf16", "bf16")
-C5 = Spec("c5_verify_inert_boundary", 4, None, 4, 16, 2, 128, "bf16", 4, 64, "bf16", "bf16",
+CHUNKED_PREFILL = Spec("chunked_prefill_8193q_on_32768", 3, [40961], 8193, 32, 4, 128, "bf16", 8, 128, "bf16", "bf16")
+VERIFY = Spec("verify_16x4q_inert_boundary", 4, None, 4, 16, 2, 128, "bf16", 4, 64, "bf16", "bf16",
           len_range=(2040, 2060), len_extra=4, num_seqs=16)
 
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+CONFIGS = {"tiny_decode": TINY_DECODE, "batched_decode": BATCHED_DECODE, "long_decode": LONG_DECODE,
+           "chunked_prefill": CHUNKED_PREFILL, "verify": VERIFY}
 
 
 @dataclasses.dataclass

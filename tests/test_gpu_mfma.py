@@ -89,7 +89,7 @@ SHAPES = [(f"h{h}_d{d}", h, d) for h in (1, 2, 4, 8, 16) for d in (64, 128)]
 
 @pytest.mark.parametrize("name,h,d", SHAPES, ids=[s[0] for s in SHAPES])
 def test_mfma_scores_within_bound_and_selection_exact(name, h, d):
-    sp = dataclasses.replace(W.C4, h_idx=h, d_idx=d, budget=256)
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, h_idx=h, d_idx=d, budget=256)
     # two sequences, query counts spanning several 256/H-query workgroups
     # and a ragged last group, plus a causal triangle over several chunks
     wl = W.make(sp, lens=[1500, 2100], n_q=[300, 37], seed=41 + h + d)
@@ -104,7 +104,7 @@ def test_mfma_scores_within_bound_and_selection_exact(name, h, d):
 
 @pytest.mark.parametrize("ratio", [1, 16])
 def test_mfma_other_ratios(ratio):
-    sp = dataclasses.replace(W.C4, budget=64 * ratio, ratio=ratio)
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, budget=64 * ratio, ratio=ratio)
     wl = W.make(sp, lens=[3000 if ratio == 16 else 700], n_q=[90], seed=51 + ratio)
     _, got = mfma_scores(wl)
     check_bound(wl, got, np.arange(wl.total_q))
@@ -113,10 +113,10 @@ def test_mfma_other_ratios(ratio):
 
 def test_mfma_decode_batch_and_verify_window():
     # one query per sequence (decode layout) and the verify config's shape
-    sp = dataclasses.replace(W.C2, budget=512)
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=512)
     wl = W.make(sp, lens=[5000, 3333, 700, 4097], seed=61)
     full_check(wl, mfma=True)
-    wl5 = W.make(W.C5, seed=W.C5.seed + 200)
+    wl5 = W.make(W.VERIFY, seed=W.VERIFY.seed + 200)
     _print(f"[mfma] verify: lens={wl5.lens[:4]}... n_q={wl5.n_q[:4]}...")
     full_check(wl5, mfma=True)
 
@@ -124,7 +124,7 @@ def test_mfma_decode_batch_and_verify_window():
 def test_recheck_accepts_canonical_scores_all_dtypes():
     # the certifying top-k on canonical scores (any dtype pair) is exact too
     for idx_dt, kc_dt, kv in (("f32", "f32", "f32"), ("bf16", "e4m3", "bf16"), ("f32", "bf16", "bf16")):
-        sp = dataclasses.replace(W.C1, idx_dtype=idx_dt, kc_dtype=kc_dt, kv_dtype=kv, budget=256,
+        sp = dataclasses.replace(W.TINY_DECODE, idx_dtype=idx_dt, kc_dtype=kc_dt, kv_dtype=kv, budget=256,
                                  h_idx=4, d_idx=64)
         wl = W.make(sp, lens=[4000, 2500, 900], seed=71)
         from indexer_selected_sparse_amd import pipeline
@@ -140,7 +140,7 @@ def test_recheck_accepts_canonical_scores_all_dtypes():
 def test_flat_rows_take_the_whole_row_recompute():
     # all weights zero: every score is exactly 0, the undecided band is the
     # whole row (more than the candidate buffer), which is then recomputed
-    sp = dataclasses.replace(W.C4, budget=256)
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, budget=256)
     wl = W.make(sp, lens=[12000], n_q=[20], seed=81)
     wl.w[:] = 0.0
     res, ref, _ = full_check(wl, mfma=True)
@@ -148,18 +148,18 @@ def test_flat_rows_take_the_whole_row_recompute():
 
 
 def test_half_zero_weights_many_exact_ties():
-    sp = dataclasses.replace(W.C4, budget=512)
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, budget=512)
     wl = W.make(sp, lens=[9000], n_q=[64], seed=83)
     wl.w[:, ::2] = 0.0
     wl.q_idx[:, 1::2] = -wl.q_idx[:, 1::2].abs()   # remaining heads mostly negative: many zeros
     full_check(wl, mfma=True)
 
 
-def test_full_size_c4_prefill_mfma_sampled():
-    wl = W.make(W.C4)
+def test_full_size_chunked_prefill_mfma_sampled():
+    wl = W.make(W.CHUNKED_PREFILL)
     rng = np.random.default_rng(5)
     q = np.array(sorted({0, wl.total_q - 1} | set(rng.choice(wl.total_q, 24, replace=False).tolist())))
-    _print(f"[mfma] full c4: total_q={wl.total_q}, sampled {len(q)} queries")
+    _print(f"[mfma] full chunked prefill: total_q={wl.total_q}, sampled {len(q)} queries")
     res, dp = run_gpu(wl, mfma=True)
     ref = oracle.run_workload(wl, query_ids=q, want_scores=True)
     check_compress(wl, res, ref)
@@ -171,4 +171,4 @@ def test_full_size_c4_prefill_mfma_sampled():
         nb = int(Ls[i]) // wl.spec.ratio
         err = np.abs(res["scores"][i, :nb].astype(np.float64) - ref["scores"][j])
         assert np.all(err <= E[j][:nb]), f"query {i}: MFMA score outside its bound"
-    _print(f"[mfma] full c4: idx exact on samples, out worst err/limit {worst:.3f}")
+    _print(f"[mfma] full chunked prefill: idx exact on samples, out worst err/limit {worst:.3f}")

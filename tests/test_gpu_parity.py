@@ -26,14 +26,14 @@ def _print(*a):
 # ------------------------------------------------------------ small cases
 SMALL = [
     # (spec, lens, n_q or None, overrides)
-    ("c1", W.C1, [4096], None, {}),
-    ("c1_ragged", W.C1, [1027, 4099, 333, 2], None, {"budget": 256}),
-    ("c2_small", W.C2, [3001, 1234, 777, 5002, 2049, 2052], None, {}),
-    ("c2_budget64", W.C2, [1500, 903, 64, 65, 3], None, {"budget": 64}),
-    ("c3_small_e4m3", W.C3, [6001, 3003, 1000], None, {"budget": 512}),
-    ("c4_small_prefill", W.C4, [1500], [300], {"budget": 256}),
-    ("c5_small_verify", W.C5, [2044, 2050, 2051, 2052, 2055, 2064], None, {}),
-    ("c5_full_shape", W.C5, None, None, {}),
+    ("tiny", W.TINY_DECODE, [4096], None, {}),
+    ("tiny_ragged", W.TINY_DECODE, [1027, 4099, 333, 2], None, {"budget": 256}),
+    ("batched_small", W.BATCHED_DECODE, [3001, 1234, 777, 5002, 2049, 2052], None, {}),
+    ("batched_budget64", W.BATCHED_DECODE, [1500, 903, 64, 65, 3], None, {"budget": 64}),
+    ("long_small_e4m3", W.LONG_DECODE, [6001, 3003, 1000], None, {"budget": 512}),
+    ("prefill_small", W.CHUNKED_PREFILL, [1500], [300], {"budget": 256}),
+    ("verify_small", W.VERIFY, [2044, 2050, 2051, 2052, 2055, 2064], None, {}),
+    ("verify_full_shape", W.VERIFY, None, None, {}),
 ]
 
 
@@ -59,7 +59,7 @@ DTYPES = [
 @pytest.mark.parametrize("name,kv,idx_dt,kc_dt", DTYPES, ids=[d[0] for d in DTYPES])
 @pytest.mark.parametrize("h_idx,d_idx", [(1, 64), (2, 128), (4, 64), (8, 128), (16, 64), (16, 128)])
 def test_indexer_dtype_and_shape_matrix(name, kv, idx_dt, kc_dt, h_idx, d_idx):
-    sp = dataclasses.replace(W.C2, kv_dtype=kv, idx_dtype=idx_dt, kc_dtype=kc_dt, h_idx=h_idx,
+    sp = dataclasses.replace(W.BATCHED_DECODE, kv_dtype=kv, idx_dtype=idx_dt, kc_dtype=kc_dt, h_idx=h_idx,
                              d_idx=d_idx, hq=8, hkv=2, budget=128)
     wl = W.make(sp, lens=[900, 517, 131], seed=7)
     full_check(wl)
@@ -68,26 +68,26 @@ def test_indexer_dtype_and_shape_matrix(name, kv, idx_dt, kc_dt, h_idx, d_idx):
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (32, 2)])
 @pytest.mark.parametrize("kv", ["bf16", "f32"])
 def test_gqa_group_sizes(hq, hkv, kv):
-    sp = dataclasses.replace(W.C2, hq=hq, hkv=hkv, kv_dtype=kv, budget=256)
+    sp = dataclasses.replace(W.BATCHED_DECODE, hq=hq, hkv=hkv, kv_dtype=kv, budget=256)
     wl = W.make(sp, lens=[1400, 77, 2100], seed=11)
     full_check(wl)
 
 
 @pytest.mark.parametrize("ratio", [1, 2, 8, 16, 64])
 def test_other_ratios(ratio):
-    sp = dataclasses.replace(W.C2, ratio=ratio, budget=64 * ratio, hq=8, hkv=1)
+    sp = dataclasses.replace(W.BATCHED_DECODE, ratio=ratio, budget=64 * ratio, hq=8, hkv=1)
     wl = W.make(sp, lens=[64 * ratio * 3 + ratio - 1, 100, ratio * 70 + 1], seed=13)
     full_check(wl)
 
 
 def test_prefill_ragged_chunks_and_empty_sequence():
-    sp = dataclasses.replace(W.C4, budget=128)
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, budget=128)
     wl = W.make(sp, lens=[700, 300, 90, 1025], n_q=[33, 0, 90, 1], seed=17)
     full_check(wl)
 
 
 def test_equal_scores_pick_lowest_blocks():
-    sp = dataclasses.replace(W.C2, budget=256)
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=256)
     wl = W.make(sp, lens=[4000, 2000], seed=19)
     wl.q_idx.zero_()                       # every score is +0: ties everywhere
     res, ref, _ = full_check(wl)
@@ -96,7 +96,7 @@ def test_equal_scores_pick_lowest_blocks():
 
 
 def test_nonpositive_scores_with_some_ties():
-    sp = dataclasses.replace(W.C2, budget=512)
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=512)
     wl = W.make(sp, lens=[6000, 3001], seed=23)
     # half of the indexer heads get no weight, making many scores exactly 0
     wl.w[:, ::2] = 0.0
@@ -104,7 +104,7 @@ def test_nonpositive_scores_with_some_ties():
 
 
 def test_decode_equals_prefill_row_and_two_chunks_equal_one():
-    sp = dataclasses.replace(W.C4, budget=256)
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, budget=256)
     wl = W.make(sp, lens=[2500], n_q=[40], seed=29)
     res_all, _ = run_gpu(wl)
     # the same sequence as two chunks: the first 17 queries, then the rest
@@ -137,7 +137,7 @@ def _sample(total, k, seed=0):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c5"])
+@pytest.mark.parametrize("cfg", ["tiny_decode", "batched_decode", "verify"])
 def test_full_size_all_queries(cfg):
     wl = W.make(W.CONFIGS[cfg])
     _print(f"[parity] full {cfg}: B={wl.num_seqs} total_q={wl.total_q} max_len={max(wl.lens)}")
@@ -145,16 +145,16 @@ def test_full_size_all_queries(cfg):
     _print(f"[parity] full {cfg}: ok, worst err/limit = {worst:.3f}")
 
 
-def test_full_size_c3_long_context_e4m3():
-    wl = W.make(W.C3)
-    _print(f"[parity] full c3: B={wl.num_seqs} len={wl.lens[0]}")
+def test_full_size_long_context_e4m3():
+    wl = W.make(W.LONG_DECODE)
+    _print(f"[parity] full long decode: B={wl.num_seqs} len={wl.lens[0]}")
     _, _, worst = full_check(wl)
-    _print(f"[parity] full c3: ok, worst err/limit = {worst:.3f}")
+    _print(f"[parity] full long decode: ok, worst err/limit = {worst:.3f}")
 
 
-def test_full_size_c4_prefill_sampled():
-    wl = W.make(W.C4)
+def test_full_size_chunked_prefill_sampled():
+    wl = W.make(W.CHUNKED_PREFILL)
     q = _sample(wl.total_q, 24, seed=4)
-    _print(f"[parity] full c4: total_q={wl.total_q}, sampled {len(q)} queries")
+    _print(f"[parity] full chunked prefill: total_q={wl.total_q}, sampled {len(q)} queries")
     _, _, worst = full_check(wl, query_ids=q)
-    _print(f"[parity] full c4: ok, worst err/limit = {worst:.3f}")
+    _print(f"[parity] full chunked prefill: ok, worst err/limit = {worst:.3f}")

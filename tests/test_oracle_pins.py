@@ -286,7 +286,7 @@ def test_inert_bound_dispatch_table_from_the_pages(page):
     ib = page["inert_bound"]
     assert ib["budget"] + ib["ratio"] - 1 == ib["value"] == 2051
     tab = page["dispatch_table"]
-    spec = W.C5
+    spec = W.VERIFY
     wl = W.small(spec, lens=[2060], n_q=[1], seed=31)
     kc, _ = oracle.compress(wl.k_idx.float().numpy(), wl.kv_offsets, 4, "bf16")
     kcv = oracle.kc_values(kc, "bf16")
@@ -311,7 +311,7 @@ def test_inert_bound_dispatch_table_from_the_pages(page):
 
 
 def test_budget_covering_prefix_is_dense_attention():
-    spec = W.C1
+    spec = W.TINY_DECODE
     wl = W.small(spec, lens=[300], n_q=[5], seed=2)
     kc, _ = oracle.compress(wl.k_idx.numpy(), wl.kv_offsets, 4, "f32")
     Kr, Vr = wl.K.numpy(), wl.V.numpy()
@@ -327,7 +327,7 @@ def test_budget_covering_prefix_is_dense_attention():
 def test_sparse_pipeline_equals_masked_dense_attention_from_torch():
     # Selection from a brute-force top-k over the oracle's scores, attention
     # from torch's fp64 SDPA with a boolean mask: two independent routines.
-    spec = W.C5
+    spec = W.VERIFY
     wl = W.small(spec, lens=[150, 97], n_q=[4, 3], seed=17, budget=32)
     kc, _ = oracle.compress(wl.k_idx.float().numpy(), wl.kv_offsets, 4, "bf16")
     kcv = oracle.kc_values(kc, "bf16")
@@ -354,7 +354,7 @@ def test_sparse_pipeline_equals_masked_dense_attention_from_torch():
 
 
 def test_chunked_equals_single_shot_and_decode_equals_prefill_row():
-    spec = W.C4
+    spec = W.CHUNKED_PREFILL
     wl = W.small(spec, lens=[600], n_q=[40], seed=5, budget=256)
     allq = oracle.run_workload(wl)
     first = oracle.run_workload(wl, query_ids=np.arange(0, 17))
