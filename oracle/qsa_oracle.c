@@ -12,7 +12,7 @@
  *            tokens, equal to the group's mean ("Agentic shootout" page,
  *            report "Flash-Next support: vLLM vs Atlas", section (a)6, the
  *            compressed-key cache bullet; "PR 16 review", section (a), the
- *            QSA bullet: "4-token mean-pooled blocks").  The optional e4m3
+ *            QSA bullet: blocks of 4 tokens, mean-pooled).  The optional e4m3
  *            index plane stores codes with one fp32 scale per block equal to
  *            max|x|/448 (the long-context decode workload's definition; the
  *            ATOM model-support page lists an fp8 index plane).
@@ -29,7 +29,7 @@
  *            (vLLM report (a)6: selection rows are -1 padded).
  *  tokens    T(L) = tokens of the selected blocks plus the incomplete tail
  *            block, which is always visible ("llama.cpp vs Atlas" report,
- *            section (a)3: the tail block is "always visible").
+ *            section (a)3: the incomplete tail block is visible to every query).
  *  attn      softmax(scale * q_h . K_t) V_t over T(L) for each query head h,
  *            KV head floor(h / (Hq/Hkv)); fp64 on exactly widened inputs.
  *
