@@ -506,6 +506,275 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_kernel(AttnArgs A) {
     attn_body<BF16, G>(A);
 }
 
+// ---------------------------------------------------------------------------
+// Decode, bf16: K/V staged through a per-wave LDS ring by direct-to-LDS loads.
+//
+// A gather of scattered 256-byte rows only reaches HBM speed with a great
+// deal of data in flight per CU; register double-buffering caps that at two
+// steps per wave.  Here every step's K and V tiles (16 tokens x 256 B each)
+// are fetched with global_load_lds_dwordx4 straight into a ring of D slots of
+// LDS, issued D-1 steps ahead of the step being computed, so a wave keeps
+// (D-1) x 8 KB in flight without holding registers for it.  Completion is
+// tracked with vmcnt (the loads complete in order), and a slot is refilled
+// only after the step that used it has been read back into registers.  The
+// arithmetic of a step is the shared compute_step, so decode and prefill
+// compute the same operations on the same values.
+constexpr int kSlotBytes = 2 * kStep * kD * 2;      // K tile + V tile, bf16: 8 KB
+
+// s_waitcnt immediate meaning "vmcnt <= n", leaving expcnt and lgkmcnt free.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS byte address of a pointer into this workgroup's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t *)p;
+}
+
+// One global_load_lds_dwordx4: lane l's 16 bytes from `src` land at LDS byte
+// lds_dst + 16*l.  Issued through inline assembly so that the compiler does
+// not treat every later LDS read as dependent on every load still in flight
+// (it cannot tell the ring slots apart and would drain the whole ring before
+// each read); the kernel orders the ring itself with explicit vmcnt waits.
+// M0 carries the LDS destination; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Issue the 8 direct-to-LDS loads of step `st` into the slot at LDS address
+// `slot` and return the step's wave-uniform token-valid mask.  Token rows are
+// resolved as in issue_step, from a slot table of up to 128 entries held in
+// two registers (lane j of tab0/tab1 = block id of part slot j / 64 + j), so
+// lanes 0..15 end up holding the rows of tokens 0..15.  Load j
+// covers tokens 4j..4j+3: lane l fetches 16-byte chunk c of token 4j + l/16
+// into LDS byte l*16 of the j-th kilobyte (the hardware places lane l's 16
+// bytes at l*16).  K chunks are swizzled by token parity (position p holds
+// chunk p ^ (token & 1)) so the QK reads of tokens tk and tk+1 fall in
+// different LDS banks; V is stored as is.
+__device__ __forceinline__ uint32_t issue_step_lds(const WaveWork &W, int st, int lane,
+                                                   uint32_t tab0, uint32_t tab1,
+                                                   const uint16_t *__restrict__ kbase,
+                                                   const uint16_t *__restrict__ vbase,
+                                                   int64_t row_stride, uint32_t slot) {
+    const int t = st * kStep + (lane & (kStep - 1));
+    int rel = t >> W.log2r;                          // slot of the part, < 2 * 64
+    rel = rel > 2 * kWave - 1 ? 2 * kWave - 1 : rel;
+    const int b0 = __builtin_amdgcn_ds_bpermute((rel & (kWave - 1)) << 2, (int)tab0);
+    const int b1 = __builtin_amdgcn_ds_bpermute((rel & (kWave - 1)) << 2, (int)tab1);
+    const int b = rel < kWave ? b0 : b1;
+    int row = 0;
+    bool ok = false;
+    if (t < W.nblk_tok) {
+        ok = b >= 0 && (int64_t)b < W.nb;
+        row = ok ? (b << W.log2r) + (t & ((1 << W.log2r) - 1)) : 0;
+    } else if (t < W.ntok) {
+        row = (int)(W.tail0 + (t - W.nblk_tok));
+        ok = true;
+    }
+    const uint32_t valid = (uint32_t)__ballot(ok && lane < kStep) & 0xffffu;
+    const int p = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tq = 4 * j + (lane >> 4);
+        const int r = __builtin_amdgcn_ds_bpermute(tq << 2, row);
+        const int ck = p ^ (tq & 1);
+        dma16(kbase + (int64_t)r * row_stride + ck * 8, slot + j * 1024);
+        dma16(vbase + (int64_t)r * row_stride + p * 8, slot + 4096 + j * 1024);
+    }
+    return valid;
+}
+
+// Read a landed step back into registers in the layout compute_step uses.
+__device__ __forceinline__ void load_step_lds(const uint8_t *slot, int lane, int tk, int ds,
+                                              StepBuf<true> &B) {
+    const uint4 *kt = reinterpret_cast<const uint4 *>(slot);
+    const int sw = tk & 1;                       // tokens tk and tk+8 share parity
+    const uint4 a0 = kt[tk * 16 + ((2 * ds) ^ sw)], a1 = kt[tk * 16 + ((2 * ds + 1) ^ sw)];
+    const uint4 b0 = kt[(tk + 8) * 16 + ((2 * ds) ^ sw)], b1 = kt[(tk + 8) * 16 + ((2 * ds + 1) ^ sw)];
+    B.kA[0] = a0.x; B.kA[1] = a0.y; B.kA[2] = a0.z; B.kA[3] = a0.w;
+    B.kA[4] = a1.x; B.kA[5] = a1.y; B.kA[6] = a1.z; B.kA[7] = a1.w;
+    B.kB[0] = b0.x; B.kB[1] = b0.y; B.kB[2] = b0.z; B.kB[3] = b0.w;
+    B.kB[4] = b1.x; B.kB[5] = b1.y; B.kB[6] = b1.z; B.kB[7] = b1.w;
+    const uint32_t *vt = reinterpret_cast<const uint32_t *>(slot + 4096);
+#pragma unroll
+    for (int tt = 0; tt < kStep; ++tt) B.v[tt][0] = vt[tt * kWave + lane];
+}
+
+// Wait until step `st` has landed when only `left` later steps are in flight
+// (the ring's drain at the end of a part).
+template <int D>
+__device__ __forceinline__ void wait_drain(int left) {
+    if constexpr (D > 3) { if (left == 3) { wait_vmcnt<24>(); return; } }
+    if constexpr (D > 2) { if (left == 2) { wait_vmcnt<16>(); return; } }
+    if (left == 1) { wait_vmcnt<8>(); return; }
+    wait_vmcnt<0>();
+}
+
+template <int G, int D>
+__device__ __forceinline__ void attn_decode_lds_body(const AttnArgs &A) {
+    constexpr int NH = AttnState<G>::NH;
+    __shared__ __align__(16) AttnLds<G> L;
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t wid = (int64_t)blockIdx.x * kWgWaves + wave;
+    const int g = (int)(wid % A.hkv);
+    const int64_t t2 = wid / A.hkv;
+    const int c = (int)(t2 % A.n_part);
+    const int64_t i = t2 / A.n_part;
+    if (i >= A.total_q) return;                      // uniform over the wave
+
+    const QueryPos qp = query_pos(A.kv_off, nullptr, A.q_off, A.num_seqs, i);
+    const int64_t nb = qp.L >> A.log2r;
+    const int64_t nsel = nb < A.K ? nb : (int64_t)A.K;
+    const int64_t per = (nsel + A.n_part - 1) / A.n_part;
+    const int64_t s_beg = imin64((int64_t)c * per, nsel);
+    const int64_t s_end = imin64(s_beg + per, nsel);
+    WaveWork W;
+    W.sel = A.idx + i * (int64_t)A.K + s_beg;
+    W.nslot = (int)(s_end - s_beg);
+    W.log2r = A.log2r;
+    W.nblk_tok = W.nslot << A.log2r;
+    W.tail0 = nb << A.log2r;
+    W.nb = nb;
+    W.ntok = W.nblk_tok + ((c == A.n_part - 1) ? (int)(qp.L - W.tail0) : 0);
+
+    const int tk = lane >> 3, ds = lane & 7;
+    const int hb = head_base<G>(ds);
+    const int qh0 = g * G;
+    const int64_t row_stride = (int64_t)A.hkv * kD;
+    const uint16_t *__restrict__ kbase = static_cast<const uint16_t *>(A.k) + (qp.kv_row0 * A.hkv + g) * kD;
+    const uint16_t *__restrict__ vbase = static_cast<const uint16_t *>(A.v) + (qp.kv_row0 * A.hkv + g) * kD;
+    uint8_t *ring = dyn_lds + wave * (D * kSlotBytes);
+
+    // Slot table: lane j of tab0 / tab1 holds the block id of part slot j /
+    // 64 + j (a part has at most 128 slots: n_part >= K / 128).
+    const uint32_t tab0 = (uint32_t)(lane < W.nslot ? W.sel[lane] : -1);
+    const uint32_t tab1 = (uint32_t)(kWave + lane < W.nslot ? W.sel[kWave + lane] : -1);
+    // The ring loads are invisible to the compiler, so it would place the
+    // wait for the slot table inside the prologue loop below (waiting for the
+    // ring loads as well); consuming the table here puts that wait up front.
+    asm volatile("" ::"v"(tab0), "v"(tab1));
+
+    AttnState<G> S;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) { S.m_run[h] = -INFINITY; S.l_run[h] = 0.0f; }
+#pragma unroll
+    for (int h = 0; h < G; ++h) { S.o[h][0] = 0.0f; S.o[h][1] = 0.0f; }
+
+    const int nsteps = (W.ntok + kStep - 1) / kStep;
+    const uint32_t ring_addr = lds_addr(ring);
+
+    // valid masks of the issued, not yet computed steps (oldest in bits 0..15)
+    uint64_t fifo = 0;
+    int pending = 0;
+    int slot_in = 0, slot_out = 0;
+    auto issue = [&](int s) {
+        const uint32_t m = issue_step_lds(W, s, lane, tab0, tab1, kbase, vbase, row_stride,
+                                          ring_addr + slot_in * kSlotBytes);
+        fifo |= (uint64_t)m << (16 * pending);
+        ++pending;
+        slot_in = slot_in + 1 == D ? 0 : slot_in + 1;
+    };
+    // The query slices travel through the ring as well (a compiler-visible
+    // load would make the compiler wait for it, and so for the whole ring,
+    // inside the loop): the wave's G query rows (G x 256 contiguous bytes) go
+    // to the last slot, which the prologue leaves free, and are read back into
+    // registers once they have landed.
+    QSlices<true, G> Q;
+    if (nsteps > 0) {
+        const uint32_t qslot = ring_addr + (D - 1) * kSlotBytes;
+        const uint16_t *qsrc = static_cast<const uint16_t *>(A.q) + (i * A.hq + qh0) * kD;
+        constexpr int kQLoads = G >= 4 ? G / 4 : 1;          // 1 KB per load
+#pragma unroll
+        for (int j = 0; j < kQLoads; ++j) {
+            const int e = (j * kWave + lane) * 8;              // bf16 element of this lane
+            dma16(qsrc + (e < G * kD ? e : 0), qslot + j * 1024);
+        }
+    }
+    const int npro = nsteps < D - 1 ? nsteps : D - 1;
+    for (int s = 0; s < npro; ++s) issue(s);
+    if (nsteps > 0) {
+        wait_drain<D>(npro);                       // the query loads are older than the steps
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 *qs = reinterpret_cast<const uint4 *>(ring + (D - 1) * kSlotBytes);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int h = qk_head<G>(j, ds);
+#pragma unroll
+            for (int c4 = 0; c4 < 2; ++c4) {
+                const uint4 x = qs[h * 16 + ds * 2 + c4];
+                Q.v[j][4 * c4] = x.x; Q.v[j][4 * c4 + 1] = x.y;
+                Q.v[j][4 * c4 + 2] = x.z; Q.v[j][4 * c4 + 3] = x.w;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): read out before the slot is refilled
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int st = 0; st < nsteps; ++st) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + D - 1 < nsteps) {
+            issue(st + D - 1);
+            wait_vmcnt<8 * (D - 1)>();
+        } else {
+            wait_drain<D>(nsteps - 1 - st);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        StepBuf<true> B;
+        load_step_lds(ring + slot_out * kSlotBytes, lane, tk, ds, B);
+        B.valid = (uint32_t)(fifo & 0xffffu);
+        fifo >>= 16;
+        --pending;
+        slot_out = slot_out + 1 == D ? 0 : slot_out + 1;
+        compute_step<true, G>(B, Q, A.c, tk, ds, hb, L.p[wave], L.alpha[wave], S);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const float l = tok_sum(S.l_run[h]);
+        if (tk == 0) {
+            L.l[wave][hb + h] = l;
+            L.m[wave][hb + h] = S.m_run[h];
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        if (A.n_part == 1) {
+            const float l = L.l[wave][h];
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            const int64_t off = (i * A.hq + qh0 + h) * kD + 2 * lane;
+            reinterpret_cast<uint32_t *>(A.out)[off >> 1] = pack_bf16x2(S.o[h][0] * inv, S.o[h][1] * inv);
+        } else {
+            const int64_t slot = (i * A.hq + qh0 + h) * A.n_part + c;
+            reinterpret_cast<float2 *>(A.ws_o + slot * kD)[lane] = make_float2(S.o[h][0], S.o[h][1]);
+            if (lane == 0) {
+                A.ws_ml[slot * 2 + 0] = L.m[wave][h];
+                A.ws_ml[slot * 2 + 1] = L.l[wave][h];
+            }
+        }
+    }
+}
+
+template <int G, int D>
+__global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_lds_kernel(AttnArgs A) {
+    attn_decode_lds_body<G, D>(A);
+}
+
 // Merge part partials: one wave per (query, head); lane s < n_part reads
 // partial s's (m, l), the wave forms the weights, then every lane accumulates
 // dims 2p, 2p+1 over the partials (all partial loads issued together).
@@ -547,18 +816,63 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_combine_kernel(
     }
 }
 
+// Ring depth of the decode kernel: as deep as the LDS of one CU allows for
+// the workgroups that share it (4 waves x D slots x 8 KB per workgroup, two
+// or more workgroups per CU get D = 2).
+int ring_depth(int64_t workgroups) {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return workgroups <= cus[dev] ? 4 : 2;
+}
+
+template <int G, int D>
+hipError_t launch_decode_lds(const AttnArgs &A, dim3 grid, hipStream_t st) {
+    const size_t lds = (size_t)kWgWaves * D * kSlotBytes;
+    static hipError_t attr = hipFuncSetAttribute((const void *)attn_decode_lds_kernel<G, D>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((attn_decode_lds_kernel<G, D>), grid, dim3(kWgWaves * kWave), lds, st, A);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_lds_g(const AttnArgs &A, int G, dim3 grid, hipStream_t st) {
+    switch (G) {
+    case 1: return launch_decode_lds<1, D>(A, grid, st);
+    case 2: return launch_decode_lds<2, D>(A, grid, st);
+    case 4: return launch_decode_lds<4, D>(A, grid, st);
+    case 8: return launch_decode_lds<8, D>(A, grid, st);
+    default: return launch_decode_lds<16, D>(A, grid, st);
+    }
+}
+
 template <bool BF16>
-hipError_t launch_attn_t(const AttnArgs &A, int G, hipStream_t st) {
+hipError_t launch_attn_t(const AttnArgs &A, int G, bool decode, hipStream_t st) {
     const int64_t waves = A.total_q * A.n_part * A.hkv;
     dim3 grid((unsigned)((waves + kWgWaves - 1) / kWgWaves));
     dim3 block(kWgWaves * kWave);
+    hipError_t e = hipSuccess;
     if constexpr (BF16) {
-        switch (G) {
-        case 1: hipLaunchKernelGGL((attn_kernel_w3<BF16, 1>), grid, block, 0, st, A); break;
-        case 2: hipLaunchKernelGGL((attn_kernel_w3<BF16, 2>), grid, block, 0, st, A); break;
-        case 4: hipLaunchKernelGGL((attn_kernel_w3<BF16, 4>), grid, block, 0, st, A); break;
-        case 8: hipLaunchKernelGGL((attn_kernel<BF16, 8>), grid, block, 0, st, A); break;
-        default: hipLaunchKernelGGL((attn_kernel<BF16, 16>), grid, block, 0, st, A); break;
+        if (decode) {
+            const int D = ring_depth((int64_t)grid.x);
+            trace("attn decode lds ring D=%d workgroups=%u", D, grid.x);
+            e = D == 4 ? launch_decode_lds_g<4>(A, G, grid, st) : launch_decode_lds_g<2>(A, G, grid, st);
+        } else {
+            switch (G) {
+            case 1: hipLaunchKernelGGL((attn_kernel_w3<BF16, 1>), grid, block, 0, st, A); break;
+            case 2: hipLaunchKernelGGL((attn_kernel_w3<BF16, 2>), grid, block, 0, st, A); break;
+            case 4: hipLaunchKernelGGL((attn_kernel_w3<BF16, 4>), grid, block, 0, st, A); break;
+            case 8: hipLaunchKernelGGL((attn_kernel<BF16, 8>), grid, block, 0, st, A); break;
+            default: hipLaunchKernelGGL((attn_kernel<BF16, 16>), grid, block, 0, st, A); break;
+            }
+            e = hipGetLastError();
         }
     } else {
         switch (G) {
@@ -568,8 +882,8 @@ hipError_t launch_attn_t(const AttnArgs &A, int G, hipStream_t st) {
         case 8: hipLaunchKernelGGL((attn_kernel<BF16, 8>), grid, block, 0, st, A); break;
         default: hipLaunchKernelGGL((attn_kernel<BF16, 16>), grid, block, 0, st, A); break;
         }
+        e = hipGetLastError();
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess || A.n_part == 1) return e;
     const int64_t rows = A.total_q * A.hq;
     dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves));
@@ -619,7 +933,8 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     const int G = a.hq / a.hkv;
     trace("attn total_q=%lld hkv=%d G=%d parts=%d dtype=%d", (long long)b.total_q, a.hkv, G,
           A.n_part, a.dtype);
-    return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, st) : launch_attn_t<false>(A, G, st);
+    return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, decode, st)
+                                : launch_attn_t<false>(A, G, decode, st);
 }
 
 }  // namespace qsa
