@@ -27,6 +27,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The attention kernels keep their matrix-core
+# accumulators in ordinary VGPRs (the compiler would otherwise pick AGPRs,
+# and every online-softmax rescale would copy them out and back).
+EXTRA_FLAGS = {"qsa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
@@ -38,8 +44,8 @@ def _filter(stderr: str) -> str:
 
 def _compile(hipcc: str, src: str) -> tuple[str, int, str]:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-c", src, "-o", obj]
+    cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []),
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     return obj, r.returncode, _filter(r.stderr)
 

@@ -551,23 +551,38 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_dst) {
                  : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
                  : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit byte offset
+// per lane, so a row address costs one 32-bit multiply-add.
+__device__ __forceinline__ void dma16_off(const void *base, uint32_t off, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// Issue the 8 direct-to-LDS loads of step `st` into the slot at LDS address
-// `slot` and return the step's wave-uniform token-valid mask.  Token rows are
-// resolved as in issue_step, from a slot table of up to 128 entries held in
-// two registers (lane j of tab0/tab1 = block id of part slot j / 64 + j), so
-// lanes 0..15 end up holding the rows of tokens 0..15.  Load j
-// covers tokens 4j..4j+3: lane l fetches 16-byte chunk c of token 4j + l/16
-// into LDS byte l*16 of the j-th kilobyte (the hardware places lane l's 16
-// bytes at l*16).  K chunks are swizzled by token parity (position p holds
-// chunk p ^ (token & 1)) so the QK reads of tokens tk and tk+1 fall in
-// different LDS banks; V is stored as is.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Issue the 8 direct-to-LDS loads of step `st` (16 tokens) into the slot at
+// LDS address `slot` and return the step's wave-uniform token-valid mask.
+// A token's row is resolved from the slot table (up to 128 part slots held in
+// two registers: lane j of tab0 / tab1 = block id of part slot j / 64 + j), a
+// selected block id giving rows b*ratio.., a tail position giving itself;
+// malformed ids and positions past the end give "no token" and read row 0.
+// Lanes 0..15 end up holding the rows of tokens 0..15.  Row byte offsets are
+// 32-bit (the launcher checks that a sequence's K rows span less than 4 GiB).  Load j covers tokens
+// 4j..4j+3: lane l fills LDS bytes l*16.. of the j-th kilobyte (the hardware
+// places lane l's 16 bytes at l*16), i.e. position p = l%16 of token
+// t = 4j + l/16.  Position p of token t holds the row's 16-byte chunk p ^ t
+// (a per-token rotation of the 16 chunks), in the K tile and in the V tile,
+// so the matrix-operand reads below hit 16 different LDS bank groups.
 __device__ __forceinline__ uint32_t issue_step_lds(const WaveWork &W, int st, int lane,
                                                    uint32_t tab0, uint32_t tab1,
                                                    const uint16_t *__restrict__ kbase,
                                                    const uint16_t *__restrict__ vbase,
-                                                   int64_t row_stride, uint32_t slot) {
+                                                   uint32_t row_bytes, uint32_t slot) {
     const int t = st * kStep + (lane & (kStep - 1));
     int rel = t >> W.log2r;                          // slot of the part, < 2 * 64
     rel = rel > 2 * kWave - 1 ? 2 * kWave - 1 : rel;
@@ -589,27 +604,11 @@ __device__ __forceinline__ uint32_t issue_step_lds(const WaveWork &W, int st, in
     for (int j = 0; j < 4; ++j) {
         const int tq = 4 * j + (lane >> 4);
         const int r = __builtin_amdgcn_ds_bpermute(tq << 2, row);
-        const int ck = p ^ (tq & 1);
-        dma16(kbase + (int64_t)r * row_stride + ck * 8, slot + j * 1024);
-        dma16(vbase + (int64_t)r * row_stride + p * 8, slot + 4096 + j * 1024);
+        const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)((p ^ tq) << 4);
+        dma16_off(kbase, off, slot + j * 1024);
+        dma16_off(vbase, off, slot + 4096 + j * 1024);
     }
     return valid;
-}
-
-// Read a landed step back into registers in the layout compute_step uses.
-__device__ __forceinline__ void load_step_lds(const uint8_t *slot, int lane, int tk, int ds,
-                                              StepBuf<true> &B) {
-    const uint4 *kt = reinterpret_cast<const uint4 *>(slot);
-    const int sw = tk & 1;                       // tokens tk and tk+8 share parity
-    const uint4 a0 = kt[tk * 16 + ((2 * ds) ^ sw)], a1 = kt[tk * 16 + ((2 * ds + 1) ^ sw)];
-    const uint4 b0 = kt[(tk + 8) * 16 + ((2 * ds) ^ sw)], b1 = kt[(tk + 8) * 16 + ((2 * ds + 1) ^ sw)];
-    B.kA[0] = a0.x; B.kA[1] = a0.y; B.kA[2] = a0.z; B.kA[3] = a0.w;
-    B.kA[4] = a1.x; B.kA[5] = a1.y; B.kA[6] = a1.z; B.kA[7] = a1.w;
-    B.kB[0] = b0.x; B.kB[1] = b0.y; B.kB[2] = b0.z; B.kB[3] = b0.w;
-    B.kB[4] = b1.x; B.kB[5] = b1.y; B.kB[6] = b1.z; B.kB[7] = b1.w;
-    const uint32_t *vt = reinterpret_cast<const uint32_t *>(slot + 4096);
-#pragma unroll
-    for (int tt = 0; tt < kStep; ++tt) B.v[tt][0] = vt[tt * kWave + lane];
 }
 
 // Wait until step `st` has landed when only `left` later steps are in flight
@@ -622,27 +621,66 @@ __device__ __forceinline__ void wait_drain(int left) {
     wait_vmcnt<0>();
 }
 
-template <int G, int D>
-__device__ __forceinline__ void attn_decode_lds_body(const AttnArgs &A) {
-    constexpr int NH = AttnState<G>::NH;
-    __shared__ __align__(16) AttnLds<G> L;
-    extern __shared__ __align__(16) uint8_t dyn_lds[];
+__device__ __forceinline__ float quad_group_max(float x) {
+    // max over lanes l, l^16, l^32, l^48 (same lane%16)
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float quad_group_sum(float x) {
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Decode attention of one wave on the matrix cores.  Per 16-token step:
+//  QK: S[t][n] = K[t,:] . q_n for the 16 tokens t (M) and up to 16 query
+//      heads n of the KV head (N; heads >= G are zero columns), four
+//      v_mfma_f32_16x16x32_bf16 over the 128 dims.  Lane l gets S for head
+//      n = l%16 and tokens 4(l/16)..+3.
+//  softmax: online, fp32, exp2 domain; the running max of head n is shared
+//      by the four lanes that hold it (permlane swaps).
+//  PV: O^T[d][n] += V^T[d][t] P[t][n] as eight v_mfma_f32_16x16x16_bf16
+//      tiles of 16 dims (M) by the 16 heads (N) over the 16 tokens (K).  The
+//      B operand P[t][n] (4 tokens of head n per lane) is exactly what the
+//      QK tile left in the lane.  P is fed as two bf16 terms, hi = P with the
+//      low 16 bits cleared and lo = bf16(P - hi), so the weights carry 16
+//      significant bits (relative error <= 2^-16) instead of bf16's 8; V is
+//      bf16 data and enters unchanged.  The V^T operand is read with the
+//      gfx950 transposed LDS load (ds_read_b64_tr_b16: lane i of each 16-lane
+//      group gets column i of the four rows its group points at).
+//  Lane l accumulates O^T for head l%16, dims 16m + 4(l/16) + 0..3, m < 8.
+template <int D>
+__device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) {
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t wid = (int64_t)blockIdx.x * kWgWaves + wave;
-    const int g = (int)(wid % A.hkv);
-    const int64_t t2 = wid / A.hkv;
+    // workgroup = (query i, KV head g, part c); its 4 waves split the part
+    const int64_t wg = blockIdx.x;
+    const int g = (int)(wg % A.hkv);
+    const int64_t t2 = wg / A.hkv;
     const int c = (int)(t2 % A.n_part);
     const int64_t i = t2 / A.n_part;
-    if (i >= A.total_q) return;                      // uniform over the wave
+    if (i >= A.total_q) return;                      // uniform over the workgroup
 
     const QueryPos qp = query_pos(A.kv_off, nullptr, A.q_off, A.num_seqs, i);
     const int64_t nb = qp.L >> A.log2r;
     const int64_t nsel = nb < A.K ? nb : (int64_t)A.K;
     const int64_t per = (nsel + A.n_part - 1) / A.n_part;
-    const int64_t s_beg = imin64((int64_t)c * per, nsel);
-    const int64_t s_end = imin64(s_beg + per, nsel);
+    const int64_t p_beg = imin64((int64_t)c * per, nsel);
+    const int64_t p_end = imin64(p_beg + per, nsel);
+    const int64_t sub = (p_end - p_beg + kWgWaves - 1) / kWgWaves;
+    const int64_t s_beg = imin64(p_beg + wave * sub, p_end);
+    const int64_t s_end = imin64(s_beg + sub, p_end);
+    const bool owns_tail = c == A.n_part - 1 && wave == kWgWaves - 1;
     WaveWork W;
     W.sel = A.idx + i * (int64_t)A.K + s_beg;
     W.nslot = (int)(s_end - s_beg);
@@ -650,80 +688,72 @@ __device__ __forceinline__ void attn_decode_lds_body(const AttnArgs &A) {
     W.nblk_tok = W.nslot << A.log2r;
     W.tail0 = nb << A.log2r;
     W.nb = nb;
-    W.ntok = W.nblk_tok + ((c == A.n_part - 1) ? (int)(qp.L - W.tail0) : 0);
+    W.ntok = W.nblk_tok + (owns_tail ? (int)(qp.L - W.tail0) : 0);
 
-    const int tk = lane >> 3, ds = lane & 7;
-    const int hb = head_base<G>(ds);
+    const int n = lane & 15;                        // head column of this lane
+    const int gq = lane >> 4;                       // 16-lane group
     const int qh0 = g * G;
-    const int64_t row_stride = (int64_t)A.hkv * kD;
+    const uint32_t row_bytes = (uint32_t)A.hkv * kD * 2;
     const uint16_t *__restrict__ kbase = static_cast<const uint16_t *>(A.k) + (qp.kv_row0 * A.hkv + g) * kD;
     const uint16_t *__restrict__ vbase = static_cast<const uint16_t *>(A.v) + (qp.kv_row0 * A.hkv + g) * kD;
     uint8_t *ring = dyn_lds + wave * (D * kSlotBytes);
 
-    // Slot table: lane j of tab0 / tab1 holds the block id of part slot j /
-    // 64 + j (a part has at most 128 slots: n_part >= K / 128).
+    const int nsteps = (W.ntok + kStep - 1) / kStep;
+    const uint32_t ring_addr = lds_addr(ring);
     const uint32_t tab0 = (uint32_t)(lane < W.nslot ? W.sel[lane] : -1);
     const uint32_t tab1 = (uint32_t)(kWave + lane < W.nslot ? W.sel[kWave + lane] : -1);
+    // Query rows (G x 256 contiguous bytes) travel through the last ring slot,
+    // which the prologue leaves free (a compiler-visible load would make the
+    // compiler wait for it, and so for the whole ring, inside the loop).  They
+    // are requested together with the slot table, so the two latencies overlap.
+    if (nsteps > 0) {
+        const uint32_t qslot = ring_addr + (D - 1) * kSlotBytes;
+        const uint16_t *qsrc = static_cast<const uint16_t *>(A.q) + (i * A.hq + qh0) * kD;
+        const int nq = (G * kD * 2 + 1023) / 1024;        // 1 KB per load, G <= 16
+        for (int j = 0; j < nq; ++j) {
+            const int e = (j * kWave + lane) * 8;          // bf16 element of this lane
+            dma16(qsrc + (e < G * kD ? e : 0), qslot + j * 1024);
+        }
+    }
     // The ring loads are invisible to the compiler, so it would place the
     // wait for the slot table inside the prologue loop below (waiting for the
     // ring loads as well); consuming the table here puts that wait up front.
     asm volatile("" ::"v"(tab0), "v"(tab1));
 
-    AttnState<G> S;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) { S.m_run[h] = -INFINITY; S.l_run[h] = 0.0f; }
-#pragma unroll
-    for (int h = 0; h < G; ++h) { S.o[h][0] = 0.0f; S.o[h][1] = 0.0f; }
-
-    const int nsteps = (W.ntok + kStep - 1) / kStep;
-    const uint32_t ring_addr = lds_addr(ring);
-
-    // valid masks of the issued, not yet computed steps (oldest in bits 0..15)
-    uint64_t fifo = 0;
+    uint64_t fifo = 0;                               // valid masks of issued steps
     int pending = 0;
     int slot_in = 0, slot_out = 0;
     auto issue = [&](int s) {
-        const uint32_t m = issue_step_lds(W, s, lane, tab0, tab1, kbase, vbase, row_stride,
+        const uint32_t m = issue_step_lds(W, s, lane, tab0, tab1, kbase, vbase, row_bytes,
                                           ring_addr + slot_in * kSlotBytes);
         fifo |= (uint64_t)m << (16 * pending);
         ++pending;
         slot_in = slot_in + 1 == D ? 0 : slot_in + 1;
     };
-    // The query slices travel through the ring as well (a compiler-visible
-    // load would make the compiler wait for it, and so for the whole ring,
-    // inside the loop): the wave's G query rows (G x 256 contiguous bytes) go
-    // to the last slot, which the prologue leaves free, and are read back into
-    // registers once they have landed.
-    QSlices<true, G> Q;
-    if (nsteps > 0) {
-        const uint32_t qslot = ring_addr + (D - 1) * kSlotBytes;
-        const uint16_t *qsrc = static_cast<const uint16_t *>(A.q) + (i * A.hq + qh0) * kD;
-        constexpr int kQLoads = G >= 4 ? G / 4 : 1;          // 1 KB per load
-#pragma unroll
-        for (int j = 0; j < kQLoads; ++j) {
-            const int e = (j * kWave + lane) * 8;              // bf16 element of this lane
-            dma16(qsrc + (e < G * kD ? e : 0), qslot + j * 1024);
-        }
-    }
+
     const int npro = nsteps < D - 1 ? nsteps : D - 1;
     for (int s = 0; s < npro; ++s) issue(s);
+
+    bf16x8_t qb[4];                                  // B operand: q_n, dims 32k + 8gq ..
     if (nsteps > 0) {
-        wait_drain<D>(npro);                       // the query loads are older than the steps
+        if (nsteps < D - 1) wait_drain<D>(npro);
+        else wait_drain<D>(D - 1);                   // the query loads are older than the steps
         __builtin_amdgcn_sched_barrier(0);
         const uint4 *qs = reinterpret_cast<const uint4 *>(ring + (D - 1) * kSlotBytes);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int h = qk_head<G>(j, ds);
-#pragma unroll
-            for (int c4 = 0; c4 < 2; ++c4) {
-                const uint4 x = qs[h * 16 + ds * 2 + c4];
-                Q.v[j][4 * c4] = x.x; Q.v[j][4 * c4 + 1] = x.y;
-                Q.v[j][4 * c4 + 2] = x.z; Q.v[j][4 * c4 + 3] = x.w;
-            }
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const uint4 x = n < G ? qs[n * 16 + 4 * k4 + gq] : make_uint4(0u, 0u, 0u, 0u);
+            qb[k4] = __builtin_bit_cast(bf16x8_t, x);
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): read out before the slot is refilled
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): read out before the slot is refilled
         __builtin_amdgcn_sched_barrier(0);
     }
+
+    f32x4_t o[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
     for (int st = 0; st < nsteps; ++st) {
         __builtin_amdgcn_sched_barrier(0);
         if (st + D - 1 < nsteps) {
@@ -733,46 +763,142 @@ __device__ __forceinline__ void attn_decode_lds_body(const AttnArgs &A) {
             wait_drain<D>(nsteps - 1 - st);
         }
         __builtin_amdgcn_sched_barrier(0);
-        StepBuf<true> B;
-        load_step_lds(ring + slot_out * kSlotBytes, lane, tk, ds, B);
-        B.valid = (uint32_t)(fifo & 0xffffu);
+        const uint32_t valid = (uint32_t)(fifo & 0xffffu);
         fifo >>= 16;
         --pending;
+        const uint8_t *slot = ring + slot_out * kSlotBytes;
         slot_out = slot_out + 1 == D ? 0 : slot_out + 1;
-        compute_step<true, G>(B, Q, A.c, tk, ds, hb, L.p[wave], L.alpha[wave], S);
+
+        // ---- QK: token n of the tile (row of A), dims 32k + 8gq .. +8
+        const uint4 *kt = reinterpret_cast<const uint4 *>(slot);
+        f32x4_t sacc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const uint4 a = kt[n * 16 + ((4 * k4 + gq) ^ n)];
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qb[k4], sacc,
+                                                           0, 0, 0);
+        }
+        // ---- V^T operands (transposed reads), issued before the softmax
+        s16x4_t va[8];
+        {
+            // lanes 4a+c of group gq point at token 4gq + a, dims 16m + 4c
+            const int tv = 4 * gq + ((lane & 15) >> 2);
+            const int cc = lane & 3;
+            typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+            const uint32_t vrow = lds_addr(slot + 4096 + tv * 256);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int ch = 2 * m + (cc >> 1);
+                const uint32_t addr = vrow + ((ch ^ tv) << 4) + ((cc & 1) << 3);
+                va[m] = __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                        (lds_s16x4 *)(uintptr_t)addr));
+            }
+        }
+        // ---- online softmax for head n over tokens 4gq .. 4gq+3
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            x[e] = ((valid >> (4 * gq + e)) & 1u) ? sacc[e] * A.c : -INFINITY;
+        // The reference max m_run is raised only when a score exceeds it by
+        // more than 8 (log2 domain): weights relative to a stale reference are
+        // at most 2^8, which fp32 and the bf16 terms below hold easily, and the
+        // common factor cancels in o / l.  Rescales thus happen a few times
+        // per part instead of at nearly every step.
+        const float mloc = quad_group_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool raise = mloc > m_run + 8.0f;
+        if (__ballot(raise) != 0) {
+            const float m_new = raise ? mloc : m_run;
+            const float alpha = raise ? exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) o[m] *= alpha;
+            m_run = m_new;
+        }
+        const float m_safe = m_run == -INFINITY ? 0.0f : m_run;
+        float pr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[e] = exp2f(x[e] - m_safe);
+        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        // ---- P as hi + lo bf16 terms
+        s16x4_t ph, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t u = __float_as_uint(pr[e]);
+            const float hi = __uint_as_float(u & 0xffff0000u);
+            ph[e] = (short)(u >> 16);
+            pl[e] = (short)bf16_rne_bits(pr[e] - hi);
+        }
+        // ---- PV
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[m], ph, o[m], 0, 0, 0);
+            o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[m], pl, o[m], 0, 0, 0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // ---- merge the 4 waves of the workgroup through LDS (each wave writes
+    // its fragments into its own, now idle, ring region), then wave w
+    // finishes dims tiles 2w and 2w+1 of every head.
+    const float l_tot = quad_group_sum(l_run);
+    {
+        f32x4_t *frag = reinterpret_cast<f32x4_t *>(ring);             // [8][64]
+        float *ml = reinterpret_cast<float *>(ring + 8 * kWave * 16);  // [64][2]
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const float l = tok_sum(S.l_run[h]);
-        if (tk == 0) {
-            L.l[wave][hb + h] = l;
-            L.m[wave][hb + h] = S.m_run[h];
+        for (int m = 0; m < 8; ++m) frag[m * kWave + lane] = o[m];
+        ml[2 * lane] = m_run;
+        ml[2 * lane + 1] = l_tot;
+    }
+    __syncthreads();
+    float mv[kWgWaves], lv[kWgWaves];
+#pragma unroll
+    for (int v = 0; v < kWgWaves; ++v) {
+        const float *ml = reinterpret_cast<const float *>(dyn_lds + v * (D * kSlotBytes) + 8 * kWave * 16);
+        mv[v] = ml[2 * lane];
+        lv[v] = ml[2 * lane + 1];
+    }
+    float M = mv[0];
+#pragma unroll
+    for (int v = 1; v < kWgWaves; ++v) M = fmaxf(M, mv[v]);
+    const float Ms = M == -INFINITY ? 0.0f : M;
+    float wv[kWgWaves], L = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kWgWaves; ++v) {
+        wv[v] = exp2f(mv[v] - Ms);
+        L += wv[v] * lv[v];
+    }
+    if (n >= G) return;
+    const int h = qh0 + n;
+    const int64_t slotp = (i * A.hq + h) * A.n_part + c;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        const int m = 2 * wave + k2;
+        f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < kWgWaves; ++v) {
+            const f32x4_t *frag = reinterpret_cast<const f32x4_t *>(dyn_lds + v * (D * kSlotBytes));
+            acc += wv[v] * frag[m * kWave + lane];
+        }
+        const int d0 = 16 * m + 4 * gq;
+        if (A.n_part == 1) {
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            uint2 w2;
+            w2.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+            w2.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + (i * A.hq + h) * kD + d0) = w2;
+        } else {
+            *reinterpret_cast<f32x4_t *>(A.ws_o + slotp * kD + d0) = acc;
         }
     }
-    wave_lds_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        if (A.n_part == 1) {
-            const float l = L.l[wave][h];
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const int64_t off = (i * A.hq + qh0 + h) * kD + 2 * lane;
-            reinterpret_cast<uint32_t *>(A.out)[off >> 1] = pack_bf16x2(S.o[h][0] * inv, S.o[h][1] * inv);
-        } else {
-            const int64_t slot = (i * A.hq + qh0 + h) * A.n_part + c;
-            reinterpret_cast<float2 *>(A.ws_o + slot * kD)[lane] = make_float2(S.o[h][0], S.o[h][1]);
-            if (lane == 0) {
-                A.ws_ml[slot * 2 + 0] = L.m[wave][h];
-                A.ws_ml[slot * 2 + 1] = L.l[wave][h];
-            }
-        }
+    if (A.n_part > 1 && wave == 0 && gq == 0) {
+        A.ws_ml[slotp * 2 + 0] = M;
+        A.ws_ml[slotp * 2 + 1] = L;
     }
 }
 
-template <int G, int D>
-__global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_lds_kernel(AttnArgs A) {
-    attn_decode_lds_body<G, D>(A);
+template <int D>
+__global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(AttnArgs A, int G) {
+    attn_decode_mfma_body<D>(A, G);
 }
 
 // Merge part partials: one wave per (query, head); lane s < n_part reads
@@ -819,7 +945,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_combine_kernel(
 // Ring depth of the decode kernel: as deep as the LDS of one CU allows for
 // the workgroups that share it (4 waves x D slots x 8 KB per workgroup, two
 // or more workgroups per CU get D = 2).
-int ring_depth(int64_t workgroups) {
+int cu_count() {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -829,41 +955,39 @@ int ring_depth(int64_t workgroups) {
             n = 256;
         cus[dev] = n;
     }
-    return workgroups <= cus[dev] ? 4 : 2;
+    return cus[dev];
 }
 
-template <int G, int D>
-hipError_t launch_decode_lds(const AttnArgs &A, dim3 grid, hipStream_t st) {
+// Workgroups per CU the decode split aims for: a random gather of 256-byte
+// rows needs at least 8 waves per CU to approach the HBM limit (measured:
+// about 2.9 TB/s with 4 waves per CU, 4.7-5.6 TB/s with 8).
+constexpr int kDecodeWgPerCu = 2;
+
+int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
+
+template <int D>
+hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, hipStream_t st) {
     const size_t lds = (size_t)kWgWaves * D * kSlotBytes;
-    static hipError_t attr = hipFuncSetAttribute((const void *)attn_decode_lds_kernel<G, D>,
+    static hipError_t attr = hipFuncSetAttribute((const void *)attn_decode_mfma_kernel<D>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn_decode_lds_kernel<G, D>), grid, dim3(kWgWaves * kWave), lds, st, A);
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), grid, dim3(kWgWaves * kWave), lds, st, A, G);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_decode_lds_g(const AttnArgs &A, int G, dim3 grid, hipStream_t st) {
-    switch (G) {
-    case 1: return launch_decode_lds<1, D>(A, grid, st);
-    case 2: return launch_decode_lds<2, D>(A, grid, st);
-    case 4: return launch_decode_lds<4, D>(A, grid, st);
-    case 8: return launch_decode_lds<8, D>(A, grid, st);
-    default: return launch_decode_lds<16, D>(A, grid, st);
-    }
-}
-
 template <bool BF16>
-hipError_t launch_attn_t(const AttnArgs &A, int G, bool decode, hipStream_t st) {
+hipError_t launch_attn_t(const AttnArgs &A, int G, bool mfma, hipStream_t st) {
     const int64_t waves = A.total_q * A.n_part * A.hkv;
     dim3 grid((unsigned)((waves + kWgWaves - 1) / kWgWaves));
     dim3 block(kWgWaves * kWave);
     hipError_t e = hipSuccess;
     if constexpr (BF16) {
-        if (decode) {
+        if (mfma) {
+            // one workgroup per (query, KV head, part)
+            grid = dim3((unsigned)(A.total_q * A.hkv * A.n_part));
             const int D = ring_depth((int64_t)grid.x);
             trace("attn decode lds ring D=%d workgroups=%u", D, grid.x);
-            e = D == 4 ? launch_decode_lds_g<4>(A, G, grid, st) : launch_decode_lds_g<2>(A, G, grid, st);
+            e = D == 4 ? launch_decode_mfma<4>(A, G, grid, st) : launch_decode_mfma<2>(A, G, grid, st);
         } else {
             switch (G) {
             case 1: hipLaunchKernelGGL((attn_kernel_w3<BF16, 1>), grid, block, 0, st, A); break;
@@ -896,9 +1020,10 @@ hipError_t launch_attn_t(const AttnArgs &A, int G, bool decode, hipStream_t st) 
 
 int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio, bool decode) {
     (void)b; (void)a;
-    // Parts per query.  Decode cuts the K selected blocks into runs of 32 (at
-    // most 16 runs); prefill keeps one part per (query, KV head).  Never a
-    // function of the batch.
+    // Parts per query of the register-staged kernel (fp32, or bf16 rows past
+    // 32-bit offsets): decode cuts the K selected blocks into runs of 32 (at
+    // most 16 runs); prefill keeps one part per (query, KV head).  This is
+    // also the most parts any decode launch uses, so it sizes the workspace.
     if (!decode) return 1;
     const int K = budget / ratio;
     int s = K / 32;
@@ -906,6 +1031,24 @@ int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio
     if (s < 1) s = 1;
     return s;
 }
+
+namespace {
+// Parts per (query, KV head) of the matrix-core decode kernel: enough
+// workgroups for about one per CU, each part keeping at least 256 tokens
+// (4 waves x 4 steps); at most the register kernel's count, so the
+// workspace bound holds.  Depends on the batch size, so a query's output
+// may differ in the last bits between batch sizes (the split of its
+// reduction changes), never between runs of the same batch.
+int mfma_decode_parts(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
+    const int64_t units = b.total_q * (int64_t)a.hkv;
+    const int64_t want = (kDecodeWgPerCu * cu_count() + units - 1) / (units > 0 ? units : 1);
+    const int64_t cap_tokens = ((int64_t)budget) / 256;
+    int64_t p = want < cap_tokens ? want : cap_tokens;
+    const int reg_parts = attn_num_splits(b, a, budget, ratio, true);
+    if (p > reg_parts) p = reg_parts;
+    return p < 1 ? 1 : (int)p;
+}
+}  // namespace
 
 size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
     const int parts = attn_num_splits(b, a, budget, ratio, true);
@@ -923,7 +1066,15 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     A.num_seqs = b.num_seqs; A.hq = a.hq; A.hkv = a.hkv;
     A.log2r = __builtin_ctz((unsigned)ratio);
     A.K = budget / ratio;
-    A.n_part = attn_num_splits(b, a, budget, ratio, decode);
+    // The matrix-core decode kernel addresses a sequence's K/V rows with
+    // 32-bit byte offsets; longer sequences take the register-staged kernel.
+    const bool rows32 = (uint64_t)b.max_kv_len * (uint64_t)a.hkv * kD * 2 < (1ull << 32);
+    // bf16 decode and prefill both run on the matrix-core kernel; prefill
+    // keeps one part per (query, KV head), so its result never depends on
+    // the rest of the batch (chunked prefill equals single-shot bit for bit).
+    const bool mfma_path = a.dtype == QSA_BF16 && rows32;
+    A.n_part = mfma_path ? (decode ? mfma_decode_parts(b, a, budget, ratio) : 1)
+                         : attn_num_splits(b, a, budget, ratio, decode);
     A.c = a.softmax_scale * kLog2e;
     A.total_q = b.total_q;
     A.out = out;
@@ -933,8 +1084,8 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     const int G = a.hq / a.hkv;
     trace("attn total_q=%lld hkv=%d G=%d parts=%d dtype=%d", (long long)b.total_q, a.hkv, G,
           A.n_part, a.dtype);
-    return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, decode, st)
-                                : launch_attn_t<false>(A, G, decode, st);
+    return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, mfma_path, st)
+                                : launch_attn_t<false>(A, G, false, st);
 }
 
 }  // namespace qsa
