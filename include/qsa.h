@@ -162,7 +162,12 @@ qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, 
 qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b,
                            float *scores, int64_t ld_scores, uint32_t flags, void *stream);
 
-/* Workspace bytes qsa_topk_blocks needs (0 when recheck is NULL). */
+/* Workspace bytes qsa_topk_blocks needs.  With recheck == NULL (canonical
+ * scores) it is non-zero for batches of at most 256 query rows, which are
+ * selected by a multi-workgroup method that keeps per-row, per-chunk lists in
+ * the workspace (0 for larger batches).  With recheck it holds per-sequence
+ * key-norm maxima.  The workspace needs no initialisation and carries no
+ * state between calls. */
 size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio,
                                const qsa_indexer *recheck);
 
@@ -201,10 +206,12 @@ size_t qsa_attn_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t bu
  *  out: device [total_q, hq, d], dtype of q.
  *  ws:  decode: device workspace of at least qsa_attn_workspace_size()
  *       bytes; prefill: unused (may be NULL).
- * A query's result does not depend on the other queries of the launch: the
- * decode split count depends only on budget/ratio and prefill does not split,
- * so outputs are bit-identical across batch compositions (chunked prefill
- * equals single-shot prefill bit for bit).
+ * Prefill does not split a query's reduction, so its outputs do not depend
+ * on the rest of the batch (chunked prefill equals single-shot prefill bit
+ * for bit).  Decode splits each query's selected blocks into a number of
+ * parts chosen from the batch size (to fill the GPU), so a decode output is
+ * deterministic for a given batch size but may differ in the last bits
+ * between batch sizes; the selection itself never does.
  * Decode requires one query per sequence (q_offsets NULL or
  * max_q_per_seq == 1), so L = N_s.  Prefill takes any n_s (chunked prefill or
  * speculative verify): each query uses its own causal L and its own regime

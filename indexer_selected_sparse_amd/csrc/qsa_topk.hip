@@ -689,6 +689,347 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cert_kernel(
     emit_selection(LdsKey{lds_keys}, nb, T, need_eq, total_eq, out, K, S);
 }
 
+// ------------------------------------------------------------------------
+// Few-row batches (decode): each row is spread over many CUs.
+//
+// A single workgroup per row is bounded by what one CU can pull from the
+// memory hierarchy (a 32K-block row of scores alone is 128 KB).  For batches
+// of at most kMultiMaxRows rows the selection runs in two kernels, each
+// spread over the GPU, with the same exact result:
+//  1. classify (row x 2048-block chunks).  Every workgroup of a row takes the
+//     same deterministic sample of the row (64 segments of 32 consecutive
+//     blocks spread evenly; the whole row when it has at most 2048 blocks),
+//     histograms it over 2048 bins linear in the score between the sample's
+//     min and max, and picks two bins: jH, above which about (k - margin)
+//     sample scores lie, and jL, above which about (k + margin) lie, k being
+//     the rank the K-th largest score would have in the sample.  The bin map
+//     is monotone in the score, so "bin > jH" (in), "jL <= bin <= jH"
+//     (candidate) and "bin < jL" (out) split the scores in order.  Each
+//     workgroup writes the in and candidate blocks of its chunk to its own
+//     region of the workspace (no atomics, nothing to clear between calls).
+//     Dense rows (nb <= K) get their identity selection from chunk 0.
+//  2. finish (one workgroup per row).  If #in <= K <= #in + #candidates and
+//     nothing overflowed, the K - #in best candidates by (score desc, index
+//     asc) are found with the exact radix select; the selected blocks are
+//     marked in an LDS bitmap and written in ascending order by a scan.
+//     Otherwise (adversarial or heavily tied rows) the row is selected by the
+//     exact single-workgroup method.  Either way the output is exact.
+constexpr int kMultiMaxRows = 256;
+constexpr int kSample = 2048;
+constexpr int kSegLen = 32;
+constexpr int kClassifyChunk = 2048;
+constexpr int kClassifyThreads = 256;
+constexpr int kChunkCandCap = 1024;        // candidates one chunk may record
+constexpr int kMultiCandMax = 3072;        // candidates a row may have in total
+constexpr int kBitmapWordsMax = 131072 / 32;
+constexpr int kMaxChunks = 131072 / kClassifyChunk;
+
+__host__ __device__ constexpr size_t chunk_region_bytes(int K) {
+    return 16 + (size_t)K * 4 + (size_t)kChunkCandCap * 8;
+}
+
+// Region of chunk c of row i: counts {n_in, n_cand}, in[K], cand_key[cap],
+// cand_idx[cap].
+struct ChunkWs {
+    uint32_t *cnt;
+    uint32_t *in_idx;
+    uint32_t *cand_key;
+    uint32_t *cand_idx;
+};
+
+__device__ __forceinline__ ChunkWs chunk_ws(const void *ws, int64_t i, int c, int nchunks, int K) {
+    uint8_t *base = const_cast<uint8_t *>(static_cast<const uint8_t *>(ws)) +
+                    ((size_t)i * nchunks + c) * chunk_region_bytes(K);
+    ChunkWs r;
+    r.cnt = reinterpret_cast<uint32_t *>(base);
+    r.in_idx = reinterpret_cast<uint32_t *>(base + 16);
+    r.cand_key = r.in_idx + K;
+    r.cand_idx = r.cand_key + kChunkCandCap;
+    return r;
+}
+
+__global__ __launch_bounds__(kClassifyThreads) void topk_classify_kernel(
+    const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int nchunks,
+    int32_t *__restrict__ idx, void *__restrict__ ws) {
+    __shared__ uint32_t hist[kSample];
+    __shared__ uint32_t red[kClassifyThreads / kWave];
+    __shared__ float fred[2][kClassifyThreads / kWave];
+    __shared__ int sel[2];
+    const int64_t i = blockIdx.y;
+    const int c = blockIdx.x;
+    const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    if (nb <= K) {
+        if (c == 0) {
+            int32_t *out = idx + i * (int64_t)K;
+            for (int t = threadIdx.x; t < K; t += kClassifyThreads) out[t] = (t < nb) ? t : -1;
+        }
+        return;
+    }
+    const int64_t b0 = (int64_t)c * kClassifyChunk;
+    if (b0 >= nb) return;                          // uniform over the workgroup
+    const float *__restrict__ row = scores + i * ld;
+    constexpr int kPer = kClassifyChunk / kClassifyThreads;   // 8
+    // this chunk's scores and this thread's part of the sample, loaded together
+    float x[kPer], smp[kPer];
+    const bool whole = nb <= kSample;
+    const int ns = whole ? (int)nb : kSample;
+    constexpr int kSegs = kSample / kSegLen;
+    const int64_t seg_step = whole ? 0 : (nb - kSegLen) / (kSegs - 1);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t b = b0 + u * kClassifyThreads + threadIdx.x;
+        x[u] = b < nb ? row[b] : 0.0f;
+        const int t = u * kClassifyThreads + threadIdx.x;
+        const int64_t sb = whole ? t : (t / kSegLen) * seg_step + (t % kSegLen);
+        smp[u] = t < ns ? row[sb] : 0.0f;
+    }
+    for (int t = threadIdx.x; t < kSample; t += kClassifyThreads) hist[t] = 0;
+    // sample range
+    float vmin = INFINITY, vmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        if (u * kClassifyThreads + (int)threadIdx.x < ns) {
+            vmin = fminf(vmin, smp[u]);
+            vmax = fmaxf(vmax, smp[u]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, o, kWave));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, o, kWave));
+    }
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    if (lane == 0) { fred[0][wave] = vmin; fred[1][wave] = vmax; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kClassifyThreads / kWave; ++w) {
+        vmin = fminf(vmin, fred[0][w]);
+        vmax = fmaxf(vmax, fred[1][w]);
+    }
+    // monotone bin map: -1 below the sample range, 2047 at and above its top
+    const float span = vmax - vmin;
+    const float scale = span > 0.0f ? (float)kSample / span : 0.0f;
+    auto bin_of = [&](float v) -> int {
+        if (!(span > 0.0f)) return v < vmin ? -1 : (v > vmin ? kSample - 1 : 0);
+        const float t = (v - vmin) * scale;
+        return t < 0.0f ? -1 : (t >= (float)(kSample - 1) ? kSample - 1 : (int)t);
+    };
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if (u * kClassifyThreads + (int)threadIdx.x < ns) atomicAdd(&hist[bin_of(smp[u])], 1u);
+    __syncthreads();
+    // sample ranks of the bracket
+    uint32_t rank_hi, rank_lo;
+    if (whole) {
+        rank_hi = rank_lo = (uint32_t)K;
+    } else {
+        const float frac = (float)K / (float)nb;
+        const float ks = frac * (float)ns;
+        const float sd = __builtin_sqrtf(ks * (1.0f - frac));
+        const int margin = (int)(4.0f * sd) + 8;
+        const int kr = (int)__builtin_ceilf(ks);
+        rank_hi = (uint32_t)(kr - margin < 1 ? 1 : kr - margin);
+        rank_lo = (uint32_t)(kr + margin > ns ? ns : kr + margin);
+    }
+    // descending cumulative counts: thread t owns bins 8t..8t+7 from the top
+    constexpr int kBpt = kSample / kClassifyThreads;
+    uint32_t own = 0;
+    const int top = kSample - 1 - (int)threadIdx.x * kBpt;
+#pragma unroll
+    for (int e = 0; e < kBpt; ++e) own += hist[top - e];
+    // exclusive scan of `own` over threads (in order)
+    uint32_t incl = own;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) red[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kClassifyThreads / kWave; ++w) before += w < wave ? red[w] : 0u;
+    uint32_t cum = before + incl - own;            // sample scores in bins above `top`
+#pragma unroll
+    for (int e = 0; e < kBpt; ++e) {
+        const uint32_t h = hist[top - e];
+        // jH: the bin where the count from the top first reaches rank_hi, etc.
+        if (cum < rank_hi && cum + h >= rank_hi) sel[0] = top - e;
+        if (cum < rank_lo && cum + h >= rank_lo) sel[1] = top - e;
+        cum += h;
+    }
+    __syncthreads();
+    const int jH = sel[0], jL = sel[1];
+    // classify this chunk: in = bin > jH, candidate = jL <= bin <= jH
+    const ChunkWs r = chunk_ws(ws, i, c, nchunks, K);
+    uint32_t n_in = 0, n_cd = 0;
+    uint64_t m_in[kPer], m_cd[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t b = b0 + u * kClassifyThreads + threadIdx.x;
+        const bool ok = b < nb;
+        const int bn = bin_of(x[u]);
+        m_in[u] = __ballot(ok && bn > jH);
+        m_cd[u] = __ballot(ok && bn >= jL && bn <= jH);
+        n_in += (uint32_t)__builtin_popcountll(m_in[u]);
+        n_cd += (uint32_t)__builtin_popcountll(m_cd[u]);
+    }
+    // per-wave totals -> offsets of this wave inside the chunk's lists
+    __shared__ uint32_t wcnt[2][kClassifyThreads / kWave];
+    if (lane == 0) { wcnt[0][wave] = n_in; wcnt[1][wave] = n_cd; }
+    __syncthreads();
+    uint32_t off_in = 0, off_cd = 0, tot_in = 0, tot_cd = 0;
+#pragma unroll
+    for (int w = 0; w < kClassifyThreads / kWave; ++w) {
+        off_in += w < wave ? wcnt[0][w] : 0u;
+        off_cd += w < wave ? wcnt[1][w] : 0u;
+        tot_in += wcnt[0][w];
+        tot_cd += wcnt[1][w];
+    }
+    if (threadIdx.x == 0) { r.cnt[0] = tot_in; r.cnt[1] = tot_cd; }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const uint32_t b = (uint32_t)(b0 + u * kClassifyThreads + threadIdx.x);
+        if ((m_in[u] >> lane) & 1u) {
+            const uint32_t pos = off_in + lanes_below(m_in[u]);
+            if (pos < (uint32_t)K) r.in_idx[pos] = b;
+        }
+        if ((m_cd[u] >> lane) & 1u) {
+            const uint32_t pos = off_cd + lanes_below(m_cd[u]);
+            if (pos < (uint32_t)kChunkCandCap) {
+                r.cand_key[pos] = order_key(x[u]);
+                r.cand_idx[pos] = b;
+            }
+        }
+        off_in += (uint32_t)__builtin_popcountll(m_in[u]);
+        off_cd += (uint32_t)__builtin_popcountll(m_cd[u]);
+    }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(
+    const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int nchunks,
+    int32_t *__restrict__ idx, const void *__restrict__ ws) {
+    __shared__ TopkShared S;
+    __shared__ uint32_t ck[kMultiCandMax], ci[kMultiCandMax];
+    __shared__ uint32_t bitmap[kBitmapWordsMax];
+    __shared__ uint32_t c_in[kMaxChunks + 1], c_cd[kMaxChunks + 1];
+    __shared__ uint32_t bad;
+    const int64_t i = blockIdx.x;
+    const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    if (nb <= K) return;                           // written by the classify kernel
+    int32_t *out = idx + i * (int64_t)K;
+    const int nch = (int)((nb + kClassifyChunk - 1) / kClassifyChunk);
+    // per-chunk counts -> prefix offsets: lane c of wave 0 reads chunk c
+    // (at most 64 chunks), then a wave scan
+    if (threadIdx.x < kWave) {
+        const int ln0 = threadIdx.x;
+        uint32_t ni = 0, nd = 0;
+        if (ln0 < nch) {
+            const ChunkWs r = chunk_ws(ws, i, ln0, nchunks, K);
+            ni = r.cnt[0];
+            nd = r.cnt[1];
+        }
+        const bool over = __ballot(ln0 < nch && (ni > (uint32_t)K || nd > (uint32_t)kChunkCandCap)) != 0;
+        uint32_t si = ni, sd = nd;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t yi = (uint32_t)__shfl_up((int)si, o, kWave);
+            const uint32_t yd = (uint32_t)__shfl_up((int)sd, o, kWave);
+            if (ln0 >= o) { si += yi; sd += yd; }
+        }
+        if (ln0 < nch) { c_in[ln0] = si - ni; c_cd[ln0] = sd - nd; }
+        if (ln0 == nch - 1) {
+            c_in[nch] = si;
+            c_cd[nch] = sd;
+            bad = over || si > (uint32_t)K || sd > (uint32_t)kMultiCandMax || si + sd < (uint32_t)K;
+        }
+    }
+    __syncthreads();
+    if (bad) {
+        // the bracket missed: exact select over the whole row
+        const GlobalKey key{scores + i * ld};
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+        for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+            const uint32_t k = key(b);
+            kmin = min(kmin, k);
+            kmax = max(kmax, k);
+        }
+        wg_minmax(kmin, kmax, S);
+        select_row(key, nb, K, kmin, kmax, out, S);
+        return;
+    }
+    const uint32_t n_in = c_in[nch], n_cand = c_cd[nch];
+    const uint32_t need = (uint32_t)K - n_in;
+    const int nwords = (int)((nb + 31) / 32);
+    for (int w = threadIdx.x; w < nwords; w += kTopkThreads) bitmap[w] = 0u;
+    // gather the candidates of every chunk (wave w takes chunks w, w+16, ...)
+    const int wv = threadIdx.x / kWave, ln = threadIdx.x & (kWave - 1);
+    uint32_t cmin = 0xffffffffu, cmax = 0u;
+    for (int c = wv; c < nch; c += kTopkWaves) {
+        const ChunkWs r = chunk_ws(ws, i, c, nchunks, K);
+        const uint32_t nd = c_cd[c + 1] - c_cd[c];
+        for (uint32_t j = ln; j < nd; j += kWave) {
+            const uint32_t k = r.cand_key[j];
+            ck[c_cd[c] + j] = k;
+            ci[c_cd[c] + j] = r.cand_idx[j];
+            cmin = min(cmin, k);
+            cmax = max(cmax, k);
+        }
+    }
+    wg_minmax(cmin, cmax, S);                      // barriers publish ck, ci, bitmap
+    for (int c = wv; c < nch; c += kTopkWaves) {
+        const ChunkWs r = chunk_ws(ws, i, c, nchunks, K);
+        const uint32_t ni = c_in[c + 1] - c_in[c];
+        for (uint32_t j = ln; j < ni; j += kWave) {
+            const uint32_t b = r.in_idx[j];
+            atomicOr(&bitmap[b >> 5], 1u << (b & 31));
+        }
+    }
+    if (need > 0) {
+        uint32_t need_eq, total_eq;
+        const uint32_t T = radix_select(LdsKey{ck}, (int64_t)n_cand, need, cmin, cmax, S, need_eq,
+                                        total_eq);
+        const bool all_eq = need_eq >= total_eq;
+        for (uint32_t j = threadIdx.x; j < n_cand; j += kTopkThreads) {
+            const uint32_t k = ck[j];
+            bool take = k > T;
+            if (k == T) {
+                if (all_eq) {
+                    take = true;
+                } else {
+                    // ties at T go to the lower block index
+                    const uint32_t me = ci[j];
+                    uint32_t rank = 0;
+                    for (uint32_t q = 0; q < n_cand; ++q) rank += (ck[q] == T && ci[q] < me) ? 1u : 0u;
+                    take = rank < need_eq;
+                }
+            }
+            if (take) atomicOr(&bitmap[ci[j] >> 5], 1u << (ci[j] & 31));
+        }
+    }
+    __syncthreads();
+    // ascending output: per-thread runs of words, popcounts scanned
+    const int per = (nwords + kTopkThreads - 1) / kTopkThreads;
+    const int w0 = threadIdx.x * per;
+    uint32_t cnt = 0;
+    for (int w = w0; w < w0 + per && w < nwords; ++w) cnt += (uint32_t)__builtin_popcount(bitmap[w]);
+    uint32_t tot;
+    uint32_t pos = wg_scan(cnt, S, tot);
+    for (int w = w0; w < w0 + per && w < nwords; ++w) {
+        uint32_t m = bitmap[w];
+        while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1;
+            if (pos < (uint32_t)K) out[pos] = w * 32 + bit;
+            ++pos;
+        }
+    }
+}
+
 }  // namespace
 
 static int64_t norm_chunks(const qsa_batch &b, int ratio) {
@@ -697,8 +1038,13 @@ static int64_t norm_chunks(const qsa_batch &b, int ratio) {
 }
 
 size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa_indexer *recheck) {
-    (void)budget;
-    if (recheck == nullptr) return 0;
+    if (recheck == nullptr) {
+        // few-row batches use the multi-workgroup select and its row lists
+        if (b.total_q < 1 || b.total_q > kMultiMaxRows) return 0;
+        const int64_t max_nb = b.max_kv_len / ratio;
+        const int64_t nch = max_nb > 0 ? (max_nb + kClassifyChunk - 1) / kClassifyChunk : 1;
+        return (size_t)b.total_q * (size_t)nch * chunk_region_bytes(budget / ratio) + 256;
+    }
     return (size_t)b.num_seqs * (size_t)norm_chunks(b, ratio) * sizeof(float) + 256;
 }
 
@@ -737,6 +1083,18 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
         hipLaunchKernelGGL(topk_cert_kernel, grid, dim3(kTopkThreads), lds, st, scores, ld,
                            b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, cix,
                            part, nch);
+        return hipGetLastError();
+    }
+    if (b.total_q <= kMultiMaxRows && max_nb <= (int64_t)kBitmapWordsMax * 32) {
+        const int chunks = (int)(max_nb > 0 ? (max_nb + kClassifyChunk - 1) / kClassifyChunk : 1);
+        trace("topk multi rows=%lld K=%d ratio=%d chunks=%d", (long long)b.total_q, K, ratio, chunks);
+        hipLaunchKernelGGL(topk_classify_kernel, dim3((unsigned)chunks, (unsigned)b.total_q),
+                           dim3(kClassifyThreads), 0, st, scores, ld, b.kv_offsets, b.q_offsets,
+                           b.num_seqs, log2r, K, chunks, idx, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(topk_finish_kernel, grid, dim3(kTopkThreads), 0, st, scores, ld,
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, chunks, idx, ws);
         return hipGetLastError();
     }
     if (max_nb <= kLdsKeys) {

@@ -36,7 +36,8 @@ class DeviceProblem:
     idx: torch.Tensor
     out: torch.Tensor
     attn_ws: Optional[torch.Tensor]
-    topk_ws: Optional[torch.Tensor]
+    topk_ws: Optional[torch.Tensor]        # certified (matrix-core scores) selection
+    topk_ws_canon: Optional[torch.Tensor]  # selection from canonical scores
     decode: bool
 
     @property
@@ -53,7 +54,7 @@ class DeviceProblem:
     def topk(self, certified: bool = False, stream=None) -> None:
         recheck = (self.q_idx, self.w, self.kc, self.kc_scale) if certified else None
         topk_blocks(self.scores, self.budget, self.ratio, self.batch, self.idx, recheck=recheck,
-                    ws=self.topk_ws if certified else None, stream=stream)
+                    ws=self.topk_ws if certified else self.topk_ws_canon, stream=stream)
 
     def attend(self, stream=None) -> None:
         fn = sparse_attn_decode if self.decode else sparse_attn_prefill
@@ -91,10 +92,13 @@ def upload(wl, device: str = "cuda", decode: Optional[bool] = None, mfma_ws: boo
         scores=torch.zeros((max(tq, 1), ld), dtype=torch.float32, device=device),
         idx=torch.full((max(tq, 1), sp.budget // sp.ratio), -7, dtype=torch.int32, device=device),
         out=torch.zeros((max(tq, 1), sp.hq, sp.d), dtype=q.dtype, device=device),
-        attn_ws=None, topk_ws=None, decode=decode)
+        attn_ws=None, topk_ws=None, topk_ws_canon=None, decode=decode)
     nws = attn_workspace_size(q, K, V, sp.softmax_scale, sp.budget, sp.ratio, batch)
     if nws:
         dp.attn_ws = torch.empty(nws, dtype=torch.uint8, device=device)
+    cws = topk_workspace_size(batch, sp.budget, sp.ratio, None)
+    if cws:
+        dp.topk_ws_canon = torch.empty(cws, dtype=torch.uint8, device=device)
     if mfma_ws:
         tws = topk_workspace_size(batch, sp.budget, sp.ratio,
                                   (dp.q_idx, dp.w, dp.kc, dp.kc_scale))

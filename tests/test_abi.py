@@ -158,7 +158,12 @@ def test_workspace_sizes():
     # decode cuts K=512 into 16 parts: 16 partials of (m, l) + 128 outputs
     # per query head
     assert n >= 32 * 32 * 16 * 130 * 4
-    assert Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, None) == 0
+    # canonical scores: a few-row batch keeps per-row lists (header, K "in"
+    # indices, candidate keys and indices); large batches need none
+    n = Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, None)
+    assert n >= 32 * (512 * 4 + 2 * 1024 * 4)
+    big = _batch(total_q=4096, num_seqs=4096)
+    assert Q.lib().qsa_topk_workspace_size(ctypes.byref(big), 2048, 4, None) == 0
     # re-checked top-k: one fp32 key-norm maximum per 256 blocks per sequence
     ix = _ix()
     n = Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, ctypes.byref(ix))
