@@ -12,8 +12,10 @@ Workloads (synthetic, seeded; see qsa_workloads):
                 sparse prefill attention.
 
 A step is one pass of the whole hot path over one batch with every input
-resident in HBM.  Key compression is an ingest-time pass, timed on its own
-(`compress_ms`).  Decode steps rotate over several device copies of the
+resident in HBM.  `value` is queries per second of the step replayed from a
+HIP graph (one graph per input copy); `step_ms.eager` is the same step
+launched call by call.  Key compression is an ingest-time pass, timed on its
+own (`compress_ms`).  Decode steps rotate over several device copies of the
 inputs (more distinct bytes than the 256 MB last-level cache holds), so a
 step is not served from a cache warmed by the previous one.
 
@@ -41,7 +43,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
-VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector peak (dot2 / dual-issue forms)
 ATTN_SRC = os.path.join(ROOT, "indexer_selected_sparse_amd", "csrc", "qsa_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_hbm_traffic.md")
 
@@ -55,6 +56,8 @@ def parse():
                    choices=["batched_decode", "long_decode", "chunked_prefill"])
     p.add_argument("--replicas", type=int, default=0, help="input copies to rotate over (0=auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time eager launches only (default: replay the step from a HIP graph)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
@@ -249,10 +252,41 @@ def main():
         e[3].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    ms_step = dt * 1e3 / args.steps
+    eager_ms_step = dt * 1e3 / args.steps
     t_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    # The whole step captured once per input copy in a HIP graph and replayed:
+    # the way a serving loop runs it (no call synchronises or allocates, so
+    # the step captures as is).  Kernel times above come from the eager loop.
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for p in reps:                      # settle lazy initialisation outside capture
+                score(p)
+                topk(p)
+                p.attend()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for p in reps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                score(p)
+                topk(p)
+                p.attend()
+            graphs.append(g)
+        for s_ in range(args.warmup):
+            graphs[s_ % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            graphs[s_ % R].replay()
+        torch.cuda.synchronize()
+        graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = graph_ms_step if graphs else eager_ms_step
 
     qps = wl.total_q / (ms_step / 1e3)
     rec = {
@@ -267,13 +301,17 @@ def main():
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R},
         "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn},
+        "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
     }
     if prefill:
         f_idx, f_attn = prefill_flops(wl)
         ach = f_attn / (t_attn * 1e-3) / 1e12
-        rec["roofline"] = {"bound": "alu", "achieved": ach, "peak": VALU_FP32_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / VALU_FP32_PEAK_TFLOPS, "traffic": None,
+        # the prefill attention computes QK and PV on the bf16 matrix cores
+        # (PV as two bf16 terms of the probabilities, counted once here); it
+        # is bounded by gathering each query's own token set, not by them
+        rec["roofline"] = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                            "kernel": "qsa_sparse_attn_prefill (causal gather attention)",
                            "flops_per_launch": f_attn, "avg_ms": t_attn}
         mf = f_idx / (t_score * 1e-3) / 1e12
