@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import qsa_workloads as W
 from tests.parity import full_check, gpu_available, run_gpu
 
@@ -158,3 +159,67 @@ def test_full_size_chunked_prefill_sampled():
     _print(f"[parity] full chunked prefill: total_q={wl.total_q}, sampled {len(q)} queries")
     _, _, worst = full_check(wl, query_ids=q)
     _print(f"[parity] full chunked prefill: ok, worst err/limit = {worst:.3f}")
+
+
+def test_decode_workspace_reused_across_batch_shapes():
+    # one decode workspace shared by batches of different shapes, used
+    # alternately: each shape must reproduce its first result bit for bit
+    # (the workspace carries no state between calls)
+    from indexer_selected_sparse_amd import pipeline
+    big = W.make(W.BATCHED_DECODE, lens=[9000 + 997 * j for j in range(24)], seed=31)
+    small = W.make(dataclasses.replace(W.LONG_DECODE, kc_dtype="bf16"), lens=[20000, 12000, 30001], seed=32)
+    dps = [pipeline.upload(wl, "cuda") for wl in (big, small)]
+    ws = torch.zeros(max(dp.attn_ws.numel() for dp in dps), dtype=torch.uint8, device="cuda")
+    for dp in dps:
+        dp.attn_ws = ws
+        dp.compress()
+    outs = []
+    for rnd in range(3):
+        for k, dp in enumerate(dps):
+            dp.step()
+            torch.cuda.synchronize()
+            o = dp.out.clone()
+            if rnd == 0:
+                outs.append(o)
+            else:
+                assert torch.equal(o, outs[k]), f"round {rnd} batch {k} differs"
+    for wl, o in zip((big, small), outs):
+        ref = oracle.run_workload(wl, query_ids=np.arange(min(wl.total_q, 4)))
+        from tests.parity import check_out
+        check_out(wl, {"out": o.float().cpu().numpy().astype(np.float64)}, ref, np.arange(min(wl.total_q, 4)))
+
+
+def test_graph_replays_match_eager():
+    # the whole decode step captured in a HIP graph and replayed several
+    # times, with eager work and synchronisation between replays
+    from indexer_selected_sparse_amd import pipeline
+    wl = W.make(W.BATCHED_DECODE, lens=[8200 + 1711 * j for j in range(12)], seed=33)
+    dp = pipeline.upload(wl, "cuda")
+    dp.compress()
+    dp.step()
+    torch.cuda.synchronize()
+    eager = (dp.scores.clone(), dp.idx.clone(), dp.out.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dp.step()
+    for rep in range(4):
+        dp.scores.fill_(-1.0)
+        dp.idx.fill_(-5)
+        dp.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        # scores past a row's visible blocks are left untouched by design
+        nbs = [int(L) // wl.spec.ratio for L in wl.visible_lengths()]
+        for r, nb in enumerate(nbs):
+            assert torch.equal(dp.scores[r, :nb], eager[0][r, :nb]), f"replay {rep}: scores row {r}"
+        assert torch.equal(dp.idx, eager[1]), f"replay {rep}: idx differs from the eager step"
+        assert torch.equal(dp.out, eager[2]), f"replay {rep}: out differs from the eager step"
+        dp.step()                       # eager work between replays
+        torch.cuda.synchronize()
