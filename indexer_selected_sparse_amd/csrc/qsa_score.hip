@@ -13,12 +13,15 @@
 // e4m3 code) is exact in fp32, so a fused multiply-add there gives the same
 // bits as multiply-then-add; fp32 inputs use a separate multiply and add.
 //
-// Decode is a GEMV per query and bound by HBM bandwidth (and, for e4m3 keys,
-// by VALU issue): one lane owns one block and keeps its whole key row in
-// registers (all row loads of the wave are in flight together, so the L1
-// keeps each line for the burst); the query's H x D values are wave-uniform,
-// read through the scalar unit.  Workgroup = 256 blocks of one query; blocks
-// that are not yet visible to the query (b >= floor(L/ratio)) are skipped.
+// Decode is a GEMV per query.  One lane owns one block (a compressed key
+// row); the query's H x D values are wave-uniform and reach the FMAs through
+// the scalar unit.  Workgroup = 256 blocks of one query; blocks that are not
+// yet visible to the query (b >= floor(L/ratio)) are skipped.  With bf16
+// queries and bf16 / e4m3 keys the arithmetic is H*D fused multiply-adds per
+// block on the vector ALU (the canonical order admits no packed or matrix
+// form), which for decode batches takes about as long as reading the keys.
+#include <type_traits>
+
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -97,24 +100,16 @@ __device__ __forceinline__ void load_q(const float *__restrict__ q, int off, flo
     for (int e = 0; e < N; ++e) v[e] = q[off + e];
 }
 
-// acc + q*k with the canonical rounding: fused only when q*k is exact.
-template <bool EXACT>
-__device__ __forceinline__ float mac(float acc, float q, float k) {
-    if constexpr (EXACT) {
-        return __builtin_fmaf(q, k, acc);
-    } else {
-        float p = q * k;
-        return acc + p;
-    }
-}
-
+// At least one fp32 operand: products are rounded, so multiply and add are
+// separate operations.  The key row is widened once to fp32 and kept in
+// registers; the query values are wave-uniform and come through the scalar
+// unit.
 template <typename QT, typename KT, int D, int H>
-__global__ __launch_bounds__(kScoreThreads) void score_canonical_kernel(
+__global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
     const QT *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const float *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
     int log2r, float *__restrict__ scores, int64_t ld) {
-    constexpr bool kExact = std::is_same<QT, uint16_t>::value && !std::is_same<KT, float>::value;
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
@@ -126,88 +121,229 @@ __global__ __launch_bounds__(kScoreThreads) void score_canonical_kernel(
 
     const float sc = kE4M3 ? kc_scale[row] : 1.0f;
     const float *__restrict__ wi = w + i * (int64_t)H;
+    float kf[D];
+    {
+        KRow<KT, D> k;
+        k.load(kc + row * D);
+        if constexpr (kE4M3) {
+#pragma unroll
+            for (int c = 0; c < D / 4; ++c) {
+                const float2 lo = e4m3x2_to_f32<false>(k.u[c]);
+                const float2 hi = e4m3x2_to_f32<true>(k.u[c]);
+                kf[4 * c] = lo.x; kf[4 * c + 1] = lo.y; kf[4 * c + 2] = hi.x; kf[4 * c + 3] = hi.y;
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < D; ++d) kf[d] = k.get(d);
+        }
+    }
+    const QT *__restrict__ q = q_idx + i * (int64_t)(H * D);
     float s = 0.0f;
-
-    if constexpr (kExact) {
-        // bf16 query x (bf16 | e4m3) key: every product is exact in fp32, so
-        // the canonical step acc = fl(acc + q*k) is one IEEE fused
-        // multiply-add.  The query pair (q_d, q_d+1) arrives as one dword in
-        // an SGPR and is widened by two scalar ops (shift / mask); the
-        // scheduling groups below interleave each scalar widening with its
-        // FMA so that only a few widened values are live at a time (scalar
-        // and vector ops of different waves issue in the same cycle).
-        float kf[D];
-        {
-            KRow<KT, D> k;
-            k.load(kc + row * D);
-            if constexpr (kE4M3) {
+#pragma unroll 1
+    for (int h = 0; h < H; ++h) {
+        float dot = 0.0f;
 #pragma unroll
-                for (int c = 0; c < D / 4; ++c) {
-                    const float2 a = e4m3x2_to_f32<false>(k.u[c]);
-                    const float2 bb = e4m3x2_to_f32<true>(k.u[c]);
-                    kf[4 * c] = a.x; kf[4 * c + 1] = a.y; kf[4 * c + 2] = bb.x; kf[4 * c + 3] = bb.y;
-                }
-            } else {
+        for (int d0 = 0; d0 < D; d0 += 32) {
+            float qv[32];
+            load_q<32>(q, h * D + d0, qv);
 #pragma unroll
-                for (int d = 0; d < D; ++d) kf[d] = k.get(d);
+            for (int e = 0; e < 32; ++e) {
+                const float p = qv[e] * kf[d0 + e];
+                dot = dot + p;
             }
         }
-        const uint32_t *__restrict__ q32 =
-            reinterpret_cast<const uint32_t *>(q_idx) + i * (int64_t)(H * D / 2);
-#pragma unroll 1
-        for (int h = 0; h < H; ++h) {
-            float dot = 0.0f;
+        if constexpr (kE4M3) dot = dot * sc;
+        const float r = dot > 0.0f ? dot : 0.0f;
+        const float t = wi[h] * r;
+        s = s + t;
+    }
+    if (active) scores[i * ld + b] = s;
+}
+
+// Exact products (bf16 query; bf16 or e4m3 keys).  One lane owns one block;
+// its whole key row is requested at once (the loads of a row go out back to
+// back, so the L1 still holds each line for the later pieces of it), and the
+// row is widened and used chunk by chunk (kExactChunk dims) as it lands: the
+// H per-head sums advance together chunk by chunk, each in ascending d, so
+// every head's chain of fused multiply-adds is the canonical one.  Widening
+// one chunk at a time keeps the register footprint at one raw row, one
+// widened chunk and H sums, so every workgroup of a decode batch is resident
+// at once; with the whole row widened up front (128 registers for it alone)
+// three workgroups fit per CU and the fourth ran as a second round on an
+// otherwise idle chip.  Measured on one MI355X, the FMA chain then runs at
+// the VALU issue rate and the remaining time is the wait for the first rows.
+constexpr int kExactChunk = 32;
+constexpr int kExactThreads = 256;
+
+// The key loads and the query loads of this kernel are written as
+// instructions with explicit waits.  Left to itself the compiler issues the
+// chunk loads out of order (loads complete in issue order, so a wait for
+// chunk 0 then also waits for later chunks) and hoists the query loads of all
+// (chunk, head) steps ahead of their use until scalar registers spill.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// Compile-time loop: f(integral_constant<int, B>) ... f(integral_constant<int, E-1>).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// One 16-byte load of this lane's key row at byte offset OFF.
+template <int OFF>
+__device__ __forceinline__ u32x4 key_load16(const void *row) {
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(r) : "v"(row), "n"(OFF) : "memory");
+    return r;
+}
+// Wait until at most N vector loads are outstanding; the registers of the
+// chunk that is about to be used are tied to the wait so that nothing reads
+// them earlier.
+template <int N, int L>
+__device__ __forceinline__ void key_wait(u32x4 (&u)[L]) {
+    static_assert(L == 2 || L == 4, "chunk of 2 or 4 loads");
+    if constexpr (L == 2)
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(u[0]), "+v"(u[1]) : "n"(N));
+    else
+        asm volatile("s_waitcnt vmcnt(%4)" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]) : "n"(N));
+}
+// Query values, 16 wave-uniform dwords per (chunk, head) step, go through
+// the scalar unit into scalar registers one step ahead: a step's wait and the
+// next step's load are one statement, so the load is in flight while the
+// step's FMAs run.  The wait is also tied to the sum the previous step wrote
+// (so that step is finished and only two steps' values are live).  Scalar
+// loads may complete out of order, hence lgkmcnt(0).
+template <int OFF>
+__device__ __forceinline__ u32x16 query_load16(const uint32_t *p) {
+    u32x16 r;
+    asm volatile("s_load_dwordx16 %0, %1, %2" : "=s"(r) : "s"(p), "n"(OFF) : "memory");
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x16 query_wait_load16(u32x16 &cur, float &prev, const uint32_t *p) {
+    u32x16 nxt;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_load_dwordx16 %0, %3, %4"
+                 : "=&s"(nxt), "+s"(cur), "+v"(prev) : "s"(p), "n"(OFF) : "memory");
+    return nxt;
+}
+template <int OFF>
+__device__ __forceinline__ u32x16 query_wait_load16(u32x16 &cur, const uint32_t *p) {
+    u32x16 nxt;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_load_dwordx16 %0, %2, %3"
+                 : "=&s"(nxt), "+s"(cur) : "s"(p), "n"(OFF) : "memory");
+    return nxt;
+}
+__device__ __forceinline__ void query_wait(u32x16 &u, float &prev) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(u), "+v"(prev));
+}
+
+template <typename KT, int CH>
+__device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * (int)sizeof(KT) / 16], float (&f)[CH]) {
+    if constexpr (std::is_same<KT, uint8_t>::value) {
 #pragma unroll
-            for (int j = 0; j < D / 2; ++j) {
-                const uint32_t u = q32[h * (D / 2) + j];
-                dot = __builtin_fmaf(bf16lo(u), kf[2 * j], dot);
-                dot = __builtin_fmaf(bf16hi(u), kf[2 * j + 1], dot);
-            }
+        for (int v = 0; v < CH / 16; ++v) {
+            const u32x4 w4 = u[v];
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);   // one SALU op
-                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU op
+            for (int e = 0; e < 4; ++e) {
+                const float2 a = e4m3x2_to_f32<false>(w4[e]);
+                const float2 b = e4m3x2_to_f32<true>(w4[e]);
+                f[16 * v + 4 * e] = a.x; f[16 * v + 4 * e + 1] = a.y;
+                f[16 * v + 4 * e + 2] = b.x; f[16 * v + 4 * e + 3] = b.y;
             }
-            if constexpr (kE4M3) dot = dot * sc;
-            const float r = dot > 0.0f ? dot : 0.0f;
-            const float t = wi[h] * r;
-            s = s + t;
         }
     } else {
-        // fp32 on either side: products are rounded, so multiply and add are
-        // separate operations.  The key row is widened once to fp32.
-        float kf[D];
-        {
-            KRow<KT, D> k;
-            k.load(kc + row * D);
-            if constexpr (kE4M3) {
 #pragma unroll
-                for (int c = 0; c < D / 4; ++c) {
-                    const float2 lo = e4m3x2_to_f32<false>(k.u[c]);
-                    const float2 hi = e4m3x2_to_f32<true>(k.u[c]);
-                    kf[4 * c] = lo.x; kf[4 * c + 1] = lo.y; kf[4 * c + 2] = hi.x; kf[4 * c + 3] = hi.y;
-                }
+        for (int v = 0; v < CH / 8; ++v) {
+            const u32x4 w4 = u[v];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[8 * v + 2 * e] = bf16lo(w4[e]);
+                f[8 * v + 2 * e + 1] = bf16hi(w4[e]);
+            }
+        }
+    }
+}
+
+template <typename KT, int D, int H>
+__global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
+    const float *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
+    int log2r, float *__restrict__ scores, int64_t ld) {
+    constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
+    constexpr int CH = kExactChunk;
+    constexpr int NCH = D / CH;
+    constexpr int LPC = CH * (int)sizeof(KT) / 16;   // 16-byte loads per chunk of one row
+    constexpr int QW = CH / 2;                       // query dwords per (chunk, head)
+    static_assert(D % CH == 0 && (LPC == 2 || LPC == 4) && QW == 16, "chunk layout");
+    static_assert((NCH - 1) * LPC < 64, "loads in flight fit the wait counter");
+    const int64_t i = blockIdx.x;
+    const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    const int64_t b = (int64_t)blockIdx.y * kExactThreads + threadIdx.x;
+    if ((int64_t)blockIdx.y * kExactThreads >= nb) return;   // whole workgroup invisible
+    const bool active = b < nb;
+    const int64_t row = qp.blk_row0 + (active ? b : 0);
+    const float sc = kE4M3 ? kc_scale[row] : 1.0f;
+    const KT *krow = kc + row * D;
+    const uint32_t *q32 = reinterpret_cast<const uint32_t *>(q_idx) + i * (int64_t)(H * D / 2);
+
+    u32x4 raw[NCH][LPC];
+    static_for<0, NCH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        raw[c][0] = key_load16<c * LPC * 16 + 0>(krow);
+        raw[c][1] = key_load16<c * LPC * 16 + 16>(krow);
+        if constexpr (LPC == 4) {
+            raw[c][2] = key_load16<c * LPC * 16 + 32>(krow);
+            raw[c][3] = key_load16<c * LPC * 16 + 48>(krow);
+        }
+    });
+    u32x16 qbuf[2];
+    qbuf[0] = query_load16<0>(q32);
+
+    float acc[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) acc[h] = 0.0f;
+    // (chunk, head) steps in order; chunk c is waited for at its first step
+    // (the loads of chunks c+1.. may still be in flight).
+    static_for<0, NCH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        key_wait<(NCH - 1 - c) * LPC>(raw[c]);
+        float kf[CH];
+        widen_chunk<KT, CH>(raw[c], kf);
+        static_for<0, H>([&](auto hh) {
+            constexpr int h = decltype(hh)::value;
+            constexpr int t = c * H + h;
+            u32x16 &qu = qbuf[t & 1];
+            constexpr int tn = t + 1;                // next step: its query offset in bytes
+            constexpr int off = 4 * ((tn % H) * (D / 2) + (tn / H) * QW);
+            if constexpr (tn < NCH * H) {
+                if constexpr (t == 0)
+                    qbuf[tn & 1] = query_wait_load16<off>(qu, q32);
+                else
+                    qbuf[tn & 1] = query_wait_load16<off>(qu, acc[(t - 1) % H], q32);
             } else {
-#pragma unroll
-                for (int d = 0; d < D; ++d) kf[d] = k.get(d);
+                query_wait(qu, acc[(t - 1 + H) % H]);
             }
-        }
-        const QT *__restrict__ q = q_idx + i * (int64_t)(H * D);
-#pragma unroll 1
-        for (int h = 0; h < H; ++h) {
-            float dot = 0.0f;
 #pragma unroll
-            for (int d0 = 0; d0 < D; d0 += 32) {
-                float qv[32];
-                load_q<32>(q, h * D + d0, qv);
-#pragma unroll
-                for (int e = 0; e < 32; ++e) dot = mac<false>(dot, qv[e], kf[d0 + e]);
+            for (int j = 0; j < QW; ++j) {
+                acc[h] = __builtin_fmaf(bf16lo(qu[j]), kf[2 * j], acc[h]);
+                acc[h] = __builtin_fmaf(bf16hi(qu[j]), kf[2 * j + 1], acc[h]);
             }
-            if constexpr (kE4M3) dot = dot * sc;
-            const float r = dot > 0.0f ? dot : 0.0f;
-            const float t = wi[h] * r;
-            s = s + t;
-        }
+        });
+    });
+    const float *__restrict__ wi = w + i * (int64_t)H;
+    float s = 0.0f;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        float dot = acc[h];
+        if constexpr (kE4M3) dot = dot * sc;
+        const float r = dot > 0.0f ? dot : 0.0f;
+        const float t = wi[h] * r;
+        s = s + t;
     }
     if (active) scores[i * ld + b] = s;
 }
@@ -217,19 +353,39 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
                       int64_t ld, dim3 grid, hipStream_t st) {
     const QT *q = static_cast<const QT *>(ix.q_idx);
     const KT *kc = static_cast<const KT *>(ix.kc);
-    dim3 block(kScoreThreads);
-#define QSA_SCORE_LAUNCH(HH)                                                                   \
-    hipLaunchKernelGGL((score_canonical_kernel<QT, KT, D, HH>), grid, block, 0, st, q, ix.w, kc, \
+    constexpr bool kExact = std::is_same<QT, uint16_t>::value && !std::is_same<KT, float>::value;
+    const int64_t max_nb = b.max_kv_len >> log2r;
+    if constexpr (kExact) {
+        grid.y = (unsigned)((max_nb + kExactThreads - 1) / kExactThreads);
+        dim3 block(kExactThreads);
+#define QSA_SCORE_LAUNCH(HH)                                                                       \
+    hipLaunchKernelGGL((score_exact_kernel<KT, D, HH>), grid, block, 0, st, q, ix.w, kc,           \
                        ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
                        scores, ld)
-    switch (ix.h_idx) {
-    case 1: QSA_SCORE_LAUNCH(1); break;
-    case 2: QSA_SCORE_LAUNCH(2); break;
-    case 4: QSA_SCORE_LAUNCH(4); break;
-    case 8: QSA_SCORE_LAUNCH(8); break;
-    default: QSA_SCORE_LAUNCH(16); break;
-    }
+        switch (ix.h_idx) {
+        case 1: QSA_SCORE_LAUNCH(1); break;
+        case 2: QSA_SCORE_LAUNCH(2); break;
+        case 4: QSA_SCORE_LAUNCH(4); break;
+        case 8: QSA_SCORE_LAUNCH(8); break;
+        default: QSA_SCORE_LAUNCH(16); break;
+        }
 #undef QSA_SCORE_LAUNCH
+    } else {
+        grid.y = (unsigned)((max_nb + kScoreThreads - 1) / kScoreThreads);
+        dim3 block(kScoreThreads);
+#define QSA_SCORE_LAUNCH(HH)                                                                       \
+    hipLaunchKernelGGL((score_rounded_kernel<QT, KT, D, HH>), grid, block, 0, st, q, ix.w, kc,     \
+                       ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
+                       scores, ld)
+        switch (ix.h_idx) {
+        case 1: QSA_SCORE_LAUNCH(1); break;
+        case 2: QSA_SCORE_LAUNCH(2); break;
+        case 4: QSA_SCORE_LAUNCH(4); break;
+        case 8: QSA_SCORE_LAUNCH(8); break;
+        default: QSA_SCORE_LAUNCH(16); break;
+        }
+#undef QSA_SCORE_LAUNCH
+    }
     return hipGetLastError();
 }
 
@@ -247,7 +403,7 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int64_t max_nb = b.max_kv_len >> log2r;
     if (b.total_q == 0 || max_nb == 0) return hipSuccess;
-    dim3 grid((unsigned)b.total_q, (unsigned)((max_nb + kScoreThreads - 1) / kScoreThreads));
+    dim3 grid((unsigned)b.total_q, 1);   // grid.y is set per kernel form
     trace("score_canonical grid=(%u,%u) h_idx=%d d_idx=%d q=%d kc=%d", grid.x, grid.y, ix.h_idx,
           ix.d_idx, ix.q_dtype, ix.kc_dtype);
     const bool qb = ix.q_dtype == QSA_BF16;
