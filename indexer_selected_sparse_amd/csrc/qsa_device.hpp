@@ -6,10 +6,20 @@
 // therefore the same as a rounded multiply followed by a rounded add.
 #pragma once
 
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qsa {
+
+// Compile-time loop: f(integral_constant<int, B>) ... f(integral_constant<int, E-1>).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 constexpr int kWave = 64;
 

@@ -183,15 +183,6 @@ constexpr int kExactThreads = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
-// Compile-time loop: f(integral_constant<int, B>) ... f(integral_constant<int, E-1>).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
 // One 16-byte load of this lane's key row at byte offset OFF.
 template <int OFF>
 __device__ __forceinline__ u32x4 key_load16(const void *row) {
