@@ -12,6 +12,56 @@
 
 namespace qsa {
 
+// ---- wave-wide (64-lane) scans and reductions on the DPP network.  Shuffles
+// (__shfl_*) go through ds_bpermute, an LDS round trip per step; these use
+// DPP row shifts and the row broadcasts of the gfx9 family instead, a few
+// cycles per step.  Lanes whose DPP source is outside the row (or rows not
+// selected by the row mask) receive `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp_u32<kDppRowShr1>(0u, x);
+    x += dpp_u32<kDppRowShr2>(0u, x);
+    x += dpp_u32<kDppRowShr4>(0u, x);
+    x += dpp_u32<kDppRowShr8>(0u, x);          // prefix within each row of 16
+    x += dpp_u32<kDppRowBcast15, 0xa>(0u, x);  // rows 1, 3 += last lane of rows 0, 2
+    x += dpp_u32<kDppRowBcast31, 0xc>(0u, x);  // rows 2, 3 += lane 31 (rows 0-1 total)
+    return x;
+}
+// Wave-uniform reductions (the result of lane 63, read into a scalar).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+    x = op(x, dpp_u32<kDppRowShr1>(x, x));
+    x = op(x, dpp_u32<kDppRowShr2>(x, x));
+    x = op(x, dpp_u32<kDppRowShr4>(x, x));
+    x = op(x, dpp_u32<kDppRowShr8>(x, x));
+    x = op(x, dpp_u32<kDppRowBcast15, 0xa>(x, x));
+    x = op(x, dpp_u32<kDppRowBcast31, 0xc>(x, x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+    return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+__device__ __forceinline__ float wave_min_f32(float x) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+
 // Compile-time loop: f(integral_constant<int, B>) ... f(integral_constant<int, E-1>).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {

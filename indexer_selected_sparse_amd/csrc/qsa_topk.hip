@@ -69,12 +69,7 @@ struct TopkShared {
 __device__ __forceinline__ uint32_t wg_scan(uint32_t v, TopkShared &S, uint32_t &total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_scan(v);
     if (lane == kWave - 1) S.wsum[wave] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -91,11 +86,8 @@ __device__ __forceinline__ uint32_t wg_scan(uint32_t v, TopkShared &S, uint32_t 
 
 // Workgroup min and max of uint keys.
 __device__ __forceinline__ void wg_minmax(uint32_t &mn, uint32_t &mx, TopkShared &S) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
     const int wave = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) { S.wmin[wave] = mn; S.wmax[wave] = mx; }
     __syncthreads();
@@ -795,11 +787,8 @@ __global__ __launch_bounds__(kClassifyThreads) void topk_classify_kernel(
             vmax = fmaxf(vmax, smp[u]);
         }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        vmin = fminf(vmin, __shfl_xor(vmin, o, kWave));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, o, kWave));
-    }
+    vmin = wave_min_f32(vmin);
+    vmax = wave_max_f32(vmax);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     if (lane == 0) { fred[0][wave] = vmin; fred[1][wave] = vmax; }
     __syncthreads();
@@ -840,12 +829,7 @@ __global__ __launch_bounds__(kClassifyThreads) void topk_classify_kernel(
 #pragma unroll
     for (int e = 0; e < kBpt; ++e) own += hist[top - e];
     // exclusive scan of `own` over threads (in order)
-    uint32_t incl = own;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)incl, o, kWave);
-        if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_scan(own);
     if (lane == kWave - 1) red[wave] = incl;
     __syncthreads();
     uint32_t before = 0;
@@ -934,13 +918,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(
             nd = r.cnt[1];
         }
         const bool over = __ballot(ln0 < nch && (ni > (uint32_t)K || nd > (uint32_t)kChunkCandCap)) != 0;
-        uint32_t si = ni, sd = nd;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const uint32_t yi = (uint32_t)__shfl_up((int)si, o, kWave);
-            const uint32_t yd = (uint32_t)__shfl_up((int)sd, o, kWave);
-            if (ln0 >= o) { si += yi; sd += yd; }
-        }
+        const uint32_t si = wave_incl_scan(ni), sd = wave_incl_scan(nd);
         if (ln0 < nch) { c_in[ln0] = si - ni; c_cd[ln0] = sd - nd; }
         if (ln0 == nch - 1) {
             c_in[nch] = si;
