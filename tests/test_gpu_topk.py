@@ -3,10 +3,13 @@
 Rows are fed straight to the C ABI and the selected block indices must equal
 the oracle's selection bit for bit: the K largest (score, -index) pairs in
 ascending index order, -1 padded, identity in the dense regime (nb <= K).
-Few-row batches take the multi-workgroup select (sample bracket, classify,
-finish); the cases below include rows whose bracket cannot hold (top scores
-hidden between the sampled segments, all-equal rows), which must fall back to
-the exact whole-row select, and rows with exact ties across the threshold.
+Few-row batches whose rows have at most 8192 blocks take the fused
+single-workgroup select (sample bracket, in-LDS candidate lists, exact radix
+select); longer rows take the two-kernel classify / finish select.  Every case
+runs on both: once as given and once with a 40000-block row appended.  The
+cases include rows whose bracket cannot hold (top scores hidden between the
+sampled segments, all-equal rows), which must fall back to the exact
+whole-row select, and rows with exact ties across the threshold.
 """
 import numpy as np
 import pytest
@@ -19,8 +22,20 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
+_LONG = np.random.default_rng(99).random(40000).astype(np.float32)
+
+
 def _run(rows, budget=2048, ratio=4):
-    """rows: list of 1-D float32 arrays (one per query; nb = len(row))."""
+    """rows: list of 1-D float32 arrays (one per query; nb = len(row)).  Runs
+    the batch as given, then (for few-row batches) with a 40000-block row
+    appended so that the two-kernel select handles the same rows."""
+    n = _run_once(rows, budget, ratio)
+    if len(rows) < 256 and max(len(r) for r in rows) <= 8192:
+        _run_once(list(rows) + [_LONG], budget, ratio)
+    return n
+
+
+def _run_once(rows, budget, ratio):
     import indexer_selected_sparse_amd as Q
     K = budget // ratio
     lens = [len(r) * ratio + (i % ratio) for i, r in enumerate(rows)]   # ragged tails
@@ -103,3 +118,22 @@ def test_small_budget_and_other_ratio():
     rows = [_relu_like(rng, n) for n in (70, 100, 5000, 40000)]
     _run(rows, budget=256, ratio=4)
     _run(rows, budget=2048, ratio=16)
+
+
+def test_fused_path_edge_cases():
+    # rows of at most 8192 blocks: the fused single-workgroup select (and,
+    # through _run, the two-kernel select with a long row appended)
+    rng = np.random.default_rng(7)
+    # exact ties across the threshold
+    _run([rng.integers(0, 40, n).astype(np.float32) for n in (1500, 6000, 8192)])
+    # top scores hidden between the sampled segments -> exact fallback
+    nb = 8192
+    step = (nb - 32) // 63
+    r = (rng.random(nb).astype(np.float32) * 0.5).astype(np.float32)
+    hidden = np.concatenate([np.arange(j * step + 40, j * step + 50) for j in range(63)])
+    r[hidden] = 10.0 + rng.random(len(hidden)).astype(np.float32)
+    _run([r, _relu_like(rng, 3000)])
+    # all-equal rows
+    _run([np.zeros(n, dtype=np.float32) for n in (700, 2048, 4000, 8192)] + [np.full(5000, 3.5, np.float32)])
+    # negative and mixed-sign scores
+    _run([rng.standard_normal(n).astype(np.float32) for n in (600, 4097, 8191)])
