@@ -663,27 +663,51 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    // workgroup = (query i, KV head g, part c); its 4 waves split the part
-    const int64_t wg = blockIdx.x;
-    const int g = (int)(wg % A.hkv);
-    const int64_t t2 = wg / A.hkv;
-    const int c = (int)(t2 % A.n_part);
-    const int64_t i = t2 / A.n_part;
+    // workgroup = (query i, KV head g, part c); its 4 waves split the part.
+    // 32-bit index arithmetic: the grid, K and the part sizes are below 2^31
+    // (the launcher's grid is a 32-bit count), and 64-bit division by a
+    // runtime divisor is a long dependent sequence at the head of every wave.
+    const uint32_t wg = blockIdx.x;
+    const int g = (int)(wg % (uint32_t)A.hkv);
+    const uint32_t t2 = wg / (uint32_t)A.hkv;
+    const int c = (int)(t2 % (uint32_t)A.n_part);
+    const int64_t i = (int64_t)(t2 / (uint32_t)A.n_part);
     if (i >= A.total_q) return;                      // uniform over the workgroup
+
+    // This wave's share [s_beg, s_end) of the query's nsel selected blocks.
+    auto split = [&](int nsel_, int64_t &sb, int64_t &se) {
+        const int per = (nsel_ + A.n_part - 1) / A.n_part;
+        const int p_beg = min(c * per, nsel_);
+        const int p_end = min(p_beg + per, nsel_);
+        const int sub = (p_end - p_beg + kWgWaves - 1) / kWgWaves;
+        sb = min(p_beg + wave * sub, p_end);
+        se = min((int)sb + sub, p_end);
+    };
+    // The slot table (this wave's selected block ids) is requested before
+    // the query's length is known, for the common case of a row with at least
+    // K blocks (nsel = K), so its latency overlaps that of the offsets; a
+    // shorter row loads it again below.
+    int64_t s_beg, s_end;
+    split(A.K, s_beg, s_end);
+    const int32_t *sel = A.idx + i * (int64_t)A.K + s_beg;
+    int nslot = (int)(s_end - s_beg);
+    uint32_t tab0 = (uint32_t)(lane < nslot ? sel[lane] : -1);
+    uint32_t tab1 = (uint32_t)(kWave + lane < nslot ? sel[kWave + lane] : -1);
 
     const QueryPos qp = query_pos(A.kv_off, nullptr, A.q_off, A.num_seqs, i);
     const int64_t nb = qp.L >> A.log2r;
     const int64_t nsel = nb < A.K ? nb : (int64_t)A.K;
-    const int64_t per = (nsel + A.n_part - 1) / A.n_part;
-    const int64_t p_beg = imin64((int64_t)c * per, nsel);
-    const int64_t p_end = imin64(p_beg + per, nsel);
-    const int64_t sub = (p_end - p_beg + kWgWaves - 1) / kWgWaves;
-    const int64_t s_beg = imin64(p_beg + wave * sub, p_end);
-    const int64_t s_end = imin64(s_beg + sub, p_end);
+    if (nsel < A.K) {                                // wave-uniform
+        split((int)nsel, s_beg, s_end);
+        sel = A.idx + i * (int64_t)A.K + s_beg;
+        nslot = (int)(s_end - s_beg);
+        tab0 = (uint32_t)(lane < nslot ? sel[lane] : -1);
+        tab1 = (uint32_t)(kWave + lane < nslot ? sel[kWave + lane] : -1);
+    }
     const bool owns_tail = c == A.n_part - 1 && wave == kWgWaves - 1;
     WaveWork W;
-    W.sel = A.idx + i * (int64_t)A.K + s_beg;
-    W.nslot = (int)(s_end - s_beg);
+    W.sel = sel;
+    W.nslot = nslot;
     W.log2r = A.log2r;
     W.nblk_tok = W.nslot << A.log2r;
     W.tail0 = nb << A.log2r;
@@ -700,8 +724,6 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
 
     const int nsteps = (W.ntok + kStep - 1) / kStep;
     const uint32_t ring_addr = lds_addr(ring);
-    const uint32_t tab0 = (uint32_t)(lane < W.nslot ? W.sel[lane] : -1);
-    const uint32_t tab1 = (uint32_t)(kWave + lane < W.nslot ? W.sel[kWave + lane] : -1);
     // Query rows (G x 256 contiguous bytes) travel through the last ring slot,
     // which the prologue leaves free (a compiler-visible load would make the
     // compiler wait for it, and so for the whole ring, inside the loop).  They
@@ -902,8 +924,9 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(Attn
 }
 
 // Merge part partials: one wave per (query, head); lane s < n_part reads
-// partial s's (m, l), the wave forms the weights, then every lane accumulates
-// dims 2p, 2p+1 over the partials (all partial loads issued together).
+// partial s's (m, l), the wave forms the weights (DPP reductions), then every
+// lane accumulates dims 2p, 2p+1 over the partials (all partial loads issued
+// together, so the kernel costs one memory round trip).
 constexpr int kMaxGroups = 32;
 
 template <bool BF16>
@@ -921,10 +944,10 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_combine_kernel(
         if (s < n_part) os[s] = reinterpret_cast<const float2 *>(ws_o + (r * n_part + s) * kD)[lane];
     const float m_s = lane < n_part ? ml[2 * lane] : -INFINITY;
     const float l_s = lane < n_part ? ml[2 * lane + 1] : 0.0f;
-    const float mmax = wave_max(m_s);
+    const float mmax = wave_max_f32(m_s);
     const float msafe = mmax == -INFINITY ? 0.0f : mmax;
     const float w_s = l_s > 0.0f ? exp2f(m_s - msafe) : 0.0f;
-    const float l = wave_sum(w_s * l_s);
+    const float l = wave_sum_f32(w_s * l_s);
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
     for (int s = 0; s < kMaxGroups; ++s) {

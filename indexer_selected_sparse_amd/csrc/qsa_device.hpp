@@ -56,6 +56,11 @@ __device__ __forceinline__ float wave_max_f32(float x) {
         return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
     }));
 }
+__device__ __forceinline__ float wave_sum_f32(float x) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
 __device__ __forceinline__ float wave_min_f32(float x) {
     return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
         return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
