@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches only (default: replay the step from a HIP graph)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                   help="keep K, V and the indexer caches in page pools of PAGE_SIZE tokens "
+                        "(random physical page order) and call the paged entry points")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -196,6 +199,12 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     base = pipeline.upload(wl, dev, decode=not prefill, mfma_ws=prefill)
+    if args.paged:
+        if prefill:
+            print(json.dumps({"error": "--paged runs the decode workloads (matrix-core prefill "
+                                       "scores read contiguous caches only)"}))
+            sys.exit(2)
+        base = pipeline.page(base, wl.lens, args.paged, seed=spec.seed)
 
     # compression (ingest pass), timed on its own
     base.compress()
@@ -299,7 +308,7 @@ def main():
                                else str(wl.lens[0])),
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
-                   "input_replicas": R},
+                   "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {})},
         "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn},
         "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
@@ -320,7 +329,7 @@ def main():
                                "avg_ms": t_score}
     else:
         attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
-        traffic = recorded_traffic(spec.name)
+        traffic = None if args.paged else recorded_traffic(spec.name)
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                            "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 typedef enum qsa_status {
     QSA_OK = 0,
@@ -114,7 +114,7 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio);
 
 /* Thread-local text of the last error ("" if none). Never NULL. */
 const char *qsa_last_error(void);
-/* Library version string, e.g. "qsa 0.1.0 (abi 1, gfx950)". */
+/* Library version string, e.g. "qsa 0.2.0 (abi 2, gfx950)". */
 const char *qsa_version(void);
 /* QSA_ABI_VERSION the library was built with. */
 int32_t qsa_abi_version(void);
@@ -225,6 +225,50 @@ qsa_status qsa_sparse_attn_decode(const qsa_attn *a, const int32_t *idx, int32_t
 qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_t budget,
                                    int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                    size_t ws_bytes, void *stream);
+
+/* ---- Paged caches.  The serving engines on the pages keep K/V and the
+ * indexer cache in fixed-size pages addressed through a per-sequence block
+ * table (vLLM report (a)1 and (a)6: the indexer K cache and the selection go
+ * through the paged KV layout; "Agentic shootout", vLLM vs Atlas: paged
+ * attention over the selected blocks).  Page j of sequence s holds its
+ * logical token rows j*page_size .. j*page_size + page_size - 1 and its
+ * compressed rows j*(page_size/ratio) .. ; physical page p holds pool rows
+ * p*page_size .. of K, V and k_idx, and p*(page_size/ratio) .. of kc and
+ * kc_scale.  The _paged entry points below compute exactly what their
+ * contiguous counterparts compute on the same logical rows (bit for bit: only
+ * addresses change); the batch's kv_offsets give lengths only (N_s =
+ * kv_offsets[s+1] - kv_offsets[s]) and blk_offsets is not read (may be NULL).
+ * Every page a sequence uses must be listed; other table entries are not read. */
+typedef struct qsa_paged_kv {
+    const int32_t *block_table;  /* device int32 [num_seqs, max_pages]: physical page of
+                                    each logical page, in [0, num_pages) */
+    int64_t max_pages;           /* entries per sequence row of block_table, >= ceil(N_s/page_size) */
+    int64_t num_pages;           /* physical pages in each pool */
+    int32_t page_size;           /* tokens per page: a power of two and a multiple of ratio */
+} qsa_paged_kv;
+
+/* qsa_compress_keys on paged k_idx / kc / kc_scale pools (same arithmetic).
+ * Errors: as qsa_compress_keys, plus INVALID_ARGUMENT (pg, block table, page
+ * size not a power-of-two multiple of ratio, num_pages < 1). */
+qsa_status qsa_compress_keys_paged(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                                   const qsa_batch *b, const int64_t *first_block, void *kc,
+                                   int32_t kc_dtype, float *kc_scale, const qsa_paged_kv *pg,
+                                   void *stream);
+
+/* qsa_index_score reading kc / kc_scale from pools (QSA_SCORE_CANONICAL only;
+ * QSA_SCORE_MFMA with paging returns UNSUPPORTED). */
+qsa_status qsa_index_score_paged(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b,
+                                 float *scores, int64_t ld_scores, uint32_t flags,
+                                 const qsa_paged_kv *pg, void *stream);
+
+/* qsa_sparse_attn_decode / _prefill reading K and V from pools (same
+ * workspace as the contiguous calls). */
+qsa_status qsa_sparse_attn_decode_paged(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                        int32_t ratio, const qsa_batch *b, void *out, void *ws,
+                                        size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
+qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                         int32_t ratio, const qsa_batch *b, void *out, void *ws,
+                                         size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
 
 #ifdef __cplusplus
 }

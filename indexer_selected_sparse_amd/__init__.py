@@ -30,6 +30,8 @@ EXPORTS = (
     "qsa_inert_bound", "qsa_last_error", "qsa_version", "qsa_abi_version",
     "qsa_compress_keys", "qsa_index_score", "qsa_topk_workspace_size", "qsa_topk_blocks",
     "qsa_attn_workspace_size", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
+    "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
+    "qsa_sparse_attn_prefill_paged",
 )
 
 
@@ -57,6 +59,11 @@ class _Attn(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("dtype", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class _PagedKV(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int64),
+                ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,6 +95,13 @@ def lib():
         for f in (L.qsa_sparse_attn_decode, L.qsa_sparse_attn_prefill):
             f.restype = i32
             f.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+        L.qsa_compress_keys_paged.restype = i32
+        L.qsa_compress_keys_paged.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P]
+        L.qsa_index_score_paged.restype = i32
+        L.qsa_index_score_paged.argtypes = [P, i32, P, P, i64, ctypes.c_uint32, P, P]
+        for f in (L.qsa_sparse_attn_decode_paged, L.qsa_sparse_attn_prefill_paged):
+            f.restype = i32
+            f.argtypes = [P, P, i32, i32, P, P, P, sz, P, P]
         _lib = L
     return _lib
 
@@ -165,6 +179,23 @@ class Batch:
                       None if self.q_offsets is None else self.q_offsets.data_ptr())
 
 
+@dataclass
+class Paging:
+    """Paged caches (C qsa_paged_kv): page j of sequence s is physical page
+    block_table[s, j]; every pool holds num_pages pages (page_size token rows
+    of K, V, k_idx; page_size/ratio rows of kc, kc_scale)."""
+    block_table: torch.Tensor           # device int32 [num_seqs, max_pages]
+    num_pages: int
+    page_size: int
+
+    def _c(self) -> _PagedKV:
+        _dev(self.block_table, "block_table")
+        if self.block_table.dtype != torch.int32 or self.block_table.dim() != 2:
+            raise TypeError("block_table must be a 2-D int32 tensor")
+        return _PagedKV(self.block_table.data_ptr(), self.block_table.shape[1], int(self.num_pages),
+                        int(self.page_size))
+
+
 # -------------------------------------------------------------- functions
 def inert_bound(budget: int, ratio: int) -> int:
     return int(lib().qsa_inert_bound(budget, ratio))
@@ -176,15 +207,22 @@ def version() -> str:
 
 def compress_keys(k_idx: torch.Tensor, ratio: int, batch: Batch, kc: torch.Tensor,
                   kc_scale: Optional[torch.Tensor] = None, first_block: Optional[torch.Tensor] = None,
-                  stream=None) -> None:
-    """qsa_compress_keys: writes kc (f32, bf16, or uint8 e4m3 codes) [+ kc_scale]."""
+                  stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_compress_keys (qsa_compress_keys_paged with `paging`): writes kc (f32,
+    bf16, or uint8 e4m3 codes) [+ kc_scale]."""
     _dev(k_idx, "k_idx")
     _dev(kc, "kc")
     kcd = QSA_FP8_E4M3 if kc.dtype == torch.uint8 else _dtype_code(kc)
     b = batch._c()
-    _check(lib().qsa_compress_keys(_ptr(k_idx), _dtype_code(k_idx), k_idx.shape[-1], ratio,
-                                   ctypes.byref(b), _ptr(first_block), _ptr(kc), kcd,
-                                   _ptr(kc_scale), _stream(stream)))
+    if paging is None:
+        _check(lib().qsa_compress_keys(_ptr(k_idx), _dtype_code(k_idx), k_idx.shape[-1], ratio,
+                                       ctypes.byref(b), _ptr(first_block), _ptr(kc), kcd,
+                                       _ptr(kc_scale), _stream(stream)))
+    else:
+        pg = paging._c()
+        _check(lib().qsa_compress_keys_paged(_ptr(k_idx), _dtype_code(k_idx), k_idx.shape[-1], ratio,
+                                             ctypes.byref(b), _ptr(first_block), _ptr(kc), kcd,
+                                             _ptr(kc_scale), ctypes.byref(pg), _stream(stream)))
 
 
 def _indexer(q_idx, w, kc, kc_scale) -> _Indexer:
@@ -199,13 +237,18 @@ def _indexer(q_idx, w, kc, kc_scale) -> _Indexer:
 
 
 def index_score(q_idx, w, kc, kc_scale, ratio: int, batch: Batch, scores: torch.Tensor,
-                mode: int = QSA_SCORE_CANONICAL, stream=None) -> None:
-    """qsa_index_score into scores [total_q, ld]."""
+                mode: int = QSA_SCORE_CANONICAL, stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_index_score (qsa_index_score_paged with `paging`) into scores [total_q, ld]."""
     _dev(scores, "scores")
     ix = _indexer(q_idx, w, kc, kc_scale)
     b = batch._c()
-    _check(lib().qsa_index_score(ctypes.byref(ix), ratio, ctypes.byref(b), _ptr(scores),
-                                 scores.shape[1], mode, _stream(stream)))
+    if paging is None:
+        _check(lib().qsa_index_score(ctypes.byref(ix), ratio, ctypes.byref(b), _ptr(scores),
+                                     scores.shape[1], mode, _stream(stream)))
+    else:
+        pg = paging._c()
+        _check(lib().qsa_index_score_paged(ctypes.byref(ix), ratio, ctypes.byref(b), _ptr(scores),
+                                           scores.shape[1], mode, ctypes.byref(pg), _stream(stream)))
 
 
 def topk_workspace_size(batch: Batch, budget: int, ratio: int, recheck=None) -> int:
@@ -243,22 +286,33 @@ def attn_workspace_size(q, k, v, softmax_scale, budget: int, ratio: int, batch: 
     return int(lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), budget, ratio))
 
 
-def _attn_call(fn, q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws, stream):
+def _attn_call(fn, fn_paged, q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws, stream,
+               paging):
     _dev(idx, "idx")
     _dev(out, "out")
     a = _attn(q, k, v, softmax_scale)
     b = batch._c()
-    _check(fn(ctypes.byref(a), _ptr(idx), budget, ratio, ctypes.byref(b), _ptr(out), _ptr(ws),
-              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if paging is None:
+        _check(fn(ctypes.byref(a), _ptr(idx), budget, ratio, ctypes.byref(b), _ptr(out), _ptr(ws),
+                  nbytes, _stream(stream)))
+    else:
+        pg = paging._c()
+        _check(fn_paged(ctypes.byref(a), _ptr(idx), budget, ratio, ctypes.byref(b), _ptr(out),
+                        _ptr(ws), nbytes, ctypes.byref(pg), _stream(stream)))
 
 
 def sparse_attn_decode(q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws=None,
-                       stream=None) -> None:
-    _attn_call(lib().qsa_sparse_attn_decode, q, k, v, softmax_scale, idx, budget, ratio, batch,
-               out, ws, stream)
+                       stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_sparse_attn_decode (qsa_sparse_attn_decode_paged with `paging`: k, v are pools)."""
+    L = lib()
+    _attn_call(L.qsa_sparse_attn_decode, L.qsa_sparse_attn_decode_paged, q, k, v, softmax_scale, idx,
+               budget, ratio, batch, out, ws, stream, paging)
 
 
 def sparse_attn_prefill(q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws=None,
-                        stream=None) -> None:
-    _attn_call(lib().qsa_sparse_attn_prefill, q, k, v, softmax_scale, idx, budget, ratio, batch,
-               out, ws, stream)
+                        stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_sparse_attn_prefill (qsa_sparse_attn_prefill_paged with `paging`: k, v are pools)."""
+    L = lib()
+    _attn_call(L.qsa_sparse_attn_prefill, L.qsa_sparse_attn_prefill_paged, q, k, v, softmax_scale,
+               idx, budget, ratio, batch, out, ws, stream, paging)

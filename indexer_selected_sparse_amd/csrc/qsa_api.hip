@@ -141,11 +141,32 @@ static qsa_status check_attn(const qsa_attn *a) {
     return ok();
 }
 
+// Paged caches: the descriptor and the batch it must cover.  Pool rows stay
+// below 2^31 (the kernels index rows with 32-bit integers).
+static qsa_status check_paging(const qsa_paged_kv *pg, const qsa_batch *b, int32_t ratio) {
+    if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
+    if (!pg->block_table) return fail(QSA_ERR_INVALID_ARGUMENT, "paging.block_table is NULL");
+    if (!is_pow2(pg->page_size) || pg->page_size < ratio)
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "paging.page_size=%d must be a power of two and a multiple of ratio=%d", pg->page_size, ratio);
+    if (pg->num_pages < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "paging.num_pages=%lld must be >= 1",
+                                       (long long)pg->num_pages);
+    if (pg->num_pages > (0x7fffffffLL / pg->page_size))
+        return fail(QSA_ERR_UNSUPPORTED, "paging: num_pages*page_size=%lld exceeds 2^31-1 pool rows",
+                    (long long)(pg->num_pages * pg->page_size));
+    const int64_t need = (b->max_kv_len + pg->page_size - 1) / pg->page_size;
+    if (pg->max_pages < need || pg->max_pages < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "paging.max_pages=%lld must be >= ceil(max_kv_len/page_size)=%lld",
+                    (long long)pg->max_pages, (long long)need);
+    return ok();
+}
+
 static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
                               const qsa_batch *b, void *out, void *ws, size_t ws_bytes, bool decode,
-                              hipStream_t st) {
+                              const qsa_paged_kv *pg, hipStream_t st) {
     qsa_status s = check_attn(a);
     if (s == QSA_OK) s = check_batch(b, false);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
     if (s == QSA_OK) s = check_budget(budget, ratio);
     if (s != QSA_OK) return s;
     if (!idx) return fail(QSA_ERR_INVALID_ARGUMENT, "idx is NULL");
@@ -158,7 +179,7 @@ static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t bud
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_attn_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
-    return hip_status(launch_attn(*a, idx, budget, ratio, *b, out, ws, decode, st),
+    return hip_status(launch_attn(*a, idx, budget, ratio, *b, out, ws, decode, pg, st),
                       "sparse attention launch");
 }
 
@@ -175,14 +196,16 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio) {
 
 const char *qsa_last_error(void) { return g_err; }
 
-const char *qsa_version(void) { return "qsa 0.1.0 (abi 1, gfx950)"; }
+const char *qsa_version(void) { return "qsa 0.2.0 (abi 2, gfx950)"; }
 
 int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
-qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
-                             const qsa_batch *b, const int64_t *first_block, void *kc,
-                             int32_t kc_dtype, float *kc_scale, void *stream) {
-    qsa_status s = check_batch(b, true);
+static qsa_status compress_common(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                                  const qsa_batch *b, const int64_t *first_block, void *kc,
+                                  int32_t kc_dtype, float *kc_scale, const qsa_paged_kv *pg,
+                                  void *stream) {
+    qsa_status s = check_batch(b, pg == nullptr);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
     if (s != QSA_OK) return s;
     if (!k_idx) return fail(QSA_ERR_INVALID_ARGUMENT, "k_idx is NULL");
     if (!kc) return fail(QSA_ERR_INVALID_ARGUMENT, "kc is NULL");
@@ -198,17 +221,36 @@ qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, 
     if ((b->max_kv_len / ratio) > 0xffffffffLL * 16)
         return fail(QSA_ERR_UNSUPPORTED, "max_kv_len=%lld is too large", (long long)b->max_kv_len);
     return hip_status(launch_compress(k_idx, k_dtype, d_idx, ratio, *b, first_block, kc, kc_dtype,
-                                      kc_scale, (hipStream_t)stream),
+                                      kc_scale, pg, (hipStream_t)stream),
                       "qsa_compress_keys launch");
 }
 
-qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b, float *scores,
-                           int64_t ld_scores, uint32_t flags, void *stream) {
+qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                             const qsa_batch *b, const int64_t *first_block, void *kc,
+                             int32_t kc_dtype, float *kc_scale, void *stream) {
+    return compress_common(k_idx, k_dtype, d_idx, ratio, b, first_block, kc, kc_dtype, kc_scale,
+                           nullptr, stream);
+}
+
+qsa_status qsa_compress_keys_paged(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                                   const qsa_batch *b, const int64_t *first_block, void *kc,
+                                   int32_t kc_dtype, float *kc_scale, const qsa_paged_kv *pg,
+                                   void *stream) {
+    if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
+    return compress_common(k_idx, k_dtype, d_idx, ratio, b, first_block, kc, kc_dtype, kc_scale, pg,
+                           stream);
+}
+
+static qsa_status score_common(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b, float *scores,
+                               int64_t ld_scores, uint32_t flags, const qsa_paged_kv *pg, void *stream) {
     if (flags != QSA_SCORE_CANONICAL && flags != QSA_SCORE_MFMA)
         return fail(QSA_ERR_INVALID_ARGUMENT, "flags=%u must be QSA_SCORE_CANONICAL or QSA_SCORE_MFMA", flags);
     const bool mfma = flags == QSA_SCORE_MFMA;
+    if (mfma && pg)
+        return fail(QSA_ERR_UNSUPPORTED, "QSA_SCORE_MFMA does not read paged caches; use QSA_SCORE_CANONICAL");
     qsa_status s = check_indexer(ix, mfma);
-    if (s == QSA_OK) s = check_batch(b, true);
+    if (s == QSA_OK) s = check_batch(b, pg == nullptr);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
     if (s == QSA_OK) s = check_ratio(ratio);
     if (s == QSA_OK) s = check_rows(b, ratio);
     if (s != QSA_OK) return s;
@@ -218,8 +260,19 @@ qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch
         return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
                     (long long)ld_scores, (long long)need_ld);
     hipError_t e = mfma ? launch_score_mfma(*ix, ratio, *b, scores, ld_scores, (hipStream_t)stream)
-                        : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, (hipStream_t)stream);
+                        : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, pg, (hipStream_t)stream);
     return hip_status(e, "qsa_index_score launch");
+}
+
+qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b, float *scores,
+                           int64_t ld_scores, uint32_t flags, void *stream) {
+    return score_common(ix, ratio, b, scores, ld_scores, flags, nullptr, stream);
+}
+
+qsa_status qsa_index_score_paged(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b, float *scores,
+                                 int64_t ld_scores, uint32_t flags, const qsa_paged_kv *pg, void *stream) {
+    if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
+    return score_common(ix, ratio, b, scores, ld_scores, flags, pg, stream);
 }
 
 size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio,
@@ -262,12 +315,26 @@ size_t qsa_attn_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t bu
 
 qsa_status qsa_sparse_attn_decode(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
                                   const qsa_batch *b, void *out, void *ws, size_t ws_bytes, void *stream) {
-    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, true, (hipStream_t)stream);
+    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, true, nullptr, (hipStream_t)stream);
 }
 
 qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
                                    const qsa_batch *b, void *out, void *ws, size_t ws_bytes, void *stream) {
-    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, false, (hipStream_t)stream);
+    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, false, nullptr, (hipStream_t)stream);
+}
+
+qsa_status qsa_sparse_attn_decode_paged(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                        int32_t ratio, const qsa_batch *b, void *out, void *ws,
+                                        size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {
+    if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
+    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, true, pg, (hipStream_t)stream);
+}
+
+qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                         int32_t ratio, const qsa_batch *b, void *out, void *ws,
+                                         size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {
+    if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
+    return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, false, pg, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -57,6 +57,7 @@ struct AttnArgs {
     void *out;
     float *ws_o;             // [total_q, hq, n_part, D]
     float *ws_ml;            // [total_q, hq, n_part, 2]
+    PageMap pm;              // paged K/V pools (pm.table == nullptr: contiguous)
 };
 
 template <int G>
@@ -193,6 +194,22 @@ struct WaveWork {
     int64_t nb;                       // complete blocks visible to the query
     int log2r;
 };
+
+// A selected block id as the table holds it for the kernels: with paged K/V
+// the physical block of the pool (a page holds whole blocks), -1 for an id
+// outside [0, nb) (which the kernels then treat as "no token").
+__device__ __forceinline__ int slot_phys(int b, const PageMap &pm, int64_t seq, int64_t nb, int log2r) {
+    if (pm.table == nullptr) return b;
+    if (b < 0 || (int64_t)b >= nb) return -1;
+    return (int)paged_row(pm, seq, b, pm.log2_page - log2r);
+}
+// Paged pools: the tail's first pool row, and no logical bound on block ids
+// (they were checked when translated).
+__device__ __forceinline__ void page_wave(WaveWork &W, const PageMap &pm, int64_t seq, int64_t L) {
+    if (pm.table == nullptr) return;
+    W.tail0 = L > W.tail0 ? paged_row(pm, seq, W.tail0, pm.log2_page) : 0;
+    W.nb = int64_t(1) << 62;
+}
 
 // Issue the loads of step `st`.  Lane t < 16 resolves token 16*st+t to a row
 // of the sequence (a selected block id from the slot table, one slot per
@@ -399,13 +416,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs &A) {
     W.tail0 = nb << A.log2r;
     W.nb = nb;
     W.ntok = W.nblk_tok + ((c == A.n_part - 1) ? (int)(qp.L - W.tail0) : 0);
+    page_wave(W, A.pm, qp.seq, qp.L);
+    const int64_t row0 = A.pm.table ? 0 : qp.kv_row0;     // rows are pool rows when paged
 
     const int tk = lane >> 3, ds = lane & 7;
     const int hb = head_base<G>(ds);
     const int qh0 = g * G;                          // first query head of this KV head
     const int64_t row_stride = (int64_t)A.hkv * kD; // elements between consecutive tokens
-    const T *__restrict__ kbase = static_cast<const T *>(A.k) + (qp.kv_row0 * A.hkv + g) * kD;
-    const T *__restrict__ vbase = static_cast<const T *>(A.v) + (qp.kv_row0 * A.hkv + g) * kD;
+    const T *__restrict__ kbase = static_cast<const T *>(A.k) + (row0 * A.hkv + g) * kD;
+    const T *__restrict__ vbase = static_cast<const T *>(A.v) + (row0 * A.hkv + g) * kD;
 
     // query slices for the QK mapping (kept in registers for the whole part)
     QSlices<BF16, G> Q;
@@ -432,14 +451,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs &A) {
 
     // Slot table: lane j holds selected block id of slot tab_base + j.
     int tab_base = 0;
-    uint32_t slot_tab = (uint32_t)(lane < W.nslot ? W.sel[lane] : -1);
+    uint32_t slot_tab = (uint32_t)slot_phys(lane < W.nslot ? W.sel[lane] : -1, A.pm, qp.seq, nb, A.log2r);
     const int nsteps = (W.ntok + kStep - 1) / kStep;
     auto ensure_table = [&](int st) {
         const int first = (st * kStep) >> W.log2r;
         const int last = (st * kStep + kStep - 1) >> W.log2r;
         if (st * kStep < W.nblk_tok && (first < tab_base || last >= tab_base + kWave)) {
             tab_base = first;
-            slot_tab = (uint32_t)(tab_base + lane < W.nslot ? W.sel[tab_base + lane] : -1);
+            slot_tab = (uint32_t)slot_phys(tab_base + lane < W.nslot ? W.sel[tab_base + lane] : -1, A.pm,
+                                           qp.seq, nb, A.log2r);
         }
     };
 
@@ -572,7 +592,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // selected block id giving rows b*ratio.., a tail position giving itself;
 // malformed ids and positions past the end give "no token" and read row 0.
 // Lanes 0..15 end up holding the rows of tokens 0..15.  Row byte offsets are
-// 32-bit (the launcher checks that a sequence's K rows span less than 4 GiB).  Load j covers tokens
+// 32-bit (the launcher checks that a sequence's K rows, or the pool's with paged K/V, span less
+// than 4 GiB).  Load j covers tokens
 // 4j..4j+3: lane l fills LDS bytes l*16.. of the j-th kilobyte (the hardware
 // places lane l's 16 bytes at l*16), i.e. position p = l%16 of token
 // t = 4j + l/16.  Position p of token t holds the row's 16-byte chunk p ^ t
@@ -713,13 +734,19 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     W.tail0 = nb << A.log2r;
     W.nb = nb;
     W.ntok = W.nblk_tok + (owns_tail ? (int)(qp.L - W.tail0) : 0);
+    if (A.pm.table) {                                // paged pools: physical block ids and rows
+        page_wave(W, A.pm, qp.seq, qp.L);
+        tab0 = (uint32_t)slot_phys((int)tab0, A.pm, qp.seq, nb, A.log2r);
+        tab1 = (uint32_t)slot_phys((int)tab1, A.pm, qp.seq, nb, A.log2r);
+    }
+    const int64_t row0 = A.pm.table ? 0 : qp.kv_row0;
 
     const int n = lane & 15;                        // head column of this lane
     const int gq = lane >> 4;                       // 16-lane group
     const int qh0 = g * G;
     const uint32_t row_bytes = (uint32_t)A.hkv * kD * 2;
-    const uint16_t *__restrict__ kbase = static_cast<const uint16_t *>(A.k) + (qp.kv_row0 * A.hkv + g) * kD;
-    const uint16_t *__restrict__ vbase = static_cast<const uint16_t *>(A.v) + (qp.kv_row0 * A.hkv + g) * kD;
+    const uint16_t *__restrict__ kbase = static_cast<const uint16_t *>(A.k) + (row0 * A.hkv + g) * kD;
+    const uint16_t *__restrict__ vbase = static_cast<const uint16_t *>(A.v) + (row0 * A.hkv + g) * kD;
     uint8_t *ring = dyn_lds + wave * (D * kSlotBytes);
 
     const int nsteps = (W.ntok + kStep - 1) / kStep;
@@ -1081,7 +1108,8 @@ size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, i
 }
 
 hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ratio,
-                       const qsa_batch &b, void *out, void *ws, bool decode, hipStream_t st) {
+                       const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
+                       hipStream_t st) {
     if (b.total_q == 0) return hipSuccess;
     AttnArgs A;
     A.q = a.q; A.k = a.k; A.v = a.v; A.idx = idx;
@@ -1090,8 +1118,11 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     A.log2r = __builtin_ctz((unsigned)ratio);
     A.K = budget / ratio;
     // The matrix-core decode kernel addresses a sequence's K/V rows with
-    // 32-bit byte offsets; longer sequences take the register-staged kernel.
-    const bool rows32 = (uint64_t)b.max_kv_len * (uint64_t)a.hkv * kD * 2 < (1ull << 32);
+    // 32-bit byte offsets; longer sequences (larger pools) take the register-staged kernel.
+    // With paged K/V the offsets address the whole pool.
+    const uint64_t span_rows = pg ? (uint64_t)pg->num_pages * (uint64_t)pg->page_size : (uint64_t)b.max_kv_len;
+    const bool rows32 = span_rows * (uint64_t)a.hkv * kD * 2 < (1ull << 32);
+    A.pm = page_map(pg);
     // bf16 decode and prefill both run on the matrix-core kernel; prefill
     // keeps one part per (query, KV head), so its result never depends on
     // the rest of the batch (chunked prefill equals single-shot bit for bit).

@@ -47,7 +47,7 @@ template <typename TIn, int DPL, int KC>
 __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const TIn *__restrict__ k_idx, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ first_block, int log2_ratio,
-    float inv_ratio, void *__restrict__ kc, float *__restrict__ kc_scale) {
+    float inv_ratio, void *__restrict__ kc, float *__restrict__ kc_scale, PageMap pm) {
     constexpr int D = DPL * kWave;
     const int s = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -56,14 +56,18 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const int64_t row0 = kv_off[s];
     const int64_t nb = (kv_off[s + 1] - row0) >> log2_ratio;
     const int64_t fb = first_block ? first_block[s] : 0;
-    const int64_t out0 = blk_off[s];
+    const int64_t out0 = pm.table ? 0 : blk_off[s];
     const int64_t b_base =
         ((int64_t)blockIdx.x * kCompressWaves + wave) * kBlocksPerWave;
 
     for (int u = 0; u < kBlocksPerWave; ++u) {
         const int64_t b = b_base + u;
         if (b >= nb || b < fb) continue;
-        const TIn *src = k_idx + (row0 + (b << log2_ratio)) * D + lane * DPL;
+        // the block's first token row (a page holds whole blocks) and its output row
+        const int64_t in_row = pm.table ? paged_row(pm, s, b << log2_ratio, pm.log2_page)
+                                        : row0 + (b << log2_ratio);
+        const int64_t out_row = pm.table ? paged_row(pm, s, b, pm.log2_page - log2_ratio) : out0 + b;
+        const TIn *src = k_idx + in_row * D + lane * DPL;
         float acc[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
         float m[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) m[e] = acc[e] * inv_ratio;
-        const int64_t o = (out0 + b) * D + lane * DPL;
+        const int64_t o = out_row * D + lane * DPL;
         if constexpr (KC == 0) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e) static_cast<float *>(kc)[o + e] = m[e];
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
             for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(m[e]));
             amax = wave_max(amax);
             const float scale = amax / 448.0f;    // correctly rounded division
-            if (lane == 0) kc_scale[out0 + b] = scale;
+            if (lane == 0) kc_scale[out_row] = scale;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) {
                 uint32_t c = 0;
@@ -107,22 +111,23 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
 
 template <typename TIn, int DPL>
 hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb, int log2r,
-                       void *kc, int kc_dtype, float *kc_scale, dim3 grid, hipStream_t st) {
+                       void *kc, int kc_dtype, float *kc_scale, const PageMap &pm, dim3 grid,
+                       hipStream_t st) {
     const float inv = 1.0f / (float)(1 << log2r);
     const TIn *x = static_cast<const TIn *>(k_idx);
     dim3 block(kCompressWaves * kWave);
     switch (kc_dtype) {
     case QSA_F32:
         hipLaunchKernelGGL((compress_kernel<TIn, DPL, 0>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale);
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
         break;
     case QSA_BF16:
         hipLaunchKernelGGL((compress_kernel<TIn, DPL, 1>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale);
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
         break;
     default:
         hipLaunchKernelGGL((compress_kernel<TIn, DPL, 2>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale);
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
         break;
     }
     return hipGetLastError();
@@ -132,7 +137,8 @@ hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb,
 
 hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
                            const int64_t *first_block, void *kc, int kc_dtype, float *kc_scale,
-                           hipStream_t st) {
+                           const qsa_paged_kv *pg, hipStream_t st) {
+    const PageMap pm = page_map(pg);
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int64_t max_nb = b.max_kv_len >> log2r;
     const int64_t per_wg = (int64_t)kCompressWaves * kBlocksPerWave;
@@ -142,10 +148,10 @@ hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio,
           ratio, k_dtype, kc_dtype);
     const bool bf = (k_dtype == QSA_BF16);
     if (d_idx == 64)
-        return bf ? dispatch_kc<uint16_t, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st)
-                  : dispatch_kc<float, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st);
-    return bf ? dispatch_kc<uint16_t, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st)
-              : dispatch_kc<float, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, grid, st);
+        return bf ? dispatch_kc<uint16_t, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
+                  : dispatch_kc<float, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
+    return bf ? dispatch_kc<uint16_t, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
+              : dispatch_kc<float, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
 }
 
 }  // namespace qsa

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qsa.h"
+
 namespace qsa {
 
 // ---- wave-wide (64-lane) scans and reductions on the DPP network.  Shuffles
@@ -65,6 +67,29 @@ __device__ __forceinline__ float wave_min_f32(float x) {
     return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
         return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
     }));
+}
+
+// Paged caches: logical row t of sequence s lives in pool row
+// table[s * stride + (t >> log2_rows)] << log2_rows | (t & (2^log2_rows - 1)),
+// where 2^log2_rows rows make a page (token rows: page_size; compressed rows:
+// page_size / ratio).  table == nullptr: the contiguous layout (no paging).
+struct PageMap {
+    const int32_t *table;
+    int64_t stride;
+    int log2_page;           // token rows per page
+};
+inline PageMap page_map(const qsa_paged_kv *pg) {
+    PageMap m{nullptr, 0, 0};
+    if (pg) {
+        m.table = pg->block_table;
+        m.stride = pg->max_pages;
+        m.log2_page = __builtin_ctz((unsigned)pg->page_size);
+    }
+    return m;
+}
+__device__ __forceinline__ int64_t paged_row(const PageMap &pm, int64_t seq, int64_t t, int log2_rows) {
+    const int64_t page = pm.table[seq * pm.stride + (t >> log2_rows)];
+    return (page << log2_rows) | (t & ((int64_t(1) << log2_rows) - 1));
 }
 
 // Compile-time loop: f(integral_constant<int, B>) ... f(integral_constant<int, E-1>).

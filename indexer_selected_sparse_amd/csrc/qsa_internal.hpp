@@ -11,14 +11,17 @@
 
 namespace qsa {
 
+// Paged pools (pg != nullptr) or the contiguous layout (pg == nullptr) for the
+// launchers that take `pg`.
+
 // Key compression (mean-pool of complete blocks).
 hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
                            const int64_t *first_block, void *kc, int kc_dtype, float *kc_scale,
-                           hipStream_t st);
+                           const qsa_paged_kv *pg, hipStream_t st);
 
 // Canonical (bit-defined) indexer scores, decode and prefill.
 hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
-                                  float *scores, int64_t ld, hipStream_t st);
+                                  float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st);
 
 // Matrix-core indexer scores (bf16 only), prefill.
 hipError_t launch_score_mfma(const qsa_indexer &ix, int ratio, const qsa_batch &b, float *scores,
@@ -36,7 +39,8 @@ int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio
 // Workspace of the decode entry point (prefill needs none).
 size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio);
 hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ratio,
-                       const qsa_batch &b, void *out, void *ws, bool decode, hipStream_t st);
+                       const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
+                       hipStream_t st);
 
 // Host tracing (QSA_TRACE=1): one line per launch on stderr.
 bool trace_enabled();

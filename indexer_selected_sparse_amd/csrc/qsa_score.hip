@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
     const QT *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const float *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld) {
+    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
     const int64_t b = (int64_t)blockIdx.y * kScoreThreads + threadIdx.x;
     if ((int64_t)blockIdx.y * kScoreThreads >= nb) return;   // whole workgroup invisible
     const bool active = b < nb;
-    const int64_t row = qp.blk_row0 + (active ? b : 0);
+    const int64_t row = pm.table ? paged_row(pm, qp.seq, active ? b : 0, pm.log2_page - log2r)
+                                 : qp.blk_row0 + (active ? b : 0);
 
     const float sc = kE4M3 ? kc_scale[row] : 1.0f;
     const float *__restrict__ wi = w + i * (int64_t)H;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const float *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld) {
+    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     constexpr int CH = kExactChunk;
     constexpr int NCH = D / CH;
@@ -277,7 +278,8 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     const int64_t b = (int64_t)blockIdx.y * kExactThreads + threadIdx.x;
     if ((int64_t)blockIdx.y * kExactThreads >= nb) return;   // whole workgroup invisible
     const bool active = b < nb;
-    const int64_t row = qp.blk_row0 + (active ? b : 0);
+    const int64_t row = pm.table ? paged_row(pm, qp.seq, active ? b : 0, pm.log2_page - log2r)
+                                 : qp.blk_row0 + (active ? b : 0);
     const float sc = kE4M3 ? kc_scale[row] : 1.0f;
     const KT *krow = kc + row * D;
     const uint32_t *q32 = reinterpret_cast<const uint32_t *>(q_idx) + i * (int64_t)(H * D / 2);
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
 
 template <typename QT, typename KT, int D>
 hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, float *scores,
-                      int64_t ld, dim3 grid, hipStream_t st) {
+                      int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st) {
     const QT *q = static_cast<const QT *>(ix.q_idx);
     const KT *kc = static_cast<const KT *>(ix.kc);
     constexpr bool kExact = std::is_same<QT, uint16_t>::value && !std::is_same<KT, float>::value;
@@ -352,7 +354,7 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 #define QSA_SCORE_LAUNCH(HH)                                                                       \
     hipLaunchKernelGGL((score_exact_kernel<KT, D, HH>), grid, block, 0, st, q, ix.w, kc,           \
                        ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
-                       scores, ld)
+                       scores, ld, pm)
         switch (ix.h_idx) {
         case 1: QSA_SCORE_LAUNCH(1); break;
         case 2: QSA_SCORE_LAUNCH(2); break;
@@ -367,7 +369,7 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 #define QSA_SCORE_LAUNCH(HH)                                                                       \
     hipLaunchKernelGGL((score_rounded_kernel<QT, KT, D, HH>), grid, block, 0, st, q, ix.w, kc,     \
                        ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
-                       scores, ld)
+                       scores, ld, pm)
         switch (ix.h_idx) {
         case 1: QSA_SCORE_LAUNCH(1); break;
         case 2: QSA_SCORE_LAUNCH(2); break;
@@ -382,15 +384,16 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 
 template <typename QT, typename KT>
 hipError_t dispatch_d(const qsa_indexer &ix, int log2r, const qsa_batch &b, float *scores,
-                      int64_t ld, dim3 grid, hipStream_t st) {
-    return ix.d_idx == 64 ? dispatch_h<QT, KT, 64>(ix, log2r, b, scores, ld, grid, st)
-                          : dispatch_h<QT, KT, 128>(ix, log2r, b, scores, ld, grid, st);
+                      int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st) {
+    return ix.d_idx == 64 ? dispatch_h<QT, KT, 64>(ix, log2r, b, scores, ld, pm, grid, st)
+                          : dispatch_h<QT, KT, 128>(ix, log2r, b, scores, ld, pm, grid, st);
 }
 
 }  // namespace
 
 hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
-                                  float *scores, int64_t ld, hipStream_t st) {
+                                  float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st) {
+    const PageMap pm = page_map(pg);
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int64_t max_nb = b.max_kv_len >> log2r;
     if (b.total_q == 0 || max_nb == 0) return hipSuccess;
@@ -400,14 +403,14 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
     const bool qb = ix.q_dtype == QSA_BF16;
     switch (ix.kc_dtype) {
     case QSA_F32:
-        return qb ? dispatch_d<uint16_t, float>(ix, log2r, b, scores, ld, grid, st)
-                  : dispatch_d<float, float>(ix, log2r, b, scores, ld, grid, st);
+        return qb ? dispatch_d<uint16_t, float>(ix, log2r, b, scores, ld, pm, grid, st)
+                  : dispatch_d<float, float>(ix, log2r, b, scores, ld, pm, grid, st);
     case QSA_BF16:
-        return qb ? dispatch_d<uint16_t, uint16_t>(ix, log2r, b, scores, ld, grid, st)
-                  : dispatch_d<float, uint16_t>(ix, log2r, b, scores, ld, grid, st);
+        return qb ? dispatch_d<uint16_t, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st)
+                  : dispatch_d<float, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st);
     default:
-        return qb ? dispatch_d<uint16_t, uint8_t>(ix, log2r, b, scores, ld, grid, st)
-                  : dispatch_d<float, uint8_t>(ix, log2r, b, scores, ld, grid, st);
+        return qb ? dispatch_d<uint16_t, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st)
+                  : dispatch_d<float, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st);
     }
 }
 

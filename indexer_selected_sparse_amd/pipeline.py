@@ -11,8 +11,10 @@ from typing import Optional
 
 import torch
 
-from . import (QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch, attn_workspace_size, compress_keys,
-               index_score, sparse_attn_decode, sparse_attn_prefill, topk_blocks,
+import numpy as np
+
+from . import (QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch, Paging, attn_workspace_size,
+               compress_keys, index_score, sparse_attn_decode, sparse_attn_prefill, topk_blocks,
                topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}
@@ -39,17 +41,19 @@ class DeviceProblem:
     topk_ws: Optional[torch.Tensor]        # certified (matrix-core scores) selection
     topk_ws_canon: Optional[torch.Tensor]  # selection from canonical scores
     decode: bool
+    paging: Optional[Paging] = None        # K, V, k_idx, kc (+ scale) are page pools
 
     @property
     def blocks_per_query(self) -> int:
         return self.budget // self.ratio
 
     def compress(self, stream=None) -> None:
-        compress_keys(self.k_idx, self.ratio, self.batch, self.kc, self.kc_scale, stream=stream)
+        compress_keys(self.k_idx, self.ratio, self.batch, self.kc, self.kc_scale, stream=stream,
+                      paging=self.paging)
 
     def score(self, mode: int = QSA_SCORE_CANONICAL, stream=None) -> None:
         index_score(self.q_idx, self.w, self.kc, self.kc_scale, self.ratio, self.batch, self.scores,
-                    mode=mode, stream=stream)
+                    mode=mode, stream=stream, paging=self.paging)
 
     def topk(self, certified: bool = False, stream=None) -> None:
         recheck = (self.q_idx, self.w, self.kc, self.kc_scale) if certified else None
@@ -59,7 +63,7 @@ class DeviceProblem:
     def attend(self, stream=None) -> None:
         fn = sparse_attn_decode if self.decode else sparse_attn_prefill
         fn(self.q, self.K, self.V, self.softmax_scale, self.idx, self.budget, self.ratio,
-           self.batch, self.out, self.attn_ws, stream=stream)
+           self.batch, self.out, self.attn_ws, stream=stream, paging=self.paging)
 
     def step(self, mfma: bool = False, stream=None) -> None:
         """One pass of the hot path: score -> top-k -> sparse attention."""
@@ -105,3 +109,43 @@ def upload(wl, device: str = "cuda", decode: Optional[bool] = None, mfma_ws: boo
         if tws:
             dp.topk_ws = torch.empty(tws, dtype=torch.uint8, device=device)
     return dp
+
+
+def page(dp: DeviceProblem, lens, page_size: int, seed: int = 0, extra_pages: int = 0) -> DeviceProblem:
+    """A copy of `dp` whose K, V, k_idx and compressed keys live in page pools:
+    the pages of every sequence at random physical pages (seeded), plus
+    `extra_pages` unused pages.  `lens` are the sequences' token counts; the
+    compressed keys are copied from dp.kc, so compress `dp` first (or call
+    compress() on the result)."""
+    P, r = int(page_size), dp.ratio
+    lens = [int(n) for n in lens]
+    npg = [(n + P - 1) // P for n in lens]
+    num_pages = sum(npg) + int(extra_pages)
+    rng = np.random.default_rng(seed)
+    phys = rng.permutation(num_pages)[:sum(npg)]
+    table = np.zeros((len(lens), max(1, max(npg))), dtype=np.int32)
+    tok_rows, blk_rows, u = [], [], 0
+    for s_, (n, m) in enumerate(zip(lens, npg)):
+        table[s_, :m] = phys[u:u + m]
+        u += m
+        t = np.arange(n)
+        tok_rows.append(table[s_, t // P].astype(np.int64) * P + t % P)
+        b = np.arange(n // r)
+        blk_rows.append(table[s_, b // (P // r)].astype(np.int64) * (P // r) + b % (P // r))
+    dev = dp.K.device
+    tok = torch.from_numpy(np.concatenate(tok_rows)).to(dev)
+    blk = torch.from_numpy(np.concatenate(blk_rows)).to(dev)
+
+    def pool(t: torch.Tensor, rows: int, idx: torch.Tensor) -> torch.Tensor:
+        p = torch.zeros((rows,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+        p.index_copy_(0, idx, t[:idx.numel()])
+        return p
+
+    out = DeviceProblem(**{**dp.__dict__})
+    out.K = pool(dp.K, num_pages * P, tok)
+    out.V = pool(dp.V, num_pages * P, tok)
+    out.k_idx = pool(dp.k_idx, num_pages * P, tok)
+    out.kc = pool(dp.kc, num_pages * (P // r), blk)
+    out.kc_scale = None if dp.kc_scale is None else pool(dp.kc_scale, num_pages * (P // r), blk)
+    out.paging = Paging(torch.from_numpy(table).to(dev), num_pages, P)
+    return out

@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_versions_and_inert_bound():
-    assert Q.lib().qsa_abi_version() == 1
+    assert Q.lib().qsa_abi_version() == 2
     assert "gfx950" in Q.version()
     with open(os.path.join(ROOT, "tests", "golden", "page_constants.json")) as f:
         page = json.load(f)
@@ -104,6 +104,37 @@ def compress(k=FAKE, kdt=Q.QSA_BF16, d=128, ratio=4, b=None, kc=FAKE, kcdt=Q.QSA
                                      P(scale), None)
 
 
+def _pg(**kw):
+    d = dict(block_table=FAKE, max_pages=64, num_pages=128, page_size=64)
+    d.update(kw)
+    return Q._PagedKV(**d)
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+def score_paged(pg="default", flags=0, b=None):
+    ix, b = _ix(), b or _batch(blk_offsets=None)
+    pg = _pg() if pg == "default" else pg
+    return Q.lib().qsa_index_score_paged(ctypes.byref(ix), 4, ctypes.byref(b), P(FAKE), 1024, flags,
+                                         _ref(pg), None)
+
+
+def decode_paged(pg="default"):
+    a, b = _attn(), _batch(blk_offsets=None)
+    pg = _pg() if pg == "default" else pg
+    return Q.lib().qsa_sparse_attn_decode_paged(ctypes.byref(a), P(FAKE), 2048, 4, ctypes.byref(b),
+                                                P(FAKE), P(FAKE), 1 << 30, _ref(pg), None)
+
+
+def compress_paged(pg="default"):
+    b = _batch(blk_offsets=None)
+    pg = _pg() if pg == "default" else pg
+    return Q.lib().qsa_compress_keys_paged(P(FAKE), Q.QSA_BF16, 128, 4, ctypes.byref(b), None, P(FAKE),
+                                           Q.QSA_BF16, None, _ref(pg), None)
+
+
 INV, UNS, WS = Q.QSA_ERR_INVALID_ARGUMENT, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
 
 CASES = [
@@ -142,6 +173,17 @@ CASES = [
     ("decode multi-query batch", lambda: decode(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)),
      INV, "prefill"),
     ("prefill null idx", lambda: prefill(idx=None), INV, "idx"),
+    ("paged score null descriptor", lambda: score_paged(pg=None), INV, "paging descriptor"),
+    ("paged score null table", lambda: score_paged(pg=_pg(block_table=None)), INV, "block_table"),
+    ("paged score page 48", lambda: score_paged(pg=_pg(page_size=48)), INV, "page_size=48"),
+    ("paged score page below ratio", lambda: score_paged(pg=_pg(page_size=2)), INV, "page_size=2"),
+    ("paged score too few pages", lambda: score_paged(pg=_pg(max_pages=63)), INV, "max_pages=63"),
+    ("paged score mfma", lambda: score_paged(flags=1), UNS, "paged"),
+    ("paged pool too large", lambda: score_paged(pg=_pg(num_pages=1 << 26)), UNS, "2^31"),
+    ("paged decode no pages", lambda: decode_paged(pg=_pg(num_pages=0)), INV, "num_pages=0"),
+    ("paged decode null descriptor", lambda: decode_paged(pg=None), INV, "paging descriptor"),
+    ("paged compress null table", lambda: compress_paged(pg=_pg(block_table=None)),
+     INV, "block_table"),
 ]
 
 
