@@ -270,6 +270,95 @@ qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, 
                                          int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                          size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
 
+/* ---- Ingest and rewind.  Serving engines append each new token's raw
+ * indexer key and compress every block it completes inside the decode step
+ * (vLLM report (a)6: one compressor work item per completed group, with the
+ * raw keys of the incomplete group kept in a per-request circular buffer
+ * whose capacity is a whole number of groups; the second "vLLM vs Atlas"
+ * report, section (a), QSA sparse attention + indexer: the fused
+ * pre-indexer commits the raw-key suffix to a circular state cache).  A rollback lowers the sequence length and must rewind the
+ * indexer state with it; the defect investigations page (Defect 1, fix plan
+ * PR-F) traces a crash to an indexer cursor left behind by a rollback, and
+ * asks that a rewind the state cannot follow be declined.
+ *
+ * Here the caller's sequence lengths are the only cursor: the batch passed
+ * to qsa_ingest gives each sequence's length N_s AFTER the append and its
+ * n_s new tokens (positions N_s - n_s .. N_s - 1), and the pooled count is
+ * floor(N_s/ratio) by definition.  A rollback is just a shorter N_s on a
+ * later call; nothing in the library has to be moved back.  The only state
+ * is a ring of the last raw keys per sequence and, per ring slot, the
+ * window of positions it still holds, which qsa_ingest checks before it
+ * completes a block from old keys. */
+typedef struct qsa_key_ring {
+    void *keys;            /* device [num_slots, capacity, d_idx] of the raw keys' dtype;
+                              position p of a sequence lives at row p % capacity of its slot */
+    int64_t *window;       /* device int64 [num_slots, 2] = {lo, hi}: the slot holds the raw
+                              keys of positions lo .. hi-1.  A fresh slot is {0, 0}. */
+    const int32_t *slots;  /* device int32 [num_seqs]: slot of sequence s; NULL = slot s */
+    int64_t num_slots;     /* >= 1 (>= num_seqs when slots is NULL) */
+    int32_t capacity;      /* tokens per slot: a multiple of ratio, >= ratio */
+} qsa_key_ring;
+
+/* Optional K/V append done by the same launch (the engine's paged KV write
+ * that precedes sparse attention, vLLM report (a)6 dataflow). */
+typedef struct qsa_kv_append {
+    const void *k_new;     /* device [total_q, hkv, d] rows of the new tokens */
+    const void *v_new;     /* device [total_q, hkv, d] */
+    void *k, *v;           /* caches laid out as qsa_attn.k / .v (or pools when paged) */
+    int32_t dtype;         /* QSA_F32 | QSA_BF16 */
+    int32_t hkv, d;        /* hkv >= 1, d == 128 */
+} qsa_kv_append;
+
+/* Per-sequence result codes written to status[s] (device int32 [num_seqs]). */
+#define QSA_INGEST_OK 0
+#define QSA_INGEST_LOST_KEYS 1    /* a block completed here needs a raw key the ring no
+                                     longer holds (rollback deeper than the ring, or skipped
+                                     positions); that block's compressed key is NOT written */
+#define QSA_INGEST_BAD_SLOT 2     /* slots[s] outside [0, num_slots): nothing written */
+#define QSA_INGEST_TOO_LONG 3     /* N_s beyond the block table (paged) or n_s > N_s:
+                                     nothing written */
+#define QSA_REWIND_DECLINED 4     /* qsa_ring_rewind only: see there */
+
+/* Append the n_s new tokens of every sequence.  For each new position p
+ * (ascending): the raw key k_new[row] is stored in the ring when p >= N_s -
+ * capacity, and K/V rows are written when kv != NULL; for every block b in
+ * floor((N_s - n_s)/ratio) .. floor(N_s/ratio) - 1 (those this append
+ * completes) kc[b] (+ kc_scale[b]) is written with exactly the arithmetic of
+ * qsa_compress_keys over the block's raw keys, old ones read from the ring,
+ * new ones from k_new.  Reads of the ring see it as it was before the call.
+ * Afterwards the slot's window is {max(lo', N_s - capacity), N_s} with lo' =
+ * min(lo, N_s - n_s) (or N_s - n_s when N_s - n_s > hi: skipped positions).
+ *  k_new:  device [total_q, d_idx] (rows by q_offsets; NULL q_offsets = one
+ *          new token per sequence), k_dtype QSA_F32 | QSA_BF16; the ring
+ *          keys have the same dtype.
+ *  b:      kv_offsets give N_s after the append (and the contiguous rows of
+ *          K, V when not paged); blk_offsets the kc rows when not paged;
+ *          max_q_per_seq >= max n_s; max_kv_len >= max N_s.
+ *  kc, kc_dtype, kc_scale: as qsa_compress_keys.
+ *  kv:     NULL, or the K/V append.
+ *  status: device int32 [num_seqs] or NULL: one QSA_INGEST_* code per sequence.
+ *  pg:     NULL (contiguous rows) or the paging of kc, kc_scale, K and V.
+ * Sequences sharing a ring slot in one call race (undefined).  Host errors:
+ * INVALID_ARGUMENT (null pointers, capacity, num_slots), UNSUPPORTED (ratio,
+ * d_idx, dtypes, kv->d), HIP. */
+qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                      const qsa_batch *b, const qsa_key_ring *ring, void *kc, int32_t kc_dtype,
+                      float *kc_scale, const qsa_kv_append *kv, int32_t *status,
+                      const qsa_paged_kv *pg, void *stream);
+
+/* Explicit rollback gate (defect investigations page, fix plan PR-F: a
+ * rewind the indexer state cannot follow is declined, not applied).  The
+ * batch's kv_offsets give the lengths N_s after the rollback.  Per sequence:
+ * if N_s <= hi and min(lo, N_s) <= ratio*floor(N_s/ratio) (the ring still
+ * holds the raw keys of the incomplete block), the window becomes
+ * {min(lo, N_s), N_s} and status[s] = QSA_INGEST_OK; otherwise nothing
+ * changes and status[s] = QSA_REWIND_DECLINED (or QSA_INGEST_BAD_SLOT).
+ * Calling it is optional: qsa_ingest applies the same rule to any shorter
+ * length, but reports a lost key only when the block completes.
+ * Errors: INVALID_ARGUMENT (null pointers), HIP. */
+qsa_status qsa_ring_rewind(const qsa_batch *b, int32_t ratio, const qsa_key_ring *ring,
+                           int32_t *status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

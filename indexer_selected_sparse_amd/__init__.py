@@ -31,8 +31,11 @@ EXPORTS = (
     "qsa_compress_keys", "qsa_index_score", "qsa_topk_workspace_size", "qsa_topk_blocks",
     "qsa_attn_workspace_size", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
-    "qsa_sparse_attn_prefill_paged",
+    "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind",
 )
+
+# per-sequence codes written by qsa_ingest / qsa_ring_rewind
+INGEST_OK, INGEST_LOST_KEYS, INGEST_BAD_SLOT, INGEST_TOO_LONG, REWIND_DECLINED = range(5)
 
 
 class QsaError(RuntimeError):
@@ -64,6 +67,17 @@ class _Attn(ctypes.Structure):
 class _PagedKV(ctypes.Structure):
     _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int64),
                 ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32)]
+
+
+class _KeyRing(ctypes.Structure):
+    _fields_ = [("keys", ctypes.c_void_p), ("window", ctypes.c_void_p), ("slots", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int64), ("capacity", ctypes.c_int32)]
+
+
+class _KvAppend(ctypes.Structure):
+    _fields_ = [("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32)]
 
 
 _lib = None
@@ -102,6 +116,10 @@ def lib():
         for f in (L.qsa_sparse_attn_decode_paged, L.qsa_sparse_attn_prefill_paged):
             f.restype = i32
             f.argtypes = [P, P, i32, i32, P, P, P, sz, P, P]
+        L.qsa_ingest.restype = i32
+        L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
+        L.qsa_ring_rewind.restype = i32
+        L.qsa_ring_rewind.argtypes = [P, i32, P, P, P]
         _lib = L
     return _lib
 
@@ -194,6 +212,34 @@ class Paging:
             raise TypeError("block_table must be a 2-D int32 tensor")
         return _PagedKV(self.block_table.data_ptr(), self.block_table.shape[1], int(self.num_pages),
                         int(self.page_size))
+
+
+@dataclass
+class KeyRing:
+    """Raw indexer keys of the last `capacity` positions per ring slot (C
+    qsa_key_ring).  keys [num_slots, capacity, d_idx] (dtype of the raw keys);
+    window int64 [num_slots, 2] = {lo, hi} (a fresh slot is {0, 0}); slots:
+    int32 [num_seqs] slot of each sequence, or None for slot s."""
+    keys: torch.Tensor
+    window: torch.Tensor
+    slots: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def empty(num_slots: int, capacity: int, d_idx: int, dtype=torch.bfloat16, device="cuda"):
+        return KeyRing(torch.zeros((num_slots, capacity, d_idx), dtype=dtype, device=device),
+                       torch.zeros((num_slots, 2), dtype=torch.int64, device=device))
+
+    def _c(self) -> _KeyRing:
+        _dev(self.keys, "ring.keys")
+        _dev(self.window, "ring.window")
+        if self.window.dtype != torch.int64 or tuple(self.window.shape) != (self.keys.shape[0], 2):
+            raise TypeError("ring.window must be int64 [num_slots, 2]")
+        if self.slots is not None:
+            _dev(self.slots, "ring.slots")
+            if self.slots.dtype != torch.int32:
+                raise TypeError("ring.slots must be int32")
+        return _KeyRing(self.keys.data_ptr(), self.window.data_ptr(), _ptr(self.slots),
+                        self.keys.shape[0], self.keys.shape[1])
 
 
 # -------------------------------------------------------------- functions
@@ -316,3 +362,45 @@ def sparse_attn_prefill(q, k, v, softmax_scale, idx, budget, ratio, batch, out, 
     L = lib()
     _attn_call(L.qsa_sparse_attn_prefill, L.qsa_sparse_attn_prefill_paged, q, k, v, softmax_scale,
                idx, budget, ratio, batch, out, ws, stream, paging)
+
+
+def ingest(k_new: torch.Tensor, ratio: int, batch: Batch, ring: KeyRing, kc: torch.Tensor,
+           kc_scale: Optional[torch.Tensor] = None, kv=None, status: Optional[torch.Tensor] = None,
+           stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_ingest: append the new tokens of every sequence (positions N_s - n_s ..
+    N_s - 1 with N_s from batch.kv_offsets and n_s from batch.q_offsets, one per
+    sequence when None): raw keys into the ring, every block they complete into
+    kc [+ kc_scale], and, with kv = (k_new, v_new, K, V), the K/V rows.
+    status: device int32 [num_seqs] or None (INGEST_* codes per sequence)."""
+    _dev(k_new, "k_new")
+    _dev(kc, "kc")
+    kcd = QSA_FP8_E4M3 if kc.dtype == torch.uint8 else _dtype_code(kc)
+    if ring.keys.dtype != k_new.dtype or ring.keys.shape[-1] != k_new.shape[-1]:
+        raise TypeError("ring.keys must have the dtype and width of k_new")
+    kva = None
+    if kv is not None:
+        kn, vn, K, V = kv
+        for t, n in ((kn, "kv.k_new"), (vn, "kv.v_new"), (K, "kv.k"), (V, "kv.v")):
+            _dev(t, n)
+        if not (kn.dtype == vn.dtype == K.dtype == V.dtype):
+            raise TypeError("K/V append tensors must share one dtype")
+        kva = _KvAppend(kn.data_ptr(), vn.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(K),
+                        K.shape[-2], K.shape[-1])
+    if status is not None:
+        _dev(status, "status")
+    b, rg = batch._c(), ring._c()
+    pg = None if paging is None else paging._c()
+    _check(lib().qsa_ingest(_ptr(k_new), _dtype_code(k_new), k_new.shape[-1], ratio, ctypes.byref(b),
+                            ctypes.byref(rg), _ptr(kc), kcd, _ptr(kc_scale),
+                            None if kva is None else ctypes.byref(kva), _ptr(status),
+                            None if pg is None else ctypes.byref(pg), _stream(stream)))
+
+
+def ring_rewind(batch: Batch, ratio: int, ring: KeyRing, status: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """qsa_ring_rewind: the rollback gate to the lengths in batch.kv_offsets
+    (per sequence INGEST_OK, or REWIND_DECLINED with the window unchanged)."""
+    if status is not None:
+        _dev(status, "status")
+    b, rg = batch._c(), ring._c()
+    _check(lib().qsa_ring_rewind(ctypes.byref(b), ratio, ctypes.byref(rg), _ptr(status), _stream(stream)))

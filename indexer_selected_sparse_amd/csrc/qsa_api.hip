@@ -196,7 +196,7 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio) {
 
 const char *qsa_last_error(void) { return g_err; }
 
-const char *qsa_version(void) { return "qsa 0.2.0 (abi 2, gfx950)"; }
+const char *qsa_version(void) { return "qsa 0.3.0 (abi 2, gfx950)"; }
 
 int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
@@ -335,6 +335,66 @@ qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, 
                                          size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {
     if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
     return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, false, pg, (hipStream_t)stream);
+}
+
+static qsa_status check_ring(const qsa_key_ring *ring, const qsa_batch *b, int32_t ratio) {
+    if (!ring) return fail(QSA_ERR_INVALID_ARGUMENT, "ring is NULL");
+    if (!ring->keys) return fail(QSA_ERR_INVALID_ARGUMENT, "ring.keys is NULL");
+    if (!ring->window) return fail(QSA_ERR_INVALID_ARGUMENT, "ring.window is NULL");
+    if (ring->capacity < ratio || ring->capacity % ratio != 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ring.capacity=%d must be a positive multiple of ratio=%d",
+                    ring->capacity, ratio);
+    if (ring->num_slots < 1 || (!ring->slots && ring->num_slots < b->num_seqs))
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "ring.num_slots=%lld must be >= 1 (>= num_seqs=%d when ring.slots is NULL)",
+                    (long long)ring->num_slots, b->num_seqs);
+    if (ring->num_slots > 0x7fffffffLL)
+        return fail(QSA_ERR_UNSUPPORTED, "ring.num_slots=%lld exceeds 2^31-1", (long long)ring->num_slots);
+    return ok();
+}
+
+qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t ratio,
+                      const qsa_batch *b, const qsa_key_ring *ring, void *kc, int32_t kc_dtype,
+                      float *kc_scale, const qsa_kv_append *kv, int32_t *status,
+                      const qsa_paged_kv *pg, void *stream) {
+    qsa_status s = check_batch(b, pg == nullptr);
+    if (s == QSA_OK) s = check_ratio(ratio);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
+    if (s == QSA_OK) s = check_ring(ring, b, ratio);
+    if (s != QSA_OK) return s;
+    if (!k_new) return fail(QSA_ERR_INVALID_ARGUMENT, "k_new is NULL");
+    if (!kc) return fail(QSA_ERR_INVALID_ARGUMENT, "kc is NULL");
+    if (k_dtype != QSA_F32 && k_dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "k_dtype=%d must be QSA_F32 or QSA_BF16", k_dtype);
+    if (kc_dtype != QSA_F32 && kc_dtype != QSA_BF16 && kc_dtype != QSA_FP8_E4M3)
+        return fail(QSA_ERR_UNSUPPORTED, "kc_dtype=%d is not a qsa_dtype", kc_dtype);
+    if (kc_dtype == QSA_FP8_E4M3 && !kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "kc_scale is NULL but kc_dtype is QSA_FP8_E4M3");
+    if (d_idx != 64 && d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d must be 64 or 128", d_idx);
+    if (b->q_offsets && b->max_q_per_seq < 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "batch.max_q_per_seq=%d must be >= 0", b->max_q_per_seq);
+    if (kv) {
+        if (!kv->k_new || !kv->v_new || !kv->k || !kv->v)
+            return fail(QSA_ERR_INVALID_ARGUMENT, "kv.k_new/v_new/k/v must not be NULL");
+        if (kv->dtype != QSA_F32 && kv->dtype != QSA_BF16)
+            return fail(QSA_ERR_UNSUPPORTED, "kv.dtype=%d must be QSA_F32 or QSA_BF16", kv->dtype);
+        if (kv->hkv < 1 || kv->hkv > 64)
+            return fail(QSA_ERR_UNSUPPORTED, "kv.hkv=%d must be in [1, 64]", kv->hkv);
+        if (kv->d != 128) return fail(QSA_ERR_UNSUPPORTED, "kv.d=%d must be 128", kv->d);
+    }
+    return hip_status(launch_ingest(k_new, k_dtype, d_idx, ratio, *b, *ring, kc, kc_dtype, kc_scale, kv,
+                                    status, pg, (hipStream_t)stream),
+                      "qsa_ingest launch");
+}
+
+qsa_status qsa_ring_rewind(const qsa_batch *b, int32_t ratio, const qsa_key_ring *ring, int32_t *status,
+                           void *stream) {
+    qsa_status s = check_batch(b, false);
+    if (s == QSA_OK) s = check_ratio(ratio);
+    if (s == QSA_OK) s = check_ring(ring, b, ratio);
+    if (s != QSA_OK) return s;
+    return hip_status(launch_ring_rewind(*b, ratio, *ring, status, (hipStream_t)stream),
+                      "qsa_ring_rewind launch");
 }
 
 }  // extern "C"

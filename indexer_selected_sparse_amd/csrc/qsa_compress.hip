@@ -11,36 +11,13 @@
 // times 1/ratio (exact for a power-of-two ratio, identical to dividing).
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+#include "qsa_kc.hpp"
 
 namespace qsa {
 namespace {
 
 constexpr int kCompressWaves = 4;        // waves per workgroup
 constexpr int kBlocksPerWave = 4;        // blocks a wave handles (loads issued together)
-
-template <typename TIn, int DPL>
-__device__ __forceinline__ void load_row(const TIn *__restrict__ p, float (&x)[DPL]);
-
-template <>
-__device__ __forceinline__ void load_row<uint16_t, 1>(const uint16_t *__restrict__ p, float (&x)[1]) {
-    x[0] = bf16_to_f32(p[0]);
-}
-template <>
-__device__ __forceinline__ void load_row<uint16_t, 2>(const uint16_t *__restrict__ p, float (&x)[2]) {
-    uint32_t u = *reinterpret_cast<const uint32_t *>(p);
-    x[0] = bf16lo(u);
-    x[1] = bf16hi(u);
-}
-template <>
-__device__ __forceinline__ void load_row<float, 1>(const float *__restrict__ p, float (&x)[1]) {
-    x[0] = p[0];
-}
-template <>
-__device__ __forceinline__ void load_row<float, 2>(const float *__restrict__ p, float (&x)[2]) {
-    float2 v = *reinterpret_cast<const float2 *>(p);
-    x[0] = v.x;
-    x[1] = v.y;
-}
 
 // KC: 0 = fp32, 1 = bf16, 2 = e4m3 (+ scale)
 template <typename TIn, int DPL, int KC>
@@ -80,32 +57,7 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
         float m[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) m[e] = acc[e] * inv_ratio;
-        const int64_t o = out_row * D + lane * DPL;
-        if constexpr (KC == 0) {
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) static_cast<float *>(kc)[o + e] = m[e];
-        } else if constexpr (KC == 1) {
-#pragma unroll
-            for (int e = 0; e < DPL; ++e)
-                static_cast<uint16_t *>(kc)[o + e] = (uint16_t)f32_to_bf16_bits(m[e]);
-        } else {
-            float amax = 0.0f;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(m[e]));
-            amax = wave_max(amax);
-            const float scale = amax / 448.0f;    // correctly rounded division
-            if (lane == 0) kc_scale[out_row] = scale;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) {
-                uint32_t c = 0;
-                if (scale != 0.0f) {
-                    float y = m[e] / scale;
-                    y = fminf(fmaxf(y, -448.0f), 448.0f);
-                    c = f32_to_e4m3(y);
-                }
-                static_cast<uint8_t *>(kc)[o + e] = (uint8_t)c;
-            }
-        }
+        store_kc<KC, DPL>(m, kc, kc_scale, out_row, lane);
     }
 }
 

@@ -42,6 +42,15 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
                        const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
                        hipStream_t st);
 
+// Ingest of new tokens (ring commit, completed-block compression, optional
+// K/V append) and the ring's rollback gate.
+hipError_t launch_ingest(const void *k_new, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
+                         const qsa_key_ring &ring, void *kc, int kc_dtype, float *kc_scale,
+                         const qsa_kv_append *kv, int32_t *status, const qsa_paged_kv *pg,
+                         hipStream_t st);
+hipError_t launch_ring_rewind(const qsa_batch &b, int ratio, const qsa_key_ring &ring, int32_t *status,
+                              hipStream_t st);
+
 // Host tracing (QSA_TRACE=1): one line per launch on stderr.
 bool trace_enabled();
 void trace(const char *fmt, ...);

@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -135,6 +135,32 @@ def compress_paged(pg="default"):
                                            Q.QSA_BF16, None, _ref(pg), None)
 
 
+def _ring(**kw):
+    d = dict(keys=FAKE, window=FAKE, slots=None, num_slots=2, capacity=8)
+    d.update(kw)
+    return Q._KeyRing(**d)
+
+
+def _kv(**kw):
+    d = dict(k_new=FAKE, v_new=FAKE, k=FAKE, v=FAKE, dtype=Q.QSA_BF16, hkv=4, d=128)
+    d.update(kw)
+    return Q._KvAppend(**d)
+
+
+def ingest(ring="default", kv=None, kdt=Q.QSA_BF16, d=128, ratio=4, kcdt=Q.QSA_BF16, scale=None, pg=None,
+           b=None, k_new=FAKE):
+    b = b or _batch()
+    ring = _ring() if ring == "default" else ring
+    return Q.lib().qsa_ingest(P(k_new), kdt, d, ratio, ctypes.byref(b), _ref(ring), P(FAKE), kcdt, P(scale),
+                              _ref(kv), None, _ref(pg), None)
+
+
+def rewind(ring="default", ratio=4, b=None):
+    b = b or _batch()
+    ring = _ring() if ring == "default" else ring
+    return Q.lib().qsa_ring_rewind(ctypes.byref(b), ratio, _ref(ring), None, None)
+
+
 INV, UNS, WS = Q.QSA_ERR_INVALID_ARGUMENT, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
 
 CASES = [
@@ -184,6 +210,24 @@ CASES = [
     ("paged decode null descriptor", lambda: decode_paged(pg=None), INV, "paging descriptor"),
     ("paged compress null table", lambda: compress_paged(pg=_pg(block_table=None)),
      INV, "block_table"),
+    ("ingest null ring", lambda: ingest(ring=None), INV, "ring is NULL"),
+    ("ingest null ring keys", lambda: ingest(ring=_ring(keys=None)), INV, "ring.keys"),
+    ("ingest null window", lambda: ingest(ring=_ring(window=None)), INV, "ring.window"),
+    ("ingest capacity below ratio", lambda: ingest(ring=_ring(capacity=2)), INV, "ring.capacity=2"),
+    ("ingest capacity not whole blocks", lambda: ingest(ring=_ring(capacity=10)), INV, "ring.capacity=10"),
+    ("ingest too few slots", lambda: ingest(ring=_ring(num_slots=1)), INV, "ring.num_slots=1"),
+    ("ingest null k_new", lambda: ingest(k_new=None), INV, "k_new"),
+    ("ingest e4m3 without scale", lambda: ingest(kcdt=Q.QSA_FP8_E4M3), INV, "kc_scale"),
+    ("ingest ratio 3", lambda: ingest(ratio=3), UNS, "ratio=3"),
+    ("ingest d_idx 32", lambda: ingest(d=32), UNS, "d_idx=32"),
+    ("ingest kv null", lambda: ingest(kv=_kv(v=None)), INV, "kv.k_new/v_new/k/v"),
+    ("ingest kv d 64", lambda: ingest(kv=_kv(d=64)), UNS, "kv.d=64"),
+    ("ingest kv fp8", lambda: ingest(kv=_kv(dtype=Q.QSA_FP8_E4M3)), UNS, "kv.dtype"),
+    ("ingest contiguous needs blk_offsets", lambda: ingest(b=_batch(blk_offsets=None)), INV, "blk_offsets"),
+    ("ingest paged page 48", lambda: ingest(pg=_pg(page_size=48), b=_batch(blk_offsets=None)), INV,
+     "page_size=48"),
+    ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
+    ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]
 
 
