@@ -15,7 +15,9 @@ A step is one pass of the whole hot path over one batch with every input
 resident in HBM.  `value` is queries per second of the step replayed from a
 HIP graph (one graph per input copy); `step_ms.eager` is the same step
 launched call by call.  Key compression is an ingest-time pass, timed on its
-own (`compress_ms`).  Decode steps rotate over several device copies of the
+own (`compress_ms`); with --ingest each decode step first appends every
+sequence's newest token (qsa_ingest: its raw key into the ring, the block
+it completes, its K/V rows), as a serving step does.  Decode steps rotate over several device copies of the
 inputs (more distinct bytes than the 256 MB last-level cache holds), so a
 step is not served from a cache warmed by the previous one.
 
@@ -62,6 +64,9 @@ def parse():
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                    help="keep K, V and the indexer caches in page pools of PAGE_SIZE tokens "
                         "(random physical page order) and call the paged entry points")
+    p.add_argument("--ingest", action="store_true",
+                   help="decode: each step first appends every sequence's newest token "
+                        "(qsa_ingest: raw key into the ring, the block it completes, K/V rows)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -96,6 +101,24 @@ def algorithmic_bytes(wl):
         score += nb * (sp.d_idx * s_kc + s_scale) + sp.h_idx * sp.d_idx * s_qi + 4 * sp.h_idx
         attn += T * 2 * sp.hkv * sp.d * s_kv + sp.hq * sp.d * 2 * s_kv + 4 * K
     return score + attn, attn, score
+
+
+def ingest_bytes(wl):
+    """Per-step bytes of appending one token per sequence: read its raw key
+    and K/V rows, write them to the ring and the caches, and for a sequence
+    whose length is a multiple of ratio read ratio-1 ring rows and write the
+    compressed key (+ scale) of the completed block."""
+    sp = wl.spec
+    s_kv = 2 if sp.kv_dtype == "bf16" else 4
+    s_k = 2 if sp.idx_dtype == "bf16" else 4
+    s_kc = {"bf16": 2, "f32": 4, "e4m3": 1}[sp.kc_dtype]
+    s_scale = 4 if sp.kc_dtype == "e4m3" else 0
+    tot = 0
+    for L in wl.lens:
+        tot += 2 * (sp.d_idx * s_k + 2 * sp.hkv * sp.d * s_kv)
+        if int(L) % sp.ratio == 0:
+            tot += (sp.ratio - 1) * sp.d_idx * s_k + sp.d_idx * s_kc + s_scale
+    return tot
 
 
 def prefill_flops(wl):
@@ -205,6 +228,9 @@ def main():
                                        "scores read contiguous caches only)"}))
             sys.exit(2)
         base = pipeline.page(base, wl.lens, args.paged, seed=spec.seed)
+    if args.ingest and prefill:
+        print(json.dumps({"error": "--ingest runs the decode workloads"}))
+        sys.exit(2)
 
     # compression (ingest pass), timed on its own
     base.compress()
@@ -216,6 +242,9 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     compress_ms = ev0.elapsed_time(ev1) / 5
+    if args.ingest:
+        pipeline.attach_ingest(base, wl)
+        step_bytes += ingest_bytes(wl)
 
     if prefill:
         R = args.replicas or 1      # the score matrix alone (336 MB) exceeds the LLC
@@ -228,8 +257,17 @@ def main():
         c.kc = base.kc.clone()
         c.kc_scale = None if base.kc_scale is None else base.kc_scale.clone()
         c.q, c.q_idx, c.w = base.q.clone(), base.q_idx.clone(), base.w.clone()
+        if base.ing is not None:
+            c.ing = pipeline.IngestState(
+                pipeline.KeyRing(base.ing.ring.keys.clone(), base.ing.ring.window.clone()),
+                base.ing.k_new.clone(), base.ing.k_row.clone(), base.ing.v_row.clone(),
+                base.ing.status.clone())
         reps.append(c)
     torch.cuda.synchronize()
+
+    def ingest(p):
+        if p.ing is not None:
+            p.ingest()
 
     def score(p):
         p.score(QSA_SCORE_MFMA) if prefill else p.score()
@@ -239,6 +277,7 @@ def main():
 
     for s in range(args.warmup):
         p = reps[s % R]
+        ingest(p)
         score(p)
         topk(p)
         p.attend()
@@ -246,12 +285,14 @@ def main():
 
     # events are recorded on torch's current stream, which is the stream
     # every library call below is enqueued on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         p = reps[s % R]
         e = evs[s]
+        e[4].record()
+        ingest(p)
         e[0].record()
         score(p)
         e[1].record()
@@ -265,6 +306,7 @@ def main():
     t_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    t_ingest = float(np.mean([e[4].elapsed_time(e[0]) for e in evs])) if args.ingest else None
 
     # The whole step captured once per input copy in a HIP graph and replayed:
     # the way a serving loop runs it (no call synchronises or allocates, so
@@ -275,6 +317,7 @@ def main():
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for p in reps:                      # settle lazy initialisation outside capture
+                ingest(p)
                 score(p)
                 topk(p)
                 p.attend()
@@ -283,6 +326,7 @@ def main():
         for p in reps:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
+                ingest(p)
                 score(p)
                 topk(p)
                 p.attend()
@@ -308,8 +352,11 @@ def main():
                                else str(wl.lens[0])),
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
-                   "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {})},
-        "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn},
+                   "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {}),
+                   **({"ingest": "one token per sequence",
+                       "ring_capacity": int(base.ing.ring.keys.shape[1])} if args.ingest else {})},
+        "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn,
+                      **({"ingest": t_ingest} if args.ingest else {})},
         "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
     }
@@ -337,6 +384,12 @@ def main():
         rec["step_hbm_gbps"] = step_bytes / (ms_step * 1e-3) / 1e9
         rec["step_bytes"] = step_bytes
         rec["index_score_gbps"] = score_bytes / (t_score * 1e-3) / 1e9
+    if args.ingest:
+        torch.cuda.synchronize()
+        ok = all(bool((p.ing.status == 0).all()) for p in reps)
+        if not ok:
+            print(json.dumps({"error": "ingest reported a non-zero status"}))
+            sys.exit(1)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, prefill)
     print(json.dumps(rec), flush=True)

@@ -13,11 +13,22 @@ import torch
 
 import numpy as np
 
-from . import (QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch, Paging, attn_workspace_size,
-               compress_keys, index_score, sparse_attn_decode, sparse_attn_prefill, topk_blocks,
-               topk_workspace_size)
+from . import (INGEST_OK, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch, KeyRing, Paging,
+               attn_workspace_size, compress_keys, index_score, ingest, sparse_attn_decode,
+               sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}
+
+
+@dataclass
+class IngestState:
+    """What a decode step appends: each sequence's newest token (position
+    N_s - 1), its raw indexer key into the ring, its K/V rows into the caches."""
+    ring: KeyRing
+    k_new: torch.Tensor                 # [B, d_idx] raw indexer keys
+    k_row: torch.Tensor                 # [B, hkv, d]
+    v_row: torch.Tensor                 # [B, hkv, d]
+    status: torch.Tensor                # int32 [B]
 
 
 @dataclass
@@ -42,6 +53,7 @@ class DeviceProblem:
     topk_ws_canon: Optional[torch.Tensor]  # selection from canonical scores
     decode: bool
     paging: Optional[Paging] = None        # K, V, k_idx, kc (+ scale) are page pools
+    ing: Optional[IngestState] = None      # set by attach_ingest()
 
     @property
     def blocks_per_query(self) -> int:
@@ -50,6 +62,14 @@ class DeviceProblem:
     def compress(self, stream=None) -> None:
         compress_keys(self.k_idx, self.ratio, self.batch, self.kc, self.kc_scale, stream=stream,
                       paging=self.paging)
+
+    def ingest(self, stream=None) -> None:
+        """Append every sequence's newest token (qsa_ingest, one token per
+        sequence): ring commit, the block it completes, its K/V rows."""
+        st = self.ing
+        ingest(st.k_new, self.ratio, self.batch, st.ring, self.kc, self.kc_scale,
+               kv=(st.k_row, st.v_row, self.K, self.V), status=st.status, stream=stream,
+               paging=self.paging)
 
     def score(self, mode: int = QSA_SCORE_CANONICAL, stream=None) -> None:
         index_score(self.q_idx, self.w, self.kc, self.kc_scale, self.ratio, self.batch, self.scores,
@@ -66,7 +86,9 @@ class DeviceProblem:
            self.batch, self.out, self.attn_ws, stream=stream, paging=self.paging)
 
     def step(self, mfma: bool = False, stream=None) -> None:
-        """One pass of the hot path: score -> top-k -> sparse attention."""
+        """One pass of the hot path: [ingest ->] score -> top-k -> sparse attention."""
+        if self.ing is not None:
+            self.ingest(stream=stream)
         self.score(QSA_SCORE_MFMA if mfma else QSA_SCORE_CANONICAL, stream=stream)
         self.topk(certified=mfma, stream=stream)
         self.attend(stream=stream)
@@ -149,3 +171,29 @@ def page(dp: DeviceProblem, lens, page_size: int, seed: int = 0, extra_pages: in
     out.kc_scale = None if dp.kc_scale is None else pool(dp.kc_scale, num_pages * (P // r), blk)
     out.paging = Paging(torch.from_numpy(table).to(dev), num_pages, P)
     return out
+
+
+def attach_ingest(dp: DeviceProblem, wl, capacity: Optional[int] = None) -> DeviceProblem:
+    """Give a decode problem a raw-key ring (`capacity` tokens per sequence,
+    default 2*ratio), filled by one prefill-sized qsa_ingest of every token
+    (which also rewrites kc exactly as compress() does), and the rows its
+    steps re-append: the newest token of each sequence (its raw key and K/V
+    rows, equal to what the caches already hold, so outputs are unchanged)."""
+    if not dp.decode:
+        raise ValueError("attach_ingest: decode problems only")
+    r = dp.ratio
+    cap = int(capacity or 2 * r)
+    dev = dp.kc.device
+    lens = [int(n) for n in wl.lens]
+    B = len(lens)
+    ring = KeyRing.empty(B, cap, wl.k_idx.shape[-1], dtype=wl.k_idx.dtype, device=dev)
+    status = torch.full((B,), -1, dtype=torch.int32, device=dev)
+    every = Batch.from_lengths(lens, lens, ratio=r, device=dev)
+    ingest(wl.k_idx.to(dev), r, every, ring, dp.kc, dp.kc_scale, status=status, paging=dp.paging)
+    torch.cuda.synchronize()
+    if not bool((status == INGEST_OK).all()):
+        raise RuntimeError(f"attach_ingest: ingest status {status.tolist()}")
+    last = torch.tensor(np.cumsum(lens) - 1, dtype=torch.int64)
+    dp.ing = IngestState(ring, wl.k_idx[last].to(dev).contiguous(), wl.K[last].to(dev).contiguous(),
+                         wl.V[last].to(dev).contiguous(), status)
+    return dp

@@ -75,13 +75,20 @@ class Rig:
         self.kv_hist = [(np.zeros((0,) + ((hkv, 128) if hkv else (0,)), np.int16),) * 2 for _ in range(B)]
         self.status = torch.full((B,), -1, dtype=torch.int32, device=DEV)
 
-    def batch(self, lens, news):
+    def batch(self, lens, news, one_each=False):
+        """one_each: every sequence appends exactly one token, passed as a
+        batch without q_offsets (the decode-step form)."""
         kv = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
         qo = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
-        return Q.Batch(torch.from_numpy(kv).to(DEV), torch.zeros(self.B + 1, dtype=torch.int64, device=DEV),
-                       torch.from_numpy(qo).to(DEV), int(qo[-1]), self.max_len, max(1, int(max(news))))
+        kvt = torch.from_numpy(kv).to(DEV)
+        blk = torch.zeros(self.B + 1, dtype=torch.int64, device=DEV)
+        if one_each:
+            assert all(n == 1 for n in news)
+            return Q.Batch(kvt, blk, None, self.B, self.max_len, 1)
+        return Q.Batch(kvt, blk, torch.from_numpy(qo).to(DEV), int(qo[-1]), self.max_len,
+                       max(1, int(max(news))))
 
-    def append(self, starts, news):
+    def append(self, starts, news, one_each=False):
         lens = [s + n for s, n in zip(starts, news)]
         tot = int(sum(news))
         k_new = torch.randn((max(tot, 1), self.d)).to(self.k_dtype)
@@ -89,7 +96,7 @@ class Rig:
         if self.hkv:
             kvn = (torch.randn((max(tot, 1), self.hkv, 128)).to(torch.bfloat16),
                    torch.randn((max(tot, 1), self.hkv, 128)).to(torch.bfloat16))
-        b = self.batch(lens, news)
+        b = self.batch(lens, news, one_each)
         self.status.fill_(-1)
         Q.ingest(k_new.to(DEV), self.r, b, self.ring, self.kc, self.kc_scale,
                  kv=None if kvn is None else (kvn[0].to(DEV), kvn[1].to(DEV), self.K, self.V),
@@ -196,6 +203,35 @@ def test_ingest_histories_match_oracle(case):
         n_lost += sum(x == OI.LOST_KEYS for x in got)
         rig.check()
     if cap == r:
+        assert n_lost > 0
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"r{c[0]}_cap{c[1]}_d{c[2]}_{c[4]}_P{c[5]}_hkv{c[6]}"
+                                             for c in CASES])
+def test_decode_appends_match_oracle(case):
+    """One token per sequence per call, passed without q_offsets (the
+    single-token kernel), with implicit rollbacks and rollback gates."""
+    r, cap, d, kdt, kind, P, hkv = case
+    rig = Rig(B=7, max_len=200, page=P, ratio=r, cap=cap, d_idx=d, k_dtype=kdt, kc_kind=kind, hkv=hkv,
+              seed=r * 31 + cap)
+    rng = rig.rng
+    rig.append([0] * rig.B, [int(x) for x in rng.integers(1, 40, rig.B)])
+    n_lost = 0
+    for step in range(60):
+        if step % 9 == 8:
+            rig.rewind([max(c - int(rng.choice([0, 1, 2, 3, 5, 9])), 1) for c in rig.cur])
+            rig.check()
+            continue
+        starts = []
+        for c in rig.cur:
+            drop = int(rng.choice([0] * 8 + [1, 2, 3, 6, 11]))
+            starts.append(min(max(c - drop, 0), rig.max_len - 1))
+        got = rig.append(starts, [1] * rig.B, one_each=True)
+        n_lost += sum(x == OI.LOST_KEYS for x in got)
+        if step % 5 == 0:
+            rig.check()
+    rig.check()
+    if cap == r and r > 1:
         assert n_lost > 0
 
 
@@ -325,3 +361,50 @@ def test_decode_loop_on_ingested_caches_equals_compressed_caches():
         outs.append((idx.clone(), out.clone()))
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
+@pytest.mark.parametrize("paged", [0, 64])
+def test_decode_step_with_ingest_equals_step_without(paged):
+    """attach_ingest() + a step that first re-appends every sequence's newest
+    token gives the same selection and output as the plain step, eagerly and
+    on every replay of a captured HIP graph."""
+    import dataclasses
+
+    import qsa_workloads as W
+    from indexer_selected_sparse_amd import pipeline
+    sp = dataclasses.replace(W.LONG_DECODE, budget=512)     # e4m3 compressed keys
+    wl = W.make(sp, lens=[4001, 2222, 517, 1024, 8], seed=5)
+
+    def problem():
+        dp = pipeline.upload(wl, DEV, decode=True)
+        dp.compress()
+        return pipeline.page(dp, wl.lens, paged, seed=1) if paged else dp
+
+    ref = problem()
+    ref.step()
+    dp = pipeline.attach_ingest(problem(), wl)
+    for _ in range(2):
+        dp.idx.fill_(-7)
+        dp.out.zero_()
+        dp.step()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.idx, ref.idx)
+        assert torch.equal(dp.out.view(torch.int16), ref.out.view(torch.int16))
+        assert (dp.ing.status == Q.INGEST_OK).all()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dp.step()
+    for _ in range(3):
+        dp.idx.fill_(-7)
+        dp.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.idx, ref.idx)
+        assert torch.equal(dp.out.view(torch.int16), ref.out.view(torch.int16))
