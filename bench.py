@@ -67,6 +67,9 @@ def parse():
     p.add_argument("--ingest", action="store_true",
                    help="decode: each step first appends every sequence's newest token "
                         "(qsa_ingest: raw key into the ring, the block it completes, K/V rows)")
+    p.add_argument("--kc-dtype", default=None, choices=["f32", "bf16", "e4m3", "fp4"],
+                   help="store the compressed index keys in this format instead of the workload's "
+                        "(fp4: E2M1 values with one E8M0 scale per 32 dims)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -92,8 +95,8 @@ def algorithmic_bytes(wl):
     excluded.  Returns (step_bytes, attention_bytes, score_bytes)."""
     sp = wl.spec
     s_kv = 2 if sp.kv_dtype == "bf16" else 4
-    s_kc = {"bf16": 2, "f32": 4, "e4m3": 1}[sp.kc_dtype]
-    s_scale = 4 if sp.kc_dtype == "e4m3" else 0
+    s_kc = {"bf16": 2, "f32": 4, "e4m3": 1, "fp4": 0.5}[sp.kc_dtype]
+    s_scale = {"e4m3": 4, "fp4": sp.d_idx // 32}.get(sp.kc_dtype, 0)
     s_qi = 2 if sp.idx_dtype == "bf16" else 4
     K = sp.budget // sp.ratio
     attn = score = 0
@@ -111,8 +114,8 @@ def ingest_bytes(wl):
     sp = wl.spec
     s_kv = 2 if sp.kv_dtype == "bf16" else 4
     s_k = 2 if sp.idx_dtype == "bf16" else 4
-    s_kc = {"bf16": 2, "f32": 4, "e4m3": 1}[sp.kc_dtype]
-    s_scale = 4 if sp.kc_dtype == "e4m3" else 0
+    s_kc = {"bf16": 2, "f32": 4, "e4m3": 1, "fp4": 0.5}[sp.kc_dtype]
+    s_scale = {"e4m3": 4, "fp4": sp.d_idx // 32}.get(sp.kc_dtype, 0)
     tot = 0
     for L in wl.lens:
         tot += 2 * (sp.d_idx * s_k + 2 * sp.hkv * sp.d * s_kv)
@@ -159,7 +162,8 @@ def cpu_baseline(wl, seconds, prefill):
     import oracle
     sp = wl.spec
     kc, kc_scale = oracle.compress(wl.k_idx.float().numpy(), wl.kv_offsets, sp.ratio, sp.kc_dtype)
-    kcv = oracle.kc_values(kc, sp.kc_dtype)
+    kcv = oracle.kc_values(kc, sp.kc_dtype, kc_scale)
+    kc_scale = oracle.score_scale(kc_scale, sp.kc_dtype)
     blk = wl.blk_offsets()
     Ls = wl.visible_lengths()
     qseq = wl.query_seq()
@@ -217,6 +221,13 @@ def main():
 
     spec = W.CONFIGS[args.workload]
     prefill = args.workload == "chunked_prefill"
+    if args.kc_dtype and args.kc_dtype != spec.kc_dtype:
+        if prefill:
+            print(json.dumps({"error": "--kc-dtype runs the decode workloads (matrix-core prefill "
+                                       "scores take bf16 compressed keys)"}))
+            sys.exit(2)
+        import dataclasses
+        spec = dataclasses.replace(spec, kc_dtype=args.kc_dtype)
     wl = W.make(spec)
     step_bytes, attn_bytes, score_bytes = algorithmic_bytes(wl)
     dev = "cuda:0"
@@ -376,7 +387,7 @@ def main():
                                "avg_ms": t_score}
     else:
         attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
-        traffic = None if args.paged else recorded_traffic(spec.name)
+        traffic = None if (args.paged or args.kc_dtype) else recorded_traffic(spec.name)
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                            "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",

@@ -38,7 +38,8 @@
  *
  * Layouts (row-major, varlen-packed, int64 offsets [B+1] with offsets[0]=0):
  *  k_idx [sum N_s, d_idx]; K, V [sum N_s, hkv, d];
- *  kc [sum floor(N_s/ratio), d_idx] (+ kc_scale [same rows] f32 for e4m3);
+ *  kc [sum floor(N_s/ratio), d_idx] (+ kc_scale [same rows] f32 for e4m3;
+ *  fp4: d_idx/2 bytes per row + kc_scale [same rows, d_idx/32] E8M0 bytes);
  *  q [total_q, hq, d]; q_idx [total_q, h_idx, d_idx]; w [total_q, h_idx] f32;
  *  scores [total_q, ld_scores] f32; idx [total_q, budget/ratio] int32;
  *  out [total_q, hq, d] (dtype of q).
@@ -69,7 +70,10 @@ typedef enum qsa_status {
 typedef enum qsa_dtype {
     QSA_F32 = 0,
     QSA_BF16 = 1,
-    QSA_FP8_E4M3 = 2 /* OCP E4M3FN: bias 7, max finite 448, no infinities */
+    QSA_FP8_E4M3 = 2, /* OCP E4M3FN: bias 7, max finite 448, no infinities */
+    QSA_FP4_E2M1 = 3  /* compressed keys only: OCP E2M1 codes, two per byte (dim 2j in
+                         the low nibble of byte j), with one E8M0 scale byte 2^(e-127)
+                         per 32 dims in a second plane (kc_scale) */
 } qsa_dtype;
 
 /* A varlen batch.  Offsets are DEVICE int64 arrays of num_seqs+1 entries. */
@@ -88,10 +92,12 @@ typedef struct qsa_batch {
 typedef struct qsa_indexer {
     const void *q_idx;           /* [total_q, h_idx, d_idx], dtype q_dtype */
     const float *w;              /* [total_q, h_idx] per-query head weights */
-    const void *kc;              /* [sum nb, d_idx] compressed keys, dtype kc_dtype */
-    const float *kc_scale;       /* [sum nb] iff kc_dtype == QSA_FP8_E4M3, else NULL */
-    int32_t q_dtype;             /* QSA_F32 | QSA_BF16 */
-    int32_t kc_dtype;            /* QSA_F32 | QSA_BF16 | QSA_FP8_E4M3 */
+    const void *kc;              /* [sum nb, d_idx] compressed keys, dtype kc_dtype
+                                    ([sum nb, d_idx/2] bytes for QSA_FP4_E2M1) */
+    const void *kc_scale;        /* e4m3: f32 [sum nb]; fp4: E8M0 bytes [sum nb, d_idx/32];
+                                    NULL for the other dtypes */
+    int32_t q_dtype;             /* QSA_F32 | QSA_BF16 (QSA_BF16 with QSA_FP4_E2M1 keys) */
+    int32_t kc_dtype;            /* QSA_F32 | QSA_BF16 | QSA_FP8_E4M3 | QSA_FP4_E2M1 */
     int32_t h_idx;               /* 1, 2, 4, 8 or 16 */
     int32_t d_idx;               /* 64 | 128 */
 } qsa_indexer;
@@ -128,24 +134,34 @@ int32_t qsa_abi_version(void);
  * amax = max_d |mean_d|, scale = amax/448 (fp32, correctly rounded) is written
  * to kc_scale[b] and code_d = e4m3_rne(clamp(mean_d/scale, +-448)); scale 0
  * gives all-zero codes.  (The e4m3 index plane with a per-block fp32 scale of
- * max|x|/448 is the long-context decode workload's definition.)
+ * max|x|/448 is the long-context decode workload's definition.)  fp4 (the
+ * E2M1 + E8M0 index plane of the "ATOM Model Support Guide" page,
+ * DeepSeek-V4.1: values and scales in two planes): per group of 32 dims,
+ * X = floor(log2(amax)) - 2 clamped to [-127, 127] (X = -127 when amax = 0;
+ * 2 is E2M1's largest exponent, as in the OCP MX rule), kc_scale byte
+ * X + 127, and code_d = the nearest E2M1 value of mean_d * 2^-X (ties to the
+ * even mantissa, magnitudes past 6 give 6; the sign bit is kept).
  *  k_idx:  device [sum N_s, d_idx], k_dtype QSA_F32 | QSA_BF16.
  *  ratio:  power of two in [1, 64]; d_idx in {64, 128}.
  *  first_block: device int64 [B] or NULL; blocks b < first_block[s] are not
  *          rewritten (incremental ingest after appending tokens).
- *  kc:     device [sum nb, d_idx] of kc_dtype (any of the three).
- *  kc_scale: device f32 [sum nb], required iff kc_dtype == QSA_FP8_E4M3.
+ *  kc:     device [sum nb, d_idx] of kc_dtype (any of the four; fp4 rows are
+ *          d_idx/2 bytes).
+ *  kc_scale: device f32 [sum nb] for QSA_FP8_E4M3, E8M0 bytes [sum nb, d_idx/32]
+ *          for QSA_FP4_E2M1 (required for both), else ignored.
  * Errors: INVALID_ARGUMENT (null pointers, num_seqs < 1), UNSUPPORTED (ratio,
  * d_idx, dtype), HIP. */
 qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                              const qsa_batch *b, const int64_t *first_block, void *kc,
-                             int32_t kc_dtype, float *kc_scale, void *stream);
+                             int32_t kc_dtype, void *kc_scale, void *stream);
 
 /* Indexer scores.  For every query i and visible block b < floor(L_i/ratio)
  * of its sequence:  s_b = sum_h w_h * ReLU(q_idx[i,h,:] . kc_b)  ("PR 16
  * review" (a): relu score of a 4Q+1K indexer; one key head, vLLM report
  * (a)1 validator).  For e4m3 keys the dot is taken over the code values and
- * then multiplied by kc_scale[b].
+ * then multiplied by kc_scale[b].  For fp4 keys each key value is its code
+ * value times its group's 2^(e-127), which is exact in fp32, and the dot runs
+ * over those values (needs a bf16 q_idx).
  *  QSA_SCORE_CANONICAL: the fp32 result of one fixed evaluation order —
  *    dot = +0; for d ascending: dot = fl(dot + fl(q*k)); [dot = fl(dot*scale)];
  *    r = dot > 0 ? dot : +0; s = +0; for h ascending: s = fl(s + fl(w_h*r)).
@@ -252,7 +268,7 @@ typedef struct qsa_paged_kv {
  * size not a power-of-two multiple of ratio, num_pages < 1). */
 qsa_status qsa_compress_keys_paged(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                                    const qsa_batch *b, const int64_t *first_block, void *kc,
-                                   int32_t kc_dtype, float *kc_scale, const qsa_paged_kv *pg,
+                                   int32_t kc_dtype, void *kc_scale, const qsa_paged_kv *pg,
                                    void *stream);
 
 /* qsa_index_score reading kc / kc_scale from pools (QSA_SCORE_CANONICAL only;
@@ -334,7 +350,7 @@ typedef struct qsa_kv_append {
  *  b:      kv_offsets give N_s after the append (and the contiguous rows of
  *          K, V when not paged); blk_offsets the kc rows when not paged;
  *          max_q_per_seq >= max n_s; max_kv_len >= max N_s.
- *  kc, kc_dtype, kc_scale: as qsa_compress_keys.
+ *  kc, kc_dtype, kc_scale: as qsa_compress_keys (any of the four dtypes).
  *  kv:     NULL, or the K/V append.
  *  status: device int32 [num_seqs] or NULL: one QSA_INGEST_* code per sequence.
  *  pg:     NULL (contiguous rows) or the paging of kc, kc_scale, K and V.
@@ -343,7 +359,7 @@ typedef struct qsa_kv_append {
  * d_idx, dtypes, kv->d), HIP. */
 qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                       const qsa_batch *b, const qsa_key_ring *ring, void *kc, int32_t kc_dtype,
-                      float *kc_scale, const qsa_kv_append *kv, int32_t *status,
+                      void *kc_scale, const qsa_kv_append *kv, int32_t *status,
                       const qsa_paged_kv *pg, void *stream);
 
 /* Explicit rollback gate (defect investigations page, fix plan PR-F: a

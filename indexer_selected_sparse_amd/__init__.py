@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_HIP = range(5)
-QSA_F32, QSA_BF16, QSA_FP8_E4M3 = 0, 1, 2
+QSA_F32, QSA_BF16, QSA_FP8_E4M3, QSA_FP4_E2M1 = 0, 1, 2, 3
 QSA_SCORE_CANONICAL, QSA_SCORE_MFMA = 0, 1
 
 EXPORTS = (
@@ -145,6 +145,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return QSA_BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return QSA_FP8_E4M3
+    if t.dtype == torch.float4_e2m1fn_x2:
+        return QSA_FP4_E2M1
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

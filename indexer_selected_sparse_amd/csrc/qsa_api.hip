@@ -110,12 +110,18 @@ static qsa_status check_indexer(const qsa_indexer *ix, bool mfma) {
     if (!ix->kc) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc is NULL");
     if (ix->q_dtype != QSA_F32 && ix->q_dtype != QSA_BF16)
         return fail(QSA_ERR_UNSUPPORTED, "indexer.q_dtype=%d must be QSA_F32 or QSA_BF16", ix->q_dtype);
-    if (ix->kc_dtype != QSA_F32 && ix->kc_dtype != QSA_BF16 && ix->kc_dtype != QSA_FP8_E4M3)
+    if (ix->kc_dtype != QSA_F32 && ix->kc_dtype != QSA_BF16 && ix->kc_dtype != QSA_FP8_E4M3 &&
+        ix->kc_dtype != QSA_FP4_E2M1)
         return fail(QSA_ERR_UNSUPPORTED, "indexer.kc_dtype=%d is not a qsa_dtype", ix->kc_dtype);
-    if (ix->kc_dtype == QSA_FP8_E4M3 && !ix->kc_scale)
-        return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc_scale is NULL but kc_dtype is QSA_FP8_E4M3");
-    if (ix->kc_dtype != QSA_FP8_E4M3 && ix->kc_scale)
-        return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc_scale must be NULL unless kc_dtype is QSA_FP8_E4M3");
+    const bool scaled = ix->kc_dtype == QSA_FP8_E4M3 || ix->kc_dtype == QSA_FP4_E2M1;
+    if (scaled && !ix->kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "indexer.kc_scale is NULL but kc_dtype=%d needs scales",
+                    ix->kc_dtype);
+    if (!scaled && ix->kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "indexer.kc_scale must be NULL unless kc_dtype is QSA_FP8_E4M3 or QSA_FP4_E2M1");
+    if (ix->kc_dtype == QSA_FP4_E2M1 && ix->q_dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "fp4 compressed keys need a bf16 q_idx (q_dtype=%d)", ix->q_dtype);
     if (ix->h_idx != 1 && ix->h_idx != 2 && ix->h_idx != 4 && ix->h_idx != 8 && ix->h_idx != 16)
         return fail(QSA_ERR_UNSUPPORTED, "indexer.h_idx=%d must be 1, 2, 4, 8 or 16", ix->h_idx);
     if (ix->d_idx != 64 && ix->d_idx != 128)
@@ -202,7 +208,7 @@ int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
 static qsa_status compress_common(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                                   const qsa_batch *b, const int64_t *first_block, void *kc,
-                                  int32_t kc_dtype, float *kc_scale, const qsa_paged_kv *pg,
+                                  int32_t kc_dtype, void *kc_scale, const qsa_paged_kv *pg,
                                   void *stream) {
     qsa_status s = check_batch(b, pg == nullptr);
     if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
@@ -213,10 +219,10 @@ static qsa_status compress_common(const void *k_idx, int32_t k_dtype, int32_t d_
     if (s != QSA_OK) return s;
     if (k_dtype != QSA_F32 && k_dtype != QSA_BF16)
         return fail(QSA_ERR_UNSUPPORTED, "k_dtype=%d must be QSA_F32 or QSA_BF16", k_dtype);
-    if (kc_dtype != QSA_F32 && kc_dtype != QSA_BF16 && kc_dtype != QSA_FP8_E4M3)
+    if (kc_dtype != QSA_F32 && kc_dtype != QSA_BF16 && kc_dtype != QSA_FP8_E4M3 && kc_dtype != QSA_FP4_E2M1)
         return fail(QSA_ERR_UNSUPPORTED, "kc_dtype=%d is not a qsa_dtype", kc_dtype);
-    if (kc_dtype == QSA_FP8_E4M3 && !kc_scale)
-        return fail(QSA_ERR_INVALID_ARGUMENT, "kc_scale is NULL but kc_dtype is QSA_FP8_E4M3");
+    if ((kc_dtype == QSA_FP8_E4M3 || kc_dtype == QSA_FP4_E2M1) && !kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "kc_scale is NULL but kc_dtype=%d needs scales", kc_dtype);
     if (d_idx != 64 && d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d must be 64 or 128", d_idx);
     if ((b->max_kv_len / ratio) > 0xffffffffLL * 16)
         return fail(QSA_ERR_UNSUPPORTED, "max_kv_len=%lld is too large", (long long)b->max_kv_len);
@@ -227,14 +233,14 @@ static qsa_status compress_common(const void *k_idx, int32_t k_dtype, int32_t d_
 
 qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                              const qsa_batch *b, const int64_t *first_block, void *kc,
-                             int32_t kc_dtype, float *kc_scale, void *stream) {
+                             int32_t kc_dtype, void *kc_scale, void *stream) {
     return compress_common(k_idx, k_dtype, d_idx, ratio, b, first_block, kc, kc_dtype, kc_scale,
                            nullptr, stream);
 }
 
 qsa_status qsa_compress_keys_paged(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                                    const qsa_batch *b, const int64_t *first_block, void *kc,
-                                   int32_t kc_dtype, float *kc_scale, const qsa_paged_kv *pg,
+                                   int32_t kc_dtype, void *kc_scale, const qsa_paged_kv *pg,
                                    void *stream) {
     if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
     return compress_common(k_idx, k_dtype, d_idx, ratio, b, first_block, kc, kc_dtype, kc_scale, pg,
@@ -288,6 +294,8 @@ qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_ind
     if (s == QSA_OK) s = check_budget(budget, ratio);
     if (s == QSA_OK) s = check_rows(b, ratio);
     if (s == QSA_OK && recheck) s = check_indexer(recheck, false);
+    if (s == QSA_OK && recheck && recheck->kc_dtype == QSA_FP4_E2M1)
+        return fail(QSA_ERR_UNSUPPORTED, "recheck: fp4 compressed keys are scored canonically only");
     if (s != QSA_OK) return s;
     if (recheck && b->max_kv_len / ratio > kTopkRecheckMaxBlocks)
         return fail(QSA_ERR_UNSUPPORTED,
@@ -355,7 +363,7 @@ static qsa_status check_ring(const qsa_key_ring *ring, const qsa_batch *b, int32
 
 qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                       const qsa_batch *b, const qsa_key_ring *ring, void *kc, int32_t kc_dtype,
-                      float *kc_scale, const qsa_kv_append *kv, int32_t *status,
+                      void *kc_scale, const qsa_kv_append *kv, int32_t *status,
                       const qsa_paged_kv *pg, void *stream) {
     qsa_status s = check_batch(b, pg == nullptr);
     if (s == QSA_OK) s = check_ratio(ratio);
@@ -366,10 +374,10 @@ qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t
     if (!kc) return fail(QSA_ERR_INVALID_ARGUMENT, "kc is NULL");
     if (k_dtype != QSA_F32 && k_dtype != QSA_BF16)
         return fail(QSA_ERR_UNSUPPORTED, "k_dtype=%d must be QSA_F32 or QSA_BF16", k_dtype);
-    if (kc_dtype != QSA_F32 && kc_dtype != QSA_BF16 && kc_dtype != QSA_FP8_E4M3)
+    if (kc_dtype != QSA_F32 && kc_dtype != QSA_BF16 && kc_dtype != QSA_FP8_E4M3 && kc_dtype != QSA_FP4_E2M1)
         return fail(QSA_ERR_UNSUPPORTED, "kc_dtype=%d is not a qsa_dtype", kc_dtype);
-    if (kc_dtype == QSA_FP8_E4M3 && !kc_scale)
-        return fail(QSA_ERR_INVALID_ARGUMENT, "kc_scale is NULL but kc_dtype is QSA_FP8_E4M3");
+    if ((kc_dtype == QSA_FP8_E4M3 || kc_dtype == QSA_FP4_E2M1) && !kc_scale)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "kc_scale is NULL but kc_dtype=%d needs scales", kc_dtype);
     if (d_idx != 64 && d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d must be 64 or 128", d_idx);
     if (b->q_offsets && b->max_q_per_seq < 0)
         return fail(QSA_ERR_INVALID_ARGUMENT, "batch.max_q_per_seq=%d must be >= 0", b->max_q_per_seq);

@@ -3,7 +3,8 @@
 // section (a)6: one compressed key per complete group; "PR 16 review",
 // section (a): 4-token mean-pooled blocks), stored as fp32, bf16 or OCP e4m3
 // with one fp32 scale max|x|/448 per block (the e4m3 index plane of the
-// long-context decode workload).
+// long-context decode workload), or as fp4 E2M1 codes with one E8M0 scale
+// per 32 dims ("ATOM Model Support Guide" page, DeepSeek-V4.1 index plane).
 //
 // A streaming HBM pass: each wave owns whole blocks; a lane owns DPL
 // consecutive dims of the d_idx-wide row, so every row load of the wave is one
@@ -24,7 +25,7 @@ template <typename TIn, int DPL, int KC>
 __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const TIn *__restrict__ k_idx, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ first_block, int log2_ratio,
-    float inv_ratio, void *__restrict__ kc, float *__restrict__ kc_scale, PageMap pm) {
+    float inv_ratio, void *__restrict__ kc, void *__restrict__ kc_scale, PageMap pm) {
     constexpr int D = DPL * kWave;
     const int s = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
 
 template <typename TIn, int DPL>
 hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb, int log2r,
-                       void *kc, int kc_dtype, float *kc_scale, const PageMap &pm, dim3 grid,
+                       void *kc, int kc_dtype, void *kc_scale, const PageMap &pm, dim3 grid,
                        hipStream_t st) {
     const float inv = 1.0f / (float)(1 << log2r);
     const TIn *x = static_cast<const TIn *>(k_idx);
@@ -77,8 +78,12 @@ hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb,
         hipLaunchKernelGGL((compress_kernel<TIn, DPL, 1>), grid, block, 0, st, x, b.kv_offsets,
                            b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
         break;
-    default:
+    case QSA_FP8_E4M3:
         hipLaunchKernelGGL((compress_kernel<TIn, DPL, 2>), grid, block, 0, st, x, b.kv_offsets,
+                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
+        break;
+    default:
+        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 3>), grid, block, 0, st, x, b.kv_offsets,
                            b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
         break;
     }
@@ -88,7 +93,7 @@ hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb,
 }  // namespace
 
 hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
-                           const int64_t *first_block, void *kc, int kc_dtype, float *kc_scale,
+                           const int64_t *first_block, void *kc, int kc_dtype, void *kc_scale,
                            const qsa_paged_kv *pg, hipStream_t st) {
     const PageMap pm = page_map(pg);
     const int log2r = __builtin_ctz((unsigned)ratio);

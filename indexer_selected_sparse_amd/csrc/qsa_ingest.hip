@@ -67,7 +67,7 @@ template <typename TIn, int DPL, int KC>
 __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_one_kernel(
     const TIn *__restrict__ k_new, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, int num_seqs, int log2r, float inv_ratio, RingArgs ring,
-    void *__restrict__ kc, float *__restrict__ kc_scale, KvArgs kv, int32_t *__restrict__ status,
+    void *__restrict__ kc, void *__restrict__ kc_scale, KvArgs kv, int32_t *__restrict__ status,
     PageMap pm) {
     constexpr int D = DPL * kWave;
     constexpr int kKeyChunks = D * (int)sizeof(TIn) / 16;
@@ -183,7 +183,7 @@ template <typename TIn, int DPL, int KC>
 __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
     const TIn *__restrict__ k_new, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int log2r,
-    float inv_ratio, RingArgs ring, void *__restrict__ kc, float *__restrict__ kc_scale, KvArgs kv,
+    float inv_ratio, RingArgs ring, void *__restrict__ kc, void *__restrict__ kc_scale, KvArgs kv,
     int32_t *__restrict__ status, PageMap pm, int items_per_seq) {
     constexpr int D = DPL * kWave;
     constexpr int kKeyBytes = D * (int)sizeof(TIn);
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void ring_rewind_kernel(const int64_t *__restr
 
 template <typename TIn, int DPL>
 hipError_t dispatch_ingest(const void *k_new, const qsa_batch &b, int log2r, const RingArgs &ring,
-                           void *kc, int kc_dtype, float *kc_scale, const KvArgs &kv, int32_t *status,
+                           void *kc, int kc_dtype, void *kc_scale, const KvArgs &kv, int32_t *status,
                            const PageMap &pm, dim3 grid, dim3 block, int items, hipStream_t st) {
     const float inv = 1.0f / (float)(1 << log2r);
     const TIn *x = static_cast<const TIn *>(k_new);
@@ -334,7 +334,8 @@ hipError_t dispatch_ingest(const void *k_new, const qsa_batch &b, int log2r, con
     switch (kc_dtype) {
     case QSA_F32: QSA_INGEST_LAUNCH(0); break;
     case QSA_BF16: QSA_INGEST_LAUNCH(1); break;
-    default: QSA_INGEST_LAUNCH(2); break;
+    case QSA_FP8_E4M3: QSA_INGEST_LAUNCH(2); break;
+    default: QSA_INGEST_LAUNCH(3); break;
     }
 #undef QSA_INGEST_LAUNCH
     return hipGetLastError();
@@ -347,7 +348,7 @@ RingArgs ring_args(const qsa_key_ring &r) {
 }  // namespace
 
 hipError_t launch_ingest(const void *k_new, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
-                         const qsa_key_ring &ring, void *kc, int kc_dtype, float *kc_scale,
+                         const qsa_key_ring &ring, void *kc, int kc_dtype, void *kc_scale,
                          const qsa_kv_append *kv, int32_t *status, const qsa_paged_kv *pg,
                          hipStream_t st) {
     const PageMap pm = page_map(pg);

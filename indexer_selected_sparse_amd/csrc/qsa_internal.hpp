@@ -16,7 +16,7 @@ namespace qsa {
 
 // Key compression (mean-pool of complete blocks).
 hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
-                           const int64_t *first_block, void *kc, int kc_dtype, float *kc_scale,
+                           const int64_t *first_block, void *kc, int kc_dtype, void *kc_scale,
                            const qsa_paged_kv *pg, hipStream_t st);
 
 // Canonical (bit-defined) indexer scores, decode and prefill.
@@ -45,7 +45,7 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
 // Ingest of new tokens (ring commit, completed-block compression, optional
 // K/V append) and the ring's rollback gate.
 hipError_t launch_ingest(const void *k_new, int k_dtype, int d_idx, int ratio, const qsa_batch &b,
-                         const qsa_key_ring &ring, void *kc, int kc_dtype, float *kc_scale,
+                         const qsa_key_ring &ring, void *kc, int kc_dtype, void *kc_scale,
                          const qsa_kv_append *kv, int32_t *status, const qsa_paged_kv *pg,
                          hipStream_t st);
 hipError_t launch_ring_rewind(const qsa_batch &b, int ratio, const qsa_key_ring &ring, int32_t *status,

@@ -39,15 +39,52 @@ __device__ __forceinline__ void load_row<float, 2>(const float *__restrict__ p, 
     x[1] = v.y;
 }
 
-// KC: 0 = fp32, 1 = bf16 (round to nearest even), 2 = e4m3 + fp32 scale.
-// m = this lane's DPL means; the whole wave must call it (e4m3 reduces amax
-// over the wave).
+// E2M1 code of y: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 in magnitude,
+// ties to the even mantissa (code bit 0), magnitudes past 6 give 6; the sign
+// bit of y is kept (bit 3).
+__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
+    const float a = fabsf(y);
+    const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.0f  ? 6u : 7u;
+    return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// KC: 0 = fp32, 1 = bf16 (round to nearest even), 2 = e4m3 + fp32 scale
+// (kc_scale: float per row), 3 = fp4: E2M1 codes two per byte, one E8M0
+// scale byte per 32 dims (kc_scale: bytes [rows, D/32]) with exponent
+// X = floor(log2(amax of the group)) - 2 in [-127, 127] (-127 for amax 0).
+// m = this lane's DPL means; the whole wave must call it (e4m3 and fp4
+// reduce amax over lanes).
 template <int KC, int DPL>
 __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict__ kc,
-                                         float *__restrict__ kc_scale, int64_t out_row, int lane) {
+                                         void *__restrict__ kc_scale, int64_t out_row, int lane) {
     constexpr int D = DPL * kWave;
     const int64_t o = out_row * D + lane * DPL;
-    if constexpr (KC == 0) {
+    if constexpr (KC == 3) {
+        constexpr int LPG = 32 / DPL;                 // lanes per 32-dim group
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(m[e]));
+#pragma unroll
+        for (int off = LPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+        int X = -127;
+        if (amax != 0.0f) {
+            X = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;   // amax = f * 2^k, f in [0.5, 1)
+            X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        }
+        uint32_t c[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) c[e] = f32_to_e2m1(__builtin_amdgcn_ldexpf(m[e], -X));
+        uint8_t *codes = static_cast<uint8_t *>(kc) + out_row * (D / 2);
+        if constexpr (DPL == 2) {
+            codes[lane] = (uint8_t)(c[0] | (c[1] << 4));
+        } else {
+            const uint32_t hi = (uint32_t)__shfl_xor((int)c[0], 1, kWave);
+            if ((lane & 1) == 0) codes[lane >> 1] = (uint8_t)(c[0] | (hi << 4));
+        }
+        if (lane % LPG == 0)
+            static_cast<uint8_t *>(kc_scale)[out_row * (D / 32) + lane / LPG] = (uint8_t)(X + 127);
+    } else if constexpr (KC == 0) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) static_cast<float *>(kc)[o + e] = m[e];
     } else if constexpr (KC == 1) {
@@ -60,7 +97,7 @@ __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict
         for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(m[e]));
         amax = wave_max(amax);
         const float scale = amax / 448.0f;    // correctly rounded division
-        if (lane == 0) kc_scale[out_row] = scale;
+        if (lane == 0) static_cast<float *>(kc_scale)[out_row] = scale;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
             uint32_t c = 0;

@@ -4,7 +4,10 @@
 // review" section (a): a 4Q+1K indexer with a relu score over 4-token
 // mean-pooled blocks; the single key head is the vLLM report's validator
 // (indexer kv heads == 1, section (a)1).  For e4m3 keys the dot runs over the
-// code values and is then multiplied by the block's fp32 scale.
+// code values and is then multiplied by the block's fp32 scale.  For fp4 keys
+// ("ATOM Model Support Guide" page, DeepSeek-V4.1: E2M1 values with E8M0
+// scales) each key value is its code value times its 32-dim group's power of
+// two, exact in fp32, and the dot runs over those values.
 //
 // The score decides an integer (the selection), so it is evaluated in one
 // fixed fp32 order that the CPU oracle follows too: for each head, a
@@ -29,6 +32,19 @@ namespace qsa {
 namespace {
 
 constexpr int kScoreThreads = 256;
+
+// fp4 index plane: a byte holds two E2M1 codes (tag type of the key row).
+struct Fp4x2 {
+    uint8_t v;
+};
+template <typename KT>
+struct KeyBits {
+    static constexpr int value = 8 * (int)sizeof(KT);
+};
+template <>
+struct KeyBits<Fp4x2> {
+    static constexpr int value = 4;
+};
 
 template <typename KT, int D>
 struct KRow;
@@ -196,8 +212,10 @@ __device__ __forceinline__ u32x4 key_load16(const void *row) {
 // them earlier.
 template <int N, int L>
 __device__ __forceinline__ void key_wait(u32x4 (&u)[L]) {
-    static_assert(L == 2 || L == 4, "chunk of 2 or 4 loads");
-    if constexpr (L == 2)
+    static_assert(L == 1 || L == 2 || L == 4, "chunk of 1, 2 or 4 loads");
+    if constexpr (L == 1)
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(u[0]) : "n"(N));
+    else if constexpr (L == 2)
         asm volatile("s_waitcnt vmcnt(%2)" : "+v"(u[0]), "+v"(u[1]) : "n"(N));
     else
         asm volatile("s_waitcnt vmcnt(%4)" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]) : "n"(N));
@@ -232,9 +250,40 @@ __device__ __forceinline__ void query_wait(u32x16 &u, float &prev) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(u), "+v"(prev));
 }
 
+// The E8M0 scale bytes of this lane's fp4 row (D/32 of them), requested
+// before the key loads so that the wait for the first chunk covers them.
+template <int D>
+__device__ __forceinline__ uint32_t fp4_scale_load(const uint8_t *p) {
+    uint32_t r;
+    if constexpr (D == 128)
+        asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    else
+        asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+// 2^(e - 127) from an E8M0 byte e (e = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
 template <typename KT, int CH>
-__device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * (int)sizeof(KT) / 16], float (&f)[CH]) {
-    if constexpr (std::is_same<KT, uint8_t>::value) {
+__device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * KeyBits<KT>::value / 128], float (&f)[CH],
+                                            float scl) {
+    if constexpr (std::is_same<KT, Fp4x2>::value) {
+        // byte j of the chunk holds dims 2j (low nibble) and 2j+1; the
+        // conversion multiplies by the group's power of two exactly
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const u32x4 w4 = u[0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], scl, 0);
+            const f32x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], scl, 1);
+            const f32x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], scl, 2);
+            const f32x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], scl, 3);
+            f[8 * e + 0] = r0.x; f[8 * e + 1] = r0.y; f[8 * e + 2] = r1.x; f[8 * e + 3] = r1.y;
+            f[8 * e + 4] = r2.x; f[8 * e + 5] = r2.y; f[8 * e + 6] = r3.x; f[8 * e + 7] = r3.y;
+        }
+    } else if constexpr (std::is_same<KT, uint8_t>::value) {
 #pragma unroll
         for (int v = 0; v < CH / 16; ++v) {
             const u32x4 w4 = u[v];
@@ -262,15 +311,16 @@ __device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * (int)sizeof(KT
 template <typename KT, int D, int H>
 __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
-    const float *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
+    const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
     int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
+    constexpr bool kFP4 = std::is_same<KT, Fp4x2>::value;
     constexpr int CH = kExactChunk;
     constexpr int NCH = D / CH;
-    constexpr int LPC = CH * (int)sizeof(KT) / 16;   // 16-byte loads per chunk of one row
-    constexpr int QW = CH / 2;                       // query dwords per (chunk, head)
-    static_assert(D % CH == 0 && (LPC == 2 || LPC == 4) && QW == 16, "chunk layout");
+    constexpr int LPC = CH * KeyBits<KT>::value / 128;   // 16-byte loads per chunk of one row
+    constexpr int QW = CH / 2;                           // query dwords per (chunk, head)
+    static_assert(D % CH == 0 && (LPC == 1 || LPC == 2 || LPC == 4) && QW == 16, "chunk layout");
     static_assert((NCH - 1) * LPC < 64, "loads in flight fit the wait counter");
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
@@ -280,15 +330,17 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     const bool active = b < nb;
     const int64_t row = pm.table ? paged_row(pm, qp.seq, active ? b : 0, pm.log2_page - log2r)
                                  : qp.blk_row0 + (active ? b : 0);
-    const float sc = kE4M3 ? kc_scale[row] : 1.0f;
-    const KT *krow = kc + row * D;
+    const float sc = kE4M3 ? static_cast<const float *>(kc_scale)[row] : 1.0f;
+    const uint8_t *krow = reinterpret_cast<const uint8_t *>(kc) + row * (D * KeyBits<KT>::value / 8);
     const uint32_t *q32 = reinterpret_cast<const uint32_t *>(q_idx) + i * (int64_t)(H * D / 2);
 
+    uint32_t sbits = 0;
+    if constexpr (kFP4) sbits = fp4_scale_load<D>(static_cast<const uint8_t *>(kc_scale) + row * (D / 32));
     u32x4 raw[NCH][LPC];
     static_for<0, NCH>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         raw[c][0] = key_load16<c * LPC * 16 + 0>(krow);
-        raw[c][1] = key_load16<c * LPC * 16 + 16>(krow);
+        if constexpr (LPC >= 2) raw[c][1] = key_load16<c * LPC * 16 + 16>(krow);
         if constexpr (LPC == 4) {
             raw[c][2] = key_load16<c * LPC * 16 + 32>(krow);
             raw[c][3] = key_load16<c * LPC * 16 + 48>(krow);
@@ -305,8 +357,9 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     static_for<0, NCH>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         key_wait<(NCH - 1 - c) * LPC>(raw[c]);
+        if constexpr (kFP4 && c == 0) asm volatile("" : "+v"(sbits));   // landed before chunk 0
         float kf[CH];
-        widen_chunk<KT, CH>(raw[c], kf);
+        widen_chunk<KT, CH>(raw[c], kf, kFP4 ? e8m0_to_f32((sbits >> (8 * c)) & 0xffu) : 1.0f);
         static_for<0, H>([&](auto hh) {
             constexpr int h = decltype(hh)::value;
             constexpr int t = c * H + h;
@@ -368,8 +421,8 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
         dim3 block(kScoreThreads);
 #define QSA_SCORE_LAUNCH(HH)                                                                       \
     hipLaunchKernelGGL((score_rounded_kernel<QT, KT, D, HH>), grid, block, 0, st, q, ix.w, kc,     \
-                       ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
-                       scores, ld, pm)
+                       static_cast<const float *>(ix.kc_scale), b.kv_offsets, b.blk_offsets,      \
+                       b.q_offsets, b.num_seqs, log2r, scores, ld, pm)
         switch (ix.h_idx) {
         case 1: QSA_SCORE_LAUNCH(1); break;
         case 2: QSA_SCORE_LAUNCH(2); break;
@@ -408,9 +461,11 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
     case QSA_BF16:
         return qb ? dispatch_d<uint16_t, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st)
                   : dispatch_d<float, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st);
-    default:
+    case QSA_FP8_E4M3:
         return qb ? dispatch_d<uint16_t, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st)
                   : dispatch_d<float, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st);
+    default:   // fp4 keys take a bf16 query (checked by the caller)
+        return dispatch_d<uint16_t, Fp4x2>(ix, log2r, b, scores, ld, pm, grid, st);
     }
 }
 

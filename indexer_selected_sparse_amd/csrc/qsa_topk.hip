@@ -1268,8 +1268,8 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
         trace("topk_cert norms grid=%dx%d", nch, b.num_seqs);
         hipLaunchKernelGGL(block_norm_kernel, dim3((unsigned)nch, (unsigned)b.num_seqs),
                            dim3(kNormThreads), 0, st, recheck->kc, recheck->kc_dtype,
-                           recheck->kc_scale, recheck->d_idx, b.blk_offsets, nch, part);
-        const CertIndexer cix{recheck->q_idx, recheck->w, recheck->kc, recheck->kc_scale,
+                           static_cast<const float *>(recheck->kc_scale), recheck->d_idx, b.blk_offsets, nch, part);
+        const CertIndexer cix{recheck->q_idx, recheck->w, recheck->kc, static_cast<const float *>(recheck->kc_scale),
                               recheck->q_dtype, recheck->kc_dtype, recheck->h_idx, recheck->d_idx};
         trace("topk_cert grid=%u K=%d ratio=%d lds_keys=%lld", grid.x, K, ratio, (long long)max_nb);
         hipLaunchKernelGGL(topk_cert_kernel, grid, dim3(kTopkThreads), lds, st, scores, ld,

@@ -17,7 +17,20 @@ from . import (INGEST_OK, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch, KeyRing, P
                attn_workspace_size, compress_keys, index_score, ingest, sparse_attn_decode,
                sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
-_KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}
+_KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
+             "fp4": torch.float4_e2m1fn_x2}
+
+
+def alloc_kc(rows: int, d_idx: int, kind: str, device):
+    """Compressed-key storage of `rows` blocks: (kc, kc_scale).  fp4 rows are
+    d_idx/2 bytes of E2M1 pairs with d_idx/32 E8M0 scale bytes; e4m3 rows have
+    one fp32 scale; the others none."""
+    if kind == "fp4":
+        kc = torch.empty((rows, d_idx // 2), dtype=torch.uint8, device=device).view(torch.float4_e2m1fn_x2)
+        sc = torch.empty((rows, d_idx // 32), dtype=torch.uint8, device=device).view(torch.float8_e8m0fnu)
+        return kc, sc
+    kc = torch.empty((rows, d_idx), dtype=_KC_TORCH[kind], device=device)
+    return kc, (torch.empty(rows, dtype=torch.float32, device=device) if kind == "e4m3" else None)
 
 
 @dataclass
@@ -103,9 +116,7 @@ def upload(wl, device: str = "cuda", decode: Optional[bool] = None, mfma_ws: boo
     batch = Batch.from_lengths(wl.lens, q_lens, ratio=sp.ratio, device=device)
     nb_tot = int(sum(n // sp.ratio for n in wl.lens))
     d_idx = sp.d_idx
-    kc = torch.empty((max(nb_tot, 1), d_idx), dtype=_KC_TORCH[sp.kc_dtype], device=device)
-    kc_scale = torch.empty(max(nb_tot, 1), dtype=torch.float32, device=device) \
-        if sp.kc_dtype == "e4m3" else None
+    kc, kc_scale = alloc_kc(max(nb_tot, 1), d_idx, sp.kc_dtype, device)
     ld = max(1, (max(wl.lens) + sp.ratio - 1) // sp.ratio)
     tq = wl.total_q
     K = wl.K.to(device)
@@ -159,6 +170,8 @@ def page(dp: DeviceProblem, lens, page_size: int, seed: int = 0, extra_pages: in
     blk = torch.from_numpy(np.concatenate(blk_rows)).to(dev)
 
     def pool(t: torch.Tensor, rows: int, idx: torch.Tensor) -> torch.Tensor:
+        if t.dtype in (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu):   # byte formats
+            return pool(t.view(torch.uint8), rows, idx).view(t.dtype)
         p = torch.zeros((rows,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
         p.index_copy_(0, idx, t[:idx.numel()])
         return p

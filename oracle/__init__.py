@@ -27,7 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libqsa_oracle.so")
 _FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
           "-std=c99", "-Wall", "-Wextra"]
 
-KIND = {"f32": 0, "bf16": 1, "e4m3": 2}
+KIND = {"f32": 0, "bf16": 1, "e4m3": 2, "fp4": 3}
 
 
 def build() -> str:
@@ -57,6 +57,14 @@ def lib():
         L.qo_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.qo_e4m3_encode.restype = ctypes.c_uint8
         L.qo_e4m3_encode.argtypes = [ctypes.c_float]
+        L.qo_e2m1_decode.restype = ctypes.c_float
+        L.qo_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.qo_e2m1_encode.restype = ctypes.c_uint8
+        L.qo_e2m1_encode.argtypes = [ctypes.c_float]
+        L.qo_e8m0_exponent.restype = i32
+        L.qo_e8m0_exponent.argtypes = [ctypes.c_float]
+        L.qo_fp4_value.restype = ctypes.c_float
+        L.qo_fp4_value.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
         L.qo_compress.restype = i32
         L.qo_compress.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
         L.qo_score_row.restype = i32
@@ -108,6 +116,23 @@ def e4m3_decode(codes) -> np.ndarray:
     return table[codes]
 
 
+def e2m1_decode(codes) -> np.ndarray:
+    """Values of 4-bit E2M1 codes (one code per array element)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib().qo_e2m1_decode(c) for c in range(16)], dtype=np.float32)
+    return table[codes & 15]
+
+
+def e2m1_encode(x) -> np.ndarray:
+    x = _f32(x)
+    f = lib().qo_e2m1_encode
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def e8m0_exponent(amax: float) -> int:
+    return int(lib().qo_e8m0_exponent(float(amax)))
+
+
 def e4m3_encode(x) -> np.ndarray:
     x = _f32(x)
     f = lib().qo_e4m3_encode
@@ -117,8 +142,10 @@ def e4m3_encode(x) -> np.ndarray:
 # ---------------------------------------------------------------- compress
 def compress(k_idx, kv_offsets, ratio: int, kind: str):
     """Mean-pool complete blocks.  Returns (kc, scale): kc is float32 for
-    "f32", uint16 bf16 bits for "bf16", uint8 codes for "e4m3" (scale is a
-    float32 array for "e4m3", else None)."""
+    "f32", uint16 bf16 bits for "bf16", uint8 codes for "e4m3" (scale: a
+    float32 array), and for "fp4" uint8 [nb, d/2] bytes of two E2M1 codes
+    (dim 2j in the low nibble of byte j) with uint8 [nb, d/32] E8M0 scale
+    bytes; scale is None for "f32" and "bf16"."""
     x = _f32(k_idx)
     kv_off = np.ascontiguousarray(kv_offsets, dtype=np.int64)
     B = len(kv_off) - 1
@@ -126,22 +153,43 @@ def compress(k_idx, kv_offsets, ratio: int, kind: str):
     nb = (np.diff(kv_off) // ratio).astype(np.int64)
     blk_off = np.concatenate([[0], np.cumsum(nb)]).astype(np.int64)
     tot = int(blk_off[-1])
-    dt = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[kind]
-    out = np.zeros((tot, d), dtype=dt)
-    scale = np.zeros(tot, dtype=np.float32) if kind == "e4m3" else None
+    dt = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "fp4": np.uint8}[kind]
+    out = np.zeros((tot, d // 2 if kind == "fp4" else d), dtype=dt)
+    scale = None
+    if kind == "e4m3":
+        scale = np.zeros(tot, dtype=np.float32)
+    elif kind == "fp4":
+        scale = np.zeros((tot, d // 32), dtype=np.uint8)
     rc = lib().qo_compress(_p(x), _p(kv_off), _p(blk_off), B, d, ratio, KIND[kind], _p(out),
                            _p(scale))
     _check(rc, "compress")
     return out, scale
 
 
-def kc_values(kc, kind: str) -> np.ndarray:
-    """Exact fp32 values of stored compressed keys (codes for e4m3)."""
+def kc_values(kc, kind: str, scale=None) -> np.ndarray:
+    """Exact fp32 values of stored compressed keys: the code values for e4m3
+    (its per-block scale multiplies the dot afterwards); for fp4 each value
+    is code value * 2^(E - 127) of its 32-dim group, exact in fp32."""
     if kind == "f32":
         return _f32(kc)
     if kind == "bf16":
         return bf16_bits_to_f32(kc)
+    if kind == "fp4":
+        kc = np.asarray(kc, dtype=np.uint8)
+        nb, half = kc.shape
+        codes = np.empty((nb, 2 * half), dtype=np.uint8)
+        codes[:, 0::2] = kc & 15
+        codes[:, 1::2] = kc >> 4
+        vals = e2m1_decode(codes).astype(np.float64)
+        exps = np.repeat(np.asarray(scale, dtype=np.int64) - 127, 32, axis=1)
+        return np.ldexp(vals, exps).astype(np.float32)
     return e4m3_decode(kc)
+
+
+def score_scale(kc_scale, kind: str):
+    """The per-block scale that multiplies the dot (e4m3 only; fp4 scales are
+    folded into the key values by kc_values)."""
+    return kc_scale if kind == "e4m3" else None
 
 
 # ------------------------------------------------------------------- score
@@ -234,7 +282,8 @@ def run_workload(wl, query_ids=None, want_scores=False, want_out=True, n_threads
     idx, scores (list of per-query arrays), out."""
     sp = wl.spec
     kc, kc_scale = compress(wl.k_idx.float().numpy(), wl.kv_offsets, sp.ratio, sp.kc_dtype)
-    kcv = kc_values(kc, sp.kc_dtype)
+    kcv = kc_values(kc, sp.kc_dtype, kc_scale)
+    dot_scale = score_scale(kc_scale, sp.kc_dtype)
     blk = wl.blk_offsets()
     Ls = wl.visible_lengths()
     qseq = wl.query_seq()
@@ -255,7 +304,7 @@ def run_workload(wl, query_ids=None, want_scores=False, want_out=True, n_threads
         Vr = wl.V[a:b].float().numpy()
         ka, kb = int(blk[s]), int(blk[s + 1])
         idx, scores, out = run_queries(
-            Kr, Vr, kcv[ka:kb], None if kc_scale is None else kc_scale[ka:kb],
+            Kr, Vr, kcv[ka:kb], None if dot_scale is None else dot_scale[ka:kb],
             wl.q[gq].float().numpy(), wl.q_idx[gq].float().numpy(), wl.w[gq].numpy(), Ls[gq],
             sp.ratio, sp.budget, sp.softmax_scale, want_scores=want_scores, want_out=want_out,
             n_threads=n_threads)

@@ -26,7 +26,7 @@ it or the rollback is declined):
   window to {min(lo, N), N}.
 
 Pure Python over small cases; the block mean is the C oracle's.  Pinned in
-`tests/test_oracle_pins.py` against a literal ring of tagged rows (each row
+`tests/test_ingest_oracle.py` against a literal ring of tagged rows (each row
 remembers the position it was last written for).
 """
 from __future__ import annotations
@@ -47,12 +47,13 @@ class SlotOracle:
         self.d, self.r, self.cap, self.kind = d, ratio, capacity, kind
         self.lo, self.hi = 0, 0
         self.hist = np.full((0, d), np.nan, dtype=np.float32)  # NaN = never written
-        # block -> (stored row, scale or None) as last written by an append
-        self.kc: Dict[int, Tuple[np.ndarray, Optional[float]]] = {}
+        # block -> (stored row, scale(s) or None) as last written by an append:
+        # one fp32 scale for e4m3, the d/32 E8M0 bytes for fp4
+        self.kc: Dict[int, Tuple[np.ndarray, Optional[np.ndarray]]] = {}
 
     def _block(self, rows: np.ndarray):
         kc, sc = _compress(rows, np.array([0, self.r], dtype=np.int64), self.r, self.kind)
-        return kc[0].copy(), (None if sc is None else float(sc[0]))
+        return kc[0].copy(), (None if sc is None else np.array(sc[0]).copy())
 
     def ingest(self, N: int, new_keys: np.ndarray) -> int:
         """Append the rows of `new_keys` as positions N - n .. N - 1."""

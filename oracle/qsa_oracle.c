@@ -15,7 +15,12 @@
  *            QSA bullet: blocks of 4 tokens, mean-pooled).  The optional e4m3
  *            index plane stores codes with one fp32 scale per block equal to
  *            max|x|/448 (the long-context decode workload's definition; the
- *            ATOM model-support page lists an fp8 index plane).
+ *            ATOM model-support page lists an fp8 index plane).  The fp4
+ *            index plane ("ATOM Model Support Guide" page, DeepSeek-V4.1:
+ *            E2M1 values and E8M0 scales in two planes) stores one E2M1 code
+ *            per dim and one power-of-two scale per 32 dims: the scale
+ *            exponent is floor(log2 amax) - 2 (2 = the largest E2M1
+ *            exponent), and each code is the nearest E2M1 value of x / scale.
  *  score     s_b = sum_h w_h * ReLU(q_h . kc_b) ("PR 16 review", section (a):
  *            a 4Q+1K indexer with a relu score; the single key head is the
  *            vLLM report's validator, indexer kv heads == 1).  Evaluated in
@@ -97,16 +102,66 @@ uint8_t qo_e4m3_encode(float x) {
     return (uint8_t)(best | ((bits_from_f32(x) >> 31) ? 0x80 : 0));
 }
 
+/* E2M1 (4 bits): sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+ * Exponent 0 is subnormal (m * 0.5); otherwise (1 + m/2) * 2^(e-1).  The
+ * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6; there is no NaN or infinity. */
+float qo_e2m1_decode(uint8_t c) {
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (float)(s ? -v : v);
+}
+
+/* fp32 -> E2M1, round to nearest, ties to the even mantissa; magnitudes past
+ * 6 give 6 (the nearest value).  Brute force over the 8 magnitudes in exact
+ * arithmetic; the sign bit is copied. */
+uint8_t qo_e2m1_encode(float x) {
+    double a = fabs((double)x);
+    int best = 0;
+    if (a > 6.0) return (uint8_t)(7 | ((bits_from_f32(x) >> 31) ? 8 : 0));   /* 6 is nearest */
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs((double)qo_e2m1_decode((uint8_t)c) - a);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            bestd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | ((bits_from_f32(x) >> 31) ? 8 : 0));
+}
+
+/* Scale exponent X of a 32-dim group (scale = 2^X, stored as the E8M0 byte
+ * X + 127): floor(log2(amax)) - 2, clamped to [-127, 127]; amax 0 gives
+ * -127.  frexpf gives amax = f * 2^k with f in [0.5, 1), so floor(log2) is
+ * k - 1 (subnormal amax included). */
+int qo_e8m0_exponent(float amax) {
+    if (amax == 0.0f) return -127;
+    int k;
+    (void)frexpf(amax, &k);
+    int x = (k - 1) - 2;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+    return x;
+}
+
+/* Exact value of an fp4 key element: code value times 2^(E - 127). */
+float qo_fp4_value(uint8_t code, uint8_t e8m0) {
+    return (float)ldexp((double)qo_e2m1_decode(code), (int)e8m0 - 127);
+}
+
 /* ------------------------------------------------------------- compress */
 
 /* Mean-pool every complete block of every sequence.
  * x: [sum N, d] fp32 (raw indexer keys, exactly widened); kv_off/blk_off:
  * [B+1]; kind 0 = fp32 out (float*), 1 = bf16 bits (uint16_t*), 2 = e4m3
- * codes (uint8_t*) plus scale[sum nb].  Returns 0, or -1 on bad arguments. */
+ * codes (uint8_t*) plus float scale[sum nb], 3 = fp4: E2M1 codes packed two
+ * per byte (uint8_t [sum nb][d/2], dim 2j in the low nibble of byte j) plus
+ * E8M0 scale bytes (uint8_t scale[sum nb][d/32]).  Returns 0, or -1 on bad
+ * arguments. */
 int qo_compress(const float *x, const int64_t *kv_off, const int64_t *blk_off, int B,
-                int d, int ratio, int kind, void *out, float *scale) {
-    if (!x || !kv_off || !blk_off || !out || d <= 0 || ratio <= 0 || kind < 0 || kind > 2) return -1;
-    if (kind == 2 && !scale) return -1;
+                int d, int ratio, int kind, void *out, void *scale) {
+    if (!x || !kv_off || !blk_off || !out || d <= 0 || ratio <= 0 || kind < 0 || kind > 3) return -1;
+    if ((kind == 2 || kind == 3) && !scale) return -1;
+    if (kind == 3 && d % 32 != 0) return -1;
     float *m = (float *)malloc(sizeof(float) * (size_t)d);
     if (!m) return -1;
     for (int s = 0; s < B; ++s) {
@@ -125,11 +180,25 @@ int qo_compress(const float *x, const int64_t *kv_off, const int64_t *blk_off, i
                 memcpy((float *)out + o * d, m, sizeof(float) * (size_t)d);
             } else if (kind == 1) {
                 for (int j = 0; j < d; ++j) ((uint16_t *)out)[o * d + j] = qo_bf16_round(m[j]);
+            } else if (kind == 3) {
+                uint8_t *codes = (uint8_t *)out + o * (d / 2);
+                uint8_t *sc8 = (uint8_t *)scale + o * (d / 32);
+                memset(codes, 0, (size_t)(d / 2));
+                for (int g = 0; g < d / 32; ++g) {
+                    float amax = 0.0f;
+                    for (int j = 32 * g; j < 32 * g + 32; ++j) if (fabsf(m[j]) > amax) amax = fabsf(m[j]);
+                    int X = qo_e8m0_exponent(amax);
+                    sc8[g] = (uint8_t)(X + 127);
+                    for (int j = 32 * g; j < 32 * g + 32; ++j) {
+                        uint8_t c = qo_e2m1_encode(ldexpf(m[j], -X));
+                        codes[j / 2] |= (uint8_t)((j & 1) ? (c << 4) : c);
+                    }
+                }
             } else {
                 float amax = 0.0f;
                 for (int j = 0; j < d; ++j) if (fabsf(m[j]) > amax) amax = fabsf(m[j]);
                 float sc = amax / 448.0f;
-                scale[o] = sc;
+                ((float *)scale)[o] = sc;
                 for (int j = 0; j < d; ++j) {
                     uint8_t c = 0;
                     if (sc != 0.0f) {

@@ -36,8 +36,13 @@ def run_gpu(wl, mfma: bool = False, decode=None):
     dp.compress()
     dp.step(mfma=mfma)
     torch.cuda.synchronize()
+    def host(t):   # byte formats torch cannot copy as such travel as uint8
+        if t.dtype in (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu):
+            t = t.view(torch.uint8)
+        return t.cpu()
+
     res = {
-        "kc": dp.kc.cpu(), "kc_scale": None if dp.kc_scale is None else dp.kc_scale.cpu(),
+        "kc": host(dp.kc), "kc_scale": None if dp.kc_scale is None else host(dp.kc_scale),
         "scores": dp.scores.cpu().numpy(), "idx": dp.idx.cpu().numpy(),
         "out": dp.out.float().cpu().numpy().astype(np.float64),
     }
@@ -49,7 +54,7 @@ def kc_bits(kc: torch.Tensor, kind: str) -> np.ndarray:
         return kc.numpy().view(np.uint32)
     if kind == "bf16":
         return kc.view(torch.int16).numpy().view(np.uint16)
-    return kc.numpy().view(np.uint8)
+    return kc.view(torch.uint8).numpy()
 
 
 def oracle_kc_bits(kc: np.ndarray, kind: str) -> np.ndarray:
@@ -66,6 +71,9 @@ def check_compress(wl, res, ref):
     if kind == "e4m3":
         gs = res["kc_scale"].numpy()[:n].view(np.uint32)
         assert np.array_equal(gs, ref["kc_scale"].view(np.uint32)), "kc_scale mismatch"
+    if kind == "fp4":
+        gs = res["kc_scale"].numpy()[:n]
+        assert np.array_equal(gs, ref["kc_scale"]), "fp4 scale bytes mismatch"
 
 
 def check_scores(wl, res, ref, query_ids):

@@ -226,6 +226,11 @@ CASES = [
     ("ingest contiguous needs blk_offsets", lambda: ingest(b=_batch(blk_offsets=None)), INV, "blk_offsets"),
     ("ingest paged page 48", lambda: ingest(pg=_pg(page_size=48), b=_batch(blk_offsets=None)), INV,
      "page_size=48"),
+    ("score fp4 with f32 query", lambda: score(ix=_ix(q_dtype=Q.QSA_F32, kc_dtype=Q.QSA_FP4_E2M1,
+                                                       kc_scale=FAKE)), UNS, "bf16 q_idx"),
+    ("score fp4 without scales", lambda: score(ix=_ix(kc_dtype=Q.QSA_FP4_E2M1)), INV, "needs scales"),
+    ("compress fp4 without scales", lambda: compress(kcdt=Q.QSA_FP4_E2M1), INV, "needs scales"),
+    ("topk recheck fp4", lambda: topk(recheck=_ix(kc_dtype=Q.QSA_FP4_E2M1, kc_scale=FAKE)), UNS, "fp4"),
     ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
     ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]

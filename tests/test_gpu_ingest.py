@@ -20,10 +20,12 @@ DEV = "cuda"
 
 
 def kc_torch_dtype(kind: str):
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[kind]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8, "fp4": torch.uint8}[kind]
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype in (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu):
+        t = t.view(torch.uint8)
     t = t.detach().cpu().contiguous()
     if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy()
@@ -57,11 +59,17 @@ class Rig:
         brows = self.num_pages * (page // ratio)
         kct = kc_torch_dtype(kc_kind)
         # garbage everywhere a call must not write
-        if kct == torch.uint8:
+        if kc_kind == "fp4":
+            self.kc = torch.randint(0, 255, (brows, d_idx // 2), generator=g,
+                                    dtype=torch.uint8).to(DEV).view(torch.float4_e2m1fn_x2)
+            self.kc_scale = torch.randint(0, 255, (brows, d_idx // 32), generator=g,
+                                          dtype=torch.uint8).to(DEV).view(torch.float8_e8m0fnu)
+        elif kct == torch.uint8:
             self.kc = torch.randint(0, 255, (brows, d_idx), generator=g, dtype=torch.uint8).to(DEV)
+            self.kc_scale = torch.randn(brows, generator=g).to(DEV)
         else:
             self.kc = torch.randn((brows, d_idx), generator=g).to(kct).to(DEV)
-        self.kc_scale = torch.randn(brows, generator=g).to(DEV) if kc_kind == "e4m3" else None
+            self.kc_scale = None
         self.K = torch.randn((rows, hkv, 128), generator=g).to(torch.bfloat16).to(DEV) if hkv else None
         self.V = torch.randn((rows, hkv, 128), generator=g).to(torch.bfloat16).to(DEV) if hkv else None
         self.num_slots = B + 3
@@ -139,8 +147,8 @@ class Rig:
 
     def check(self):
         win = self.ring.window.cpu().numpy()
-        kc = self.kc.cpu()
-        kcs = None if self.kc_scale is None else self.kc_scale.cpu().numpy()
+        kc = self.kc.view(torch.uint8).cpu() if self.kind == "fp4" else self.kc.cpu()
+        kcs = None if self.kc_scale is None else _bits(self.kc_scale)
         ring = _bits(self.ring.keys)
         bpp = self.P // self.r
         for s in range(self.B):
@@ -149,8 +157,10 @@ class Rig:
             for g, (row, sc) in o.kc.items():
                 phys = int(self.table[s, g // bpp]) * bpp + g % bpp
                 assert np.array_equal(_bits(kc[phys]), _oracle_row_bits(row, self.kind)), (s, g)
-                if sc is not None:
-                    assert np.float32(kcs[phys]).view(np.int32) == np.float32(sc).view(np.int32), (s, g)
+                if sc is not None and self.kind == "fp4":
+                    assert np.array_equal(kcs[phys], sc), (s, g)
+                elif sc is not None:
+                    assert kcs[phys] == np.float32(sc).view(np.int32), (s, g)
             want = self.key_hist[s]
             for p in range(o.lo, o.hi):
                 got = ring[sl, p % self.cap]
@@ -171,6 +181,7 @@ CASES = [
     (4, 4, 128, torch.bfloat16, "f32", 8, 2),
     (2, 6, 128, torch.bfloat16, "bf16", 4, 1),
     (4, 12, 128, torch.bfloat16, "e4m3", 64, 8),
+    (4, 8, 64, torch.bfloat16, "fp4", 16, 2),
 ]
 
 

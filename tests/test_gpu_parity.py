@@ -32,6 +32,7 @@ SMALL = [
     ("batched_small", W.BATCHED_DECODE, [3001, 1234, 777, 5002, 2049, 2052], None, {}),
     ("batched_budget64", W.BATCHED_DECODE, [1500, 903, 64, 65, 3], None, {"budget": 64}),
     ("long_small_e4m3", W.LONG_DECODE, [6001, 3003, 1000], None, {"budget": 512}),
+    ("long_small_fp4", W.LONG_DECODE, [6001, 3003, 1000, 37], None, {"budget": 512, "kc_dtype": "fp4"}),
     ("prefill_small", W.CHUNKED_PREFILL, [1500], [300], {"budget": 256}),
     ("verify_small", W.VERIFY, [2044, 2050, 2051, 2052, 2055, 2064], None, {}),
     ("verify_full_shape", W.VERIFY, None, None, {}),
@@ -54,6 +55,7 @@ DTYPES = [
     ("q_f32_kc_e4m3", "f32", "f32", "e4m3"),
     ("q_bf16_kc_f32", "bf16", "bf16", "f32"),
     ("q_f32_kc_bf16", "f32", "f32", "bf16"),
+    ("q_bf16_kc_fp4", "bf16", "bf16", "fp4"),
 ]
 
 

@@ -51,7 +51,7 @@ class TagRing:
                 continue
             kc, sc = oracle.compress(np.stack(rows), np.array([0, self.r], dtype=np.int64), self.r,
                                      self.kind)
-            self.kc[g] = (kc[0].copy(), None if sc is None else float(sc[0]))
+            self.kc[g] = (kc[0].copy(), None if sc is None else np.array(sc[0]).copy())
         for p in range(start, N):                     # writes after every read
             self.tags[p % self.cap] = p
             self.rows[p % self.cap] = keys[p - start]
@@ -65,12 +65,14 @@ def _same_blocks(a, b):
     assert a.keys() == b.keys()
     for g in a:
         assert np.array_equal(a[g][0], b[g][0]), g
-        assert a[g][1] == b[g][1], g
+        assert (a[g][1] is None) == (b[g][1] is None), g
+        if a[g][1] is not None:
+            assert np.array_equal(a[g][1], b[g][1]), g
 
 
 CONFIGS = [  # (ratio, capacity, d, kind)
     (4, 4, 8, "bf16"), (4, 8, 8, "f32"), (4, 12, 8, "e4m3"), (2, 6, 4, "bf16"),
-    (8, 8, 4, "f32"), (1, 1, 4, "f32"), (1, 3, 4, "bf16"), (4, 16, 8, "e4m3"),
+    (8, 8, 4, "f32"), (1, 1, 4, "f32"), (1, 3, 4, "bf16"), (4, 16, 8, "e4m3"), (4, 8, 64, "fp4"),
 ]
 
 

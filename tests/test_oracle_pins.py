@@ -374,3 +374,99 @@ def test_indexer_memory_sizing_matches_page(page):
     kc, _ = oracle.compress(np.zeros((m["tokens"] // 64, 128), np.float32),
                             np.array([0, m["tokens"] // 64]), m["ratio"], "bf16")
     assert kc.nbytes == m["tokens"] // 64 // m["ratio"] * m["head_dim"] * m["bytes_per_elem"]
+
+
+# ------------------------------------------------------- fp4 index plane
+# E2M1 magnitudes as the OCP microscaling format lists them, codes 0..7.
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_matches_the_format_table():
+    vals = oracle.e2m1_decode(np.arange(16, dtype=np.uint8))
+    assert vals[:8].tolist() == E2M1_MAGNITUDES
+    assert (-vals[8:]).tolist() == E2M1_MAGNITUDES
+    assert np.signbit(vals[8])                      # code 8 is -0
+
+
+@pytest.mark.parametrize("x,code", [
+    (0.0, 0), (0.25, 0), (0.2500001, 1), (0.5, 1), (0.7499999, 1), (0.75, 2), (1.25, 2),
+    (1.2500001, 3), (1.75, 4), (2.5, 4), (2.5000002, 5), (3.5, 6), (5.0, 6), (5.0000005, 7),
+    (6.0, 7), (7.9, 7), (1e30, 7), (-0.1, 8), (-0.3, 9), (-5.0, 14), (-7.0, 15),
+])
+def test_e2m1_encode_midpoints_and_saturation(x, code):
+    # midpoints between neighbours go to the even mantissa (code bit 0);
+    # past 6 the nearest value is 6
+    assert int(oracle.e2m1_encode(np.array([x], dtype=np.float32))[0]) == code
+
+
+def test_e2m1_encode_is_nearest_on_random_values():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(4000) * 3).astype(np.float32)
+    got = oracle.e2m1_decode(oracle.e2m1_encode(x)).astype(np.float64)
+    grid = np.array(E2M1_MAGNITUDES)
+    best = np.min(np.abs(np.abs(x.astype(np.float64))[:, None] - grid[None, :]), axis=1)
+    assert np.all(np.abs(np.abs(got) - np.abs(x)) == best)
+    nz = got != 0
+    assert np.all(np.sign(got[nz]) == np.sign(x[nz]))
+
+
+def _floor_log2_by_search(a: float) -> int:
+    n = 0
+    while 2.0 ** n > a:
+        n -= 1
+    while 2.0 ** (n + 1) <= a:
+        n += 1
+    return n
+
+
+def test_e8m0_exponent_is_floor_log2_minus_two():
+    rng = np.random.default_rng(4)
+    vals = list(np.float32(2.0) ** rng.integers(-140, 120, 60)) + \
+        list(rng.random(60).astype(np.float32) * np.float32(2.0) ** rng.integers(-130, 100, 60))
+    vals += [np.float32(1.0), np.nextafter(np.float32(1.0), np.float32(0)), np.float32(6.0),
+             np.float32(1e-45), np.float32(3.4e38)]
+    for a in vals:
+        a = np.float32(a)
+        if a == 0:
+            continue
+        want = min(max(_floor_log2_by_search(float(a)) - 2, -127), 127)
+        assert oracle.e8m0_exponent(a) == want, a
+    assert oracle.e8m0_exponent(0.0) == -127
+
+
+def test_fp4_compress_hand_worked_block():
+    # ratio 1, 64 dims = two groups.  Group 0 holds 4 (amax 4: floor(log2) 2,
+    # X = 0, scale 1) so its other values are coded as they are; group 1 is
+    # group 0 times 2^-10 (X = -10).  Values: 4, 0.25 (tie -> 0), 0.75 (tie
+    # -> 1.0), 2.5 (tie -> 2), 3.5 (tie -> 4), 5.5 (-> 6), -1.3 (-> -1.5),
+    # -0.2 (-> -0), then zeros.
+    g0 = np.zeros(32, dtype=np.float32)
+    g0[:8] = [4.0, 0.25, 0.75, 2.5, 3.5, 5.5, -1.3, -0.2]
+    x = np.concatenate([g0, g0 * np.float32(2.0 ** -10)])[None, :]
+    kc, sc = oracle.compress(x, np.array([0, 1], dtype=np.int64), 1, "fp4")
+    assert sc.tolist() == [[127, 117]]
+    want = [6, 0, 2, 4, 6, 7, 11, 8] + [0] * 24
+    codes = np.empty(64, dtype=np.uint8)
+    codes[0::2], codes[1::2] = kc[0] & 15, kc[0] >> 4
+    assert codes[:32].tolist() == want and codes[32:].tolist() == want
+    v = oracle.kc_values(kc, "fp4", sc)[0]
+    assert v[:8].tolist() == [4.0, 0.0, 1.0, 2.0, 4.0, 6.0, -1.5, -0.0]
+    assert np.array_equal(v[32:], v[:32] * np.float32(2.0 ** -10))
+
+
+def test_fp4_compress_error_bound_and_group_scales():
+    # every decoded value is within half a grid step of the mean (one step of
+    # 2 * 2^X past 6 * 2^X); each 32-dim group gets its own scale
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((40, 128)).astype(np.float32)
+    x[:, 32:64] *= 1000.0
+    off = np.array([0, 40], dtype=np.int64)
+    kc, sc = oracle.compress(x, off, 4, "fp4")
+    mean, _ = oracle.compress(x, off, 4, "f32")
+    v = oracle.kc_values(kc, "fp4", sc).astype(np.float64)
+    X = np.repeat(sc.astype(np.int64) - 127, 32, axis=1)
+    y = np.abs(mean.astype(np.float64)) / np.ldexp(1.0, X)
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    err = np.abs(v - mean) / np.ldexp(1.0, X)
+    assert np.all(err <= np.maximum(step / 2, np.where(y > 6, y - 6, 0)) + 1e-12)
+    assert np.all(sc[:, 1] >= sc[:, 0] + 8)   # x1000 is about 2^10 larger
