@@ -30,6 +30,7 @@ while the attention source is unchanged since the counters were taken.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -70,6 +71,9 @@ def parse():
     p.add_argument("--kc-dtype", default=None, choices=["f32", "bf16", "e4m3", "fp4"],
                    help="store the compressed index keys in this format instead of the workload's "
                         "(fp4: E2M1 values with one E8M0 scale per 32 dims)")
+    p.add_argument("--budget", type=int, default=0,
+                   help="token budget instead of the workload's (e.g. 8192: budget/ratio = 2048 "
+                        "blocks, the other value the pages' model validator allows)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -221,12 +225,13 @@ def main():
 
     spec = W.CONFIGS[args.workload]
     prefill = args.workload == "chunked_prefill"
+    if args.budget and args.budget != spec.budget:
+        spec = dataclasses.replace(spec, budget=args.budget)
     if args.kc_dtype and args.kc_dtype != spec.kc_dtype:
         if prefill:
             print(json.dumps({"error": "--kc-dtype runs the decode workloads (matrix-core prefill "
                                        "scores take bf16 compressed keys)"}))
             sys.exit(2)
-        import dataclasses
         spec = dataclasses.replace(spec, kc_dtype=args.kc_dtype)
     wl = W.make(spec)
     step_bytes, attn_bytes, score_bytes = algorithmic_bytes(wl)
@@ -387,7 +392,7 @@ def main():
                                "avg_ms": t_score}
     else:
         attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
-        traffic = None if (args.paged or args.kc_dtype) else recorded_traffic(spec.name)
+        traffic = None if (args.paged or args.kc_dtype or args.budget) else recorded_traffic(spec.name)
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                            "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",

@@ -33,6 +33,9 @@ SMALL = [
     ("batched_budget64", W.BATCHED_DECODE, [1500, 903, 64, 65, 3], None, {"budget": 64}),
     ("long_small_e4m3", W.LONG_DECODE, [6001, 3003, 1000], None, {"budget": 512}),
     ("long_small_fp4", W.LONG_DECODE, [6001, 3003, 1000, 37], None, {"budget": 512, "kc_dtype": "fp4"}),
+    # budget/ratio = 2048: dense up to L = 8195, sparse from 8196
+    ("long_k2048", W.LONG_DECODE, [20000, 9000, 8195, 8196, 700], None, {"budget": 8192}),
+    ("batched_k2048", W.BATCHED_DECODE, [30001, 8196, 12000], None, {"budget": 8192}),
     ("prefill_small", W.CHUNKED_PREFILL, [1500], [300], {"budget": 256}),
     ("verify_small", W.VERIFY, [2044, 2050, 2051, 2052, 2055, 2064], None, {}),
     ("verify_full_shape", W.VERIFY, None, None, {}),

@@ -137,3 +137,15 @@ def test_fused_path_edge_cases():
     _run([np.zeros(n, dtype=np.float32) for n in (700, 2048, 4000, 8192)] + [np.full(5000, 3.5, np.float32)])
     # negative and mixed-sign scores
     _run([rng.standard_normal(n).astype(np.float32) for n in (600, 4097, 8191)])
+
+
+def test_k2048_rows():
+    # budget/ratio = 2048, the other block count the pages' model validator
+    # allows: dense rows (nb <= 2048), the boundary, and sparse rows on both
+    # the few-row and the many-row paths, with ties
+    rng = np.random.default_rng(21)
+    rows = [_relu_like(rng, n) for n in (100, 2048, 2049, 4097, 8192, 20000, 32768)]
+    rows.append(rng.integers(0, 30, 9000).astype(np.float32))
+    _run(rows, budget=8192)
+    many = [_relu_like(rng, int(n)) for n in rng.integers(1800, 6000, 300)]
+    _run(many, budget=8192)
