@@ -74,6 +74,9 @@ def parse():
     p.add_argument("--budget", type=int, default=0,
                    help="token budget instead of the workload's (e.g. 8192: budget/ratio = 2048 "
                         "blocks, the other value the pages' model validator allows)")
+    p.add_argument("--local-blocks", type=int, default=0,
+                   help="decode: also keep the last N complete blocks of every query (union with "
+                        "its top-k selection, qsa_topk_blocks_local)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -92,11 +95,13 @@ def token_counts(wl):
     return out
 
 
-def algorithmic_bytes(wl):
+def algorithmic_bytes(wl, tokens=None):
     """Per-step bytes the decode method must move: index scan over the visible
     compressed keys, K/V rows of the selected token set, q and out, indexer
     query/weights and the idx row.  Scores are an intermediate and are
-    excluded.  Returns (step_bytes, attention_bytes, score_bytes)."""
+    excluded.  `tokens`: per-query |T| to use instead of the top-k rule (a
+    selection with the recent window kept).  Returns (step_bytes,
+    attention_bytes, score_bytes)."""
     sp = wl.spec
     s_kv = 2 if sp.kv_dtype == "bf16" else 4
     s_kc = {"bf16": 2, "f32": 4, "e4m3": 1, "fp4": 0.5}[sp.kc_dtype]
@@ -104,7 +109,9 @@ def algorithmic_bytes(wl):
     s_qi = 2 if sp.idx_dtype == "bf16" else 4
     K = sp.budget // sp.ratio
     attn = score = 0
-    for L, nb, T in token_counts(wl):
+    for j, (L, nb, T) in enumerate(token_counts(wl)):
+        if tokens is not None:
+            T = int(tokens[j])
         score += nb * (sp.d_idx * s_kc + s_scale) + sp.h_idx * sp.d_idx * s_qi + 4 * sp.h_idx
         attn += T * 2 * sp.hkv * sp.d * s_kv + sp.hq * sp.d * 2 * s_kv + 4 * K
     return score + attn, attn, score
@@ -261,6 +268,19 @@ def main():
     if args.ingest:
         pipeline.attach_ingest(base, wl)
         step_bytes += ingest_bytes(wl)
+    if args.local_blocks:
+        if prefill:
+            print(json.dumps({"error": "--local-blocks runs the decode workloads"}))
+            sys.exit(2)
+        pipeline.set_local_blocks(base, args.local_blocks)
+        base.score()
+        base.topk()
+        torch.cuda.synchronize()
+        # the union's size depends on the selection: count its tokens
+        valid = (base.idx >= 0).sum(dim=1).cpu().numpy()
+        tok = [int(v) * spec.ratio + (L - (L // spec.ratio) * spec.ratio)
+               for v, L in zip(valid, (int(x) for x in wl.visible_lengths()))]
+        step_bytes, attn_bytes, score_bytes = algorithmic_bytes(wl, tok)
 
     if prefill:
         R = args.replicas or 1      # the score matrix alone (336 MB) exceeds the LLC
@@ -369,6 +389,7 @@ def main():
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {}),
+                   **({"local_blocks": args.local_blocks} if args.local_blocks else {}),
                    **({"ingest": "one token per sequence",
                        "ring_capacity": int(base.ing.ring.keys.shape[1])} if args.ingest else {})},
         "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn,
@@ -392,7 +413,8 @@ def main():
                                "avg_ms": t_score}
     else:
         attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
-        traffic = None if (args.paged or args.kc_dtype or args.budget) else recorded_traffic(spec.name)
+        traffic = None if (args.paged or args.kc_dtype or args.budget or args.local_blocks) \
+            else recorded_traffic(spec.name)
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                            "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",

@@ -242,6 +242,23 @@ qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_
                                    int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                    size_t ws_bytes, void *stream);
 
+/* Block top-k with a recent window always kept: the second "llama.cpp vs
+ * Atlas" report's adoption plan (section (d), phase 3, item 6) keeps the
+ * most recent tokens as a union with the top-k set, and the first one
+ * (section (a)3) lists a count of local blocks among the indexer's
+ * parameters.  The window is taken in whole blocks.  Row i of idx
+ * (int32 [total_q, K + local_blocks], K = budget/ratio) is the ascending
+ * union of the blocks qsa_topk_blocks selects and the last
+ * min(local_blocks, nb) complete blocks, -1 padded.  In the dense regime it
+ * equals qsa_topk_blocks' row.  Attend it by passing
+ * budget + local_blocks*ratio to the attention call (same token set rule:
+ * the listed blocks plus the incomplete tail).  Workspace as
+ * qsa_topk_blocks(budget).  Errors: as qsa_topk_blocks, plus UNSUPPORTED
+ * when local_blocks < 0 or K + local_blocks > 2048. */
+qsa_status qsa_topk_blocks_local(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
+                                 int32_t budget, int32_t ratio, int32_t local_blocks, const qsa_batch *b,
+                                 int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- Paged caches.  The serving engines on the pages keep K/V and the
  * indexer cache in fixed-size pages addressed through a per-sequence block
  * table (vLLM report (a)1 and (a)6: the indexer K cache and the selection go

@@ -31,7 +31,7 @@ EXPORTS = (
     "qsa_compress_keys", "qsa_index_score", "qsa_topk_workspace_size", "qsa_topk_blocks",
     "qsa_attn_workspace_size", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
-    "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind",
+    "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
 )
 
 # per-sequence codes written by qsa_ingest / qsa_ring_rewind
@@ -116,6 +116,8 @@ def lib():
         for f in (L.qsa_sparse_attn_decode_paged, L.qsa_sparse_attn_prefill_paged):
             f.restype = i32
             f.argtypes = [P, P, i32, i32, P, P, P, sz, P, P]
+        L.qsa_topk_blocks_local.restype = i32
+        L.qsa_topk_blocks_local.argtypes = [P, i64, P, i32, i32, i32, P, P, P, sz, P]
         L.qsa_ingest.restype = i32
         L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
         L.qsa_ring_rewind.restype = i32
@@ -307,18 +309,23 @@ def topk_workspace_size(batch: Batch, budget: int, ratio: int, recheck=None) -> 
 
 
 def topk_blocks(scores, budget: int, ratio: int, batch: Batch, idx: torch.Tensor,
-                recheck=None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+                recheck=None, ws: Optional[torch.Tensor] = None, stream=None,
+                local_blocks: int = 0) -> None:
     """qsa_topk_blocks into idx [total_q, budget/ratio] int32.  `recheck` is the
-    tuple (q_idx, w, kc, kc_scale) when scores came from QSA_SCORE_MFMA."""
+    tuple (q_idx, w, kc, kc_scale) when scores came from QSA_SCORE_MFMA.  With
+    local_blocks > 0 this is qsa_topk_blocks_local: idx [total_q, budget/ratio
+    + local_blocks] also keeps the last local_blocks complete blocks."""
     _dev(scores, "scores")
     _dev(idx, "idx")
     b = batch._c()
     ix = None if recheck is None else _indexer(*recheck)
-    _check(lib().qsa_topk_blocks(_ptr(scores), scores.shape[1],
-                                 None if ix is None else ctypes.byref(ix), budget, ratio,
-                                 ctypes.byref(b), _ptr(idx), _ptr(ws),
-                                 0 if ws is None else ws.numel() * ws.element_size(),
-                                 _stream(stream)))
+    args = (_ptr(scores), scores.shape[1], None if ix is None else ctypes.byref(ix), budget, ratio)
+    tail = (ctypes.byref(b), _ptr(idx), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+            _stream(stream))
+    if local_blocks:
+        _check(lib().qsa_topk_blocks_local(*args, int(local_blocks), *tail))
+    else:
+        _check(lib().qsa_topk_blocks(*args, *tail))
 
 
 def _attn(q, k, v, softmax_scale) -> _Attn:

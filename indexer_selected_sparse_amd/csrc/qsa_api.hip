@@ -287,9 +287,9 @@ size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio
     return topk_workspace_bytes(*b, budget, ratio, recheck);
 }
 
-qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
-                           int32_t budget, int32_t ratio, const qsa_batch *b, int32_t *idx,
-                           void *ws, size_t ws_bytes, void *stream) {
+static qsa_status topk_common(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
+                              int32_t budget, int32_t ratio, int32_t local_blocks, const qsa_batch *b,
+                              int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
     qsa_status s = check_batch(b, recheck != nullptr);
     if (s == QSA_OK) s = check_budget(budget, ratio);
     if (s == QSA_OK) s = check_rows(b, ratio);
@@ -297,6 +297,9 @@ qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_ind
     if (s == QSA_OK && recheck && recheck->kc_dtype == QSA_FP4_E2M1)
         return fail(QSA_ERR_UNSUPPORTED, "recheck: fp4 compressed keys are scored canonically only");
     if (s != QSA_OK) return s;
+    if (local_blocks < 0 || budget / ratio + local_blocks > 2048)
+        return fail(QSA_ERR_UNSUPPORTED, "local_blocks=%d: budget/ratio + local_blocks must be in [K, 2048]",
+                    local_blocks);
     if (recheck && b->max_kv_len / ratio > kTopkRecheckMaxBlocks)
         return fail(QSA_ERR_UNSUPPORTED,
                     "re-checked top-k supports at most %lld blocks per row (max_kv_len/ratio=%lld)",
@@ -311,9 +314,24 @@ qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_ind
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(QSA_ERR_WORKSPACE, "top-k workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_topk_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
-    return hip_status(launch_topk(scores, ld_scores, recheck, budget, ratio, *b, idx, ws,
-                                  (hipStream_t)stream),
-                      "qsa_topk_blocks launch");
+    const int ldi = budget / ratio + local_blocks;
+    hipError_t e = launch_topk(scores, ld_scores, recheck, budget, ratio, *b, idx, ldi, ws, (hipStream_t)stream);
+    if (e == hipSuccess && local_blocks > 0)
+        e = launch_topk_local(budget, ratio, local_blocks, *b, idx, ldi, (hipStream_t)stream);
+    return hip_status(e, "qsa_topk_blocks launch");
+}
+
+qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
+                           int32_t budget, int32_t ratio, const qsa_batch *b, int32_t *idx,
+                           void *ws, size_t ws_bytes, void *stream) {
+    return topk_common(scores, ld_scores, recheck, budget, ratio, 0, b, idx, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_topk_blocks_local(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
+                                 int32_t budget, int32_t ratio, int32_t local_blocks, const qsa_batch *b,
+                                 int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
+    return topk_common(scores, ld_scores, recheck, budget, ratio, local_blocks, b, idx, ws, ws_bytes,
+                       stream);
 }
 
 size_t qsa_attn_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t budget, int32_t ratio) {

@@ -32,7 +32,11 @@ hipError_t launch_score_mfma(const qsa_indexer &ix, int ratio, const qsa_batch &
 constexpr int64_t kTopkRecheckMaxBlocks = 32768;
 size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa_indexer *recheck);
 hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *recheck, int budget,
-                       int ratio, const qsa_batch &b, int32_t *idx, void *ws, hipStream_t st);
+                       int ratio, const qsa_batch &b, int32_t *idx, int ldi, void *ws, hipStream_t st);
+// In place: row i of idx (stride ldi) becomes the ascending union of its
+// top-K selection and the last local_blocks complete blocks.
+hipError_t launch_topk_local(int budget, int ratio, int local_blocks, const qsa_batch &b, int32_t *idx,
+                             int ldi, hipStream_t st);
 
 // Sparse gather attention (decode and prefill share the kernel).
 int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio, bool decode);

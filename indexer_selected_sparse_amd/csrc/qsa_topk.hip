@@ -347,13 +347,13 @@ __device__ __forceinline__ void cache_row(const float *__restrict__ row, int64_t
 template <bool CACHED>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
-    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx) {
+    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx, int ldi) {
     __shared__ TopkShared S;
     extern __shared__ uint32_t lds_keys[];
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
-    int32_t *out = idx + i * (int64_t)K;
+    int32_t *out = idx + i * (int64_t)ldi;
     if (nb <= K) {
         for (int t = threadIdx.x; t < K; t += kTopkThreads) out[t] = (t < nb) ? t : -1;
         return;
@@ -536,7 +536,7 @@ struct BandKey {
 __global__ __launch_bounds__(kTopkThreads) void topk_cert_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, int K, int32_t *__restrict__ idx, CertIndexer ix,
+    int log2r, int K, int32_t *__restrict__ idx, int ldi, CertIndexer ix,
     const float *__restrict__ norm_part, int n_norm_chunks) {
     __shared__ TopkShared S;
     __shared__ CertShared C;
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cert_kernel(
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
-    int32_t *out = idx + i * (int64_t)K;
+    int32_t *out = idx + i * (int64_t)ldi;
     if (nb <= K) {
         for (int t = threadIdx.x; t < K; t += kTopkThreads) out[t] = (t < nb) ? t : -1;
         return;
@@ -743,7 +743,7 @@ __device__ __forceinline__ ChunkWs chunk_ws(const void *ws, int64_t i, int c, in
 __global__ __launch_bounds__(kClassifyThreads) void topk_classify_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int nchunks,
-    int32_t *__restrict__ idx, void *__restrict__ ws) {
+    int32_t *__restrict__ idx, int ldi, void *__restrict__ ws) {
     __shared__ uint32_t hist[kSample];
     __shared__ uint32_t red[kClassifyThreads / kWave];
     __shared__ float fred[2][kClassifyThreads / kWave];
@@ -754,7 +754,7 @@ __global__ __launch_bounds__(kClassifyThreads) void topk_classify_kernel(
     const int64_t nb = qp.L >> log2r;
     if (nb <= K) {
         if (c == 0) {
-            int32_t *out = idx + i * (int64_t)K;
+            int32_t *out = idx + i * (int64_t)ldi;
             for (int t = threadIdx.x; t < K; t += kClassifyThreads) out[t] = (t < nb) ? t : -1;
         }
         return;
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kClassifyThreads) void topk_classify_kernel(
 __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int nchunks,
-    int32_t *__restrict__ idx, const void *__restrict__ ws) {
+    int32_t *__restrict__ idx, int ldi, const void *__restrict__ ws) {
     __shared__ TopkShared S;
     __shared__ uint32_t ck[kMultiCandMax], ci[kMultiCandMax];
     __shared__ uint32_t bitmap[kBitmapWordsMax];
@@ -905,7 +905,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(
     const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
     if (nb <= K) return;                           // written by the classify kernel
-    int32_t *out = idx + i * (int64_t)K;
+    int32_t *out = idx + i * (int64_t)ldi;
     const int nch = (int)((nb + kClassifyChunk - 1) / kClassifyChunk);
     // per-chunk counts -> prefix offsets: lane c of wave 0 reads chunk c
     // (at most 64 chunks), then a wave scan
@@ -1024,7 +1024,7 @@ constexpr int kFusedMaxBlocks = 8192;       // measured: from 16K blocks the two
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
-    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx) {
+    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx, int ldi) {
     static_assert(KPT * kTopkThreads <= 32768 && kSample == 2 * kTopkThreads,
                   "row fits the registers; two sample values per thread");
     __shared__ TopkShared S;
@@ -1036,7 +1036,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
-    int32_t *out = idx + i * (int64_t)K;
+    int32_t *out = idx + i * (int64_t)ldi;
     if (nb <= K) {
         for (int t = threadIdx.x; t < K; t += kTopkThreads) out[t] = (t < nb) ? t : -1;
         return;
@@ -1241,7 +1241,7 @@ size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *recheck, int budget,
-                       int ratio, const qsa_batch &b, int32_t *idx, void *ws, hipStream_t st) {
+                       int ratio, const qsa_batch &b, int32_t *idx, int ldi, void *ws, hipStream_t st) {
     if (b.total_q == 0) return hipSuccess;
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int K = budget / ratio;
@@ -1273,7 +1273,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
                               recheck->q_dtype, recheck->kc_dtype, recheck->h_idx, recheck->d_idx};
         trace("topk_cert grid=%u K=%d ratio=%d lds_keys=%lld", grid.x, K, ratio, (long long)max_nb);
         hipLaunchKernelGGL(topk_cert_kernel, grid, dim3(kTopkThreads), lds, st, scores, ld,
-                           b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, cix,
+                           b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, ldi, cix,
                            part, nch);
         return hipGetLastError();
     }
@@ -1282,7 +1282,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
               (long long)max_nb);
 #define QSA_TOPK_FUSED(KPT)                                                                        \
     hipLaunchKernelGGL(topk_fused_kernel<KPT>, grid, dim3(kTopkThreads), 0, st, scores, ld,         \
-                       b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx)
+                       b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, ldi)
         static_assert(kFusedMaxBlocks == 8 * kTopkThreads, "fused instantiations cover the limit");
         if (max_nb <= 2 * kTopkThreads) QSA_TOPK_FUSED(2);
         else if (max_nb <= 4 * kTopkThreads) QSA_TOPK_FUSED(4);
@@ -1295,22 +1295,59 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
         trace("topk multi rows=%lld K=%d ratio=%d chunks=%d", (long long)b.total_q, K, ratio, chunks);
         hipLaunchKernelGGL(topk_classify_kernel, dim3((unsigned)chunks, (unsigned)b.total_q),
                            dim3(kClassifyThreads), 0, st, scores, ld, b.kv_offsets, b.q_offsets,
-                           b.num_seqs, log2r, K, chunks, idx, ws);
+                           b.num_seqs, log2r, K, chunks, idx, ldi, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(topk_finish_kernel, grid, dim3(kTopkThreads), 0, st, scores, ld,
-                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, chunks, idx, ws);
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, chunks, idx, ldi, ws);
         return hipGetLastError();
     }
     if (max_nb <= kLdsKeys) {
         trace("topk grid=%u K=%d ratio=%d lds_keys=%lld", grid.x, K, ratio, (long long)max_nb);
         hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTopkThreads), lds, st, scores, ld,
-                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx);
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, ldi);
     } else {
         trace("topk grid=%u K=%d ratio=%d streaming", grid.x, K, ratio);
         hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(kTopkThreads), 0, st, scores, ld,
-                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx);
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, ldi);
     }
+    return hipGetLastError();
+}
+
+// Recent window kept: row i of idx (stride ldi) holds the ascending top-K
+// selection, -1 padded; rewrite it in place as the ascending union of that
+// selection and the last min(w, nb) complete blocks, -1 padded to K + w
+// entries.  The selection's entries below the window stay where they are,
+// so one wave per row counts them and writes only what follows.
+__global__ __launch_bounds__(kWave) void topk_local_kernel(
+    const int64_t *__restrict__ kv_off, const int64_t *__restrict__ q_off, int num_seqs, int log2r,
+    int K, int w, int32_t *__restrict__ idx, int ldi) {
+    const int64_t i = blockIdx.x;
+    const int lane = threadIdx.x;
+    const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    const int64_t wv = nb < w ? nb : w;
+    const int64_t bound = nb - wv;                 // first block of the window
+    int32_t *row = idx + i * (int64_t)ldi;
+    uint32_t keep = 0;                             // entries in [0, bound): a prefix of the row
+    for (int j = lane; j < K; j += kWave) {
+        const int32_t e = row[j];
+        keep += (e >= 0 && (int64_t)e < bound) ? 1u : 0u;
+    }
+    keep = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(keep), 63);
+    for (int j = (int)keep + lane; j < K + w; j += kWave) {
+        const int64_t t = j - (int64_t)keep;
+        row[j] = t < wv ? (int32_t)(bound + t) : -1;
+    }
+}
+
+hipError_t launch_topk_local(int budget, int ratio, int local_blocks, const qsa_batch &b, int32_t *idx,
+                             int ldi, hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    const int log2r = __builtin_ctz((unsigned)ratio);
+    trace("topk_local rows=%lld K=%d w=%d", (long long)b.total_q, budget / ratio, local_blocks);
+    hipLaunchKernelGGL(topk_local_kernel, dim3((unsigned)b.total_q), dim3(kWave), 0, st, b.kv_offsets,
+                       b.q_offsets, b.num_seqs, log2r, budget / ratio, local_blocks, idx, ldi);
     return hipGetLastError();
 }
 

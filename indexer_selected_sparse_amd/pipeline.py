@@ -67,6 +67,7 @@ class DeviceProblem:
     decode: bool
     paging: Optional[Paging] = None        # K, V, k_idx, kc (+ scale) are page pools
     ing: Optional[IngestState] = None      # set by attach_ingest()
+    local_blocks: int = 0                  # recent complete blocks always kept (set_local_blocks())
 
     @property
     def blocks_per_query(self) -> int:
@@ -91,12 +92,13 @@ class DeviceProblem:
     def topk(self, certified: bool = False, stream=None) -> None:
         recheck = (self.q_idx, self.w, self.kc, self.kc_scale) if certified else None
         topk_blocks(self.scores, self.budget, self.ratio, self.batch, self.idx, recheck=recheck,
-                    ws=self.topk_ws if certified else self.topk_ws_canon, stream=stream)
+                    ws=self.topk_ws if certified else self.topk_ws_canon, stream=stream,
+                    local_blocks=self.local_blocks)
 
     def attend(self, stream=None) -> None:
         fn = sparse_attn_decode if self.decode else sparse_attn_prefill
-        fn(self.q, self.K, self.V, self.softmax_scale, self.idx, self.budget, self.ratio,
-           self.batch, self.out, self.attn_ws, stream=stream, paging=self.paging)
+        fn(self.q, self.K, self.V, self.softmax_scale, self.idx, self.budget + self.local_blocks * self.ratio,
+           self.ratio, self.batch, self.out, self.attn_ws, stream=stream, paging=self.paging)
 
     def step(self, mfma: bool = False, stream=None) -> None:
         """One pass of the hot path: [ingest ->] score -> top-k -> sparse attention."""
@@ -209,4 +211,16 @@ def attach_ingest(dp: DeviceProblem, wl, capacity: Optional[int] = None) -> Devi
     last = torch.tensor(np.cumsum(lens) - 1, dtype=torch.int64)
     dp.ing = IngestState(ring, wl.k_idx[last].to(dev).contiguous(), wl.K[last].to(dev).contiguous(),
                          wl.V[last].to(dev).contiguous(), status)
+    return dp
+
+
+def set_local_blocks(dp: DeviceProblem, local_blocks: int) -> DeviceProblem:
+    """Keep the last `local_blocks` complete blocks of every query besides its
+    top-k selection (qsa_topk_blocks_local): widens idx to budget/ratio +
+    local_blocks entries and sizes the attention workspace for it."""
+    dp.local_blocks = int(local_blocks)
+    K2 = dp.budget // dp.ratio + dp.local_blocks
+    dp.idx = torch.full((dp.idx.shape[0], K2), -7, dtype=torch.int32, device=dp.idx.device)
+    nws = attn_workspace_size(dp.q, dp.K, dp.V, dp.softmax_scale, K2 * dp.ratio, dp.ratio, dp.batch)
+    dp.attn_ws = torch.empty(nws, dtype=torch.uint8, device=dp.idx.device) if nws else None
     return dp

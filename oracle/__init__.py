@@ -212,6 +212,20 @@ def topk_row(scores, K: int) -> np.ndarray:
     return out
 
 
+def window_union(idx, nb: int, local_blocks: int) -> np.ndarray:
+    """A top-k row (ascending, -1 padded) with the last min(local_blocks, nb)
+    complete blocks added: the ascending union, -1 padded to
+    len(idx) + local_blocks entries (the second "llama.cpp vs Atlas"
+    report, section (d), phase 3, item 6: the most recent tokens are kept as
+    a union with the top-k set, here in whole blocks)."""
+    keep = {int(b) for b in idx if b >= 0}
+    keep |= set(range(max(nb - local_blocks, 0), nb))
+    out = np.full(len(idx) + local_blocks, -1, dtype=np.int32)
+    srt = sorted(keep)
+    out[:len(srt)] = srt
+    return out
+
+
 def token_set(idx, ratio: int, L: int) -> np.ndarray:
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     K = len(idx)

@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -82,6 +82,12 @@ def topk(scores=FAKE, ld=1024, recheck=None, budget=2048, ratio=4, b=None, idx=F
     b = b or _batch()
     return Q.lib().qsa_topk_blocks(P(scores), ld, None if recheck is None else ctypes.byref(recheck),
                                    budget, ratio, ctypes.byref(b), P(idx), P(ws), nws, None)
+
+
+def topk_local(local_blocks, budget=2048, ratio=4):
+    b = _batch()
+    return Q.lib().qsa_topk_blocks_local(P(FAKE), 1024, None, budget, ratio, local_blocks, ctypes.byref(b),
+                                         P(FAKE), None, 0, None)
 
 
 def decode(a=None, idx=FAKE, budget=2048, ratio=4, b=None, out=FAKE, ws=FAKE, nws=1 << 30):
@@ -231,6 +237,8 @@ CASES = [
     ("score fp4 without scales", lambda: score(ix=_ix(kc_dtype=Q.QSA_FP4_E2M1)), INV, "needs scales"),
     ("compress fp4 without scales", lambda: compress(kcdt=Q.QSA_FP4_E2M1), INV, "needs scales"),
     ("topk recheck fp4", lambda: topk(recheck=_ix(kc_dtype=Q.QSA_FP4_E2M1, kc_scale=FAKE)), UNS, "fp4"),
+    ("topk local negative", lambda: topk_local(-1), UNS, "local_blocks=-1"),
+    ("topk local too wide", lambda: topk_local(1537), UNS, "local_blocks=1537"),
     ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
     ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]

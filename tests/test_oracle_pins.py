@@ -470,3 +470,15 @@ def test_fp4_compress_error_bound_and_group_scales():
     err = np.abs(v - mean) / np.ldexp(1.0, X)
     assert np.all(err <= np.maximum(step / 2, np.where(y > 6, y - 6, 0)) + 1e-12)
     assert np.all(sc[:, 1] >= sc[:, 0] + 8)   # x1000 is about 2^10 larger
+
+
+# ------------------------------------------------- recent window kept
+@pytest.mark.parametrize("idx,nb,w,want", [
+    ([2, 5, 9, -1], 12, 3, [2, 5, 9, 10, 11, -1, -1]),          # disjoint: union adds 3
+    ([1, 10, 11, -1], 12, 2, [1, 10, 11, -1, -1, -1]),          # window already selected
+    ([3, 9, 10, -1], 12, 4, [3, 8, 9, 10, 11, -1, -1, -1]),     # partly selected
+    ([0, 1, 2, 3], 4, 8, [0, 1, 2, 3] + [-1] * 8),              # dense row, window past block 0
+    ([-1, -1], 0, 2, [-1, -1, -1, -1]),                          # no complete block yet
+])
+def test_window_union_hand_cases(idx, nb, w, want):
+    assert oracle.window_union(np.array(idx), nb, w).tolist() == want
