@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--local-blocks", type=int, default=0,
                    help="decode: also keep the last N complete blocks of every query (union with "
                         "its top-k selection, qsa_topk_blocks_local)")
+    p.add_argument("--token-pool", default=None, choices=["max", "mean"],
+                   help="decode: select blocks from pooled token scores (every token scored on its "
+                        "raw indexer key, each block reduced by max or mean) instead of compressed keys")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -268,6 +271,20 @@ def main():
     if args.ingest:
         pipeline.attach_ingest(base, wl)
         step_bytes += ingest_bytes(wl)
+    if args.token_pool:
+        if prefill:
+            print(json.dumps({"error": "--token-pool runs the decode workloads"}))
+            sys.exit(2)
+        from indexer_selected_sparse_amd import QSA_POOL_MAX, QSA_POOL_MEAN
+        pipeline.set_token_pool(base, QSA_POOL_MAX if args.token_pool == "max" else QSA_POOL_MEAN)
+        # the scan reads every raw key (and writes token scores) instead of the compressed keys
+        sp_ = spec
+        s_k = 2 if sp_.idx_dtype == "bf16" else 4
+        extra = sum(int(L) * sp_.d_idx * s_k for L in wl.visible_lengths()) - \
+            sum((int(L) // sp_.ratio) * sp_.d_idx * {"bf16": 2, "f32": 4, "e4m3": 1, "fp4": 0.5}[sp_.kc_dtype]
+                for L in wl.visible_lengths())
+        step_bytes += extra
+        score_bytes += extra
     if args.local_blocks:
         if prefill:
             print(json.dumps({"error": "--local-blocks runs the decode workloads"}))
@@ -390,6 +407,7 @@ def main():
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {}),
                    **({"local_blocks": args.local_blocks} if args.local_blocks else {}),
+                   **({"token_pool": args.token_pool} if args.token_pool else {}),
                    **({"ingest": "one token per sequence",
                        "ring_capacity": int(base.ing.ring.keys.shape[1])} if args.ingest else {})},
         "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn,
@@ -413,8 +431,8 @@ def main():
                                "avg_ms": t_score}
     else:
         attn_gbps = attn_bytes / (t_attn * 1e-3) / 1e9
-        traffic = None if (args.paged or args.kc_dtype or args.budget or args.local_blocks) \
-            else recorded_traffic(spec.name)
+        traffic = None if (args.paged or args.kc_dtype or args.budget or args.local_blocks
+                           or args.token_pool) else recorded_traffic(spec.name)
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                            "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",

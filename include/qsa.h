@@ -259,6 +259,27 @@ qsa_status qsa_topk_blocks_local(const float *scores, int64_t ld_scores, const q
                                  int32_t budget, int32_t ratio, int32_t local_blocks, const qsa_batch *b,
                                  int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
+/* Two-stage selection from token scores: the second "vLLM vs Atlas" report
+ * (section (a)3, the block-pooling refinement) scores every token, reduces
+ * each block of `ratio` tokens to one score and takes the block top-k on
+ * those.  Token scores come from qsa_index_score with ratio 1 on the raw
+ * indexer keys (pass k_idx as kc and kv_offsets as blk_offsets); this call
+ * pools them, for every query i and complete block b < floor(L_i/ratio):
+ *   QSA_POOL_MAX:  blk[i,b] = max_j tok[i, b*ratio + j]
+ *   QSA_POOL_MEAN: blk[i,b] = (sum_j tok[i, b*ratio + j], fp32 left to right,
+ *                  from +0) * (1/ratio)
+ * then qsa_topk_blocks on blk selects as usual.  The report names no
+ * reduction; max is the reading that keeps a block with one strong token.
+ *  tok: device f32 [total_q, ld_tok], ld_tok >= max_kv_len; blk: device f32
+ *  [total_q, ld_blk], ld_blk >= ceil(max_kv_len/ratio); entries past
+ *  floor(L_i/ratio) are left untouched.
+ * Errors: INVALID_ARGUMENT (pointers, leading dimensions, mode),
+ * UNSUPPORTED (ratio), HIP. */
+#define QSA_POOL_MAX 0
+#define QSA_POOL_MEAN 1
+qsa_status qsa_pool_scores(const float *tok, int64_t ld_tok, int32_t ratio, int32_t mode,
+                           const qsa_batch *b, float *blk, int64_t ld_blk, void *stream);
+
 /* ---- Paged caches.  The serving engines on the pages keep K/V and the
  * indexer cache in fixed-size pages addressed through a per-sequence block
  * table (vLLM report (a)1 and (a)6: the indexer K cache and the selection go

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_HIP = range(5)
 QSA_F32, QSA_BF16, QSA_FP8_E4M3, QSA_FP4_E2M1 = 0, 1, 2, 3
 QSA_SCORE_CANONICAL, QSA_SCORE_MFMA = 0, 1
+QSA_POOL_MAX, QSA_POOL_MEAN = 0, 1
 
 EXPORTS = (
     "qsa_inert_bound", "qsa_last_error", "qsa_version", "qsa_abi_version",
@@ -32,6 +33,7 @@ EXPORTS = (
     "qsa_attn_workspace_size", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
     "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
+    "qsa_pool_scores",
 )
 
 # per-sequence codes written by qsa_ingest / qsa_ring_rewind
@@ -118,6 +120,8 @@ def lib():
             f.argtypes = [P, P, i32, i32, P, P, P, sz, P, P]
         L.qsa_topk_blocks_local.restype = i32
         L.qsa_topk_blocks_local.argtypes = [P, i64, P, i32, i32, i32, P, P, P, sz, P]
+        L.qsa_pool_scores.restype = i32
+        L.qsa_pool_scores.argtypes = [P, i64, i32, i32, P, P, i64, P]
         L.qsa_ingest.restype = i32
         L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
         L.qsa_ring_rewind.restype = i32
@@ -413,3 +417,14 @@ def ring_rewind(batch: Batch, ratio: int, ring: KeyRing, status: Optional[torch.
         _dev(status, "status")
     b, rg = batch._c(), ring._c()
     _check(lib().qsa_ring_rewind(ctypes.byref(b), ratio, ctypes.byref(rg), _ptr(status), _stream(stream)))
+
+
+def pool_scores(tok: torch.Tensor, ratio: int, mode: int, batch: Batch, blk: torch.Tensor,
+                stream=None) -> None:
+    """qsa_pool_scores: block scores blk [total_q, >= ceil(max_kv_len/ratio)]
+    from token scores tok [total_q, >= max_kv_len] (QSA_POOL_MAX or _MEAN)."""
+    _dev(tok, "tok")
+    _dev(blk, "blk")
+    b = batch._c()
+    _check(lib().qsa_pool_scores(_ptr(tok), tok.shape[1], ratio, mode, ctypes.byref(b), _ptr(blk),
+                                 blk.shape[1], _stream(stream)))

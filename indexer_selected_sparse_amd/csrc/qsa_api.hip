@@ -423,4 +423,24 @@ qsa_status qsa_ring_rewind(const qsa_batch *b, int32_t ratio, const qsa_key_ring
                       "qsa_ring_rewind launch");
 }
 
+qsa_status qsa_pool_scores(const float *tok, int64_t ld_tok, int32_t ratio, int32_t mode,
+                           const qsa_batch *b, float *blk, int64_t ld_blk, void *stream) {
+    qsa_status s = check_batch(b, false);
+    if (s == QSA_OK) s = check_ratio(ratio);
+    if (s == QSA_OK) s = check_rows(b, ratio);
+    if (s != QSA_OK) return s;
+    if (!tok || !blk) return fail(QSA_ERR_INVALID_ARGUMENT, "tok/blk must not be NULL");
+    if (mode != QSA_POOL_MAX && mode != QSA_POOL_MEAN)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "mode=%d must be QSA_POOL_MAX or QSA_POOL_MEAN", mode);
+    if (ld_tok < b->max_kv_len || ld_tok < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_tok=%lld must be >= max_kv_len=%lld", (long long)ld_tok,
+                    (long long)b->max_kv_len);
+    const int64_t need = (b->max_kv_len + ratio - 1) / ratio;
+    if (ld_blk < need || ld_blk < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_blk=%lld must be >= ceil(max_kv_len/ratio)=%lld",
+                    (long long)ld_blk, (long long)need);
+    return hip_status(launch_pool_scores(tok, ld_tok, ratio, mode, *b, blk, ld_blk, (hipStream_t)stream),
+                      "qsa_pool_scores launch");
+}
+
 }  // extern "C"

@@ -23,6 +23,10 @@ hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio,
 hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
                                   float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st);
 
+// Block pooling of token scores (QSA_POOL_MAX / QSA_POOL_MEAN).
+hipError_t launch_pool_scores(const float *tok, int64_t ld_tok, int ratio, int mode, const qsa_batch &b,
+                              float *blk, int64_t ld_blk, hipStream_t st);
+
 // Matrix-core indexer scores (bf16 only), prefill.
 hipError_t launch_score_mfma(const qsa_indexer &ix, int ratio, const qsa_batch &b, float *scores,
                              int64_t ld, hipStream_t st);

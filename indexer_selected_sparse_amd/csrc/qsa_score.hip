@@ -444,6 +444,40 @@ hipError_t dispatch_d(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 
 }  // namespace
 
+// Block pooling of token scores (max, or the fp32 mean in token order).
+template <int MODE>
+__global__ __launch_bounds__(kScoreThreads) void pool_scores_kernel(
+    const float *__restrict__ tok, int64_t ld_tok, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ q_off, int num_seqs, int log2r, float inv_ratio, float *__restrict__ blk,
+    int64_t ld_blk) {
+    const int64_t i = blockIdx.y;
+    const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    const int64_t b = (int64_t)blockIdx.x * kScoreThreads + threadIdx.x;
+    if (b >= nb) return;
+    const float *t = tok + i * ld_tok + (b << log2r);
+    float acc = MODE == QSA_POOL_MAX ? t[0] : 0.0f + t[0];
+    for (int j = 1; j < (1 << log2r); ++j) acc = MODE == QSA_POOL_MAX ? fmaxf(acc, t[j]) : acc + t[j];
+    blk[i * ld_blk + b] = MODE == QSA_POOL_MAX ? acc : acc * inv_ratio;
+}
+
+hipError_t launch_pool_scores(const float *tok, int64_t ld_tok, int ratio, int mode, const qsa_batch &b,
+                              float *blk, int64_t ld_blk, hipStream_t st) {
+    const int log2r = __builtin_ctz((unsigned)ratio);
+    const int64_t max_nb = b.max_kv_len >> log2r;
+    if (b.total_q == 0 || max_nb == 0) return hipSuccess;
+    dim3 grid((unsigned)((max_nb + kScoreThreads - 1) / kScoreThreads), (unsigned)b.total_q);
+    const float inv = 1.0f / (float)ratio;
+    trace("pool_scores grid=(%u,%u) ratio=%d mode=%d", grid.x, grid.y, ratio, mode);
+    if (mode == QSA_POOL_MAX)
+        hipLaunchKernelGGL(pool_scores_kernel<QSA_POOL_MAX>, grid, dim3(kScoreThreads), 0, st, tok, ld_tok,
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, inv, blk, ld_blk);
+    else
+        hipLaunchKernelGGL(pool_scores_kernel<QSA_POOL_MEAN>, grid, dim3(kScoreThreads), 0, st, tok, ld_tok,
+                           b.kv_offsets, b.q_offsets, b.num_seqs, log2r, inv, blk, ld_blk);
+    return hipGetLastError();
+}
+
 hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
                                   float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st) {
     const PageMap pm = page_map(pg);

@@ -13,9 +13,9 @@ import torch
 
 import numpy as np
 
-from . import (INGEST_OK, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch, KeyRing, Paging,
-               attn_workspace_size, compress_keys, index_score, ingest, sparse_attn_decode,
-               sparse_attn_prefill, topk_blocks, topk_workspace_size)
+from . import (INGEST_OK, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch,
+               KeyRing, Paging, attn_workspace_size, compress_keys, index_score, ingest, pool_scores,
+               sparse_attn_decode, sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
              "fp4": torch.float4_e2m1fn_x2}
@@ -68,6 +68,8 @@ class DeviceProblem:
     paging: Optional[Paging] = None        # K, V, k_idx, kc (+ scale) are page pools
     ing: Optional[IngestState] = None      # set by attach_ingest()
     local_blocks: int = 0                  # recent complete blocks always kept (set_local_blocks())
+    token_pool: Optional[int] = None       # QSA_POOL_*: block scores pooled from token scores
+    tok_scores: Optional[torch.Tensor] = None
 
     @property
     def blocks_per_query(self) -> int:
@@ -86,6 +88,16 @@ class DeviceProblem:
                paging=self.paging)
 
     def score(self, mode: int = QSA_SCORE_CANONICAL, stream=None) -> None:
+        if self.token_pool is not None:
+            # every token scored on its raw key (ratio 1: kc rows are k_idx rows),
+            # then each block of `ratio` tokens pooled
+            bt = self.batch
+            tb = Batch(bt.kv_offsets, bt.kv_offsets, bt.q_offsets, bt.total_q, bt.max_kv_len,
+                       bt.max_q_per_seq)
+            index_score(self.q_idx, self.w, self.k_idx, None, 1, tb, self.tok_scores, stream=stream,
+                        paging=self.paging)
+            pool_scores(self.tok_scores, self.ratio, self.token_pool, bt, self.scores, stream=stream)
+            return
         index_score(self.q_idx, self.w, self.kc, self.kc_scale, self.ratio, self.batch, self.scores,
                     mode=mode, stream=stream, paging=self.paging)
 
@@ -223,4 +235,17 @@ def set_local_blocks(dp: DeviceProblem, local_blocks: int) -> DeviceProblem:
     dp.idx = torch.full((dp.idx.shape[0], K2), -7, dtype=torch.int32, device=dp.idx.device)
     nws = attn_workspace_size(dp.q, dp.K, dp.V, dp.softmax_scale, K2 * dp.ratio, dp.ratio, dp.batch)
     dp.attn_ws = torch.empty(nws, dtype=torch.uint8, device=dp.idx.device) if nws else None
+    return dp
+
+
+def set_token_pool(dp: DeviceProblem, mode: int) -> DeviceProblem:
+    """Select blocks from pooled token scores instead of compressed keys
+    (canonical token scores on the raw indexer keys, then qsa_pool_scores
+    with QSA_POOL_MAX or QSA_POOL_MEAN, then the usual block top-k)."""
+    if mode not in (QSA_POOL_MAX, QSA_POOL_MEAN):
+        raise ValueError("mode must be QSA_POOL_MAX or QSA_POOL_MEAN")
+    dp.token_pool = mode
+    rows = dp.scores.shape[0]
+    dp.tok_scores = torch.zeros((rows, max(1, dp.batch.max_kv_len)), dtype=torch.float32,
+                                device=dp.scores.device)
     return dp

@@ -205,6 +205,27 @@ def score_row(q, w, kc_vals, kc_scale=None) -> np.ndarray:
     return out
 
 
+def pool_scores(tok, ratio: int, mode: str) -> np.ndarray:
+    """Block scores from token scores (the second "vLLM vs Atlas" report,
+    section (a)3, block pooling): one per complete block, "max" of its
+    tokens' scores, or "mean": their fp32 sum left to right from +0, times
+    1/ratio (exact for a power of two)."""
+    tok = _f32(tok)
+    nb = len(tok) // ratio
+    out = np.zeros(nb, dtype=np.float32)
+    inv = np.float32(1.0) / np.float32(ratio)
+    for b in range(nb):
+        seg = tok[b * ratio:(b + 1) * ratio]
+        if mode == "max":
+            out[b] = max(seg)
+        else:
+            acc = np.float32(0.0)
+            for v in seg:
+                acc = np.float32(acc + v)
+            out[b] = np.float32(acc * inv)
+    return out
+
+
 def topk_row(scores, K: int) -> np.ndarray:
     s = _f32(scores)
     out = np.zeros(K, dtype=np.int32)

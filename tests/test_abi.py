@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -239,6 +239,10 @@ CASES = [
     ("topk recheck fp4", lambda: topk(recheck=_ix(kc_dtype=Q.QSA_FP4_E2M1, kc_scale=FAKE)), UNS, "fp4"),
     ("topk local negative", lambda: topk_local(-1), UNS, "local_blocks=-1"),
     ("topk local too wide", lambda: topk_local(1537), UNS, "local_blocks=1537"),
+    ("pool bad mode", lambda: Q.lib().qsa_pool_scores(P(FAKE), 4096, 4, 2, ctypes.byref(_batch()), P(FAKE),
+                                                     1024, None), INV, "mode=2"),
+    ("pool ld_tok small", lambda: Q.lib().qsa_pool_scores(P(FAKE), 4095, 4, 0, ctypes.byref(_batch()), P(FAKE),
+                                                          1024, None), INV, "ld_tok=4095"),
     ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
     ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]

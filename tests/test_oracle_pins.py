@@ -482,3 +482,14 @@ def test_fp4_compress_error_bound_and_group_scales():
 ])
 def test_window_union_hand_cases(idx, nb, w, want):
     assert oracle.window_union(np.array(idx), nb, w).tolist() == want
+
+
+# ------------------------------------------- pooled token scores
+def test_pool_scores_hand_cases():
+    tok = np.array([1, 5, 2, 0, 0.5, 0.25, 0.125, 0.0625, 9, 9], dtype=np.float32)
+    assert oracle.pool_scores(tok, 4, "max").tolist() == [5.0, 0.5]          # the tail 9, 9 is no block
+    assert oracle.pool_scores(tok, 4, "mean").tolist() == [2.0, 0.234375]
+    assert oracle.pool_scores(tok, 1, "max").tolist() == tok.tolist()         # ratio 1 is the identity
+    # fp32 order: 2^24 + 1 + 1 loses both ones left to right, mean then 2^22
+    big = np.array([2.0 ** 24, 1, 1, 0], dtype=np.float32)
+    assert oracle.pool_scores(big, 4, "mean").tolist() == [2.0 ** 22]
