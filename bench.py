@@ -80,6 +80,12 @@ def parse():
     p.add_argument("--token-pool", default=None, choices=["max", "mean"],
                    help="decode: select blocks from pooled token scores (every token scored on its "
                         "raw indexer key, each block reduced by max or mean) instead of compressed keys")
+    p.add_argument("--layers", type=int, default=1,
+                   help="decode: one step runs this many attention layers (layer 0 is the workload; "
+                        "the others draw their own K, V, q on the device)")
+    p.add_argument("--full-every", type=int, default=1,
+                   help="with --layers: layer l has its own indexer when l %% F == 0; the others reuse "
+                        "the previous full layer's selection")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -302,7 +308,7 @@ def main():
     if prefill:
         R = args.replicas or 1      # the score matrix alone (336 MB) exceeds the LLC
     else:
-        R = args.replicas or max(2, math.ceil(2 * 256e6 / step_bytes) + 1)
+        R = args.replicas or max(2, math.ceil(2 * 256e6 / (step_bytes * max(1, args.layers))) + 1)
     reps = [base]
     for _ in range(R - 1):
         c = pipeline.DeviceProblem(**{**base.__dict__})
@@ -317,6 +323,37 @@ def main():
                 base.ing.status.clone())
         reps.append(c)
     torch.cuda.synchronize()
+
+    n_layers = max(1, args.layers)
+    stacks = None
+    if n_layers > 1:
+        if prefill or args.ingest or args.token_pool or args.local_blocks or args.no_graph:
+            print(json.dumps({"error": "--layers runs the plain decode step, replayed from a graph"}))
+            sys.exit(2)
+        gen = torch.Generator(device=dev).manual_seed(spec.seed + 101)
+
+        def fresh(t):
+            return torch.randn(t.shape, generator=gen, device=dev, dtype=torch.float32).to(t.dtype)
+
+        def layer_of(p, l):
+            c = pipeline.DeviceProblem(**{**p.__dict__})
+            c.K, c.V, c.q = fresh(p.K), fresh(p.V), fresh(p.q)
+            c.out = torch.zeros_like(p.out)
+            if l % args.full_every == 0:
+                c.q_idx, c.k_idx = fresh(p.q_idx), fresh(p.k_idx)
+                c.w = torch.rand(p.w.shape, generator=gen, device=dev)
+                c.kc = p.kc.clone()
+                c.kc_scale = None if p.kc_scale is None else p.kc_scale.clone()
+                c.scores = torch.zeros_like(p.scores)
+                c.idx = p.idx.clone()
+                c.compress()
+            return c
+
+        stacks = [pipeline.LayerStack([p] + [layer_of(p, l) for l in range(1, n_layers)], args.full_every)
+                  for p in reps]
+        torch.cuda.synchronize()
+        n_full = sum(stacks[0].full)
+        step_bytes = n_full * score_bytes + n_layers * attn_bytes + (step_bytes - score_bytes - attn_bytes)
 
     def ingest(p):
         if p.ing is not None:
@@ -376,13 +413,22 @@ def main():
                 p.attend()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for p in reps:
+        if stacks is not None:
+            with torch.cuda.stream(side):
+                for st_ in stacks:
+                    st_.step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+        for k_, p in enumerate(reps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                ingest(p)
-                score(p)
-                topk(p)
-                p.attend()
+                if stacks is not None:
+                    stacks[k_].step()
+                else:
+                    ingest(p)
+                    score(p)
+                    topk(p)
+                    p.attend()
             graphs.append(g)
         for s_ in range(args.warmup):
             graphs[s_ % R].replay()
@@ -394,18 +440,20 @@ def main():
         graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_step = graph_ms_step if graphs else eager_ms_step
 
-    qps = wl.total_q / (ms_step / 1e3)
+    qps = wl.total_q * n_layers / (ms_step / 1e3)
     rec = {
         "metric": "sparse-attn decode queries/s + achieved HBM GB/s (% roofline) at 32K-128K ctx",
         "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{spec.name}", "num_seqs": wl.num_seqs, "queries_per_step": wl.total_q,
+        "config": {"workload": f"{spec.name}", "num_seqs": wl.num_seqs, "queries_per_step": wl.total_q * n_layers,
                    "context": (f"U[{spec.len_range[0]},{spec.len_range[1]}]" if spec.len_range
                                else str(wl.lens[0])),
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {}),
+                   **({"layers": n_layers, "full_every": args.full_every,
+                       "layers_with_own_indexer": sum(stacks[0].full)} if stacks is not None else {}),
                    **({"local_blocks": args.local_blocks} if args.local_blocks else {}),
                    **({"token_pool": args.token_pool} if args.token_pool else {}),
                    **({"ingest": "one token per sequence",

@@ -6,8 +6,8 @@ kernels.  Inputs are the varlen-packed tensors described in include/qsa.h.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
-from typing import Optional
+from dataclasses import dataclass, field
+from typing import List, Optional
 
 import torch
 
@@ -249,3 +249,35 @@ def set_token_pool(dp: DeviceProblem, mode: int) -> DeviceProblem:
     dp.tok_scores = torch.zeros((rows, max(1, dp.batch.max_kv_len)), dtype=torch.float32,
                                 device=dp.scores.device)
     return dp
+
+
+@dataclass
+class LayerStack:
+    """A decode step over several attention layers whose indexers are either
+    full or shared (the first "llama.cpp vs Atlas" report, section (a)3: a
+    shared layer reuses the top-k of the previous full layer).  Layer l is
+    full when l % full_every == 0; a shared layer skips scoring and top-k and
+    attends its own K/V with the selection of the last full layer before it."""
+    layers: List[DeviceProblem]
+    full_every: int = 1
+    full: List[bool] = field(default_factory=list)
+
+    def __post_init__(self):
+        if self.full_every < 1:
+            raise ValueError("full_every must be >= 1")
+        self.full = [l % self.full_every == 0 for l in range(len(self.layers))]
+        src = None
+        for dp, f in zip(self.layers, self.full):
+            if f:
+                src = dp
+            else:   # a shared layer reads (and never writes) the full layer's selection
+                if dp.idx.shape != src.idx.shape:
+                    raise ValueError("shared layers need the full layer's selection width")
+                dp.idx = src.idx
+
+    def step(self, stream=None) -> None:
+        for dp, f in zip(self.layers, self.full):
+            if f:
+                dp.score(stream=stream)
+                dp.topk(stream=stream)
+            dp.attend(stream=stream)
