@@ -1025,11 +1025,11 @@ template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx, int ldi) {
-    static_assert(KPT * kTopkThreads <= 32768 && kSample == 2 * kTopkThreads,
-                  "row fits the registers; two sample values per thread");
+    static_assert(KPT <= 16 && KPT * kTopkThreads / 32 <= kTopkThreads && kSample == 2 * kTopkThreads,
+                  "row fits the registers; one bitmap word per thread; two sample values per thread");
     __shared__ TopkShared S;
-    __shared__ uint32_t ck[kMultiCandMax], ci[kMultiCandMax];
-    __shared__ uint32_t bitmap[KPT * kTopkThreads / 32];
+    __shared__ uint32_t bitmap[KPT * kTopkThreads / 32];   // selected blocks
+    __shared__ uint32_t tbits[KPT * kTopkThreads / 32];    // blocks whose key equals the threshold
     __shared__ uint32_t wcnt[2][kTopkWaves];
     __shared__ float fred[2][kTopkWaves];
     __shared__ int sel[2];
@@ -1063,7 +1063,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(
     }
     const int nwords = (int)((nb + 31) / 32);
     for (int t = threadIdx.x; t < kSample; t += kTopkThreads) S.hist[t] = 0;
-    for (int w = threadIdx.x; w < nwords; w += kTopkThreads) bitmap[w] = 0u;
+    for (int w = threadIdx.x; w < nwords; w += kTopkThreads) { bitmap[w] = 0u; tbits[w] = 0u; }
+
     // sample range
     float vmin = INFINITY, vmax = -INFINITY;
 #pragma unroll
@@ -1124,101 +1125,135 @@ __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(
     }
     __syncthreads();
     const int jH = sel[0], jL = sel[1];
-    // count the split: in = bin > jH, candidate = jL <= bin <= jH
-    uint32_t n_in = 0, n_cd = 0;
+    // Classify every element once (in: above the bracket; candidate: inside
+    // it); the counts and the candidates' key range come from one reduction.
+    uint32_t kx[KPT];
+    uint32_t cls = 0;                              // bit u: candidate; bit 16 + u: in
+    uint32_t n_in = 0, n_cd = 0, cmin = 0xffffffffu, cmax = 0u;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
         const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
         const bool ok = b < nb;
         const int bn = bin_of(x[u]);
-        n_in += (uint32_t)__builtin_popcountll(__ballot(ok && bn > jH));
-        n_cd += (uint32_t)__builtin_popcountll(__ballot(ok && bn >= jL && bn <= jH));
+        kx[u] = order_key(x[u]);
+        if (ok && bn > jH) {
+            cls |= 1u << (16 + u);
+            ++n_in;
+        } else if (ok && bn >= jL) {
+            cls |= 1u << u;
+            ++n_cd;
+            cmin = min(cmin, kx[u]);
+            cmax = max(cmax, kx[u]);
+        }
     }
-    if (lane == 0) { wcnt[0][wave] = n_in; wcnt[1][wave] = n_cd; }
+    {
+        const uint32_t w_in = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n_in), kWave - 1);
+        const uint32_t w_cd = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n_cd), kWave - 1);
+        const uint32_t w_mn = wave_min_u32(cmin), w_mx = wave_max_u32(cmax);
+        if (lane == 0) { wcnt[0][wave] = w_in; wcnt[1][wave] = w_cd; S.wmin[wave] = w_mn; S.wmax[wave] = w_mx; }
+    }
     __syncthreads();
-    uint32_t off_cd = 0, tot_in = 0, tot_cd = 0;
+    uint32_t tot_in = 0, tot_cd = 0;
+    cmin = 0xffffffffu;
+    cmax = 0u;
 #pragma unroll
     for (int w = 0; w < kTopkWaves; ++w) {
-        off_cd += w < wave ? wcnt[1][w] : 0u;
         tot_in += wcnt[0][w];
         tot_cd += wcnt[1][w];
+        cmin = min(cmin, S.wmin[w]);
+        cmax = max(cmax, S.wmax[w]);
     }
-    if (tot_in > (uint32_t)K || tot_in + tot_cd < (uint32_t)K || tot_cd > (uint32_t)kMultiCandMax) {
+    if (tot_in > (uint32_t)K || tot_in + tot_cd < (uint32_t)K) {
         // the bracket missed: exact select over the whole row
+        __syncthreads();                           // every wave has read S.wmin / S.wmax
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int64_t b = (int64_t)u * kTopkThreads + threadIdx.x;
             if (b < nb) {
-                const uint32_t k = order_key(x[u]);
-                kmin = min(kmin, k);
-                kmax = max(kmax, k);
+                kmin = min(kmin, kx[u]);
+                kmax = max(kmax, kx[u]);
             }
         }
         wg_minmax(kmin, kmax, S);
         select_row(GlobalKey{row}, nb, K, kmin, kmax, out, S);
         return;
     }
-    // in blocks -> bitmap; candidates -> (key, block) lists in LDS
-    uint32_t cmin = 0xffffffffu, cmax = 0u;
+    // The threshold: the need-th largest candidate key, by MSB-first radix
+    // digits over the candidates held in registers (as radix_select does
+    // over a list).
+    const uint32_t need0 = (uint32_t)K - tot_in;
+    uint32_t T = 0xffffffffu, need_eq = 0, total_eq = 0;
+    if (need0 > 0) {
+        const uint32_t diff = cmin ^ cmax;
+        if (diff == 0) {
+            T = cmin;
+            need_eq = need0;
+            total_eq = tot_cd;
+        } else {
+            const int hi_bit = 31 - __builtin_clz(diff);
+            uint32_t prefix = hi_bit == 31 ? 0u : (cmax & ~((2u << hi_bit) - 1u));
+            uint32_t need = need0;
+            int lo_bit = hi_bit + 1;
+            while (lo_bit > 0) {
+                const int width = lo_bit >= kDigitBits ? kDigitBits : lo_bit;
+                const int shift = lo_bit - width;
+                const uint32_t mask_hi = lo_bit >= 32 ? 0u : ~((1u << lo_bit) - 1u);
+                for (int t = threadIdx.x; t < kBins; t += kTopkThreads) S.hist[t] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int u = 0; u < KPT; ++u)
+                    if (((cls >> u) & 1u) && (kx[u] & mask_hi) == prefix)
+                        atomicAdd(&S.hist[(kx[u] >> shift) & ((1u << width) - 1u)], 1u);
+                __syncthreads();
+                uint32_t above;
+                const int d = find_bin(1 << width, need, S, above);
+                total_eq = S.hist[d];
+                prefix |= (uint32_t)d << shift;
+                need -= above;
+                lo_bit = shift;
+                __syncthreads();
+            }
+            T = prefix;
+            need_eq = need;
+        }
+    }
+    // Mark: in blocks and candidates above T are selected; candidates equal
+    // to T are all selected when all of them are needed, else they go to
+    // the tie bitmap, where the lowest block indices win.
+    const bool split_ties = need0 > 0 && need_eq < total_eq;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
         const uint32_t b = (uint32_t)(u * kTopkThreads + threadIdx.x);
-        const bool ok = (int64_t)b < nb;
-        const int bn = bin_of(x[u]);
-        if (ok && bn > jH) atomicOr(&bitmap[b >> 5], 1u << (b & 31));
-        const bool cd = ok && bn >= jL && bn <= jH;
-        const uint64_t mc = __ballot(cd);
-        if (cd) {
-            const uint32_t pos = off_cd + lanes_below(mc);
-            const uint32_t k = order_key(x[u]);
-            ck[pos] = k;
-            ci[pos] = b;
-            cmin = min(cmin, k);
-            cmax = max(cmax, k);
-        }
-        off_cd += (uint32_t)__builtin_popcountll(mc);
-    }
-    wg_minmax(cmin, cmax, S);                      // barriers publish ck, ci, bitmap
-    const uint32_t need = (uint32_t)K - tot_in;
-    if (need > 0) {
-        uint32_t need_eq, total_eq;
-        const uint32_t T = radix_select(LdsKey{ck}, (int64_t)tot_cd, need, cmin, cmax, S, need_eq,
-                                        total_eq);
-        const bool all_eq = need_eq >= total_eq;
-        for (uint32_t j = threadIdx.x; j < tot_cd; j += kTopkThreads) {
-            const uint32_t k = ck[j];
-            bool take = k > T;
-            if (k == T) {
-                if (all_eq) {
-                    take = true;
-                } else {
-                    // ties at T go to the lower block index
-                    const uint32_t me = ci[j];
-                    uint32_t rank = 0;
-                    for (uint32_t q = 0; q < tot_cd; ++q) rank += (ck[q] == T && ci[q] < me) ? 1u : 0u;
-                    take = rank < need_eq;
-                }
-            }
-            if (take) atomicOr(&bitmap[ci[j] >> 5], 1u << (ci[j] & 31));
+        const uint32_t bit = 1u << (b & 31);
+        if ((cls >> (16 + u)) & 1u) {
+            atomicOr(&bitmap[b >> 5], bit);
+        } else if (need0 > 0 && ((cls >> u) & 1u)) {
+            if (kx[u] > T) atomicOr(&bitmap[b >> 5], bit);
+            else if (kx[u] == T) atomicOr(split_ties ? &tbits[b >> 5] : &bitmap[b >> 5], bit);
         }
     }
     __syncthreads();
-    // ascending output: per-thread runs of words, popcounts scanned
-    const int per = (nwords + kTopkThreads - 1) / kTopkThreads;
-    const int w0 = threadIdx.x * per;
-    uint32_t cnt = 0;
-    for (int w = w0; w < w0 + per && w < nwords; ++w) cnt += (uint32_t)__builtin_popcount(bitmap[w]);
-    uint32_t tot;
-    uint32_t pos = wg_scan(cnt, S, tot);
-    for (int w = w0; w < w0 + per && w < nwords; ++w) {
-        uint32_t m = bitmap[w];
-        while (m) {
-            const int bit = __builtin_ctz(m);
-            m &= m - 1;
-            if (pos < (uint32_t)K) out[pos] = w * 32 + bit;
-            ++pos;
+    // Ascending output: thread t owns bitmap word t.
+    const int w = threadIdx.x;
+    uint32_t word = w < nwords ? bitmap[w] : 0u;
+    if (split_ties) {
+        uint32_t tm = w < nwords ? tbits[w] : 0u;
+        uint32_t tall;
+        uint32_t r = wg_scan((uint32_t)__builtin_popcount(tm), S, tall);   // ties in lower words
+        while (tm && r < need_eq) {
+            word |= 1u << __builtin_ctz(tm);
+            tm &= tm - 1;
+            ++r;
         }
+    }
+    uint32_t tot;
+    uint32_t pos = wg_scan((uint32_t)__builtin_popcount(word), S, tot);
+    while (word) {
+        const int bit = __builtin_ctz(word);
+        word &= word - 1;
+        if (pos < (uint32_t)K) out[pos] = w * 32 + bit;
+        ++pos;
     }
 }
 
