@@ -228,3 +228,13 @@ def test_graph_replays_match_eager():
         assert torch.equal(dp.out, eager[2]), f"replay {rep}: out differs from the eager step"
         dp.step()                       # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("budget", [2048, 8192])
+def test_maximum_row_length(budget):
+    # the longest row the library accepts: 131072 complete blocks (plus a
+    # ragged tail of 3 tokens), with K = 512 and K = 2048
+    sp = dataclasses.replace(W.LONG_DECODE, hq=8, hkv=1, budget=budget)
+    wl = W.make(sp, lens=[4 * 131072 + 3], seed=91)
+    _print(f"[parity] max row: L={wl.lens[0]} budget={budget}")
+    full_check(wl)
