@@ -369,8 +369,9 @@ typedef struct qsa_kv_append {
                                      longer holds (rollback deeper than the ring, or skipped
                                      positions); that block's compressed key is NOT written */
 #define QSA_INGEST_BAD_SLOT 2     /* slots[s] outside [0, num_slots): nothing written */
-#define QSA_INGEST_TOO_LONG 3     /* N_s beyond the block table (paged), n_s > N_s, or
-                                     n_s > batch.max_q_per_seq: nothing written */
+#define QSA_INGEST_TOO_LONG 3     /* N_s beyond the block table (paged), n_s > N_s, or more
+                                     new tokens than the launch was sized for (the caller
+                                     must keep n_s <= batch.max_q_per_seq): nothing written */
 #define QSA_REWIND_DECLINED 4     /* qsa_ring_rewind only: see there */
 
 /* Append the n_s new tokens of every sequence.  For each new position p
