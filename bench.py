@@ -83,6 +83,9 @@ def parse():
     p.add_argument("--layers", type=int, default=1,
                    help="decode: one step runs this many attention layers (layer 0 is the workload; "
                         "the others draw their own K, V, q on the device)")
+    p.add_argument("--unfused-layers", action="store_true",
+                   help="with --layers: one attention launch per layer instead of one per full layer "
+                        "and its shared layers")
     p.add_argument("--full-every", type=int, default=1,
                    help="with --layers: layer l has its own indexer when l %% F == 0; the others reuse "
                         "the previous full layer's selection")
@@ -349,7 +352,8 @@ def main():
                 c.compress()
             return c
 
-        stacks = [pipeline.LayerStack([p] + [layer_of(p, l) for l in range(1, n_layers)], args.full_every)
+        stacks = [pipeline.LayerStack([p] + [layer_of(p, l) for l in range(1, n_layers)], args.full_every,
+                                      fused=not args.unfused_layers)
                   for p in reps]
         torch.cuda.synchronize()
         n_full = sum(stacks[0].full)
@@ -452,7 +456,7 @@ def main():
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {}),
-                   **({"layers": n_layers, "full_every": args.full_every,
+                   **({"layers": n_layers, "full_every": args.full_every, "fused_layers": not args.unfused_layers,
                        "layers_with_own_indexer": sum(stacks[0].full)} if stacks is not None else {}),
                    **({"local_blocks": args.local_blocks} if args.local_blocks else {}),
                    **({"token_pool": args.token_pool} if args.token_pool else {}),

@@ -324,6 +324,31 @@ qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, 
                                          int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                          size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
 
+/* ---- Layers that share one selection.  The first "llama.cpp vs Atlas"
+ * report (section (a)3) lists indexers that are either full or shared: a
+ * shared layer attends its own K/V with the top-k of the last full layer.
+ * qsa_sparse_attn_decode_layers runs the decode attention of n_layers such
+ * layers (the full one and the shared ones after it) as one launch over the
+ * same idx: layer l's output equals, bit for bit, that of
+ * qsa_sparse_attn_decode(_paged)(&layers[l], idx, ..., outs[l]) on its own.
+ *  layers: host array of n_layers (1 .. QSA_MAX_LAYERS) descriptors with
+ *          the same dtype, hq, hkv and d (q, k, v and softmax_scale may
+ *          differ; with pg, k and v are each layer's pools, all addressed
+ *          through the one block table).
+ *  outs:   host array of n_layers device pointers, each [total_q, hq, d].
+ *  ws:     device workspace of at least qsa_attn_layers_workspace_size()
+ *          bytes (n_layers slices, one per layer).
+ *  pg:     NULL for contiguous K/V, else the paging descriptor.
+ * Errors: as qsa_sparse_attn_decode, plus INVALID_ARGUMENT when n_layers is
+ * out of range, an outs entry is NULL or the layers' shapes differ. */
+#define QSA_MAX_LAYERS 8
+size_t qsa_attn_layers_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t n_layers,
+                                      int32_t budget, int32_t ratio);
+qsa_status qsa_sparse_attn_decode_layers(const qsa_attn *layers, int32_t n_layers, const int32_t *idx,
+                                         int32_t budget, int32_t ratio, const qsa_batch *b,
+                                         void *const *outs, void *ws, size_t ws_bytes,
+                                         const qsa_paged_kv *pg, void *stream);
+
 /* ---- Ingest and rewind.  Serving engines append each new token's raw
  * indexer key and compress every block it completes inside the decode step
  * (vLLM report (a)6: one compressor work item per completed group, with the

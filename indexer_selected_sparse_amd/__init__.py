@@ -33,8 +33,10 @@ EXPORTS = (
     "qsa_attn_workspace_size", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
     "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
-    "qsa_pool_scores",
+    "qsa_pool_scores", "qsa_attn_layers_workspace_size", "qsa_sparse_attn_decode_layers",
 )
+
+MAX_LAYERS = 8   # QSA_MAX_LAYERS
 
 # per-sequence codes written by qsa_ingest / qsa_ring_rewind
 INGEST_OK, INGEST_LOST_KEYS, INGEST_BAD_SLOT, INGEST_TOO_LONG, REWIND_DECLINED = range(5)
@@ -122,6 +124,10 @@ def lib():
         L.qsa_topk_blocks_local.argtypes = [P, i64, P, i32, i32, i32, P, P, P, sz, P]
         L.qsa_pool_scores.restype = i32
         L.qsa_pool_scores.argtypes = [P, i64, i32, i32, P, P, i64, P]
+        L.qsa_attn_layers_workspace_size.restype = sz
+        L.qsa_attn_layers_workspace_size.argtypes = [P, P, i32, i32, i32]
+        L.qsa_sparse_attn_decode_layers.restype = i32
+        L.qsa_sparse_attn_decode_layers.argtypes = [P, i32, P, i32, i32, P, P, P, sz, P, P]
         L.qsa_ingest.restype = i32
         L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
         L.qsa_ring_rewind.restype = i32
@@ -367,6 +373,33 @@ def sparse_attn_decode(q, k, v, softmax_scale, idx, budget, ratio, batch, out, w
     L = lib()
     _attn_call(L.qsa_sparse_attn_decode, L.qsa_sparse_attn_decode_paged, q, k, v, softmax_scale, idx,
                budget, ratio, batch, out, ws, stream, paging)
+
+
+def attn_layers_workspace_size(q, k, v, softmax_scale, n_layers: int, budget: int, ratio: int,
+                               batch: Batch) -> int:
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    return int(lib().qsa_attn_layers_workspace_size(ctypes.byref(b), ctypes.byref(a), n_layers, budget, ratio))
+
+
+def sparse_attn_decode_layers(layers, idx, budget, ratio, batch, outs, ws, stream=None,
+                              paging: Optional[Paging] = None) -> None:
+    """qsa_sparse_attn_decode_layers: layers = [(q, k, v, softmax_scale), ...]
+    sharing idx; outs = one output tensor per layer; ws: device workspace of
+    attn_layers_workspace_size bytes."""
+    _dev(idx, "idx")
+    n = len(layers)
+    if len(outs) != n:
+        raise ValueError("one output per layer")
+    arr = (_Attn * max(n, 1))(*[_attn(*lay) for lay in layers])
+    for o in outs:
+        _dev(o, "out")
+    optrs = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    b = batch._c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pg = None if paging is None else ctypes.byref(paging._c())
+    _check(lib().qsa_sparse_attn_decode_layers(arr, n, _ptr(idx), budget, ratio, ctypes.byref(b), optrs,
+                                               _ptr(ws), nbytes, pg, _stream(stream)))
 
 
 def sparse_attn_prefill(q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws=None,

@@ -356,6 +356,46 @@ qsa_status qsa_sparse_attn_decode_paged(const qsa_attn *a, const int32_t *idx, i
     return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, true, pg, (hipStream_t)stream);
 }
 
+size_t qsa_attn_layers_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t n_layers, int32_t budget,
+                                      int32_t ratio) {
+    if (!b || !a || check_budget(budget, ratio) != QSA_OK || a->hkv < 1 || n_layers < 1 ||
+        n_layers > QSA_MAX_LAYERS)
+        return 0;
+    return (size_t)n_layers * attn_layer_stride_bytes(*b, *a, budget, ratio);
+}
+
+qsa_status qsa_sparse_attn_decode_layers(const qsa_attn *layers, int32_t n_layers, const int32_t *idx,
+                                         int32_t budget, int32_t ratio, const qsa_batch *b, void *const *outs,
+                                         void *ws, size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {
+    if (!layers) return fail(QSA_ERR_INVALID_ARGUMENT, "layers is NULL");
+    if (n_layers < 1 || n_layers > QSA_MAX_LAYERS)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "n_layers=%d must be in [1, %d]", n_layers, QSA_MAX_LAYERS);
+    if (!outs) return fail(QSA_ERR_INVALID_ARGUMENT, "outs is NULL");
+    for (int l = 0; l < n_layers; ++l) {
+        qsa_status s = check_attn(&layers[l]);
+        if (s != QSA_OK) return s;
+        if (!outs[l]) return fail(QSA_ERR_INVALID_ARGUMENT, "outs[%d] is NULL", l);
+        if (layers[l].dtype != layers[0].dtype || layers[l].hq != layers[0].hq ||
+            layers[l].hkv != layers[0].hkv || layers[l].d != layers[0].d)
+            return fail(QSA_ERR_INVALID_ARGUMENT, "layers[%d] differs from layers[0] in dtype, hq, hkv or d", l);
+    }
+    qsa_status s = check_batch(b, false);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
+    if (s == QSA_OK) s = check_budget(budget, ratio);
+    if (s != QSA_OK) return s;
+    if (!idx) return fail(QSA_ERR_INVALID_ARGUMENT, "idx is NULL");
+    if (b->q_offsets != nullptr && b->max_q_per_seq != 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "decode takes one query per sequence (q_offsets NULL or max_q_per_seq == 1)");
+    const size_t need = (size_t)n_layers * attn_layer_stride_bytes(*b, layers[0], budget, ratio);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
+                    "(qsa_attn_layers_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return hip_status(launch_attn_layers(layers, n_layers, idx, budget, ratio, *b, outs, ws, pg,
+                                         (hipStream_t)stream),
+                      "layered sparse attention launch");
+}
+
 qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, int32_t budget,
                                          int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                          size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {

@@ -60,6 +60,16 @@ struct AttnArgs {
     PageMap pm;              // paged K/V pools (pm.table == nullptr: contiguous)
 };
 
+// Several layers that share one selection in one launch (blockIdx.y = layer):
+// each layer's q, k, v, out and its own slice of the partials workspace.
+constexpr int kMaxLayers = QSA_MAX_LAYERS;
+struct LayerPtrs {
+    const void *q[kMaxLayers], *k[kMaxLayers], *v[kMaxLayers];
+    void *out[kMaxLayers];
+    float c[kMaxLayers];     // softmax_scale * log2(e) of each layer
+    int64_t ws_stride;       // floats between the layers' workspace slices
+};
+
 template <int G>
 constexpr int ilog2() { return G <= 1 ? 0 : 1 + ilog2<G / 2>(); }
 
@@ -946,7 +956,13 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
 }
 
 template <int D>
-__global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(AttnArgs A, int G) {
+__global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(AttnArgs A, int G, LayerPtrs Lp) {
+    if (gridDim.y > 1) {
+        const int l = blockIdx.y;
+        A.q = Lp.q[l]; A.k = Lp.k[l]; A.v = Lp.v[l]; A.out = Lp.out[l]; A.c = Lp.c[l];
+        A.ws_o += l * Lp.ws_stride;
+        if (A.ws_ml) A.ws_ml += l * Lp.ws_stride;
+    }
     attn_decode_mfma_body<D>(A, G);
 }
 
@@ -959,7 +975,13 @@ constexpr int kMaxGroups = 32;
 template <bool BF16>
 __global__ __launch_bounds__(kWgWaves * kWave) void attn_combine_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int n_part, int64_t rows,
-    void *__restrict__ out) {
+    void *__restrict__ out, LayerPtrs Lp) {
+    if (gridDim.y > 1) {
+        const int l = blockIdx.y;
+        ws_o += l * Lp.ws_stride;
+        ws_ml += l * Lp.ws_stride;
+        out = Lp.out[l];
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = (int64_t)blockIdx.x * kWgWaves + wave;   // query*hq + head
@@ -1016,28 +1038,29 @@ constexpr int kDecodeWgPerCu = 2;
 int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
 
 template <int D>
-hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, hipStream_t st) {
+hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, const LayerPtrs &Lp, hipStream_t st) {
     const size_t lds = (size_t)kWgWaves * D * kSlotBytes;
     static hipError_t attr = hipFuncSetAttribute((const void *)attn_decode_mfma_kernel<D>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), grid, dim3(kWgWaves * kWave), lds, st, A, G);
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), grid, dim3(kWgWaves * kWave), lds, st, A, G, Lp);
     return hipGetLastError();
 }
 
 template <bool BF16>
-hipError_t launch_attn_t(const AttnArgs &A, int G, bool mfma, hipStream_t st) {
+hipError_t launch_attn_t(const AttnArgs &A, int G, bool mfma, hipStream_t st, const LayerPtrs &Lp,
+                         int n_layers = 1) {
     const int64_t waves = A.total_q * A.n_part * A.hkv;
     dim3 grid((unsigned)((waves + kWgWaves - 1) / kWgWaves));
     dim3 block(kWgWaves * kWave);
     hipError_t e = hipSuccess;
     if constexpr (BF16) {
         if (mfma) {
-            // one workgroup per (query, KV head, part)
-            grid = dim3((unsigned)(A.total_q * A.hkv * A.n_part));
-            const int D = ring_depth((int64_t)grid.x);
-            trace("attn decode lds ring D=%d workgroups=%u", D, grid.x);
-            e = D == 4 ? launch_decode_mfma<4>(A, G, grid, st) : launch_decode_mfma<2>(A, G, grid, st);
+            // one workgroup per (query, KV head, part) [x layer]
+            grid = dim3((unsigned)(A.total_q * A.hkv * A.n_part), (unsigned)n_layers);
+            const int D = ring_depth((int64_t)grid.x * n_layers);
+            trace("attn decode lds ring D=%d workgroups=%u layers=%d", D, grid.x, n_layers);
+            e = D == 4 ? launch_decode_mfma<4>(A, G, grid, Lp, st) : launch_decode_mfma<2>(A, G, grid, Lp, st);
         } else {
             switch (G) {
             case 1: hipLaunchKernelGGL((attn_kernel_w3<BF16, 1>), grid, block, 0, st, A); break;
@@ -1060,9 +1083,9 @@ hipError_t launch_attn_t(const AttnArgs &A, int G, bool mfma, hipStream_t st) {
     }
     if (e != hipSuccess || A.n_part == 1) return e;
     const int64_t rows = A.total_q * A.hq;
-    dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves));
+    dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves), (unsigned)n_layers);
     hipLaunchKernelGGL((attn_combine_kernel<BF16>), cgrid, block, 0, st, A.ws_o, A.ws_ml, A.n_part,
-                       rows, A.out);
+                       rows, A.out, Lp);
     return hipGetLastError();
 }
 
@@ -1107,11 +1130,11 @@ size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, i
     return rows * (kD + 2) * sizeof(float) + 256;
 }
 
-hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ratio,
-                       const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
-                       hipStream_t st) {
-    if (b.total_q == 0) return hipSuccess;
-    AttnArgs A;
+namespace {
+// Kernel arguments of one attention call; returns whether the matrix-core
+// kernel runs it.
+bool attn_args(const qsa_attn &a, const int32_t *idx, int budget, int ratio, const qsa_batch &b, void *out,
+               void *ws, bool decode, const qsa_paged_kv *pg, AttnArgs &A) {
     A.q = a.q; A.k = a.k; A.v = a.v; A.idx = idx;
     A.kv_off = b.kv_offsets; A.q_off = b.q_offsets;
     A.num_seqs = b.num_seqs; A.hq = a.hq; A.hkv = a.hkv;
@@ -1135,11 +1158,53 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     const size_t rows = (size_t)b.total_q * (size_t)a.hq * (size_t)A.n_part;
     A.ws_o = static_cast<float *>(ws);
     A.ws_ml = A.n_part > 1 ? static_cast<float *>(ws) + rows * kD : nullptr;
+    return mfma_path;
+}
+}  // namespace
+
+hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ratio,
+                       const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
+                       hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    AttnArgs A;
+    const bool mfma_path = attn_args(a, idx, budget, ratio, b, out, ws, decode, pg, A);
     const int G = a.hq / a.hkv;
     trace("attn total_q=%lld hkv=%d G=%d parts=%d dtype=%d", (long long)b.total_q, a.hkv, G,
           A.n_part, a.dtype);
-    return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, mfma_path, st)
-                                : launch_attn_t<false>(A, G, false, st);
+    const LayerPtrs none{};
+    return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, mfma_path, st, none)
+                                : launch_attn_t<false>(A, G, false, st, none);
+}
+
+size_t attn_layer_stride_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
+    return (attn_workspace_bytes(b, a, budget, ratio) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_attn_layers(const qsa_attn *layers, int n_layers, const int32_t *idx, int budget, int ratio,
+                              const qsa_batch &b, void *const *outs, void *ws, const qsa_paged_kv *pg,
+                              hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    const size_t stride = attn_layer_stride_bytes(b, layers[0], budget, ratio);
+    AttnArgs A;
+    const bool mfma_path = attn_args(layers[0], idx, budget, ratio, b, outs[0], ws, true, pg, A);
+    const int G = layers[0].hq / layers[0].hkv;
+    if (!mfma_path || n_layers == 1) {   // one launch per layer
+        for (int l = 0; l < n_layers; ++l) {
+            hipError_t e = launch_attn(layers[l], idx, budget, ratio, b, outs[l],
+                                       static_cast<uint8_t *>(ws) + l * stride, true, pg, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    LayerPtrs Lp{};
+    for (int l = 0; l < n_layers; ++l) {
+        Lp.q[l] = layers[l].q; Lp.k[l] = layers[l].k; Lp.v[l] = layers[l].v; Lp.out[l] = outs[l];
+        Lp.c[l] = layers[l].softmax_scale * kLog2e;
+    }
+    Lp.ws_stride = (int64_t)(stride / sizeof(float));
+    trace("attn layers=%d total_q=%lld hkv=%d G=%d parts=%d", n_layers, (long long)b.total_q,
+          layers[0].hkv, G, A.n_part);
+    return launch_attn_t<true>(A, G, true, st, Lp, n_layers);
 }
 
 }  // namespace qsa

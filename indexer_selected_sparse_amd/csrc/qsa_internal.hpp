@@ -50,6 +50,13 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
                        const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
                        hipStream_t st);
 
+// Decode attention of several layers sharing one selection (one launch on
+// the matrix-core path); workspace: n_layers slices of attn_layer_stride_bytes.
+size_t attn_layer_stride_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio);
+hipError_t launch_attn_layers(const qsa_attn *layers, int n_layers, const int32_t *idx, int budget, int ratio,
+                              const qsa_batch &b, void *const *outs, void *ws, const qsa_paged_kv *pg,
+                              hipStream_t st);
+
 // Ingest of new tokens (ring commit, completed-block compression, optional
 // K/V append) and the ring's rollback gate.
 hipError_t launch_ingest(const void *k_new, int k_dtype, int d_idx, int ratio, const qsa_batch &b,

@@ -13,9 +13,10 @@ import torch
 
 import numpy as np
 
-from . import (INGEST_OK, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA, Batch,
-               KeyRing, Paging, attn_workspace_size, compress_keys, index_score, ingest, pool_scores,
-               sparse_attn_decode, sparse_attn_prefill, topk_blocks, topk_workspace_size)
+from . import (INGEST_OK, MAX_LAYERS, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA,
+               Batch, KeyRing, Paging, attn_layers_workspace_size, attn_workspace_size, compress_keys,
+               index_score, ingest, pool_scores, sparse_attn_decode, sparse_attn_decode_layers,
+               sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
              "fp4": torch.float4_e2m1fn_x2}
@@ -257,10 +258,17 @@ class LayerStack:
     full or shared (the first "llama.cpp vs Atlas" report, section (a)3: a
     shared layer reuses the top-k of the previous full layer).  Layer l is
     full when l % full_every == 0; a shared layer skips scoring and top-k and
-    attends its own K/V with the selection of the last full layer before it."""
+    attends its own K/V with the selection of the last full layer before it.
+    With `fused`, the decode attention of a full layer and the shared layers
+    after it runs as one qsa_sparse_attn_decode_layers launch (up to
+    MAX_LAYERS layers each; outputs bit-identical to per-layer calls)."""
     layers: List[DeviceProblem]
     full_every: int = 1
+    fused: bool = True
     full: List[bool] = field(default_factory=list)
+    groups: List[List[DeviceProblem]] = field(default_factory=list)
+    heads: List[DeviceProblem] = field(default_factory=list)
+    group_ws: Optional[torch.Tensor] = None
 
     def __post_init__(self):
         if self.full_every < 1:
@@ -270,14 +278,50 @@ class LayerStack:
         for dp, f in zip(self.layers, self.full):
             if f:
                 src = dp
+                self.groups.append([dp])
+                self.heads.append(dp)
             else:   # a shared layer reads (and never writes) the full layer's selection
                 if dp.idx.shape != src.idx.shape:
                     raise ValueError("shared layers need the full layer's selection width")
                 dp.idx = src.idx
+                if len(self.groups[-1]) == MAX_LAYERS:
+                    self.groups.append([dp])
+                else:
+                    self.groups[-1].append(dp)
+        if self.fused:
+            need = max([self._group_ws_bytes(g) for g in self.groups] + [0])
+            if need:
+                self.group_ws = torch.empty(need, dtype=torch.uint8, device=self.layers[0].idx.device)
+
+    def _fusable(self, g: List[DeviceProblem]) -> bool:
+        h = g[0]
+        if len(g) < 2 or not all(dp.decode for dp in g):
+            return False
+        same_pg = all((dp.paging is None) == (h.paging is None) for dp in g) and (
+            h.paging is None or all(dp.paging.block_table.data_ptr() == h.paging.block_table.data_ptr()
+                                    and dp.paging.num_pages == h.paging.num_pages
+                                    and dp.paging.page_size == h.paging.page_size for dp in g))
+        return same_pg and all(dp.budget + dp.local_blocks * dp.ratio == h.budget + h.local_blocks * h.ratio
+                               and dp.ratio == h.ratio and dp.q.shape == h.q.shape and dp.K.shape[1:] == h.K.shape[1:]
+                               and dp.q.dtype == h.q.dtype for dp in g)
+
+    def _group_ws_bytes(self, g: List[DeviceProblem]) -> int:
+        if not self._fusable(g):
+            return 0
+        h = g[0]
+        return attn_layers_workspace_size(h.q, h.K, h.V, h.softmax_scale, len(g),
+                                          h.budget + h.local_blocks * h.ratio, h.ratio, h.batch)
 
     def step(self, stream=None) -> None:
-        for dp, f in zip(self.layers, self.full):
-            if f:
-                dp.score(stream=stream)
-                dp.topk(stream=stream)
-            dp.attend(stream=stream)
+        for g in self.groups:
+            h = g[0]
+            if any(h is x for x in self.heads):   # a full layer: its own selection first
+                h.score(stream=stream)
+                h.topk(stream=stream)
+            if self.fused and self._fusable(g):
+                sparse_attn_decode_layers([(dp.q, dp.K, dp.V, dp.softmax_scale) for dp in g], h.idx,
+                                          h.budget + h.local_blocks * h.ratio, h.ratio, h.batch,
+                                          [dp.out for dp in g], self.group_ws, stream=stream, paging=h.paging)
+            else:
+                for dp in g:
+                    dp.attend(stream=stream)

@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -167,6 +167,18 @@ def rewind(ring="default", ratio=4, b=None):
     return Q.lib().qsa_ring_rewind(ctypes.byref(b), ratio, _ref(ring), None, None)
 
 
+def decode_layers(layers=None, n=None, outs="default", ws=FAKE, nws=1 << 30, b=None, idx=FAKE):
+    layers = [_attn(), _attn()] if layers is None else layers
+    n = len(layers) if n is None else n
+    arr = (Q._Attn * max(len(layers), 1))(*layers)
+    if outs == "default":
+        outs = [FAKE] * max(len(layers), 1)
+    optrs = None if outs is None else (ctypes.c_void_p * len(outs))(*outs)
+    b = b or _batch()
+    return Q.lib().qsa_sparse_attn_decode_layers(arr, n, P(idx), 2048, 4, ctypes.byref(b), optrs, P(ws), nws,
+                                                 None, None)
+
+
 INV, UNS, WS = Q.QSA_ERR_INVALID_ARGUMENT, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
 
 CASES = [
@@ -243,6 +255,15 @@ CASES = [
                                                      1024, None), INV, "mode=2"),
     ("pool ld_tok small", lambda: Q.lib().qsa_pool_scores(P(FAKE), 4095, 4, 0, ctypes.byref(_batch()), P(FAKE),
                                                           1024, None), INV, "ld_tok=4095"),
+    ("layers zero", lambda: decode_layers(n=0), INV, "n_layers=0"),
+    ("layers nine", lambda: decode_layers(layers=[_attn()] * 9), INV, "n_layers=9"),
+    ("layers null outs", lambda: decode_layers(outs=None), INV, "outs is NULL"),
+    ("layers null out entry", lambda: decode_layers(outs=[FAKE, 0]), INV, "outs[1]"),
+    ("layers shape mismatch", lambda: decode_layers(layers=[_attn(), _attn(hkv=8)]), INV, "layers[1]"),
+    ("layers bad layer", lambda: decode_layers(layers=[_attn(), _attn(d=64)]), UNS, "attn.d=64"),
+    ("layers workspace small", lambda: decode_layers(nws=16), WS, "qsa_attn_layers_workspace_size"),
+    ("layers multi-query batch",
+     lambda: decode_layers(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)), INV, "one query"),
     ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
     ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]
@@ -272,3 +293,8 @@ def test_workspace_sizes():
     n = Q.lib().qsa_topk_workspace_size(ctypes.byref(b), 2048, 4, ctypes.byref(ix))
     assert n >= 32 * (1024 // 256) * 4
     assert Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2047, 4) == 0
+    # layered decode: one 256-byte aligned single-layer slice per layer
+    one = Q.lib().qsa_attn_workspace_size(ctypes.byref(b), ctypes.byref(a), 2048, 4)
+    n4 = Q.lib().qsa_attn_layers_workspace_size(ctypes.byref(b), ctypes.byref(a), 4, 2048, 4)
+    assert n4 == 4 * ((one + 255) // 256 * 256)
+    assert Q.lib().qsa_attn_layers_workspace_size(ctypes.byref(b), ctypes.byref(a), 9, 2048, 4) == 0

@@ -48,3 +48,52 @@ def test_shared_indexer_layers(n_layers, full_every):
                                      wl.V[a:b].float().numpy(), toks, sp.softmax_scale)
         got = dp.out.float().cpu().numpy().astype(np.float64)
         check_out(wl, {"out": got}, {"out": exp}, np.arange(wl.total_q))
+
+
+@pytest.mark.parametrize("n_layers,full_every,paged", [(4, 4, False), (11, 11, False), (6, 3, True)])
+def test_fused_layers_equal_per_layer_calls(n_layers, full_every, paged):
+    """One layered attention launch per full layer and its shared layers gives
+    every layer's output bit for bit as its own decode call (11 layers: a
+    group beyond the 8-layer launch limit splits)."""
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=512)
+    lens = [5000, 1234, 777, 80, 2052, 4099, 3, 1]
+    wls = [W.make(sp, lens=lens, seed=90 + l) for l in range(n_layers)]
+
+    def build(fused):
+        layers = []
+        table = None
+        for l, wl in enumerate(wls):
+            dp = pipeline.upload(wl, "cuda")
+            if l % full_every == 0:
+                dp.compress()
+            if paged:
+                dp = pipeline.page(dp, lens, 64, seed=5)
+                if table is None:
+                    table = dp.paging
+                else:   # one block table for every layer's pools
+                    assert torch.equal(dp.paging.block_table, table.block_table)
+                    dp.paging = table
+            layers.append(dp)
+        return pipeline.LayerStack(layers, full_every, fused=fused)
+
+    a, b = build(True), build(False)
+    assert a.group_ws is not None
+    a.step()
+    b.step()
+    torch.cuda.synchronize()
+    for l, (x, y) in enumerate(zip(a.layers, b.layers)):
+        assert torch.equal(x.idx, y.idx), l
+        assert torch.equal(x.out.view(torch.int16), y.out.view(torch.int16)), l
+    # the per-layer outputs also match the oracle on the first shared layer
+    wl, dp = wls[1], a.layers[1]
+    sel = oracle.run_workload(wls[0])["idx"]
+    Ls, qseq = wl.visible_lengths(), wl.query_seq()
+    exp = np.zeros((wl.total_q, sp.hq, sp.d))
+    for i in range(wl.total_q):
+        s = int(qseq[i])
+        a0, b0 = int(wl.kv_offsets[s]), int(wl.kv_offsets[s + 1])
+        toks = oracle.token_set(sel[i], sp.ratio, int(Ls[i]))
+        exp[i] = oracle.attn(wl.q[i].float().numpy(), wl.K[a0:b0].float().numpy(),
+                             wl.V[a0:b0].float().numpy(), toks, sp.softmax_scale)
+    check_out(wl, {"out": dp.out.float().cpu().numpy().astype(np.float64)}, {"out": exp},
+              np.arange(wl.total_q))
