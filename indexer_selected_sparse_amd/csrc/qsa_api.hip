@@ -388,7 +388,7 @@ qsa_status qsa_sparse_attn_decode_layers(const qsa_attn *layers, int32_t n_layer
         return fail(QSA_ERR_INVALID_ARGUMENT,
                     "decode takes one query per sequence (q_offsets NULL or max_q_per_seq == 1)");
     const size_t need = (size_t)n_layers * attn_layer_stride_bytes(*b, layers[0], budget, ratio);
-    if (ws == nullptr || ws_bytes < need)
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_attn_layers_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
     return hip_status(launch_attn_layers(layers, n_layers, idx, budget, ratio, *b, outs, ws, pg,
