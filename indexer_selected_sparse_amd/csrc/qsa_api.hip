@@ -7,6 +7,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <set>
+#include <tuple>
+
 #include "qsa_internal.hpp"
 
 namespace qsa {
@@ -30,6 +34,19 @@ static qsa_status ok() {
 static qsa_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return ok();
     return fail(QSA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+hipError_t enable_dyn_lds(const void *fn, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::set<std::tuple<int, const void *, int>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count(std::make_tuple(dev, fn, bytes))) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert(std::make_tuple(dev, fn, bytes));
+    return e;
 }
 
 bool trace_enabled() {

@@ -35,6 +35,8 @@
 //    come through LDS and meet fp32-widened V in plain FMAs.  (bf16
 //    probabilities would cost up to 2^-8 relative per weight, visible when a
 //    few tokens carry the softmax.)
+#include <atomic>
+
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -1018,16 +1020,16 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_combine_kernel(
 // the workgroups that share it (4 waves x D slots x 8 KB per workgroup, two
 // or more workgroups per CU get D = 2).
 int cu_count() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 // Workgroups per CU the decode split aims for: a random gather of 256-byte
@@ -1040,8 +1042,7 @@ int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
 template <int D>
 hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, const LayerPtrs &Lp, hipStream_t st) {
     const size_t lds = (size_t)kWgWaves * D * kSlotBytes;
-    static hipError_t attr = hipFuncSetAttribute((const void *)attn_decode_mfma_kernel<D>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D>, (int)lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), grid, dim3(kWgWaves * kWave), lds, st, A, G, Lp);
     return hipGetLastError();

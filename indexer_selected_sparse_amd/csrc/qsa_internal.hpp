@@ -67,6 +67,9 @@ hipError_t launch_ring_rewind(const qsa_batch &b, int ratio, const qsa_key_ring 
                               hipStream_t st);
 
 // Host tracing (QSA_TRACE=1): one line per launch on stderr.
+// Allow a kernel `bytes` of dynamic LDS on the current device (once per
+// kernel, size and device; later calls return at once).
+hipError_t enable_dyn_lds(const void *fn, int bytes);
 bool trace_enabled();
 void trace(const char *fmt, ...);
 

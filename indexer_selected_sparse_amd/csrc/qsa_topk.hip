@@ -26,8 +26,6 @@
 //  4. An ordered pass emits every key > T and the first `need` keys == T by
 //     index: elements are visited round-major (index order), and per
 //     (round, wave) counts, scanned once, give each output position.
-#include <mutex>
-
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -1283,18 +1281,10 @@ hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *reche
     const int64_t max_nb = b.max_kv_len >> log2r;
     const size_t lds = (size_t)(max_nb > 0 ? max_nb : 1) * sizeof(uint32_t);
     dim3 grid((unsigned)b.total_q);
-    // Dynamic LDS above the 64 KB default must be enabled per kernel.
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [] {
-        attr_err = hipFuncSetAttribute((const void *)topk_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(kLdsKeys * sizeof(uint32_t)));
-        if (attr_err == hipSuccess)
-            attr_err = hipFuncSetAttribute((const void *)topk_cert_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kLdsKeys * sizeof(uint32_t)));
-    });
+    // Dynamic LDS above the 64 KB default must be enabled per kernel (and device).
+    hipError_t attr_err = enable_dyn_lds((const void *)topk_kernel<true>, (int)(kLdsKeys * sizeof(uint32_t)));
+    if (attr_err == hipSuccess)
+        attr_err = enable_dyn_lds((const void *)topk_cert_kernel, (int)(kLdsKeys * sizeof(uint32_t)));
     if (attr_err != hipSuccess) return attr_err;
     if (recheck != nullptr) {
         if (max_nb > kTopkRecheckMaxBlocks) return hipErrorNotSupported;
