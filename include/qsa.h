@@ -426,6 +426,23 @@ qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t
                       void *kc_scale, const qsa_kv_append *kv, int32_t *status,
                       const qsa_paged_kv *pg, void *stream);
 
+/* The decode step's append and canonical scores in one launch: the same
+ * results, bit for bit, as qsa_ingest(k_new, k_dtype, ix->d_idx, ratio, b,
+ * ring, ix->kc, ix->kc_dtype, ix->kc_scale, kv, status, pg) followed by
+ * qsa_index_score(_paged)(ix, ratio, b, scores, ld_scores,
+ * QSA_SCORE_CANONICAL, pg).  vLLM report (a)6 has the compressor work item
+ * run inside the step; here the block a sequence's new token completes is
+ * scored by the wave that compresses it, and every other block by the usual
+ * scorer, so the append needs no launch of its own.  One new token and one
+ * query per sequence (batch.q_offsets NULL), a bf16 q_idx and bf16, e4m3 or
+ * fp4 compressed keys; ix->kc and ix->kc_scale are written (the indexer's
+ * const pointers notwithstanding).  Errors: those of the two calls, plus
+ * INVALID_ARGUMENT for q_offsets != NULL and UNSUPPORTED for other dtypes. */
+qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ratio, const qsa_batch *b,
+                                  const qsa_key_ring *ring, const qsa_kv_append *kv, int32_t *status,
+                                  const qsa_indexer *ix, float *scores, int64_t ld_scores,
+                                  const qsa_paged_kv *pg, void *stream);
+
 /* Explicit rollback gate (defect investigations page, fix plan PR-F: a
  * rewind the indexer state cannot follow is declined, not applied).  The
  * batch's kv_offsets give the lengths N_s after the rollback.  Per sequence:

@@ -34,6 +34,7 @@ EXPORTS = (
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
     "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
     "qsa_pool_scores", "qsa_attn_layers_workspace_size", "qsa_sparse_attn_decode_layers",
+    "qsa_ingest_index_score",
 )
 
 MAX_LAYERS = 8   # QSA_MAX_LAYERS
@@ -130,6 +131,8 @@ def lib():
         L.qsa_sparse_attn_decode_layers.argtypes = [P, i32, P, i32, i32, P, P, P, sz, P, P]
         L.qsa_ingest.restype = i32
         L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
+        L.qsa_ingest_index_score.restype = i32
+        L.qsa_ingest_index_score.argtypes = [P, i32, i32, P, P, P, P, P, P, i64, P, P]
         L.qsa_ring_rewind.restype = i32
         L.qsa_ring_rewind.argtypes = [P, i32, P, P, P]
         _lib = L
@@ -410,6 +413,23 @@ def sparse_attn_prefill(q, k, v, softmax_scale, idx, budget, ratio, batch, out, 
                idx, budget, ratio, batch, out, ws, stream, paging)
 
 
+def _check_ring_keys(ring: KeyRing, k_new: torch.Tensor) -> None:
+    if ring.keys.dtype != k_new.dtype or ring.keys.shape[-1] != k_new.shape[-1]:
+        raise TypeError("ring.keys must have the dtype and width of k_new")
+
+
+def _kv_append(kv) -> Optional[_KvAppend]:
+    if kv is None:
+        return None
+    kn, vn, K, V = kv
+    for t, n in ((kn, "kv.k_new"), (vn, "kv.v_new"), (K, "kv.k"), (V, "kv.v")):
+        _dev(t, n)
+    if not (kn.dtype == vn.dtype == K.dtype == V.dtype):
+        raise TypeError("K/V append tensors must share one dtype")
+    return _KvAppend(kn.data_ptr(), vn.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(K),
+                     K.shape[-2], K.shape[-1])
+
+
 def ingest(k_new: torch.Tensor, ratio: int, batch: Batch, ring: KeyRing, kc: torch.Tensor,
            kc_scale: Optional[torch.Tensor] = None, kv=None, status: Optional[torch.Tensor] = None,
            stream=None, paging: Optional[Paging] = None) -> None:
@@ -421,17 +441,8 @@ def ingest(k_new: torch.Tensor, ratio: int, batch: Batch, ring: KeyRing, kc: tor
     _dev(k_new, "k_new")
     _dev(kc, "kc")
     kcd = QSA_FP8_E4M3 if kc.dtype == torch.uint8 else _dtype_code(kc)
-    if ring.keys.dtype != k_new.dtype or ring.keys.shape[-1] != k_new.shape[-1]:
-        raise TypeError("ring.keys must have the dtype and width of k_new")
-    kva = None
-    if kv is not None:
-        kn, vn, K, V = kv
-        for t, n in ((kn, "kv.k_new"), (vn, "kv.v_new"), (K, "kv.k"), (V, "kv.v")):
-            _dev(t, n)
-        if not (kn.dtype == vn.dtype == K.dtype == V.dtype):
-            raise TypeError("K/V append tensors must share one dtype")
-        kva = _KvAppend(kn.data_ptr(), vn.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(K),
-                        K.shape[-2], K.shape[-1])
+    _check_ring_keys(ring, k_new)
+    kva = _kv_append(kv)
     if status is not None:
         _dev(status, "status")
     b, rg = batch._c(), ring._c()
@@ -440,6 +451,27 @@ def ingest(k_new: torch.Tensor, ratio: int, batch: Batch, ring: KeyRing, kc: tor
                             ctypes.byref(rg), _ptr(kc), kcd, _ptr(kc_scale),
                             None if kva is None else ctypes.byref(kva), _ptr(status),
                             None if pg is None else ctypes.byref(pg), _stream(stream)))
+
+
+def ingest_index_score(k_new: torch.Tensor, ratio: int, batch: Batch, ring: KeyRing, q_idx, w, kc,
+                       kc_scale, scores: torch.Tensor, kv=None, status: Optional[torch.Tensor] = None,
+                       stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_ingest_index_score: ingest(k_new, ..., kc, kc_scale, kv, status) then
+    index_score(q_idx, w, kc, kc_scale, ...) in one launch, for a decode batch
+    (one new token and one query per sequence)."""
+    _dev(k_new, "k_new")
+    _dev(scores, "scores")
+    _check_ring_keys(ring, k_new)
+    ix = _indexer(q_idx, w, kc, kc_scale)
+    kva = _kv_append(kv)
+    if status is not None:
+        _dev(status, "status")
+    b, rg = batch._c(), ring._c()
+    pg = None if paging is None else paging._c()
+    _check(lib().qsa_ingest_index_score(_ptr(k_new), _dtype_code(k_new), ratio, ctypes.byref(b), ctypes.byref(rg),
+                                        None if kva is None else ctypes.byref(kva), _ptr(status), ctypes.byref(ix),
+                                        _ptr(scores), scores.shape[1], None if pg is None else ctypes.byref(pg),
+                                        _stream(stream)))
 
 
 def ring_rewind(batch: Batch, ratio: int, ring: KeyRing, status: Optional[torch.Tensor] = None,

@@ -436,6 +436,18 @@ static qsa_status check_ring(const qsa_key_ring *ring, const qsa_batch *b, int32
     return ok();
 }
 
+static qsa_status check_kv_append(const qsa_kv_append *kv) {
+    if (!kv) return ok();
+    if (!kv->k_new || !kv->v_new || !kv->k || !kv->v)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "kv.k_new/v_new/k/v must not be NULL");
+    if (kv->dtype != QSA_F32 && kv->dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "kv.dtype=%d must be QSA_F32 or QSA_BF16", kv->dtype);
+    if (kv->hkv < 1 || kv->hkv > 64)
+        return fail(QSA_ERR_UNSUPPORTED, "kv.hkv=%d must be in [1, 64]", kv->hkv);
+    if (kv->d != 128) return fail(QSA_ERR_UNSUPPORTED, "kv.d=%d must be 128", kv->d);
+    return ok();
+}
+
 qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t ratio,
                       const qsa_batch *b, const qsa_key_ring *ring, void *kc, int32_t kc_dtype,
                       void *kc_scale, const qsa_kv_append *kv, int32_t *status,
@@ -456,18 +468,44 @@ qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t
     if (d_idx != 64 && d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d must be 64 or 128", d_idx);
     if (b->q_offsets && b->max_q_per_seq < 0)
         return fail(QSA_ERR_INVALID_ARGUMENT, "batch.max_q_per_seq=%d must be >= 0", b->max_q_per_seq);
-    if (kv) {
-        if (!kv->k_new || !kv->v_new || !kv->k || !kv->v)
-            return fail(QSA_ERR_INVALID_ARGUMENT, "kv.k_new/v_new/k/v must not be NULL");
-        if (kv->dtype != QSA_F32 && kv->dtype != QSA_BF16)
-            return fail(QSA_ERR_UNSUPPORTED, "kv.dtype=%d must be QSA_F32 or QSA_BF16", kv->dtype);
-        if (kv->hkv < 1 || kv->hkv > 64)
-            return fail(QSA_ERR_UNSUPPORTED, "kv.hkv=%d must be in [1, 64]", kv->hkv);
-        if (kv->d != 128) return fail(QSA_ERR_UNSUPPORTED, "kv.d=%d must be 128", kv->d);
-    }
+    s = check_kv_append(kv);
+    if (s != QSA_OK) return s;
     return hip_status(launch_ingest(k_new, k_dtype, d_idx, ratio, *b, *ring, kc, kc_dtype, kc_scale, kv,
                                     status, pg, (hipStream_t)stream),
                       "qsa_ingest launch");
+}
+
+qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ratio, const qsa_batch *b,
+                                  const qsa_key_ring *ring, const qsa_kv_append *kv, int32_t *status,
+                                  const qsa_indexer *ix, float *scores, int64_t ld_scores,
+                                  const qsa_paged_kv *pg, void *stream) {
+    qsa_status s = check_indexer(ix, false);
+    if (s == QSA_OK) s = check_batch(b, pg == nullptr);
+    if (s == QSA_OK) s = check_ratio(ratio);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
+    if (s == QSA_OK) s = check_rows(b, ratio);
+    if (s == QSA_OK) s = check_ring(ring, b, ratio);
+    if (s == QSA_OK) s = check_kv_append(kv);
+    if (s != QSA_OK) return s;
+    if (b->q_offsets)
+        return fail(QSA_ERR_INVALID_ARGUMENT,
+                    "qsa_ingest_index_score takes one new token and one query per sequence "
+                    "(batch.q_offsets must be NULL); use qsa_ingest and qsa_index_score");
+    if (ix->q_dtype != QSA_BF16 || ix->kc_dtype == QSA_F32)
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "qsa_ingest_index_score needs a bf16 q_idx and bf16, e4m3 or fp4 compressed keys "
+                    "(q_dtype=%d, kc_dtype=%d)", ix->q_dtype, ix->kc_dtype);
+    if (!k_new) return fail(QSA_ERR_INVALID_ARGUMENT, "k_new is NULL");
+    if (k_dtype != QSA_F32 && k_dtype != QSA_BF16)
+        return fail(QSA_ERR_UNSUPPORTED, "k_dtype=%d must be QSA_F32 or QSA_BF16", k_dtype);
+    if (!scores) return fail(QSA_ERR_INVALID_ARGUMENT, "scores is NULL");
+    const int64_t need_ld = (b->max_kv_len + ratio - 1) / ratio;
+    if (ld_scores < need_ld || ld_scores < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
+                    (long long)ld_scores, (long long)need_ld);
+    return hip_status(launch_ingest_score(k_new, k_dtype, ratio, *b, *ring, kv, status, *ix, scores, ld_scores, pg,
+                                          (hipStream_t)stream),
+                      "qsa_ingest_index_score launch");
 }
 
 qsa_status qsa_ring_rewind(const qsa_batch *b, int32_t ratio, const qsa_key_ring *ring, int32_t *status,

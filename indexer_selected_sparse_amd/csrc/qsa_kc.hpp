@@ -54,11 +54,15 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
 // scale byte per 32 dims (kc_scale: bytes [rows, D/32]) with exponent
 // X = floor(log2(amax of the group)) - 2 in [-127, 127] (-127 for amax 0).
 // m = this lane's DPL means; the whole wave must call it (e4m3 and fp4
-// reduce amax over lanes).
+// reduce amax over lanes).  dec receives the stored key's values as the
+// scorer widens them (exact): bf16 and fp32 values, e4m3 code values (sc =
+// the row's scale, applied after the dot), fp4 code values times 2^X.
 template <int KC, int DPL>
 __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict__ kc,
-                                         void *__restrict__ kc_scale, int64_t out_row, int lane) {
+                                         void *__restrict__ kc_scale, int64_t out_row, int lane,
+                                         float (&dec)[DPL], float &sc) {
     constexpr int D = DPL * kWave;
+    sc = 1.0f;
     const int64_t o = out_row * D + lane * DPL;
     if constexpr (KC == 3) {
         constexpr int LPG = 32 / DPL;                 // lanes per 32-dim group
@@ -75,6 +79,15 @@ __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict
         uint32_t c[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) c[e] = f32_to_e2m1(__builtin_amdgcn_ldexpf(m[e], -X));
+        {
+            const uint32_t E = (uint32_t)(X + 127);
+            const float scl = __uint_as_float(E ? (E << 23) : 0x00400000u);   // 2^X (E = 0: 2^-127)
+            uint32_t word = c[0];
+            if constexpr (DPL == 2) word |= c[1] << 4;
+            const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scl, 0);
+            dec[0] = v[0];
+            if constexpr (DPL == 2) dec[1] = v[1];
+        }
         uint8_t *codes = static_cast<uint8_t *>(kc) + out_row * (D / 2);
         if constexpr (DPL == 2) {
             codes[lane] = (uint8_t)(c[0] | (c[1] << 4));
@@ -86,11 +99,17 @@ __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict
             static_cast<uint8_t *>(kc_scale)[out_row * (D / 32) + lane / LPG] = (uint8_t)(X + 127);
     } else if constexpr (KC == 0) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) static_cast<float *>(kc)[o + e] = m[e];
+        for (int e = 0; e < DPL; ++e) {
+            static_cast<float *>(kc)[o + e] = m[e];
+            dec[e] = m[e];
+        }
     } else if constexpr (KC == 1) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e)
-            static_cast<uint16_t *>(kc)[o + e] = (uint16_t)f32_to_bf16_bits(m[e]);
+        for (int e = 0; e < DPL; ++e) {
+            const uint32_t bits = f32_to_bf16_bits(m[e]);
+            static_cast<uint16_t *>(kc)[o + e] = (uint16_t)bits;
+            dec[e] = bf16_to_f32((uint16_t)bits);
+        }
     } else {
         float amax = 0.0f;
 #pragma unroll
@@ -98,6 +117,7 @@ __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict
         amax = wave_max(amax);
         const float scale = amax / 448.0f;    // correctly rounded division
         if (lane == 0) static_cast<float *>(kc_scale)[out_row] = scale;
+        sc = scale;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
             uint32_t c = 0;
@@ -107,7 +127,48 @@ __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict
                 c = f32_to_e4m3(y);
             }
             static_cast<uint8_t *>(kc)[o + e] = (uint8_t)c;
+            dec[e] = e4m3x2_to_f32<false>(c).x;
         }
+    }
+}
+
+template <int KC, int DPL>
+__device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict__ kc,
+                                         void *__restrict__ kc_scale, int64_t out_row, int lane) {
+    float dec[DPL], sc;
+    store_kc<KC, DPL>(m, kc, kc_scale, out_row, lane, dec, sc);
+}
+
+// The values of a stored compressed-key row as the scorer widens them (this
+// lane's DPL dims; sc = the e4m3 row scale, else 1).
+template <int KC, int DPL>
+__device__ __forceinline__ void load_kc_values(const void *__restrict__ kc, const void *__restrict__ kc_scale,
+                                               int64_t row, int lane, float (&dec)[DPL], float &sc) {
+    constexpr int D = DPL * kWave;
+    sc = 1.0f;
+    if constexpr (KC == 3) {
+        const uint8_t *codes = static_cast<const uint8_t *>(kc) + row * (D / 2);
+        const uint32_t E = static_cast<const uint8_t *>(kc_scale)[row * (D / 32) + lane * DPL / 32];
+        const float scl = __uint_as_float(E ? (E << 23) : 0x00400000u);
+        const uint32_t byte = codes[lane * DPL / 2];
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, scl, 0);
+        if constexpr (DPL == 2) {
+            dec[0] = v[0];
+            dec[1] = v[1];
+        } else {
+            dec[0] = (lane & 1) ? v[1] : v[0];
+        }
+    } else if constexpr (KC == 2) {
+        sc = static_cast<const float *>(kc_scale)[row];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            dec[e] = e4m3x2_to_f32<false>(static_cast<const uint8_t *>(kc)[row * D + lane * DPL + e]).x;
+    } else if constexpr (KC == 1) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) dec[e] = bf16_to_f32(static_cast<const uint16_t *>(kc)[row * D + lane * DPL + e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) dec[e] = static_cast<const float *>(kc)[row * D + lane * DPL + e];
     }
 }
 

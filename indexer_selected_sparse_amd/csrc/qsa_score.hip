@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "qsa_device.hpp"
+#include "qsa_ingest.hpp"
 #include "qsa_internal.hpp"
 
 namespace qsa {
@@ -308,12 +309,14 @@ __device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * KeyBits<KT>::v
     }
 }
 
-template <typename KT, int D, int H>
-__global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
+// SKIP_NEW: leave out the block the query's last token completes (L a
+// multiple of the ratio), which the fused append scores itself.
+template <typename KT, int D, int H, bool SKIP_NEW>
+__device__ __forceinline__ void score_exact_body(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
+    int log2r, float *__restrict__ scores, int64_t ld, const PageMap &pm, int64_t i, int64_t by) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     constexpr bool kFP4 = std::is_same<KT, Fp4x2>::value;
     constexpr int CH = kExactChunk;
@@ -322,12 +325,12 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     constexpr int QW = CH / 2;                           // query dwords per (chunk, head)
     static_assert(D % CH == 0 && (LPC == 1 || LPC == 2 || LPC == 4) && QW == 16, "chunk layout");
     static_assert((NCH - 1) * LPC < 64, "loads in flight fit the wait counter");
-    const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
-    const int64_t b = (int64_t)blockIdx.y * kExactThreads + threadIdx.x;
-    if ((int64_t)blockIdx.y * kExactThreads >= nb) return;   // whole workgroup invisible
-    const bool active = b < nb;
+    const int64_t b = by * kExactThreads + threadIdx.x;
+    if (by * kExactThreads >= nb) return;   // whole workgroup invisible
+    bool active = b < nb;
+    if constexpr (SKIP_NEW) active = active && !(b == nb - 1 && (qp.L & ((1 << log2r) - 1)) == 0);
     const int64_t row = pm.table ? paged_row(pm, qp.seq, active ? b : 0, pm.log2_page - log2r)
                                  : qp.blk_row0 + (active ? b : 0);
     const float sc = kE4M3 ? static_cast<const float *>(kc_scale)[row] : 1.0f;
@@ -394,6 +397,86 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     if (active) scores[i * ld + b] = s;
 }
 
+template <typename KT, int D, int H>
+__global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
+    const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
+    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
+    score_exact_body<KT, D, H, false>(q_idx, w, kc, kc_scale, kv_off, blk_off, q_off, num_seqs, log2r, scores,
+                                      ld, pm, blockIdx.x, blockIdx.y);
+}
+
+// Canonical score of one block whose key a wave holds (lane l: dims
+// l*DPL.., values as the scorer widens them; sc: the e4m3 row scale), with
+// score_exact_body's arithmetic: per head an fp32 fused multiply-add chain
+// over ascending d from +0, then the scale, ReLU and the weighted sum over
+// ascending heads.  Lane h computes head h's chain; lane 0 writes.
+template <int D, int H, bool E4M3>
+__device__ __forceinline__ void score_one_block(const float (&dec)[D / kWave], float sc,
+                                                const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
+                                                int64_t i, float *__restrict__ dst, int lane) {
+    constexpr int DPL = D / kWave;
+    const int h = lane < H ? lane : H - 1;
+    const uint4 *q4 = reinterpret_cast<const uint4 *>(q_idx + (i * H + h) * D);
+    uint32_t qd[D / 2];
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+        const uint4 v = q4[j];
+        qd[4 * j] = v.x; qd[4 * j + 1] = v.y; qd[4 * j + 2] = v.z; qd[4 * j + 3] = v.w;
+    }
+    float dot = 0.0f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const float k = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec[d % DPL]), d / DPL));
+        const float q = (d & 1) ? bf16hi(qd[d / 2]) : bf16lo(qd[d / 2]);
+        dot = __builtin_fmaf(q, k, dot);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) {
+        float dd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dot), hh));
+        if constexpr (E4M3) dd = dd * sc;
+        const float r = dd > 0.0f ? dd : 0.0f;
+        const float t = w[i * H + hh] * r;
+        s = s + t;
+    }
+    if (lane == 0) *dst = s;
+}
+
+// Append + canonical score in one launch, for a decode step (one new token
+// and one query per sequence).  Workgroups x < num_seqs score query x as
+// score_exact_kernel does, except the block the new token completes; the
+// workgroups after them (y = 0) run one append wave per sequence
+// (append_one), which writes that block's compressed key (or, when the
+// append could not, takes the key already stored) and scores the block with
+// the same arithmetic.  Nothing else the scorer reads is written here, so the
+// result equals the append followed by the score, bit for bit.
+template <typename KT, int D, int H, typename TIn>
+__global__ __launch_bounds__(kExactThreads) void ingest_score_kernel(
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KT *__restrict__ kc,
+    void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off, const int64_t *__restrict__ blk_off,
+    int num_seqs, int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, const TIn *__restrict__ k_new,
+    float inv_ratio, RingArgs ring, KvArgs kv, int32_t *__restrict__ status) {
+    if ((int)blockIdx.x < num_seqs) {
+        score_exact_body<KT, D, H, true>(q_idx, w, kc, kc_scale, kv_off, blk_off, nullptr, num_seqs, log2r,
+                                         scores, ld, pm, blockIdx.x, blockIdx.y);
+        return;
+    }
+    if (blockIdx.y != 0) return;
+    constexpr int DPL = D / kWave;
+    constexpr int KC = std::is_same<KT, Fp4x2>::value ? 3 : (std::is_same<KT, uint8_t>::value ? 2 : 1);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int sq = (int)(blockIdx.x - num_seqs) * (kExactThreads / kWave) + (int)(threadIdx.x / kWave);
+    if (sq >= num_seqs) return;
+    AppendOut<DPL> a = append_one<TIn, DPL, KC>(k_new, kv_off, blk_off, sq, log2r, inv_ratio, ring, kc, kc_scale,
+                                                kv, status, pm, lane);
+    if (!a.complete) return;
+    if (!a.stored) load_kc_values<KC, DPL>(kc, kc_scale, a.kc_row, lane, a.dec, a.sc);
+    const int64_t g = ((kv_off[sq + 1] - kv_off[sq]) >> log2r) - 1;
+    score_one_block<D, H, KC == 2>(a.dec, a.sc, q_idx, w, sq, scores + sq * ld + g, lane);
+}
+
 template <typename QT, typename KT, int D>
 hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, float *scores,
                       int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st) {
@@ -440,6 +523,48 @@ hipError_t dispatch_d(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
                       int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st) {
     return ix.d_idx == 64 ? dispatch_h<QT, KT, 64>(ix, log2r, b, scores, ld, pm, grid, st)
                           : dispatch_h<QT, KT, 128>(ix, log2r, b, scores, ld, pm, grid, st);
+}
+
+struct FusedArgs {
+    const uint16_t *q_idx;
+    const float *w;
+    void *kc, *kc_scale;
+    const int64_t *kv_off, *blk_off;
+    int num_seqs, log2r;
+    float *scores;
+    int64_t ld;
+    PageMap pm;
+    const void *k_new;
+    float inv_ratio;
+    RingArgs ring;
+    KvArgs kv;
+    int32_t *status;
+};
+
+template <typename KT, int D, int H, typename TIn>
+hipError_t fused_launch(const FusedArgs &f, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((ingest_score_kernel<KT, D, H, TIn>), grid, dim3(kExactThreads), 0, st, f.q_idx, f.w,
+                       static_cast<KT *>(f.kc), f.kc_scale, f.kv_off, f.blk_off, f.num_seqs, f.log2r, f.scores,
+                       f.ld, f.pm, static_cast<const TIn *>(f.k_new), f.inv_ratio, f.ring, f.kv, f.status);
+    return hipGetLastError();
+}
+
+template <typename KT, int D, typename TIn>
+hipError_t fused_h(const FusedArgs &f, int h, dim3 grid, hipStream_t st) {
+    switch (h) {
+    case 1: return fused_launch<KT, D, 1, TIn>(f, grid, st);
+    case 2: return fused_launch<KT, D, 2, TIn>(f, grid, st);
+    case 4: return fused_launch<KT, D, 4, TIn>(f, grid, st);
+    case 8: return fused_launch<KT, D, 8, TIn>(f, grid, st);
+    default: return fused_launch<KT, D, 16, TIn>(f, grid, st);
+    }
+}
+
+template <typename KT>
+hipError_t fused_d(const FusedArgs &f, int d, int h, bool k_bf16, dim3 grid, hipStream_t st) {
+    if (d == 64)
+        return k_bf16 ? fused_h<KT, 64, uint16_t>(f, h, grid, st) : fused_h<KT, 64, float>(f, h, grid, st);
+    return k_bf16 ? fused_h<KT, 128, uint16_t>(f, h, grid, st) : fused_h<KT, 128, float>(f, h, grid, st);
 }
 
 }  // namespace
@@ -500,6 +625,51 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
                   : dispatch_d<float, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st);
     default:   // fp4 keys take a bf16 query (checked by the caller)
         return dispatch_d<uint16_t, Fp4x2>(ix, log2r, b, scores, ld, pm, grid, st);
+    }
+}
+
+hipError_t launch_ingest_score(const void *k_new, int k_dtype, int ratio, const qsa_batch &b,
+                               const qsa_key_ring &ring, const qsa_kv_append *kv, int32_t *status,
+                               const qsa_indexer &ix, float *scores, int64_t ld, const qsa_paged_kv *pg,
+                               hipStream_t st) {
+    if (b.num_seqs == 0) return hipSuccess;
+    FusedArgs f;
+    f.q_idx = static_cast<const uint16_t *>(ix.q_idx);
+    f.w = ix.w;
+    f.kc = const_cast<void *>(ix.kc);
+    f.kc_scale = const_cast<void *>(ix.kc_scale);
+    f.kv_off = b.kv_offsets;
+    f.blk_off = b.blk_offsets;
+    f.num_seqs = b.num_seqs;
+    f.log2r = __builtin_ctz((unsigned)ratio);
+    f.scores = scores;
+    f.ld = ld;
+    f.pm = page_map(pg);
+    f.k_new = k_new;
+    f.inv_ratio = 1.0f / (float)(1 << f.log2r);
+    f.ring = RingArgs{ring.keys, ring.window, ring.slots, ring.num_slots, (int64_t)ring.capacity};
+    f.kv = KvArgs{nullptr, nullptr, nullptr, nullptr, 0};
+    if (kv) {
+        f.kv.k_new = static_cast<const uint8_t *>(kv->k_new);
+        f.kv.v_new = static_cast<const uint8_t *>(kv->v_new);
+        f.kv.k = static_cast<uint8_t *>(kv->k);
+        f.kv.v = static_cast<uint8_t *>(kv->v);
+        f.kv.row_bytes = kv->hkv * kv->d * (kv->dtype == QSA_BF16 ? 2 : 4);
+    }
+    f.status = status;
+    // x: one scoring workgroup per query, then one append wave per sequence;
+    // y: the scorer's 256-block groups (at least one, for the appends)
+    const int64_t max_nb = b.max_kv_len >> f.log2r;
+    const int waves = kExactThreads / kWave;
+    dim3 grid((unsigned)(b.num_seqs + (b.num_seqs + waves - 1) / waves),
+              (unsigned)(max_nb > 0 ? (max_nb + kExactThreads - 1) / kExactThreads : 1));
+    trace("ingest_score grid=(%u,%u) h_idx=%d d_idx=%d kc=%d kv=%d", grid.x, grid.y, ix.h_idx, ix.d_idx,
+          ix.kc_dtype, f.kv.row_bytes);
+    const bool kb = k_dtype == QSA_BF16;
+    switch (ix.kc_dtype) {
+    case QSA_BF16: return fused_d<uint16_t>(f, ix.d_idx, ix.h_idx, kb, grid, st);
+    case QSA_FP8_E4M3: return fused_d<uint8_t>(f, ix.d_idx, ix.h_idx, kb, grid, st);
+    default: return fused_d<Fp4x2>(f, ix.d_idx, ix.h_idx, kb, grid, st);   // fp4 (checked by the caller)
     }
 }
 

@@ -15,7 +15,7 @@ import numpy as np
 
 from . import (INGEST_OK, MAX_LAYERS, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA,
                Batch, KeyRing, Paging, attn_layers_workspace_size, attn_workspace_size, compress_keys,
-               index_score, ingest, pool_scores, sparse_attn_decode, sparse_attn_decode_layers,
+               index_score, ingest, ingest_index_score, pool_scores, sparse_attn_decode, sparse_attn_decode_layers,
                sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
@@ -71,6 +71,7 @@ class DeviceProblem:
     local_blocks: int = 0                  # recent complete blocks always kept (set_local_blocks())
     token_pool: Optional[int] = None       # QSA_POOL_*: block scores pooled from token scores
     tok_scores: Optional[torch.Tensor] = None
+    fuse_ingest: bool = True               # append + canonical scores in one launch when possible
 
     @property
     def blocks_per_query(self) -> int:
@@ -87,6 +88,21 @@ class DeviceProblem:
         ingest(st.k_new, self.ratio, self.batch, st.ring, self.kc, self.kc_scale,
                kv=(st.k_row, st.v_row, self.K, self.V), status=st.status, stream=stream,
                paging=self.paging)
+
+    def ingest_fusable(self, mode: int = QSA_SCORE_CANONICAL) -> bool:
+        """Whether the append and the scores can run as one qsa_ingest_index_score
+        launch: a decode batch, canonical scores on compressed keys, a bf16
+        query and bf16 / e4m3 / fp4 keys."""
+        return (self.fuse_ingest and self.ing is not None and self.batch.q_offsets is None
+                and mode == QSA_SCORE_CANONICAL and self.token_pool is None
+                and self.q_idx.dtype == torch.bfloat16 and self.kc.dtype != torch.float32)
+
+    def ingest_score(self, stream=None) -> None:
+        """qsa_ingest_index_score: ingest() and score() in one launch."""
+        st = self.ing
+        ingest_index_score(st.k_new, self.ratio, self.batch, st.ring, self.q_idx, self.w, self.kc,
+                           self.kc_scale, self.scores, kv=(st.k_row, st.v_row, self.K, self.V),
+                           status=st.status, stream=stream, paging=self.paging)
 
     def score(self, mode: int = QSA_SCORE_CANONICAL, stream=None) -> None:
         if self.token_pool is not None:
@@ -115,9 +131,13 @@ class DeviceProblem:
 
     def step(self, mfma: bool = False, stream=None) -> None:
         """One pass of the hot path: [ingest ->] score -> top-k -> sparse attention."""
-        if self.ing is not None:
-            self.ingest(stream=stream)
-        self.score(QSA_SCORE_MFMA if mfma else QSA_SCORE_CANONICAL, stream=stream)
+        mode = QSA_SCORE_MFMA if mfma else QSA_SCORE_CANONICAL
+        if self.ingest_fusable(mode):
+            self.ingest_score(stream=stream)
+        else:
+            if self.ing is not None:
+                self.ingest(stream=stream)
+            self.score(mode, stream=stream)
         self.topk(certified=mfma, stream=stream)
         self.attend(stream=stream)
 

@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -179,6 +179,14 @@ def decode_layers(layers=None, n=None, outs="default", ws=FAKE, nws=1 << 30, b=N
                                                  None, None)
 
 
+def ingest_score(b=None, ix=None, scores=FAKE, ld=1024, kdt=Q.QSA_BF16):
+    b = b or _batch()
+    ix = ix or _ix()
+    ring = _ring()
+    return Q.lib().qsa_ingest_index_score(P(FAKE), kdt, 4, ctypes.byref(b), ctypes.byref(ring), None, None,
+                                          ctypes.byref(ix), P(scores), ld, None, None)
+
+
 INV, UNS, WS = Q.QSA_ERR_INVALID_ARGUMENT, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
 
 CASES = [
@@ -264,6 +272,13 @@ CASES = [
     ("layers workspace small", lambda: decode_layers(nws=16), WS, "qsa_attn_layers_workspace_size"),
     ("layers multi-query batch",
      lambda: decode_layers(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)), INV, "one query"),
+    ("ingest+score multi-query batch", lambda: ingest_score(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)),
+     INV, "q_offsets must be NULL"),
+    ("ingest+score f32 keys", lambda: ingest_score(ix=_ix(kc_dtype=Q.QSA_F32)), UNS, "bf16, e4m3 or fp4"),
+    ("ingest+score f32 query", lambda: ingest_score(ix=_ix(q_dtype=Q.QSA_F32)), UNS, "bf16 q_idx"),
+    ("ingest+score null scores", lambda: ingest_score(scores=None), INV, "scores is NULL"),
+    ("ingest+score ld small", lambda: ingest_score(ld=1023), INV, "ld_scores=1023"),
+    ("ingest+score raw key fp8", lambda: ingest_score(kdt=Q.QSA_FP8_E4M3), UNS, "k_dtype"),
     ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
     ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]

@@ -1,0 +1,153 @@
+"""qsa_ingest_index_score (the decode step's append and canonical scores in
+one launch) against the two calls it replaces, qsa_ingest followed by
+qsa_index_score, on two copies of the same state.  Random histories of
+one-token appends with implicit rollbacks (blocks whose older keys the ring
+lost), sequences pointed at an invalid ring slot, every compressed-key
+format, both raw-key dtypes, paged and contiguous caches.  After every step,
+bit for bit: scores, compressed keys and scales, ring keys and windows,
+statuses and K/V rows.  (The two calls themselves are checked against the
+oracle in test_gpu_ingest.py and the parity tests.)"""
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_sparse_amd as Q
+from tests.parity import gpu_available
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def _bits(t):
+    if t.dtype in (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu):
+        t = t.view(torch.uint8)
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy()
+    return t.numpy()
+
+
+class State:
+    def __init__(self, B, max_len, r, cap, d, H, k_dtype, kind, hkv, paged, seed):
+        g = torch.Generator().manual_seed(seed)
+        rng = np.random.default_rng(seed)
+        self.B, self.max_len, self.r, self.d, self.H = B, max_len, r, d, H
+        self.paged = paged
+        if paged:
+            P = max(16, 2 * r)
+            pps = -(-max_len // P)
+            num_pages = B * pps + 3
+            table = rng.permutation(num_pages)[:B * pps].reshape(B, pps).astype(np.int32)
+            self.paging = Q.Paging(torch.from_numpy(table).to(DEV), num_pages, P)
+            rows, brows = num_pages * P, num_pages * (P // r)
+        else:
+            self.paging = None
+            rows, brows = B * max_len, B * (max_len // r)
+        if kind == "fp4":
+            self.kc = torch.randint(0, 255, (brows, d // 2), generator=g, dtype=torch.uint8).to(DEV) \
+                .view(torch.float4_e2m1fn_x2)
+            self.kc_scale = torch.randint(100, 140, (brows, d // 32), generator=g, dtype=torch.uint8).to(DEV) \
+                .view(torch.float8_e8m0fnu)
+        elif kind == "e4m3":
+            self.kc = torch.randint(0, 126, (brows, d), generator=g, dtype=torch.uint8).to(DEV)
+            self.kc_scale = torch.rand(brows, generator=g).to(DEV)
+        else:
+            self.kc = torch.randn((brows, d), generator=g).to(torch.bfloat16).to(DEV)
+            self.kc_scale = None
+        self.K = torch.randn((rows, hkv, 128), generator=g).to(torch.bfloat16).to(DEV) if hkv else None
+        self.V = torch.randn((rows, hkv, 128), generator=g).to(torch.bfloat16).to(DEV) if hkv else None
+        self.num_slots = B + 2
+        self.ring = Q.KeyRing(torch.randn((self.num_slots, cap, d), generator=g).to(k_dtype).to(DEV),
+                              torch.zeros((self.num_slots, 2), dtype=torch.int64, device=DEV),
+                              torch.zeros(B, dtype=torch.int32, device=DEV))
+        self.status = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+        self.ld = -(-max_len // r) + 3
+        self.scores = torch.full((B, self.ld), float("nan"), device=DEV)
+
+    def clone(self):
+        c = object.__new__(State)
+        c.__dict__.update(self.__dict__)
+        for n in ("kc", "kc_scale", "K", "V", "status", "scores"):
+            t = getattr(self, n)
+            setattr(c, n, None if t is None else t.clone())
+        c.ring = Q.KeyRing(self.ring.keys.clone(), self.ring.window.clone(), self.ring.slots.clone())
+        return c
+
+    def batch(self, lens):
+        kv = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)).to(DEV)
+        blk = torch.from_numpy(np.concatenate([[0], np.cumsum([n // self.r for n in lens])]).astype(np.int64)).to(DEV)
+        return Q.Batch(kv, blk, None, self.B, self.max_len, 1)
+
+    def tensors(self):
+        out = {"kc": self.kc, "K": self.K, "V": self.V, "status": self.status, "scores": self.scores,
+               "ring": self.ring.keys, "window": self.ring.window}
+        if self.kc_scale is not None:
+            out["kc_scale"] = self.kc_scale
+        return {k: v for k, v in out.items() if v is not None}
+
+
+CASES = [  # (kind, k dtype, d, H, ratio, capacity, hkv, paged)
+    ("bf16", torch.bfloat16, 128, 8, 4, 8, 2, True),
+    ("e4m3", torch.float32, 128, 16, 4, 12, 2, True),
+    ("fp4", torch.bfloat16, 128, 8, 4, 8, 0, True),
+    ("fp4", torch.float32, 64, 4, 8, 16, 2, False),
+    ("e4m3", torch.bfloat16, 64, 1, 4, 4, 0, False),
+    ("bf16", torch.float32, 64, 2, 16, 32, 1, False),
+    ("fp4", torch.bfloat16, 64, 16, 16, 16, 2, True),
+]
+
+
+@pytest.mark.parametrize("kind,k_dtype,d,H,r,cap,hkv,paged", CASES,
+                         ids=[f"{c[0]}-{str(c[1])[6:]}-d{c[2]}-h{c[3]}-r{c[4]}-{'paged' if c[7] else 'flat'}"
+                              for c in CASES])
+def test_fused_equals_ingest_then_score(kind, k_dtype, d, H, r, cap, hkv, paged):
+    B, max_len = 6, 240
+    seed = 17 * d + 3 * r + H + (1 if paged else 0)
+    rng = np.random.default_rng(seed)
+    a = State(B, max_len, r, cap, d, H, k_dtype, kind, hkv, paged, seed)
+    b = a.clone()
+    slot_of = rng.permutation(a.num_slots)[:B].astype(np.int32)
+    lens = [int(x) for x in rng.integers(1, 120, B)]
+    g = torch.Generator().manual_seed(seed)
+    n_stored = n_lost = n_bad = 0
+    for step in range(48):
+        for s in range(B):
+            u = rng.random()
+            if u < 0.1 and lens[s] > 2 * r:           # implicit rollback: a shorter N on this append
+                lens[s] -= int(rng.integers(1, 2 * r))
+            lens[s] = min(lens[s] + 1, max_len)
+        slots = slot_of.copy()
+        bad = rng.random(B) < 0.06
+        slots[bad] = -1
+        n_bad += int(bad.sum())
+        for st in (a, b):
+            st.ring.slots.copy_(torch.from_numpy(slots))
+        batch = a.batch(lens)
+        k_new = torch.randn((B, d), generator=g).to(k_dtype).to(DEV)
+        q_idx = torch.randn((B, H, d), generator=g).to(torch.bfloat16).to(DEV)
+        w = torch.rand((B, H), generator=g).to(DEV)
+        kvn = None
+        if hkv:
+            kvn = (torch.randn((B, hkv, 128), generator=g).to(torch.bfloat16).to(DEV),
+                   torch.randn((B, hkv, 128), generator=g).to(torch.bfloat16).to(DEV))
+        # the two calls
+        Q.ingest(k_new, r, batch, a.ring, a.kc, a.kc_scale,
+                 kv=None if kvn is None else (kvn[0], kvn[1], a.K, a.V), status=a.status, paging=a.paging)
+        Q.index_score(q_idx, w, a.kc, a.kc_scale, r, batch, a.scores, paging=a.paging)
+        # one launch
+        Q.ingest_index_score(k_new, r, batch, b.ring, q_idx, w, b.kc, b.kc_scale, b.scores,
+                             kv=None if kvn is None else (kvn[0], kvn[1], b.K, b.V), status=b.status,
+                             paging=b.paging)
+        torch.cuda.synchronize()
+        ta, tb = a.tensors(), b.tensors()
+        for name in ta:
+            assert np.array_equal(_bits(ta[name]), _bits(tb[name])), (step, name)
+        st = a.status.cpu().numpy()
+        done = np.array([n % r == 0 for n in lens])
+        n_stored += int(((st == Q.INGEST_OK) & done).sum())
+        n_lost += int((st == Q.INGEST_LOST_KEYS).sum())
+    # the histories reached every path of the fused kernel
+    assert n_stored > 0 and n_lost > 0 and n_bad > 0
