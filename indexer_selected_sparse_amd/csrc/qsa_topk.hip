@@ -531,7 +531,10 @@ struct BandKey {
     __device__ __forceinline__ uint32_t operator()(int64_t j) const { return keys[cand[j]]; }
 };
 
-__global__ __launch_bounds__(kTopkThreads) void topk_cert_kernel(
+// At most 64 VGPRs (8 waves per SIMD), so that two rows' workgroups share a
+// CU as with the plain selection; at 90 VGPRs one row held a CU alone and
+// a prefill batch took twice as long.
+__global__ __launch_bounds__(kTopkThreads, 8) void topk_cert_kernel(
     const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
     int log2r, int K, int32_t *__restrict__ idx, int ldi, CertIndexer ix,
