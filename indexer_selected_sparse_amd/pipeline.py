@@ -293,6 +293,9 @@ class LayerStack:
     def __post_init__(self):
         if self.full_every < 1:
             raise ValueError("full_every must be >= 1")
+        if any(dp.ing is not None for dp in self.layers):
+            raise ValueError("LayerStack runs score, top-k and attention only; append each layer's new tokens "
+                             "(qsa_ingest) before its step")
         self.full = [l % self.full_every == 0 for l in range(len(self.layers))]
         src = None
         for dp, f in zip(self.layers, self.full):
