@@ -120,7 +120,7 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio);
 
 /* Thread-local text of the last error ("" if none). Never NULL. */
 const char *qsa_last_error(void);
-/* Library version string, e.g. "qsa 0.2.0 (abi 2, gfx950)". */
+/* Library version string, e.g. "qsa 0.4.0 (abi 2, gfx950)". */
 const char *qsa_version(void);
 /* QSA_ABI_VERSION the library was built with. */
 int32_t qsa_abi_version(void);

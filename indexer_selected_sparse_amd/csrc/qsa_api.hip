@@ -219,7 +219,7 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio) {
 
 const char *qsa_last_error(void) { return g_err; }
 
-const char *qsa_version(void) { return "qsa 0.3.0 (abi 2, gfx950)"; }
+const char *qsa_version(void) { return "qsa 0.4.0 (abi 2, gfx950)"; }
 
 int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
