@@ -97,3 +97,38 @@ def test_fused_layers_equal_per_layer_calls(n_layers, full_every, paged):
                              wl.V[a0:b0].float().numpy(), toks, sp.softmax_scale)
     check_out(wl, {"out": dp.out.float().cpu().numpy().astype(np.float64)}, {"out": exp},
               np.arange(wl.total_q))
+
+
+@pytest.mark.parametrize("cfg,lens", [("tiny_decode", [4096, 1500]), ("batched_decode", [9000, 1234, 80, 20000, 4099])])
+def test_layers_api_each_layer_its_own_scale(cfg, lens):
+    """qsa_sparse_attn_decode_layers with a different q, K, V and softmax scale
+    per layer equals each layer's own decode call bit for bit (bf16: one
+    layered launch; fp32: the per-layer launches it falls back to)."""
+    import indexer_selected_sparse_amd as Q
+    sp = W.CONFIGS[cfg]
+    base = pipeline.upload(W.make(sp, lens=lens, seed=71), "cuda")
+    base.compress()
+    base.score()
+    base.topk()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+
+    def fresh(t):
+        return torch.randn(t.shape, generator=gen, device="cuda", dtype=torch.float32).to(t.dtype)
+
+    n = 3
+    layers = [(base.q, base.K, base.V, base.softmax_scale)]
+    for l in range(1, n):
+        layers.append((fresh(base.q), fresh(base.K), fresh(base.V), base.softmax_scale * (1.0 + 0.25 * l)))
+    outs = [torch.full_like(base.out, float("nan")) for _ in range(n)]
+    nws = Q.attn_layers_workspace_size(*layers[0], n, base.budget, base.ratio, base.batch)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    Q.sparse_attn_decode_layers(layers, base.idx, base.budget, base.ratio, base.batch, outs, ws)
+    torch.cuda.synchronize()
+    for l, (q, K, V, sc) in enumerate(layers):
+        ref = torch.full_like(base.out, float("nan"))
+        one = Q.attn_workspace_size(q, K, V, sc, base.budget, base.ratio, base.batch)
+        w1 = torch.empty(max(one, 1), dtype=torch.uint8, device="cuda")
+        Q.sparse_attn_decode(q, K, V, sc, base.idx, base.budget, base.ratio, base.batch, ref, w1)
+        torch.cuda.synchronize()
+        bits = torch.int16 if ref.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(outs[l].view(bits), ref.view(bits)), l
