@@ -129,6 +129,19 @@ def e2m1_encode(x) -> np.ndarray:
     return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
 
 
+_FP4_TABLE = None
+
+
+def fp4_value_table() -> np.ndarray:
+    """[16, 256] float32: the exact value of E2M1 code c under E8M0 scale
+    byte e (qo_fp4_value: code value times 2^(e - 127))."""
+    global _FP4_TABLE
+    if _FP4_TABLE is None:
+        f = lib().qo_fp4_value
+        _FP4_TABLE = np.array([[f(c, e) for e in range(256)] for c in range(16)], dtype=np.float32)
+    return _FP4_TABLE
+
+
 def e8m0_exponent(amax: float) -> int:
     return int(lib().qo_e8m0_exponent(float(amax)))
 
@@ -180,9 +193,8 @@ def kc_values(kc, kind: str, scale=None) -> np.ndarray:
         codes = np.empty((nb, 2 * half), dtype=np.uint8)
         codes[:, 0::2] = kc & 15
         codes[:, 1::2] = kc >> 4
-        vals = e2m1_decode(codes).astype(np.float64)
-        exps = np.repeat(np.asarray(scale, dtype=np.int64) - 127, 32, axis=1)
-        return np.ldexp(vals, exps).astype(np.float32)
+        exps = np.repeat(np.asarray(scale, dtype=np.uint8), 32, axis=1)
+        return fp4_value_table()[codes, exps]
     return e4m3_decode(kc)
 
 

@@ -434,6 +434,18 @@ def test_e8m0_exponent_is_floor_log2_minus_two():
     assert oracle.e8m0_exponent(0.0) == -127
 
 
+def test_fp4_value_is_code_value_times_power_of_two():
+    # every (code, scale byte) a stored row can hold: the E2M1 value of the
+    # format table times 2^(e - 127), exact in fp32 (e = 0 is 2^-127)
+    tab = oracle.fp4_value_table()
+    for c in range(16):
+        mag = E2M1_MAGNITUDES[c & 7]
+        for e in range(255):
+            want = np.float32(math.ldexp(-mag if c & 8 else mag, e - 127))
+            got = tab[c, e]
+            assert got.view(np.uint32) == want.view(np.uint32), (c, e, got, want)
+
+
 def test_fp4_compress_hand_worked_block():
     # ratio 1, 64 dims = two groups.  Group 0 holds 4 (amax 4: floor(log2) 2,
     # X = 0, scale 1) so its other values are coded as they are; group 1 is
