@@ -32,9 +32,25 @@
  *    the limit.  A failed kernel launch returns QSA_ERR_HIP with the HIP
  *    error text.  Device-side contents (offset arrays) are not read by the
  *    host; they must satisfy the layout rules below (out-of-contract
- *    contents are undefined behaviour).  NaN/Inf inputs are out of contract.
+ *    contents are undefined behaviour, and are caught in debug mode, below).
+ *    NaN/Inf inputs are out of contract.
  *  - The library never substitutes dense attention for sparse attention past
  *    the inert bound: the regime is decided per query from its own L.
+ *  - Debug mode (environment variable QSA_DEBUG=1, read on every call):
+ *    before its own kernels each call runs a check of the device arrays it
+ *    reads — kv_offsets[0] == 0 and 0 <= N_s <= max_kv_len; blk_offsets (when
+ *    read) the prefix sums of floor(N_s/ratio); q_offsets[0] == 0,
+ *    q_offsets[B] == total_q and 0 <= n_s <= min(N_s, max_q_per_seq); every
+ *    idx entry read by attention in [-1, floor(L/ratio)); every block-table
+ *    entry of a used page in [0, num_pages) — waits for it, and on a
+ *    violation returns QSA_ERR_DEVICE_ASSERT (qsa_last_error() names the
+ *    rule, the sequence or query and the value) without launching anything
+ *    else.  Calls then also wait for their own kernels, so a debug-mode call
+ *    synchronises its stream and cannot be captured in a graph.  ("Atlas
+ *    Flash-Next defect investigations" page, Defect 4, proposed fix, items
+ *    1-2, and fix plan PR-G: debug asserts on offsets and typed row offsets.)
+ *  - Test hook: with QSA_TEST_FORCE_LAUNCH_ERROR=1 every call that passes
+ *    host validation returns QSA_ERR_HIP without touching a device.
  *
  * Layouts (row-major, varlen-packed, int64 offsets [B+1] with offsets[0]=0):
  *  k_idx [sum N_s, d_idx]; K, V [sum N_s, hkv, d];
@@ -57,14 +73,17 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 typedef enum qsa_status {
     QSA_OK = 0,
     QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, inconsistent sizes */
     QSA_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels implement */
     QSA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
-    QSA_ERR_HIP = 4               /* a HIP call or kernel launch failed */
+    QSA_ERR_HIP = 4,              /* a HIP call or kernel launch failed */
+    QSA_ERR_DEVICE_ASSERT = 5     /* debug mode only: the contents of a device argument broke
+                                     the layout rules (see "Debug mode" above); nothing of the
+                                     call was launched */
 } qsa_status;
 
 typedef enum qsa_dtype {
@@ -120,7 +139,7 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio);
 
 /* Thread-local text of the last error ("" if none). Never NULL. */
 const char *qsa_last_error(void);
-/* Library version string, e.g. "qsa 0.4.0 (abi 2, gfx950)". */
+/* Library version string, e.g. "qsa 0.5.0 (abi 3, gfx950)". */
 const char *qsa_version(void);
 /* QSA_ABI_VERSION the library was built with. */
 int32_t qsa_abi_version(void);

@@ -22,7 +22,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
-QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_HIP = range(5)
+QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_HIP, QSA_ERR_DEVICE_ASSERT = range(6)
+ABI_VERSION = 3   # QSA_ABI_VERSION of include/qsa.h
 QSA_F32, QSA_BF16, QSA_FP8_E4M3, QSA_FP4_E2M1 = 0, 1, 2, 3
 QSA_SCORE_CANONICAL, QSA_SCORE_MFMA = 0, 1
 QSA_POOL_MAX, QSA_POOL_MEAN = 0, 1

@@ -11,6 +11,7 @@
 #include <set>
 #include <tuple>
 
+#include "qsa_debug.hpp"
 #include "qsa_internal.hpp"
 
 namespace qsa {
@@ -66,6 +67,83 @@ void trace(const char *fmt, ...) {
     vfprintf(stderr, fmt, ap);
     fprintf(stderr, "\n");
     va_end(ap);
+}
+
+static bool env_flag(const char *name) {
+    const char *s = getenv(name);
+    return s && s[0] && s[0] != '0';
+}
+
+// QSA_DEBUG=1: device-side argument contents are checked before every
+// launch, and every call waits for its kernels (so that a fault is reported
+// by the call that caused it).  Read on every call, so a process can switch
+// it on and off; a call in debug mode synchronises and cannot be captured in
+// a graph.
+static bool debug_enabled() { return env_flag("QSA_DEBUG"); }
+
+// QSA_TEST_FORCE_LAUNCH_ERROR=1: every entry point that passes host
+// validation returns QSA_ERR_HIP without touching a device (a test hook for
+// the error path of a failed launch).
+static bool forced_launch_error() { return env_flag("QSA_TEST_FORCE_LAUNCH_ERROR"); }
+
+static const char *debug_check_name(int32_t code) {
+    switch (code) {
+    case QSA_DBG_KV_OFFSETS: return "kv_offsets: offsets[0] != 0, a negative length or a length past max_kv_len";
+    case QSA_DBG_BLK_OFFSETS: return "blk_offsets: not the prefix sums of floor(N_s/ratio)";
+    case QSA_DBG_Q_OFFSETS:
+        return "q_offsets: offsets[0] != 0, offsets[B] != total_q, or a query count below 0, above N_s or above "
+               "max_q_per_seq";
+    case QSA_DBG_IDX_RANGE: return "idx: a selected block id outside [-1, floor(L/ratio))";
+    case QSA_DBG_PAGE_ID: return "block_table: a page id outside [0, num_pages)";
+    default: return "unknown check";
+    }
+}
+
+// What the debug check reads for a call on batch b (blk: the call reads
+// blk_offsets; pg: the paging descriptor or NULL).
+static DebugCheck batch_check(const qsa_batch &b, int32_t ratio, bool blk, const qsa_paged_kv *pg) {
+    DebugCheck c;
+    c.kv_off = b.kv_offsets;
+    c.blk_off = blk ? b.blk_offsets : nullptr;
+    c.q_off = b.q_offsets;
+    c.num_seqs = b.num_seqs;
+    c.max_q_per_seq = b.q_offsets ? b.max_q_per_seq : 1;
+    c.total_q = b.total_q;
+    c.max_kv_len = b.max_kv_len;
+    c.log2r = ratio > 0 ? __builtin_ctz((unsigned)ratio) : 0;
+    if (pg) {
+        c.table = pg->block_table;
+        c.max_pages = pg->max_pages;
+        c.num_pages = pg->num_pages;
+        c.page_size = pg->page_size;
+    }
+    return c;
+}
+
+// Run one validated call's launches: the forced-error hook, the debug check
+// of device contents (nothing of the call is launched on a violation), the
+// launch itself and, in debug mode, a wait for it.
+template <typename F>
+static qsa_status launch_checked(const char *what, const DebugCheck &dc, void *stream, F &&launch) {
+    if (forced_launch_error())
+        return fail(QSA_ERR_HIP, "%s: launch failed (forced by QSA_TEST_FORCE_LAUNCH_ERROR)", what);
+    hipStream_t st = (hipStream_t)stream;
+    const bool dbg = debug_enabled();
+    if (dbg) {
+        int32_t code = 0;
+        int64_t where = 0, value = 0;
+        hipError_t e = launch_debug_check(dc, st);
+        if (e == hipSuccess) e = read_debug_status(st, code, where, value);
+        if (e != hipSuccess) return hip_status(e, what);
+        if (code != 0)
+            return fail(QSA_ERR_DEVICE_ASSERT,
+                        "%s: debug check failed: %s (sequence or query %lld, value %lld); nothing was launched",
+                        what, debug_check_name(code), (long long)where, (long long)value);
+        trace("%s: debug check passed", what);
+    }
+    hipError_t e = launch(st);
+    if (e == hipSuccess && dbg) e = hipStreamSynchronize(st);
+    return hip_status(e, what);
 }
 
 static bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -202,8 +280,11 @@ static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t bud
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_attn_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
-    return hip_status(launch_attn(*a, idx, budget, ratio, *b, out, ws, decode, pg, st),
-                      "sparse attention launch");
+    DebugCheck dc = batch_check(*b, ratio, false, pg);
+    dc.idx = idx;
+    dc.ldi = budget / ratio;
+    return launch_checked(decode ? "qsa_sparse_attn_decode" : "qsa_sparse_attn_prefill", dc, st,
+                          [&](hipStream_t s_) { return launch_attn(*a, idx, budget, ratio, *b, out, ws, decode, pg, s_); });
 }
 
 }  // namespace qsa
@@ -219,7 +300,7 @@ int32_t qsa_inert_bound(int32_t budget, int32_t ratio) {
 
 const char *qsa_last_error(void) { return g_err; }
 
-const char *qsa_version(void) { return "qsa 0.4.0 (abi 2, gfx950)"; }
+const char *qsa_version(void) { return "qsa 0.5.0 (abi 3, gfx950)"; }
 
 int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
@@ -243,9 +324,9 @@ static qsa_status compress_common(const void *k_idx, int32_t k_dtype, int32_t d_
     if (d_idx != 64 && d_idx != 128) return fail(QSA_ERR_UNSUPPORTED, "d_idx=%d must be 64 or 128", d_idx);
     if ((b->max_kv_len / ratio) > 0xffffffffLL * 16)
         return fail(QSA_ERR_UNSUPPORTED, "max_kv_len=%lld is too large", (long long)b->max_kv_len);
-    return hip_status(launch_compress(k_idx, k_dtype, d_idx, ratio, *b, first_block, kc, kc_dtype,
-                                      kc_scale, pg, (hipStream_t)stream),
-                      "qsa_compress_keys launch");
+    return launch_checked("qsa_compress_keys", batch_check(*b, ratio, pg == nullptr, pg), stream, [&](hipStream_t st) {
+        return launch_compress(k_idx, k_dtype, d_idx, ratio, *b, first_block, kc, kc_dtype, kc_scale, pg, st);
+    });
 }
 
 qsa_status qsa_compress_keys(const void *k_idx, int32_t k_dtype, int32_t d_idx, int32_t ratio,
@@ -282,9 +363,10 @@ static qsa_status score_common(const qsa_indexer *ix, int32_t ratio, const qsa_b
     if (ld_scores < need_ld || ld_scores < 1)
         return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
                     (long long)ld_scores, (long long)need_ld);
-    hipError_t e = mfma ? launch_score_mfma(*ix, ratio, *b, scores, ld_scores, (hipStream_t)stream)
-                        : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, pg, (hipStream_t)stream);
-    return hip_status(e, "qsa_index_score launch");
+    return launch_checked("qsa_index_score", batch_check(*b, ratio, pg == nullptr, pg), stream, [&](hipStream_t st) {
+        return mfma ? launch_score_mfma(*ix, ratio, *b, scores, ld_scores, st)
+                    : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, pg, st);
+    });
 }
 
 qsa_status qsa_index_score(const qsa_indexer *ix, int32_t ratio, const qsa_batch *b, float *scores,
@@ -332,10 +414,13 @@ static qsa_status topk_common(const float *scores, int64_t ld_scores, const qsa_
         return fail(QSA_ERR_WORKSPACE, "top-k workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_topk_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
     const int ldi = budget / ratio + local_blocks;
-    hipError_t e = launch_topk(scores, ld_scores, recheck, budget, ratio, *b, idx, ldi, ws, (hipStream_t)stream);
-    if (e == hipSuccess && local_blocks > 0)
-        e = launch_topk_local(budget, ratio, local_blocks, *b, idx, ldi, (hipStream_t)stream);
-    return hip_status(e, "qsa_topk_blocks launch");
+    return launch_checked("qsa_topk_blocks", batch_check(*b, ratio, recheck != nullptr, nullptr), stream,
+                          [&](hipStream_t st) {
+                              hipError_t e = launch_topk(scores, ld_scores, recheck, budget, ratio, *b, idx, ldi, ws, st);
+                              if (e == hipSuccess && local_blocks > 0)
+                                  e = launch_topk_local(budget, ratio, local_blocks, *b, idx, ldi, st);
+                              return e;
+                          });
 }
 
 qsa_status qsa_topk_blocks(const float *scores, int64_t ld_scores, const qsa_indexer *recheck,
@@ -408,9 +493,12 @@ qsa_status qsa_sparse_attn_decode_layers(const qsa_attn *layers, int32_t n_layer
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_attn_layers_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
-    return hip_status(launch_attn_layers(layers, n_layers, idx, budget, ratio, *b, outs, ws, pg,
-                                         (hipStream_t)stream),
-                      "layered sparse attention launch");
+    DebugCheck dc = batch_check(*b, ratio, false, pg);
+    dc.idx = idx;
+    dc.ldi = budget / ratio;
+    return launch_checked("qsa_sparse_attn_decode_layers", dc, stream, [&](hipStream_t st) {
+        return launch_attn_layers(layers, n_layers, idx, budget, ratio, *b, outs, ws, pg, st);
+    });
 }
 
 qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, int32_t budget,
@@ -470,9 +558,11 @@ qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t
         return fail(QSA_ERR_INVALID_ARGUMENT, "batch.max_q_per_seq=%d must be >= 0", b->max_q_per_seq);
     s = check_kv_append(kv);
     if (s != QSA_OK) return s;
-    return hip_status(launch_ingest(k_new, k_dtype, d_idx, ratio, *b, *ring, kc, kc_dtype, kc_scale, kv,
-                                    status, pg, (hipStream_t)stream),
-                      "qsa_ingest launch");
+    DebugCheck dc = batch_check(*b, ratio, pg == nullptr, pg);
+    dc.strict_q = false;
+    return launch_checked("qsa_ingest", dc, stream, [&](hipStream_t st) {
+        return launch_ingest(k_new, k_dtype, d_idx, ratio, *b, *ring, kc, kc_dtype, kc_scale, kv, status, pg, st);
+    });
 }
 
 qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ratio, const qsa_batch *b,
@@ -503,9 +593,11 @@ qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ra
     if (ld_scores < need_ld || ld_scores < 1)
         return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
                     (long long)ld_scores, (long long)need_ld);
-    return hip_status(launch_ingest_score(k_new, k_dtype, ratio, *b, *ring, kv, status, *ix, scores, ld_scores, pg,
-                                          (hipStream_t)stream),
-                      "qsa_ingest_index_score launch");
+    return launch_checked("qsa_ingest_index_score", batch_check(*b, ratio, pg == nullptr, pg), stream,
+                          [&](hipStream_t st) {
+                              return launch_ingest_score(k_new, k_dtype, ratio, *b, *ring, kv, status, *ix, scores,
+                                                         ld_scores, pg, st);
+                          });
 }
 
 qsa_status qsa_ring_rewind(const qsa_batch *b, int32_t ratio, const qsa_key_ring *ring, int32_t *status,
@@ -514,8 +606,8 @@ qsa_status qsa_ring_rewind(const qsa_batch *b, int32_t ratio, const qsa_key_ring
     if (s == QSA_OK) s = check_ratio(ratio);
     if (s == QSA_OK) s = check_ring(ring, b, ratio);
     if (s != QSA_OK) return s;
-    return hip_status(launch_ring_rewind(*b, ratio, *ring, status, (hipStream_t)stream),
-                      "qsa_ring_rewind launch");
+    return launch_checked("qsa_ring_rewind", batch_check(*b, ratio, false, nullptr), stream,
+                          [&](hipStream_t st) { return launch_ring_rewind(*b, ratio, *ring, status, st); });
 }
 
 qsa_status qsa_pool_scores(const float *tok, int64_t ld_tok, int32_t ratio, int32_t mode,
@@ -534,8 +626,9 @@ qsa_status qsa_pool_scores(const float *tok, int64_t ld_tok, int32_t ratio, int3
     if (ld_blk < need || ld_blk < 1)
         return fail(QSA_ERR_INVALID_ARGUMENT, "ld_blk=%lld must be >= ceil(max_kv_len/ratio)=%lld",
                     (long long)ld_blk, (long long)need);
-    return hip_status(launch_pool_scores(tok, ld_tok, ratio, mode, *b, blk, ld_blk, (hipStream_t)stream),
-                      "qsa_pool_scores launch");
+    return launch_checked("qsa_pool_scores", batch_check(*b, ratio, false, nullptr), stream, [&](hipStream_t st) {
+        return launch_pool_scores(tok, ld_tok, ratio, mode, *b, blk, ld_blk, st);
+    });
 }
 
 }  // extern "C"

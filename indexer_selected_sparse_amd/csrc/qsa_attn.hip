@@ -644,6 +644,46 @@ __device__ __forceinline__ uint32_t issue_step_lds(const WaveWork &W, int st, in
     return valid;
 }
 
+// Slots a wave holds in LDS when its share of a part exceeds the 128 that
+// tab0 / tab1 hold (prefill with more than 512 selected blocks, or a decode
+// launch with few parts): at most ceil(2048 / 4) (K <= 2048, one part).
+constexpr int kBigTabSlots = 2048 / kWgWaves;
+constexpr int kBigTabBytes = kBigTabSlots * 4;
+typedef __attribute__((address_space(3))) int32_t lds_i32_t;
+
+// issue_step_lds with the wave's slot table in LDS at byte address `tab`
+// (kBigTabSlots entries, -1 past the part's slots): each of lanes 0..15 reads
+// the block id of its own token's slot.
+__device__ __forceinline__ uint32_t issue_step_lds_tab(const WaveWork &W, int st, int lane, uint32_t tab,
+                                                       const uint16_t *__restrict__ kbase,
+                                                       const uint16_t *__restrict__ vbase,
+                                                       uint32_t row_bytes, uint32_t slot) {
+    const int t = st * kStep + (lane & (kStep - 1));
+    int rel = t >> W.log2r;
+    rel = rel > kBigTabSlots - 1 ? kBigTabSlots - 1 : rel;
+    const int b = *(const lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)rel);
+    int row = 0;
+    bool ok = false;
+    if (t < W.nblk_tok) {
+        ok = b >= 0 && (int64_t)b < W.nb;
+        row = ok ? (b << W.log2r) + (t & ((1 << W.log2r) - 1)) : 0;
+    } else if (t < W.ntok) {
+        row = (int)(W.tail0 + (t - W.nblk_tok));
+        ok = true;
+    }
+    const uint32_t valid = (uint32_t)__ballot(ok && lane < kStep) & 0xffffu;
+    const int p = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tq = 4 * j + (lane >> 4);
+        const int r = __builtin_amdgcn_ds_bpermute(tq << 2, row);
+        const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)((p ^ tq) << 4);
+        dma16_off(kbase, off, slot + j * 1024);
+        dma16_off(vbase, off, slot + 4096 + j * 1024);
+    }
+    return valid;
+}
+
 // Wait until step `st` has landed when only `left` later steps are in flight
 // (the ring's drain at the end of a part).
 template <int D>
@@ -691,7 +731,7 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 //      gfx950 transposed LDS load (ds_read_b64_tr_b16: lane i of each 16-lane
 //      group gets column i of the four rows its group points at).
 //  Lane l accumulates O^T for head l%16, dims 16m + 4(l/16) + 0..3, m < 8.
-template <int D>
+template <int D, bool BIG>
 __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -724,8 +764,11 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     split(A.K, s_beg, s_end);
     const int32_t *sel = A.idx + i * (int64_t)A.K + s_beg;
     int nslot = (int)(s_end - s_beg);
-    uint32_t tab0 = (uint32_t)(lane < nslot ? sel[lane] : -1);
-    uint32_t tab1 = (uint32_t)(kWave + lane < nslot ? sel[kWave + lane] : -1);
+    uint32_t tab0 = 0, tab1 = 0;
+    if constexpr (!BIG) {
+        tab0 = (uint32_t)(lane < nslot ? sel[lane] : -1);
+        tab1 = (uint32_t)(kWave + lane < nslot ? sel[kWave + lane] : -1);
+    }
 
     const QueryPos qp = query_pos(A.kv_off, nullptr, A.q_off, A.num_seqs, i);
     const int64_t nb = qp.L >> A.log2r;
@@ -734,8 +777,24 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
         split((int)nsel, s_beg, s_end);
         sel = A.idx + i * (int64_t)A.K + s_beg;
         nslot = (int)(s_end - s_beg);
-        tab0 = (uint32_t)(lane < nslot ? sel[lane] : -1);
-        tab1 = (uint32_t)(kWave + lane < nslot ? sel[kWave + lane] : -1);
+        if constexpr (!BIG) {
+            tab0 = (uint32_t)(lane < nslot ? sel[lane] : -1);
+            tab1 = (uint32_t)(kWave + lane < nslot ? sel[kWave + lane] : -1);
+        }
+    }
+    // BIG: the whole share (at most kBigTabSlots slots) into this wave's LDS
+    // table, block ids translated to pool blocks when paged, -1 past the end.
+    const uint32_t big_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes + wave * kBigTabBytes);
+    if constexpr (BIG) {
+        int32_t v[kBigTabSlots / kWave];
+#pragma unroll
+        for (int j = 0; j < kBigTabSlots / kWave; ++j)
+            v[j] = j * kWave + lane < nslot ? sel[j * kWave + lane] : -1;
+#pragma unroll
+        for (int j = 0; j < kBigTabSlots / kWave; ++j) {
+            const int32_t b = A.pm.table ? slot_phys(v[j], A.pm, qp.seq, nb, A.log2r) : v[j];
+            *(lds_i32_t *)(uintptr_t)(big_tab + 4u * (uint32_t)(j * kWave + lane)) = b;
+        }
     }
     const bool owns_tail = c == A.n_part - 1 && wave == kWgWaves - 1;
     WaveWork W;
@@ -748,8 +807,10 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     W.ntok = W.nblk_tok + (owns_tail ? (int)(qp.L - W.tail0) : 0);
     if (A.pm.table) {                                // paged pools: physical block ids and rows
         page_wave(W, A.pm, qp.seq, qp.L);
-        tab0 = (uint32_t)slot_phys((int)tab0, A.pm, qp.seq, nb, A.log2r);
-        tab1 = (uint32_t)slot_phys((int)tab1, A.pm, qp.seq, nb, A.log2r);
+        if constexpr (!BIG) {
+            tab0 = (uint32_t)slot_phys((int)tab0, A.pm, qp.seq, nb, A.log2r);
+            tab1 = (uint32_t)slot_phys((int)tab1, A.pm, qp.seq, nb, A.log2r);
+        }
     }
     const int64_t row0 = A.pm.table ? 0 : qp.kv_row0;
 
@@ -785,8 +846,11 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     int pending = 0;
     int slot_in = 0, slot_out = 0;
     auto issue = [&](int s) {
-        const uint32_t m = issue_step_lds(W, s, lane, tab0, tab1, kbase, vbase, row_bytes,
-                                          ring_addr + slot_in * kSlotBytes);
+        uint32_t m;
+        if constexpr (BIG)
+            m = issue_step_lds_tab(W, s, lane, big_tab, kbase, vbase, row_bytes, ring_addr + slot_in * kSlotBytes);
+        else
+            m = issue_step_lds(W, s, lane, tab0, tab1, kbase, vbase, row_bytes, ring_addr + slot_in * kSlotBytes);
         fifo |= (uint64_t)m << (16 * pending);
         ++pending;
         slot_in = slot_in + 1 == D ? 0 : slot_in + 1;
@@ -957,7 +1021,7 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     }
 }
 
-template <int D>
+template <int D, bool BIG>
 __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(AttnArgs A, int G, LayerPtrs Lp) {
     if (gridDim.y > 1) {
         const int l = blockIdx.y;
@@ -965,7 +1029,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(Attn
         A.ws_o += l * Lp.ws_stride;
         if (A.ws_ml) A.ws_ml += l * Lp.ws_stride;
     }
-    attn_decode_mfma_body<D>(A, G);
+    attn_decode_mfma_body<D, BIG>(A, G);
 }
 
 // Merge part partials: one wave per (query, head); lane s < n_part reads
@@ -1039,13 +1103,21 @@ constexpr int kDecodeWgPerCu = 2;
 
 int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
 
-template <int D>
+template <int D, bool BIG>
 hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, const LayerPtrs &Lp, hipStream_t st) {
-    const size_t lds = (size_t)kWgWaves * D * kSlotBytes;
-    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D>, (int)lds);
+    const size_t lds = (size_t)kWgWaves * (D * kSlotBytes + (BIG ? kBigTabBytes : 0));
+    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D, BIG>, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D>), grid, dim3(kWgWaves * kWave), lds, st, A, G, Lp);
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, BIG>), grid, dim3(kWgWaves * kWave), lds, st, A, G, Lp);
     return hipGetLastError();
+}
+
+// Largest share of one wave, in slots: ceil(ceil(K / n_part) / kWgWaves).
+// Past 2 * kWave the registers tab0 / tab1 cannot hold the share and the
+// kernel keeps the slot table in LDS.
+bool big_table(const AttnArgs &A) {
+    const int per = (A.K + A.n_part - 1) / A.n_part;
+    return (per + kWgWaves - 1) / kWgWaves > 2 * kWave;
 }
 
 template <bool BF16>
@@ -1060,8 +1132,14 @@ hipError_t launch_attn_t(const AttnArgs &A, int G, bool mfma, hipStream_t st, co
             // one workgroup per (query, KV head, part) [x layer]
             grid = dim3((unsigned)(A.total_q * A.hkv * A.n_part), (unsigned)n_layers);
             const int D = ring_depth((int64_t)grid.x * n_layers);
-            trace("attn decode lds ring D=%d workgroups=%u layers=%d", D, grid.x, n_layers);
-            e = D == 4 ? launch_decode_mfma<4>(A, G, grid, Lp, st) : launch_decode_mfma<2>(A, G, grid, Lp, st);
+            const bool big = big_table(A);
+            trace("attn decode lds ring D=%d workgroups=%u layers=%d lds_table=%d", D, grid.x, n_layers, (int)big);
+            if (big)
+                e = D == 4 ? launch_decode_mfma<4, true>(A, G, grid, Lp, st)
+                           : launch_decode_mfma<2, true>(A, G, grid, Lp, st);
+            else
+                e = D == 4 ? launch_decode_mfma<4, false>(A, G, grid, Lp, st)
+                           : launch_decode_mfma<2, false>(A, G, grid, Lp, st);
         } else {
             switch (G) {
             case 1: hipLaunchKernelGGL((attn_kernel_w3<BF16, 1>), grid, block, 0, st, A); break;

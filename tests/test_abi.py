@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_versions_and_inert_bound():
-    assert Q.lib().qsa_abi_version() == 2
+    assert Q.lib().qsa_abi_version() == 3
     assert "gfx950" in Q.version()
     with open(os.path.join(ROOT, "tests", "golden", "page_constants.json")) as f:
         page = json.load(f)
@@ -313,3 +313,52 @@ def test_workspace_sizes():
     n4 = Q.lib().qsa_attn_layers_workspace_size(ctypes.byref(b), ctypes.byref(a), 4, 2048, 4)
     assert n4 == 4 * ((one + 255) // 256 * 256)
     assert Q.lib().qsa_attn_layers_workspace_size(ctypes.byref(b), ctypes.byref(a), 9, 2048, 4) == 0
+
+
+# ------------------------------------------------ forced launch failure hook
+HOOK = "QSA_TEST_FORCE_LAUNCH_ERROR"
+VALID_CALLS = [
+    ("compress", lambda: compress()),
+    ("compress paged", lambda: compress_paged()),
+    ("score", lambda: score()),
+    ("score paged", lambda: score_paged()),
+    ("topk", lambda: topk(b=_batch(total_q=4096, num_seqs=4096))),
+    ("topk local", lambda: Q.lib().qsa_topk_blocks_local(P(FAKE), 1024, None, 2048, 4, 8,
+                                                         ctypes.byref(_batch(total_q=4096, num_seqs=4096)),
+                                                         P(FAKE), None, 0, None)),
+    ("decode", lambda: decode()),
+    ("decode paged", lambda: decode_paged()),
+    ("prefill", lambda: prefill()),
+    ("decode layers", lambda: decode_layers()),
+    ("ingest", lambda: ingest()),
+    ("ingest + score", lambda: ingest_score()),
+    ("rewind", lambda: rewind()),
+    ("pool", lambda: Q.lib().qsa_pool_scores(P(FAKE), 4096, 4, 0, ctypes.byref(_batch()), P(FAKE), 1024, None)),
+]
+
+
+@pytest.mark.parametrize("name,thunk", VALID_CALLS, ids=[c[0] for c in VALID_CALLS])
+def test_forced_launch_failure_returns_hip_error(monkeypatch, name, thunk):
+    # host validation passes, then the hook fails the launch without touching
+    # a device (the pointers are fake)
+    monkeypatch.setenv(HOOK, "1")
+    assert thunk() == Q.QSA_ERR_HIP
+    assert HOOK in _err() and "launch failed" in _err()
+
+
+def test_forced_launch_failure_does_not_hide_validation(monkeypatch):
+    monkeypatch.setenv(HOOK, "1")
+    assert compress(ratio=3) == UNS and "ratio=3" in _err()
+    assert decode(nws=16) == WS
+    monkeypatch.setenv(HOOK, "0")
+    assert compress(ratio=5) == UNS
+
+
+def test_binding_raises_qsa_error_with_the_status(monkeypatch):
+    import torch
+    monkeypatch.setenv(HOOK, "1")
+    with pytest.raises(Q.QsaError) as e:
+        Q._check(score())
+    assert e.value.status == Q.QSA_ERR_HIP and HOOK in e.value.message
+    assert Q.QSA_ERR_DEVICE_ASSERT == 5
+    del torch

@@ -6,7 +6,8 @@ lost), sequences pointed at an invalid ring slot, every compressed-key
 format, both raw-key dtypes, paged and contiguous caches.  After every step,
 bit for bit: scores, compressed keys and scales, ring keys and windows,
 statuses and K/V rows.  (The two calls themselves are checked against the
-oracle in test_gpu_ingest.py and the parity tests.)"""
+oracle in test_gpu_ingest.py and the parity tests; the fused launch alone is
+also checked against the ingest oracle and the score oracle below.)"""
 import numpy as np
 import pytest
 import torch
@@ -156,3 +157,126 @@ def test_fused_equals_ingest_then_score(kind, k_dtype, d, H, r, cap, hkv, paged,
         n_lost += int((st == Q.INGEST_LOST_KEYS).sum())
     # the histories reached every path of the fused kernel
     assert n_stored > 0 and n_lost > 0 and n_bad > 0
+
+
+# ---------------------------------------------------------------------------
+# The fused launch on its own against the oracles: the ingest oracle
+# (oracle/ingest.py) for statuses, windows, ring rows, completed compressed
+# keys and K/V rows, and the canonical-score oracle for every score of every
+# row, computed from the compressed keys the row then holds.
+from oracle import ingest as OI  # noqa: E402
+import oracle as O  # noqa: E402
+
+ORACLE_CASES = [  # (kind, k dtype, d, H, ratio, capacity, hkv, paged, B)
+    ("bf16", BF, 128, 8, 4, 8, 2, True, 6),
+    ("e4m3", F32, 128, 16, 4, 12, 2, True, 6),
+    ("fp4", BF, 64, 4, 8, 16, 1, True, 5),
+    ("e4m3", BF, 64, 2, 4, 8, 1, False, 1),
+]
+
+
+def _kind_name(kind):
+    return {"bf16": "bf16", "e4m3": "e4m3", "fp4": "fp4"}[kind]
+
+
+@pytest.mark.parametrize("kind,k_dtype,d,H,r,cap,hkv,paged,B", ORACLE_CASES,
+                         ids=[f"{c[0]}-d{c[2]}-h{c[3]}-r{c[4]}-{'paged' if c[7] else 'flat'}" for c in ORACLE_CASES])
+def test_fused_against_oracles(kind, k_dtype, d, H, r, cap, hkv, paged, B):
+    max_len = 200
+    seed = 1000 + 7 * d + r + H + B
+    rng = np.random.default_rng(seed)
+    st = State(B, max_len, r, cap, d, H, k_dtype, kind, hkv, paged, seed)
+    slot_of = rng.permutation(st.num_slots)[:B].astype(np.int32)
+    orc = {int(sl): OI.SlotOracle(d, r, cap, _kind_name(kind)) for sl in slot_of}
+    lens = [0] * B
+    g = torch.Generator().manual_seed(seed)
+    seen = {"ok_block": 0, "lost": 0, "bad": 0}
+    P = st.paging.page_size if paged else None
+    tbl = st.paging.block_table.cpu().numpy() if paged else None
+
+    def blk_row(s, b):
+        if paged:
+            per = P // r
+            return int(tbl[s, b // per]) * per + b % per
+        return b                       # B == 1: sequence 0's blocks start at row 0
+
+    def tok_row(s, t):
+        return int(tbl[s, t // P]) * P + t % P if paged else t
+
+    for step in range(40):
+        for s in range(B):
+            if rng.random() < 0.35 / r and lens[s] > 2 * r:
+                lens[s] -= int(rng.integers(1, 2 * r))
+            lens[s] = min(lens[s] + 1, max_len)
+        slots = slot_of.copy()
+        bad = rng.random(B) < 0.2 / r
+        slots[bad] = -1
+        st.ring.slots.copy_(torch.from_numpy(slots))
+        batch = st.batch(lens)
+        k_new = torch.randn((B, d), generator=g).to(k_dtype)
+        q_idx = torch.randn((B, H, d), generator=g).to(torch.bfloat16)
+        w = torch.rand((B, H), generator=g)
+        kvn = None
+        if hkv:
+            kvn = (torch.randn((B, hkv, 128), generator=g).to(BF), torch.randn((B, hkv, 128), generator=g).to(BF))
+        st.status.fill_(-1)
+        Q.ingest_index_score(k_new.to(DEV), r, batch, st.ring, q_idx.to(DEV), w.to(DEV), st.kc, st.kc_scale,
+                             st.scores, kv=None if kvn is None else (kvn[0].to(DEV), kvn[1].to(DEV), st.K, st.V),
+                             status=st.status, paging=st.paging)
+        torch.cuda.synchronize()
+        status = st.status.cpu().numpy()
+        kc_host = _bits(st.kc)
+        sc_host = None if st.kc_scale is None else _bits(st.kc_scale)
+        win = st.ring.window.cpu().numpy()
+        scores = st.scores.cpu().numpy()
+        kf = k_new.float().numpy()
+        for s in range(B):
+            N = lens[s]
+            if bad[s]:
+                assert status[s] == OI.BAD_SLOT, (step, s, status[s])
+                seen["bad"] += 1
+            else:
+                o = orc[int(slots[s])]
+                want = o.ingest(N, kf[s:s + 1])
+                assert status[s] == want, (step, s, status[s], want)
+                assert win[slots[s]].tolist() == [o.lo, o.hi], (step, s, win[slots[s]], o.lo, o.hi)
+                ring_keys = _bits(st.ring.keys[int(slots[s])])
+                for p_, row in o.ring_positions().items():
+                    want_row = o.hist[p_]
+                    got_row = ring_keys[row]
+                    exp_bits = (torch.from_numpy(want_row).to(k_dtype).view(torch.int16).numpy()
+                                if k_dtype == BF else want_row.view(np.int32))
+                    assert np.array_equal(got_row, exp_bits), (step, s, p_)
+                if N % r == 0 and want == OI.OK:
+                    b = N // r - 1
+                    row_o, sc_o = o.kc[b]
+                    got = kc_host[blk_row(s, b)]
+                    exp = (row_o.astype(np.uint16).view(np.int16) if kind == "bf16" else row_o.astype(np.uint8))
+                    assert np.array_equal(got, exp), (step, s, "completed block key")
+                    if kind == "e4m3":
+                        assert sc_host[blk_row(s, b)] == np.float32(sc_o).view(np.int32), (step, s, "scale")
+                    elif kind == "fp4":
+                        assert np.array_equal(sc_host[blk_row(s, b)], sc_o.astype(np.uint8)), (step, s, "scale")
+                    seen["ok_block"] += 1
+                seen["lost"] += int(want == OI.LOST_KEYS)
+                if hkv:
+                    kr = _bits(st.K[tok_row(s, N - 1)])
+                    assert np.array_equal(kr, _bits(kvn[0][s])), (step, s, "K row")
+            # every score of the row from the compressed keys it now holds
+            nb = N // r
+            if nb == 0:
+                continue
+            rows = np.array([blk_row(s, b) for b in range(nb)])
+            if kind == "bf16":
+                kv_ = O.kc_values(kc_host[rows].view(np.uint16), "bf16")
+                dscale = None
+            elif kind == "e4m3":
+                kv_ = O.kc_values(kc_host[rows], "e4m3")
+                dscale = sc_host[rows].view(np.float32)
+            else:
+                kv_ = O.kc_values(kc_host[rows], "fp4", sc_host[rows])
+                dscale = None
+            ref = O.score_row(q_idx[s].float().numpy(), w[s].numpy(), kv_, dscale)
+            got = scores[s, :nb]
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (step, s, "scores")
+    assert seen["ok_block"] > 0 and seen["lost"] > 0 and seen["bad"] > 0, seen

@@ -4,8 +4,9 @@ in page pools addressed through a per-sequence block table).
 Paging only moves rows, so every paged call must reproduce its contiguous
 counterpart bit for bit: compressed keys (gathered back out of the pool),
 canonical scores, the selection and the attention output; the contiguous
-calls are checked against the oracle in test_gpu_parity, and one case here
-is checked against it directly.  The pools hold each sequence's pages in a
+calls are checked against the oracle in test_gpu_parity, and every paged
+case here is also checked against the oracle directly (compressed keys,
+scores and indices bit for bit, outputs within tolerance).  The pools hold each sequence's pages in a
 random physical order among extra pages filled with garbage; table entries a
 sequence does not use point at page 0.
 """
@@ -16,8 +17,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import qsa_workloads as W
-from tests.parity import full_check, gpu_available
+from tests.parity import check_compress, check_idx, check_out, check_scores, full_check, gpu_available
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -109,6 +111,17 @@ def _run_paged(name, spec, lens, nq, page_size, extra_pages=5, seed=0):
                        dp.out.view(torch.uint8) if dp.out.dtype == torch.bfloat16 else dp.out), \
         f"attention output differs (max {float((out.float() - dp.out.float()).abs().max()):.3g})"
     print(f"[paged] {name}: paged == contiguous (kc, scores, idx, out)", flush=True)
+
+    # and the paged results themselves against the oracle
+    res = {"kc": kcp[rows_t].cpu(), "kc_scale": None if kcsp is None else kcsp[rows_t].cpu(),
+           "scores": got_s, "idx": idx.cpu().numpy(), "out": out.float().cpu().numpy().astype(np.float64)}
+    ref = oracle.run_workload(wl, want_scores=True)
+    q = np.arange(wl.total_q)
+    check_compress(wl, res, ref)
+    check_scores(wl, res, ref, q)
+    check_idx(res, ref, q)
+    worst = check_out(wl, res, ref, q)
+    print(f"[paged] {name}: paged results == oracle (worst err/limit {worst:.3f})", flush=True)
     return wl
 
 

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import qsa_workloads as W
-from tests.parity import full_check, gpu_available, run_gpu
+from tests.parity import check_idx, check_out, full_check, gpu_available, run_gpu
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -126,13 +126,19 @@ def test_decode_equals_prefill_row_and_two_chunks_equal_one():
     assert np.array_equal(np.concatenate([r1["idx"], r2["idx"]]), res_all["idx"])
     assert np.array_equal(np.concatenate([r1["out"], r2["out"]]), res_all["out"])
     # the last query alone, as a decode batch: same selection bits; the
-    # decode entry point splits the blocks, so the output agrees to fp32
-    # rounding rather than bit for bit
+    # decode entry point splits the blocks (its output is not bit-identical
+    # to the prefill row), so its output is held to the oracle at the stated
+    # tolerance, like every other output
     last = W.Workload(sp, wl.lens, [1], wl.kv_offsets, np.array([0, 1]), wl.K, wl.V, wl.k_idx,
                       wl.q[39:], wl.q_idx[39:], wl.w[39:])
     r3, _ = run_gpu(last, decode=True)
     assert np.array_equal(r3["idx"][0], res_all["idx"][39])
-    assert np.allclose(r3["out"][0], res_all["out"][39], rtol=2e-2, atol=2e-3)
+    ref_last = oracle.run_workload(last)
+    check_idx(r3, ref_last, [0])
+    check_out(last, r3, ref_last, [0])
+    ref_all = oracle.run_workload(wl)
+    check_idx(res_all, ref_all, np.arange(wl.total_q))
+    check_out(wl, res_all, ref_all, np.arange(wl.total_q))
     del a
 
 
@@ -158,11 +164,12 @@ def test_full_size_long_context_e4m3():
     _print(f"[parity] full long decode: ok, worst err/limit = {worst:.3f}")
 
 
-def test_full_size_chunked_prefill_sampled():
+def test_full_size_chunked_prefill_all_queries():
+    # all 8193 queries of the chunk: compressed keys, every canonical score,
+    # every selection and every output against the oracle
     wl = W.make(W.CHUNKED_PREFILL)
-    q = _sample(wl.total_q, 24, seed=4)
-    _print(f"[parity] full chunked prefill: total_q={wl.total_q}, sampled {len(q)} queries")
-    _, _, worst = full_check(wl, query_ids=q)
+    _print(f"[parity] full chunked prefill: total_q={wl.total_q}, every query")
+    _, _, worst = full_check(wl)
     _print(f"[parity] full chunked prefill: ok, worst err/limit = {worst:.3f}")
 
 
