@@ -261,6 +261,21 @@ qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_
                                    int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                    size_t ws_bytes, void *stream);
 
+/* qsa_sparse_attn_decode for callers that cannot allocate (code under HIP
+ * graph capture that may not call hipMalloc, tight serving loops, harnesses
+ * that forbid allocation): the same computation and the same kernels, with
+ * the split partials kept in a static device array of 16 MiB that the
+ * library holds on every GPU it runs on until the process ends, instead of
+ * a caller workspace.  Results equal qsa_sparse_attn_decode's bit for bit.
+ * All calls on one GPU share that array and keep no state in it between
+ * calls; calls that overlap on one GPU (concurrent streams or threads) race
+ * and give undefined results.  Errors: as qsa_sparse_attn_decode, and
+ * QSA_ERR_WORKSPACE when qsa_attn_workspace_size() of the batch exceeds
+ * 16 MiB (e.g. more than 2048 query rows x 32 heads at K = 512); the call
+ * never allocates. */
+qsa_status qsa_sparse_attn_decode_static(const qsa_attn *a, const int32_t *idx, int32_t budget,
+                                         int32_t ratio, const qsa_batch *b, void *out, void *stream);
+
 /* Block top-k with a recent window always kept: the second "llama.cpp vs
  * Atlas" report's adoption plan (section (d), phase 3, item 6) keeps the
  * most recent tokens as a union with the top-k set, and the first one

@@ -35,7 +35,7 @@ EXPORTS = (
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
     "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
     "qsa_pool_scores", "qsa_attn_layers_workspace_size", "qsa_sparse_attn_decode_layers",
-    "qsa_ingest_index_score",
+    "qsa_ingest_index_score", "qsa_sparse_attn_decode_static",
 )
 
 MAX_LAYERS = 8   # QSA_MAX_LAYERS
@@ -134,6 +134,8 @@ def lib():
         L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
         L.qsa_ingest_index_score.restype = i32
         L.qsa_ingest_index_score.argtypes = [P, i32, i32, P, P, P, P, P, P, i64, P, P]
+        L.qsa_sparse_attn_decode_static.restype = i32
+        L.qsa_sparse_attn_decode_static.argtypes = [P, P, i32, i32, P, P, P]
         L.qsa_ring_rewind.restype = i32
         L.qsa_ring_rewind.argtypes = [P, i32, P, P, P]
         _lib = L
@@ -404,6 +406,17 @@ def sparse_attn_decode_layers(layers, idx, budget, ratio, batch, outs, ws, strea
     pg = None if paging is None else ctypes.byref(paging._c())
     _check(lib().qsa_sparse_attn_decode_layers(arr, n, _ptr(idx), budget, ratio, ctypes.byref(b), optrs,
                                                _ptr(ws), nbytes, pg, _stream(stream)))
+
+
+def sparse_attn_decode_static(q, k, v, softmax_scale, idx, budget, ratio, batch, out, stream=None):
+    """qsa_sparse_attn_decode_static: decode attention with the split partials
+    in the library's static device array (no workspace argument)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (out, "out")):
+        _dev(t, n)
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    _check(lib().qsa_sparse_attn_decode_static(ctypes.byref(a), _ptr(idx), budget, ratio, ctypes.byref(b),
+                                               _ptr(out), _stream(stream)))
 
 
 def sparse_attn_prefill(q, k, v, softmax_scale, idx, budget, ratio, batch, out, ws=None,

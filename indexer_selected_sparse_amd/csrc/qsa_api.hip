@@ -262,9 +262,9 @@ static qsa_status check_paging(const qsa_paged_kv *pg, const qsa_batch *b, int32
     return ok();
 }
 
-static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
-                              const qsa_batch *b, void *out, void *ws, size_t ws_bytes, bool decode,
-                              const qsa_paged_kv *pg, hipStream_t st) {
+// Host validation of an attention call, workspace excluded.
+static qsa_status attn_validate(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                                const qsa_batch *b, void *out, bool decode, const qsa_paged_kv *pg) {
     qsa_status s = check_attn(a);
     if (s == QSA_OK) s = check_batch(b, false);
     if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
@@ -276,16 +276,32 @@ static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t bud
         return fail(QSA_ERR_INVALID_ARGUMENT,
                     "decode takes one query per sequence (q_offsets NULL or max_q_per_seq == 1); "
                     "use qsa_sparse_attn_prefill for max_q_per_seq=%d", b->max_q_per_seq);
-    const size_t need = decode ? attn_workspace_bytes(*b, *a, budget, ratio) : 0;
-    if (need > 0 && (ws == nullptr || ws_bytes < need))
-        return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
-                    "(qsa_attn_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return ok();
+}
+
+// Launch a validated attention call (ws: at least attn_workspace_bytes for decode).
+static qsa_status attn_launch(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                              const qsa_batch *b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
+                              void *st) {
     DebugCheck dc = batch_check(*b, ratio, false, pg);
     dc.idx = idx;
     dc.ldi = budget / ratio;
     return launch_checked(decode ? "qsa_sparse_attn_decode" : "qsa_sparse_attn_prefill", dc, st,
                           [&](hipStream_t s_) { return launch_attn(*a, idx, budget, ratio, *b, out, ws, decode, pg, s_); });
 }
+
+static qsa_status attn_common(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                              const qsa_batch *b, void *out, void *ws, size_t ws_bytes, bool decode,
+                              const qsa_paged_kv *pg, hipStream_t st) {
+    qsa_status s = attn_validate(a, idx, budget, ratio, b, out, decode, pg);
+    if (s != QSA_OK) return s;
+    const size_t need = decode ? attn_workspace_bytes(*b, *a, budget, ratio) : 0;
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(QSA_ERR_WORKSPACE, "attention workspace of %zu bytes is smaller than the %zu required "
+                    "(qsa_attn_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return attn_launch(a, idx, budget, ratio, b, out, ws, decode, pg, st);
+}
+
 
 }  // namespace qsa
 
@@ -444,6 +460,27 @@ size_t qsa_attn_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t bu
 qsa_status qsa_sparse_attn_decode(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
                                   const qsa_batch *b, void *out, void *ws, size_t ws_bytes, void *stream) {
     return attn_common(a, idx, budget, ratio, b, out, ws, ws_bytes, true, nullptr, (hipStream_t)stream);
+}
+
+qsa_status qsa_sparse_attn_decode_static(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,
+                                         const qsa_batch *b, void *out, void *stream) {
+    qsa_status s = attn_validate(a, idx, budget, ratio, b, out, true, nullptr);
+    if (s != QSA_OK) return s;
+    const size_t need = attn_workspace_bytes(*b, *a, budget, ratio);
+    if (need > kAttnStaticScratchBytes)
+        return fail(QSA_ERR_WORKSPACE,
+                    "qsa_sparse_attn_decode_static: this batch needs %zu bytes of scratch (total_q x hq x parts "
+                    "x 130 floats), more than the %zu bytes of the static array; use qsa_sparse_attn_decode "
+                    "with a workspace", need, kAttnStaticScratchBytes);
+    if (forced_launch_error())
+        return fail(QSA_ERR_HIP, "qsa_sparse_attn_decode_static: launch failed (forced by "
+                    "QSA_TEST_FORCE_LAUNCH_ERROR)");
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = attn_static_scratch(&ws);
+        if (e != hipSuccess) return hip_status(e, "qsa_sparse_attn_decode_static: scratch address");
+    }
+    return attn_launch(a, idx, budget, ratio, b, out, ws, true, nullptr, stream);
 }
 
 qsa_status qsa_sparse_attn_prefill(const qsa_attn *a, const int32_t *idx, int32_t budget, int32_t ratio,

@@ -36,6 +36,7 @@
 //    probabilities would cost up to 2^-8 relative per weight, visible when a
 //    few tokens carry the softmax.)
 #include <atomic>
+#include <mutex>
 
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
@@ -1253,6 +1254,35 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
     const LayerPtrs none{};
     return a.dtype == QSA_BF16 ? launch_attn_t<true>(A, G, mfma_path, st, none)
                                 : launch_attn_t<false>(A, G, false, st, none);
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention without a caller workspace, for callers that cannot
+// allocate: the split partials live in `scratch`, a file-scope device array
+// that every GPU the library runs on holds until the process ends.  Host
+// code never passes the array's name to a kernel (in host code it is only a
+// stand-in for the symbol); the device address is resolved once per device
+// with hipGetSymbolAddress and kept.  All calls on one GPU share the array,
+// so calls that overlap on one GPU race.
+static __device__ __align__(256) uint8_t scratch[kAttnStaticScratchBytes];
+
+hipError_t attn_static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void *addr[kMaxScratchDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 size_t attn_layer_stride_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {

@@ -50,6 +50,13 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
                        const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
                        hipStream_t st);
 
+// Decode attention with the split partials in a static device array (no
+// caller workspace): its size, and its address on the current device
+// (resolved with hipGetSymbolAddress on the first call per device).
+constexpr size_t kAttnStaticScratchBytes = size_t(16) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t attn_static_scratch(void **ptr);
+
 // Decode attention of several layers sharing one selection (one launch on
 // the matrix-core path); workspace: n_layers slices of attn_layer_stride_bytes.
 size_t attn_layer_stride_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio);

@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)
@@ -362,3 +362,17 @@ def test_binding_raises_qsa_error_with_the_status(monkeypatch):
     assert e.value.status == Q.QSA_ERR_HIP and HOOK in e.value.message
     assert Q.QSA_ERR_DEVICE_ASSERT == 5
     del torch
+
+
+def test_static_decode_rejects_batches_past_its_array(monkeypatch):
+    a = _attn()
+    b = _batch(total_q=4096, num_seqs=4096)
+    st = Q.lib().qsa_sparse_attn_decode_static(ctypes.byref(a), P(FAKE), 2048, 4, ctypes.byref(b), P(FAKE), None)
+    assert st == Q.QSA_ERR_WORKSPACE and "static array" in _err()
+    assert Q.lib().qsa_sparse_attn_decode_static(ctypes.byref(_attn(hq=30)), P(FAKE), 2048, 4,
+                                                 ctypes.byref(_batch()), P(FAKE), None) == INV
+    assert Q.lib().qsa_sparse_attn_decode_static(ctypes.byref(a), P(FAKE), 2048, 4, ctypes.byref(_batch()), None,
+                                                 None) == INV
+    monkeypatch.setenv(HOOK, "1")
+    assert Q.lib().qsa_sparse_attn_decode_static(ctypes.byref(a), P(FAKE), 2048, 4, ctypes.byref(_batch()),
+                                                 P(FAKE), None) == Q.QSA_ERR_HIP
