@@ -91,6 +91,11 @@ def parse():
     p.add_argument("--full-every", type=int, default=1,
                    help="with --layers: layer l has its own indexer when l %% F == 0; the others reuse "
                         "the previous full layer's selection")
+    p.add_argument("--unfused-select", action="store_true",
+                   help="decode: scores and top-k as two calls (qsa_index_score, qsa_topk_blocks) instead of "
+                        "qsa_index_score_topk")
+    p.add_argument("--no-long", action="store_true",
+                   help="batched_decode: skip the long_decode sub-record (the 128K end of the metric)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="only run a plain device-to-device copy of this many MiB (5 times) "
                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters, then exit")
@@ -220,9 +225,21 @@ def cpu_baseline(wl, seconds, prefill):
     dt = time.perf_counter() - t0
     what = "decode queries" if not prefill else "prefill queries (seeded subset)"
     return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"{reps} x {len(jobs)} {what} of the workload (score + full sort + fp64 "
                       f"attention per query; compression excluded), {dt:.1f} s on {threads} "
                       f"threads of {os.cpu_count()} host cpus"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -241,11 +258,32 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n, "copies": 5}))
         return
+    rec = measure(args, args.workload, cpu=not args.no_cpu_baseline)
+    if args.workload == "batched_decode" and not args.no_long and not any(
+            (args.paged, args.ingest, args.kc_dtype, args.budget, args.local_blocks, args.token_pool,
+             args.layers > 1)):
+        # the 128K end of the metric in the same run: its own step time,
+        # queries/s and roofline fractions (no CPU baseline)
+        lr = measure(args, "long_decode", cpu=False)
+        rec["long_decode"] = {k: lr[k] for k in ("config", "value", "unit", "ms_per_step", "step_ms_percentiles",
+                                                 "kernel_ms", "roofline", "step_hbm_gbps", "step_hbm_frac",
+                                                 "step_bytes", "index_score_gbps") if k in lr}
+    print(json.dumps(rec), flush=True)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measure(args, workload, cpu):
+    """Time the hot path of one workload; returns its JSON record."""
+    import torch
+    log(f"{workload}: generating inputs")
     import qsa_workloads as W
     from indexer_selected_sparse_amd import QSA_SCORE_MFMA, pipeline
 
-    spec = W.CONFIGS[args.workload]
-    prefill = args.workload == "chunked_prefill"
+    spec = W.CONFIGS[workload]
+    prefill = workload == "chunked_prefill"
     if args.budget and args.budget != spec.budget:
         spec = dataclasses.replace(spec, budget=args.budget)
     if args.kc_dtype and args.kc_dtype != spec.kc_dtype:
@@ -369,17 +407,25 @@ def main():
         if p.ing is not None and not fuse_ing:
             p.ingest()
 
+    # scores and their selection as one qsa_index_score_topk call (the
+    # scorer writes per-chunk candidate lists, a small finish selects)
+    fuse_sel = (not prefill and not fuse_ing and not args.unfused_select and base.select_fusable())
+
     def score(p):
         if fuse_ing:
             p.ingest_score()
         elif prefill:
             p.score(QSA_SCORE_MFMA)
+        elif fuse_sel:
+            p.score_topk()
         else:
             p.score()
 
     def topk(p):
-        p.topk(certified=prefill)
+        if not fuse_sel:
+            p.topk(certified=prefill)
 
+    log(f"{workload}: {R} input copies resident; timing {args.steps} steps")
     for s in range(args.warmup):
         p = reps[s % R]
         ingest(p)
@@ -454,7 +500,23 @@ def main():
             graphs[s_ % R].replay()
         torch.cuda.synchronize()
         graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        # the distribution over steps comes from a second pass with an event
+        # before every replay (an event record between replays costs a few
+        # microseconds itself, so this pass is not the one `value` is from)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        for s_ in range(args.steps):
+            marks[s_].record()
+            graphs[s_ % R].replay()
+        marks[args.steps].record()
+        torch.cuda.synchronize()
+        per_step = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)])
+    else:
+        per_step = np.array([e[4].elapsed_time(e[3]) for e in evs])
     ms_step = graph_ms_step if graphs else eager_ms_step
+    pct = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+           "p90": float(np.percentile(per_step, 90)), "mean": float(per_step.mean()),
+           "source": ("HIP events between consecutive graph replays (a second pass of the same steps; the "
+                      "events add their own cost to each step)") if graphs else "HIP events per eager step"}
 
     qps = wl.total_q * n_layers / (ms_step / 1e3)
     rec = {
@@ -467,15 +529,17 @@ def main():
                                else str(wl.lens[0])),
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
-                   "input_replicas": R, **({"paged_page_size": args.paged} if args.paged else {}),
+                   "input_replicas": R, "score_and_select": "one call" if fuse_sel else "two calls",
+                   **({"paged_page_size": args.paged} if args.paged else {}),
                    **({"layers": n_layers, "full_every": args.full_every, "fused_layers": not args.unfused_layers,
                        "layers_with_own_indexer": sum(stacks[0].full)} if stacks is not None else {}),
                    **({"local_blocks": args.local_blocks} if args.local_blocks else {}),
                    **({"token_pool": args.token_pool} if args.token_pool else {}),
                    **({"ingest": "one token per sequence", "ingest_fused_with_scores": fuse_ing,
                        "ring_capacity": int(base.ing.ring.keys.shape[1])} if args.ingest else {})},
-        "kernel_ms": {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn,
-                      **({"ingest": t_ingest} if args.ingest else {})},
+        "step_ms_percentiles": pct,
+        "kernel_ms": {**({"index_score_topk": t_score} if fuse_sel else {"index_score": t_score, "topk": t_topk}),
+                      "sparse_attn": t_attn, **({"ingest": t_ingest} if args.ingest else {})},
         "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
     }
@@ -502,6 +566,7 @@ def main():
                            "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",
                            "bytes_per_launch": attn_bytes, "avg_ms": t_attn}
         rec["step_hbm_gbps"] = step_bytes / (ms_step * 1e-3) / 1e9
+        rec["step_hbm_frac"] = rec["step_hbm_gbps"] / HBM_PEAK_GBPS
         rec["step_bytes"] = step_bytes
         rec["index_score_gbps"] = score_bytes / (t_score * 1e-3) / 1e9
     if args.ingest:
@@ -510,9 +575,10 @@ def main():
         if not ok:
             print(json.dumps({"error": "ingest reported a non-zero status"}))
             sys.exit(1)
-    if not args.no_cpu_baseline:
+    if cpu:
+        log(f"{workload}: oracle baseline on the host cores")
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, prefill)
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 if __name__ == "__main__":

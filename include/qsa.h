@@ -358,6 +358,29 @@ qsa_status qsa_sparse_attn_prefill_paged(const qsa_attn *a, const int32_t *idx, 
                                          int32_t ratio, const qsa_batch *b, void *out, void *ws,
                                          size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
 
+/* Canonical scores and their block top-k in one call: the same scores and
+ * the same idx, bit for bit, as qsa_index_score(ix, ratio, b, scores,
+ * ld_scores, QSA_SCORE_CANONICAL, [pg]) followed by qsa_topk_blocks(scores,
+ * ld_scores, NULL, budget, ratio, b, idx, ...).  For batches of at most 256
+ * query rows (decode) the scorer also writes, per chunk of 64 consecutive
+ * blocks, the chunk's best few blocks (enough for the chunk's expected share
+ * of the top K many times over) into the workspace, and the selection is
+ * made from those lists when a certificate shows it equals the selection
+ * from the whole row: T, the K-th largest listed score, exceeds every
+ * chunk's last listed score, so every block scoring at least T is listed.
+ * A row that fails the certificate is selected from its whole score row.
+ * (The "PR 16 review" report on the "Agentic shootout" page, section (b),
+ * names the host-side top-k as the v1 cliff; this keeps the selection on the
+ * device and small.)
+ *  pg:  NULL (contiguous kc) or the paging of kc / kc_scale.
+ *  ws:  device workspace of at least qsa_score_topk_workspace_size() bytes;
+ *       no initialisation, no state between calls.
+ * Errors: those of qsa_index_score and qsa_topk_blocks. */
+size_t qsa_score_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio);
+qsa_status qsa_index_score_topk(const qsa_indexer *ix, int32_t budget, int32_t ratio, const qsa_batch *b,
+                                float *scores, int64_t ld_scores, int32_t *idx, void *ws, size_t ws_bytes,
+                                const qsa_paged_kv *pg, void *stream);
+
 /* ---- Layers that share one selection.  The first "llama.cpp vs Atlas"
  * report (section (a)3) lists indexers that are either full or shared: a
  * shared layer attends its own K/V with the top-k of the last full layer.

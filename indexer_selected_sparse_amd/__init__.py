@@ -35,7 +35,8 @@ EXPORTS = (
     "qsa_compress_keys_paged", "qsa_index_score_paged", "qsa_sparse_attn_decode_paged",
     "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
     "qsa_pool_scores", "qsa_attn_layers_workspace_size", "qsa_sparse_attn_decode_layers",
-    "qsa_ingest_index_score", "qsa_sparse_attn_decode_static",
+    "qsa_ingest_index_score", "qsa_sparse_attn_decode_static", "qsa_score_topk_workspace_size",
+    "qsa_index_score_topk",
 )
 
 MAX_LAYERS = 8   # QSA_MAX_LAYERS
@@ -134,6 +135,10 @@ def lib():
         L.qsa_ingest.argtypes = [P, i32, i32, i32, P, P, P, i32, P, P, P, P, P]
         L.qsa_ingest_index_score.restype = i32
         L.qsa_ingest_index_score.argtypes = [P, i32, i32, P, P, P, P, P, P, i64, P, P]
+        L.qsa_score_topk_workspace_size.restype = sz
+        L.qsa_score_topk_workspace_size.argtypes = [P, i32, i32]
+        L.qsa_index_score_topk.restype = i32
+        L.qsa_index_score_topk.argtypes = [P, i32, i32, P, P, i64, P, P, sz, P, P]
         L.qsa_sparse_attn_decode_static.restype = i32
         L.qsa_sparse_attn_decode_static.argtypes = [P, P, i32, i32, P, P, P]
         L.qsa_ring_rewind.restype = i32
@@ -315,6 +320,25 @@ def index_score(q_idx, w, kc, kc_scale, ratio: int, batch: Batch, scores: torch.
         pg = paging._c()
         _check(lib().qsa_index_score_paged(ctypes.byref(ix), ratio, ctypes.byref(b), _ptr(scores),
                                            scores.shape[1], mode, ctypes.byref(pg), _stream(stream)))
+
+
+def score_topk_workspace_size(batch: Batch, budget: int, ratio: int) -> int:
+    b = batch._c()
+    return int(lib().qsa_score_topk_workspace_size(ctypes.byref(b), budget, ratio))
+
+
+def index_score_topk(q_idx, w, kc, kc_scale, budget: int, ratio: int, batch: Batch, scores: torch.Tensor,
+                     idx: torch.Tensor, ws: Optional[torch.Tensor], stream=None,
+                     paging: Optional[Paging] = None) -> None:
+    """qsa_index_score_topk: canonical scores and their block top-k in one call."""
+    _dev(scores, "scores")
+    _dev(idx, "idx")
+    ix = _indexer(q_idx, w, kc, kc_scale)
+    b = batch._c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pg = None if paging is None else ctypes.byref(paging._c())
+    _check(lib().qsa_index_score_topk(ctypes.byref(ix), budget, ratio, ctypes.byref(b), _ptr(scores),
+                                      scores.shape[1], _ptr(idx), _ptr(ws), nbytes, pg, _stream(stream)))
 
 
 def topk_workspace_size(batch: Batch, budget: int, ratio: int, recheck=None) -> int:

@@ -13,6 +13,7 @@
 
 #include "qsa_debug.hpp"
 #include "qsa_internal.hpp"
+#include "qsa_lists.hpp"
 
 namespace qsa {
 
@@ -381,7 +382,7 @@ static qsa_status score_common(const qsa_indexer *ix, int32_t ratio, const qsa_b
                     (long long)ld_scores, (long long)need_ld);
     return launch_checked("qsa_index_score", batch_check(*b, ratio, pg == nullptr, pg), stream, [&](hipStream_t st) {
         return mfma ? launch_score_mfma(*ix, ratio, *b, scores, ld_scores, st)
-                    : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, pg, st);
+                    : launch_score_canonical(*ix, ratio, *b, scores, ld_scores, pg, st, ListArgs{});
     });
 }
 
@@ -394,6 +395,36 @@ qsa_status qsa_index_score_paged(const qsa_indexer *ix, int32_t ratio, const qsa
                                  int64_t ld_scores, uint32_t flags, const qsa_paged_kv *pg, void *stream) {
     if (!pg) return fail(QSA_ERR_INVALID_ARGUMENT, "paging descriptor is NULL");
     return score_common(ix, ratio, b, scores, ld_scores, flags, pg, stream);
+}
+
+size_t qsa_score_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio) {
+    if (!b || check_budget(budget, ratio) != QSA_OK) return 0;
+    return score_topk_workspace_bytes(*b, budget, ratio);
+}
+
+qsa_status qsa_index_score_topk(const qsa_indexer *ix, int32_t budget, int32_t ratio, const qsa_batch *b,
+                                float *scores, int64_t ld_scores, int32_t *idx, void *ws, size_t ws_bytes,
+                                const qsa_paged_kv *pg, void *stream) {
+    qsa_status s = check_indexer(ix, false);
+    if (s == QSA_OK) s = check_batch(b, pg == nullptr);
+    if (s == QSA_OK && pg) s = check_paging(pg, b, ratio);
+    if (s == QSA_OK) s = check_budget(budget, ratio);
+    if (s == QSA_OK) s = check_rows(b, ratio);
+    if (s != QSA_OK) return s;
+    if (!scores) return fail(QSA_ERR_INVALID_ARGUMENT, "scores is NULL");
+    if (!idx) return fail(QSA_ERR_INVALID_ARGUMENT, "idx is NULL");
+    const int64_t need_ld = (b->max_kv_len + ratio - 1) / ratio;
+    if (ld_scores < need_ld || ld_scores < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
+                    (long long)ld_scores, (long long)need_ld);
+    const size_t need = score_topk_workspace_bytes(*b, budget, ratio);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(QSA_ERR_WORKSPACE, "score + top-k workspace of %zu bytes is smaller than the %zu required "
+                    "(qsa_score_topk_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return launch_checked("qsa_index_score_topk", batch_check(*b, ratio, pg == nullptr, pg), stream,
+                          [&](hipStream_t st) {
+                              return launch_score_topk(*ix, budget, ratio, *b, scores, ld_scores, idx, ws, pg, st);
+                          });
 }
 
 size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio,

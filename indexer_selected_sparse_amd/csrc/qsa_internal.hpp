@@ -19,9 +19,12 @@ hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio,
                            const int64_t *first_block, void *kc, int kc_dtype, void *kc_scale,
                            const qsa_paged_kv *pg, hipStream_t st);
 
-// Canonical (bit-defined) indexer scores, decode and prefill.
+// Canonical (bit-defined) indexer scores, decode and prefill; with la.keys
+// set, also the per-chunk candidate lists of qsa_lists.hpp.
+struct ListArgs;
 hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
-                                  float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st);
+                                  float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st,
+                                  const ListArgs &la);
 
 // Block pooling of token scores (QSA_POOL_MAX / QSA_POOL_MEAN).
 hipError_t launch_pool_scores(const float *tok, int64_t ld_tok, int ratio, int mode, const qsa_batch &b,
@@ -37,6 +40,13 @@ constexpr int64_t kTopkRecheckMaxBlocks = 32768;
 size_t topk_workspace_bytes(const qsa_batch &b, int budget, int ratio, const qsa_indexer *recheck);
 hipError_t launch_topk(const float *scores, int64_t ld, const qsa_indexer *recheck, int budget,
                        int ratio, const qsa_batch &b, int32_t *idx, int ldi, void *ws, hipStream_t st);
+// Canonical scores and their block top-k in one call (qsa_index_score_topk):
+// few-row batches take the scorer's candidate lists (qsa_lists.hpp) and the
+// list finish; larger batches the two plain launches.
+bool score_topk_uses_lists(const qsa_batch &b);
+size_t score_topk_workspace_bytes(const qsa_batch &b, int budget, int ratio);
+hipError_t launch_score_topk(const qsa_indexer &ix, int budget, int ratio, const qsa_batch &b, float *scores,
+                             int64_t ld, int32_t *idx, void *ws, const qsa_paged_kv *pg, hipStream_t st);
 // In place: row i of idx (stride ldi) becomes the ascending union of its
 // top-K selection and the last local_blocks complete blocks.
 hipError_t launch_topk_local(int budget, int ratio, int local_blocks, const qsa_batch &b, int32_t *idx,

@@ -1,0 +1,109 @@
+// Per-chunk candidate lists that the canonical scorer writes for the block
+// top-k of few-row (decode) batches.
+//
+// Every wave of the scorer holds the scores of one chunk of 64 consecutive
+// blocks of a query row.  Besides the scores it writes the chunk's best
+// list_len(nb, K) blocks by (score desc, index asc) — their order keys and
+// lanes, in ascending block order, padded with key 0 (below every real key)
+// — and, when the chunk held more blocks than that, the key of its last
+// listed block (the cutoff; 0 when the list holds the whole chunk).  The
+// lists of a row, chunk after chunk, are therefore in ascending block order.
+//
+// The finish kernel selects from the lists alone when that is provably the
+// same as selecting from the whole row: with T the K-th largest listed key,
+// if T > 0 and every cutoff is strictly below T, then every block with key
+// >= T is listed (an unlisted block has key <= its chunk's cutoff < T), so T
+// and the lowest-index blocks among the keys equal to T are exactly those
+// of the whole row.  Otherwise it selects from the whole row.
+//
+// list_len: m = ceil(64 K / nb) is the expected number of selected blocks in
+// a chunk (scores without locality); the list keeps m + 4 ceil(sqrt(m)) + 3,
+// at most 64, so for independent scores a chunk overflows its list with a
+// probability of order 1e-6 (Poisson tail), and the row falls back.
+#pragma once
+
+#include <stdint.h>
+
+#include "qsa_device.hpp"
+
+namespace qsa {
+
+constexpr int kListChunk = 64;                 // blocks per chunk (one scorer wave)
+static_assert(kListChunk == 64, "a chunk is one wave");
+constexpr int64_t kListMaxEntries = 16384;     // listed entries a row may have (finish holds them in LDS)
+
+// (32-bit arithmetic: nb <= 131072 and K <= 2048.)
+__host__ __device__ inline int list_len(int64_t nb, int K) {
+    const uint32_t n = (uint32_t)nb;
+    const uint32_t m = (kListChunk * (uint32_t)K + n - 1u) / n;
+    uint32_t s = 0;
+    while (s * s < m) ++s;
+    const uint32_t k = m + 4u * s + 3u;
+    return k > (uint32_t)kListChunk ? kListChunk : (int)k;
+}
+
+// Lists of one call: row i's entries start at i * stride, its cutoffs at
+// i * cstride (one per chunk).  keys == nullptr: no lists.
+struct ListArgs {
+    uint32_t *keys;
+    uint8_t *loc;
+    uint32_t *cut;
+    int64_t stride;
+    int64_t cstride;
+    int K;
+};
+
+// Order-preserving map of a finite float to uint32 (larger float, larger
+// key); never 0 for a finite input, which leaves 0 free for padding.
+__device__ __forceinline__ uint32_t list_order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t list_lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The wave's list for the chunk whose first block is `chunk0` (a multiple
+// of 64) of query row `row` with nb visible blocks: lane l holds block
+// chunk0 + l, its score s and whether it is visible (`active`).
+__device__ __forceinline__ void emit_chunk_list(const ListArgs &la, int64_t row, int64_t nb, int64_t chunk0,
+                                                bool active, float s, int lane) {
+    if (chunk0 >= nb) return;                                  // uniform over the wave
+    const int kk = list_len(nb, la.K);
+    const uint32_t key = active ? list_order_key(s) : 0u;
+    const uint64_t act = __ballot(active);
+    uint64_t sel = act;
+    uint32_t cut = 0;
+    if (__builtin_popcountll(act) > kk) {
+        // t = the kk-th largest key: the largest t with #(key >= t) >= kk,
+        // two bits per step (three independent counts), MSB first
+        uint32_t t = 0;
+        for (int bit = 30; bit >= 0; bit -= 2) {
+            const uint32_t c3 = t | (3u << bit), c2 = t | (2u << bit), c1 = t | (1u << bit);
+            const int n3 = __builtin_popcountll(__ballot(key >= c3));
+            const int n2 = __builtin_popcountll(__ballot(key >= c2));
+            const int n1 = __builtin_popcountll(__ballot(key >= c1));
+            t = n3 >= kk ? c3 : (n2 >= kk ? c2 : (n1 >= kk ? c1 : t));
+        }
+        const uint64_t gt = __ballot(key > t);
+        const uint64_t eq = __ballot(key == t);
+        const uint32_t need = (uint32_t)kk - (uint32_t)__builtin_popcountll(gt);
+        sel = gt | __ballot(key == t && list_lanes_below(eq) < need);
+        cut = t;
+    }
+    const int64_t base = row * la.stride + (chunk0 >> 6) * kk;
+    const int nsel = __builtin_popcountll(sel);
+    if ((sel >> lane) & 1u) {                                 // slots 0 .. nsel-1
+        const uint32_t pos = list_lanes_below(sel);
+        la.keys[base + pos] = key;
+        la.loc[base + pos] = (uint8_t)lane;
+    }
+    if (lane >= nsel && lane < kk) {                          // padding: slots nsel .. kk-1
+        la.keys[base + lane] = 0u;
+        la.loc[base + lane] = 0;
+    }
+    if (lane == 0) la.cut[row * la.cstride + (chunk0 >> 6)] = cut;
+}
+
+}  // namespace qsa

@@ -28,6 +28,7 @@
 #include "qsa_device.hpp"
 #include "qsa_ingest.hpp"
 #include "qsa_internal.hpp"
+#include "qsa_lists.hpp"
 
 namespace qsa {
 namespace {
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
     const QT *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const float *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
+    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, ListArgs la) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     const int64_t i = blockIdx.x;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
         s = s + t;
     }
     if (active) scores[i * ld + b] = s;
+    if (la.keys) emit_chunk_list(la, i, nb, b - (threadIdx.x & (kWave - 1)), active, s, threadIdx.x & (kWave - 1));
 }
 
 // Exact products (bf16 query; bf16 or e4m3 keys).  One lane owns one block;
@@ -316,7 +318,8 @@ __device__ __forceinline__ void score_exact_body(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld, const PageMap &pm, int64_t i, int64_t by) {
+    int log2r, float *__restrict__ scores, int64_t ld, const PageMap &pm, int64_t i, int64_t by,
+    const ListArgs &la) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     constexpr bool kFP4 = std::is_same<KT, Fp4x2>::value;
     constexpr int CH = kExactChunk;
@@ -395,6 +398,7 @@ __device__ __forceinline__ void score_exact_body(
         s = s + t;
     }
     if (active) scores[i * ld + b] = s;
+    if (la.keys) emit_chunk_list(la, i, nb, b - (threadIdx.x & (kWave - 1)), active, s, threadIdx.x & (kWave - 1));
 }
 
 template <typename KT, int D, int H>
@@ -402,9 +406,9 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm) {
+    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, ListArgs la) {
     score_exact_body<KT, D, H, false>(q_idx, w, kc, kc_scale, kv_off, blk_off, q_off, num_seqs, log2r, scores,
-                                      ld, pm, blockIdx.x, blockIdx.y);
+                                      ld, pm, blockIdx.x, blockIdx.y, la);
 }
 
 // Canonical score of one block whose key a wave holds (lane l: dims
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(kExactThreads) void ingest_score_kernel(
     float inv_ratio, RingArgs ring, KvArgs kv, int32_t *__restrict__ status) {
     if ((int)blockIdx.x < num_seqs) {
         score_exact_body<KT, D, H, true>(q_idx, w, kc, kc_scale, kv_off, blk_off, nullptr, num_seqs, log2r,
-                                         scores, ld, pm, blockIdx.x, blockIdx.y);
+                                         scores, ld, pm, blockIdx.x, blockIdx.y, ListArgs{});
         return;
     }
     if (blockIdx.y != 0) return;
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(kExactThreads) void ingest_score_kernel(
 
 template <typename QT, typename KT, int D>
 hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, float *scores,
-                      int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st) {
+                      int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st, const ListArgs &la) {
     const QT *q = static_cast<const QT *>(ix.q_idx);
     const KT *kc = static_cast<const KT *>(ix.kc);
     constexpr bool kExact = std::is_same<QT, uint16_t>::value && !std::is_same<KT, float>::value;
@@ -490,7 +494,7 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 #define QSA_SCORE_LAUNCH(HH)                                                                       \
     hipLaunchKernelGGL((score_exact_kernel<KT, D, HH>), grid, block, 0, st, q, ix.w, kc,           \
                        ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
-                       scores, ld, pm)
+                       scores, ld, pm, la)
         switch (ix.h_idx) {
         case 1: QSA_SCORE_LAUNCH(1); break;
         case 2: QSA_SCORE_LAUNCH(2); break;
@@ -505,7 +509,7 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 #define QSA_SCORE_LAUNCH(HH)                                                                       \
     hipLaunchKernelGGL((score_rounded_kernel<QT, KT, D, HH>), grid, block, 0, st, q, ix.w, kc,     \
                        static_cast<const float *>(ix.kc_scale), b.kv_offsets, b.blk_offsets,      \
-                       b.q_offsets, b.num_seqs, log2r, scores, ld, pm)
+                       b.q_offsets, b.num_seqs, log2r, scores, ld, pm, la)
         switch (ix.h_idx) {
         case 1: QSA_SCORE_LAUNCH(1); break;
         case 2: QSA_SCORE_LAUNCH(2); break;
@@ -520,9 +524,9 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
 
 template <typename QT, typename KT>
 hipError_t dispatch_d(const qsa_indexer &ix, int log2r, const qsa_batch &b, float *scores,
-                      int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st) {
-    return ix.d_idx == 64 ? dispatch_h<QT, KT, 64>(ix, log2r, b, scores, ld, pm, grid, st)
-                          : dispatch_h<QT, KT, 128>(ix, log2r, b, scores, ld, pm, grid, st);
+                      int64_t ld, const PageMap &pm, dim3 grid, hipStream_t st, const ListArgs &la) {
+    return ix.d_idx == 64 ? dispatch_h<QT, KT, 64>(ix, log2r, b, scores, ld, pm, grid, st, la)
+                          : dispatch_h<QT, KT, 128>(ix, log2r, b, scores, ld, pm, grid, st, la);
 }
 
 struct FusedArgs {
@@ -604,7 +608,8 @@ hipError_t launch_pool_scores(const float *tok, int64_t ld_tok, int ratio, int m
 }
 
 hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_batch &b,
-                                  float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st) {
+                                  float *scores, int64_t ld, const qsa_paged_kv *pg, hipStream_t st,
+                                  const ListArgs &la) {
     const PageMap pm = page_map(pg);
     const int log2r = __builtin_ctz((unsigned)ratio);
     const int64_t max_nb = b.max_kv_len >> log2r;
@@ -615,16 +620,16 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
     const bool qb = ix.q_dtype == QSA_BF16;
     switch (ix.kc_dtype) {
     case QSA_F32:
-        return qb ? dispatch_d<uint16_t, float>(ix, log2r, b, scores, ld, pm, grid, st)
-                  : dispatch_d<float, float>(ix, log2r, b, scores, ld, pm, grid, st);
+        return qb ? dispatch_d<uint16_t, float>(ix, log2r, b, scores, ld, pm, grid, st, la)
+                  : dispatch_d<float, float>(ix, log2r, b, scores, ld, pm, grid, st, la);
     case QSA_BF16:
-        return qb ? dispatch_d<uint16_t, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st)
-                  : dispatch_d<float, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st);
+        return qb ? dispatch_d<uint16_t, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st, la)
+                  : dispatch_d<float, uint16_t>(ix, log2r, b, scores, ld, pm, grid, st, la);
     case QSA_FP8_E4M3:
-        return qb ? dispatch_d<uint16_t, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st)
-                  : dispatch_d<float, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st);
+        return qb ? dispatch_d<uint16_t, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st, la)
+                  : dispatch_d<float, uint8_t>(ix, log2r, b, scores, ld, pm, grid, st, la);
     default:   // fp4 keys take a bf16 query (checked by the caller)
-        return dispatch_d<uint16_t, Fp4x2>(ix, log2r, b, scores, ld, pm, grid, st);
+        return dispatch_d<uint16_t, Fp4x2>(ix, log2r, b, scores, ld, pm, grid, st, la);
     }
 }
 

@@ -27,6 +27,7 @@
 //     index: elements are visited round-major (index order), and per
 //     (round, wave) counts, scanned once, give each output position.
 #include "qsa_device.hpp"
+#include "qsa_lists.hpp"
 #include "qsa_internal.hpp"
 
 namespace qsa {
@@ -1258,7 +1259,279 @@ __global__ __launch_bounds__(kTopkThreads) void topk_fused_kernel(
     }
 }
 
+// ------------------------------------------------------------------------
+// Selection from the scorer's per-chunk candidate lists (qsa_lists.hpp):
+// one 1024-thread workgroup per row, few barriers.
+//  1. The row's listed keys (requested together with the row's offsets, for
+//     the first kSpecEntries entries) go to LDS with their block ids, in list
+//     order (ascending block order); one exchange gives the listed keys' min
+//     and max, how many are real (not padding) and the largest chunk cutoff.
+//  2. A histogram of 1024 bins linear in the score between min and max (one
+//     bin per thread): the bin map is monotone, so the K-th largest key T
+//     lies in the bin where the count from the top first reaches K.
+//  3. That bin's keys (typically a handful) go to a short LDS list, and one
+//     wave finds T among them exactly by bisection (MSB first, two bits per
+//     step); more than 64 keys in the bin (heavy ties, adversarial spreads)
+//     take the exact radix select over the whole list instead.
+//  4. Certificate: T > 0 and every chunk cutoff < T (then every block with
+//     key >= T is listed).  Output in ascending order: thread t owns list
+//     entries [t*E, t*E + E); one scan of (keys > T, keys == T) per thread
+//     gives its first output position, above + min(ties before, ties needed),
+//     because ties are taken in list (= block) order.
+// A row that fails the certificate, or whose lists exceed the LDS (`cap`
+// entries), is selected from its whole score row.
+constexpr int kListBins = kTopkThreads;             // one bin per thread
+constexpr int kSpecEntries = 4 * kTopkThreads;      // list entries requested before the length is known
+constexpr int kBinCandMax = kWave;                  // threshold-bin keys one wave resolves
+
+__global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
+    const float *__restrict__ scores, int64_t ld, const int64_t *__restrict__ kv_off,
+    const int64_t *__restrict__ q_off, int num_seqs, int log2r, int K, int32_t *__restrict__ idx, int ldi,
+    ListArgs la, int cap) {
+    __shared__ TopkShared S;
+    __shared__ uint32_t bcand[kBinCandMax];
+    extern __shared__ uint32_t lds_lists[];          // keys [cap], then block ids [cap]
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t i = blockIdx.x;
+    const uint32_t *__restrict__ gk = la.keys + i * la.stride;
+    const uint8_t *__restrict__ gl = la.loc + i * la.stride;
+    const uint32_t *__restrict__ gc = la.cut + i * la.cstride;
+    // Speculative requests (inside the row's regions whatever its length):
+    // the first list entries and chunk cutoffs, alongside the offsets.
+    const int spec_n = (int)(la.stride < kSpecEntries ? la.stride : kSpecEntries);
+    const int spec_c = (int)(la.cstride < kTopkThreads ? la.cstride : kTopkThreads);
+    uint32_t k[4], l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = (int)threadIdx.x + u * kTopkThreads;
+        k[u] = j < spec_n ? gk[j] : 0u;
+        l[u] = j < spec_n ? gl[j] : 0u;
+    }
+    const uint32_t c0 = (int)threadIdx.x < spec_c ? gc[threadIdx.x] : 0u;
+    const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
+    const int64_t nb = qp.L >> log2r;
+    int32_t *out = idx + i * (int64_t)ldi;
+    if (nb <= K) {
+        for (int t = threadIdx.x; t < K; t += kTopkThreads) out[t] = (t < nb) ? t : -1;
+        return;
+    }
+    const int kk = list_len(nb, K);
+    const int nch = (int)((nb + kListChunk - 1) / kListChunk);
+    const int M = nch * kk;
+    if (M <= cap) {
+        uint32_t *keys = lds_lists;
+        int32_t *blk = reinterpret_cast<int32_t *>(lds_lists + cap);
+        uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u;
+        uint32_t mcut = (int)threadIdx.x < nch ? c0 : 0u;
+        for (int c = (int)threadIdx.x + kTopkThreads; c < nch; c += kTopkThreads) mcut = max(mcut, gc[c]);
+        auto put = [&](int j, uint32_t key, uint32_t lane_of) {
+            keys[j] = key;
+            blk[j] = (int32_t)(((uint32_t)j / (uint32_t)kk) * kListChunk + lane_of);
+            if (key != 0u) {                         // padding (key 0) is not a block
+                kmin = min(kmin, key);
+                kmax = max(kmax, key);
+                ++nreal;
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = (int)threadIdx.x + u * kTopkThreads;
+            if (j < M && j < spec_n) put(j, k[u], l[u]);
+        }
+        for (int j = (int)threadIdx.x + spec_n; j < M; j += kTopkThreads) put(j, gk[j], gl[j]);
+        S.hist[threadIdx.x] = 0u;                    // the linear histogram's bin
+        // one exchange for the four reductions (its barrier also publishes keys / blk)
+        {
+            const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax), w_mc = wave_max_u32(mcut);
+            const uint32_t w_n = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nreal), kWave - 1);
+            if (lane == 0) {
+                S.wmin[wave] = w_mn;
+                S.wmax[wave] = w_mx;
+                S.wsum[wave] = w_n;
+                S.cand[wave] = w_mc;
+            }
+            __syncthreads();
+            kmin = S.wmin[0];
+            kmax = S.wmax[0];
+            nreal = S.wsum[0];
+            mcut = S.cand[0];
+#pragma unroll
+            for (int w = 1; w < kTopkWaves; ++w) {
+                kmin = min(kmin, S.wmin[w]);
+                kmax = max(kmax, S.wmax[w]);
+                nreal += S.wsum[w];
+                mcut = max(mcut, S.cand[w]);
+            }
+        }
+        uint32_t T = 0u, need_eq = 0u, total_eq = 0u;
+        bool found = false;
+        const float vmin = key_value(kmin), vmax = key_value(kmax);
+        const float scale = (float)kListBins / (vmax - vmin);
+        if (nreal < (uint32_t)K || mcut >= kmax) {
+            // fewer listed blocks than K, or a cutoff at or above every
+            // listed key: the certificate cannot hold
+        } else if (kmin == kmax) {
+            T = kmin;
+            need_eq = (uint32_t)K;
+            total_eq = nreal;
+            found = true;
+        } else if (scale < 3.0e38f) {
+            auto bin_of = [&](uint32_t key) {
+                return min(kListBins - 1, (int)((key_value(key) - vmin) * scale));
+            };
+            for (int j = threadIdx.x; j < M; j += kTopkThreads) {
+                const uint32_t key = keys[j];
+                if (key != 0u) atomicAdd(&S.hist[bin_of(key)], 1u);
+            }
+            if (threadIdx.x == 0) S.s2 = 0u;
+            __syncthreads();
+            // thread t owns bin kListBins-1-t: the count above it by one scan
+            const int bin = kListBins - 1 - (int)threadIdx.x;
+            const uint32_t h = S.hist[bin];
+            uint32_t tot;
+            const uint32_t above = wg_scan(h, S, tot);
+            if (above < (uint32_t)K && (uint32_t)K <= above + h) {
+                S.s0 = (uint32_t)bin;
+                S.s1 = above;
+                S.s3 = h;
+            }
+            __syncthreads();
+            const int tb = (int)S.s0;
+            const uint32_t need = (uint32_t)K - S.s1;
+            const uint32_t nbin = S.s3;
+            if (nbin <= (uint32_t)kBinCandMax) {
+                for (int j = threadIdx.x; j < M; j += kTopkThreads) {
+                    const uint32_t key = keys[j];
+                    if (key != 0u && bin_of(key) == tb) bcand[atomicAdd(&S.s2, 1u)] = key;
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    // the need-th largest of the bin's nbin keys, exactly
+                    const uint32_t key = lane < (int)nbin ? bcand[lane] : 0u;
+                    uint32_t t = 0;
+                    for (int bit = 30; bit >= 0; bit -= 2) {
+                        const uint32_t c3 = t | (3u << bit), c2 = t | (2u << bit), c1 = t | (1u << bit);
+                        const uint32_t n3 = (uint32_t)__builtin_popcountll(__ballot(key >= c3));
+                        const uint32_t n2 = (uint32_t)__builtin_popcountll(__ballot(key >= c2));
+                        const uint32_t n1 = (uint32_t)__builtin_popcountll(__ballot(key >= c1));
+                        t = n3 >= need ? c3 : (n2 >= need ? c2 : (n1 >= need ? c1 : t));
+                    }
+                    const uint32_t gt = (uint32_t)__builtin_popcountll(__ballot(key > t));
+                    const uint32_t eq = (uint32_t)__builtin_popcountll(__ballot(key == t));
+                    if (lane == 0) {
+                        S.s0 = t;
+                        S.s1 = need - gt;
+                        S.s3 = eq;
+                    }
+                }
+                __syncthreads();
+                T = S.s0;
+                need_eq = S.s1;
+                total_eq = S.s3;
+                found = true;
+            }
+        }
+        if (!found && nreal >= (uint32_t)K && mcut < kmax) {
+            __syncthreads();
+            T = radix_select(LdsKey{keys}, (int64_t)M, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
+        }
+        if (T != 0u && mcut < T) {
+            // ordered output: thread t owns list entries [t*E, t*E + E)
+            const int E = (M + kTopkThreads - 1) / kTopkThreads;
+            const int j0 = (int)threadIdx.x * E;
+            const int j1 = j0 + E < M ? j0 + E : M;
+            uint32_t ngt = 0, neq = 0;
+            for (int j = j0; j < j1; ++j) {
+                const uint32_t key = keys[j];
+                ngt += key > T ? 1u : 0u;
+                neq += key == T ? 1u : 0u;
+            }
+            uint32_t tot;
+            const uint32_t before = wg_scan((ngt << 16) | neq, S, tot);   // both counts < 2^16
+            uint32_t tie = before & 0xffffu;
+            uint32_t pos = (before >> 16) + min(tie, need_eq);
+            for (int j = j0; j < j1; ++j) {
+                const uint32_t key = keys[j];
+                bool take = key > T;
+                if (key == T) {
+                    take = tie < need_eq;
+                    ++tie;
+                }
+                if (take) {
+                    if (pos < (uint32_t)K) out[pos] = blk[j];
+                    ++pos;
+                }
+            }
+            return;
+        }
+        __syncthreads();
+    }
+    // the whole score row
+    const float *__restrict__ row = scores + i * ld;
+    const GlobalKey key{row};
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll 4
+    for (int64_t b = threadIdx.x; b < nb; b += kTopkThreads) {
+        const uint32_t kx = key(b);
+        kmin = min(kmin, kx);
+        kmax = max(kmax, kx);
+    }
+    wg_minmax(kmin, kmax, S);
+    select_row(key, nb, K, kmin, kmax, out, S);
+}
+
 }  // namespace
+
+// Candidate lists of a score + select call: row stride of ceil(max_nb/64)
+// chunks of 64 entries (keys u32, then chunk cutoffs u32, then lanes u8).
+static int64_t list_chunks(const qsa_batch &b, int ratio) {
+    const int64_t max_nb = b.max_kv_len / ratio;
+    return max_nb > 0 ? (max_nb + kListChunk - 1) / kListChunk : 1;
+}
+
+bool score_topk_uses_lists(const qsa_batch &b) { return b.total_q >= 1 && b.total_q <= kMultiMaxRows; }
+
+size_t score_topk_workspace_bytes(const qsa_batch &b, int budget, int ratio) {
+    if (!score_topk_uses_lists(b)) return topk_workspace_bytes(b, budget, ratio, nullptr);
+    const size_t rows = (size_t)b.total_q, nch = (size_t)list_chunks(b, ratio);
+    const size_t keys = rows * nch * kListChunk * 4, cuts = rows * nch * 4, locs = rows * nch * kListChunk;
+    return ((keys + 255) & ~(size_t)255) + ((cuts + 255) & ~(size_t)255) + locs + 256;
+}
+
+hipError_t launch_score_topk(const qsa_indexer &ix, int budget, int ratio, const qsa_batch &b, float *scores,
+                             int64_t ld, int32_t *idx, void *ws, const qsa_paged_kv *pg, hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    const int K = budget / ratio;
+    if (!score_topk_uses_lists(b)) {
+        hipError_t e = launch_score_canonical(ix, ratio, b, scores, ld, pg, st, ListArgs{});
+        if (e != hipSuccess) return e;
+        return launch_topk(scores, ld, nullptr, budget, ratio, b, idx, K, ws, st);
+    }
+    const int64_t nch = list_chunks(b, ratio);
+    const size_t rows = (size_t)b.total_q;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    const size_t keys_bytes = (rows * nch * kListChunk * 4 + 255) & ~(size_t)255;
+    const size_t cuts_bytes = (rows * nch * 4 + 255) & ~(size_t)255;
+    ListArgs la;
+    la.keys = reinterpret_cast<uint32_t *>(base);
+    la.cut = reinterpret_cast<uint32_t *>(base + keys_bytes);
+    la.loc = base + keys_bytes + cuts_bytes;
+    la.stride = nch * kListChunk;
+    la.cstride = nch;
+    la.K = K;
+    hipError_t e = launch_score_canonical(ix, ratio, b, scores, ld, pg, st, la);
+    if (e != hipSuccess) return e;
+    const int64_t bound = nch * kListChunk;
+    const int cap = (int)(bound < kListMaxEntries ? bound : kListMaxEntries);
+    const size_t lds = (size_t)cap * 8;
+    e = enable_dyn_lds((const void *)topk_lists_kernel, (int)lds);
+    if (e != hipSuccess) return e;
+    const int log2r = __builtin_ctz((unsigned)ratio);
+    trace("topk lists rows=%lld K=%d chunks=%lld cap=%d", (long long)b.total_q, K, (long long)nch, cap);
+    hipLaunchKernelGGL(topk_lists_kernel, dim3((unsigned)b.total_q), dim3(kTopkThreads), lds, st, scores, ld,
+                       b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, K, la, cap);
+    return hipGetLastError();
+}
 
 static int64_t norm_chunks(const qsa_batch &b, int ratio) {
     const int64_t max_nb = b.max_kv_len / ratio;

@@ -15,8 +15,8 @@ import numpy as np
 
 from . import (INGEST_OK, MAX_LAYERS, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA,
                Batch, KeyRing, Paging, attn_layers_workspace_size, attn_workspace_size, compress_keys,
-               index_score, ingest, ingest_index_score, pool_scores, sparse_attn_decode, sparse_attn_decode_layers,
-               sparse_attn_prefill, topk_blocks, topk_workspace_size)
+               index_score, index_score_topk, ingest, ingest_index_score, pool_scores, score_topk_workspace_size,
+               sparse_attn_decode, sparse_attn_decode_layers, sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
              "fp4": torch.float4_e2m1fn_x2}
@@ -72,6 +72,8 @@ class DeviceProblem:
     token_pool: Optional[int] = None       # QSA_POOL_*: block scores pooled from token scores
     tok_scores: Optional[torch.Tensor] = None
     fuse_ingest: bool = True               # append + canonical scores in one launch when possible
+    sel_ws: Optional[torch.Tensor] = None  # qsa_index_score_topk workspace
+    fuse_select: bool = True               # canonical scores and their top-k in one call when possible
 
     @property
     def blocks_per_query(self) -> int:
@@ -118,6 +120,17 @@ class DeviceProblem:
         index_score(self.q_idx, self.w, self.kc, self.kc_scale, self.ratio, self.batch, self.scores,
                     mode=mode, stream=stream, paging=self.paging)
 
+    def select_fusable(self, mode: int = QSA_SCORE_CANONICAL) -> bool:
+        """Whether scores and selection can run as one qsa_index_score_topk
+        call (canonical scores on compressed keys, no window)."""
+        return (self.fuse_select and mode == QSA_SCORE_CANONICAL and self.token_pool is None
+                and self.local_blocks == 0)
+
+    def score_topk(self, stream=None) -> None:
+        """qsa_index_score_topk: score() and topk() in one call."""
+        index_score_topk(self.q_idx, self.w, self.kc, self.kc_scale, self.budget, self.ratio, self.batch,
+                         self.scores, self.idx, self.sel_ws, stream=stream, paging=self.paging)
+
     def topk(self, certified: bool = False, stream=None) -> None:
         recheck = (self.q_idx, self.w, self.kc, self.kc_scale) if certified else None
         topk_blocks(self.scores, self.budget, self.ratio, self.batch, self.idx, recheck=recheck,
@@ -134,11 +147,15 @@ class DeviceProblem:
         mode = QSA_SCORE_MFMA if mfma else QSA_SCORE_CANONICAL
         if self.ingest_fusable(mode):
             self.ingest_score(stream=stream)
+            self.topk(certified=mfma, stream=stream)
         else:
             if self.ing is not None:
                 self.ingest(stream=stream)
-            self.score(mode, stream=stream)
-        self.topk(certified=mfma, stream=stream)
+            if self.select_fusable(mode):
+                self.score_topk(stream=stream)
+            else:
+                self.score(mode, stream=stream)
+                self.topk(certified=mfma, stream=stream)
         self.attend(stream=stream)
 
 
@@ -171,6 +188,9 @@ def upload(wl, device: str = "cuda", decode: Optional[bool] = None, mfma_ws: boo
     cws = topk_workspace_size(batch, sp.budget, sp.ratio, None)
     if cws:
         dp.topk_ws_canon = torch.empty(cws, dtype=torch.uint8, device=device)
+    sws = score_topk_workspace_size(batch, sp.budget, sp.ratio)
+    if sws:
+        dp.sel_ws = torch.empty(sws, dtype=torch.uint8, device=device)
     if mfma_ws:
         tws = topk_workspace_size(batch, sp.budget, sp.ratio,
                                   (dp.q_idx, dp.w, dp.kc, dp.kc_scale))
