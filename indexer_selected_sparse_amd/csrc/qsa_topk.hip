@@ -1290,7 +1290,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
     ListArgs la, int cap) {
     __shared__ TopkShared S;
     __shared__ uint32_t bcand[kBinCandMax];
-    extern __shared__ uint32_t lds_lists[];          // keys [cap], then block ids [cap]
+    extern __shared__ uint32_t lds_lists[];          // keys [cap], then lanes [cap] (bytes)
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t i = blockIdx.x;
     const uint32_t *__restrict__ gk = la.keys + i * la.stride;
@@ -1320,27 +1320,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
     const int M = nch * kk;
     if (M <= cap) {
         uint32_t *keys = lds_lists;
-        int32_t *blk = reinterpret_cast<int32_t *>(lds_lists + cap);
+        uint8_t *locs = reinterpret_cast<uint8_t *>(lds_lists + cap);
+        // entries j = t + u*1024 (u < 4) stay in registers too (kr); the
+        // rest (rows with more than 4096 entries) are read back from LDS
         uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u;
         uint32_t mcut = (int)threadIdx.x < nch ? c0 : 0u;
         for (int c = (int)threadIdx.x + kTopkThreads; c < nch; c += kTopkThreads) mcut = max(mcut, gc[c]);
-        auto put = [&](int j, uint32_t key, uint32_t lane_of) {
-            keys[j] = key;
-            blk[j] = (int32_t)(((uint32_t)j / (uint32_t)kk) * kListChunk + lane_of);
+        auto note = [&](uint32_t key) {
             if (key != 0u) {                         // padding (key 0) is not a block
                 kmin = min(kmin, key);
                 kmax = max(kmax, key);
                 ++nreal;
             }
         };
+        uint32_t kr[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = (int)threadIdx.x + u * kTopkThreads;
-            if (j < M && j < spec_n) put(j, k[u], l[u]);
+            kr[u] = 0u;
+            if (j < M) {
+                kr[u] = j < spec_n ? k[u] : gk[j];
+                keys[j] = kr[u];
+                locs[j] = (uint8_t)(j < spec_n ? l[u] : gl[j]);
+                note(kr[u]);
+            }
         }
-        for (int j = (int)threadIdx.x + spec_n; j < M; j += kTopkThreads) put(j, gk[j], gl[j]);
+        for (int j = (int)threadIdx.x + 4 * kTopkThreads; j < M; j += kTopkThreads) {
+            const uint32_t key = gk[j];
+            keys[j] = key;
+            locs[j] = gl[j];
+            note(key);
+        }
         S.hist[threadIdx.x] = 0u;                    // the linear histogram's bin
-        // one exchange for the four reductions (its barrier also publishes keys / blk)
+        // one exchange for the four reductions (its barrier also publishes keys / locs)
         {
             const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax), w_mc = wave_max_u32(mcut);
             const uint32_t w_n = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nreal), kWave - 1);
@@ -1379,7 +1391,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             auto bin_of = [&](uint32_t key) {
                 return min(kListBins - 1, (int)((key_value(key) - vmin) * scale));
             };
-            for (int j = threadIdx.x; j < M; j += kTopkThreads) {
+            int kb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kb[u] = kr[u] != 0u ? bin_of(kr[u]) : -1;
+                if (kb[u] >= 0) atomicAdd(&S.hist[kb[u]], 1u);
+            }
+            for (int j = (int)threadIdx.x + 4 * kTopkThreads; j < M; j += kTopkThreads) {
                 const uint32_t key = keys[j];
                 if (key != 0u) atomicAdd(&S.hist[bin_of(key)], 1u);
             }
@@ -1400,26 +1418,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             const uint32_t need = (uint32_t)K - S.s1;
             const uint32_t nbin = S.s3;
             if (nbin <= (uint32_t)kBinCandMax) {
-                for (int j = threadIdx.x; j < M; j += kTopkThreads) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (kb[u] == tb) bcand[atomicAdd(&S.s2, 1u)] = kr[u];
+                for (int j = (int)threadIdx.x + 4 * kTopkThreads; j < M; j += kTopkThreads) {
                     const uint32_t key = keys[j];
                     if (key != 0u && bin_of(key) == tb) bcand[atomicAdd(&S.s2, 1u)] = key;
                 }
                 __syncthreads();
                 if (wave == 0) {
-                    // the need-th largest of the bin's nbin keys, exactly
-                    const uint32_t key = lane < (int)nbin ? bcand[lane] : 0u;
-                    uint32_t t = 0;
-                    for (int bit = 30; bit >= 0; bit -= 2) {
-                        const uint32_t c3 = t | (3u << bit), c2 = t | (2u << bit), c1 = t | (1u << bit);
-                        const uint32_t n3 = (uint32_t)__builtin_popcountll(__ballot(key >= c3));
-                        const uint32_t n2 = (uint32_t)__builtin_popcountll(__ballot(key >= c2));
-                        const uint32_t n1 = (uint32_t)__builtin_popcountll(__ballot(key >= c1));
-                        t = n3 >= need ? c3 : (n2 >= need ? c2 : (n1 >= need ? c1 : t));
+                    // the need-th largest of the bin's nbin keys, exactly: lane
+                    // l < nbin counts the bin's keys above and equal to its own
+                    // (broadcast reads), and the key whose rank range holds
+                    // `need` is T
+                    const bool own = lane < (int)nbin;
+                    const uint32_t key = own ? bcand[lane] : 0u;
+                    uint32_t gt = 0, eq = 0;
+                    for (int j = 0; j < (int)nbin; ++j) {
+                        const uint32_t o = bcand[j];
+                        gt += o > key ? 1u : 0u;
+                        eq += o == key ? 1u : 0u;
                     }
-                    const uint32_t gt = (uint32_t)__builtin_popcountll(__ballot(key > t));
-                    const uint32_t eq = (uint32_t)__builtin_popcountll(__ballot(key == t));
-                    if (lane == 0) {
-                        S.s0 = t;
+                    const bool hit = own && gt < need && need <= gt + eq;
+                    const uint64_t m = __ballot(hit);
+                    if (hit && lane == (int)__builtin_ctzll(m)) {
+                        S.s0 = key;
                         S.s1 = need - gt;
                         S.s3 = eq;
                     }
@@ -1436,7 +1459,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             T = radix_select(LdsKey{keys}, (int64_t)M, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
         }
         if (T != 0u && mcut < T) {
-            // ordered output: thread t owns list entries [t*E, t*E + E)
+            // ordered output: thread t owns list entries [t*E, t*E + E); entry j
+            // is lane locs[j] of chunk j / kk
             const int E = (M + kTopkThreads - 1) / kTopkThreads;
             const int j0 = (int)threadIdx.x * E;
             const int j1 = j0 + E < M ? j0 + E : M;
@@ -1450,6 +1474,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             const uint32_t before = wg_scan((ngt << 16) | neq, S, tot);   // both counts < 2^16
             uint32_t tie = before & 0xffffu;
             uint32_t pos = (before >> 16) + min(tie, need_eq);
+            int chunk = j0 < M ? j0 / kk : 0;
+            int slot = j0 - chunk * kk;
             for (int j = j0; j < j1; ++j) {
                 const uint32_t key = keys[j];
                 bool take = key > T;
@@ -1458,8 +1484,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
                     ++tie;
                 }
                 if (take) {
-                    if (pos < (uint32_t)K) out[pos] = blk[j];
+                    if (pos < (uint32_t)K) out[pos] = chunk * kListChunk + locs[j];
                     ++pos;
+                }
+                if (++slot == kk) {
+                    slot = 0;
+                    ++chunk;
                 }
             }
             return;
@@ -1523,7 +1553,7 @@ hipError_t launch_score_topk(const qsa_indexer &ix, int budget, int ratio, const
     if (e != hipSuccess) return e;
     const int64_t bound = nch * kListChunk;
     const int cap = (int)(bound < kListMaxEntries ? bound : kListMaxEntries);
-    const size_t lds = (size_t)cap * 8;
+    const size_t lds = (size_t)cap * 5;
     e = enable_dyn_lds((const void *)topk_lists_kernel, (int)lds);
     if (e != hipSuccess) return e;
     const int log2r = __builtin_ctz((unsigned)ratio);
