@@ -21,9 +21,16 @@ it completes, its K/V rows), as a serving step does.  Decode steps rotate over s
 inputs (more distinct bytes than the 256 MB last-level cache holds), so a
 step is not served from a cache warmed by the previous one.
 
+A decode step runs as qsa_decode_step, timed as its two halves: the scorer
+(scores + per-chunk candidate lists) and the attention call whose workgroups
+select their own part of the selection from the lists (--unfused-step: a
+finish launch selects, then the plain attention call).
+
 `roofline` describes the dominant kernel: for decode, the sparse attention
-call (gather kernel + split combine), timed with HIP events on the stream it
-runs on; achieved = algorithmic bytes / its mean duration.  `traffic` comes
+call (selection from the lists + gather kernel + split combine), timed with
+HIP events on the stream it runs on; achieved = algorithmic bytes (the
+selected K/V rows, q, out and the idx row; the lists, about 0.2% of that, are
+not counted) / its mean duration.  `traffic` comes
 from the FETCH_SIZE / WRITE_SIZE counter summary under profiles/, used only
 while the attention source is unchanged since the counters were taken.
 """
@@ -94,6 +101,10 @@ def parse():
     p.add_argument("--unfused-select", action="store_true",
                    help="decode: scores and top-k as two calls (qsa_index_score, qsa_topk_blocks) instead of "
                         "qsa_index_score_topk")
+    p.add_argument("--unfused-step", action="store_true",
+                   help="decode: the selection as its own launch (qsa_index_score_topk, then "
+                        "qsa_sparse_attn_decode) instead of inside the attention kernel (qsa_decode_step, "
+                        "timed as its two halves)")
     p.add_argument("--no-long", action="store_true",
                    help="batched_decode: skip the long_decode sub-record (the 128K end of the metric)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -410,12 +421,19 @@ def measure(args, workload, cpu):
     # scores and their selection as one qsa_index_score_topk call (the
     # scorer writes per-chunk candidate lists, a small finish selects)
     fuse_sel = (not prefill and not fuse_ing and not args.unfused_select and base.select_fusable())
+    # a decode step as qsa_decode_step: the scorer writes the lists and each
+    # attention workgroup selects its own part from them; timed as the step's
+    # two halves (qsa_index_score_lists, qsa_sparse_attn_decode_lists), which
+    # launch the same kernels as the one call
+    fuse_step = fuse_sel and stacks is None and not args.unfused_step and base.step_fusable()
 
     def score(p):
         if fuse_ing:
             p.ingest_score()
         elif prefill:
             p.score(QSA_SCORE_MFMA)
+        elif fuse_step:
+            p.score_lists()
         elif fuse_sel:
             p.score_topk()
         else:
@@ -425,13 +443,19 @@ def measure(args, workload, cpu):
         if not fuse_sel:
             p.topk(certified=prefill)
 
+    def attend(p):
+        if fuse_step:
+            p.attend_lists()
+        else:
+            p.attend()
+
     log(f"{workload}: {R} input copies resident; timing {args.steps} steps")
     for s in range(args.warmup):
         p = reps[s % R]
         ingest(p)
         score(p)
         topk(p)
-        p.attend()
+        attend(p)
     torch.cuda.synchronize()
 
     # events are recorded on torch's current stream, which is the stream
@@ -449,7 +473,7 @@ def measure(args, workload, cpu):
         e[1].record()
         topk(p)
         e[2].record()
-        p.attend()
+        attend(p)
         e[3].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -472,7 +496,7 @@ def measure(args, workload, cpu):
                 ingest(p)
                 score(p)
                 topk(p)
-                p.attend()
+                attend(p)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         if stacks is not None:
@@ -490,7 +514,7 @@ def measure(args, workload, cpu):
                     ingest(p)
                     score(p)
                     topk(p)
-                    p.attend()
+                    attend(p)
             graphs.append(g)
         for s_ in range(args.warmup):
             graphs[s_ % R].replay()
@@ -530,6 +554,8 @@ def measure(args, workload, cpu):
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R, "score_and_select": "one call" if fuse_sel else "two calls",
+                   "selection": ("inside the attention kernel (qsa_decode_step)" if fuse_step
+                                 else "own launch" if not prefill else "certified top-k launch"),
                    **({"paged_page_size": args.paged} if args.paged else {}),
                    **({"layers": n_layers, "full_every": args.full_every, "fused_layers": not args.unfused_layers,
                        "layers_with_own_indexer": sum(stacks[0].full)} if stacks is not None else {}),
@@ -538,8 +564,10 @@ def measure(args, workload, cpu):
                    **({"ingest": "one token per sequence", "ingest_fused_with_scores": fuse_ing,
                        "ring_capacity": int(base.ing.ring.keys.shape[1])} if args.ingest else {})},
         "step_ms_percentiles": pct,
-        "kernel_ms": {**({"index_score_topk": t_score} if fuse_sel else {"index_score": t_score, "topk": t_topk}),
-                      "sparse_attn": t_attn, **({"ingest": t_ingest} if args.ingest else {})},
+        "kernel_ms": {**({"index_score_lists": t_score, "sparse_attn_select": t_attn} if fuse_step else
+                         {"index_score_topk": t_score, "sparse_attn": t_attn} if fuse_sel else
+                         {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn}),
+                      **({"ingest": t_ingest} if args.ingest else {})},
         "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
     }
@@ -563,7 +591,9 @@ def measure(args, workload, cpu):
                            or args.token_pool) else recorded_traffic(spec.name)
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
-                           "kernel": "qsa_sparse_attn_decode (gather attention + split combine)",
+                           "kernel": ("qsa_sparse_attn_decode_lists (per-part selection from the candidate "
+                                      "lists + gather attention + split combine)" if fuse_step else
+                                      "qsa_sparse_attn_decode (gather attention + split combine)"),
                            "bytes_per_launch": attn_bytes, "avg_ms": t_attn}
         rec["step_hbm_gbps"] = step_bytes / (ms_step * 1e-3) / 1e9
         rec["step_hbm_frac"] = rec["step_hbm_gbps"] / HBM_PEAK_GBPS

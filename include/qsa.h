@@ -381,6 +381,50 @@ qsa_status qsa_index_score_topk(const qsa_indexer *ix, int32_t budget, int32_t r
                                 float *scores, int64_t ld_scores, int32_t *idx, void *ws, size_t ws_bytes,
                                 const qsa_paged_kv *pg, void *stream);
 
+/* The whole decode step in two launches (plus the split combine): the same
+ * scores, idx and out, bit for bit, as qsa_index_score_topk followed by
+ * qsa_sparse_attn_decode(_paged) on the same batch.  The scorer writes its
+ * per-chunk candidate lists (see qsa_index_score_topk), and every workgroup
+ * of the attention kernel — one per (query, KV head, part of the selected
+ * blocks) — derives the block ids of its own part from those lists with the
+ * same certificate, or exactly from the query's score row when the
+ * certificate fails; the workgroups of KV head 0, part 0 write idx.  No
+ * workgroup waits for another, and no separate top-k launch runs.  (The
+ * second "vLLM vs Atlas" report on the "Agentic shootout" page, section
+ * (a)6, runs indexer, KV update and sparse attention as one step; the
+ * third "Flash-Next support" report, section (d), item 3, recommends
+ * splitting the key work from the query work within one launch.)
+ * Decode batches of one query per sequence.  Batches of more than 256
+ * queries, and K/V the matrix-core kernel does not address (fp32, or rows
+ * past 32-bit offsets), run qsa_index_score_topk and qsa_sparse_attn_decode
+ * instead, with the same results.
+ *  ix, a:  as for qsa_index_score and qsa_sparse_attn_decode.
+ *  scores: device f32 [total_q, ld_scores] (written, canonical).
+ *  idx:    device int32 [total_q, budget/ratio] (written).
+ *  out:    device [total_q, hq, d] (dtype of q).
+ *  ws:     device workspace of at least qsa_decode_step_workspace_size()
+ *          bytes; no initialisation, no state between calls.
+ *  pg:     NULL, or the paging of kc, kc_scale, K and V.
+ * Errors: those of qsa_index_score_topk and qsa_sparse_attn_decode. */
+size_t qsa_decode_step_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t budget, int32_t ratio);
+qsa_status qsa_decode_step(const qsa_indexer *ix, const qsa_attn *a, int32_t budget, int32_t ratio,
+                           const qsa_batch *b, float *scores, int64_t ld_scores, int32_t *idx, void *out, void *ws,
+                           size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
+
+/* The two halves of qsa_decode_step as separate calls, in this order on one
+ * stream, with the same workspace (for a caller that times them apart or
+ * puts work between them): qsa_index_score_lists writes the scores and the
+ * candidate lists (into ws; a reads only the attention shape, for the
+ * workspace size); qsa_sparse_attn_decode_lists selects and attends, and
+ * writes idx and out.  Together they equal qsa_decode_step bit for bit.
+ * Errors: as qsa_decode_step. */
+qsa_status qsa_index_score_lists(const qsa_indexer *ix, const qsa_attn *a, int32_t budget, int32_t ratio,
+                                 const qsa_batch *b, float *scores, int64_t ld_scores, void *ws, size_t ws_bytes,
+                                 const qsa_paged_kv *pg, void *stream);
+qsa_status qsa_sparse_attn_decode_lists(const qsa_attn *a, int32_t budget, int32_t ratio, const qsa_batch *b,
+                                        const float *scores, int64_t ld_scores, int32_t *idx, void *out, void *ws,
+                                        size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
+
 /* ---- Layers that share one selection.  The first "llama.cpp vs Atlas"
  * report (section (a)3) lists indexers that are either full or shared: a
  * shared layer attends its own K/V with the top-k of the last full layer.

@@ -36,7 +36,8 @@ EXPORTS = (
     "qsa_sparse_attn_prefill_paged", "qsa_ingest", "qsa_ring_rewind", "qsa_topk_blocks_local",
     "qsa_pool_scores", "qsa_attn_layers_workspace_size", "qsa_sparse_attn_decode_layers",
     "qsa_ingest_index_score", "qsa_sparse_attn_decode_static", "qsa_score_topk_workspace_size",
-    "qsa_index_score_topk",
+    "qsa_index_score_topk", "qsa_decode_step_workspace_size", "qsa_decode_step", "qsa_index_score_lists",
+    "qsa_sparse_attn_decode_lists",
 )
 
 MAX_LAYERS = 8   # QSA_MAX_LAYERS
@@ -139,6 +140,14 @@ def lib():
         L.qsa_score_topk_workspace_size.argtypes = [P, i32, i32]
         L.qsa_index_score_topk.restype = i32
         L.qsa_index_score_topk.argtypes = [P, i32, i32, P, P, i64, P, P, sz, P, P]
+        L.qsa_decode_step_workspace_size.restype = sz
+        L.qsa_decode_step_workspace_size.argtypes = [P, P, i32, i32]
+        L.qsa_decode_step.restype = i32
+        L.qsa_decode_step.argtypes = [P, P, i32, i32, P, P, i64, P, P, P, sz, P, P]
+        L.qsa_index_score_lists.restype = i32
+        L.qsa_index_score_lists.argtypes = [P, P, i32, i32, P, P, i64, P, sz, P, P]
+        L.qsa_sparse_attn_decode_lists.restype = i32
+        L.qsa_sparse_attn_decode_lists.argtypes = [P, i32, i32, P, P, i64, P, P, P, sz, P, P]
         L.qsa_sparse_attn_decode_static.restype = i32
         L.qsa_sparse_attn_decode_static.argtypes = [P, P, i32, i32, P, P, P]
         L.qsa_ring_rewind.restype = i32
@@ -339,6 +348,56 @@ def index_score_topk(q_idx, w, kc, kc_scale, budget: int, ratio: int, batch: Bat
     pg = None if paging is None else ctypes.byref(paging._c())
     _check(lib().qsa_index_score_topk(ctypes.byref(ix), budget, ratio, ctypes.byref(b), _ptr(scores),
                                       scores.shape[1], _ptr(idx), _ptr(ws), nbytes, pg, _stream(stream)))
+
+
+def decode_step_workspace_size(q, k, v, softmax_scale, budget: int, ratio: int, batch: Batch) -> int:
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    return int(lib().qsa_decode_step_workspace_size(ctypes.byref(b), ctypes.byref(a), budget, ratio))
+
+
+def decode_step(q_idx, w, kc, kc_scale, q, k, v, softmax_scale, budget: int, ratio: int, batch: Batch,
+                scores: torch.Tensor, idx: torch.Tensor, out: torch.Tensor, ws: Optional[torch.Tensor],
+                stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_decode_step: scores, selection and sparse attention of a decode batch."""
+    for t, n in ((scores, "scores"), (idx, "idx"), (out, "out")):
+        _dev(t, n)
+    ix = _indexer(q_idx, w, kc, kc_scale)
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pg = None if paging is None else ctypes.byref(paging._c())
+    _check(lib().qsa_decode_step(ctypes.byref(ix), ctypes.byref(a), budget, ratio, ctypes.byref(b), _ptr(scores),
+                                 scores.shape[1], _ptr(idx), _ptr(out), _ptr(ws), nbytes, pg, _stream(stream)))
+
+
+def index_score_lists(q_idx, w, kc, kc_scale, q, k, v, softmax_scale, budget: int, ratio: int, batch: Batch,
+                      scores: torch.Tensor, ws: Optional[torch.Tensor], stream=None,
+                      paging: Optional[Paging] = None) -> None:
+    """qsa_index_score_lists: the scorer half of qsa_decode_step."""
+    _dev(scores, "scores")
+    ix = _indexer(q_idx, w, kc, kc_scale)
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pg = None if paging is None else ctypes.byref(paging._c())
+    _check(lib().qsa_index_score_lists(ctypes.byref(ix), ctypes.byref(a), budget, ratio, ctypes.byref(b),
+                                       _ptr(scores), scores.shape[1], _ptr(ws), nbytes, pg, _stream(stream)))
+
+
+def sparse_attn_decode_lists(q, k, v, softmax_scale, budget: int, ratio: int, batch: Batch, scores: torch.Tensor,
+                             idx: torch.Tensor, out: torch.Tensor, ws: Optional[torch.Tensor], stream=None,
+                             paging: Optional[Paging] = None) -> None:
+    """qsa_sparse_attn_decode_lists: the selection + attention half of qsa_decode_step."""
+    for t, n in ((scores, "scores"), (idx, "idx"), (out, "out")):
+        _dev(t, n)
+    a = _attn(q, k, v, softmax_scale)
+    b = batch._c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pg = None if paging is None else ctypes.byref(paging._c())
+    _check(lib().qsa_sparse_attn_decode_lists(ctypes.byref(a), budget, ratio, ctypes.byref(b), _ptr(scores),
+                                              scores.shape[1], _ptr(idx), _ptr(out), _ptr(ws), nbytes, pg,
+                                              _stream(stream)))
 
 
 def topk_workspace_size(batch: Batch, budget: int, ratio: int, recheck=None) -> int:

@@ -427,6 +427,104 @@ qsa_status qsa_index_score_topk(const qsa_indexer *ix, int32_t budget, int32_t r
                           });
 }
 
+// Workspace of qsa_decode_step: the candidate lists, then the attention
+// partials (each 256-byte aligned).
+static size_t decode_step_lists_bytes(const qsa_batch &b, int32_t budget, int32_t ratio) {
+    return (score_topk_workspace_bytes(b, budget, ratio) + 255) & ~(size_t)255;
+}
+
+size_t qsa_decode_step_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t budget, int32_t ratio) {
+    if (!b || !a || check_budget(budget, ratio) != QSA_OK || a->hkv < 1) return 0;
+    return decode_step_lists_bytes(*b, budget, ratio) + attn_workspace_bytes(*b, *a, budget, ratio);
+}
+
+// Shared validation of the decode-step calls.
+static qsa_status decode_step_check(const qsa_indexer *ix, const qsa_attn *a, int32_t budget, int32_t ratio,
+                                    const qsa_batch *b, const float *scores, int64_t ld_scores, int32_t *idx,
+                                    void *out, void *ws, size_t ws_bytes, const qsa_paged_kv *pg) {
+    qsa_status s = ix ? check_indexer(ix, false) : ok();
+    if (s == QSA_OK) s = attn_validate(a, idx, budget, ratio, b, out, true, pg);
+    if (s == QSA_OK) s = check_batch(b, ix != nullptr && pg == nullptr);   // the scorer reads blk_offsets
+    if (s == QSA_OK) s = check_rows(b, ratio);
+    if (s != QSA_OK) return s;
+    if (!scores) return fail(QSA_ERR_INVALID_ARGUMENT, "scores is NULL");
+    const int64_t need_ld = (b->max_kv_len + ratio - 1) / ratio;
+    if (ld_scores < need_ld || ld_scores < 1)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
+                    (long long)ld_scores, (long long)need_ld);
+    const size_t need = decode_step_lists_bytes(*b, budget, ratio) + attn_workspace_bytes(*b, *a, budget, ratio);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(QSA_ERR_WORKSPACE, "decode step workspace of %zu bytes is smaller than the %zu required "
+                    "(qsa_decode_step_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    return ok();
+}
+
+// The scorer half: scores, and the candidate lists when the batch has them.
+static hipError_t decode_step_score(const qsa_indexer &ix, int32_t budget, int32_t ratio, const qsa_batch &b,
+                                    float *scores, int64_t ld, void *ws, const qsa_paged_kv *pg, hipStream_t st) {
+    if (!score_topk_uses_lists(b)) return launch_score_canonical(ix, ratio, b, scores, ld, pg, st, ListArgs{});
+    return launch_score_canonical(ix, ratio, b, scores, ld, pg, st, list_args(b, budget, ratio, ws));
+}
+
+// The attention half: the selection (in the attention kernel when it can
+// make it, else the list finish or the plain top-k) and the attention.
+static hipError_t decode_step_attend(const qsa_attn &a, int32_t budget, int32_t ratio, const qsa_batch &b,
+                                     const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
+                                     const qsa_paged_kv *pg, hipStream_t st) {
+    void *attn_ws = ws ? static_cast<uint8_t *>(ws) + decode_step_lists_bytes(b, budget, ratio) : nullptr;
+    if (!score_topk_uses_lists(b)) {
+        hipError_t e = launch_topk(scores, ld, nullptr, budget, ratio, b, idx, budget / ratio, ws, st);
+        if (e != hipSuccess) return e;
+        return launch_attn(a, idx, budget, ratio, b, out, attn_ws, true, pg, st);
+    }
+    const ListArgs la = list_args(b, budget, ratio, ws);
+    if (attn_select_supported(b, a, pg))
+        return launch_attn_select(a, budget, ratio, b, la, scores, ld, idx, out, attn_ws, pg, st);
+    hipError_t e = launch_topk_from_lists(scores, ld, budget, ratio, b, idx, la, st);
+    if (e != hipSuccess) return e;
+    return launch_attn(a, idx, budget, ratio, b, out, attn_ws, true, pg, st);
+}
+
+qsa_status qsa_decode_step(const qsa_indexer *ix, const qsa_attn *a, int32_t budget, int32_t ratio,
+                           const qsa_batch *b, float *scores, int64_t ld_scores, int32_t *idx, void *out, void *ws,
+                           size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {
+    if (!ix) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer is NULL");
+    qsa_status s = decode_step_check(ix, a, budget, ratio, b, scores, ld_scores, idx, out, ws, ws_bytes, pg);
+    if (s != QSA_OK) return s;
+    return launch_checked("qsa_decode_step", batch_check(*b, ratio, pg == nullptr, pg), stream, [&](hipStream_t st) {
+        hipError_t e = decode_step_score(*ix, budget, ratio, *b, scores, ld_scores, ws, pg, st);
+        if (e != hipSuccess) return e;
+        return decode_step_attend(*a, budget, ratio, *b, scores, ld_scores, idx, out, ws, pg, st);
+    });
+}
+
+qsa_status qsa_index_score_lists(const qsa_indexer *ix, const qsa_attn *a, int32_t budget, int32_t ratio,
+                                 const qsa_batch *b, float *scores, int64_t ld_scores, void *ws, size_t ws_bytes,
+                                 const qsa_paged_kv *pg, void *stream) {
+    if (!ix) return fail(QSA_ERR_INVALID_ARGUMENT, "indexer is NULL");
+    // idx and out are not touched by this half: validate with stand-ins
+    int32_t dummy_idx = 0;
+    qsa_status s = decode_step_check(ix, a, budget, ratio, b, scores, ld_scores, &dummy_idx, &dummy_idx, ws,
+                                     ws_bytes, pg);
+    if (s != QSA_OK) return s;
+    return launch_checked("qsa_index_score_lists", batch_check(*b, ratio, pg == nullptr, pg), stream,
+                          [&](hipStream_t st) {
+                              return decode_step_score(*ix, budget, ratio, *b, scores, ld_scores, ws, pg, st);
+                          });
+}
+
+qsa_status qsa_sparse_attn_decode_lists(const qsa_attn *a, int32_t budget, int32_t ratio, const qsa_batch *b,
+                                        const float *scores, int64_t ld_scores, int32_t *idx, void *out, void *ws,
+                                        size_t ws_bytes, const qsa_paged_kv *pg, void *stream) {
+    qsa_status s = decode_step_check(nullptr, a, budget, ratio, b, scores, ld_scores, idx, out, ws, ws_bytes, pg);
+    if (s != QSA_OK) return s;
+    return launch_checked("qsa_sparse_attn_decode_lists", batch_check(*b, ratio, false, pg), stream,
+                          [&](hipStream_t st) {
+                              return decode_step_attend(*a, budget, ratio, *b, scores, ld_scores, idx, out, ws, pg,
+                                                        st);
+                          });
+}
+
 size_t qsa_topk_workspace_size(const qsa_batch *b, int32_t budget, int32_t ratio,
                                const qsa_indexer *recheck) {
     if (!b || check_budget(budget, ratio) != QSA_OK) return 0;

@@ -40,6 +40,7 @@
 
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+#include "qsa_lists.hpp"
 
 namespace qsa {
 namespace {
@@ -61,6 +62,13 @@ struct AttnArgs {
     float *ws_o;             // [total_q, hq, n_part, D]
     float *ws_ml;            // [total_q, hq, n_part, 2]
     PageMap pm;              // paged K/V pools (pm.table == nullptr: contiguous)
+    // selection inside the decode kernel (qsa_decode_step): the scorer's
+    // candidate lists, the score rows (exact fallback) and the idx rows the
+    // workgroups of KV head 0, part 0 write
+    ListArgs la;
+    const float *scores;
+    int64_t ld;
+    int32_t *idx_out;
 };
 
 // Several layers that share one selection in one launch (blockIdx.y = layer):
@@ -715,6 +723,341 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---------------------------------------------------------------------------
+// Selection inside the decode kernel (qsa_decode_step).  Every workgroup
+// (query i, KV head g, part c) derives the block ids of its own part of the
+// query's ascending selection — positions [p_beg, p_end) — from the scorer's
+// per-chunk candidate lists (qsa_lists.hpp), with the same certificate as
+// the list finish of qsa_index_score_topk; a row the certificate does not
+// cover (or whose lists do not fit) is selected exactly from its whole
+// score row.  The workgroup of KV head 0, part 0 also writes the idx row.
+// No workgroup waits for another.  Scratch lives in the LDS of the ring,
+// which is free until the first step is issued; the part's slot table goes
+// to the LDS region after the rings (kWgWaves * kBigTabSlots entries).
+constexpr int kSelThreads = kWgWaves * kWave;          // 256
+constexpr int kSelBins = 1024;
+constexpr int kSelBinCand = kWave;
+struct SelScratch {
+    uint32_t hist[kSelBins];
+    uint32_t red[4][kWgWaves];
+    uint32_t s[8];
+    uint32_t bc[kSelBinCand];
+};
+constexpr int kSelScratchBytes = (int)((sizeof(SelScratch) + 255) & ~(size_t)255);
+
+__device__ __forceinline__ float sel_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Exclusive prefix sum over the 256 threads (thread order); total in `tot`.
+// `slot` picks one of the four exchange rows (consecutive calls use
+// different rows, so no trailing barrier is needed).
+__device__ __forceinline__ uint32_t sel_scan(uint32_t v, SelScratch &X, int slot, uint32_t &tot) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane == kWave - 1) X.red[slot][wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < kWgWaves; ++w) {
+        const uint32_t x = X.red[slot][w];
+        before += w < wave ? x : 0u;
+        t += x;
+    }
+    tot = t;
+    return before + incl - v;
+}
+
+// Exact need-th largest key among key(j), j < n (MSB-first radix, 8-bit
+// digits below the bits kmin and kmax share); 256 threads.
+template <typename KeyF>
+__device__ __forceinline__ uint32_t sel_radix(const KeyF &key, int64_t n, uint32_t need, uint32_t kmin, uint32_t kmax,
+                              SelScratch &X, uint32_t &need_eq, uint32_t &total_eq) {
+    const uint32_t diff = kmin ^ kmax;
+    if (diff == 0) {
+        need_eq = need;
+        total_eq = (uint32_t)n;
+        return kmin;
+    }
+    const int hi_bit = 31 - __builtin_clz(diff);
+    uint32_t prefix = hi_bit == 31 ? 0u : (kmax & ~((2u << hi_bit) - 1u));
+    int lo_bit = hi_bit + 1;
+    total_eq = 0;
+    while (lo_bit > 0) {
+        const int width = lo_bit >= 8 ? 8 : lo_bit;
+        const int shift = lo_bit - width;
+        const uint32_t mask_hi = lo_bit >= 32 ? 0u : ~((1u << lo_bit) - 1u);
+        __syncthreads();
+        X.hist[threadIdx.x] = 0u;
+        __syncthreads();
+        for (int64_t j = threadIdx.x; j < n; j += kSelThreads) {
+            const uint32_t k = key(j);
+            if ((k & mask_hi) == prefix) atomicAdd(&X.hist[(k >> shift) & ((1u << width) - 1u)], 1u);
+        }
+        __syncthreads();
+        // thread t owns digit (2^width - 1 - t), counting from the top
+        const int d = (1 << width) - 1 - (int)threadIdx.x;
+        const uint32_t h = d >= 0 ? X.hist[d] : 0u;
+        uint32_t tot;
+        const uint32_t above = sel_scan(h, X, 0, tot);
+        if (d >= 0 && above < need && need <= above + h) {
+            X.s[4] = (uint32_t)d;
+            X.s[5] = above;
+            X.s[6] = h;
+        }
+        __syncthreads();
+        prefix |= X.s[4] << shift;
+        need -= X.s[5];
+        total_eq = X.s[6];
+        lo_bit = shift;
+    }
+    need_eq = need;
+    return prefix;
+}
+
+// Ordered output of a selection over n entries in ascending block order:
+// thread t owns entries [t*E, t*E + E); an entry is selected when its key is
+// > T, or == T among the first need_eq such entries.  Selected positions in
+// [p_beg, p_end) go to the part table (physical block ids when paged); with
+// `row_out`, every position goes to the idx row.
+template <typename KeyF, typename BlkF>
+__device__ __forceinline__ void sel_emit(const KeyF &key, const BlkF &blk_of, int64_t n, uint32_t T, uint32_t need_eq,
+                         int p_beg, int p_end, uint32_t tab, int32_t *row_out, const AttnArgs &A, int seq,
+                         int64_t nb, SelScratch &X) {
+    const int64_t E = (n + kSelThreads - 1) / kSelThreads;
+    const int64_t j0 = (int64_t)threadIdx.x * E;
+    const int64_t j1 = j0 + E < n ? j0 + E : n;
+    uint32_t ngt = 0, neq = 0;
+    for (int64_t j = j0; j < j1; ++j) {
+        const uint32_t k = key(j);
+        ngt += k > T ? 1u : 0u;
+        neq += k == T ? 1u : 0u;
+    }
+    uint32_t tgt, teq;
+    const uint32_t gbefore = sel_scan(ngt, X, 1, tgt);
+    const uint32_t ebefore = sel_scan(neq, X, 2, teq);
+    uint32_t tie = ebefore;
+    uint32_t pos = gbefore + min(tie, need_eq);
+    for (int64_t j = j0; j < j1; ++j) {
+        const uint32_t k = key(j);
+        bool take = k > T;
+        if (k == T) {
+            take = tie < need_eq;
+            ++tie;
+        }
+        if (take) {
+            const int32_t b = blk_of(j);
+            if (row_out) row_out[pos] = b;
+            if ((int)pos >= p_beg && (int)pos < p_end) {
+                const int32_t pb = A.pm.table ? slot_phys(b, A.pm, seq, nb, A.log2r) : b;
+                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)(pos - p_beg)) = pb;
+            }
+            ++pos;
+        }
+    }
+}
+
+// Fill the part table for positions [p_beg, p_end) of query i's selection
+// (nb > 0 visible blocks) and, for the designated workgroup, the idx row.
+template <int D>
+__device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t nb, int p_beg, int p_end,
+                            bool designated, uint32_t tab, uint8_t *ring_lds) {
+    SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
+    const int K = A.K;
+    int32_t *row_out = designated ? A.idx_out + i * (int64_t)K : nullptr;
+    if (nb <= K) {                                           // dense regime: identity
+        for (int j = threadIdx.x; j < K; j += kSelThreads) {
+            if (row_out) row_out[j] = j < nb ? j : -1;
+            if (j >= p_beg && j < p_end) {
+                const int32_t pb = A.pm.table ? slot_phys(j, A.pm, seq, nb, A.log2r) : j;
+                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)(j - p_beg)) = pb;
+            }
+        }
+        __syncthreads();
+        return;
+    }
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int kk = list_len(nb, K);
+    const int nch = (int)((nb + kListChunk - 1) / kListChunk);
+    const int M = nch * kk;
+    constexpr int cap = (kWgWaves * D * kSlotBytes - kSelScratchBytes) / 5;
+    uint32_t *keys = reinterpret_cast<uint32_t *>(ring_lds + kSelScratchBytes);
+    uint8_t *locs = reinterpret_cast<uint8_t *>(keys + cap);
+    uint32_t T = 0, need_eq = 0, total_eq = 0;
+    bool certified = false;
+    if (M <= cap) {
+        const uint32_t *__restrict__ gk = A.la.keys + i * A.la.stride;
+        const uint8_t *__restrict__ gl = A.la.loc + i * A.la.stride;
+        const uint32_t *__restrict__ gc = A.la.cut + i * A.la.cstride;
+        uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u, mcut = 0u;
+        for (int j0 = threadIdx.x; j0 < M; j0 += 4 * kSelThreads) {
+            uint32_t k[4], l[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * kSelThreads;
+                k[u] = j < M ? gk[j] : 0u;
+                l[u] = j < M ? gl[j] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * kSelThreads;
+                if (j < M) {
+                    keys[j] = k[u];
+                    locs[j] = (uint8_t)l[u];
+                    if (k[u] != 0u) {
+                        kmin = min(kmin, k[u]);
+                        kmax = max(kmax, k[u]);
+                        ++nreal;
+                    }
+                }
+            }
+        }
+        for (int cc = threadIdx.x; cc < nch; cc += kSelThreads) mcut = max(mcut, gc[cc]);
+        for (int b = threadIdx.x; b < kSelBins; b += kSelThreads) X.hist[b] = 0u;
+        {
+            const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax), w_mc = wave_max_u32(mcut);
+            const uint32_t w_n = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nreal), kWave - 1);
+            if (lane == 0) {
+                X.red[0][wave] = w_mn;
+                X.red[1][wave] = w_mx;
+                X.red[2][wave] = w_n;
+                X.red[3][wave] = w_mc;
+            }
+            __syncthreads();
+            kmin = X.red[0][0];
+            kmax = X.red[1][0];
+            nreal = X.red[2][0];
+            mcut = X.red[3][0];
+#pragma unroll
+            for (int w = 1; w < kWgWaves; ++w) {
+                kmin = min(kmin, X.red[0][w]);
+                kmax = max(kmax, X.red[1][w]);
+                nreal += X.red[2][w];
+                mcut = max(mcut, X.red[3][w]);
+            }
+            __syncthreads();                                 // X.red is reused below
+        }
+        if (nreal >= (uint32_t)K && mcut < kmax) {
+            bool found = false;
+            const float vmin = sel_key_value(kmin), vmax = sel_key_value(kmax);
+            const float scale = (float)kSelBins / (vmax - vmin);
+            if (kmin == kmax) {
+                T = kmin;
+                need_eq = (uint32_t)K;
+                total_eq = nreal;
+                found = true;
+            } else if (scale < 3.0e38f) {
+                auto bin_of = [&](uint32_t key) {
+                    return min(kSelBins - 1, (int)((sel_key_value(key) - vmin) * scale));
+                };
+                for (int j = threadIdx.x; j < M; j += kSelThreads) {
+                    const uint32_t key = keys[j];
+                    if (key != 0u) atomicAdd(&X.hist[bin_of(key)], 1u);
+                }
+                if (threadIdx.x == 0) X.s[2] = 0u;
+                __syncthreads();
+                // thread t owns bins 1023-4t-3 .. 1023-4t (descending)
+                uint32_t hb[4], own = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hb[e] = X.hist[kSelBins - 1 - 4 * (int)threadIdx.x - e];
+                    own += hb[e];
+                }
+                uint32_t tot;
+                uint32_t above = sel_scan(own, X, 0, tot);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (above < (uint32_t)K && (uint32_t)K <= above + hb[e]) {
+                        X.s[0] = (uint32_t)(kSelBins - 1 - 4 * (int)threadIdx.x - e);
+                        X.s[1] = above;
+                        X.s[3] = hb[e];
+                    }
+                    above += hb[e];
+                }
+                __syncthreads();
+                const int tb = (int)X.s[0];
+                const uint32_t need = (uint32_t)K - X.s[1];
+                const uint32_t nbin = X.s[3];
+                if (nbin <= (uint32_t)kSelBinCand) {
+                    for (int j = threadIdx.x; j < M; j += kSelThreads) {
+                        const uint32_t key = keys[j];
+                        if (key != 0u && bin_of(key) == tb) X.bc[atomicAdd(&X.s[2], 1u)] = key;
+                    }
+                    __syncthreads();
+                    if (wave == 0) {
+                        const bool mine = lane < (int)nbin;
+                        const uint32_t key = mine ? X.bc[lane] : 0u;
+                        uint32_t gt = 0, eq = 0;
+                        for (int j = 0; j < (int)nbin; ++j) {
+                            const uint32_t o = X.bc[j];
+                            gt += o > key ? 1u : 0u;
+                            eq += o == key ? 1u : 0u;
+                        }
+                        const bool hit = mine && gt < need && need <= gt + eq;
+                        const uint64_t m = __ballot(hit);
+                        if (hit && lane == (int)__builtin_ctzll(m)) {
+                            X.s[4] = key;
+                            X.s[5] = need - gt;
+                            X.s[6] = eq;
+                        }
+                    }
+                    __syncthreads();
+                    T = X.s[4];
+                    need_eq = X.s[5];
+                    total_eq = X.s[6];
+                    found = true;
+                }
+            }
+            if (!found) {
+                const uint32_t *kl = keys;
+                T = sel_radix([kl](int64_t j) { return kl[j]; }, (int64_t)M, (uint32_t)K, kmin, kmax, X, need_eq,
+                              total_eq);
+            }
+            certified = T != 0u && mcut < T;
+        }
+        (void)total_eq;
+        if (certified) {
+            sel_emit([keys](int64_t j) { return keys[j]; },
+                     [locs, kk](int64_t j) { return (int32_t)((j / kk) * kListChunk + locs[j]); }, (int64_t)M, T,
+                     need_eq, p_beg, p_end, tab, row_out, A, seq, nb, X);
+            __syncthreads();
+            return;
+        }
+        __syncthreads();
+    }
+    // the whole score row, exactly
+    const float *__restrict__ row = A.scores + i * A.ld;
+    auto rkey = [row](int64_t j) {
+        const uint32_t u = __float_as_uint(row[j]);
+        return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    };
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (int64_t j = threadIdx.x; j < nb; j += kSelThreads) {
+        const uint32_t k = rkey(j);
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+    }
+    {
+        const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax);
+        if (lane == 0) {
+            X.red[0][wave] = w_mn;
+            X.red[1][wave] = w_mx;
+        }
+        __syncthreads();
+        kmin = X.red[0][0];
+        kmax = X.red[1][0];
+#pragma unroll
+        for (int w = 1; w < kWgWaves; ++w) {
+            kmin = min(kmin, X.red[0][w]);
+            kmax = max(kmax, X.red[1][w]);
+        }
+        __syncthreads();
+    }
+    T = sel_radix(rkey, nb, (uint32_t)K, kmin, kmax, X, need_eq, total_eq);
+    sel_emit(rkey, [](int64_t j) { return (int32_t)j; }, nb, T, need_eq, p_beg, p_end, tab, row_out, A, seq, nb, X);
+    __syncthreads();
+}
+
 // Decode attention of one wave on the matrix cores.  Per 16-token step:
 //  QK: S[t][n] = K[t,:] . q_n for the 16 tokens t (M) and up to 16 query
 //      heads n of the KV head (N; heads >= G are zero columns), four
@@ -732,8 +1075,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 //      gfx950 transposed LDS load (ds_read_b64_tr_b16: lane i of each 16-lane
 //      group gets column i of the four rows its group points at).
 //  Lane l accumulates O^T for head l%16, dims 16m + 4(l/16) + 0..3, m < 8.
-template <int D, bool BIG>
+template <int D, bool BIG, bool SELECT>
 __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) {
+    static_assert(BIG || !SELECT, "the in-kernel selection fills an LDS slot table");
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -785,8 +1129,21 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     }
     // BIG: the whole share (at most kBigTabSlots slots) into this wave's LDS
     // table, block ids translated to pool blocks when paged, -1 past the end.
-    const uint32_t big_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes + wave * kBigTabBytes);
-    if constexpr (BIG) {
+    // SELECT: the workgroup's part [p_beg, p_end) is one table over the four
+    // waves' regions, filled by the selection; each wave reads its share.
+    uint32_t big_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes + wave * kBigTabBytes);
+    if constexpr (SELECT) {
+        const int per = ((int)nsel + A.n_part - 1) / A.n_part;
+        const int p_beg = min(c * per, (int)nsel);
+        const int p_end = min(p_beg + per, (int)nsel);
+        const uint32_t part_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes);
+        if (nb > 0)
+            select_part<D>(A, i, qp.seq, nb, p_beg, p_end, g == 0 && c == 0, part_tab, dyn_lds);
+        else if (g == 0 && c == 0)
+            for (int j = threadIdx.x; j < A.K; j += kSelThreads) A.idx_out[i * (int64_t)A.K + j] = -1;
+        big_tab = part_tab + 4u * (uint32_t)(s_beg - p_beg);
+    }
+    if constexpr (BIG && !SELECT) {
         int32_t v[kBigTabSlots / kWave];
 #pragma unroll
         for (int j = 0; j < kBigTabSlots / kWave; ++j)
@@ -1022,7 +1379,7 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     }
 }
 
-template <int D, bool BIG>
+template <int D, bool BIG, bool SELECT>
 __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(AttnArgs A, int G, LayerPtrs Lp) {
     if (gridDim.y > 1) {
         const int l = blockIdx.y;
@@ -1030,7 +1387,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(Attn
         A.ws_o += l * Lp.ws_stride;
         if (A.ws_ml) A.ws_ml += l * Lp.ws_stride;
     }
-    attn_decode_mfma_body<D, BIG>(A, G);
+    attn_decode_mfma_body<D, BIG, SELECT>(A, G);
 }
 
 // Merge part partials: one wave per (query, head); lane s < n_part reads
@@ -1104,12 +1461,13 @@ constexpr int kDecodeWgPerCu = 2;
 
 int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
 
-template <int D, bool BIG>
+template <int D, bool BIG, bool SELECT = false>
 hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, const LayerPtrs &Lp, hipStream_t st) {
     const size_t lds = (size_t)kWgWaves * (D * kSlotBytes + (BIG ? kBigTabBytes : 0));
-    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D, BIG>, (int)lds);
+    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D, BIG, SELECT>, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, BIG>), grid, dim3(kWgWaves * kWave), lds, st, A, G, Lp);
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, BIG, SELECT>), grid, dim3(kWgWaves * kWave), lds, st, A, G,
+                       Lp);
     return hipGetLastError();
 }
 
@@ -1246,7 +1604,7 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
                        const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
                        hipStream_t st) {
     if (b.total_q == 0) return hipSuccess;
-    AttnArgs A;
+    AttnArgs A{};
     const bool mfma_path = attn_args(a, idx, budget, ratio, b, out, ws, decode, pg, A);
     const int G = a.hq / a.hkv;
     trace("attn total_q=%lld hkv=%d G=%d parts=%d dtype=%d", (long long)b.total_q, a.hkv, G,
@@ -1285,6 +1643,36 @@ hipError_t attn_static_scratch(void **ptr) {
     return hipSuccess;
 }
 
+bool attn_select_supported(const qsa_batch &b, const qsa_attn &a, const qsa_paged_kv *pg) {
+    const uint64_t span_rows = pg ? (uint64_t)pg->num_pages * (uint64_t)pg->page_size : (uint64_t)b.max_kv_len;
+    return a.dtype == QSA_BF16 && span_rows * (uint64_t)a.hkv * kD * 2 < (1ull << 32);
+}
+
+hipError_t launch_attn_select(const qsa_attn &a, int budget, int ratio, const qsa_batch &b, const ListArgs &la,
+                              const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
+                              const qsa_paged_kv *pg, hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    AttnArgs A{};
+    if (!attn_args(a, idx, budget, ratio, b, out, ws, true, pg, A)) return hipErrorNotSupported;
+    A.la = la;
+    A.scores = scores;
+    A.ld = ld;
+    A.idx_out = idx;
+    const int G = a.hq / a.hkv;
+    const dim3 grid((unsigned)(A.total_q * A.hkv * A.n_part));
+    const int D = ring_depth((int64_t)grid.x);
+    trace("attn decode with selection D=%d workgroups=%u parts=%d", D, grid.x, A.n_part);
+    const LayerPtrs none{};
+    hipError_t e = D == 4 ? launch_decode_mfma<4, true, true>(A, G, grid, none, st)
+                          : launch_decode_mfma<2, true, true>(A, G, grid, none, st);
+    if (e != hipSuccess || A.n_part == 1) return e;
+    const int64_t rows = A.total_q * A.hq;
+    dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves));
+    hipLaunchKernelGGL((attn_combine_kernel<true>), cgrid, dim3(kWgWaves * kWave), 0, st, A.ws_o, A.ws_ml, A.n_part,
+                       rows, A.out, none);
+    return hipGetLastError();
+}
+
 size_t attn_layer_stride_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
     return (attn_workspace_bytes(b, a, budget, ratio) + 255) & ~(size_t)255;
 }
@@ -1294,7 +1682,7 @@ hipError_t launch_attn_layers(const qsa_attn *layers, int n_layers, const int32_
                               hipStream_t st) {
     if (b.total_q == 0) return hipSuccess;
     const size_t stride = attn_layer_stride_bytes(b, layers[0], budget, ratio);
-    AttnArgs A;
+    AttnArgs A{};
     const bool mfma_path = attn_args(layers[0], idx, budget, ratio, b, outs[0], ws, true, pg, A);
     const int G = layers[0].hq / layers[0].hkv;
     if (!mfma_path || n_layers == 1) {   // one launch per layer

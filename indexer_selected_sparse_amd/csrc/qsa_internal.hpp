@@ -60,6 +60,18 @@ hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ra
                        const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
                        hipStream_t st);
 
+// Decode attention that selects its own blocks from the scorer's candidate
+// lists (qsa_decode_step): bf16 K/V on the matrix-core path only.
+bool attn_select_supported(const qsa_batch &b, const qsa_attn &a, const qsa_paged_kv *pg);
+hipError_t launch_attn_select(const qsa_attn &a, int budget, int ratio, const qsa_batch &b, const ListArgs &la,
+                              const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
+                              const qsa_paged_kv *pg, hipStream_t st);
+// The lists of a score + select call (workspace carve-up shared by the calls
+// that take them), and the list finish alone.
+ListArgs list_args(const qsa_batch &b, int budget, int ratio, void *ws);
+hipError_t launch_topk_from_lists(const float *scores, int64_t ld, int budget, int ratio, const qsa_batch &b,
+                                  int32_t *idx, const ListArgs &la, hipStream_t st);
+
 // Decode attention with the split partials in a static device array (no
 // caller workspace): its size, and its address on the current device
 // (resolved with hipGetSymbolAddress on the first call per device).

@@ -1528,15 +1528,7 @@ size_t score_topk_workspace_bytes(const qsa_batch &b, int budget, int ratio) {
     return ((keys + 255) & ~(size_t)255) + ((cuts + 255) & ~(size_t)255) + locs + 256;
 }
 
-hipError_t launch_score_topk(const qsa_indexer &ix, int budget, int ratio, const qsa_batch &b, float *scores,
-                             int64_t ld, int32_t *idx, void *ws, const qsa_paged_kv *pg, hipStream_t st) {
-    if (b.total_q == 0) return hipSuccess;
-    const int K = budget / ratio;
-    if (!score_topk_uses_lists(b)) {
-        hipError_t e = launch_score_canonical(ix, ratio, b, scores, ld, pg, st, ListArgs{});
-        if (e != hipSuccess) return e;
-        return launch_topk(scores, ld, nullptr, budget, ratio, b, idx, K, ws, st);
-    }
+ListArgs list_args(const qsa_batch &b, int budget, int ratio, void *ws) {
     const int64_t nch = list_chunks(b, ratio);
     const size_t rows = (size_t)b.total_q;
     uint8_t *base = static_cast<uint8_t *>(ws);
@@ -1548,19 +1540,40 @@ hipError_t launch_score_topk(const qsa_indexer &ix, int budget, int ratio, const
     la.loc = base + keys_bytes + cuts_bytes;
     la.stride = nch * kListChunk;
     la.cstride = nch;
-    la.K = K;
-    hipError_t e = launch_score_canonical(ix, ratio, b, scores, ld, pg, st, la);
-    if (e != hipSuccess) return e;
+    la.K = budget / ratio;
+    return la;
+}
+
+hipError_t launch_topk_from_lists(const float *scores, int64_t ld, int budget, int ratio, const qsa_batch &b,
+                                  int32_t *idx, const ListArgs &la, hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    const int K = budget / ratio;
+    const int64_t nch = list_chunks(b, ratio);
     const int64_t bound = nch * kListChunk;
     const int cap = (int)(bound < kListMaxEntries ? bound : kListMaxEntries);
     const size_t lds = (size_t)cap * 5;
-    e = enable_dyn_lds((const void *)topk_lists_kernel, (int)lds);
+    hipError_t e = enable_dyn_lds((const void *)topk_lists_kernel, (int)lds);
     if (e != hipSuccess) return e;
     const int log2r = __builtin_ctz((unsigned)ratio);
     trace("topk lists rows=%lld K=%d chunks=%lld cap=%d", (long long)b.total_q, K, (long long)nch, cap);
     hipLaunchKernelGGL(topk_lists_kernel, dim3((unsigned)b.total_q), dim3(kTopkThreads), lds, st, scores, ld,
                        b.kv_offsets, b.q_offsets, b.num_seqs, log2r, K, idx, K, la, cap);
     return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const qsa_indexer &ix, int budget, int ratio, const qsa_batch &b, float *scores,
+                             int64_t ld, int32_t *idx, void *ws, const qsa_paged_kv *pg, hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    const int K = budget / ratio;
+    if (!score_topk_uses_lists(b)) {
+        hipError_t e = launch_score_canonical(ix, ratio, b, scores, ld, pg, st, ListArgs{});
+        if (e != hipSuccess) return e;
+        return launch_topk(scores, ld, nullptr, budget, ratio, b, idx, K, ws, st);
+    }
+    const ListArgs la = list_args(b, budget, ratio, ws);
+    hipError_t e = launch_score_canonical(ix, ratio, b, scores, ld, pg, st, la);
+    if (e != hipSuccess) return e;
+    return launch_topk_from_lists(scores, ld, budget, ratio, b, idx, la, st);
 }
 
 static int64_t norm_chunks(const qsa_batch &b, int ratio) {

@@ -15,7 +15,8 @@ import numpy as np
 
 from . import (INGEST_OK, MAX_LAYERS, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA,
                Batch, KeyRing, Paging, attn_layers_workspace_size, attn_workspace_size, compress_keys,
-               index_score, index_score_topk, ingest, ingest_index_score, pool_scores, score_topk_workspace_size,
+               decode_step, decode_step_workspace_size, index_score, index_score_lists, index_score_topk, ingest,
+               ingest_index_score, pool_scores, score_topk_workspace_size, sparse_attn_decode_lists,
                sparse_attn_decode, sparse_attn_decode_layers, sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
@@ -74,6 +75,8 @@ class DeviceProblem:
     fuse_ingest: bool = True               # append + canonical scores in one launch when possible
     sel_ws: Optional[torch.Tensor] = None  # qsa_index_score_topk workspace
     fuse_select: bool = True               # canonical scores and their top-k in one call when possible
+    step_ws: Optional[torch.Tensor] = None # qsa_decode_step workspace
+    fuse_step: bool = True                 # decode: scores, selection and attention as qsa_decode_step
 
     @property
     def blocks_per_query(self) -> int:
@@ -131,6 +134,29 @@ class DeviceProblem:
         index_score_topk(self.q_idx, self.w, self.kc, self.kc_scale, self.budget, self.ratio, self.batch,
                          self.scores, self.idx, self.sel_ws, stream=stream, paging=self.paging)
 
+    def step_fusable(self, mode: int = QSA_SCORE_CANONICAL) -> bool:
+        """Whether a decode step can run as qsa_decode_step (decode batch,
+        canonical scores on compressed keys, no window, no fused append)."""
+        return (self.decode and self.fuse_step and self.select_fusable(mode) and not self.ingest_fusable(mode)
+                and self.ing is None and self.step_ws is not None)
+
+    def decode_step(self, stream=None) -> None:
+        """qsa_decode_step: scores, selection and sparse attention."""
+        decode_step(self.q_idx, self.w, self.kc, self.kc_scale, self.q, self.K, self.V, self.softmax_scale,
+                    self.budget, self.ratio, self.batch, self.scores, self.idx, self.out, self.step_ws,
+                    stream=stream, paging=self.paging)
+
+    def score_lists(self, stream=None) -> None:
+        """qsa_index_score_lists: the scorer half of decode_step()."""
+        index_score_lists(self.q_idx, self.w, self.kc, self.kc_scale, self.q, self.K, self.V, self.softmax_scale,
+                          self.budget, self.ratio, self.batch, self.scores, self.step_ws, stream=stream,
+                          paging=self.paging)
+
+    def attend_lists(self, stream=None) -> None:
+        """qsa_sparse_attn_decode_lists: the selection + attention half of decode_step()."""
+        sparse_attn_decode_lists(self.q, self.K, self.V, self.softmax_scale, self.budget, self.ratio, self.batch,
+                                 self.scores, self.idx, self.out, self.step_ws, stream=stream, paging=self.paging)
+
     def topk(self, certified: bool = False, stream=None) -> None:
         recheck = (self.q_idx, self.w, self.kc, self.kc_scale) if certified else None
         topk_blocks(self.scores, self.budget, self.ratio, self.batch, self.idx, recheck=recheck,
@@ -145,6 +171,9 @@ class DeviceProblem:
     def step(self, mfma: bool = False, stream=None) -> None:
         """One pass of the hot path: [ingest ->] score -> top-k -> sparse attention."""
         mode = QSA_SCORE_MFMA if mfma else QSA_SCORE_CANONICAL
+        if self.step_fusable(mode):
+            self.decode_step(stream=stream)
+            return
         if self.ingest_fusable(mode):
             self.ingest_score(stream=stream)
             self.topk(certified=mfma, stream=stream)
@@ -191,6 +220,9 @@ def upload(wl, device: str = "cuda", decode: Optional[bool] = None, mfma_ws: boo
     sws = score_topk_workspace_size(batch, sp.budget, sp.ratio)
     if sws:
         dp.sel_ws = torch.empty(sws, dtype=torch.uint8, device=device)
+    if decode:
+        dws = decode_step_workspace_size(q, K, V, sp.softmax_scale, sp.budget, sp.ratio, batch)
+        dp.step_ws = torch.empty(max(dws, 1), dtype=torch.uint8, device=device)
     if mfma_ws:
         tws = topk_workspace_size(batch, sp.budget, sp.ratio,
                                   (dp.q_idx, dp.w, dp.kc, dp.kc_scale))

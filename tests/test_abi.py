@@ -24,7 +24,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)

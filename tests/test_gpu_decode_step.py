@@ -1,0 +1,170 @@
+"""qsa_decode_step (scores, selection inside the attention kernel, attention)
+against the oracle and against the separate calls.
+
+Scores and idx must match the oracle bit for bit and the outputs lie within
+the stated tolerance; moreover idx and the outputs must equal, bit for bit,
+qsa_index_score_topk followed by qsa_sparse_attn_decode on the same batch
+(same kernels, same split of each query's blocks), and the two halves
+(qsa_index_score_lists, qsa_sparse_attn_decode_lists) must equal the one call.
+The cases reach every way the attention workgroups select: from the lists,
+from the whole score row when the certificate fails (clustered winners,
+all-equal scores) or the lists exceed the workgroup's LDS (K = 2048 on long
+rows), the dense regime and rows with no complete block, paged caches, every
+key format, and the batches that run the separate kernels instead (fp32 K/V,
+more than 256 queries).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_sparse_amd as Q
+import oracle
+import qsa_workloads as W
+from indexer_selected_sparse_amd import pipeline
+from tests.parity import check_idx, check_out, check_scores, gpu_available
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _bits(t):
+    t = t.detach().contiguous()
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16,) else t.view(torch.int32)
+
+
+def _run(wl, paged=0, oracle_check=True):
+    dp = pipeline.upload(wl, "cuda", decode=True)
+    dp.compress()
+    if paged:
+        dp = pipeline.page(dp, wl.lens, paged, seed=5, extra_pages=2)
+    dp.scores.fill_(float("nan"))
+    dp.idx.fill_(-9)
+    dp.out.zero_()
+    dp.decode_step()
+    torch.cuda.synchronize()
+    got = {"scores": dp.scores.cpu().numpy(), "idx": dp.idx.cpu().numpy(),
+           "out": dp.out.float().cpu().numpy().astype(np.float64)}
+    fused_out = dp.out.clone()
+    # the separate calls on the same inputs
+    sc2 = torch.full_like(dp.scores, float("nan"))
+    idx2 = torch.full_like(dp.idx, -9)
+    out2 = torch.zeros_like(dp.out)
+    Q.index_score_topk(dp.q_idx, dp.w, dp.kc, dp.kc_scale, dp.budget, dp.ratio, dp.batch, sc2, idx2, dp.sel_ws,
+                       paging=dp.paging)
+    Q.sparse_attn_decode(dp.q, dp.K, dp.V, dp.softmax_scale, idx2, dp.budget, dp.ratio, dp.batch, out2, dp.attn_ws,
+                         paging=dp.paging)
+    # the two halves
+    sc3 = torch.full_like(dp.scores, float("nan"))
+    idx3 = torch.full_like(dp.idx, -9)
+    out3 = torch.zeros_like(dp.out)
+    Q.index_score_lists(dp.q_idx, dp.w, dp.kc, dp.kc_scale, dp.q, dp.K, dp.V, dp.softmax_scale, dp.budget,
+                        dp.ratio, dp.batch, sc3, dp.step_ws, paging=dp.paging)
+    Q.sparse_attn_decode_lists(dp.q, dp.K, dp.V, dp.softmax_scale, dp.budget, dp.ratio, dp.batch, sc3, idx3, out3,
+                               dp.step_ws, paging=dp.paging)
+    torch.cuda.synchronize()
+    assert torch.equal(dp.idx, idx2), "decode step and separate calls select differently"
+    assert torch.equal(_bits(fused_out), _bits(out2)), "decode step output differs from the separate calls"
+    assert torch.equal(dp.idx, idx3) and torch.equal(_bits(fused_out), _bits(out3)), "halves differ"
+    if oracle_check:
+        q = np.arange(wl.total_q)
+        ref = oracle.run_workload(wl, want_scores=True)
+        check_scores(wl, got, ref, q)
+        check_idx(got, ref, q)
+        worst = check_out(wl, got, ref, q)
+        _print(f"[decode_step] {wl.spec.name} lens={list(wl.lens)[:4]}...: oracle ok, worst err/limit {worst:.3f}")
+    return dp
+
+
+def test_batched_decode_full_size():
+    _run(W.make(W.BATCHED_DECODE))
+
+
+def test_long_decode_full_size():
+    _run(W.make(W.LONG_DECODE))
+
+
+@pytest.mark.parametrize("kc_dtype", ["bf16", "e4m3", "fp4"])
+def test_key_formats_and_ragged_rows(kc_dtype):
+    sp = dataclasses.replace(W.BATCHED_DECODE, kc_dtype=kc_dtype, budget=512)
+    _run(W.make(sp, lens=[9001, 2051, 2, 530, 518, 4099, 20002, 3], seed=601))
+
+
+def test_paged_caches():
+    sp = dataclasses.replace(W.LONG_DECODE, hq=16, hkv=2, budget=1024)
+    _run(W.make(sp, lens=[20000, 7001, 1024 * 4 + 2], seed=602), paged=128)
+
+
+def test_clustered_winners_select_from_the_row():
+    sp = W.BATCHED_DECODE
+    wl = W.make(sp, lens=[20000, 9000, 30001, 4000], seed=603)
+    a = int(wl.kv_offsets[0]) + 4 * 3000
+    wl.k_idx[a:a + 4 * 300] *= 4.0
+    b = int(wl.kv_offsets[2]) + 4 * 7000
+    wl.k_idx[b:b + 4 * 700] *= 4.0
+    _run(wl)
+
+
+def test_all_equal_scores_take_the_lowest_blocks():
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=1024)
+    wl = W.make(sp, lens=[6000, 3001, 40000], seed=604)
+    wl.q_idx.zero_()
+    dp = _run(wl)
+    assert np.array_equal(dp.idx.cpu().numpy()[0], np.arange(256))
+
+
+def test_duplicated_keys_and_negative_weights():
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=512)
+    lens = [4 * 2 * 1000 + 1, 4 * 2 * 3000, 4 * 2 * 700 + 2]
+    wl = W.make(sp, lens=lens, seed=605)
+    for s, n in enumerate(lens):
+        a = int(wl.kv_offsets[s])
+        half = 4 * (n // 8)
+        wl.k_idx[a + half:a + 2 * half] = wl.k_idx[a:a + half]
+    wl.w[:, 1::2] *= -1.0
+    _run(wl)
+
+
+def test_k2048_long_rows_exceed_the_lds_lists():
+    sp = dataclasses.replace(W.LONG_DECODE, hq=8, hkv=1, budget=8192)
+    _run(W.make(sp, lens=[131072 + 3, 60000, 8196, 8195, 100], seed=606))
+
+
+def test_fp32_and_large_batches_run_the_separate_kernels():
+    _run(W.make(W.TINY_DECODE, lens=[4096, 1500, 3], seed=607))
+    sp = dataclasses.replace(W.BATCHED_DECODE, hq=8, hkv=2, budget=256)
+    rng = np.random.default_rng(608)
+    lens = [int(x) for x in rng.integers(1000, 3000, 300)]
+    _run(W.make(sp, lens=lens, seed=608), oracle_check=False)
+
+
+def test_graph_replays_match_eager():
+    wl = W.make(W.BATCHED_DECODE, lens=[8200 + 1711 * j for j in range(12)], seed=609)
+    dp = pipeline.upload(wl, "cuda", decode=True)
+    dp.compress()
+    dp.decode_step()
+    torch.cuda.synchronize()
+    eager = (dp.idx.clone(), dp.out.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.decode_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dp.decode_step()
+    for rep in range(4):
+        dp.idx.fill_(-5)
+        dp.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.idx, eager[0]), f"replay {rep}: idx"
+        assert torch.equal(_bits(dp.out), _bits(eager[1])), f"replay {rep}: out"
+        dp.decode_step()
+        torch.cuda.synchronize()
