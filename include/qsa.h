@@ -403,7 +403,8 @@ qsa_status qsa_index_score_topk(const qsa_indexer *ix, int32_t budget, int32_t r
  *  idx:    device int32 [total_q, budget/ratio] (written).
  *  out:    device [total_q, hq, d] (dtype of q).
  *  ws:     device workspace of at least qsa_decode_step_workspace_size()
- *          bytes; no initialisation, no state between calls.
+ *          bytes, 16-byte aligned (QSA_ERR_INVALID_ARGUMENT otherwise); no
+ *          initialisation, no state between calls.
  *  pg:     NULL, or the paging of kc, kc_scale, K and V.
  * Errors: those of qsa_index_score_topk and qsa_sparse_attn_decode. */
 size_t qsa_decode_step_workspace_size(const qsa_batch *b, const qsa_attn *a, int32_t budget, int32_t ratio);

@@ -456,6 +456,9 @@ static qsa_status decode_step_check(const qsa_indexer *ix, const qsa_attn *a, in
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(QSA_ERR_WORKSPACE, "decode step workspace of %zu bytes is smaller than the %zu required "
                     "(qsa_decode_step_workspace_size)", ws == nullptr ? (size_t)0 : ws_bytes, need);
+    if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 15u) != 0)
+        return fail(QSA_ERR_INVALID_ARGUMENT, "decode step workspace %p is not 16-byte aligned (the candidate "
+                    "lists are read 16 bytes at a time)", ws);
     return ok();
 }
 

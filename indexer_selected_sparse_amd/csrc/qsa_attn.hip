@@ -741,7 +741,9 @@ struct SelScratch {
     uint32_t hist[kSelBins];
     uint32_t red[4][kWgWaves];
     uint32_t s[8];
-    uint32_t bc[kSelBinCand];
+    uint32_t bcw[kWgWaves][kSelBinCand];   // the threshold bin's keys, per wave
+    uint32_t bcn[kWgWaves];
+    uint32_t tot[4][kWgWaves];
 };
 constexpr int kSelScratchBytes = (int)((sizeof(SelScratch) + 255) & ~(size_t)255);
 
@@ -817,13 +819,11 @@ __device__ __forceinline__ uint32_t sel_radix(const KeyF &key, int64_t n, uint32
 
 // Ordered output of a selection over n entries in ascending block order:
 // thread t owns entries [t*E, t*E + E); an entry is selected when its key is
-// > T, or == T among the first need_eq such entries.  Selected positions in
-// [p_beg, p_end) go to the part table (physical block ids when paged); with
-// `row_out`, every position goes to the idx row.
+// > T, or == T among the first need_eq such entries.  Selected position p
+// gets the entry's logical block id in LDS table slot p.
 template <typename KeyF, typename BlkF>
 __device__ __forceinline__ void sel_emit(const KeyF &key, const BlkF &blk_of, int64_t n, uint32_t T, uint32_t need_eq,
-                         int p_beg, int p_end, uint32_t tab, int32_t *row_out, const AttnArgs &A, int seq,
-                         int64_t nb, SelScratch &X) {
+                                         uint32_t tab, SelScratch &X) {
     const int64_t E = (n + kSelThreads - 1) / kSelThreads;
     const int64_t j0 = (int64_t)threadIdx.x * E;
     const int64_t j1 = j0 + E < n ? j0 + E : n;
@@ -846,32 +846,280 @@ __device__ __forceinline__ void sel_emit(const KeyF &key, const BlkF &blk_of, in
             ++tie;
         }
         if (take) {
-            const int32_t b = blk_of(j);
-            if (row_out) row_out[pos] = b;
-            if ((int)pos >= p_beg && (int)pos < p_end) {
-                const int32_t pb = A.pm.table ? slot_phys(b, A.pm, seq, nb, A.log2r) : b;
-                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)(pos - p_beg)) = pb;
-            }
+            *(lds_i32_t *)(uintptr_t)(tab + 4u * pos) = blk_of(j);
             ++pos;
         }
     }
 }
 
-// Fill the part table for positions [p_beg, p_end) of query i's selection
-// (nb > 0 visible blocks) and, for the designated workgroup, the idx row.
+// Lists of at most kSelRegEntries entries (every row of at most 32768
+// blocks at K <= 512) are selected from registers.  Thread t holds the
+// entries 4g .. 4g+3 for g = t + 256u, u < kSelRegGroups, so for each u the
+// four waves hold 1024 consecutive entries, wave after wave and lane after
+// lane: ascending order is (u, wave, lane, e).  The first kSelRegEntries
+// entries and kSelRegCuts * 256 cutoffs of the row's lists are requested at
+// the kernel's start, before the query's length is known (they lie inside
+// the row's region of the workspace whatever the length; entries past the
+// row's own lists are masked once it is known).
+constexpr int kSelRegGroups = 4;
+constexpr int kSelRegEntries = 4 * kSelRegGroups * kSelThreads;     // 4096
+constexpr int kSelRegCuts = 2;                                      // 512 chunks
+static_assert(kSelRegEntries / 8 <= kSelRegCuts * kSelThreads,
+              "a list of kSelRegEntries entries has at most that many chunks (>= 8 entries each)");
+struct SelPre {
+    uint4 k[kSelRegGroups];
+    uint32_t l[kSelRegGroups];
+    uint32_t c[kSelRegCuts];
+};
+
+__device__ __forceinline__ void sel_prefetch(const AttnArgs &A, int64_t i, SelPre &pf) {
+    const uint4 *__restrict__ gk = reinterpret_cast<const uint4 *>(A.la.keys + i * A.la.stride);
+    const uint32_t *__restrict__ gl = reinterpret_cast<const uint32_t *>(A.la.loc + i * A.la.stride);
+    const uint32_t *__restrict__ gc = A.la.cut + i * A.la.cstride;
+    const int s4 = (int)(A.la.stride / 4 < kSelRegEntries / 4 ? A.la.stride / 4 : kSelRegEntries / 4);
+    const int nc = (int)(A.la.cstride < kSelRegCuts * kSelThreads ? A.la.cstride : kSelRegCuts * kSelThreads);
+#pragma unroll
+    for (int u = 0; u < kSelRegGroups; ++u) {
+        const int g = (int)threadIdx.x + u * kSelThreads;
+        pf.k[u] = g < s4 ? gk[g] : make_uint4(0u, 0u, 0u, 0u);
+        pf.l[u] = g < s4 ? gl[g] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSelRegCuts; ++u) {
+        const int cc = (int)threadIdx.x + u * kSelThreads;
+        pf.c[u] = cc < nc ? gc[cc] : 0u;
+    }
+}
+
+__device__ __forceinline__ uint32_t &u4_at(uint4 &v, int e) {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// The selection from the registers (M = nch * kk <= kSelRegEntries listed
+// entries), written to LDS table slots 0 .. K-1 as logical block ids.
+// Returns false, after a barrier, when it cannot decide the row (the
+// certificate fails, or more than 64 keys share the threshold's bin): the
+// caller then selects from the whole row.  Five barriers: the list
+// statistics, the histogram, the threshold bin's keys, the emit counts, the
+// finished table.
+__device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int nch, int M, uint32_t tab,
+                                                 SelScratch &X, SelPre &pf) {
+    const int K = A.K;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u, mcut = 0u;
+#pragma unroll
+    for (int u = 0; u < kSelRegGroups; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * ((int)threadIdx.x + u * kSelThreads) + e;
+            uint32_t &key = u4_at(pf.k[u], e);
+            key = j < M ? key : 0u;
+            if (key != 0u) {
+                kmin = min(kmin, key);
+                kmax = max(kmax, key);
+                ++nreal;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kSelRegCuts; ++u)
+        if ((int)threadIdx.x + u * kSelThreads < nch) mcut = max(mcut, pf.c[u]);
+    for (int b = threadIdx.x; b < kSelBins; b += kSelThreads) X.hist[b] = 0u;
+    {
+        const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax), w_mc = wave_max_u32(mcut);
+        const uint32_t w_n = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nreal), kWave - 1);
+        if (lane == 0) {
+            X.red[0][wave] = w_mn;
+            X.red[1][wave] = w_mx;
+            X.red[2][wave] = w_n;
+            X.red[3][wave] = w_mc;
+        }
+    }
+    __syncthreads();                                                      // 1
+    kmin = X.red[0][0];
+    kmax = X.red[1][0];
+    nreal = X.red[2][0];
+    mcut = X.red[3][0];
+#pragma unroll
+    for (int w = 1; w < kWgWaves; ++w) {
+        kmin = min(kmin, X.red[0][w]);
+        kmax = max(kmax, X.red[1][w]);
+        nreal += X.red[2][w];
+        mcut = max(mcut, X.red[3][w]);
+    }
+    if (!(nreal >= (uint32_t)K && mcut < kmax)) {     // cannot certify (uniform)
+        __syncthreads();
+        return false;
+    }
+    uint32_t T, need_eq;
+    if (kmin == kmax) {
+        T = kmin;
+        need_eq = (uint32_t)K;
+    } else {
+        // A certified threshold exceeds every cutoff, so only keys from
+        // lo = max(kmin, mcut + 1) up can be it (a whole short chunk can list
+        // keys far below the rest, which would crowd coarse bins).  1024 bins
+        // linear in the key: bin = (key - lo) >> sh <= 1023.
+        const uint32_t lo = max(kmin, mcut + 1u);
+        const uint32_t span = kmax - lo;
+        const int sh = span < (uint32_t)kSelBins ? 0 : (32 - __builtin_clz(span)) - 10;
+#pragma unroll
+        for (int u = 0; u < kSelRegGroups; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t key = u4_at(pf.k[u], e);
+                if (key >= lo) atomicAdd(&X.hist[(key - lo) >> sh], 1u);
+            }
+        }
+        __syncthreads();                                                  // 2
+        // every wave finds the bin of the K-th largest: lane l owns the 16
+        // bins 1023 - 16 l down to 1008 - 16 l (the top bins first)
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(X.hist);
+        uint32_t hb[16], own = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = h4[kSelBins / 4 - 1 - 4 * lane - q];
+            hb[4 * q + 0] = v.w;
+            hb[4 * q + 1] = v.z;
+            hb[4 * q + 2] = v.y;
+            hb[4 * q + 3] = v.x;
+            own += (v.x + v.y) + (v.z + v.w);
+        }
+        const uint32_t incl = wave_incl_scan(own);
+        const uint32_t above = incl - own;
+        const bool hit = above < (uint32_t)K && (uint32_t)K <= incl;
+        const uint64_t hm = __ballot(hit);
+        if (hm == 0u) {                               // fewer than K keys above the cutoffs (uniform)
+            __syncthreads();
+            return false;
+        }
+        const int hl = (int)__builtin_ctzll(hm);
+        const int top = kSelBins - 1 - 16 * lane;
+        uint32_t tb_l = 0u, need_l = 0u, nbin_l = 0u, a = above;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (a < (uint32_t)K && (uint32_t)K <= a + hb[e]) {
+                tb_l = (uint32_t)(top - e);
+                need_l = (uint32_t)K - a;
+                nbin_l = hb[e];
+            }
+            a += hb[e];
+        }
+        const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)tb_l, hl);
+        const uint32_t need = (uint32_t)__builtin_amdgcn_readlane((int)need_l, hl);
+        const uint32_t nbin = (uint32_t)__builtin_amdgcn_readlane((int)nbin_l, hl);
+        if (nbin > (uint32_t)kSelBinCand) {           // crowded bin: the whole row decides (uniform)
+            __syncthreads();
+            return false;
+        }
+        // the bin's keys, compacted per wave in ascending order (ballots)
+        uint32_t wcnt = 0u;
+#pragma unroll
+        for (int u = 0; u < kSelRegGroups; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t key = u4_at(pf.k[u], e);
+                const bool in = key >= lo && ((key - lo) >> sh) == tb;
+                const uint64_t m = __ballot(in);
+                if (in) X.bcw[wave][wcnt + list_lanes_below(m)] = key;
+                wcnt += (uint32_t)__builtin_popcountll(m);
+            }
+        }
+        if (lane == 0) X.bcn[wave] = wcnt;
+        __syncthreads();                                                  // 3
+        // every wave ranks them: lane l < nbin holds key l of the union
+        const uint32_t o1 = X.bcn[0], o2 = o1 + X.bcn[1], o3 = o2 + X.bcn[2];
+        const uint32_t ul = (uint32_t)lane;
+        const int w = ul < o1 ? 0 : ul < o2 ? 1 : ul < o3 ? 2 : 3;
+        const uint32_t off = w == 0 ? 0u : w == 1 ? o1 : w == 2 ? o2 : o3;
+        const bool mine = ul < nbin;
+        const uint32_t key = mine ? X.bcw[w][ul - off] : 0u;
+        uint32_t gt = 0u, eq = 0u;
+        for (int j = 0; j < (int)nbin; ++j) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+            gt += o > key ? 1u : 0u;
+            eq += o == key ? 1u : 0u;
+        }
+        const bool h2 = mine && gt < need && need <= gt + eq;
+        const int l2 = (int)__builtin_ctzll(__ballot(h2));
+        T = (uint32_t)__builtin_amdgcn_readlane((int)key, l2);
+        need_eq = (uint32_t)__builtin_amdgcn_readlane((int)(need - gt), l2);
+    }
+    if (!(T != 0u && mcut < T)) {
+        __syncthreads();
+        return false;
+    }
+    // ordered emit: per (u, wave) the packed counts (gt << 16 | eq) of the
+    // entries before each lane, and the four waves' totals through LDS
+    uint32_t pre[kSelRegGroups];
+#pragma unroll
+    for (int u = 0; u < kSelRegGroups; ++u) {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t key = u4_at(pf.k[u], e);
+            c += key > T ? 0x10000u : 0u;
+            c += key == T ? 1u : 0u;
+        }
+        const uint32_t incl = wave_incl_scan(c);
+        pre[u] = incl - c;
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+        if (lane == 0) X.tot[u][wave] = tot;
+    }
+    __syncthreads();                                                      // 4
+    // chunk of entry j: j / kk by a multiply (j < 2^12, 8 <= kk <= 64: the
+    // error j * (magic - 2^20 / kk) / 2^20 < 2^-8 stays below 1 / kk)
+    const uint32_t magic = (1u << 20) / (uint32_t)kk + 1u;
+    uint32_t base = 0u;
+#pragma unroll
+    for (int u = 0; u < kSelRegGroups; ++u) {
+        uint32_t b = base;
+#pragma unroll
+        for (int w = 0; w < kWgWaves; ++w) {
+            const uint32_t t = X.tot[u][w];
+            b += w < wave ? t : 0u;
+            base += t;
+        }
+        b += pre[u];
+        uint32_t gb = b >> 16, eb = b & 0xffffu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t key = u4_at(pf.k[u], e);
+            const uint32_t isgt = key > T ? 1u : 0u, iseq = key == T ? 1u : 0u;
+            const bool take = isgt != 0u || (iseq != 0u && eb < need_eq);
+            const uint32_t pos = gb + (isgt != 0u ? min(eb, need_eq) : eb);
+            gb += isgt;
+            eb += iseq;
+            const uint32_t j = 4u * (threadIdx.x + (uint32_t)(u * kSelThreads)) + (uint32_t)e;
+            const int32_t blk = (int32_t)(((j * magic) >> 20) * kListChunk + ((pf.l[u] >> (8 * e)) & 0xffu));
+            if (take) *(lds_i32_t *)(uintptr_t)(tab + 4u * pos) = blk;
+        }
+    }
+    (void)nch;
+    __syncthreads();                                                      // 5
+    return true;
+}
+
+// Fill LDS table slots [p_beg, p_end) with query i's selected block ids
+// (physical when paged; nb > 0 visible blocks) and, for the designated
+// workgroup, write the idx row.  The selection is built as logical ids in
+// slots 0 .. K-1; a last pass copies the row out and translates the part.
+// `q_in_ring`: the query rows' loads into the ring's last slots are in
+// flight; a path that uses the whole ring waits for them and clears it.
 template <int D>
 __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t nb, int p_beg, int p_end,
-                            bool designated, uint32_t tab, uint8_t *ring_lds) {
+                                            bool designated, uint32_t tab, uint8_t *ring_lds, SelPre &pf,
+                                            bool &q_in_ring) {
     SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
     const int K = A.K;
     int32_t *row_out = designated ? A.idx_out + i * (int64_t)K : nullptr;
     if (nb <= K) {                                           // dense regime: identity
         for (int j = threadIdx.x; j < K; j += kSelThreads) {
-            if (row_out) row_out[j] = j < nb ? j : -1;
-            if (j >= p_beg && j < p_end) {
-                const int32_t pb = A.pm.table ? slot_phys(j, A.pm, seq, nb, A.log2r) : j;
-                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)(j - p_beg)) = pb;
-            }
+            const int32_t v = j < nb ? j : -1;
+            if (row_out) row_out[j] = v;
+            if (j >= p_beg && j < p_end)
+                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)j) =
+                    A.pm.table ? slot_phys(v, A.pm, seq, nb, A.log2r) : v;
         }
         __syncthreads();
         return;
@@ -880,12 +1128,20 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
     const int kk = list_len(nb, K);
     const int nch = (int)((nb + kListChunk - 1) / kListChunk);
     const int M = nch * kk;
-    constexpr int cap = (kWgWaves * D * kSlotBytes - kSelScratchBytes) / 5;
+    constexpr int cap = ((kWgWaves * D * kSlotBytes - kSelScratchBytes) / 5) & ~3;
+    static_assert(kSelScratchBytes <= kSlotBytes, "the selection scratch stays clear of the query rows' slots");
     uint32_t *keys = reinterpret_cast<uint32_t *>(ring_lds + kSelScratchBytes);
     uint8_t *locs = reinterpret_cast<uint8_t *>(keys + cap);
     uint32_t T = 0, need_eq = 0, total_eq = 0;
-    bool certified = false;
-    if (M <= cap) {
+    bool done = false;
+    if (M <= kSelRegEntries) {
+        done = select_part_regs(A, kk, nch, M, tab, X, pf);
+    } else if (M <= cap) {
+        if (q_in_ring) {                                      // the lists overwrite the whole ring
+            wait_vmcnt<0>();                                  // this wave's query loads landed,
+            __syncthreads();                                  // and every other wave's
+            q_in_ring = false;
+        }
         const uint32_t *__restrict__ gk = A.la.keys + i * A.la.stride;
         const uint8_t *__restrict__ gl = A.la.loc + i * A.la.stride;
         const uint32_t *__restrict__ gc = A.la.cut + i * A.la.cstride;
@@ -938,124 +1194,98 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
             __syncthreads();                                 // X.red is reused below
         }
         if (nreal >= (uint32_t)K && mcut < kmax) {
-            bool found = false;
-            const float vmin = sel_key_value(kmin), vmax = sel_key_value(kmax);
-            const float scale = (float)kSelBins / (vmax - vmin);
-            if (kmin == kmax) {
-                T = kmin;
-                need_eq = (uint32_t)K;
-                total_eq = nreal;
-                found = true;
-            } else if (scale < 3.0e38f) {
-                auto bin_of = [&](uint32_t key) {
-                    return min(kSelBins - 1, (int)((sel_key_value(key) - vmin) * scale));
-                };
-                for (int j = threadIdx.x; j < M; j += kSelThreads) {
-                    const uint32_t key = keys[j];
-                    if (key != 0u) atomicAdd(&X.hist[bin_of(key)], 1u);
-                }
-                if (threadIdx.x == 0) X.s[2] = 0u;
-                __syncthreads();
-                // thread t owns bins 1023-4t-3 .. 1023-4t (descending)
-                uint32_t hb[4], own = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hb[e] = X.hist[kSelBins - 1 - 4 * (int)threadIdx.x - e];
-                    own += hb[e];
-                }
-                uint32_t tot;
-                uint32_t above = sel_scan(own, X, 0, tot);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (above < (uint32_t)K && (uint32_t)K <= above + hb[e]) {
-                        X.s[0] = (uint32_t)(kSelBins - 1 - 4 * (int)threadIdx.x - e);
-                        X.s[1] = above;
-                        X.s[3] = hb[e];
-                    }
-                    above += hb[e];
-                }
-                __syncthreads();
-                const int tb = (int)X.s[0];
-                const uint32_t need = (uint32_t)K - X.s[1];
-                const uint32_t nbin = X.s[3];
-                if (nbin <= (uint32_t)kSelBinCand) {
-                    for (int j = threadIdx.x; j < M; j += kSelThreads) {
-                        const uint32_t key = keys[j];
-                        if (key != 0u && bin_of(key) == tb) X.bc[atomicAdd(&X.s[2], 1u)] = key;
-                    }
-                    __syncthreads();
-                    if (wave == 0) {
-                        const bool mine = lane < (int)nbin;
-                        const uint32_t key = mine ? X.bc[lane] : 0u;
-                        uint32_t gt = 0, eq = 0;
-                        for (int j = 0; j < (int)nbin; ++j) {
-                            const uint32_t o = X.bc[j];
-                            gt += o > key ? 1u : 0u;
-                            eq += o == key ? 1u : 0u;
-                        }
-                        const bool hit = mine && gt < need && need <= gt + eq;
-                        const uint64_t m = __ballot(hit);
-                        if (hit && lane == (int)__builtin_ctzll(m)) {
-                            X.s[4] = key;
-                            X.s[5] = need - gt;
-                            X.s[6] = eq;
-                        }
-                    }
-                    __syncthreads();
-                    T = X.s[4];
-                    need_eq = X.s[5];
-                    total_eq = X.s[6];
-                    found = true;
-                }
+            const uint32_t *kl = keys;
+            T = sel_radix([kl](int64_t j) { return kl[j]; }, (int64_t)M, (uint32_t)K, kmin, kmax, X, need_eq,
+                          total_eq);
+            if (T != 0u && mcut < T) {
+                sel_emit([keys](int64_t j) { return keys[j]; },
+                         [locs, kk](int64_t j) { return (int32_t)(((int)j / kk) * kListChunk + locs[j]); },
+                         (int64_t)M, T, need_eq, tab, X);
+                done = true;
             }
-            if (!found) {
-                const uint32_t *kl = keys;
-                T = sel_radix([kl](int64_t j) { return kl[j]; }, (int64_t)M, (uint32_t)K, kmin, kmax, X, need_eq,
-                              total_eq);
-            }
-            certified = T != 0u && mcut < T;
         }
-        (void)total_eq;
-        if (certified) {
-            sel_emit([keys](int64_t j) { return keys[j]; },
-                     [locs, kk](int64_t j) { return (int32_t)((j / kk) * kListChunk + locs[j]); }, (int64_t)M, T,
-                     need_eq, p_beg, p_end, tab, row_out, A, seq, nb, X);
+        __syncthreads();
+    }
+    if (!done) {
+        // the whole score row, exactly: staged in the ring's LDS when it fits
+        // (one pass of coalesced loads, 16 in flight per thread), else read
+        // from the score row on every pass
+        const float *__restrict__ row = A.scores + i * A.ld;
+        auto rkey = [row](int64_t j) {
+            const uint32_t u = __float_as_uint(row[j]);
+            return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        };
+        constexpr int row_cap = (kWgWaves * D * kSlotBytes - kSelScratchBytes) / 4;
+        const bool staged = nb <= row_cap;
+        uint32_t *rk = keys;
+        if (staged && q_in_ring) {                           // the row overwrites the whole ring
+            wait_vmcnt<0>();
             __syncthreads();
-            return;
+            q_in_ring = false;
         }
-        __syncthreads();
-    }
-    // the whole score row, exactly
-    const float *__restrict__ row = A.scores + i * A.ld;
-    auto rkey = [row](int64_t j) {
-        const uint32_t u = __float_as_uint(row[j]);
-        return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    };
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-    for (int64_t j = threadIdx.x; j < nb; j += kSelThreads) {
-        const uint32_t k = rkey(j);
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-    }
-    {
-        const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax);
-        if (lane == 0) {
-            X.red[0][wave] = w_mn;
-            X.red[1][wave] = w_mx;
-        }
-        __syncthreads();
-        kmin = X.red[0][0];
-        kmax = X.red[1][0];
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+        if (staged) {
+            for (int j0 = 0; j0 < (int)nb; j0 += 16 * kSelThreads) {
+                uint32_t v[16];
 #pragma unroll
-        for (int w = 1; w < kWgWaves; ++w) {
-            kmin = min(kmin, X.red[0][w]);
-            kmax = max(kmax, X.red[1][w]);
+                for (int u = 0; u < 16; ++u) {
+                    const int j = j0 + u * kSelThreads + (int)threadIdx.x;
+                    v[u] = j < (int)nb ? rkey(j) : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int j = j0 + u * kSelThreads + (int)threadIdx.x;
+                    if (j < (int)nb) {
+                        rk[j] = v[u];
+                        kmin = min(kmin, v[u]);
+                        kmax = max(kmax, v[u]);
+                    }
+                }
+            }
+        } else {
+            for (int64_t j = threadIdx.x; j < nb; j += kSelThreads) {
+                const uint32_t k = rkey(j);
+                kmin = min(kmin, k);
+                kmax = max(kmax, k);
+            }
+        }
+        {
+            const uint32_t w_mn = wave_min_u32(kmin), w_mx = wave_max_u32(kmax);
+            if (lane == 0) {
+                X.red[0][wave] = w_mn;
+                X.red[1][wave] = w_mx;
+            }
+            __syncthreads();
+            kmin = X.red[0][0];
+            kmax = X.red[1][0];
+#pragma unroll
+            for (int w = 1; w < kWgWaves; ++w) {
+                kmin = min(kmin, X.red[0][w]);
+                kmax = max(kmax, X.red[1][w]);
+            }
+            __syncthreads();
+        }
+        auto ident = [](int64_t j) { return (int32_t)j; };
+        if (staged) {
+            auto lkey = [rk](int64_t j) { return rk[j]; };
+            T = sel_radix(lkey, nb, (uint32_t)K, kmin, kmax, X, need_eq, total_eq);
+            sel_emit(lkey, ident, nb, T, need_eq, tab, X);
+        } else {
+            T = sel_radix(rkey, nb, (uint32_t)K, kmin, kmax, X, need_eq, total_eq);
+            sel_emit(rkey, ident, nb, T, need_eq, tab, X);
         }
         __syncthreads();
     }
-    T = sel_radix(rkey, nb, (uint32_t)K, kmin, kmax, X, need_eq, total_eq);
-    sel_emit(rkey, [](int64_t j) { return (int32_t)j; }, nb, T, need_eq, p_beg, p_end, tab, row_out, A, seq, nb, X);
-    __syncthreads();
+    (void)total_eq;
+    // slots 0 .. K-1 hold the selection (nb > K): the idx row, and the part
+    // translated to pool blocks when paged (each slot read and written by
+    // one thread)
+    for (int j = threadIdx.x; j < K; j += kSelThreads) {
+        lds_i32_t *slot = (lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)j);
+        if (row_out) row_out[j] = *slot;
+        if (A.pm.table && j >= p_beg && j < p_end) *slot = slot_phys(*slot, A.pm, seq, nb, A.log2r);
+    }
+    if (A.pm.table) __syncthreads();
 }
 
 // Decode attention of one wave on the matrix cores.  Per 16-token step:
@@ -1091,6 +1321,30 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     const int c = (int)(t2 % (uint32_t)A.n_part);
     const int64_t i = (int64_t)(t2 / (uint32_t)A.n_part);
     if (i >= A.total_q) return;                      // uniform over the workgroup
+    const int qh0 = g * G;
+    uint8_t *ring = dyn_lds + wave * (D * kSlotBytes);
+    const uint32_t ring_addr = lds_addr(ring);
+    // Query rows (G x 256 contiguous bytes) travel through the last ring slot,
+    // which the prologue leaves free (a compiler-visible load would make the
+    // compiler wait for it, and so for the whole ring, inside the loop).
+    auto load_q = [&]() {
+        const uint32_t qslot = ring_addr + (D - 1) * kSlotBytes;
+        const uint16_t *qsrc = static_cast<const uint16_t *>(A.q) + (i * A.hq + qh0) * kD;
+        const int nq = (G * kD * 2 + 1023) / 1024;        // 1 KB per load, G <= 16
+        for (int j = 0; j < nq; ++j) {
+            const int e = (j * kWave + lane) * 8;          // bf16 element of this lane
+            dma16(qsrc + (e < G * kD ? e : 0), qslot + j * 1024);
+        }
+    };
+    // SELECT: the lists and the query rows are requested first; neither
+    // depends on the query's length, so their latency overlaps the offsets'.
+    SelPre pf;
+    bool q_in_ring = false;
+    if constexpr (SELECT) {
+        sel_prefetch(A, i, pf);
+        load_q();
+        q_in_ring = true;
+    }
 
     // This wave's share [s_beg, s_end) of the query's nsel selected blocks.
     auto split = [&](int nsel_, int64_t &sb, int64_t &se) {
@@ -1136,12 +1390,12 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
         const int per = ((int)nsel + A.n_part - 1) / A.n_part;
         const int p_beg = min(c * per, (int)nsel);
         const int p_end = min(p_beg + per, (int)nsel);
-        const uint32_t part_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes);
+        const uint32_t sel_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes);   // slot p = position p
         if (nb > 0)
-            select_part<D>(A, i, qp.seq, nb, p_beg, p_end, g == 0 && c == 0, part_tab, dyn_lds);
+            select_part<D>(A, i, qp.seq, nb, p_beg, p_end, g == 0 && c == 0, sel_tab, dyn_lds, pf, q_in_ring);
         else if (g == 0 && c == 0)
             for (int j = threadIdx.x; j < A.K; j += kSelThreads) A.idx_out[i * (int64_t)A.K + j] = -1;
-        big_tab = part_tab + 4u * (uint32_t)(s_beg - p_beg);
+        big_tab = sel_tab + 4u * (uint32_t)s_beg;
     }
     if constexpr (BIG && !SELECT) {
         int32_t v[kBigTabSlots / kWave];
@@ -1174,27 +1428,17 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
 
     const int n = lane & 15;                        // head column of this lane
     const int gq = lane >> 4;                       // 16-lane group
-    const int qh0 = g * G;
     const uint32_t row_bytes = (uint32_t)A.hkv * kD * 2;
     const uint16_t *__restrict__ kbase = static_cast<const uint16_t *>(A.k) + (row0 * A.hkv + g) * kD;
     const uint16_t *__restrict__ vbase = static_cast<const uint16_t *>(A.v) + (row0 * A.hkv + g) * kD;
-    uint8_t *ring = dyn_lds + wave * (D * kSlotBytes);
 
     const int nsteps = (W.ntok + kStep - 1) / kStep;
-    const uint32_t ring_addr = lds_addr(ring);
-    // Query rows (G x 256 contiguous bytes) travel through the last ring slot,
-    // which the prologue leaves free (a compiler-visible load would make the
-    // compiler wait for it, and so for the whole ring, inside the loop).  They
-    // are requested together with the slot table, so the two latencies overlap.
-    if (nsteps > 0) {
-        const uint32_t qslot = ring_addr + (D - 1) * kSlotBytes;
-        const uint16_t *qsrc = static_cast<const uint16_t *>(A.q) + (i * A.hq + qh0) * kD;
-        const int nq = (G * kD * 2 + 1023) / 1024;        // 1 KB per load, G <= 16
-        for (int j = 0; j < nq; ++j) {
-            const int e = (j * kWave + lane) * 8;          // bf16 element of this lane
-            dma16(qsrc + (e < G * kD ? e : 0), qslot + j * 1024);
-        }
-    }
+    // the query rows are requested together with the slot table, so the two
+    // latencies overlap (SELECT requested them at the start)
+    if (nsteps > 0 && !q_in_ring) load_q();
+    // a wave with no steps lets its early query loads land before the merge
+    // below reuses its ring
+    if (nsteps == 0 && q_in_ring) wait_vmcnt<0>();
     // The ring loads are invisible to the compiler, so it would place the
     // wait for the slot table inside the prologue loop below (waiting for the
     // ring loads as well); consuming the table here puts that wait up front.
@@ -1463,7 +1707,9 @@ int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
 
 template <int D, bool BIG, bool SELECT = false>
 hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, const LayerPtrs &Lp, hipStream_t st) {
-    const size_t lds = (size_t)kWgWaves * (D * kSlotBytes + (BIG ? kBigTabBytes : 0));
+    // SELECT: the table holds the whole selection (slot p = position p) and a
+    // wave reads up to kBigTabSlots slots past its first one
+    const size_t lds = (size_t)kWgWaves * (D * kSlotBytes + (BIG ? kBigTabBytes : 0)) + (SELECT ? kBigTabBytes : 0);
     const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D, BIG, SELECT>, (int)lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((attn_decode_mfma_kernel<D, BIG, SELECT>), grid, dim3(kWgWaves * kWave), lds, st, A, G,
