@@ -53,6 +53,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
+# L2 read bandwidth: 16 channels x 128 B/clk per XCD, 8 XCDs, 2.4 GHz
+L2_PEAK_GBPS = 16 * 128 * 8 * 2.4
 ATTN_SRC = os.path.join(ROOT, "indexer_selected_sparse_amd", "csrc", "qsa_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_hbm_traffic.md")
 
@@ -573,14 +575,20 @@ def measure(args, workload, cpu):
     }
     if prefill:
         f_idx, f_attn = prefill_flops(wl)
-        ach = f_attn / (t_attn * 1e-3) / 1e12
-        # the prefill attention computes QK and PV on the bf16 matrix cores
-        # (PV as two bf16 terms of the probabilities, counted once here); it
-        # is bounded by gathering each query's own token set, not by them
-        rec["roofline"] = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+        # every query gathers its own token set, so the launch moves its
+        # algorithmic bytes (34 GB for 84 MB of distinct K/V) through L2: the
+        # bound is the L2's bandwidth (counters: profiles/
+        # prefill_indexer_mfma_and_gather_l2_counters.md)
+        gbps = attn_bytes / (t_attn * 1e-3) / 1e9
+        rec["roofline"] = {"bound": "l2", "achieved": gbps, "peak": L2_PEAK_GBPS, "unit": "GB/s",
+                           "frac": gbps / L2_PEAK_GBPS, "traffic": None,
                            "kernel": "qsa_sparse_attn_prefill (causal gather attention)",
-                           "flops_per_launch": f_attn, "avg_ms": t_attn}
+                           "bytes_per_launch": attn_bytes, "avg_ms": t_attn}
+        ach = f_attn / (t_attn * 1e-3) / 1e12
+        # QK and PV run on the bf16 matrix cores (PV as two bf16 terms of the
+        # probabilities, counted once here)
+        rec["mfma_attention"] = {"tflops": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "util": ach / MFMA_BF16_PEAK_TFLOPS,
+                                 "flops_per_launch": f_attn}
         mf = f_idx / (t_score * 1e-3) / 1e12
         rec["mfma_indexer"] = {"tflops": mf, "peak": MFMA_BF16_PEAK_TFLOPS,
                                "util": mf / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": f_idx,
