@@ -747,10 +747,6 @@ struct SelScratch {
 };
 constexpr int kSelScratchBytes = (int)((sizeof(SelScratch) + 255) & ~(size_t)255);
 
-__device__ __forceinline__ float sel_key_value(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
 // Exclusive prefix sum over the 256 threads (thread order); total in `tot`.
 // `slot` picks one of the four exchange rows (consecutive calls use
 // different rows, so no trailing barrier is needed).
@@ -1100,51 +1096,23 @@ __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int 
     return true;
 }
 
-// Fill LDS table slots [p_beg, p_end) with query i's selected block ids
-// (physical when paged; nb > 0 visible blocks) and, for the designated
-// workgroup, write the idx row.  The selection is built as logical ids in
-// slots 0 .. K-1; a last pass copies the row out and translates the part.
-// `q_in_ring`: the query rows' loads into the ring's last slots are in
-// flight; a path that uses the whole ring waits for them and clears it.
+// The selection paths taken rarely: lists of more than kSelRegEntries
+// entries (staged in the ring's LDS), and the whole score row when the lists
+// cannot decide (staged in LDS when it fits).  The caller has emptied the
+// ring (no query rows in flight).  Fills LDS table slots 0 .. K-1 with
+// logical block ids and ends with a barrier.
 template <int D>
-__device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t nb, int p_beg, int p_end,
-                                            bool designated, uint32_t tab, uint8_t *ring_lds, SelPre &pf,
-                                            bool &q_in_ring) {
+__device__ __forceinline__ void select_slow(const uint32_t *__restrict__ gk, const uint8_t *__restrict__ gl,
+                                         const uint32_t *__restrict__ gc, const float *__restrict__ row, int64_t nb,
+                                         int K, int kk, int nch, int M, uint32_t tab, uint8_t *ring_lds) {
     SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
-    const int K = A.K;
-    int32_t *row_out = designated ? A.idx_out + i * (int64_t)K : nullptr;
-    if (nb <= K) {                                           // dense regime: identity
-        for (int j = threadIdx.x; j < K; j += kSelThreads) {
-            const int32_t v = j < nb ? j : -1;
-            if (row_out) row_out[j] = v;
-            if (j >= p_beg && j < p_end)
-                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)j) =
-                    A.pm.table ? slot_phys(v, A.pm, seq, nb, A.log2r) : v;
-        }
-        __syncthreads();
-        return;
-    }
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int kk = list_len(nb, K);
-    const int nch = (int)((nb + kListChunk - 1) / kListChunk);
-    const int M = nch * kk;
     constexpr int cap = ((kWgWaves * D * kSlotBytes - kSelScratchBytes) / 5) & ~3;
-    static_assert(kSelScratchBytes <= kSlotBytes, "the selection scratch stays clear of the query rows' slots");
     uint32_t *keys = reinterpret_cast<uint32_t *>(ring_lds + kSelScratchBytes);
     uint8_t *locs = reinterpret_cast<uint8_t *>(keys + cap);
     uint32_t T = 0, need_eq = 0, total_eq = 0;
     bool done = false;
-    if (M <= kSelRegEntries) {
-        done = select_part_regs(A, kk, nch, M, tab, X, pf);
-    } else if (M <= cap) {
-        if (q_in_ring) {                                      // the lists overwrite the whole ring
-            wait_vmcnt<0>();                                  // this wave's query loads landed,
-            __syncthreads();                                  // and every other wave's
-            q_in_ring = false;
-        }
-        const uint32_t *__restrict__ gk = A.la.keys + i * A.la.stride;
-        const uint8_t *__restrict__ gl = A.la.loc + i * A.la.stride;
-        const uint32_t *__restrict__ gc = A.la.cut + i * A.la.cstride;
+    if (M > kSelRegEntries && M <= cap) {
         uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u, mcut = 0u;
         for (int j0 = threadIdx.x; j0 < M; j0 += 4 * kSelThreads) {
             uint32_t k[4], l[4];
@@ -1210,7 +1178,6 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
         // the whole score row, exactly: staged in the ring's LDS when it fits
         // (one pass of coalesced loads, 16 in flight per thread), else read
         // from the score row on every pass
-        const float *__restrict__ row = A.scores + i * A.ld;
         auto rkey = [row](int64_t j) {
             const uint32_t u = __float_as_uint(row[j]);
             return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -1218,11 +1185,6 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
         constexpr int row_cap = (kWgWaves * D * kSlotBytes - kSelScratchBytes) / 4;
         const bool staged = nb <= row_cap;
         uint32_t *rk = keys;
-        if (staged && q_in_ring) {                           // the row overwrites the whole ring
-            wait_vmcnt<0>();
-            __syncthreads();
-            q_in_ring = false;
-        }
         uint32_t kmin = 0xffffffffu, kmax = 0u;
         if (staged) {
             for (int j0 = 0; j0 < (int)nb; j0 += 16 * kSelThreads) {
@@ -1277,6 +1239,47 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
         __syncthreads();
     }
     (void)total_eq;
+}
+
+// Fill LDS table slots [p_beg, p_end) with query i's selected block ids
+// (physical when paged; nb > 0 visible blocks) and, for the designated
+// workgroup, write the idx row.  The selection is built as logical ids in
+// slots 0 .. K-1; a last pass copies the row out and translates the part.
+// `q_in_ring`: the query rows' loads into the ring's last slots are in
+// flight; a path that uses the whole ring waits for them and clears it.
+template <int D>
+__device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t nb, int p_beg, int p_end,
+                                            bool designated, uint32_t tab, uint8_t *ring_lds, SelPre &pf,
+                                            bool &q_in_ring) {
+    SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
+    const int K = A.K;
+    int32_t *row_out = designated ? A.idx_out + i * (int64_t)K : nullptr;
+    if (nb <= K) {                                           // dense regime: identity
+        for (int j = threadIdx.x; j < K; j += kSelThreads) {
+            const int32_t v = j < nb ? j : -1;
+            if (row_out) row_out[j] = v;
+            if (j >= p_beg && j < p_end)
+                *(lds_i32_t *)(uintptr_t)(tab + 4u * (uint32_t)j) =
+                    A.pm.table ? slot_phys(v, A.pm, seq, nb, A.log2r) : v;
+        }
+        __syncthreads();
+        return;
+    }
+    const int kk = list_len(nb, K);
+    const int nch = (int)((nb + kListChunk - 1) / kListChunk);
+    const int M = nch * kk;
+    static_assert(kSelScratchBytes <= kSlotBytes, "the selection scratch stays clear of the query rows' slots");
+    bool done = false;
+    if (M <= kSelRegEntries) done = select_part_regs(A, kk, nch, M, tab, X, pf);
+    if (!done) {
+        if (q_in_ring) {                                      // the slow paths use the whole ring
+            wait_vmcnt<0>();                                  // this wave's query loads landed,
+            __syncthreads();                                  // and every other wave's
+            q_in_ring = false;
+        }
+        select_slow<D>(A.la.keys + i * A.la.stride, A.la.loc + i * A.la.stride, A.la.cut + i * A.la.cstride,
+                       A.scores + i * A.ld, nb, K, kk, nch, M, tab, ring_lds);
+    }
     // slots 0 .. K-1 hold the selection (nb > K): the idx row, and the part
     // translated to pool blocks when paged (each slot read and written by
     // one thread)
