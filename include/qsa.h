@@ -426,6 +426,7 @@ qsa_status qsa_sparse_attn_decode_lists(const qsa_attn *a, int32_t budget, int32
                                         const float *scores, int64_t ld_scores, int32_t *idx, void *out, void *ws,
                                         size_t ws_bytes, const qsa_paged_kv *pg, void *stream);
 
+
 /* ---- Layers that share one selection.  The first "llama.cpp vs Atlas"
  * report (section (a)3) lists indexers that are either full or shared: a
  * shared layer attends its own K/V with the top-k of the last full layer.
@@ -544,6 +545,29 @@ qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ra
                                   const qsa_key_ring *ring, const qsa_kv_append *kv, int32_t *status,
                                   const qsa_indexer *ix, float *scores, int64_t ld_scores,
                                   const qsa_paged_kv *pg, void *stream);
+
+/* The first half of a decode step with the append inside the scoring launch:
+ * qsa_ingest_index_score (one new token per sequence: ring commit, the block
+ * it completes, optional K/V rows; the canonical scores) that also writes the
+ * candidate lists of qsa_index_score_lists into ws.  The block a sequence's
+ * new token completes is scored by the append, so its chunk lists one block
+ * fewer and leaves its last slot, which the selection fills from the score
+ * row (every unlisted block is still bounded by its chunk's cutoff).  Follow
+ * it with qsa_sparse_attn_decode_lists on the same stream and workspace: the
+ * two calls equal qsa_ingest followed by qsa_decode_step bit for bit (scores,
+ * idx, out, compressed keys, ring, statuses, K/V).  ("Agentic shootout"
+ * page, vLLM vs Atlas (a)6 — indexer, KV update and sparse attention as one
+ * step — and the third "Flash-Next support" report, section (d), item 3.)
+ *  k_new .. status: as for qsa_ingest_index_score.
+ *  ix, a, budget, ratio, b, scores, ld_scores, ws, pg: as for
+ *                   qsa_index_score_lists (ws of at least
+ *                   qsa_decode_step_workspace_size() bytes, 16-byte aligned).
+ * Errors: those of qsa_ingest_index_score and qsa_decode_step. */
+qsa_status qsa_ingest_index_score_lists(const void *k_new, int32_t k_dtype, const qsa_key_ring *ring,
+                                        const qsa_kv_append *kv, int32_t *status, const qsa_indexer *ix,
+                                        const qsa_attn *a, int32_t budget, int32_t ratio, const qsa_batch *b,
+                                        float *scores, int64_t ld_scores, void *ws, size_t ws_bytes,
+                                        const qsa_paged_kv *pg, void *stream);
 
 /* Explicit rollback gate (defect investigations page, fix plan PR-F: a
  * rewind the indexer state cannot follow is declined, not applied).  The

@@ -37,7 +37,7 @@ EXPORTS = (
     "qsa_pool_scores", "qsa_attn_layers_workspace_size", "qsa_sparse_attn_decode_layers",
     "qsa_ingest_index_score", "qsa_sparse_attn_decode_static", "qsa_score_topk_workspace_size",
     "qsa_index_score_topk", "qsa_decode_step_workspace_size", "qsa_decode_step", "qsa_index_score_lists",
-    "qsa_sparse_attn_decode_lists",
+    "qsa_sparse_attn_decode_lists", "qsa_ingest_index_score_lists",
 )
 
 MAX_LAYERS = 8   # QSA_MAX_LAYERS
@@ -148,6 +148,8 @@ def lib():
         L.qsa_index_score_lists.argtypes = [P, P, i32, i32, P, P, i64, P, sz, P, P]
         L.qsa_sparse_attn_decode_lists.restype = i32
         L.qsa_sparse_attn_decode_lists.argtypes = [P, i32, i32, P, P, i64, P, P, P, sz, P, P]
+        L.qsa_ingest_index_score_lists.restype = i32
+        L.qsa_ingest_index_score_lists.argtypes = [P, i32, P, P, P, P, P, i32, i32, P, P, i64, P, sz, P, P]
         L.qsa_sparse_attn_decode_static.restype = i32
         L.qsa_sparse_attn_decode_static.argtypes = [P, P, i32, i32, P, P, P]
         L.qsa_ring_rewind.restype = i32
@@ -569,6 +571,30 @@ def ingest_index_score(k_new: torch.Tensor, ratio: int, batch: Batch, ring: KeyR
                                         None if kva is None else ctypes.byref(kva), _ptr(status), ctypes.byref(ix),
                                         _ptr(scores), scores.shape[1], None if pg is None else ctypes.byref(pg),
                                         _stream(stream)))
+
+
+def ingest_index_score_lists(k_new: torch.Tensor, ring: KeyRing, q_idx, w, kc, kc_scale, q, k, v, softmax_scale,
+                             budget: int, ratio: int, batch: Batch, scores: torch.Tensor,
+                             ws: Optional[torch.Tensor], kv=None, status: Optional[torch.Tensor] = None,
+                             stream=None, paging: Optional[Paging] = None) -> None:
+    """qsa_ingest_index_score_lists: ingest_index_score that also writes the
+    candidate lists into ws; follow it with sparse_attn_decode_lists."""
+    _dev(k_new, "k_new")
+    _dev(scores, "scores")
+    _check_ring_keys(ring, k_new)
+    ix = _indexer(q_idx, w, kc, kc_scale)
+    a = _attn(q, k, v, softmax_scale)
+    kva = _kv_append(kv)
+    if status is not None:
+        _dev(status, "status")
+    b, rg = batch._c(), ring._c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    pg = None if paging is None else ctypes.byref(paging._c())
+    _check(lib().qsa_ingest_index_score_lists(_ptr(k_new), _dtype_code(k_new), ctypes.byref(rg),
+                                              None if kva is None else ctypes.byref(kva), _ptr(status),
+                                              ctypes.byref(ix), ctypes.byref(a), budget, ratio, ctypes.byref(b),
+                                              _ptr(scores), scores.shape[1], _ptr(ws), nbytes, pg,
+                                              _stream(stream)))
 
 
 def ring_rewind(batch: Batch, ratio: int, ring: KeyRing, status: Optional[torch.Tensor] = None,

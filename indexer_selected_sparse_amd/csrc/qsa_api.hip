@@ -734,10 +734,11 @@ qsa_status qsa_ingest(const void *k_new, int32_t k_dtype, int32_t d_idx, int32_t
     });
 }
 
-qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ratio, const qsa_batch *b,
-                                  const qsa_key_ring *ring, const qsa_kv_append *kv, int32_t *status,
-                                  const qsa_indexer *ix, float *scores, int64_t ld_scores,
-                                  const qsa_paged_kv *pg, void *stream) {
+// Shared validation of the append + score calls.
+static qsa_status ingest_score_check(const void *k_new, int32_t k_dtype, int32_t ratio, const qsa_batch *b,
+                                     const qsa_key_ring *ring, const qsa_kv_append *kv, const qsa_indexer *ix,
+                                     const float *scores, int64_t ld_scores, const qsa_paged_kv *pg,
+                                     const char *what) {
     qsa_status s = check_indexer(ix, false);
     if (s == QSA_OK) s = check_batch(b, pg == nullptr);
     if (s == QSA_OK) s = check_ratio(ratio);
@@ -748,12 +749,12 @@ qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ra
     if (s != QSA_OK) return s;
     if (b->q_offsets)
         return fail(QSA_ERR_INVALID_ARGUMENT,
-                    "qsa_ingest_index_score takes one new token and one query per sequence "
-                    "(batch.q_offsets must be NULL); use qsa_ingest and qsa_index_score");
+                    "%s takes one new token and one query per sequence "
+                    "(batch.q_offsets must be NULL); use qsa_ingest and qsa_index_score", what);
     if (ix->q_dtype != QSA_BF16 || ix->kc_dtype == QSA_F32)
         return fail(QSA_ERR_UNSUPPORTED,
-                    "qsa_ingest_index_score needs a bf16 q_idx and bf16, e4m3 or fp4 compressed keys "
-                    "(q_dtype=%d, kc_dtype=%d)", ix->q_dtype, ix->kc_dtype);
+                    "%s needs a bf16 q_idx and bf16, e4m3 or fp4 compressed keys "
+                    "(q_dtype=%d, kc_dtype=%d)", what, ix->q_dtype, ix->kc_dtype);
     if (!k_new) return fail(QSA_ERR_INVALID_ARGUMENT, "k_new is NULL");
     if (k_dtype != QSA_F32 && k_dtype != QSA_BF16)
         return fail(QSA_ERR_UNSUPPORTED, "k_dtype=%d must be QSA_F32 or QSA_BF16", k_dtype);
@@ -762,10 +763,41 @@ qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ra
     if (ld_scores < need_ld || ld_scores < 1)
         return fail(QSA_ERR_INVALID_ARGUMENT, "ld_scores=%lld must be >= ceil(max_kv_len/ratio)=%lld",
                     (long long)ld_scores, (long long)need_ld);
+    return ok();
+}
+
+qsa_status qsa_ingest_index_score(const void *k_new, int32_t k_dtype, int32_t ratio, const qsa_batch *b,
+                                  const qsa_key_ring *ring, const qsa_kv_append *kv, int32_t *status,
+                                  const qsa_indexer *ix, float *scores, int64_t ld_scores,
+                                  const qsa_paged_kv *pg, void *stream) {
+    qsa_status s = ingest_score_check(k_new, k_dtype, ratio, b, ring, kv, ix, scores, ld_scores, pg,
+                                      "qsa_ingest_index_score");
+    if (s != QSA_OK) return s;
     return launch_checked("qsa_ingest_index_score", batch_check(*b, ratio, pg == nullptr, pg), stream,
                           [&](hipStream_t st) {
                               return launch_ingest_score(k_new, k_dtype, ratio, *b, *ring, kv, status, *ix, scores,
-                                                         ld_scores, pg, st);
+                                                         ld_scores, pg, st, ListArgs{});
+                          });
+}
+
+qsa_status qsa_ingest_index_score_lists(const void *k_new, int32_t k_dtype, const qsa_key_ring *ring,
+                                        const qsa_kv_append *kv, int32_t *status, const qsa_indexer *ix,
+                                        const qsa_attn *a, int32_t budget, int32_t ratio, const qsa_batch *b,
+                                        float *scores, int64_t ld_scores, void *ws, size_t ws_bytes,
+                                        const qsa_paged_kv *pg, void *stream) {
+    qsa_status s = ingest_score_check(k_new, k_dtype, ratio, b, ring, kv, ix, scores, ld_scores, pg,
+                                      "qsa_ingest_index_score_lists");
+    if (s != QSA_OK) return s;
+    // idx and out are not touched by this half: validate with stand-ins
+    int32_t dummy = 0;
+    s = decode_step_check(ix, a, budget, ratio, b, scores, ld_scores, &dummy, &dummy, ws, ws_bytes, pg);
+    if (s != QSA_OK) return s;
+    return launch_checked("qsa_ingest_index_score_lists", batch_check(*b, ratio, pg == nullptr, pg), stream,
+                          [&](hipStream_t st) {
+                              const ListArgs la = score_topk_uses_lists(*b) ? list_args(*b, budget, ratio, ws)
+                                                                            : ListArgs{};
+                              return launch_ingest_score(k_new, k_dtype, ratio, *b, *ring, kv, status, *ix, scores,
+                                                         ld_scores, pg, st, la);
                           });
 }
 

@@ -866,6 +866,7 @@ struct SelPre {
     uint4 k[kSelRegGroups];
     uint32_t l[kSelRegGroups];
     uint32_t c[kSelRegCuts];
+    uint32_t mode;                                   // the lists' form (qsa_lists.hpp)
 };
 
 __device__ __forceinline__ void sel_prefetch(const AttnArgs &A, int64_t i, SelPre &pf) {
@@ -885,6 +886,7 @@ __device__ __forceinline__ void sel_prefetch(const AttnArgs &A, int64_t i, SelPr
         const int cc = (int)threadIdx.x + u * kSelThreads;
         pf.c[u] = cc < nc ? gc[cc] : 0u;
     }
+    pf.mode = *A.la.mode;
 }
 
 __device__ __forceinline__ uint32_t &u4_at(uint4 &v, int e) {
@@ -898,8 +900,11 @@ __device__ __forceinline__ uint32_t &u4_at(uint4 &v, int e) {
 // caller then selects from the whole row.  Five barriers: the list
 // statistics, the histogram, the threshold bin's keys, the emit counts, the
 // finished table.
+// `nslot`: entry M-1 is the block the row's newest token completed (key
+// nkey, lane nloc), which its chunk left to the selection.
 __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int nch, int M, uint32_t tab,
-                                                 SelScratch &X, SelPre &pf) {
+                                                 SelScratch &X, SelPre &pf, bool nslot, uint32_t nkey,
+                                                 uint32_t nloc) {
     const int K = A.K;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u, mcut = 0u;
@@ -910,6 +915,10 @@ __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int 
             const int j = 4 * ((int)threadIdx.x + u * kSelThreads) + e;
             uint32_t &key = u4_at(pf.k[u], e);
             key = j < M ? key : 0u;
+            if (nslot && j == M - 1) {
+                key = nkey;
+                pf.l[u] = (pf.l[u] & ~(0xffu << (8 * e))) | (nloc << (8 * e));
+            }
             if (key != 0u) {
                 kmin = min(kmin, key);
                 kmax = max(kmax, key);
@@ -1103,8 +1112,9 @@ __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int 
 // logical block ids and ends with a barrier.
 template <int D>
 __device__ __forceinline__ void select_slow(const uint32_t *__restrict__ gk, const uint8_t *__restrict__ gl,
-                                         const uint32_t *__restrict__ gc, const float *__restrict__ row, int64_t nb,
-                                         int K, int kk, int nch, int M, uint32_t tab, uint8_t *ring_lds) {
+                                            const uint32_t *__restrict__ gc, const float *__restrict__ row, int64_t nb,
+                                            int K, int kk, int nch, int M, uint32_t tab, uint8_t *ring_lds,
+                                            bool nslot, uint32_t nkey, uint32_t nloc) {
     SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     constexpr int cap = ((kWgWaves * D * kSlotBytes - kSelScratchBytes) / 5) & ~3;
@@ -1119,8 +1129,9 @@ __device__ __forceinline__ void select_slow(const uint32_t *__restrict__ gk, con
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + u * kSelThreads;
-                k[u] = j < M ? gk[j] : 0u;
-                l[u] = j < M ? gl[j] : 0u;
+                const bool nj = nslot && j == M - 1;
+                k[u] = j < M ? (nj ? nkey : gk[j]) : 0u;
+                l[u] = j < M ? (nj ? nloc : gl[j]) : 0u;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1248,9 +1259,10 @@ __device__ __forceinline__ void select_slow(const uint32_t *__restrict__ gk, con
 // `q_in_ring`: the query rows' loads into the ring's last slots are in
 // flight; a path that uses the whole ring waits for them and clears it.
 template <int D>
-__device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t nb, int p_beg, int p_end,
+__device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t L, int p_beg, int p_end,
                                             bool designated, uint32_t tab, uint8_t *ring_lds, SelPre &pf,
                                             bool &q_in_ring) {
+    const int64_t nb = L >> A.log2r;
     SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
     const int K = A.K;
     int32_t *row_out = designated ? A.idx_out + i * (int64_t)K : nullptr;
@@ -1269,8 +1281,13 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
     const int nch = (int)((nb + kListChunk - 1) / kListChunk);
     const int M = nch * kk;
     static_assert(kSelScratchBytes <= kSlotBytes, "the selection scratch stays clear of the query rows' slots");
+    // the last entry of a row whose newest token completed a block is that
+    // block, scored by the append (its chunk left the slot)
+    const bool nslot = list_new_block_slot(pf.mode, L, A.log2r);
+    const uint32_t nkey = nslot ? list_order_key(A.scores[i * A.ld + nb - 1]) : 0u;
+    const uint32_t nloc = (uint32_t)((nb - 1) & (kListChunk - 1));
     bool done = false;
-    if (M <= kSelRegEntries) done = select_part_regs(A, kk, nch, M, tab, X, pf);
+    if (M <= kSelRegEntries) done = select_part_regs(A, kk, nch, M, tab, X, pf, nslot, nkey, nloc);
     if (!done) {
         if (q_in_ring) {                                      // the slow paths use the whole ring
             wait_vmcnt<0>();                                  // this wave's query loads landed,
@@ -1278,7 +1295,7 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
             q_in_ring = false;
         }
         select_slow<D>(A.la.keys + i * A.la.stride, A.la.loc + i * A.la.stride, A.la.cut + i * A.la.cstride,
-                       A.scores + i * A.ld, nb, K, kk, nch, M, tab, ring_lds);
+                       A.scores + i * A.ld, nb, K, kk, nch, M, tab, ring_lds, nslot, nkey, nloc);
     }
     // slots 0 .. K-1 hold the selection (nb > K): the idx row, and the part
     // translated to pool blocks when paged (each slot read and written by
@@ -1395,7 +1412,7 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
         const int p_end = min(p_beg + per, (int)nsel);
         const uint32_t sel_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes);   // slot p = position p
         if (nb > 0)
-            select_part<D>(A, i, qp.seq, nb, p_beg, p_end, g == 0 && c == 0, sel_tab, dyn_lds, pf, q_in_ring);
+            select_part<D>(A, i, qp.seq, qp.L, p_beg, p_end, g == 0 && c == 0, sel_tab, dyn_lds, pf, q_in_ring);
         else if (g == 0 && c == 0)
             for (int j = threadIdx.x; j < A.K; j += kSelThreads) A.idx_out[i * (int64_t)A.K + j] = -1;
         big_tab = sel_tab + 4u * (uint32_t)s_beg;

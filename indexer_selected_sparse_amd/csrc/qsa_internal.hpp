@@ -88,10 +88,12 @@ hipError_t launch_attn_layers(const qsa_attn *layers, int n_layers, const int32_
 
 // Append of one new token per sequence and the canonical scores of a decode
 // step in one launch (bf16 q_idx; bf16, e4m3 or fp4 compressed keys).
+// With la.keys set, also the candidate lists (the chunk of the block each
+// row's newest token completes leaves its last slot to the selection).
 hipError_t launch_ingest_score(const void *k_new, int k_dtype, int ratio, const qsa_batch &b,
                                const qsa_key_ring &ring, const qsa_kv_append *kv, int32_t *status,
                                const qsa_indexer &ix, float *scores, int64_t ld, const qsa_paged_kv *pg,
-                               hipStream_t st);
+                               hipStream_t st, const ListArgs &la);
 
 // Ingest of new tokens (ring commit, completed-block compression, optional
 // K/V append) and the ring's rollback gate.

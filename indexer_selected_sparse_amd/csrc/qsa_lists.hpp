@@ -16,6 +16,14 @@
 // and the lowest-index blocks among the keys equal to T are exactly those
 // of the whole row.  Otherwise it selects from the whole row.
 //
+// With the append inside the scoring launch, the block a row's newest token
+// completes is scored by the append, not by its chunk's wave.  That chunk
+// then lists one block fewer (its cutoff is the (kk-1)-th largest key of its
+// other blocks) and leaves its last slot, which is the row's last list entry,
+// to the selection, which fills it from the score row: every unlisted block
+// is still bounded by its chunk's cutoff, and the new block is listed.  The
+// scorer records which form it wrote in one device word (`mode`).
+//
 // list_len: m = ceil(64 K / nb) is the expected number of selected blocks in
 // a chunk (scores without locality); the list keeps m + 4 ceil(sqrt(m)) + 3,
 // at most 64, so for independent scores a chunk overflows its list with a
@@ -43,7 +51,10 @@ __host__ __device__ inline int list_len(int64_t nb, int K) {
 }
 
 // Lists of one call: row i's entries start at i * stride, its cutoffs at
-// i * cstride (one per chunk).  keys == nullptr: no lists.
+// i * cstride (one per chunk).  keys == nullptr: no lists.  *mode: 0, or
+// kListNewBlockSlot when rows whose newest token completes a block leave
+// their last entry to the selection.
+constexpr uint32_t kListNewBlockSlot = 1u;
 struct ListArgs {
     uint32_t *keys;
     uint8_t *loc;
@@ -51,7 +62,15 @@ struct ListArgs {
     int64_t stride;
     int64_t cstride;
     int K;
+    uint32_t *mode;
 };
+
+// Whether the selection of row i (visible length L) must fill its last list
+// entry with the block its newest token completed (the lists' mode read from
+// the device word).
+__host__ __device__ inline bool list_new_block_slot(uint32_t mode, int64_t L, int log2r) {
+    return mode == kListNewBlockSlot && (L & ((int64_t(1) << log2r) - 1)) == 0;
+}
 
 // Order-preserving map of a finite float to uint32 (larger float, larger
 // key); never 0 for a finite input, which leaves 0 free for padding.
@@ -66,17 +85,20 @@ __device__ __forceinline__ uint32_t list_lanes_below(uint64_t m) {
 
 // The wave's list for the chunk whose first block is `chunk0` (a multiple
 // of 64) of query row `row` with nb visible blocks: lane l holds block
-// chunk0 + l, its score s and whether it is visible (`active`).
+// chunk0 + l, its score s and whether it is listed (`active`).  `reserve`:
+// the chunk holds the block the append scores; list one block fewer and pad
+// the last slot.
 __device__ __forceinline__ void emit_chunk_list(const ListArgs &la, int64_t row, int64_t nb, int64_t chunk0,
-                                                bool active, float s, int lane) {
+                                                bool active, float s, int lane, bool reserve = false) {
     if (chunk0 >= nb) return;                                  // uniform over the wave
-    const int kk = list_len(nb, la.K);
+    const int kk = list_len(nb, la.K);                         // slots per chunk
+    const int kc = kk - (reserve ? 1 : 0);                     // entries chosen here
     const uint32_t key = active ? list_order_key(s) : 0u;
     const uint64_t act = __ballot(active);
     uint64_t sel = act;
     uint32_t cut = 0;
-    if (__builtin_popcountll(act) > kk) {
-        // t = the kk-th largest key: the largest t with #(key >= t) >= kk,
+    if (__builtin_popcountll(act) > kc) {
+        // t = the kc-th largest key: the largest t with #(key >= t) >= kc,
         // two bits per step (three independent counts), MSB first
         uint32_t t = 0;
         for (int bit = 30; bit >= 0; bit -= 2) {
@@ -84,11 +106,11 @@ __device__ __forceinline__ void emit_chunk_list(const ListArgs &la, int64_t row,
             const int n3 = __builtin_popcountll(__ballot(key >= c3));
             const int n2 = __builtin_popcountll(__ballot(key >= c2));
             const int n1 = __builtin_popcountll(__ballot(key >= c1));
-            t = n3 >= kk ? c3 : (n2 >= kk ? c2 : (n1 >= kk ? c1 : t));
+            t = n3 >= kc ? c3 : (n2 >= kc ? c2 : (n1 >= kc ? c1 : t));
         }
         const uint64_t gt = __ballot(key > t);
         const uint64_t eq = __ballot(key == t);
-        const uint32_t need = (uint32_t)kk - (uint32_t)__builtin_popcountll(gt);
+        const uint32_t need = (uint32_t)kc - (uint32_t)__builtin_popcountll(gt);
         sel = gt | __ballot(key == t && list_lanes_below(eq) < need);
         cut = t;
     }

@@ -130,6 +130,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
     int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, ListArgs la) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     const int64_t i = blockIdx.x;
+    if (la.mode && i == 0 && blockIdx.y == 0 && threadIdx.x == 0) *la.mode = 0u;   // plain lists
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
     const int64_t b = (int64_t)blockIdx.y * kScoreThreads + threadIdx.x;
@@ -328,6 +329,8 @@ __device__ __forceinline__ void score_exact_body(
     constexpr int QW = CH / 2;                           // query dwords per (chunk, head)
     static_assert(D % CH == 0 && (LPC == 1 || LPC == 2 || LPC == 4) && QW == 16, "chunk layout");
     static_assert((NCH - 1) * LPC < 64, "loads in flight fit the wait counter");
+    // the lists' form, for the selection that reads them
+    if (la.mode && i == 0 && by == 0 && threadIdx.x == 0) *la.mode = SKIP_NEW ? kListNewBlockSlot : 0u;
     const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
     const int64_t b = by * kExactThreads + threadIdx.x;
@@ -398,7 +401,13 @@ __device__ __forceinline__ void score_exact_body(
         s = s + t;
     }
     if (active) scores[i * ld + b] = s;
-    if (la.keys) emit_chunk_list(la, i, nb, b - (threadIdx.x & (kWave - 1)), active, s, threadIdx.x & (kWave - 1));
+    if (la.keys) {
+        const int64_t chunk0 = b - (threadIdx.x & (kWave - 1));
+        // the chunk of the block the append scores leaves its last slot
+        const bool reserve = SKIP_NEW && (qp.L & ((1 << log2r) - 1)) == 0 && nb > 0 &&
+                             chunk0 == ((nb - 1) & ~int64_t(kListChunk - 1));
+        emit_chunk_list(la, i, nb, chunk0, active, s, threadIdx.x & (kWave - 1), reserve);
+    }
 }
 
 template <typename KT, int D, int H>
@@ -461,10 +470,10 @@ __global__ __launch_bounds__(kExactThreads) void ingest_score_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KT *__restrict__ kc,
     void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off, const int64_t *__restrict__ blk_off,
     int num_seqs, int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, const TIn *__restrict__ k_new,
-    float inv_ratio, RingArgs ring, KvArgs kv, int32_t *__restrict__ status) {
+    float inv_ratio, RingArgs ring, KvArgs kv, int32_t *__restrict__ status, ListArgs la) {
     if ((int)blockIdx.x < num_seqs) {
         score_exact_body<KT, D, H, true>(q_idx, w, kc, kc_scale, kv_off, blk_off, nullptr, num_seqs, log2r,
-                                         scores, ld, pm, blockIdx.x, blockIdx.y, ListArgs{});
+                                         scores, ld, pm, blockIdx.x, blockIdx.y, la);
         return;
     }
     if (blockIdx.y != 0) return;
@@ -543,13 +552,14 @@ struct FusedArgs {
     RingArgs ring;
     KvArgs kv;
     int32_t *status;
+    ListArgs la;
 };
 
 template <typename KT, int D, int H, typename TIn>
 hipError_t fused_launch(const FusedArgs &f, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((ingest_score_kernel<KT, D, H, TIn>), grid, dim3(kExactThreads), 0, st, f.q_idx, f.w,
                        static_cast<KT *>(f.kc), f.kc_scale, f.kv_off, f.blk_off, f.num_seqs, f.log2r, f.scores,
-                       f.ld, f.pm, static_cast<const TIn *>(f.k_new), f.inv_ratio, f.ring, f.kv, f.status);
+                       f.ld, f.pm, static_cast<const TIn *>(f.k_new), f.inv_ratio, f.ring, f.kv, f.status, f.la);
     return hipGetLastError();
 }
 
@@ -636,9 +646,10 @@ hipError_t launch_score_canonical(const qsa_indexer &ix, int ratio, const qsa_ba
 hipError_t launch_ingest_score(const void *k_new, int k_dtype, int ratio, const qsa_batch &b,
                                const qsa_key_ring &ring, const qsa_kv_append *kv, int32_t *status,
                                const qsa_indexer &ix, float *scores, int64_t ld, const qsa_paged_kv *pg,
-                               hipStream_t st) {
+                               hipStream_t st, const ListArgs &la) {
     if (b.num_seqs == 0) return hipSuccess;
     FusedArgs f;
+    f.la = la;
     f.q_idx = static_cast<const uint16_t *>(ix.q_idx);
     f.w = ix.w;
     f.kc = const_cast<void *>(ix.kc);

@@ -1308,6 +1308,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
         l[u] = j < spec_n ? gl[j] : 0u;
     }
     const uint32_t c0 = (int)threadIdx.x < spec_c ? gc[threadIdx.x] : 0u;
+    const uint32_t mode = *la.mode;
     const QueryPos qp = query_pos(kv_off, nullptr, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
     int32_t *out = idx + i * (int64_t)ldi;
@@ -1318,6 +1319,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
     const int kk = list_len(nb, K);
     const int nch = (int)((nb + kListChunk - 1) / kListChunk);
     const int M = nch * kk;
+    // the last entry of a row whose newest token completed a block is that
+    // block, scored by the append (its chunk left the slot)
+    const bool nslot = list_new_block_slot(mode, qp.L, log2r);
+    const uint32_t nkey = nslot ? list_order_key(scores[i * ld + nb - 1]) : 0u;
+    const uint32_t nloc = (uint32_t)((nb - 1) & (kListChunk - 1));
     if (M <= cap) {
         uint32_t *keys = lds_lists;
         uint8_t *locs = reinterpret_cast<uint8_t *>(lds_lists + cap);
@@ -1339,16 +1345,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             const int j = (int)threadIdx.x + u * kTopkThreads;
             kr[u] = 0u;
             if (j < M) {
-                kr[u] = j < spec_n ? k[u] : gk[j];
+                const bool nj = nslot && j == M - 1;
+                kr[u] = nj ? nkey : (j < spec_n ? k[u] : gk[j]);
                 keys[j] = kr[u];
-                locs[j] = (uint8_t)(j < spec_n ? l[u] : gl[j]);
+                locs[j] = (uint8_t)(nj ? nloc : (j < spec_n ? l[u] : gl[j]));
                 note(kr[u]);
             }
         }
         for (int j = (int)threadIdx.x + 4 * kTopkThreads; j < M; j += kTopkThreads) {
-            const uint32_t key = gk[j];
+            const bool nj = nslot && j == M - 1;
+            const uint32_t key = nj ? nkey : gk[j];
             keys[j] = key;
-            locs[j] = gl[j];
+            locs[j] = nj ? (uint8_t)nloc : gl[j];
             note(key);
         }
         S.hist[threadIdx.x] = 0u;                    // the linear histogram's bin
@@ -1525,7 +1533,8 @@ size_t score_topk_workspace_bytes(const qsa_batch &b, int budget, int ratio) {
     if (!score_topk_uses_lists(b)) return topk_workspace_bytes(b, budget, ratio, nullptr);
     const size_t rows = (size_t)b.total_q, nch = (size_t)list_chunks(b, ratio);
     const size_t keys = rows * nch * kListChunk * 4, cuts = rows * nch * 4, locs = rows * nch * kListChunk;
-    return ((keys + 255) & ~(size_t)255) + ((cuts + 255) & ~(size_t)255) + locs + 256;
+    // keys, cutoffs, lanes, then the lists' mode word
+    return ((keys + 255) & ~(size_t)255) + ((cuts + 255) & ~(size_t)255) + ((locs + 255) & ~(size_t)255) + 256;
 }
 
 ListArgs list_args(const qsa_batch &b, int budget, int ratio, void *ws) {
@@ -1534,10 +1543,12 @@ ListArgs list_args(const qsa_batch &b, int budget, int ratio, void *ws) {
     uint8_t *base = static_cast<uint8_t *>(ws);
     const size_t keys_bytes = (rows * nch * kListChunk * 4 + 255) & ~(size_t)255;
     const size_t cuts_bytes = (rows * nch * 4 + 255) & ~(size_t)255;
+    const size_t locs_bytes = (rows * nch * kListChunk + 255) & ~(size_t)255;
     ListArgs la;
     la.keys = reinterpret_cast<uint32_t *>(base);
     la.cut = reinterpret_cast<uint32_t *>(base + keys_bytes);
     la.loc = base + keys_bytes + cuts_bytes;
+    la.mode = reinterpret_cast<uint32_t *>(base + keys_bytes + cuts_bytes + locs_bytes);
     la.stride = nch * kListChunk;
     la.cstride = nch;
     la.K = budget / ratio;

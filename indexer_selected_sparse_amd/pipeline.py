@@ -16,7 +16,7 @@ import numpy as np
 from . import (INGEST_OK, MAX_LAYERS, QSA_POOL_MAX, QSA_POOL_MEAN, QSA_SCORE_CANONICAL, QSA_SCORE_MFMA,
                Batch, KeyRing, Paging, attn_layers_workspace_size, attn_workspace_size, compress_keys,
                decode_step, decode_step_workspace_size, index_score, index_score_lists, index_score_topk, ingest,
-               ingest_index_score, pool_scores, score_topk_workspace_size, sparse_attn_decode_lists,
+               ingest_index_score, ingest_index_score_lists, pool_scores, score_topk_workspace_size, sparse_attn_decode_lists,
                sparse_attn_decode, sparse_attn_decode_layers, sparse_attn_prefill, topk_blocks, topk_workspace_size)
 
 _KC_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8,
@@ -102,6 +102,21 @@ class DeviceProblem:
                 and mode == QSA_SCORE_CANONICAL and self.token_pool is None
                 and self.q_idx.dtype == torch.bfloat16 and self.kc.dtype != torch.float32)
 
+    def ingest_step_fusable(self, mode: int = QSA_SCORE_CANONICAL) -> bool:
+        """Whether a decode step with the append can run as
+        qsa_ingest_index_score_lists + qsa_sparse_attn_decode_lists."""
+        return (self.fuse_step and self.ingest_fusable(mode) and self.step_ws is not None
+                and self.local_blocks == 0)
+
+    def ingest_score_lists(self, stream=None) -> None:
+        """qsa_ingest_index_score_lists: the append, the scores and the candidate
+        lists; attend_lists() selects and attends."""
+        st = self.ing
+        ingest_index_score_lists(st.k_new, st.ring, self.q_idx, self.w, self.kc, self.kc_scale, self.q, self.K,
+                                 self.V, self.softmax_scale, self.budget, self.ratio, self.batch, self.scores,
+                                 self.step_ws, kv=(st.k_row, st.v_row, self.K, self.V), status=st.status,
+                                 stream=stream, paging=self.paging)
+
     def ingest_score(self, stream=None) -> None:
         """qsa_ingest_index_score: ingest() and score() in one launch."""
         st = self.ing
@@ -173,6 +188,10 @@ class DeviceProblem:
         mode = QSA_SCORE_MFMA if mfma else QSA_SCORE_CANONICAL
         if self.step_fusable(mode):
             self.decode_step(stream=stream)
+            return
+        if self.ingest_step_fusable(mode):
+            self.ingest_score_lists(stream=stream)
+            self.attend_lists(stream=stream)
             return
         if self.ingest_fusable(mode):
             self.ingest_score(stream=stream)

@@ -21,10 +21,36 @@ def header_functions():
     return sorted(set(re.findall(r"\b(qsa_\w+)\s*\(", txt)))
 
 
+def _header_prototypes():
+    """name -> parameter count of every function qsa.h declares."""
+    txt = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(qsa_\w+)\s*\(([^)]*)\)\s*;", txt):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_declares_every_signature():
+    # ctypes passes an undeclared integer argument as a 32-bit int; a 64-bit
+    # parameter (a leading dimension, a byte count) would then carry garbage
+    # in its upper half, so every function must have its argument types
+    L = Q.lib()
+    protos = _header_prototypes()
+    assert set(protos) == set(Q.EXPORTS)
+    for name, n in protos.items():
+        f = getattr(L, name)
+        if n == 0:
+            continue
+        assert f.argtypes is not None, f"{name}: no argtypes in the binding"
+        assert len(f.argtypes) == n, f"{name}: {len(f.argtypes)} argtypes for {n} parameters"
+
+
 def test_library_exports_every_declared_function():
     L = Q.lib()
     names = header_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(L, n), f"{n} declared in qsa.h but not exported"
     assert set(names) == set(Q.EXPORTS)

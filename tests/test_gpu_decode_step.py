@@ -168,3 +168,97 @@ def test_graph_replays_match_eager():
         assert torch.equal(_bits(dp.out), _bits(eager[1])), f"replay {rep}: out"
         dp.decode_step()
         torch.cuda.synchronize()
+
+
+# --- the decode step with the append inside the scoring launch ------------------
+# qsa_ingest_index_score_lists + qsa_sparse_attn_decode_lists.  attach_ingest()
+# re-appends every sequence's newest token with the values the caches already
+# hold, so the step must give the plain decode step's scores, idx and outputs
+# bit for bit; the rows whose newest token completes a block (L % ratio == 0)
+# take their last list entry from the append's score.
+
+def _ingest_run(wl, paged=0):
+    ref = pipeline.upload(wl, "cuda", decode=True)
+    ref.compress()
+    if paged:
+        ref = pipeline.page(ref, wl.lens, paged, seed=9, extra_pages=2)
+    ref.decode_step()
+    torch.cuda.synchronize()
+    dp = pipeline.upload(wl, "cuda", decode=True)
+    dp.compress()
+    if paged:
+        dp = pipeline.page(dp, wl.lens, paged, seed=9, extra_pages=2)
+    pipeline.attach_ingest(dp, wl)
+    assert dp.ingest_step_fusable()
+    dp.scores.fill_(float("nan"))
+    dp.idx.fill_(-9)
+    dp.out.zero_()
+    dp.ingest_score_lists()
+    dp.attend_lists()
+    torch.cuda.synchronize()
+    assert bool((dp.ing.status == 0).all()), dp.ing.status.tolist()
+    Ls = wl.visible_lengths()
+    for r, L in enumerate(Ls):
+        nb = int(L) // wl.spec.ratio
+        assert torch.equal(dp.scores[r, :nb], ref.scores[r, :nb]), f"row {r}: scores differ"
+    assert torch.equal(dp.idx, ref.idx), "selection differs from the plain decode step"
+    assert torch.equal(_bits(dp.out), _bits(ref.out)), "outputs differ from the plain decode step"
+    assert torch.equal(dp.kc.view(torch.uint8), ref.kc.view(torch.uint8)), "compressed keys changed"
+    n_slot = sum(1 for L in Ls if int(L) % wl.spec.ratio == 0 and int(L) // wl.spec.ratio > wl.spec.budget // wl.spec.ratio)
+    _print(f"[ingest step] {wl.spec.name}: {n_slot} of {len(Ls)} rows filled their last list entry from the append")
+    return dp
+
+
+def test_ingest_step_batched_decode():
+    _ingest_run(W.make(W.BATCHED_DECODE))
+
+
+def test_ingest_step_long_decode():
+    _ingest_run(W.make(W.LONG_DECODE))
+
+
+def test_ingest_step_new_block_wins():
+    # the block each sequence's newest token completes gets keys four times
+    # larger, so it is selected: the filled slot decides the selection
+    sp = dataclasses.replace(W.BATCHED_DECODE, budget=512)
+    lens = [4 * 3000, 4 * 2200 + 2, 4 * 5000, 4 * 641, 4 * 2048, 4 * 4097 + 1]
+    wl = W.make(sp, lens=lens, seed=610)
+    for s, n in enumerate(lens):
+        if n % 4 == 0:
+            a = int(wl.kv_offsets[s]) + n - 4
+            wl.k_idx[a:a + 4] *= 16.0
+    dp = _ingest_run(wl)
+    ref = oracle.run_workload(wl, want_scores=True, want_out=False)
+    check_idx({"idx": dp.idx.cpu().numpy()}, ref, np.arange(wl.total_q))
+    got = dp.idx.cpu().numpy()
+    # a ReLU score can still be small for a large key, so count rather than
+    # require every boosted block
+    hits = sum(int((n // 4 - 1) in got[s]) for s, n in enumerate(lens) if n % 4 == 0)
+    _print(f"[ingest step] boosted new blocks selected: {hits} of {sum(n % 4 == 0 for n in lens)}")
+    assert hits >= 1
+
+
+@pytest.mark.parametrize("kc_dtype", ["e4m3", "fp4"])
+def test_ingest_step_key_formats(kc_dtype):
+    sp = dataclasses.replace(W.BATCHED_DECODE, kc_dtype=kc_dtype, budget=512)
+    _ingest_run(W.make(sp, lens=[9000, 2052, 4 * 777, 520, 4 * 129, 20004, 33], seed=611))
+
+
+def test_ingest_step_paged():
+    sp = dataclasses.replace(W.LONG_DECODE, hq=16, hkv=2, budget=1024)
+    _ingest_run(W.make(sp, lens=[20000, 7000, 4 * 1024 + 4], seed=612), paged=128)
+
+
+def test_ingest_step_k2048_lists_in_lds():
+    sp = dataclasses.replace(W.LONG_DECODE, hq=8, hkv=1, budget=8192)
+    _ingest_run(W.make(sp, lens=[131072, 60000, 8196, 8192 + 64, 100], seed=613))
+
+
+def test_ingest_step_fallback_rows():
+    sp = W.BATCHED_DECODE
+    wl = W.make(sp, lens=[20000, 9000, 30000, 4000], seed=614)
+    a = int(wl.kv_offsets[0]) + 4 * 3000
+    wl.k_idx[a:a + 4 * 300] *= 4.0
+    b = int(wl.kv_offsets[2]) + 4 * 7000
+    wl.k_idx[b:b + 4 * 700] *= 4.0
+    _ingest_run(wl)
