@@ -428,9 +428,14 @@ def measure(args, workload, cpu):
     # two halves (qsa_index_score_lists, qsa_sparse_attn_decode_lists), which
     # launch the same kernels as the one call
     fuse_step = fuse_sel and stacks is None and not args.unfused_step and base.step_fusable()
+    # with the append inside the scoring launch, the same two halves
+    # (qsa_ingest_index_score_lists, then qsa_sparse_attn_decode_lists)
+    fuse_ing_step = fuse_ing and stacks is None and not args.unfused_step and base.ingest_step_fusable()
 
     def score(p):
-        if fuse_ing:
+        if fuse_ing_step:
+            p.ingest_score_lists()
+        elif fuse_ing:
             p.ingest_score()
         elif prefill:
             p.score(QSA_SCORE_MFMA)
@@ -442,11 +447,11 @@ def measure(args, workload, cpu):
             p.score()
 
     def topk(p):
-        if not fuse_sel:
+        if not fuse_sel and not fuse_ing_step:
             p.topk(certified=prefill)
 
     def attend(p):
-        if fuse_step:
+        if fuse_step or fuse_ing_step:
             p.attend_lists()
         else:
             p.attend()
@@ -556,8 +561,10 @@ def measure(args, workload, cpu):
                    "heads": f"{spec.hq}/{spec.hkv}x{spec.d}", "indexer": f"{spec.h_idx}x{spec.d_idx} {spec.kc_dtype}",
                    "ratio": spec.ratio, "budget": spec.budget, "seed": spec.seed,
                    "input_replicas": R, "score_and_select": "one call" if fuse_sel else "two calls",
-                   "selection": ("inside the attention kernel (qsa_decode_step)" if fuse_step
-                                 else "own launch" if not prefill else "certified top-k launch"),
+                   "selection": ("inside the attention kernel (qsa_decode_step)" if fuse_step else
+                                 "inside the attention kernel (qsa_ingest_index_score_lists + "
+                                 "qsa_sparse_attn_decode_lists)" if fuse_ing_step else
+                                 "own launch" if not prefill else "certified top-k launch"),
                    **({"paged_page_size": args.paged} if args.paged else {}),
                    **({"layers": n_layers, "full_every": args.full_every, "fused_layers": not args.unfused_layers,
                        "layers_with_own_indexer": sum(stacks[0].full)} if stacks is not None else {}),
@@ -566,10 +573,11 @@ def measure(args, workload, cpu):
                    **({"ingest": "one token per sequence", "ingest_fused_with_scores": fuse_ing,
                        "ring_capacity": int(base.ing.ring.keys.shape[1])} if args.ingest else {})},
         "step_ms_percentiles": pct,
-        "kernel_ms": {**({"index_score_lists": t_score, "sparse_attn_select": t_attn} if fuse_step else
+        "kernel_ms": {**({"ingest_index_score_lists": t_score, "sparse_attn_select": t_attn} if fuse_ing_step else
+                         {"index_score_lists": t_score, "sparse_attn_select": t_attn} if fuse_step else
                          {"index_score_topk": t_score, "sparse_attn": t_attn} if fuse_sel else
                          {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn}),
-                      **({"ingest": t_ingest} if args.ingest else {})},
+                      **({"ingest": t_ingest} if t_ingest is not None else {})},
         "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
     }
@@ -600,7 +608,7 @@ def measure(args, workload, cpu):
         rec["roofline"] = {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                            "kernel": ("qsa_sparse_attn_decode_lists (per-part selection from the candidate "
-                                      "lists + gather attention + split combine)" if fuse_step else
+                                      "lists + gather attention + split combine)" if fuse_step or fuse_ing_step else
                                       "qsa_sparse_attn_decode (gather attention + split combine)"),
                            "bytes_per_launch": attn_bytes, "avg_ms": t_attn}
         rec["step_hbm_gbps"] = step_bytes / (ms_step * 1e-3) / 1e9
