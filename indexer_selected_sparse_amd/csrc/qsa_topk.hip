@@ -1384,9 +1384,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             }
         }
         uint32_t T = 0u, need_eq = 0u, total_eq = 0u;
-        bool found = false;
-        const float vmin = key_value(kmin), vmax = key_value(kmax);
-        const float scale = (float)kListBins / (vmax - vmin);
+        bool found = false, hopeless = false;
         if (nreal < (uint32_t)K || mcut >= kmax) {
             // fewer listed blocks than K, or a cutoff at or above every
             // listed key: the certificate cannot hold
@@ -1395,21 +1393,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
             need_eq = (uint32_t)K;
             total_eq = nreal;
             found = true;
-        } else if (scale < 3.0e38f) {
-            auto bin_of = [&](uint32_t key) {
-                return min(kListBins - 1, (int)((key_value(key) - vmin) * scale));
-            };
+        } else {
+            // A certified threshold exceeds every cutoff, so only keys from
+            // lo = max(kmin, mcut + 1) up can be it (a short chunk listed
+            // whole can hold keys far below the rest, which would crowd
+            // coarse bins).  kListBins bins linear in the key.
+            const uint32_t lo = max(kmin, mcut + 1u);
+            const uint32_t span = kmax - lo;
+            const int sh = span < (uint32_t)kListBins ? 0 : (32 - __builtin_clz(span)) - 10;
+            static_assert(kListBins == 1024, "bin shift assumes 1024 bins");
+            auto bin_of = [&](uint32_t key) { return (int)((key - lo) >> sh); };
             int kb[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                kb[u] = kr[u] != 0u ? bin_of(kr[u]) : -1;
+                kb[u] = kr[u] >= lo ? bin_of(kr[u]) : -1;
                 if (kb[u] >= 0) atomicAdd(&S.hist[kb[u]], 1u);
             }
             for (int j = (int)threadIdx.x + 4 * kTopkThreads; j < M; j += kTopkThreads) {
                 const uint32_t key = keys[j];
-                if (key != 0u) atomicAdd(&S.hist[bin_of(key)], 1u);
+                if (key >= lo) atomicAdd(&S.hist[bin_of(key)], 1u);
             }
-            if (threadIdx.x == 0) S.s2 = 0u;
+            if (threadIdx.x == 0) {
+                S.s2 = 0u;
+                S.s0 = 0xffffffffu;                  // no bin holds the K-th key yet
+            }
             __syncthreads();
             // thread t owns bin kListBins-1-t: the count above it by one scan
             const int bin = kListBins - 1 - (int)threadIdx.x;
@@ -1422,16 +1429,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
                 S.s3 = h;
             }
             __syncthreads();
+            // fewer than K keys above the cutoffs: the certificate cannot hold
+            hopeless = S.s0 == 0xffffffffu;
             const int tb = (int)S.s0;
             const uint32_t need = (uint32_t)K - S.s1;
-            const uint32_t nbin = S.s3;
+            const uint32_t nbin = hopeless ? 0xffffffffu : S.s3;
             if (nbin <= (uint32_t)kBinCandMax) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     if (kb[u] == tb) bcand[atomicAdd(&S.s2, 1u)] = kr[u];
                 for (int j = (int)threadIdx.x + 4 * kTopkThreads; j < M; j += kTopkThreads) {
                     const uint32_t key = keys[j];
-                    if (key != 0u && bin_of(key) == tb) bcand[atomicAdd(&S.s2, 1u)] = key;
+                    if (key >= lo && bin_of(key) == tb) bcand[atomicAdd(&S.s2, 1u)] = key;
                 }
                 __syncthreads();
                 if (wave == 0) {
@@ -1462,7 +1471,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_lists_kernel(
                 found = true;
             }
         }
-        if (!found && nreal >= (uint32_t)K && mcut < kmax) {
+        if (!found && !hopeless && nreal >= (uint32_t)K && mcut < kmax) {
             __syncthreads();
             T = radix_select(LdsKey{keys}, (int64_t)M, (uint32_t)K, kmin, kmax, S, need_eq, total_eq);
         }

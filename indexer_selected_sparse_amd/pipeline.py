@@ -409,9 +409,16 @@ class LayerStack:
     def step(self, stream=None) -> None:
         for g in self.groups:
             h = g[0]
-            if any(h is x for x in self.heads):   # a full layer: its own selection first
-                h.score(stream=stream)
-                h.topk(stream=stream)
+            full = any(h is x for x in self.heads)
+            if full and len(g) == 1 and h.step_fusable():
+                h.decode_step(stream=stream)     # a full layer alone: qsa_decode_step
+                continue
+            if full:                              # a full layer: its own selection first
+                if h.select_fusable():
+                    h.score_topk(stream=stream)
+                else:
+                    h.score(stream=stream)
+                    h.topk(stream=stream)
             if self.fused and self._fusable(g):
                 sparse_attn_decode_layers([(dp.q, dp.K, dp.V, dp.softmax_scale) for dp in g], h.idx,
                                           h.budget + h.local_blocks * h.ratio, h.ratio, h.batch,
