@@ -661,8 +661,9 @@ constexpr int kBigTabBytes = kBigTabSlots * 4;
 typedef __attribute__((address_space(3))) int32_t lds_i32_t;
 
 // issue_step_lds with the wave's slot table in LDS at byte address `tab`
-// (kBigTabSlots entries, -1 past the part's slots): each of lanes 0..15 reads
-// the block id of its own token's slot.
+// (up to kBigTabSlots entries; entries past the wave's nslot slots are read
+// but not used): each of lanes 0..15 reads the block id of its own token's
+// slot.
 __device__ __forceinline__ uint32_t issue_step_lds_tab(const WaveWork &W, int st, int lane, uint32_t tab,
                                                        const uint16_t *__restrict__ kbase,
                                                        const uint16_t *__restrict__ vbase,
@@ -731,9 +732,12 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 // the list finish of qsa_index_score_topk; a row the certificate does not
 // cover (or whose lists do not fit) is selected exactly from its whole
 // score row.  The workgroup of KV head 0, part 0 also writes the idx row.
-// No workgroup waits for another.  Scratch lives in the LDS of the ring,
-// which is free until the first step is issued; the part's slot table goes
-// to the LDS region after the rings (kWgWaves * kBigTabSlots entries).
+// No workgroup waits for another.  Scratch lives in the LDS of the ring
+// (the part of it the query rows, requested at the start, do not land in),
+// which is free until the first step is issued; the selection goes to a
+// table in the LDS region after the rings whose slot p is position p of the
+// query's selection (K entries; the region holds kWgWaves * kBigTabSlots of
+// them, plus kBigTabSlots so that a wave's reads stay inside).
 constexpr int kSelThreads = kWgWaves * kWave;          // 256
 constexpr int kSelBins = 1024;
 constexpr int kSelBinCand = kWave;
@@ -1403,8 +1407,9 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     }
     // BIG: the whole share (at most kBigTabSlots slots) into this wave's LDS
     // table, block ids translated to pool blocks when paged, -1 past the end.
-    // SELECT: the workgroup's part [p_beg, p_end) is one table over the four
-    // waves' regions, filled by the selection; each wave reads its share.
+    // SELECT: one table of the whole selection (slot p = position p) over the
+    // four waves' regions, filled by the selection; each wave reads its share
+    // from its first position (the part's slots translated when paged).
     uint32_t big_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes + wave * kBigTabBytes);
     if constexpr (SELECT) {
         const int per = ((int)nsel + A.n_part - 1) / A.n_part;
