@@ -213,6 +213,38 @@ def ingest_score(b=None, ix=None, scores=FAKE, ld=1024, kdt=Q.QSA_BF16):
                                           ctypes.byref(ix), P(scores), ld, None, None)
 
 
+def score_topk(b=None, ix=None, scores=FAKE, ld=1024, idx=FAKE, ws=FAKE, nws=1 << 30):
+    b = b or _batch()
+    ix = ix or _ix()
+    return Q.lib().qsa_index_score_topk(ctypes.byref(ix), 2048, 4, ctypes.byref(b), P(scores), ld, P(idx), P(ws),
+                                        nws, None, None)
+
+
+def decode_step(b=None, ix=None, a=None, scores=FAKE, ld=1024, idx=FAKE, out=FAKE, ws=FAKE, nws=1 << 30):
+    b = b or _batch()
+    ix = ix or _ix()
+    a = a or _attn()
+    return Q.lib().qsa_decode_step(ctypes.byref(ix), ctypes.byref(a), 2048, 4, ctypes.byref(b), P(scores), ld,
+                                   P(idx), P(out), P(ws), nws, None, None)
+
+
+def attend_lists(b=None, a=None, scores=FAKE, ld=1024, idx=FAKE, out=FAKE, ws=FAKE, nws=1 << 30):
+    b = b or _batch()
+    a = a or _attn()
+    return Q.lib().qsa_sparse_attn_decode_lists(ctypes.byref(a), 2048, 4, ctypes.byref(b), P(scores), ld, P(idx),
+                                                P(out), P(ws), nws, None, None)
+
+
+def ingest_lists(b=None, ix=None, a=None, scores=FAKE, ld=1024, ws=FAKE, nws=1 << 30):
+    b = b or _batch()
+    ix = ix or _ix()
+    a = a or _attn()
+    ring = _ring()
+    return Q.lib().qsa_ingest_index_score_lists(P(FAKE), Q.QSA_BF16, ctypes.byref(ring), None, None,
+                                                ctypes.byref(ix), ctypes.byref(a), 2048, 4, ctypes.byref(b),
+                                                P(scores), ld, P(ws), nws, None, None)
+
+
 INV, UNS, WS = Q.QSA_ERR_INVALID_ARGUMENT, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
 
 CASES = [
@@ -305,6 +337,20 @@ CASES = [
     ("ingest+score null scores", lambda: ingest_score(scores=None), INV, "scores is NULL"),
     ("ingest+score ld small", lambda: ingest_score(ld=1023), INV, "ld_scores=1023"),
     ("ingest+score raw key fp8", lambda: ingest_score(kdt=Q.QSA_FP8_E4M3), UNS, "k_dtype"),
+    ("score+select null idx", lambda: score_topk(idx=None), INV, "idx is NULL"),
+    ("score+select workspace small", lambda: score_topk(nws=16), WS, "qsa_score_topk_workspace_size"),
+    ("decode step null scores", lambda: decode_step(scores=None), INV, "scores is NULL"),
+    ("decode step ld small", lambda: decode_step(ld=1023), INV, "ld_scores=1023"),
+    ("decode step workspace small", lambda: decode_step(nws=16), WS, "qsa_decode_step_workspace_size"),
+    ("decode step workspace misaligned", lambda: decode_step(ws=FAKE + 4), INV, "16-byte aligned"),
+    ("decode step multi-query batch",
+     lambda: decode_step(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)), INV, "one query"),
+    ("attend lists workspace small", lambda: attend_lists(nws=16), WS, "qsa_decode_step_workspace_size"),
+    ("ingest step multi-query batch",
+     lambda: ingest_lists(b=_batch(q_offsets=FAKE, max_q_per_seq=4, total_q=8)), INV, "q_offsets must be NULL"),
+    ("ingest step f32 keys", lambda: ingest_lists(ix=_ix(kc_dtype=Q.QSA_F32)), UNS, "bf16, e4m3 or fp4"),
+    ("ingest step workspace small", lambda: ingest_lists(nws=16), WS, "qsa_decode_step_workspace_size"),
+    ("ingest step workspace misaligned", lambda: ingest_lists(ws=FAKE + 4), INV, "16-byte aligned"),
     ("rewind null ring", lambda: rewind(ring=None), INV, "ring is NULL"),
     ("rewind ratio 0", lambda: rewind(ratio=0), UNS, "ratio=0"),
 ]
