@@ -7,7 +7,14 @@ format, both raw-key dtypes, paged and contiguous caches.  After every step,
 bit for bit: scores, compressed keys and scales, ring keys and windows,
 statuses and K/V rows.  (The two calls themselves are checked against the
 oracle in test_gpu_ingest.py and the parity tests; the fused launch alone is
-also checked against the ingest oracle and the score oracle below.)"""
+also checked against the ingest oracle and the score oracle below.)
+
+The same histories also drive the two-launch step with ingest:
+qsa_ingest_index_score_lists must leave every state tensor as
+qsa_ingest_index_score does, and the selection and attention from its lists
+must equal the whole-row top-k and the plain decode attention bit for bit,
+on rows whose newest token completes a block with lost keys or an invalid
+slot too."""
 import numpy as np
 import pytest
 import torch
@@ -157,6 +164,76 @@ def test_fused_equals_ingest_then_score(kind, k_dtype, d, H, r, cap, hkv, paged,
         n_lost += int((st == Q.INGEST_LOST_KEYS).sum())
     # the histories reached every path of the fused kernel
     assert n_stored > 0 and n_lost > 0 and n_bad > 0
+
+
+LIST_CASES = [c for c in CASES if c[6] > 0]
+
+
+@pytest.mark.parametrize("kind,k_dtype,d,H,r,cap,hkv,paged,kv_dtype", LIST_CASES,
+                         ids=[f"{c[0]}-{str(c[1])[6:]}-d{c[2]}-h{c[3]}-r{c[4]}-{'paged' if c[7] else 'flat'}"
+                              f"-kv{c[6]}x{str(c[8])[6:]}" for c in LIST_CASES])
+def test_ingest_step_lists_on_histories(kind, k_dtype, d, H, r, cap, hkv, paged, kv_dtype):
+    # qsa_ingest_index_score_lists against qsa_ingest_index_score on the same
+    # histories (every state tensor bit for bit), then the selection and
+    # attention from its lists (qsa_sparse_attn_decode_lists) against the
+    # whole-row top-k and qsa_sparse_attn_decode on the other copy's scores.
+    # Rows whose newest token completes a block take their last list entry
+    # from the append's score, including blocks scored from the stored row
+    # (lost keys, invalid slots).
+    B, max_len, budget = 6, 240, 4 * r
+    seed = 31 * d + 5 * r + H + (1 if paged else 0) + hkv
+    rng = np.random.default_rng(seed)
+    a = State(B, max_len, r, cap, d, H, k_dtype, kind, hkv, paged, seed, kv_dtype)
+    b = a.clone()
+    slot_of = rng.permutation(a.num_slots)[:B].astype(np.int32)
+    lens = [int(x) for x in rng.integers(1, 120, B)]
+    g = torch.Generator().manual_seed(seed)
+    hq = 2 * hkv
+    scale = 1.0 / np.sqrt(128.0)
+    K_ = budget // r
+    n_slot = 0
+    for step in range(40):
+        for s in range(B):
+            if rng.random() < 0.4 / r and lens[s] > 2 * r:
+                lens[s] -= int(rng.integers(1, 2 * r))
+            lens[s] = min(lens[s] + 1, max_len)
+        slots = slot_of.copy()
+        slots[rng.random(B) < 0.24 / r] = -1
+        for st in (a, b):
+            st.ring.slots.copy_(torch.from_numpy(slots))
+        batch = a.batch(lens)
+        k_new = torch.randn((B, d), generator=g).to(k_dtype).to(DEV)
+        q_idx = torch.randn((B, H, d), generator=g).to(torch.bfloat16).to(DEV)
+        w = torch.rand((B, H), generator=g).to(DEV)
+        kvn = (torch.randn((B, hkv, 128), generator=g).to(kv_dtype).to(DEV),
+               torch.randn((B, hkv, 128), generator=g).to(kv_dtype).to(DEV))
+        q = torch.randn((B, hq, 128), generator=g).to(kv_dtype).to(DEV)
+        ws = torch.empty(max(1, Q.decode_step_workspace_size(q, a.K, a.V, scale, budget, r, batch)),
+                         dtype=torch.uint8, device=DEV)
+        Q.ingest_index_score(k_new, r, batch, a.ring, q_idx, w, a.kc, a.kc_scale, a.scores,
+                             kv=(kvn[0], kvn[1], a.K, a.V), status=a.status, paging=a.paging)
+        Q.ingest_index_score_lists(k_new, b.ring, q_idx, w, b.kc, b.kc_scale, q, b.K, b.V, scale, budget, r, batch,
+                                   b.scores, ws, kv=(kvn[0], kvn[1], b.K, b.V), status=b.status, paging=b.paging)
+        torch.cuda.synchronize()
+        ta, tb = a.tensors(), b.tensors()
+        for name in ta:
+            assert np.array_equal(_bits(ta[name]), _bits(tb[name])), (step, name)
+        idx_a = torch.full((B, K_), -9, dtype=torch.int32, device=DEV)
+        idx_b = torch.full((B, K_), -9, dtype=torch.int32, device=DEV)
+        out_a = torch.zeros_like(q)
+        out_b = torch.zeros_like(q)
+        tws = Q.topk_workspace_size(batch, budget, r, None)
+        Q.topk_blocks(a.scores, budget, r, batch, idx_a, ws=torch.empty(max(1, tws), dtype=torch.uint8, device=DEV))
+        aws = Q.attn_workspace_size(q, a.K, a.V, scale, budget, r, batch)
+        Q.sparse_attn_decode(q, a.K, a.V, scale, idx_a, budget, r, batch, out_a,
+                             torch.empty(max(1, aws), dtype=torch.uint8, device=DEV), paging=a.paging)
+        Q.sparse_attn_decode_lists(q, b.K, b.V, scale, budget, r, batch, b.scores, idx_b, out_b, ws,
+                                   paging=b.paging)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_a, idx_b), (step, "selection")
+        assert np.array_equal(_bits(out_a), _bits(out_b)), (step, "outputs")
+        n_slot += sum(1 for n in lens if n % r == 0 and n // r > K_)
+    assert n_slot > 0
 
 
 # ---------------------------------------------------------------------------
