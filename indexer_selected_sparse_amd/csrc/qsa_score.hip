@@ -191,8 +191,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_rounded_kernel(
 // widened chunk and H sums, so every workgroup of a decode batch is resident
 // at once; with the whole row widened up front (128 registers for it alone)
 // three workgroups fit per CU and the fourth ran as a second round on an
-// otherwise idle chip.  Measured on one MI355X, the FMA chain then runs at
-// the VALU issue rate and the remaining time is the wait for the first rows.
+// otherwise idle chip.  The query values are wave-uniform: with at most 32
+// (chunk, head) steps they arrive with the wave's first vector loads and
+// enter the multiply-adds through DPP row broadcasts (QueryVec); longer
+// query rows go through the scalar unit, one step ahead.  Measured on one
+// MI355X, per-step scalar loads had put a scalar-cache miss (microseconds
+// under the key traffic) in front of every step.
 constexpr int kExactChunk = 32;
 constexpr int kExactThreads = 256;
 
@@ -204,7 +208,7 @@ constexpr int kExactThreads = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
-// One 16-byte load of this lane's key row at byte offset OFF.
+// One 16-byte load at byte offset OFF (key rows; query dwords).
 template <int OFF>
 __device__ __forceinline__ u32x4 key_load16(const void *row) {
     u32x4 r;
@@ -224,10 +228,10 @@ __device__ __forceinline__ void key_wait(u32x4 (&u)[L]) {
     else
         asm volatile("s_waitcnt vmcnt(%4)" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]) : "n"(N));
 }
-// Query values, 16 wave-uniform dwords per (chunk, head) step, go through
-// the scalar unit into scalar registers one step ahead: a step's wait and the
-// next step's load are one statement, so the load is in flight while the
-// step's FMAs run.  The wait is also tied to the sum the previous step wrote
+// On the scalar query path, 16 wave-uniform dwords per (chunk, head) step go
+// through the scalar unit into scalar registers one step ahead: a step's
+// wait and the next step's load are one statement, so the load is in flight
+// while the step's FMAs run.  The wait is also tied to the sum the previous step wrote
 // (so that step is finished and only two steps' values are live).  Scalar
 // loads may complete out of order, hence lgkmcnt(0).
 template <int OFF>
@@ -268,6 +272,112 @@ __device__ __forceinline__ uint32_t fp4_scale_load(const uint8_t *p) {
 // 2^(e - 127) from an E8M0 byte e (e = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+// Scalar query path (query rows of more than 32 steps): the row's NL
+// 64-byte lines are requested into the scalar cache all at once and waited
+// for in the same statement (the loads share one scratch register set, dead
+// afterwards), so the (chunk, head) steps find their values there instead of
+// each waiting out a miss in turn.
+#define QSA_QPF(LOADS) asm volatile(LOADS "s_waitcnt lgkmcnt(0)" : "=&s"(junk) : "s"(p) : "memory")
+template <int NL>
+__device__ __forceinline__ void query_prefetch(const uint32_t *p) {
+    u32x16 junk;
+    if constexpr (NL == 32)
+        QSA_QPF("s_load_dwordx16 %0, %1, 0x0\n\t" "s_load_dwordx16 %0, %1, 0x40\n\t"
+            "s_load_dwordx16 %0, %1, 0x80\n\t" "s_load_dwordx16 %0, %1, 0xc0\n\t"
+            "s_load_dwordx16 %0, %1, 0x100\n\t" "s_load_dwordx16 %0, %1, 0x140\n\t"
+            "s_load_dwordx16 %0, %1, 0x180\n\t" "s_load_dwordx16 %0, %1, 0x1c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x200\n\t" "s_load_dwordx16 %0, %1, 0x240\n\t"
+            "s_load_dwordx16 %0, %1, 0x280\n\t" "s_load_dwordx16 %0, %1, 0x2c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x300\n\t" "s_load_dwordx16 %0, %1, 0x340\n\t"
+            "s_load_dwordx16 %0, %1, 0x380\n\t" "s_load_dwordx16 %0, %1, 0x3c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x400\n\t" "s_load_dwordx16 %0, %1, 0x440\n\t"
+            "s_load_dwordx16 %0, %1, 0x480\n\t" "s_load_dwordx16 %0, %1, 0x4c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x500\n\t" "s_load_dwordx16 %0, %1, 0x540\n\t"
+            "s_load_dwordx16 %0, %1, 0x580\n\t" "s_load_dwordx16 %0, %1, 0x5c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x600\n\t" "s_load_dwordx16 %0, %1, 0x640\n\t"
+            "s_load_dwordx16 %0, %1, 0x680\n\t" "s_load_dwordx16 %0, %1, 0x6c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x700\n\t" "s_load_dwordx16 %0, %1, 0x740\n\t"
+            "s_load_dwordx16 %0, %1, 0x780\n\t" "s_load_dwordx16 %0, %1, 0x7c0\n\t");
+    else if constexpr (NL == 64)
+        QSA_QPF("s_load_dwordx16 %0, %1, 0x0\n\t" "s_load_dwordx16 %0, %1, 0x40\n\t"
+            "s_load_dwordx16 %0, %1, 0x80\n\t" "s_load_dwordx16 %0, %1, 0xc0\n\t"
+            "s_load_dwordx16 %0, %1, 0x100\n\t" "s_load_dwordx16 %0, %1, 0x140\n\t"
+            "s_load_dwordx16 %0, %1, 0x180\n\t" "s_load_dwordx16 %0, %1, 0x1c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x200\n\t" "s_load_dwordx16 %0, %1, 0x240\n\t"
+            "s_load_dwordx16 %0, %1, 0x280\n\t" "s_load_dwordx16 %0, %1, 0x2c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x300\n\t" "s_load_dwordx16 %0, %1, 0x340\n\t"
+            "s_load_dwordx16 %0, %1, 0x380\n\t" "s_load_dwordx16 %0, %1, 0x3c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x400\n\t" "s_load_dwordx16 %0, %1, 0x440\n\t"
+            "s_load_dwordx16 %0, %1, 0x480\n\t" "s_load_dwordx16 %0, %1, 0x4c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x500\n\t" "s_load_dwordx16 %0, %1, 0x540\n\t"
+            "s_load_dwordx16 %0, %1, 0x580\n\t" "s_load_dwordx16 %0, %1, 0x5c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x600\n\t" "s_load_dwordx16 %0, %1, 0x640\n\t"
+            "s_load_dwordx16 %0, %1, 0x680\n\t" "s_load_dwordx16 %0, %1, 0x6c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x700\n\t" "s_load_dwordx16 %0, %1, 0x740\n\t"
+            "s_load_dwordx16 %0, %1, 0x780\n\t" "s_load_dwordx16 %0, %1, 0x7c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x800\n\t" "s_load_dwordx16 %0, %1, 0x840\n\t"
+            "s_load_dwordx16 %0, %1, 0x880\n\t" "s_load_dwordx16 %0, %1, 0x8c0\n\t"
+            "s_load_dwordx16 %0, %1, 0x900\n\t" "s_load_dwordx16 %0, %1, 0x940\n\t"
+            "s_load_dwordx16 %0, %1, 0x980\n\t" "s_load_dwordx16 %0, %1, 0x9c0\n\t"
+            "s_load_dwordx16 %0, %1, 0xa00\n\t" "s_load_dwordx16 %0, %1, 0xa40\n\t"
+            "s_load_dwordx16 %0, %1, 0xa80\n\t" "s_load_dwordx16 %0, %1, 0xac0\n\t"
+            "s_load_dwordx16 %0, %1, 0xb00\n\t" "s_load_dwordx16 %0, %1, 0xb40\n\t"
+            "s_load_dwordx16 %0, %1, 0xb80\n\t" "s_load_dwordx16 %0, %1, 0xbc0\n\t"
+            "s_load_dwordx16 %0, %1, 0xc00\n\t" "s_load_dwordx16 %0, %1, 0xc40\n\t"
+            "s_load_dwordx16 %0, %1, 0xc80\n\t" "s_load_dwordx16 %0, %1, 0xcc0\n\t"
+            "s_load_dwordx16 %0, %1, 0xd00\n\t" "s_load_dwordx16 %0, %1, 0xd40\n\t"
+            "s_load_dwordx16 %0, %1, 0xd80\n\t" "s_load_dwordx16 %0, %1, 0xdc0\n\t"
+            "s_load_dwordx16 %0, %1, 0xe00\n\t" "s_load_dwordx16 %0, %1, 0xe40\n\t"
+            "s_load_dwordx16 %0, %1, 0xe80\n\t" "s_load_dwordx16 %0, %1, 0xec0\n\t"
+            "s_load_dwordx16 %0, %1, 0xf00\n\t" "s_load_dwordx16 %0, %1, 0xf40\n\t"
+            "s_load_dwordx16 %0, %1, 0xf80\n\t" "s_load_dwordx16 %0, %1, 0xfc0\n\t");
+    else
+        static_assert(NL == 32, "scalar query rows of 32 or 64 lines");
+}
+#undef QSA_QPF
+
+// Vector query path.  Under a decode batch's key traffic a scalar-cache miss
+// takes microseconds, and every (chunk, head) step of the scalar path waits
+// for one; here the query row instead arrives with the wave's first vector
+// loads (issued before the key row, so the wait for the first key chunk
+// covers it) and reaches the fused multiply-adds through DPP row broadcasts.
+//
+// Step t = c * H + h uses the 16 query dwords of head h, dims 32c .. 32c+31
+// (the step's block).  16-byte load g gives lane l dwords 4(l%4) .. +3 of
+// block 4g + (l/4)%4, the same in each 16-lane row, so dword k of block t is
+// in register k%4 of load t/4, at row lane 4(t%4) + k/4.  The registers of a
+// load are widened to fp32 once (8 operations for 4 steps).
+template <int H, int D>
+struct QueryVec {
+    static constexpr int NCH = D / kExactChunk;
+    static constexpr int STEPS = NCH * H;
+    static constexpr int NQ = (STEPS + 3) / 4;   // 16-byte loads per lane
+    static constexpr bool kUse = STEPS <= 32;
+};
+
+// 8 fused multiply-adds acc += q * k, dims 8m .. 8m+7 of one step in
+// ascending order: q from the widened registers (lo: even dims, hi: odd
+// dims of dwords 4m .. 4m+3) broadcast from row lane LANE, k in registers.
+// The leading s_nop gives the two wait states a DPP read needs after the
+// VALU write of its source.
+template <int LANE>
+__device__ __forceinline__ void fma8_bcast(float &acc, const float (&lo)[4], const float (&hi)[4],
+                                           const float *k) {
+    static_assert(LANE >= 0 && LANE < 16, "row lane");
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %5, %10 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %11 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %6, %12 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %13 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %7, %14 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %15 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %16 row_newbcast:%17 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]),
+          "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]), "n"(LANE));
 }
 
 template <typename KT, int CH>
@@ -343,6 +453,18 @@ __device__ __forceinline__ void score_exact_body(
     const uint8_t *krow = reinterpret_cast<const uint8_t *>(kc) + row * (D * KeyBits<KT>::value / 8);
     const uint32_t *q32 = reinterpret_cast<const uint32_t *>(q_idx) + i * (int64_t)(H * D / 2);
 
+    using QV = QueryVec<H, D>;
+    u32x4 qv[QV::kUse ? QV::NQ : 1];
+    if constexpr (QV::kUse) {
+        const int lane = threadIdx.x & (kWave - 1);
+        static_for<0, QV::NQ>([&](auto gg) {
+            constexpr int g = decltype(gg)::value;
+            int t = 4 * g + ((lane >> 2) & 3);
+            if (t >= QV::STEPS) t = 0;                       // past the last step: any valid block
+            const int c = t / H, h = t % H;
+            qv[g] = key_load16<0>(q32 + h * (D / 2) + 16 * c + 4 * (lane & 3));
+        });
+    }
     uint32_t sbits = 0;
     if constexpr (kFP4) sbits = fp4_scale_load<D>(static_cast<const uint8_t *>(kc_scale) + row * (D / 32));
     u32x4 raw[NCH][LPC];
@@ -356,22 +478,44 @@ __device__ __forceinline__ void score_exact_body(
         }
     });
     u32x16 qbuf[2];
-    qbuf[0] = query_load16<0>(q32);
+    if constexpr (!QV::kUse) {
+        query_prefetch<H * D / 32>(q32);
+        qbuf[0] = query_load16<0>(q32);
+    }
 
     float acc[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) acc[h] = 0.0f;
+    float qlo[4], qhi[4];
     // (chunk, head) steps in order; chunk c is waited for at its first step
     // (the loads of chunks c+1.. may still be in flight).
     static_for<0, NCH>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         key_wait<(NCH - 1 - c) * LPC>(raw[c]);
         if constexpr (kFP4 && c == 0) asm volatile("" : "+v"(sbits));   // landed before chunk 0
+        if constexpr (QV::kUse && c == 0) {                              // issued before chunk 0
+#pragma unroll
+            for (int g = 0; g < QV::NQ; ++g) asm volatile("" : "+v"(qv[g]));
+        }
         float kf[CH];
         widen_chunk<KT, CH>(raw[c], kf, kFP4 ? e8m0_to_f32((sbits >> (8 * c)) & 0xffu) : 1.0f);
         static_for<0, H>([&](auto hh) {
             constexpr int h = decltype(hh)::value;
             constexpr int t = c * H + h;
+            if constexpr (QV::kUse) {
+                if constexpr (t % 4 == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        qlo[r] = bf16lo(qv[t / 4][r]);
+                        qhi[r] = bf16hi(qv[t / 4][r]);
+                    }
+                }
+                fma8_bcast<4 * (t % 4) + 0>(acc[h], qlo, qhi, kf + 0);
+                fma8_bcast<4 * (t % 4) + 1>(acc[h], qlo, qhi, kf + 8);
+                fma8_bcast<4 * (t % 4) + 2>(acc[h], qlo, qhi, kf + 16);
+                fma8_bcast<4 * (t % 4) + 3>(acc[h], qlo, qhi, kf + 24);
+                return;
+            }
             u32x16 &qu = qbuf[t & 1];
             constexpr int tn = t + 1;                // next step: its query offset in bytes
             constexpr int off = 4 * ((tn % H) * (D / 2) + (tn / H) * QW);
