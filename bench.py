@@ -13,8 +13,10 @@ Workloads (synthetic, seeded; see qsa_workloads):
 
 A step is one pass of the whole hot path over one batch with every input
 resident in HBM.  `value` is queries per second of the step replayed from a
-HIP graph (one graph per input copy); `step_ms.eager` is the same step
-launched call by call.  Key compression is an ingest-time pass, timed on its
+HIP graph that holds the step on each input copy in turn (as the step runs
+inside a larger captured graph, without a graph-launch boundary between
+steps); `step_ms.graph_one_step` replays one graph per step instead, and
+`step_ms.eager` launches the step call by call.  Key compression is an ingest-time pass, timed on its
 own (`compress_ms`); with --ingest each decode step first appends every
 sequence's newest token (qsa_ingest: its raw key into the ring, the block
 it completes, its K/V rows), as a serving step does.  Decode steps rotate over several device copies of the
@@ -523,12 +525,38 @@ def measure(args, workload, cpu):
                     topk(p)
                     attend(p)
             graphs.append(g)
+        # The step on every input copy in turn, captured as one graph: the way
+        # the step runs inside a larger captured graph (a decode iteration's
+        # layers), where one kernel follows another without a graph-launch
+        # boundary (measured: about 4 us per boundary between single-step
+        # replays).  `value` is timed with it: steps // R replays, then the
+        # remaining steps % R steps from the single-step graphs, so exactly
+        # `steps` steps in all; the single-step replay time is reported beside
+        # it (step_ms.graph_one_step).
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for k_, p in enumerate(reps):
+                if stacks is not None:
+                    stacks[k_].step()
+                else:
+                    ingest(p)
+                    score(p)
+                    topk(p)
+                    attend(p)
         for s_ in range(args.warmup):
             graphs[s_ % R].replay()
+        g_all.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s_ in range(args.steps):
             graphs[s_ % R].replay()
+        torch.cuda.synchronize()
+        one_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        t0 = time.perf_counter()
+        for _ in range(args.steps // R):
+            g_all.replay()
+        for s_ in range(args.steps % R):
+            graphs[s_].replay()
         torch.cuda.synchronize()
         graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         # the distribution over steps comes from a second pass with an event
@@ -578,7 +606,8 @@ def measure(args, workload, cpu):
                          {"index_score_topk": t_score, "sparse_attn": t_attn} if fuse_sel else
                          {"index_score": t_score, "topk": t_topk, "sparse_attn": t_attn}),
                       **({"ingest": t_ingest} if t_ingest is not None else {})},
-        "step_ms": {"graph": graph_ms_step if graphs else None, "eager": eager_ms_step},
+        "step_ms": {"graph": graph_ms_step if graphs else None,
+                    "graph_one_step": one_step_ms if graphs else None, "eager": eager_ms_step},
         "compress_ms": compress_ms,
     }
     if prefill:
