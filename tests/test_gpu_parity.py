@@ -63,7 +63,11 @@ DTYPES = [
 
 
 @pytest.mark.parametrize("name,kv,idx_dt,kc_dt", DTYPES, ids=[d[0] for d in DTYPES])
-@pytest.mark.parametrize("h_idx,d_idx", [(1, 64), (2, 128), (4, 64), (8, 128), (16, 64), (16, 128)])
+# (heads, dims): query rows of 2 to 64 (chunk, head) steps, so every load
+# count of the scorer's vector query path (one partial load, 1, 2, 4 and 8
+# loads) and its scalar path (64 steps) meet the oracle
+@pytest.mark.parametrize("h_idx,d_idx", [(1, 64), (2, 64), (2, 128), (4, 64), (4, 128), (8, 128), (16, 64),
+                                         (16, 128)])
 def test_indexer_dtype_and_shape_matrix(name, kv, idx_dt, kc_dt, h_idx, d_idx):
     sp = dataclasses.replace(W.BATCHED_DECODE, kv_dtype=kv, idx_dtype=idx_dt, kc_dtype=kc_dt, h_idx=h_idx,
                              d_idx=d_idx, hq=8, hkv=2, budget=128)
