@@ -30,7 +30,8 @@ HIPCC_FLAGS = [
 # Per-source extra flags.  The attention kernels keep their matrix-core
 # accumulators in ordinary VGPRs (the compiler would otherwise pick AGPRs,
 # and every online-softmax rescale would copy them out and back).
-EXTRA_FLAGS = {"qsa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+EXTRA_FLAGS = {"qsa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+               "qsa_attn_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def sources():

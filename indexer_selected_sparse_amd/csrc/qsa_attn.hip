@@ -747,7 +747,7 @@ struct SelScratch {
     uint32_t s[8];
     uint32_t bcw[kWgWaves][kSelBinCand];   // the threshold bin's keys, per wave
     uint32_t bcn[kWgWaves];
-    uint32_t tot[4][kWgWaves];
+    uint32_t tot[8][kWgWaves];             // per register group (at most 8)
 };
 constexpr int kSelScratchBytes = (int)((sizeof(SelScratch) + 255) & ~(size_t)255);
 
@@ -852,28 +852,31 @@ __device__ __forceinline__ void sel_emit(const KeyF &key, const BlkF &blk_of, in
     }
 }
 
-// Lists of at most kSelRegEntries entries (every row of at most 32768
-// blocks at K <= 512) are selected from registers.  Thread t holds the
-// entries 4g .. 4g+3 for g = t + 256u, u < kSelRegGroups, so for each u the
-// four waves hold 1024 consecutive entries, wave after wave and lane after
-// lane: ascending order is (u, wave, lane, e).  The first kSelRegEntries
-// entries and kSelRegCuts * 256 cutoffs of the row's lists are requested at
-// the kernel's start, before the query's length is known (they lie inside
-// the row's region of the workspace whatever the length; entries past the
-// row's own lists are masked once it is known).
-constexpr int kSelRegGroups = 4;
-constexpr int kSelRegEntries = 4 * kSelRegGroups * kSelThreads;     // 4096
-constexpr int kSelRegCuts = 2;                                      // 512 chunks
-static_assert(kSelRegEntries / 8 <= kSelRegCuts * kSelThreads,
-              "a list of kSelRegEntries entries has at most that many chunks (>= 8 entries each)");
+// Lists of at most sel_reg_entries(NG) entries are selected from registers:
+// NG = 4 groups (4096 entries: every row of at most 32768 blocks at
+// K <= 512) or NG = 8 (8192 entries: rows of 32768 blocks at K = 2048).
+// Thread t holds the entries 4g .. 4g+3 for g = t + 256u, u < NG, so for
+// each u the four waves hold 1024 consecutive entries, wave after wave and
+// lane after lane: ascending order is (u, wave, lane, e).  The first
+// sel_reg_entries(NG) entries and NG/2 * 256 cutoffs of the row's lists are
+// requested at the kernel's start, before the query's length is known (they
+// lie inside the row's region of the workspace whatever the length; entries
+// past the row's own lists are masked once it is known).
+__host__ __device__ constexpr int sel_reg_entries(int NG) { return 4 * NG * kSelThreads; }
+static_assert(sel_reg_entries(8) / 8 <= 4 * kSelThreads,
+              "a list of sel_reg_entries(NG) entries has at most NG/2 * 256 chunks (>= 8 entries each)");
+template <int NG>
 struct SelPre {
-    uint4 k[kSelRegGroups];
-    uint32_t l[kSelRegGroups];
-    uint32_t c[kSelRegCuts];
+    static_assert(NG == 4 || NG == 8, "register groups");
+    uint4 k[NG];
+    uint32_t l[NG];
+    uint32_t c[NG / 2];
     uint32_t mode;                                   // the lists' form (qsa_lists.hpp)
 };
 
-__device__ __forceinline__ void sel_prefetch(const AttnArgs &A, int64_t i, SelPre &pf) {
+template <int NG>
+__device__ __forceinline__ void sel_prefetch(const AttnArgs &A, int64_t i, SelPre<NG> &pf) {
+    constexpr int kSelRegEntries = sel_reg_entries(NG), kSelRegGroups = NG, kSelRegCuts = NG / 2;
     const uint4 *__restrict__ gk = reinterpret_cast<const uint4 *>(A.la.keys + i * A.la.stride);
     const uint32_t *__restrict__ gl = reinterpret_cast<const uint32_t *>(A.la.loc + i * A.la.stride);
     const uint32_t *__restrict__ gc = A.la.cut + i * A.la.cstride;
@@ -906,9 +909,11 @@ __device__ __forceinline__ uint32_t &u4_at(uint4 &v, int e) {
 // finished table.
 // `nslot`: entry M-1 is the block the row's newest token completed (key
 // nkey, lane nloc), which its chunk left to the selection.
+template <int NG>
 __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int nch, int M, uint32_t tab,
-                                                 SelScratch &X, SelPre &pf, bool nslot, uint32_t nkey,
+                                                 SelScratch &X, SelPre<NG> &pf, bool nslot, uint32_t nkey,
                                                  uint32_t nloc) {
+    constexpr int kSelRegGroups = NG, kSelRegCuts = NG / 2;
     const int K = A.K;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t kmin = 0xffffffffu, kmax = 0u, nreal = 0u, mcut = 0u;
@@ -1076,8 +1081,9 @@ __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int 
         if (lane == 0) X.tot[u][wave] = tot;
     }
     __syncthreads();                                                      // 4
-    // chunk of entry j: j / kk by a multiply (j < 2^12, 8 <= kk <= 64: the
-    // error j * (magic - 2^20 / kk) / 2^20 < 2^-8 stays below 1 / kk)
+    // chunk of entry j: j / kk by a multiply (j < 2^13, 8 <= kk <= 64:
+    // j * magic / 2^20 exceeds j / kk by less than j / 2^20 < 1 / kk, so the
+    // floor is exact)
     const uint32_t magic = (1u << 20) / (uint32_t)kk + 1u;
     uint32_t base = 0u;
 #pragma unroll
@@ -1114,7 +1120,7 @@ __device__ __forceinline__ bool select_part_regs(const AttnArgs &A, int kk, int 
 // cannot decide (staged in LDS when it fits).  The caller has emptied the
 // ring (no query rows in flight).  Fills LDS table slots 0 .. K-1 with
 // logical block ids and ends with a barrier.
-template <int D>
+template <int D, int kSelRegEntries>
 __device__ __forceinline__ void select_slow(const uint32_t *__restrict__ gk, const uint8_t *__restrict__ gl,
                                             const uint32_t *__restrict__ gc, const float *__restrict__ row, int64_t nb,
                                             int K, int kk, int nch, int M, uint32_t tab, uint8_t *ring_lds,
@@ -1262,9 +1268,9 @@ __device__ __forceinline__ void select_slow(const uint32_t *__restrict__ gk, con
 // slots 0 .. K-1; a last pass copies the row out and translates the part.
 // `q_in_ring`: the query rows' loads into the ring's last slots are in
 // flight; a path that uses the whole ring waits for them and clears it.
-template <int D>
+template <int D, int NG>
 __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int seq, int64_t L, int p_beg, int p_end,
-                                            bool designated, uint32_t tab, uint8_t *ring_lds, SelPre &pf,
+                                            bool designated, uint32_t tab, uint8_t *ring_lds, SelPre<NG> &pf,
                                             bool &q_in_ring) {
     const int64_t nb = L >> A.log2r;
     SelScratch &X = *reinterpret_cast<SelScratch *>(ring_lds);
@@ -1291,14 +1297,15 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
     const uint32_t nkey = nslot ? list_order_key(A.scores[i * A.ld + nb - 1]) : 0u;
     const uint32_t nloc = (uint32_t)((nb - 1) & (kListChunk - 1));
     bool done = false;
-    if (M <= kSelRegEntries) done = select_part_regs(A, kk, nch, M, tab, X, pf, nslot, nkey, nloc);
+    if (M <= sel_reg_entries(NG)) done = select_part_regs<NG>(A, kk, nch, M, tab, X, pf, nslot, nkey, nloc);
     if (!done) {
         if (q_in_ring) {                                      // the slow paths use the whole ring
             wait_vmcnt<0>();                                  // this wave's query loads landed,
             __syncthreads();                                  // and every other wave's
             q_in_ring = false;
         }
-        select_slow<D>(A.la.keys + i * A.la.stride, A.la.loc + i * A.la.stride, A.la.cut + i * A.la.cstride,
+        select_slow<D, sel_reg_entries(NG)>(A.la.keys + i * A.la.stride, A.la.loc + i * A.la.stride,
+                                            A.la.cut + i * A.la.cstride,
                        A.scores + i * A.ld, nb, K, kk, nch, M, tab, ring_lds, nslot, nkey, nloc);
     }
     // slots 0 .. K-1 hold the selection (nb > K): the idx row, and the part
@@ -1329,7 +1336,7 @@ __device__ __forceinline__ void select_part(const AttnArgs &A, int64_t i, int se
 //      gfx950 transposed LDS load (ds_read_b64_tr_b16: lane i of each 16-lane
 //      group gets column i of the four rows its group points at).
 //  Lane l accumulates O^T for head l%16, dims 16m + 4(l/16) + 0..3, m < 8.
-template <int D, bool BIG, bool SELECT>
+template <int D, bool BIG, bool SELECT, int NG = 4>
 __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) {
     static_assert(BIG || !SELECT, "the in-kernel selection fills an LDS slot table");
     extern __shared__ __align__(16) uint8_t dyn_lds[];
@@ -1362,10 +1369,10 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     };
     // SELECT: the lists and the query rows are requested first; neither
     // depends on the query's length, so their latency overlaps the offsets'.
-    SelPre pf;
+    SelPre<NG> pf;
     bool q_in_ring = false;
     if constexpr (SELECT) {
-        sel_prefetch(A, i, pf);
+        sel_prefetch<NG>(A, i, pf);
         load_q();
         q_in_ring = true;
     }
@@ -1417,7 +1424,7 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
         const int p_end = min(p_beg + per, (int)nsel);
         const uint32_t sel_tab = lds_addr(dyn_lds + kWgWaves * D * kSlotBytes);   // slot p = position p
         if (nb > 0)
-            select_part<D>(A, i, qp.seq, qp.L, p_beg, p_end, g == 0 && c == 0, sel_tab, dyn_lds, pf, q_in_ring);
+            select_part<D, NG>(A, i, qp.seq, qp.L, p_beg, p_end, g == 0 && c == 0, sel_tab, dyn_lds, pf, q_in_ring);
         else if (g == 0 && c == 0)
             for (int j = threadIdx.x; j < A.K; j += kSelThreads) A.idx_out[i * (int64_t)A.K + j] = -1;
         big_tab = sel_tab + 4u * (uint32_t)s_beg;
@@ -1648,7 +1655,7 @@ __device__ __forceinline__ void attn_decode_mfma_body(const AttnArgs &A, int G) 
     }
 }
 
-template <int D, bool BIG, bool SELECT>
+template <int D, bool BIG, bool SELECT, int NG = 4>
 __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(AttnArgs A, int G, LayerPtrs Lp) {
     if (gridDim.y > 1) {
         const int l = blockIdx.y;
@@ -1656,7 +1663,7 @@ __global__ __launch_bounds__(kWgWaves * kWave) void attn_decode_mfma_kernel(Attn
         A.ws_o += l * Lp.ws_stride;
         if (A.ws_ml) A.ws_ml += l * Lp.ws_stride;
     }
-    attn_decode_mfma_body<D, BIG, SELECT>(A, G);
+    attn_decode_mfma_body<D, BIG, SELECT, NG>(A, G);
 }
 
 // Merge part partials: one wave per (query, head); lane s < n_part reads
@@ -1730,14 +1737,14 @@ constexpr int kDecodeWgPerCu = 2;
 
 int ring_depth(int64_t workgroups) { return workgroups <= cu_count() ? 4 : 2; }
 
-template <int D, bool BIG, bool SELECT = false>
+template <int D, bool BIG, bool SELECT = false, int NG = 4>
 hipError_t launch_decode_mfma(const AttnArgs &A, int G, dim3 grid, const LayerPtrs &Lp, hipStream_t st) {
     // SELECT: the table holds the whole selection (slot p = position p) and a
     // wave reads up to kBigTabSlots slots past its first one
     const size_t lds = (size_t)kWgWaves * (D * kSlotBytes + (BIG ? kBigTabBytes : 0)) + (SELECT ? kBigTabBytes : 0);
-    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D, BIG, SELECT>, (int)lds);
+    const hipError_t attr = enable_dyn_lds((const void *)attn_decode_mfma_kernel<D, BIG, SELECT, NG>, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, BIG, SELECT>), grid, dim3(kWgWaves * kWave), lds, st, A, G,
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, BIG, SELECT, NG>), grid, dim3(kWgWaves * kWave), lds, st, A, G,
                        Lp);
     return hipGetLastError();
 }
@@ -1800,6 +1807,7 @@ hipError_t launch_attn_t(const AttnArgs &A, int G, bool mfma, hipStream_t st, co
 
 }  // namespace
 
+#ifndef QSA_ATTN_WIDE_TU
 int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio, bool decode) {
     (void)b; (void)a;
     // Parts per query of the register-staged kernel (fp32, or bf16 rows past
@@ -1813,6 +1821,8 @@ int attn_num_splits(const qsa_batch &b, const qsa_attn &a, int budget, int ratio
     if (s < 1) s = 1;
     return s;
 }
+
+#endif  // QSA_ATTN_WIDE_TU
 
 namespace {
 // Parts per (query, KV head) of the matrix-core decode kernel: enough
@@ -1832,12 +1842,15 @@ int mfma_decode_parts(const qsa_batch &b, const qsa_attn &a, int budget, int rat
 }
 }  // namespace
 
+#ifndef QSA_ATTN_WIDE_TU
 size_t attn_workspace_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
     const int parts = attn_num_splits(b, a, budget, ratio, true);
     if (parts <= 1) return 0;
     const size_t rows = (size_t)b.total_q * (size_t)a.hq * (size_t)parts;
     return rows * (kD + 2) * sizeof(float) + 256;
 }
+
+#endif  // QSA_ATTN_WIDE_TU
 
 namespace {
 // Kernel arguments of one attention call; returns whether the matrix-core
@@ -1869,8 +1882,35 @@ bool attn_args(const qsa_attn &a, const int32_t *idx, int budget, int ratio, con
     A.ws_ml = A.n_part > 1 ? static_cast<float *>(ws) + rows * kD : nullptr;
     return mfma_path;
 }
+// Decode attention that selects from the lists, with NG register groups.
+template <int NG>
+hipError_t attn_select_impl(const qsa_attn &a, int budget, int ratio, const qsa_batch &b, const ListArgs &la,
+                            const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
+                            const qsa_paged_kv *pg, hipStream_t st) {
+    if (b.total_q == 0) return hipSuccess;
+    AttnArgs A{};
+    if (!attn_args(a, idx, budget, ratio, b, out, ws, true, pg, A)) return hipErrorNotSupported;
+    A.la = la;
+    A.scores = scores;
+    A.ld = ld;
+    A.idx_out = idx;
+    const int G = a.hq / a.hkv;
+    const dim3 grid((unsigned)(A.total_q * A.hkv * A.n_part));
+    const int D = ring_depth((int64_t)grid.x);
+    trace("attn decode with selection D=%d workgroups=%u parts=%d groups=%d", D, grid.x, A.n_part, NG);
+    const LayerPtrs none{};
+    hipError_t e = D == 4 ? launch_decode_mfma<4, true, true, NG>(A, G, grid, none, st)
+                          : launch_decode_mfma<2, true, true, NG>(A, G, grid, none, st);
+    if (e != hipSuccess || A.n_part == 1) return e;
+    const int64_t rows = A.total_q * A.hq;
+    dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves));
+    hipLaunchKernelGGL((attn_combine_kernel<true>), cgrid, dim3(kWgWaves * kWave), 0, st, A.ws_o, A.ws_ml, A.n_part,
+                       rows, A.out, none);
+    return hipGetLastError();
+}
 }  // namespace
 
+#ifndef QSA_ATTN_WIDE_TU
 hipError_t launch_attn(const qsa_attn &a, const int32_t *idx, int budget, int ratio,
                        const qsa_batch &b, void *out, void *ws, bool decode, const qsa_paged_kv *pg,
                        hipStream_t st) {
@@ -1922,26 +1962,18 @@ bool attn_select_supported(const qsa_batch &b, const qsa_attn &a, const qsa_page
 hipError_t launch_attn_select(const qsa_attn &a, int budget, int ratio, const qsa_batch &b, const ListArgs &la,
                               const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
                               const qsa_paged_kv *pg, hipStream_t st) {
-    if (b.total_q == 0) return hipSuccess;
-    AttnArgs A{};
-    if (!attn_args(a, idx, budget, ratio, b, out, ws, true, pg, A)) return hipErrorNotSupported;
-    A.la = la;
-    A.scores = scores;
-    A.ld = ld;
-    A.idx_out = idx;
-    const int G = a.hq / a.hkv;
-    const dim3 grid((unsigned)(A.total_q * A.hkv * A.n_part));
-    const int D = ring_depth((int64_t)grid.x);
-    trace("attn decode with selection D=%d workgroups=%u parts=%d", D, grid.x, A.n_part);
-    const LayerPtrs none{};
-    hipError_t e = D == 4 ? launch_decode_mfma<4, true, true>(A, G, grid, none, st)
-                          : launch_decode_mfma<2, true, true>(A, G, grid, none, st);
-    if (e != hipSuccess || A.n_part == 1) return e;
-    const int64_t rows = A.total_q * A.hq;
-    dim3 cgrid((unsigned)((rows + kWgWaves - 1) / kWgWaves));
-    hipLaunchKernelGGL((attn_combine_kernel<true>), cgrid, dim3(kWgWaves * kWave), 0, st, A.ws_o, A.ws_ml, A.n_part,
-                       rows, A.out, none);
-    return hipGetLastError();
+    // batches whose rows of the longest length list more than 4096 entries
+    // (32768 blocks at K = 2048) take the 8-group register path, built in a
+    // translation unit of its own: instantiated here, the 8-group kernels
+    // changed the register allocation of the 4-group ones (a third more
+    // scalar spills).  The count is not monotone in the length, so shorter
+    // rows can list more than the longest (up to 6656 entries for rows under
+    // 32768 blocks at K = 512); those take the LDS path of either kernel.
+    const int64_t nb_max = b.max_kv_len / ratio;
+    const int64_t m_max = nb_max > la.K ? (nb_max + kListChunk - 1) / kListChunk * list_len(nb_max, la.K) : 0;
+    if (m_max > sel_reg_entries(4))
+        return launch_attn_select_wide(a, budget, ratio, b, la, scores, ld, idx, out, ws, pg, st);
+    return attn_select_impl<4>(a, budget, ratio, b, la, scores, ld, idx, out, ws, pg, st);
 }
 
 size_t attn_layer_stride_bytes(const qsa_batch &b, const qsa_attn &a, int budget, int ratio) {
@@ -1974,5 +2006,7 @@ hipError_t launch_attn_layers(const qsa_attn *layers, int n_layers, const int32_
           layers[0].hkv, G, A.n_part);
     return launch_attn_t<true>(A, G, true, st, Lp, n_layers);
 }
+
+#endif  // QSA_ATTN_WIDE_TU
 
 }  // namespace qsa

@@ -66,6 +66,11 @@ bool attn_select_supported(const qsa_batch &b, const qsa_attn &a, const qsa_page
 hipError_t launch_attn_select(const qsa_attn &a, int budget, int ratio, const qsa_batch &b, const ListArgs &la,
                               const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
                               const qsa_paged_kv *pg, hipStream_t st);
+// The same for lists of more than 4096 entries per row (K = 2048 rows), in
+// a translation unit of its own (qsa_attn_wide.hip).
+hipError_t launch_attn_select_wide(const qsa_attn &a, int budget, int ratio, const qsa_batch &b, const ListArgs &la,
+                                   const float *scores, int64_t ld, int32_t *idx, void *out, void *ws,
+                                   const qsa_paged_kv *pg, hipStream_t st);
 // The lists of a score + select call (workspace carve-up shared by the calls
 // that take them), and the list finish alone.
 ListArgs list_args(const qsa_batch &b, int budget, int ratio, void *ws);

@@ -130,8 +130,10 @@ def test_duplicated_keys_and_negative_weights():
 
 
 def test_k2048_long_rows_exceed_the_lds_lists():
+    # K = 2048: rows of 32768 and 15000 blocks list 7680 and 5640 entries (the
+    # 8-group register path); 65536 blocks list 13312 (the lists staged in LDS)
     sp = dataclasses.replace(W.LONG_DECODE, hq=8, hkv=1, budget=8192)
-    _run(W.make(sp, lens=[131072 + 3, 60000, 8196, 8195, 100], seed=606))
+    _run(W.make(sp, lens=[131072 + 3, 262144 + 1, 60000, 8196, 8195, 100], seed=606))
 
 
 def test_fp32_and_large_batches_run_the_separate_kernels():
