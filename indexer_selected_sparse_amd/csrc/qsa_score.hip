@@ -422,15 +422,75 @@ __device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * KeyBits<KT>::v
     }
 }
 
+// Decode batches (one query per sequence, at most kFlatMaxRows rows) number
+// only the visible 256-block groups: workgroup g scores the g-th visible
+// group in (row, group) order, and the workgroups past the last one exit.
+// The grid is sized for every row at the longest length.  Numbered densely
+// by (row, group), its empty workgroups sat among the visible ones, and the
+// CUs that the launch's single round of workgroups gave to the longest rows
+// scored four groups while others scored one.  Each wave finds its group
+// from one round of vector loads of the offsets (lane l: rows 4l .. 4l+3)
+// and a scan of the rows' group counts over the lanes.
+constexpr int kFlatMaxRows = 4 * kWave;
+__device__ __forceinline__ int64_t readlane_i64(int64_t x, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)x, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), lane);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ bool flat_group(const int64_t *__restrict__ kv_off, const int64_t *__restrict__ blk_off,
+                                           int num_seqs, int log2r, uint32_t g, int64_t &i, int64_t &by,
+                                           QueryPos &qp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int64_t o[5], bo[4];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) o[k] = 4 * lane + k <= num_seqs ? kv_off[4 * lane + k] : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bo[k] = blk_off && 4 * lane + k < num_seqs ? blk_off[4 * lane + k] : 0;
+    uint32_t c[4], sum = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t nb = 4 * lane + k < num_seqs ? (o[k + 1] - o[k]) >> log2r : 0;
+        c[k] = (uint32_t)((nb + kExactThreads - 1) / kExactThreads);
+        sum += c[k];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint64_t m = __ballot(incl > g);
+    if (m == 0u) return false;                       // past the last visible group (uniform)
+    // lane `src` (the first whose rows reach past g) holds the row; each
+    // lane works out which of its rows that would be, and src's answer is read
+    const int src = (int)__builtin_ctzll(m);
+    uint32_t kr = 3u, gy = 0u;
+    int64_t r0 = o[3], len = o[4] - o[3], b0 = bo[3];
+#pragma unroll
+    for (int k = 3; k >= 0; --k) {
+        uint32_t before = incl - sum;
+#pragma unroll
+        for (int j = 0; j < k; ++j) before += c[j];
+        if (g >= before && g < before + c[k]) {
+            kr = (uint32_t)k;
+            gy = g - before;
+            r0 = o[k];
+            len = o[k + 1] - o[k];
+            b0 = bo[k];
+        }
+    }
+    const int k = __builtin_amdgcn_readlane((int)kr, src);
+    i = 4 * (int64_t)src + k;
+    by = (uint32_t)__builtin_amdgcn_readlane((int)gy, src);
+    qp.seq = (int)i;
+    qp.kv_row0 = readlane_i64(r0, src);
+    qp.L = readlane_i64(len, src);
+    qp.blk_row0 = readlane_i64(b0, src);
+    return true;
+}
+
 // SKIP_NEW: leave out the block the query's last token completes (L a
 // multiple of the ratio), which the fused append scores itself.
 template <typename KT, int D, int H, bool SKIP_NEW>
 __device__ __forceinline__ void score_exact_body(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
-    const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
-    const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld, const PageMap &pm, int64_t i, int64_t by,
-    const ListArgs &la) {
+    const void *__restrict__ kc_scale, int log2r, float *__restrict__ scores, int64_t ld, const PageMap &pm,
+    const QueryPos &qp, int64_t i, int64_t by, const ListArgs &la) {
     constexpr bool kE4M3 = std::is_same<KT, uint8_t>::value;
     constexpr bool kFP4 = std::is_same<KT, Fp4x2>::value;
     constexpr int CH = kExactChunk;
@@ -439,9 +499,6 @@ __device__ __forceinline__ void score_exact_body(
     constexpr int QW = CH / 2;                           // query dwords per (chunk, head)
     static_assert(D % CH == 0 && (LPC == 1 || LPC == 2 || LPC == 4) && QW == 16, "chunk layout");
     static_assert((NCH - 1) * LPC < 64, "loads in flight fit the wait counter");
-    // the lists' form, for the selection that reads them
-    if (la.mode && i == 0 && by == 0 && threadIdx.x == 0) *la.mode = SKIP_NEW ? kListNewBlockSlot : 0u;
-    const QueryPos qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
     const int64_t nb = qp.L >> log2r;
     const int64_t b = by * kExactThreads + threadIdx.x;
     if (by * kExactThreads >= nb) return;   // whole workgroup invisible
@@ -559,9 +616,18 @@ __global__ __launch_bounds__(kExactThreads) void score_exact_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const KT *__restrict__ kc,
     const void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int num_seqs,
-    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, ListArgs la) {
-    score_exact_body<KT, D, H, false>(q_idx, w, kc, kc_scale, kv_off, blk_off, q_off, num_seqs, log2r, scores,
-                                      ld, pm, blockIdx.x, blockIdx.y, la);
+    int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, ListArgs la, int flat) {
+    if (la.mode && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *la.mode = 0u;   // plain lists
+    int64_t i, by;
+    QueryPos qp;
+    if (flat) {
+        if (!flat_group(kv_off, blk_off, num_seqs, log2r, blockIdx.x, i, by, qp)) return;
+    } else {
+        i = blockIdx.x;
+        by = blockIdx.y;
+        qp = query_pos(kv_off, blk_off, q_off, num_seqs, i);
+    }
+    score_exact_body<KT, D, H, false>(q_idx, w, kc, kc_scale, log2r, scores, ld, pm, qp, i, by, la);
 }
 
 // Canonical score of one block whose key a wave holds (lane l: dims
@@ -603,8 +669,10 @@ __device__ __forceinline__ void score_one_block(const float (&dec)[D / kWave], f
 
 // Append + canonical score in one launch, for a decode step (one new token
 // and one query per sequence).  Workgroups x < num_seqs score query x as
-// score_exact_kernel does, except the block the new token completes; the
-// workgroups after them (y = 0) run one append wave per sequence
+// score_exact_kernel does, except the block the new token completes (with
+// `flat`, the scoring workgroups take the visible groups as flat_group
+// numbers them, after the append workgroups); the workgroups after them
+// (y = 0) run one append wave per sequence
 // (append_one), which writes that block's compressed key (or, when the
 // append could not, takes the key already stored) and scores the block with
 // the same arithmetic.  Nothing else the scorer reads is written here, so the
@@ -614,17 +682,36 @@ __global__ __launch_bounds__(kExactThreads) void ingest_score_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KT *__restrict__ kc,
     void *__restrict__ kc_scale, const int64_t *__restrict__ kv_off, const int64_t *__restrict__ blk_off,
     int num_seqs, int log2r, float *__restrict__ scores, int64_t ld, PageMap pm, const TIn *__restrict__ k_new,
-    float inv_ratio, RingArgs ring, KvArgs kv, int32_t *__restrict__ status, ListArgs la) {
-    if ((int)blockIdx.x < num_seqs) {
-        score_exact_body<KT, D, H, true>(q_idx, w, kc, kc_scale, kv_off, blk_off, nullptr, num_seqs, log2r,
-                                         scores, ld, pm, blockIdx.x, blockIdx.y, la);
-        return;
+    float inv_ratio, RingArgs ring, KvArgs kv, int32_t *__restrict__ status, ListArgs la, int flat) {
+    constexpr int kWaves = kExactThreads / kWave;
+    // the lists' form, for the selection that reads them
+    if (la.mode && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *la.mode = kListNewBlockSlot;
+    int ab;   // append workgroup
+    if (flat) {
+        // the append workgroups first, then the visible groups (flat_group)
+        const int na = (num_seqs + kWaves - 1) / kWaves;
+        if ((int)blockIdx.x >= na) {
+            int64_t i, by;
+            QueryPos qp;
+            if (!flat_group(kv_off, blk_off, num_seqs, log2r, blockIdx.x - (uint32_t)na, i, by, qp)) return;
+            score_exact_body<KT, D, H, true>(q_idx, w, kc, kc_scale, log2r, scores, ld, pm, qp, i, by, la);
+            return;
+        }
+        ab = (int)blockIdx.x;
+    } else {
+        if ((int)blockIdx.x < num_seqs) {
+            const QueryPos qp = query_pos(kv_off, blk_off, nullptr, num_seqs, blockIdx.x);
+            score_exact_body<KT, D, H, true>(q_idx, w, kc, kc_scale, log2r, scores, ld, pm, qp, blockIdx.x,
+                                             blockIdx.y, la);
+            return;
+        }
+        if (blockIdx.y != 0) return;
+        ab = (int)blockIdx.x - num_seqs;
     }
-    if (blockIdx.y != 0) return;
     constexpr int DPL = D / kWave;
     constexpr int KC = std::is_same<KT, Fp4x2>::value ? 3 : (std::is_same<KT, uint8_t>::value ? 2 : 1);
     const int lane = threadIdx.x & (kWave - 1);
-    const int sq = (int)(blockIdx.x - num_seqs) * (kExactThreads / kWave) + (int)(threadIdx.x / kWave);
+    const int sq = ab * kWaves + (int)(threadIdx.x / kWave);
     if (sq >= num_seqs) return;
     AppendOut<DPL> a = append_one<TIn, DPL, KC>(k_new, kv_off, blk_off, sq, log2r, inv_ratio, ring, kc, kc_scale,
                                                 kv, status, pm, lane);
@@ -643,11 +730,17 @@ hipError_t dispatch_h(const qsa_indexer &ix, int log2r, const qsa_batch &b, floa
     const int64_t max_nb = b.max_kv_len >> log2r;
     if constexpr (kExact) {
         grid.y = (unsigned)((max_nb + kExactThreads - 1) / kExactThreads);
+        // decode batches: only the visible groups, numbered over one grid row
+        const int flat = b.q_offsets == nullptr && b.total_q == b.num_seqs && b.num_seqs <= kFlatMaxRows;
+        if (flat) {
+            grid.x *= grid.y;
+            grid.y = 1;
+        }
         dim3 block(kExactThreads);
 #define QSA_SCORE_LAUNCH(HH)                                                                       \
     hipLaunchKernelGGL((score_exact_kernel<KT, D, HH>), grid, block, 0, st, q, ix.w, kc,           \
                        ix.kc_scale, b.kv_offsets, b.blk_offsets, b.q_offsets, b.num_seqs, log2r,  \
-                       scores, ld, pm, la)
+                       scores, ld, pm, la, flat)
         switch (ix.h_idx) {
         case 1: QSA_SCORE_LAUNCH(1); break;
         case 2: QSA_SCORE_LAUNCH(2); break;
@@ -697,13 +790,15 @@ struct FusedArgs {
     KvArgs kv;
     int32_t *status;
     ListArgs la;
+    int flat;   // the scoring workgroups number only the visible groups
 };
 
 template <typename KT, int D, int H, typename TIn>
 hipError_t fused_launch(const FusedArgs &f, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((ingest_score_kernel<KT, D, H, TIn>), grid, dim3(kExactThreads), 0, st, f.q_idx, f.w,
                        static_cast<KT *>(f.kc), f.kc_scale, f.kv_off, f.blk_off, f.num_seqs, f.log2r, f.scores,
-                       f.ld, f.pm, static_cast<const TIn *>(f.k_new), f.inv_ratio, f.ring, f.kv, f.status, f.la);
+                       f.ld, f.pm, static_cast<const TIn *>(f.k_new), f.inv_ratio, f.ring, f.kv, f.status, f.la,
+                       f.flat);
     return hipGetLastError();
 }
 
@@ -818,11 +913,15 @@ hipError_t launch_ingest_score(const void *k_new, int k_dtype, int ratio, const 
     }
     f.status = status;
     // x: one scoring workgroup per query, then one append wave per sequence;
-    // y: the scorer's 256-block groups (at least one, for the appends)
+    // y: the scorer's 256-block groups (at least one, for the appends).  Up
+    // to kFlatMaxRows sequences: x alone, the append workgroups and then
+    // one scoring workgroup per (sequence, group) slot
     const int64_t max_nb = b.max_kv_len >> f.log2r;
     const int waves = kExactThreads / kWave;
-    dim3 grid((unsigned)(b.num_seqs + (b.num_seqs + waves - 1) / waves),
-              (unsigned)(max_nb > 0 ? (max_nb + kExactThreads - 1) / kExactThreads : 1));
+    const unsigned ny = (unsigned)(max_nb > 0 ? (max_nb + kExactThreads - 1) / kExactThreads : 1);
+    const unsigned na = (unsigned)((b.num_seqs + waves - 1) / waves);
+    f.flat = b.num_seqs <= kFlatMaxRows;
+    dim3 grid(f.flat ? na + (unsigned)b.num_seqs * ny : (unsigned)b.num_seqs + na, f.flat ? 1u : ny);
     trace("ingest_score grid=(%u,%u) h_idx=%d d_idx=%d kc=%d kv=%d", grid.x, grid.y, ix.h_idx, ix.d_idx,
           ix.kc_dtype, f.kv.row_bytes);
     const bool kb = k_dtype == QSA_BF16;
