@@ -428,9 +428,9 @@ __device__ __forceinline__ void widen_chunk(const u32x4 (&u)[CH * KeyBits<KT>::v
 // The grid is sized for every row at the longest length.  Numbered densely
 // by (row, group), its empty workgroups sat among the visible ones, and the
 // CUs that the launch's single round of workgroups gave to the longest rows
-// scored four groups while others scored one.  Each wave finds its group
-// from one round of vector loads of the offsets (lane l: rows 4l .. 4l+3)
-// and a scan of the rows' group counts over the lanes.
+// scored four groups while others scored one.  Each wave finds its group by
+// itself: 64 rows at a time (lane l: row r0 + l), one round of vector loads
+// of the offsets, a lane scan of the rows' group counts and a ballot.
 constexpr int kFlatMaxRows = 4 * kWave;
 __device__ __forceinline__ int64_t readlane_i64(int64_t x, int lane) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)x, lane);
@@ -441,47 +441,29 @@ __device__ __forceinline__ bool flat_group(const int64_t *__restrict__ kv_off, c
                                            int num_seqs, int log2r, uint32_t g, int64_t &i, int64_t &by,
                                            QueryPos &qp) {
     const int lane = threadIdx.x & (kWave - 1);
-    int64_t o[5], bo[4];
-#pragma unroll
-    for (int k = 0; k < 5; ++k) o[k] = 4 * lane + k <= num_seqs ? kv_off[4 * lane + k] : 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bo[k] = blk_off && 4 * lane + k < num_seqs ? blk_off[4 * lane + k] : 0;
-    uint32_t c[4], sum = 0u;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t nb = 4 * lane + k < num_seqs ? (o[k + 1] - o[k]) >> log2r : 0;
-        c[k] = (uint32_t)((nb + kExactThreads - 1) / kExactThreads);
-        sum += c[k];
-    }
-    const uint32_t incl = wave_incl_scan(sum);
-    const uint64_t m = __ballot(incl > g);
-    if (m == 0u) return false;                       // past the last visible group (uniform)
-    // lane `src` (the first whose rows reach past g) holds the row; each
-    // lane works out which of its rows that would be, and src's answer is read
-    const int src = (int)__builtin_ctzll(m);
-    uint32_t kr = 3u, gy = 0u;
-    int64_t r0 = o[3], len = o[4] - o[3], b0 = bo[3];
-#pragma unroll
-    for (int k = 3; k >= 0; --k) {
-        uint32_t before = incl - sum;
-#pragma unroll
-        for (int j = 0; j < k; ++j) before += c[j];
-        if (g >= before && g < before + c[k]) {
-            kr = (uint32_t)k;
-            gy = g - before;
-            r0 = o[k];
-            len = o[k + 1] - o[k];
-            b0 = bo[k];
+    uint32_t base = 0u;                              // groups of the rows before r0
+    for (int r0 = 0; r0 < num_seqs; r0 += kWave) {
+        const int row = r0 + lane;
+        const bool in = row < num_seqs;
+        const int64_t o0 = in ? kv_off[row] : 0;
+        const int64_t o1 = in ? kv_off[row + 1] : 0;
+        const int64_t b0 = in && blk_off ? blk_off[row] : 0;
+        const uint32_t c = (uint32_t)((((o1 - o0) >> log2r) + kExactThreads - 1) / kExactThreads);
+        const uint32_t incl = base + wave_incl_scan(c);
+        const uint64_t m = __ballot(incl > g);
+        if (m != 0u) {                               // uniform
+            const int src = (int)__builtin_ctzll(m);
+            i = r0 + src;
+            by = g - (uint32_t)__builtin_amdgcn_readlane((int)(incl - c), src);
+            qp.seq = (int)i;
+            qp.kv_row0 = readlane_i64(o0, src);
+            qp.L = readlane_i64(o1 - o0, src);
+            qp.blk_row0 = readlane_i64(b0, src);
+            return true;
         }
+        base = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
     }
-    const int k = __builtin_amdgcn_readlane((int)kr, src);
-    i = 4 * (int64_t)src + k;
-    by = (uint32_t)__builtin_amdgcn_readlane((int)gy, src);
-    qp.seq = (int)i;
-    qp.kv_row0 = readlane_i64(r0, src);
-    qp.L = readlane_i64(len, src);
-    qp.blk_row0 = readlane_i64(b0, src);
-    return true;
+    return false;                                    // past the last visible group
 }
 
 // SKIP_NEW: leave out the block the query's last token completes (L a

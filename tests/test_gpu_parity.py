@@ -177,6 +177,37 @@ def test_full_size_chunked_prefill_all_queries():
     _print(f"[parity] full chunked prefill: ok, worst err/limit = {worst:.3f}")
 
 
+@pytest.mark.parametrize("n", [255, 256, 257])
+def test_decode_batches_at_the_scorer_row_limit(n):
+    # decode batches of up to 256 rows score only their visible 256-block
+    # groups, each wave finding its (row, group) from the offsets of four rows
+    # per lane; 257 rows keep the dense (row, group) grid.  The rows mix no
+    # complete block, exact multiples of 256 blocks, one block past them and
+    # ragged lengths, so rows without groups sit between others.  Scores are
+    # first set to NaN, so a group that no workgroup scored shows in the bits.
+    from indexer_selected_sparse_amd import pipeline
+    from tests.parity import check_scores
+    sp = dataclasses.replace(W.BATCHED_DECODE, hq=8, hkv=2, budget=64)
+    rng = np.random.default_rng(40 + n)
+    pick = [1, 3, 4 * 256, 4 * 256 + 3, 4 * 256 + 4, 4 * 512, 4 * 768 + 2]
+    lens = [int(pick[j % len(pick)]) if j % 3 else int(rng.integers(1, 7000)) for j in range(n)]
+    wl = W.make(sp, lens=lens, seed=40 + n)
+    dp = pipeline.upload(wl, "cuda")
+    dp.compress()
+    dp.scores.fill_(float("nan"))
+    dp.idx.fill_(-9)
+    dp.step()
+    torch.cuda.synchronize()
+    q = np.arange(wl.total_q)
+    ref = oracle.run_workload(wl, want_scores=True)
+    res = {"scores": dp.scores.cpu().numpy(), "idx": dp.idx.cpu().numpy(),
+           "out": dp.out.float().cpu().numpy().astype(np.float64)}
+    check_scores(wl, res, ref, q)
+    check_idx(res, ref, q)
+    check_out(wl, res, ref, q)
+    _print(f"[parity] {n} decode rows: ok")
+
+
 def test_decode_workspace_reused_across_batch_shapes():
     # one decode workspace shared by batches of different shapes, used
     # alternately: each shape must reproduce its first result bit for bit
