@@ -69,6 +69,7 @@ struct AttnArgs {
     const float *scores;
     int64_t ld;
     int32_t *idx_out;
+    int32_t sel_pref;        // list entries a row can hold at most (requested up front)
 };
 
 // Several layers that share one selection in one launch (blockIdx.y = layer):
@@ -880,7 +881,8 @@ __device__ __forceinline__ void sel_prefetch(const AttnArgs &A, int64_t i, SelPr
     const uint4 *__restrict__ gk = reinterpret_cast<const uint4 *>(A.la.keys + i * A.la.stride);
     const uint32_t *__restrict__ gl = reinterpret_cast<const uint32_t *>(A.la.loc + i * A.la.stride);
     const uint32_t *__restrict__ gc = A.la.cut + i * A.la.cstride;
-    const int s4 = (int)(A.la.stride / 4 < kSelRegEntries / 4 ? A.la.stride / 4 : kSelRegEntries / 4);
+    const int pref = A.sel_pref < kSelRegEntries ? A.sel_pref : kSelRegEntries;
+    const int s4 = (int)(A.la.stride / 4 < (pref + 3) / 4 ? A.la.stride / 4 : (pref + 3) / 4);
     const int nc = (int)(A.la.cstride < kSelRegCuts * kSelThreads ? A.la.cstride : kSelRegCuts * kSelThreads);
 #pragma unroll
     for (int u = 0; u < kSelRegGroups; ++u) {
@@ -1894,6 +1896,10 @@ hipError_t attn_select_impl(const qsa_attn &a, int budget, int ratio, const qsa_
     A.scores = scores;
     A.ld = ld;
     A.idx_out = idx;
+    // only the entries a row of at most max_kv_len tokens can list are
+    // requested before the row's length is known
+    const int64_t pref = list_max_entries(b.max_kv_len / ratio, la.K);
+    A.sel_pref = (int32_t)(pref < sel_reg_entries(NG) ? pref : sel_reg_entries(NG));
     const int G = a.hq / a.hkv;
     const dim3 grid((unsigned)(A.total_q * A.hkv * A.n_part));
     const int D = ring_depth((int64_t)grid.x);

@@ -50,6 +50,28 @@ __host__ __device__ inline int list_len(int64_t nb, int K) {
     return k > (uint32_t)kListChunk ? kListChunk : (int)k;
 }
 
+// The most entries one row's lists can hold over rows of at most nb_max
+// blocks (rows of at most K blocks list nothing).  ceil(nb / 64) *
+// list_len(nb, K) is not monotone in nb, but list_len depends on nb only
+// through m = ceil(64 K / nb), which for nb > K takes the values 1 .. 64;
+// within one value of m the count is largest at the largest nb.
+inline int64_t list_max_entries(int64_t nb_max, int K) {
+    if (K <= 0) return 0;
+    const int64_t t = (int64_t)kListChunk * K;
+    int64_t best = 0;
+    for (int64_t m = 1; m <= kListChunk; ++m) {
+        // nb with ceil(t / nb) == m: t / m <= nb < t / (m - 1)
+        const int64_t lo = (t + m - 1) / m;
+        int64_t hi = m == 1 ? nb_max : (t + m - 2) / (m - 1) - 1;
+        if (hi > nb_max) hi = nb_max;
+        const int64_t first = lo > K ? lo : (int64_t)K + 1;
+        if (first > hi) continue;
+        const int64_t n = ((hi + kListChunk - 1) / kListChunk) * list_len(hi, K);
+        if (n > best) best = n;
+    }
+    return best;
+}
+
 // Lists of one call: row i's entries start at i * stride, its cutoffs at
 // i * cstride (one per chunk).  keys == nullptr: no lists.  *mode: 0, or
 // kListNewBlockSlot when rows whose newest token completes a block leave
