@@ -650,15 +650,16 @@ __device__ __forceinline__ void score_one_block(const float (&dec)[D / kWave], f
 }
 
 // Append + canonical score in one launch, for a decode step (one new token
-// and one query per sequence).  Workgroups x < num_seqs score query x as
-// score_exact_kernel does, except the block the new token completes (with
-// `flat`, the scoring workgroups take the visible groups as flat_group
-// numbers them, after the append workgroups); the workgroups after them
-// (y = 0) run one append wave per sequence
+// and one query per sequence).  Scoring workgroups score a (query, 256-block
+// group) as score_exact_kernel does, except the block the new token
+// completes; append workgroups run one append wave per sequence
 // (append_one), which writes that block's compressed key (or, when the
 // append could not, takes the key already stored) and scores the block with
 // the same arithmetic.  Nothing else the scorer reads is written here, so the
-// result equals the append followed by the score, bit for bit.
+// result equals the append followed by the score, bit for bit.  Grid: with
+// `flat`, one row, the append workgroups first and then the visible groups
+// as flat_group numbers them; otherwise x < num_seqs scores query x (y: the
+// group) and the x after them (y = 0) append.
 template <typename KT, int D, int H, typename TIn>
 __global__ __launch_bounds__(kExactThreads) void ingest_score_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KT *__restrict__ kc,
