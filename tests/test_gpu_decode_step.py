@@ -94,6 +94,17 @@ def test_key_formats_and_ragged_rows(kc_dtype):
     _run(W.make(sp, lens=[9001, 2051, 2, 530, 518, 4099, 20002, 3], seed=601))
 
 
+def test_shorter_rows_list_more_than_the_longest():
+    # each attention workgroup requests, before its row's length is known,
+    # the most entries any row of at most max_kv_len tokens can list.  At
+    # K = 512 the longest row here (8292 blocks) lists 1950 entries, while
+    # rows of 8191 and 8190 blocks list 2560 (20 per chunk against 15), the
+    # most of any length up to 8292: they fill the request exactly, and a
+    # request sized by the longest row would cut off their last chunks
+    _run(W.make(W.BATCHED_DECODE, lens=[4 * 8292, 4 * 8191 + 3, 4 * 8190, 4 * 6554, 4 * 6553 + 1, 20000],
+                seed=609))
+
+
 def test_paged_caches():
     sp = dataclasses.replace(W.LONG_DECODE, hq=16, hkv=2, budget=1024)
     _run(W.make(sp, lens=[20000, 7001, 1024 * 4 + 2], seed=602), paged=128)
