@@ -20,8 +20,12 @@ namespace {
 constexpr int kCompressWaves = 4;        // waves per workgroup
 constexpr int kBlocksPerWave = 4;        // blocks a wave handles (loads issued together)
 
-// KC: 0 = fp32, 1 = bf16, 2 = e4m3 (+ scale)
-template <typename TIn, int DPL, int KC>
+// KC: 0 = fp32, 1 = bf16, 2 = e4m3 (+ scale), 3 = fp4 (+ scales).  R: the
+// ratio when known at compile time (4), else 0.  With R, all R rows of the
+// wave's blocks are requested before any is summed; with a runtime ratio
+// the rows of one block are summed before the next block's are requested,
+// and each block's loads wait behind the previous block's reduction and store.
+template <typename TIn, int DPL, int KC, int R>
 __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const TIn *__restrict__ k_idx, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ first_block, int log2_ratio,
@@ -38,6 +42,54 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     const int64_t b_base =
         ((int64_t)blockIdx.x * kCompressWaves + wave) * kBlocksPerWave;
 
+    if constexpr (R > 0) {
+        // the wave's blocks b_base .. b_base+3 that exist and are not before
+        // the first block to compress (uniform over the wave)
+        const int64_t b_lo = b_base > fb ? b_base : fb;
+        if (b_lo >= nb || b_lo >= b_base + kBlocksPerWave) return;
+        // rows first (page lookups), then every row load, then the sums: a
+        // lookup issued behind row loads would wait for all of them
+        int64_t in_row[kBlocksPerWave], out_row[kBlocksPerWave];
+        if (pm.table) {
+#pragma unroll
+            for (int u = 0; u < kBlocksPerWave; ++u) {
+                const int64_t b = b_base + u;
+                const int64_t bb = (b < nb && b >= fb) ? b : b_lo;   // a block that exists
+                in_row[u] = paged_row(pm, s, bb << log2_ratio, pm.log2_page);
+                out_row[u] = paged_row(pm, s, bb, pm.log2_page - log2_ratio);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kBlocksPerWave; ++u) {
+                const int64_t b = b_base + u;
+                const int64_t bb = (b < nb && b >= fb) ? b : b_lo;
+                in_row[u] = row0 + (bb << log2_ratio);
+                out_row[u] = out0 + bb;
+            }
+        }
+        float x[kBlocksPerWave][R][DPL];
+#pragma unroll
+        for (int u = 0; u < kBlocksPerWave; ++u) {
+            const TIn *src = k_idx + in_row[u] * D + lane * DPL;
+#pragma unroll
+            for (int j = 0; j < R; ++j) load_row<TIn, DPL>(src + (int64_t)j * D, x[u][j]);
+        }
+#pragma unroll
+        for (int u = 0; u < kBlocksPerWave; ++u) {
+            const int64_t b = b_base + u;
+            if (b >= nb || b < fb) continue;
+            float m[DPL];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < R; ++j) acc = acc + x[u][j][e];
+                m[e] = acc * inv_ratio;
+            }
+            store_kc<KC, DPL>(m, kc, kc_scale, out_row[u], lane);
+        }
+        return;
+    }
     for (int u = 0; u < kBlocksPerWave; ++u) {
         const int64_t b = b_base + u;
         if (b >= nb || b < fb) continue;
@@ -62,32 +114,32 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     }
 }
 
-template <typename TIn, int DPL>
+template <typename TIn, int DPL, int R>
 hipError_t dispatch_kc(const void *k_idx, const qsa_batch &b, const int64_t *fb, int log2r,
                        void *kc, int kc_dtype, void *kc_scale, const PageMap &pm, dim3 grid,
                        hipStream_t st) {
     const float inv = 1.0f / (float)(1 << log2r);
     const TIn *x = static_cast<const TIn *>(k_idx);
     dim3 block(kCompressWaves * kWave);
+#define QSA_COMPRESS_LAUNCH(KC)                                                                   \
+    hipLaunchKernelGGL((compress_kernel<TIn, DPL, KC, R>), grid, block, 0, st, x, b.kv_offsets,  \
+                       b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm)
     switch (kc_dtype) {
-    case QSA_F32:
-        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 0>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
-        break;
-    case QSA_BF16:
-        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 1>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
-        break;
-    case QSA_FP8_E4M3:
-        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 2>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
-        break;
-    default:
-        hipLaunchKernelGGL((compress_kernel<TIn, DPL, 3>), grid, block, 0, st, x, b.kv_offsets,
-                           b.blk_offsets, fb, log2r, inv, kc, kc_scale, pm);
-        break;
+    case QSA_F32: QSA_COMPRESS_LAUNCH(0); break;
+    case QSA_BF16: QSA_COMPRESS_LAUNCH(1); break;
+    case QSA_FP8_E4M3: QSA_COMPRESS_LAUNCH(2); break;
+    default: QSA_COMPRESS_LAUNCH(3); break;
     }
+#undef QSA_COMPRESS_LAUNCH
     return hipGetLastError();
+}
+
+template <typename TIn, int DPL>
+hipError_t dispatch_r(const void *k_idx, const qsa_batch &b, const int64_t *fb, int log2r,
+                      void *kc, int kc_dtype, void *kc_scale, const PageMap &pm, dim3 grid,
+                      hipStream_t st) {
+    return log2r == 2 ? dispatch_kc<TIn, DPL, 4>(k_idx, b, fb, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
+                      : dispatch_kc<TIn, DPL, 0>(k_idx, b, fb, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
 }
 
 }  // namespace
@@ -105,10 +157,10 @@ hipError_t launch_compress(const void *k_idx, int k_dtype, int d_idx, int ratio,
           ratio, k_dtype, kc_dtype);
     const bool bf = (k_dtype == QSA_BF16);
     if (d_idx == 64)
-        return bf ? dispatch_kc<uint16_t, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
-                  : dispatch_kc<float, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
-    return bf ? dispatch_kc<uint16_t, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
-              : dispatch_kc<float, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
+        return bf ? dispatch_r<uint16_t, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
+                  : dispatch_r<float, 1>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
+    return bf ? dispatch_r<uint16_t, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st)
+              : dispatch_r<float, 2>(k_idx, b, first_block, log2r, kc, kc_dtype, kc_scale, pm, grid, st);
 }
 
 }  // namespace qsa

@@ -114,7 +114,7 @@ __device__ __forceinline__ void store_kc(const float (&m)[DPL], void *__restrict
         float amax = 0.0f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) amax = fmaxf(amax, fabsf(m[e]));
-        amax = wave_max(amax);
+        amax = wave_max_f32(amax);             // DPP steps, no LDS round trips (max is exact in any order)
         const float scale = amax / 448.0f;    // correctly rounded division
         if (lane == 0) static_cast<float *>(kc_scale)[out_row] = scale;
         sc = scale;
