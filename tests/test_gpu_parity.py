@@ -208,6 +208,55 @@ def test_decode_batches_at_the_scorer_row_limit(n):
     _print(f"[parity] {n} decode rows: ok")
 
 
+@pytest.mark.parametrize("ratio", [4, 8])
+@pytest.mark.parametrize("kc_dtype", ["bf16", "e4m3", "fp4"])
+def test_compress_from_first_block(ratio, kc_dtype):
+    # qsa_compress_keys with first_block: blocks before first_block[s] keep
+    # what they held, the rest equal the oracle's.  Ratio 4 takes the kernel
+    # whose waves request all rows of their four blocks together (blocks
+    # before the start, or past the row's end, are read in place of a block
+    # that exists and are not stored); ratio 8 the runtime-ratio loop.  The
+    # starts fall on a wave's first block, inside a wave, at the row's end
+    # and past it.
+    import indexer_selected_sparse_amd as Q
+    from indexer_selected_sparse_amd import pipeline
+    sp = dataclasses.replace(W.BATCHED_DECODE, ratio=ratio, budget=64 * ratio, kc_dtype=kc_dtype, hq=8, hkv=1)
+    lens = [ratio * 37 + 3, ratio * 16, ratio * 5 + 1, ratio * 70 + ratio - 1, 2, ratio * 9]
+    starts = [0, 4, 6, 17, 0, 9]
+    wl = W.make(sp, lens=lens, seed=44 + ratio)
+    dp = pipeline.upload(wl, "cuda")
+    kc_u8 = dp.kc.view(torch.uint8)
+    kc_u8.fill_(0x5A)
+    if dp.kc_scale is not None:
+        dp.kc_scale.view(torch.uint8).fill_(0x3C)
+    rows = dp.kc.shape[0]
+    before = kc_u8.cpu().numpy().copy()
+    sc_u8 = None if dp.kc_scale is None else dp.kc_scale.view(torch.uint8).reshape(rows, -1)
+    sc_before = None if sc_u8 is None else sc_u8.cpu().numpy().copy()
+    fb = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    Q.compress_keys(dp.k_idx, ratio, dp.batch, dp.kc, dp.kc_scale, first_block=fb)
+    torch.cuda.synchronize()
+    got = kc_u8.cpu().numpy()
+    sc_got = None if sc_u8 is None else sc_u8.cpu().numpy()
+    ref_kc, ref_sc = oracle.compress(wl.k_idx.float().numpy(), wl.kv_offsets, ratio, kc_dtype)
+    ref_u8 = np.ascontiguousarray(ref_kc).view(np.uint8).reshape(ref_kc.shape[0], -1)
+    ref_sc_u8 = None if ref_sc is None else np.ascontiguousarray(ref_sc).view(np.uint8).reshape(ref_kc.shape[0], -1)
+    row = 0
+    for s, L in enumerate(lens):
+        for b in range(L // ratio):
+            if b < starts[s]:
+                assert np.array_equal(got[row], before[row]), f"seq {s} block {b} (before the start) was written"
+                if sc_got is not None:
+                    assert np.array_equal(sc_got[row], sc_before[row]), f"seq {s} block {b}: scale written"
+            else:
+                assert np.array_equal(got[row], ref_u8[row]), f"seq {s} block {b}: kc differs from the oracle"
+                if sc_got is not None:
+                    assert np.array_equal(sc_got[row], ref_sc_u8[row]), f"seq {s} block {b}: scale differs"
+            row += 1
+    assert row == ref_kc.shape[0]
+    _print(f"[parity] compress from first_block, ratio {ratio} {kc_dtype}: ok ({row} blocks)")
+
+
 def test_decode_workspace_reused_across_batch_shapes():
     # one decode workspace shared by batches of different shapes, used
     # alternately: each shape must reproduce its first result bit for bit
