@@ -43,7 +43,9 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_one_kernel(
                                    pm, lane);
 }
 
-template <typename TIn, int DPL, int KC>
+// R: the ratio when known at compile time (4), else 0; with R the block's
+// rows are requested together rather than one after another.
+template <typename TIn, int DPL, int KC, int R>
 __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
     const TIn *__restrict__ k_new, const int64_t *__restrict__ kv_off,
     const int64_t *__restrict__ blk_off, const int64_t *__restrict__ q_off, int log2r,
@@ -118,13 +120,28 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
                 float acc[DPL];
 #pragma unroll
                 for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-                for (int j = 0; j < (1 << log2r); ++j) {
-                    const int64_t p = b0 + j;
-                    const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
-                    float x[DPL];
-                    load_row<TIn, DPL>(src + lane * DPL, x);
+                if constexpr (R > 0) {
+                    float x[R][DPL];
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[e];
+                    for (int j = 0; j < R; ++j) {
+                        const int64_t p = b0 + j;
+                        const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
+                        load_row<TIn, DPL>(src + lane * DPL, x[j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < R; ++j) {
+#pragma unroll
+                        for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[j][e];
+                    }
+                } else {
+                    for (int j = 0; j < (1 << log2r); ++j) {
+                        const int64_t p = b0 + j;
+                        const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
+                        float x[DPL];
+                        load_row<TIn, DPL>(src + lane * DPL, x);
+#pragma unroll
+                        for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[e];
+                    }
                 }
                 float m[DPL];
 #pragma unroll
@@ -191,8 +208,12 @@ hipError_t dispatch_ingest(const void *k_new, const qsa_batch &b, int log2r, con
         hipLaunchKernelGGL((ingest_one_kernel<TIn, DPL, KC>), grid, block, 0, st, x, b.kv_offsets,  \
                            b.blk_offsets, b.num_seqs, log2r, inv, ring, kc, kc_scale, kv, status,  \
                            pm);                                                                     \
+    else if (log2r == 2)                                                                            \
+        hipLaunchKernelGGL((ingest_kernel<TIn, DPL, KC, 4>), grid, block, 0, st, x, b.kv_offsets,   \
+                           b.blk_offsets, b.q_offsets, log2r, inv, ring, kc, kc_scale, kv, status, \
+                           pm, items);                                                              \
     else                                                                                            \
-        hipLaunchKernelGGL((ingest_kernel<TIn, DPL, KC>), grid, block, 0, st, x, b.kv_offsets,      \
+        hipLaunchKernelGGL((ingest_kernel<TIn, DPL, KC, 0>), grid, block, 0, st, x, b.kv_offsets,   \
                            b.blk_offsets, b.q_offsets, log2r, inv, ring, kc, kc_scale, kv, status, \
                            pm, items)
     switch (kc_dtype) {
