@@ -29,6 +29,50 @@ namespace qsa {
 namespace {
 
 constexpr int kIngestMaxWaves = 4;
+constexpr int kIngestBlocks = 4;     // blocks per wave of the compile-time-ratio prompt ingest
+
+// One lane's DPL raw key values of a row, as stored (the ring holds raw
+// keys), and their fp32 values (exact widening, as load_row gives them).
+template <typename TIn, int DPL>
+struct RawRow {
+    TIn v[DPL];
+};
+template <typename TIn, int DPL>
+__device__ __forceinline__ RawRow<TIn, DPL> raw_load(const TIn *__restrict__ p) {
+    RawRow<TIn, DPL> r;
+    if constexpr (std::is_same<TIn, uint16_t>::value && DPL == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+        r.v[0] = (uint16_t)(u & 0xffffu);
+        r.v[1] = (uint16_t)(u >> 16);
+    } else if constexpr (std::is_same<TIn, float>::value && DPL == 2) {
+        const float2 f = *reinterpret_cast<const float2 *>(p);
+        r.v[0] = f.x;
+        r.v[1] = f.y;
+    } else {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) r.v[e] = p[e];
+    }
+    return r;
+}
+template <typename TIn, int DPL>
+__device__ __forceinline__ void raw_store(TIn *__restrict__ p, const RawRow<TIn, DPL> &r) {
+    if constexpr (std::is_same<TIn, uint16_t>::value && DPL == 2) {
+        *reinterpret_cast<uint32_t *>(p) = (uint32_t)r.v[0] | ((uint32_t)r.v[1] << 16);
+    } else if constexpr (std::is_same<TIn, float>::value && DPL == 2) {
+        *reinterpret_cast<float2 *>(p) = make_float2(r.v[0], r.v[1]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) p[e] = r.v[e];
+    }
+}
+template <typename TIn, int DPL>
+__device__ __forceinline__ void raw_widen(const RawRow<TIn, DPL> &r, float (&x)[DPL]) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        if constexpr (std::is_same<TIn, uint16_t>::value) x[e] = bf16_to_f32(r.v[e]);
+        else x[e] = r.v[e];
+    }
+}
 
 template <typename TIn, int DPL, int KC>
 __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_one_kernel(
@@ -43,8 +87,12 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_one_kernel(
                                    pm, lane);
 }
 
-// R: the ratio when known at compile time (4), else 0; with R the block's
-// rows are requested together rather than one after another.
+// R: the ratio when known at compile time (4), else 0.  With R a wave takes
+// kIngestBlocks consecutive blocks in three phases: every key row of its
+// blocks is loaded once (old keys from the ring, new ones from the input),
+// then the new tokens' ring and K/V rows are stored, then the complete
+// blocks are mean-pooled from the loaded rows.  With a runtime ratio a wave
+// takes one block and its steps go one after another.
 template <typename TIn, int DPL, int KC, int R>
 __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
     const TIn *__restrict__ k_new, const int64_t *__restrict__ kv_off,
@@ -55,7 +103,9 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
     constexpr int kKeyBytes = D * (int)sizeof(TIn);
     const int s = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
-    const int item = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    constexpr int kBlk = R > 0 ? kIngestBlocks : 1;   // blocks per wave
+    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int item = wv * kBlk;                       // the wave's first block (work item)
 
     const int64_t row0 = kv_off[s];
     const int64_t N = kv_off[s + 1] - row0;
@@ -79,7 +129,7 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
         if (item == 0 && lane == 0 && status) status[s] = code;
         return;
     }
-    if (item >= n_items && item != 0) return;
+    if (item >= n_items && item != 0) return;   // (item 0: the window and status below)
 
     const int64_t cap = ring.cap;
     TIn *const rkeys = static_cast<TIn *>(ring.keys) + (int64_t)slot * cap * D;
@@ -93,7 +143,73 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
     const int64_t n_old = start - bf;
     bool lost = false;
 
-    if (item < n_items) {
+    if constexpr (R > 0) {
+        if (item < n_items) {
+            // 1: every key row of the wave's blocks (rows past N, and blocks
+            // past the append, read a row that exists and are not used)
+            RawRow<TIn, DPL> raw[kBlk][R];
+#pragma unroll
+            for (int u = 0; u < kBlk; ++u) {
+                const int64_t g = g_first + (item + u < n_items ? item + u : item);
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t p0 = g * R + j;
+                    const int64_t p = p0 < N ? p0 : N - 1;
+                    const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
+                    raw[u][j] = raw_load<TIn, DPL>(src + lane * DPL);
+                }
+            }
+            // 2: the new tokens' ring rows (those no old key of the first
+            // block sits on) and K/V rows
+#pragma unroll
+            for (int u = 0; u < kBlk; ++u) {
+                if (item + u >= n_items) break;                  // uniform
+                const int64_t b0 = (g_first + item + u) * R;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t p = b0 + j;
+                    if (p < start || p >= N) continue;           // uniform
+                    if (p >= keep_lo && pos_mod(p - bf, cap) >= n_old)
+                        raw_store<TIn, DPL>(rkeys + pos_mod(p, cap) * D + lane * DPL, raw[u][j]);
+                    if (kv.row_bytes) {
+                        const int64_t dst = pm.table ? paged_row(pm, s, p, pm.log2_page) : row0 + p;
+                        const int64_t srow = q0 + p - start;
+                        copy_row(kv.k + dst * kv.row_bytes, kv.k_new + srow * kv.row_bytes, kv.row_bytes, lane);
+                        copy_row(kv.v + dst * kv.row_bytes, kv.v_new + srow * kv.row_bytes, kv.row_bytes, lane);
+                    }
+                }
+            }
+            // 3: the complete blocks' means, rows summed in token order
+#pragma unroll
+            for (int u = 0; u < kBlk; ++u) {
+                if (item + u >= n_items) break;                  // uniform
+                const int64_t g = g_first + item + u;
+                const int64_t b0 = g * R;
+                if (b0 + R > N) continue;                         // the append does not complete it
+                if (b0 < start) {                                 // old keys came from the ring (g == g_first)
+                    const int64_t lo = win[0], hi = win[1];
+                    const int64_t lo_eff = start <= hi ? (lo < start ? lo : start) : start;
+                    lost = lo_eff > b0;
+                    if (lost) continue;
+                }
+                float acc[DPL];
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float x[DPL];
+                    raw_widen<TIn, DPL>(raw[u][j], x);
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[e];
+                }
+                float m[DPL];
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) m[e] = acc[e] * inv_ratio;
+                const int64_t out_row = pm.table ? paged_row(pm, s, g, pm.log2_page - log2r) : blk_off[s] + g;
+                store_kc<KC, DPL>(m, kc, kc_scale, out_row, lane);
+            }
+        }
+    } else if (item < n_items) {
         const int64_t g = g_first + item;
         const int64_t b0 = g << log2r;
         const int64_t t0 = b0 > start ? b0 : start;
@@ -120,28 +236,13 @@ __global__ __launch_bounds__(kIngestMaxWaves * kWave) void ingest_kernel(
                 float acc[DPL];
 #pragma unroll
                 for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-                if constexpr (R > 0) {
-                    float x[R][DPL];
+                for (int j = 0; j < (1 << log2r); ++j) {
+                    const int64_t p = b0 + j;
+                    const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
+                    float x[DPL];
+                    load_row<TIn, DPL>(src + lane * DPL, x);
 #pragma unroll
-                    for (int j = 0; j < R; ++j) {
-                        const int64_t p = b0 + j;
-                        const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
-                        load_row<TIn, DPL>(src + lane * DPL, x[j]);
-                    }
-#pragma unroll
-                    for (int j = 0; j < R; ++j) {
-#pragma unroll
-                        for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[j][e];
-                    }
-                } else {
-                    for (int j = 0; j < (1 << log2r); ++j) {
-                        const int64_t p = b0 + j;
-                        const TIn *src = p < start ? rkeys + pos_mod(p, cap) * D : k_new + (q0 + p - start) * D;
-                        float x[DPL];
-                        load_row<TIn, DPL>(src + lane * DPL, x);
-#pragma unroll
-                        for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[e];
-                    }
+                    for (int e = 0; e < DPL; ++e) acc[e] = acc[e] + x[e];
                 }
                 float m[DPL];
 #pragma unroll
@@ -241,9 +342,12 @@ hipError_t launch_ingest(const void *k_new, int k_dtype, int d_idx, int ratio, c
     const int64_t max_n = b.q_offsets ? (int64_t)b.max_q_per_seq : 1;
     // blocks one sequence's append touches: at most floor((n + ratio - 2)/ratio) + 1
     const int64_t items = max_n > 0 ? (max_n + ratio - 2) / ratio + 1 : 1;
-    int waves = (int)(items < kIngestMaxWaves ? items : kIngestMaxWaves);
-    dim3 grid((unsigned)((items + waves - 1) / waves), (unsigned)b.num_seqs);
-    const int cap_items = (int)(grid.x * waves);
+    // blocks per wave: kIngestBlocks on the compile-time ratio-4 path
+    const int64_t kb = (log2r == 2) ? kIngestBlocks : 1;
+    const int64_t wave_items = (items + kb - 1) / kb;
+    int waves = (int)(wave_items < kIngestMaxWaves ? wave_items : kIngestMaxWaves);
+    dim3 grid((unsigned)((wave_items + waves - 1) / waves), (unsigned)b.num_seqs);
+    const int cap_items = (int)(grid.x * waves * kb);
     if (b.q_offsets == nullptr) {   // one token per sequence: one wave per sequence
         waves = kIngestMaxWaves;
         grid = dim3((unsigned)((b.num_seqs + waves - 1) / waves));
