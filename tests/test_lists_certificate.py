@@ -151,3 +151,56 @@ def test_list_len_bounds():
             m = -(-64 * K // nb)
             assert min(64, m) <= kk <= 64
     assert list_len(32768, 512) == 8 and list_len(8192, 512) == 15 and list_len(2048, 512) == 35
+
+
+_BOUND_PROGRAM = r"""
+#include <cstdio>
+#include "qsa_lists.hpp"
+int main() {
+    long long nb;
+    int K;
+    while (std::scanf("%lld %d", &nb, &K) == 2) std::printf("%lld\n", (long long)qsa::list_max_entries(nb, K));
+    return 0;
+}
+"""
+
+
+def test_list_max_entries_is_the_largest_list_a_row_can_hold(tmp_path):
+    # The attention kernels request, before a row's length is known, the most
+    # entries any row of at most nb_max blocks can list; the library computes
+    # that per value of m = ceil(64 K / nb) (the count is not monotone in nb).
+    # Here the library's host function, built on its own, against the running
+    # maximum of ceil(nb / 64) * list_len(nb, K) over every nb.
+    import os
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "bound.cpp"
+    src.write_text(_BOUND_PROGRAM)
+    exe = tmp_path / "bound"
+    subprocess.run([hipcc, "-O1", "-std=c++17", "--offload-arch=gfx950", "-I", os.path.join(root, "include"),
+                    "-I", os.path.join(root, "indexer_selected_sparse_amd", "csrc"), str(src), "-o", str(exe)],
+                   check=True, capture_output=True, text=True, timeout=300)
+    top = 140000
+    pairs, want = [], []
+    for K in (1, 2, 3, 7, 8, 63, 64, 100, 512, 1000, 1024, 2047, 2048):
+        best, run = 0, [0] * (top + 1)
+        for nb in range(1, top + 1):
+            if nb > K:
+                best = max(best, -(-nb // CHUNK) * list_len(nb, K))
+            run[nb] = best
+        nbs = set(range(1, 3001)) | set(range(1, top + 1, 61))
+        for m in range(1, CHUNK + 1):
+            edge = -(-CHUNK * K // m)
+            nbs |= {edge - 1, edge, edge + 1}
+        for nb in sorted(x for x in nbs if 1 <= x <= top):
+            pairs.append(f"{nb} {K}")
+            want.append(run[nb])
+    out = subprocess.run([str(exe)], input="\n".join(pairs) + "\n", capture_output=True, text=True, check=True,
+                         timeout=300).stdout.split()
+    got = [int(x) for x in out]
+    bad = [(p, g, w) for p, g, w in zip(pairs, got, want) if g != w]
+    assert len(got) == len(want) and not bad, bad[:5]
