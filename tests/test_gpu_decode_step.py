@@ -105,6 +105,39 @@ def test_shorter_rows_list_more_than_the_longest():
                 seed=609))
 
 
+def test_loose_max_kv_len_gives_the_same_step():
+    # max_kv_len is only the host's bound on the lengths: it sizes the
+    # scorer's grid (a slot per 256-block group of a row that long), the
+    # lists' row stride and the entries each attention workgroup requests
+    # before its row's length is known.  Four times the longest row must give
+    # the same scores, selection and outputs bit for bit; at that bound
+    # (31000 blocks) a row could list 6305 entries, so the attention also
+    # switches from the 4-group to the 8-group register selection.
+    wl = W.make(W.BATCHED_DECODE, lens=[9001, 20000, 4097, 31000, 2051, 100, 7750 * 4], seed=610)
+    dp = pipeline.upload(wl, "cuda", decode=True)
+    dp.compress()
+    dp.scores.fill_(float("nan"))
+    dp.decode_step()
+    torch.cuda.synchronize()
+    b = dp.batch
+    loose = Q.Batch(b.kv_offsets, b.blk_offsets, b.q_offsets, b.total_q, 4 * b.max_kv_len, b.max_q_per_seq)
+    ld = -(-loose.max_kv_len // dp.ratio)
+    sc2 = torch.full((b.total_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    idx2 = torch.full_like(dp.idx, -9)
+    out2 = torch.zeros_like(dp.out)
+    ws2 = torch.empty(max(Q.decode_step_workspace_size(dp.q, dp.K, dp.V, dp.softmax_scale, dp.budget, dp.ratio,
+                                                       loose), 1), dtype=torch.uint8, device="cuda")
+    Q.decode_step(dp.q_idx, dp.w, dp.kc, dp.kc_scale, dp.q, dp.K, dp.V, dp.softmax_scale, dp.budget, dp.ratio,
+                  loose, sc2, idx2, out2, ws2)
+    torch.cuda.synchronize()
+    for r, L in enumerate(wl.lens):
+        nb = L // dp.ratio
+        assert torch.equal(_bits(sc2[r, :nb]), _bits(dp.scores[r, :nb])), f"row {r}: scores differ"
+    assert torch.equal(idx2, dp.idx), "selection differs under the loose bound"
+    assert torch.equal(_bits(out2), _bits(dp.out)), "outputs differ under the loose bound"
+    _print(f"[decode_step] loose max_kv_len {loose.max_kv_len} (tight {b.max_kv_len}): identical")
+
+
 def test_paged_caches():
     sp = dataclasses.replace(W.LONG_DECODE, hq=16, hkv=2, budget=1024)
     _run(W.make(sp, lens=[20000, 7001, 1024 * 4 + 2], seed=602), paged=128)
