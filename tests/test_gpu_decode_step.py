@@ -138,6 +138,12 @@ def test_loose_max_kv_len_gives_the_same_step():
     _print(f"[decode_step] loose max_kv_len {loose.max_kv_len} (tight {b.max_kv_len}): identical")
 
 
+def test_no_row_holds_a_complete_block():
+    # every row shorter than one block: no scores, no lists (the scorer's grid
+    # is sized from zero blocks), every row dense over its tail tokens
+    _run(W.make(W.BATCHED_DECODE, lens=[1, 2, 3, 3, 1], seed=611))
+
+
 def test_paged_caches():
     sp = dataclasses.replace(W.LONG_DECODE, hq=16, hkv=2, budget=1024)
     _run(W.make(sp, lens=[20000, 7001, 1024 * 4 + 2], seed=602), paged=128)

@@ -257,6 +257,34 @@ def test_compress_from_first_block(ratio, kc_dtype):
     _print(f"[parity] compress from first_block, ratio {ratio} {kc_dtype}: ok ({row} blocks)")
 
 
+def test_batch_without_queries_writes_nothing():
+    # a prefill batch whose sequences append no queries (total_q = 0): every
+    # call succeeds, launches nothing that writes, and leaves its outputs as
+    # they were (one sentinel row each)
+    import indexer_selected_sparse_amd as Q
+    from indexer_selected_sparse_amd import pipeline
+    sp = dataclasses.replace(W.CHUNKED_PREFILL, budget=256)
+    wl = W.make(sp, lens=[1500, 300], n_q=[4, 2], seed=45)
+    dp = pipeline.upload(wl, "cuda")
+    dp.compress()
+    b = dp.batch
+    zero_q = torch.zeros(len(wl.lens) + 1, dtype=torch.int64, device="cuda")
+    empty = Q.Batch(b.kv_offsets, b.blk_offsets, zero_q, 0, b.max_kv_len, 1)
+    K = sp.budget // sp.ratio
+    scores = torch.full((1, dp.scores.shape[1]), 7.0, dtype=torch.float32, device="cuda")
+    idx = torch.full((1, K), 5, dtype=torch.int32, device="cuda")
+    out = torch.full((1,) + tuple(dp.out.shape[1:]), 3.0, dtype=dp.out.dtype, device="cuda")
+    Q.index_score(dp.q_idx, dp.w, dp.kc, dp.kc_scale, dp.ratio, empty, scores)
+    tws = torch.empty(max(Q.topk_workspace_size(empty, sp.budget, sp.ratio), 1), dtype=torch.uint8, device="cuda")
+    Q.topk_blocks(scores, sp.budget, sp.ratio, empty, idx, ws=tws)
+    sws = torch.empty(max(Q.score_topk_workspace_size(empty, sp.budget, sp.ratio), 1), dtype=torch.uint8,
+                      device="cuda")
+    Q.index_score_topk(dp.q_idx, dp.w, dp.kc, dp.kc_scale, sp.budget, sp.ratio, empty, scores, idx, sws)
+    Q.sparse_attn_prefill(dp.q, dp.K, dp.V, dp.softmax_scale, idx, sp.budget, sp.ratio, empty, out)
+    torch.cuda.synchronize()
+    assert bool((scores == 7.0).all()) and bool((idx == 5).all()) and bool((out.float() == 3.0).all())
+
+
 def test_decode_workspace_reused_across_batch_shapes():
     # one decode workspace shared by batches of different shapes, used
     # alternately: each shape must reproduce its first result bit for bit
