@@ -260,7 +260,7 @@ def cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "one GPU only: the method runs on a single MI355X here; "
+        print(json.dumps({"error": "one GPU only: the benchmark times the path on one MI355X; "
                                    "--gpus must be 1"}))
         sys.exit(2)
     import torch
