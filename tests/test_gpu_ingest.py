@@ -280,14 +280,18 @@ def test_ingest_error_codes():
 
 
 @pytest.mark.parametrize("kind", ["bf16", "e4m3"])
-def test_contiguous_prefill_ingest_equals_compress(kind):
+@pytest.mark.parametrize("kdt,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 128),
+                                   (torch.float32, 64)], ids=["bf16_d128", "bf16_d64", "f32_d128", "f32_d64"])
+def test_contiguous_prefill_ingest_equals_compress(kind, kdt, d):
     """One append per sequence from length 0 on the contiguous layout: the
     compressed keys equal qsa_compress_keys over the same keys, bit for bit,
-    and the ring ends with the last `cap` keys of every sequence."""
-    r, cap, d = 4, 8, 128
-    lens = [37, 4, 3, 130, 0, 64]
+    and the ring ends with the last `cap` keys of every sequence.  Ratio 4
+    takes the kernels' compile-time-ratio paths, for bf16 and fp32 raw keys
+    of 64 and 128 dims (one and two values per lane)."""
+    r, cap = 4, 8
+    lens = [37, 4, 3, 130, 0, 64, 1031]
     g = torch.Generator().manual_seed(5)
-    k_all = torch.randn((sum(lens), d), generator=g).to(torch.bfloat16).to(DEV)
+    k_all = torch.randn((sum(lens), d), generator=g).to(kdt).to(DEV)
     b = Q.Batch.from_lengths(lens, lens, ratio=r, device=DEV)
     nb = sum(n // r for n in lens)
     kct = kc_torch_dtype(kind)
@@ -296,7 +300,7 @@ def test_contiguous_prefill_ingest_equals_compress(kind):
     rs = torch.zeros(nb, device=DEV) if kind == "e4m3" else None
     gs = torch.full((nb,), 5.0, device=DEV) if kind == "e4m3" else None
     Q.compress_keys(k_all, r, b, ref, rs)
-    ring = Q.KeyRing.empty(len(lens), cap, d)
+    ring = Q.KeyRing.empty(len(lens), cap, d, dtype=kdt)
     st = torch.full((len(lens),), -1, dtype=torch.int32, device=DEV)
     Q.ingest(k_all, r, b, ring, got, gs, status=st)
     torch.cuda.synchronize()
